@@ -1,0 +1,217 @@
+/*
+ * psispec.h — C ABI of libpsispec, the lossless block-verification step of the
+ * Psi-Spec sampler on AMD MI355X (gfx950).
+ *
+ * What the library computes (sources are the web pages on Uno, a
+ * diffusion-augmented LLM):
+ *   - "Uno" research explainer, §3.3 (Psi-Spec): a diffusion pass proposes a
+ *     block of draft tokens x_i drawn from per-position draft distributions q_i;
+ *     the AR pass gives target distributions p_i; draft i is kept with
+ *     probability a_i = min(1, p_i(x_i) / q_i(x_i)); the longest run of kept
+ *     drafts from the start of the block survives; at the first rejected
+ *     position one token is drawn from norm(max(0, p - q)); when the whole block
+ *     survives one extra token is drawn from the last target row.
+ *   - same page, §3.3 TPF bound: one verify call emits between 1 and K+1 tokens.
+ *   - same page, §3.4 (Linear vs Tree sampler) and §7 (what "lossless" means:
+ *     the output law equals the AR law; bitwise equality with plain AR decoding
+ *     is not promised).
+ *   - Uno repository README (inference section): the user-facing sampling
+ *     controls temperature / top-p / top-k.
+ * Randomness: counter-based Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC'11), see PSISPEC RNG below.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership   Every tensor pointer is a caller-owned DEVICE buffer unless the
+ *             argument says "host". The library never allocates, frees or
+ *             synchronises; work is enqueued on `stream` (NULL = the default
+ *             stream) and the call returns right after the enqueue. Calls are
+ *             re-entrant when they use distinct workspaces; two calls that
+ *             share a workspace must be ordered on one stream.
+ * Layout      Logit tensors are contiguous row-major: a row is V consecutive
+ *             values of `dtype`. Device pointers must be 16-byte aligned; the
+ *             workspace must be 256-byte aligned.
+ * dtype       PSISPEC_DTYPE_F32 (IEEE binary32) or PSISPEC_DTYPE_BF16
+ *             (bfloat16, upper half of a binary32).
+ * Errors      Argument errors are returned synchronously (negative codes
+ *             below) and nothing is enqueued. Errors that can only be seen in
+ *             the data (a token outside [0, V), a NaN or +inf logit, a row that
+ *             is entirely -inf) are reported per request: out_len[b] = -1 and
+ *             that request's output tokens are all -1; other requests are
+ *             unaffected.
+ * Determinism The same inputs, parameters, seed and step give bitwise
+ *             identical outputs on every run; there are no floating-point
+ *             atomics anywhere in the library.
+ */
+#ifndef PSISPEC_H
+#define PSISPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PSISPEC_OK            0
+#define PSISPEC_EINVAL       -1 /* null pointer, size <= 0, temperature < 0 or not finite,
+                                   top_p outside (0, 1], top_k outside [0, V], misaligned
+                                   pointer, malformed tree topology */
+#define PSISPEC_EUNSUPPORTED -2 /* dtype other than F32/BF16, K or tree depth > 64,
+                                   tree with more than 256 nodes, top_p < 1 with
+                                   top_k == 0 or top_k > 1024 */
+#define PSISPEC_EWORKSPACE   -3 /* ws_bytes smaller than psispec_workspace_bytes(...) */
+#define PSISPEC_EHIP         -4 /* a HIP launch failed */
+
+/* ---- dtypes --------------------------------------------------------------- */
+#define PSISPEC_DTYPE_F32  0
+#define PSISPEC_DTYPE_BF16 1
+
+/* ---- flags ------------------------------------------------------------------ */
+/* psispec_verify_linear draws the drafts itself from q (exactly as
+   psispec_draft_sample with the same params would) and writes them to
+   draft_tokens, instead of reading them from there. */
+#define PSISPEC_FUSED_DRAFT 1u
+
+/* ---- limits ----------------------------------------------------------------- */
+#define PSISPEC_MAX_K         64   /* draft positions per request (one wave64 ballot) */
+#define PSISPEC_MAX_TREE_NODES 256 /* tree nodes per request */
+#define PSISPEC_MAX_TOPK      1024 /* largest top_k when top-p filtering is on */
+
+/*
+ * Sampling parameters (Uno README, inference controls: temperature, top-p,
+ * top-k).
+ *   temperature  > 0: logits z = a / temperature; == 0: greedy mode (argmax,
+ *                lowest index on ties; draft accepted iff it equals the target
+ *                argmax; no random numbers are drawn; top_k/top_p ignored).
+ *   top_k        0 or >= V disables; otherwise keep the top_k largest z per
+ *                row (ties: the lower token id wins).
+ *   top_p        1 disables; otherwise, among the tokens kept by top-k, keep the
+ *                shortest prefix of the probability-sorted list (ties: lower id
+ *                first) whose cumulative probability reaches top_p (at least
+ *                one token). Filtering is applied in the order temperature ->
+ *                top-k -> top-p -> renormalise, identically and independently
+ *                to every target row and every draft row; losslessness then
+ *                holds with respect to the filtered target distribution.
+ *   seed, step   Philox key and the step word of the counter (see RNG).
+ *   flags        bitwise OR of PSISPEC_* flags.
+ */
+typedef struct psispec_params {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  uint32_t flags;
+  uint64_t seed;
+  uint32_t step;
+  uint32_t reserved; /* must be 0 */
+} psispec_params;
+
+/*
+ * PSISPEC RNG. Every uniform is U(seed, step, b, r, d) = word0 * 2^-32 (a
+ * double in [0, 1)) where word0 is the first output word of Philox4x32-10 with
+ *   key     = (lo32(seed), hi32(seed))
+ *   counter = (d, r, b, step)
+ * b is the request, r the logit row within the request, and d the draw id:
+ *   d = 0               final sample (residual, bonus or tree stop) at row r
+ *   d = 1 + j           accept test of the j-th candidate child at row r
+ *                       (the linear sampler uses j = 0 at every position)
+ *   d = 0x40000000 + j  j-th draft drawn from draft row r
+ * Because the tree sampler uses the same layout, a chain-shaped tree gives
+ * bit-for-bit the result of psispec_verify_linear.
+ */
+
+/*
+ * Bytes of workspace sufficient for any call of this library on B requests,
+ * each reading at most `rows_per_req` logit rows of length V:
+ *   psispec_draft_sample   rows_per_req = K
+ *   psispec_verify_linear  rows_per_req = 2*K + 1
+ *   psispec_verify_tree    rows_per_req = 2*(N + 1)
+ * Returns 0 for arguments out of range. Pure host function.
+ */
+size_t psispec_workspace_bytes(int64_t B, int32_t rows_per_req, int32_t V, int dtype);
+
+/*
+ * Draft sampling (Uno explainer §3.3: the diffusion pass proposes every block
+ * position in parallel, each token drawn independently from its own draft
+ * distribution q_i).
+ *   q_logits      [B, K, V] draft logits.
+ *   draft_tokens  [B, K] int32 out: x_{b,i} drawn from softmax(filter(q_{b,i} / T))
+ *                 by inverse CDF in token-id order with U(seed, step, b, i,
+ *                 0x40000000); greedy mode (T == 0): argmax of q_{b,i}.
+ *                 A request with an invalid q row gets -1 in every slot.
+ */
+int psispec_draft_sample(const void* q_logits, int dtype, int64_t B, int32_t K, int32_t V,
+                         const psispec_params* params, int32_t* draft_tokens, void* workspace,
+                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Linear verification (Uno explainer §3.3 and §3.4 "Linear Sampler").
+ *   p_logits      [B, K+1, V] target logits; row i scores draft position i and
+ *                 row K is the bonus row used when every draft is accepted.
+ *   q_logits      [B, K, V] draft logits.
+ *   draft_tokens  [B, K] int32; input, or output with PSISPEC_FUSED_DRAFT.
+ *   out_tokens    [B, K+1] int32 out: the n accepted drafts, then the final
+ *                 token y, then -1 padding. Emitted tokens per request = n + 1.
+ *   out_len       [B] int32 out: n in [0, K] (or -1 for a request error).
+ *   out_probs     nullable [B, K, 2] float out: (p_i(x_i), q_i(x_i)) for every
+ *                 position i, after temperature and filtering; greedy mode
+ *                 writes the one-hot limits (x_i == argmax p_i, x_i == argmax q_i).
+ *   out_resid_mass nullable [B] double out: sum_j max(0, p_n(j) - q_n(j)) when
+ *                 n < K (= 1 - alpha_n, alpha = sum_j min(p, q)), 0 when n == K
+ *                 or in greedy mode.
+ * Decision rules (U as in PSISPEC RNG):
+ *   accept_i  <=>  U(seed, step, b, i, 1) * q_i(x_i) < p_i(x_i)
+ *   n         =    first i with !accept_i, else K
+ *   y         =    inverse-CDF draw, in token-id order, with U(seed, step, b, n, 0)
+ *                  from max(0, p_n - q_n) if n < K (from p_n if that is all zero),
+ *                  or from p_K if n == K.
+ */
+int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype, int64_t B, int32_t K,
+                          int32_t V, int32_t* draft_tokens, const psispec_params* params,
+                          int32_t* out_tokens, int32_t* out_len, float* out_probs, double* out_resid_mass,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Depth of a candidate tree given its HOST parent array (parent[n] in
+ * [-1, n-1]; -1 = child of the root). Returns the depth D >= 1, or a negative
+ * status for a malformed topology. Pure host function.
+ */
+int32_t psispec_tree_depth(const int32_t* parent, int32_t N);
+
+/*
+ * Tree verification (Uno explainer §3.4 "Tree Sampler": several candidate
+ * continuations checked in one verify pass). Verification rule: at a node
+ * with children c_0 < c_1 < ... (ascending node id), each child drawn i.i.d.
+ * from that node's draft distribution Q, start with r = P; child j is accepted
+ * iff U(seed, step, b, row, 1+j) * Q(tok_j) < r(tok_j); after a rejection
+ * r <- norm(max(0, r - Q)) (kept unchanged when that is all zero); the walk
+ * descends into the first accepted child; at a leaf, or when every child is
+ * rejected, the final token is drawn from r with U(seed, step, b, row, 0).
+ *   p_logits, q_logits  [B, N+1, V]; row 0 is the root context, row n+1 the
+ *                 context after node n.
+ *   parent        HOST [N] int32, parent[n] < n, -1 for children of the root;
+ *                 shared by every request.
+ *   node_tokens   [B, N] int32 candidate token of each node.
+ *   out_tokens    [B, D+1] int32 out (D = psispec_tree_depth): path tokens, the
+ *                 final token, then -1 padding.
+ *   out_path      [B, D] int32 out: node ids of the accepted path, -1 padding.
+ *   out_len       [B] int32 out: accepted path length (or -1 on error).
+ */
+int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, int64_t B, int32_t N,
+                        int32_t V, const int32_t* parent, const int32_t* node_tokens,
+                        const psispec_params* params, int32_t* out_tokens, int32_t* out_path,
+                        int32_t* out_len, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Static message for a status code. */
+const char* psispec_strerror(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int psispec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSISPEC_H */

@@ -1,0 +1,207 @@
+"""ctypes binding of the plain CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the slow, obviously-correct double-precision
+reference the GPU library is checked against. Only the test suite, the smoke
+check and the CPU-baseline leg of the benchmark may import this module; the
+GPU library and its Python binding never do.
+
+Function-level citations live in oracle.c. The functions here only marshal
+numpy arrays into the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+DRAFT_DRAW = 0x40000000
+
+
+def build() -> str:
+    """Compiles oracle.c into liboracle.so (gcc, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fPIC", "-shared",
+           "-o", _LIB, _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, u32, u64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_double
+        L.orc_philox4x32_10.argtypes = [P, P, P]
+        L.orc_philox4x32_10.restype = None
+        L.orc_uniform.argtypes = [u64, u32, u32, u32, u32]
+        L.orc_uniform.restype = f64
+        L.orc_decode_row.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, P]
+        L.orc_decode_row.restype = ctypes.c_int
+        L.orc_filter_row.argtypes = [P, ctypes.c_int, f64, ctypes.c_int, f64]
+        L.orc_filter_row.restype = None
+        L.orc_logsumexp.argtypes = [P, ctypes.c_int]
+        L.orc_logsumexp.restype = f64
+        L.orc_sample.argtypes = [P, ctypes.c_int, f64, P]
+        L.orc_sample.restype = ctypes.c_int
+        L.orc_tree_depth.argtypes = [P, ctypes.c_int]
+        L.orc_tree_depth.restype = ctypes.c_int
+        L.orc_draft_sample.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, f64, ctypes.c_int, f64,
+                                       u64, u32, P, P, P, ctypes.c_int]
+        L.orc_draft_sample.restype = ctypes.c_int
+        L.orc_verify_linear.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, f64, ctypes.c_int,
+                                        f64, u64, u32, ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int]
+        L.orc_verify_linear.restype = ctypes.c_int
+        L.orc_verify_tree.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, P, f64, ctypes.c_int,
+                                      f64, u64, u32, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int]
+        L.orc_verify_tree.restype = ctypes.c_int
+        del i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:  # raw bfloat16 bits
+        return BF16
+    raise TypeError("logits must be float32 or uint16 (bfloat16 bits)")
+
+
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def uniform(seed, step, b, r, d) -> float:
+    return lib().orc_uniform(seed, step, b, r, d)
+
+
+def logsumexp(z) -> float:
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    return lib().orc_logsumexp(_ptr(z), z.size)
+
+
+def sample(w, u):
+    """Inverse-CDF draw; returns (index, margin)."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    m = ctypes.c_double(0.0)
+    j = lib().orc_sample(_ptr(w), w.size, float(u), ctypes.byref(m))
+    return j, m.value
+
+
+def filter_row(a, temperature, top_k=0, top_p=1.0):
+    """Temperature, top-k, top-p on one row of logits; returns z (removed -> -inf)."""
+    z = np.array(a, dtype=np.float64, copy=True)
+    lib().orc_filter_row(_ptr(z), z.size, float(temperature), int(top_k), float(top_p))
+    return z
+
+
+def decode_row(logits, row):
+    """Decodes row `row` of a 2-D logit array; returns (values, bad)."""
+    a = np.ascontiguousarray(logits)
+    V = a.shape[-1]
+    out = np.zeros(V, dtype=np.float64)
+    bad = lib().orc_decode_row(_ptr(a), _dtype_code(a), int(row), V, _ptr(out))
+    return out, bool(bad)
+
+
+def tree_depth(parent) -> int:
+    p = np.ascontiguousarray(parent, dtype=np.int32)
+    return lib().orc_tree_depth(_ptr(p), p.size)
+
+
+def draft_sample(q, temperature, top_k=0, top_p=1.0, seed=0, step=0, u_override=None, nthreads=1):
+    """q: [B, K, V] float32 or uint16 (bf16 bits). Returns (tokens [B,K], margins [B,K])."""
+    q = np.ascontiguousarray(q)
+    B, K, V = q.shape
+    out = np.zeros((B, K), dtype=np.int32)
+    mg = np.zeros((B, K), dtype=np.float64)
+    ovr = None if u_override is None else np.ascontiguousarray(u_override, dtype=np.float64).reshape(B, K)
+    rc = lib().orc_draft_sample(_ptr(q), _dtype_code(q), B, K, V, float(temperature), int(top_k), float(top_p),
+                                int(seed), int(step), _ptr(out), _ptr(mg), _ptr(ovr), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_draft_sample rejected its arguments")
+    return out, mg
+
+
+def verify_linear(p, q, draft_tokens, temperature, top_k=0, top_p=1.0, seed=0, step=0, fused=False,
+                  u_override=None, nthreads=1):
+    """p: [B, K+1, V], q: [B, K, V] (float32 or uint16 bf16 bits), draft_tokens [B, K].
+
+    u_override: optional [B, K+1, 3] uniforms (slot 0 final draw, 1 accept test,
+    2 draft draw at each row) replacing the Philox stream.
+    Returns a dict with tokens, len, probs, resid, margin_acc, margin_cdf, draft.
+    """
+    p = np.ascontiguousarray(p)
+    q = np.ascontiguousarray(q)
+    B, K1, V = p.shape
+    K = K1 - 1
+    assert q.shape == (B, K, V) and p.dtype == q.dtype
+    draft = np.array(draft_tokens, dtype=np.int32, copy=True).reshape(B, K) if draft_tokens is not None \
+        else np.zeros((B, K), dtype=np.int32)
+    toks = np.zeros((B, K + 1), dtype=np.int32)
+    ln = np.zeros(B, dtype=np.int32)
+    probs = np.zeros((B, K, 2), dtype=np.float64)
+    resid = np.zeros(B, dtype=np.float64)
+    ma = np.zeros(B, dtype=np.float64)
+    mc = np.zeros(B, dtype=np.float64)
+    ovr = None if u_override is None else np.ascontiguousarray(u_override, dtype=np.float64).reshape(B, K + 1, 3)
+    rc = lib().orc_verify_linear(_ptr(p), _ptr(q), _dtype_code(p), B, K, V, _ptr(draft), float(temperature),
+                                 int(top_k), float(top_p), int(seed), int(step), int(bool(fused)), _ptr(toks),
+                                 _ptr(ln), _ptr(probs), _ptr(resid), _ptr(ma), _ptr(mc), _ptr(ovr), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_verify_linear rejected its arguments")
+    return dict(tokens=toks, len=ln, probs=probs, resid=resid, margin_acc=ma, margin_cdf=mc, draft=draft)
+
+
+def verify_tree(p, q, parent, node_tokens, temperature, top_k=0, top_p=1.0, seed=0, step=0, u_override=None,
+                max_children=None, nthreads=1):
+    """p, q: [B, N+1, V]; parent [N]; node_tokens [B, N].
+
+    u_override: optional [B, N+1, 1+max_children] (slot 0 final draw, slot 1+j
+    accept test of child j). Returns a dict with tokens, path, len, margin_acc, margin_cdf.
+    """
+    p = np.ascontiguousarray(p)
+    q = np.ascontiguousarray(q)
+    B, R, V = p.shape
+    N = R - 1
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    nt = np.ascontiguousarray(node_tokens, dtype=np.int32).reshape(B, N)
+    D = tree_depth(par)
+    if D < 0:
+        raise ValueError("malformed tree")
+    toks = np.zeros((B, D + 1), dtype=np.int32)
+    path = np.zeros((B, D), dtype=np.int32)
+    ln = np.zeros(B, dtype=np.int32)
+    ma = np.zeros(B, dtype=np.float64)
+    mc = np.zeros(B, dtype=np.float64)
+    maxC = 0
+    ovr = None
+    if u_override is not None:
+        maxC = int(max_children)
+        ovr = np.ascontiguousarray(u_override, dtype=np.float64).reshape(B, R, 1 + maxC)
+    rc = lib().orc_verify_tree(_ptr(p), _ptr(q), _dtype_code(p), B, N, V, _ptr(par), _ptr(nt), float(temperature),
+                               int(top_k), float(top_p), int(seed), int(step), _ptr(toks), _ptr(path), _ptr(ln),
+                               _ptr(ma), _ptr(mc), _ptr(ovr), maxC, int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_verify_tree rejected its arguments")
+    return dict(tokens=toks, path=path, len=ln, margin_acc=ma, margin_cdf=mc)
