@@ -1,0 +1,199 @@
+"""Python binding of libpsispec (lossless Psi-Spec block verification on MI355X).
+
+Argument marshalling only: every step of the method runs in the HIP kernels of
+libpsispec.so (built in-tree by build.py). torch provides device memory and the
+current stream; there is no CPU or torch fallback — if the library is missing
+the import fails.
+
+Function names mirror the C ABI in include/psispec.h:
+  draft_sample   psispec_draft_sample
+  verify_linear  psispec_verify_linear
+  verify_tree    psispec_verify_tree
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpsispec.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+DTYPE_F32, DTYPE_BF16 = 0, 1
+FUSED_DRAFT = 1
+MAX_K = 64
+
+
+class PsiSpecError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {strerror(status)} ({status})")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    """psispec_params (include/psispec.h)."""
+
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float),
+                ("flags", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("step", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libpsispec.so is not built ({LIB_PATH}); run "
+                          "`python -m lossless_speculative_verification_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.psispec_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
+    L.psispec_workspace_bytes.restype = sz
+    L.psispec_draft_sample.argtypes = [P, ctypes.c_int, i64, i32, i32, ctypes.POINTER(Params), P, P, sz, P]
+    L.psispec_draft_sample.restype = ctypes.c_int
+    L.psispec_verify_linear.argtypes = [P, P, ctypes.c_int, i64, i32, i32, P, ctypes.POINTER(Params), P, P, P, P,
+                                        P, sz, P]
+    L.psispec_verify_linear.restype = ctypes.c_int
+    L.psispec_tree_depth.argtypes = [P, i32]
+    L.psispec_tree_depth.restype = i32
+    L.psispec_verify_tree.argtypes = [P, P, ctypes.c_int, i64, i32, i32, P, P, ctypes.POINTER(Params), P, P, P, P,
+                                      sz, P]
+    L.psispec_verify_tree.restype = ctypes.c_int
+    L.psispec_strerror.argtypes = [ctypes.c_int]
+    L.psispec_strerror.restype = ctypes.c_char_p
+    L.psispec_version.argtypes = []
+    L.psispec_version.restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.psispec_strerror(int(status)).decode()
+
+
+def version() -> int:
+    return lib.psispec_version()
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def workspace_bytes(B: int, rows_per_req: int, V: int, dtype: int) -> int:
+    return int(lib.psispec_workspace_bytes(int(B), int(rows_per_req), int(V), int(dtype)))
+
+
+def make_params(temperature=1.0, top_k=0, top_p=1.0, seed=0, step=0, fused=False) -> Params:
+    return Params(float(temperature), int(top_k), float(top_p), FUSED_DRAFT if fused else 0, int(seed) & (2**64 - 1),
+                  int(step) & 0xFFFFFFFF, 0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != OK:
+        raise PsiSpecError(fn, rc)
+
+
+def _workspace(ws, nbytes, device):
+    if ws is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise PsiSpecError("workspace", EWORKSPACE)
+    return ws
+
+
+def draft_sample(q: torch.Tensor, temperature=1.0, top_k=0, top_p=1.0, seed=0, step=0, out=None, workspace=None,
+                 stream=None) -> torch.Tensor:
+    """Draft tokens [B, K] int32 drawn from q [B, K, V] (psispec_draft_sample)."""
+    assert q.is_cuda and q.is_contiguous() and q.dim() == 3
+    B, K, V = q.shape
+    dt = dtype_code(q)
+    out = out if out is not None else torch.empty((B, K), dtype=torch.int32, device=q.device)
+    ws = _workspace(workspace, workspace_bytes(B, K, V, dt), q.device)
+    prm = make_params(temperature, top_k, top_p, seed, step)
+    rc = lib.psispec_draft_sample(_ptr(q), dt, B, K, V, ctypes.byref(prm), _ptr(out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _check("psispec_draft_sample", rc)
+    return out
+
+
+def verify_linear(p: torch.Tensor, q: torch.Tensor, draft_tokens: torch.Tensor | None, temperature=1.0, top_k=0,
+                  top_p=1.0, seed=0, step=0, fused=False, out=None, want_probs=True, want_resid=True,
+                  workspace=None, stream=None) -> dict:
+    """psispec_verify_linear. p [B, K+1, V], q [B, K, V]; draft_tokens [B, K] int32
+    (written when fused). Returns dict(tokens [B, K+1], len [B], probs [B, K, 2]
+    or None, resid [B] or None, draft [B, K])."""
+    assert p.is_cuda and q.is_cuda and p.is_contiguous() and q.is_contiguous()
+    B, K1, V = p.shape
+    K = K1 - 1
+    assert q.shape == (B, K, V) and p.dtype == q.dtype
+    dt = dtype_code(p)
+    dev = p.device
+    if draft_tokens is None:
+        if not fused:
+            raise ValueError("draft_tokens required unless fused=True")
+        draft_tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    assert draft_tokens.dtype == torch.int32 and draft_tokens.is_contiguous()
+    if out is None:
+        out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                   len=torch.empty((B,), dtype=torch.int32, device=dev),
+                   probs=torch.empty((B, K, 2), dtype=torch.float32, device=dev) if want_probs else None,
+                   resid=torch.empty((B,), dtype=torch.float64, device=dev) if want_resid else None)
+    ws = _workspace(workspace, workspace_bytes(B, 2 * K + 1, V, dt), dev)
+    prm = make_params(temperature, top_k, top_p, seed, step, fused)
+    rc = lib.psispec_verify_linear(_ptr(p), _ptr(q), dt, B, K, V, _ptr(draft_tokens), ctypes.byref(prm),
+                                   _ptr(out["tokens"]), _ptr(out["len"]), _ptr(out.get("probs")),
+                                   _ptr(out.get("resid")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("psispec_verify_linear", rc)
+    out["draft"] = draft_tokens
+    return out
+
+
+def tree_depth(parent) -> int:
+    import numpy as np
+
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    return int(lib.psispec_tree_depth(par.ctypes.data_as(ctypes.c_void_p), par.size))
+
+
+def verify_tree(p: torch.Tensor, q: torch.Tensor, parent, node_tokens: torch.Tensor, temperature=1.0, top_k=0,
+                top_p=1.0, seed=0, step=0, out=None, workspace=None, stream=None) -> dict:
+    """psispec_verify_tree. p, q [B, N+1, V]; parent: host int sequence [N];
+    node_tokens [B, N] int32. Returns dict(tokens [B, D+1], path [B, D], len [B])."""
+    import numpy as np
+
+    assert p.is_cuda and q.is_cuda and p.is_contiguous() and q.is_contiguous()
+    B, R, V = p.shape
+    N = R - 1
+    assert q.shape == p.shape and p.dtype == q.dtype
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    assert par.size == N
+    D = int(lib.psispec_tree_depth(par.ctypes.data_as(ctypes.c_void_p), N))
+    if D < 0:
+        raise PsiSpecError("psispec_tree_depth", D)
+    dt = dtype_code(p)
+    dev = p.device
+    if out is None:
+        out = dict(tokens=torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+                   path=torch.empty((B, D), dtype=torch.int32, device=dev),
+                   len=torch.empty((B,), dtype=torch.int32, device=dev))
+    ws = _workspace(workspace, workspace_bytes(B, 2 * R, V, dt), dev)
+    prm = make_params(temperature, top_k, top_p, seed, step)
+    rc = lib.psispec_verify_tree(_ptr(p), _ptr(q), dt, B, N, V, par.ctypes.data_as(ctypes.c_void_p),
+                                 _ptr(node_tokens), ctypes.byref(prm), _ptr(out["tokens"]), _ptr(out["path"]),
+                                 _ptr(out["len"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("psispec_verify_tree", rc)
+    return out

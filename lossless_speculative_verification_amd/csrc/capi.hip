@@ -1,0 +1,206 @@
+// C ABI of libpsispec: argument validation, workspace carving and launches on
+// the caller's stream. See include/psispec.h for the contract of each call.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/psispec.h"
+#include "kernels.hpp"
+
+namespace psi {
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int elem_bytes(int dtype) { return dtype == PSISPEC_DTYPE_BF16 ? 2 : 4; }
+inline int per_vec(int dtype) { return dtype == PSISPEC_DTYPE_BF16 ? 8 : 4; }
+
+inline int nch32_of(int V, int dtype) {
+  const int64_t chunk = (int64_t)kWG * kStatNV * per_vec(dtype);
+  return (int)((V + chunk - 1) / chunk);
+}
+inline int nsb_of(int V) { return (V + kSB - 1) / kSB; }
+
+// Workspace sections, each 256-byte aligned.
+struct Layout {
+  size_t st, rs, res, dr, total;
+};
+
+inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
+  Layout L;
+  size_t off = 0;
+  const size_t nch = (size_t)nch32_of(V, dtype), nsb = (size_t)nsb_of(V);
+  L.st = off;
+  off = align_up(off + (size_t)B * rows_per_req * nch * sizeof(StatRec), 256);
+  L.rs = off;
+  off = align_up(off + (size_t)B * sizeof(ReqState), 256);
+  L.res = off;
+  off = align_up(off + (size_t)B * nsb * sizeof(ResRec), 256);
+  L.dr = off;
+  off = align_up(off + (size_t)B * rows_per_req * nsb * sizeof(DraftRec), 256);
+  L.total = off;
+  return L;
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Common checks of the sampling parameters.
+inline int check_params(const psispec_params* prm, int32_t V) {
+  if (!prm) return PSISPEC_EINVAL;
+  if (!(prm->temperature >= 0.0f) || !isfinite(prm->temperature)) return PSISPEC_EINVAL;
+  if (!(prm->top_p > 0.0f && prm->top_p <= 1.0f)) return PSISPEC_EINVAL;
+  if (prm->top_k < 0) return PSISPEC_EINVAL;
+  (void)V;
+  return PSISPEC_OK;
+}
+
+inline bool filtered(const psispec_params* prm, int32_t V) {
+  return prm->temperature > 0.0f && ((prm->top_k > 0 && prm->top_k < V) || prm->top_p < 1.0f);
+}
+
+inline void fill_common(LinCfg& c, const void* p, const void* q, int dtype, int64_t B, int32_t K, int32_t V,
+                        const psispec_params* prm, void* ws, int np) {
+  memset(&c, 0, sizeof(c));
+  c.rows.p = (const char*)p;
+  c.rows.q = (const char*)q;
+  c.rows.np = np;
+  c.rows.nq = K;
+  c.rows.V = V;
+  c.rows.esz = elem_bytes(dtype);
+  c.B = B;
+  c.K = K;
+  c.V = V;
+  const int pv = per_vec(dtype);
+  c.aligned = (V % pv == 0) && aligned16(q) && (p == nullptr || aligned16(p));
+  c.nvec = V / pv;
+  c.nch32 = nch32_of(V, dtype);
+  c.nsb = nsb_of(V);
+  const double T = (double)prm->temperature;
+  c.invT = T > 0.0 ? 1.0 / T : 0.0;
+  c.c32 = T > 0.0 ? (float)(1.4426950408889634074 / T) : 0.0f;
+  c.rng.k0 = (uint32_t)(prm->seed & 0xffffffffu);
+  c.rng.k1 = (uint32_t)(prm->seed >> 32);
+  c.rng.step = prm->step;
+  c.fused = (prm->flags & PSISPEC_FUSED_DRAFT) ? 1 : 0;
+  const Layout L = layout(B, np + K, V, dtype);
+  char* w = (char*)ws;
+  c.st = (StatRec*)(w + L.st);
+  c.ar = (ArgRec*)(w + L.st);
+  c.rs = (ReqState*)(w + L.rs);
+  c.res = (ResRec*)(w + L.res);
+  c.dr = (DraftRec*)(w + L.dr);
+}
+
+}  // namespace
+}  // namespace psi
+
+using namespace psi;
+
+extern "C" {
+
+size_t psispec_workspace_bytes(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
+  if (B <= 0 || rows_per_req <= 0 || V <= 0) return 0;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return 0;
+  return layout(B, rows_per_req, V, dtype).total;
+}
+
+int psispec_draft_sample(const void* q_logits, int dtype, int64_t B, int32_t K, int32_t V,
+                         const psispec_params* params, int32_t* draft_tokens, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!q_logits || !draft_tokens || !workspace) return PSISPEC_EINVAL;
+  if (B <= 0 || K <= 0 || V <= 0) return PSISPEC_EINVAL;
+  if (int rc = check_params(params, V)) return rc;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
+  if (K > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
+  if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
+  if (filtered(params, V)) return PSISPEC_EUNSUPPORTED;
+  if (ws_bytes < psispec_workspace_bytes(B, K, V, dtype)) return PSISPEC_EWORKSPACE;
+  LinCfg c;
+  fill_common(c, nullptr, q_logits, dtype, B, K, V, params, workspace, 0);
+  c.draft = draft_tokens;
+  const hipError_t e = params->temperature == 0.0f ? launch_draft_greedy(c, dtype, stream)
+                                                   : launch_draft_sampled(c, dtype, stream);
+  return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+}
+
+int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype, int64_t B, int32_t K, int32_t V,
+                          int32_t* draft_tokens, const psispec_params* params, int32_t* out_tokens,
+                          int32_t* out_len, float* out_probs, double* out_resid_mass, void* workspace,
+                          size_t ws_bytes, hipStream_t stream) {
+  if (!p_logits || !q_logits || !draft_tokens || !out_tokens || !out_len || !workspace) return PSISPEC_EINVAL;
+  if (B <= 0 || K <= 0 || V <= 0) return PSISPEC_EINVAL;
+  if (int rc = check_params(params, V)) return rc;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
+  if (K > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
+  if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
+  if (filtered(params, V)) return PSISPEC_EUNSUPPORTED;
+  if (ws_bytes < psispec_workspace_bytes(B, 2 * K + 1, V, dtype)) return PSISPEC_EWORKSPACE;
+  LinCfg c;
+  fill_common(c, p_logits, q_logits, dtype, B, K, V, params, workspace, K + 1);
+  c.draft = draft_tokens;
+  c.out_tokens = out_tokens;
+  c.out_len = out_len;
+  c.out_probs = out_probs;
+  c.out_resid = out_resid_mass;
+  const hipError_t e = params->temperature == 0.0f ? launch_linear_greedy(c, dtype, stream)
+                                                   : launch_linear_sampled(c, dtype, stream);
+  return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+}
+
+int32_t psispec_tree_depth(const int32_t* parent, int32_t N) {
+  if (!parent || N <= 0) return PSISPEC_EINVAL;
+  if (N > PSISPEC_MAX_TREE_NODES) return PSISPEC_EUNSUPPORTED;
+  int32_t depth[PSISPEC_MAX_TREE_NODES];
+  int32_t D = 0;
+  for (int32_t n = 0; n < N; ++n) {
+    if (parent[n] < -1 || parent[n] >= n) return PSISPEC_EINVAL;
+    depth[n] = parent[n] < 0 ? 1 : depth[parent[n]] + 1;
+    if (depth[n] > D) D = depth[n];
+  }
+  if (D > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
+  return D;
+}
+
+int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, int64_t B, int32_t N, int32_t V,
+                        const int32_t* parent, const int32_t* node_tokens, const psispec_params* params,
+                        int32_t* out_tokens, int32_t* out_path, int32_t* out_len, void* workspace, size_t ws_bytes,
+                        hipStream_t stream) {
+  (void)p_logits;
+  (void)q_logits;
+  (void)dtype;
+  (void)B;
+  (void)N;
+  (void)V;
+  (void)parent;
+  (void)node_tokens;
+  (void)params;
+  (void)out_tokens;
+  (void)out_path;
+  (void)out_len;
+  (void)workspace;
+  (void)ws_bytes;
+  (void)stream;
+  return PSISPEC_EUNSUPPORTED;
+}
+
+const char* psispec_strerror(int status) {
+  switch (status) {
+    case PSISPEC_OK:
+      return "success";
+    case PSISPEC_EINVAL:
+      return "invalid argument";
+    case PSISPEC_EUNSUPPORTED:
+      return "unsupported dtype, size or mode";
+    case PSISPEC_EWORKSPACE:
+      return "workspace too small";
+    case PSISPEC_EHIP:
+      return "HIP launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+int psispec_version(void) { return kVersion; }
+
+}  // extern "C"

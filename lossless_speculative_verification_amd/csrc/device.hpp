@@ -1,0 +1,165 @@
+// Device helpers for libpsispec (gfx950, wave64).
+//
+// Counter-based uniforms: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+// random numbers: as easy as 1, 2, 3", SC'11), with the counter layout the
+// public header documents: counter = (draw id, row, request, step),
+// key = (lo32 seed, hi32 seed), uniform = first output word / 2^32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace psi {
+
+constexpr int kWG = 256;          // threads per workgroup
+constexpr int kWave = 64;         // wave64
+constexpr int kWaves = kWG / kWave;
+constexpr int kSB = 1024;         // elements per fine-grained sub-block (one wave)
+constexpr int kChunk64 = kSB * kWaves;  // elements per workgroup in fp64-grade passes
+constexpr uint32_t kDrawFinal = 0u;
+constexpr uint32_t kDrawAccept = 1u;
+constexpr uint32_t kDrawDraft = 0x40000000u;
+
+// ---------------------------------------------------------------- Philox --
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = c0 * 0xD2511F53u, hi0 = __umulhi(c0, 0xD2511F53u);
+    const uint32_t lo1 = c2 * 0xCD9E8D57u, hi1 = __umulhi(c2, 0xCD9E8D57u);
+    const uint32_t n0 = hi1 ^ c1 ^ k0;
+    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return c0;
+}
+
+struct Rng {
+  uint32_t k0, k1, step;
+  // U(seed, step, b, r, d) in [0, 1) as a double (exact: word * 2^-32).
+  __device__ __forceinline__ double u(uint32_t b, uint32_t r, uint32_t d) const {
+    return (double)philox_word0(d, r, b, step, k0, k1) * 2.3283064365386962890625e-10;
+  }
+};
+
+// ------------------------------------------------------------- loading --
+// dtype codes of the public header
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<kF32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerVec = 4;  // elements per 16-byte vector
+  static constexpr uint32_t kNegInfWord = 0xff800000u;
+  __device__ __forceinline__ static void unpack(const uint4& v, float (&x)[4]) {
+    x[0] = __uint_as_float(v.x);
+    x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z);
+    x[3] = __uint_as_float(v.w);
+  }
+  __device__ __forceinline__ static float load1(const void* base, int64_t idx) {
+    return ((const float*)base)[idx];
+  }
+};
+template <>
+struct Elem<kBF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+  static constexpr uint32_t kNegInfWord = 0xff80ff80u;
+  __device__ __forceinline__ static void unpack(const uint4& v, float (&x)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static float load1(const void* base, int64_t idx) {
+    return __uint_as_float((uint32_t)((const uint16_t*)base)[idx] << 16);
+  }
+};
+
+// NaN-propagating maximum (gfx950 v_maximum3_f32): a NaN anywhere in a row
+// makes its maximum NaN, which the statistics then carry to the row verdict.
+__device__ __forceinline__ float fmaxnan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ bool is_neg_inf(float x) { return __float_as_uint(x) == 0xff800000u; }
+__device__ __forceinline__ bool is_neg_inf(double x) {
+  return __double_as_longlong(x) == (long long)0xfff0000000000000ull;
+}
+
+// --------------------------------------------------------- reductions --
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxnan(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_or(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);
+  return v;
+}
+
+// Workgroup-wide reductions in a fixed order (deterministic); `sh` needs kWaves slots.
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[w] = v;
+  __syncthreads();
+  float r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r = fmaxnan(r, sh[i]);
+  return r;
+}
+__device__ __forceinline__ double block_sum(double v, double* sh) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[w] = v;
+  __syncthreads();
+  double r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) r += sh[i];
+  return r;
+}
+
+// Exclusive scan of one double per thread across the workgroup, in thread
+// order; returns the exclusive prefix and writes the total. `sh` needs kWG + kWaves slots.
+__device__ __forceinline__ double block_exclusive_scan(double v, double* sh, double* total) {
+  const int t = threadIdx.x;
+  __syncthreads();
+  sh[t] = v;
+  __syncthreads();
+  // Hillis-Steele inclusive scan in shared memory (fixed order, deterministic).
+  for (int o = 1; o < kWG; o <<= 1) {
+    double add = t >= o ? sh[t - o] : 0.0;
+    __syncthreads();
+    sh[t] += add;
+    __syncthreads();
+  }
+  const double excl = t ? sh[t - 1] : 0.0;
+  *total = sh[kWG - 1];
+  __syncthreads();
+  return excl;
+}
+
+// fp64-grade exponential (device math library, < 1 ulp).
+__device__ __forceinline__ double exp64(double x) { return ::exp(x); }
+
+}  // namespace psi

@@ -1,0 +1,104 @@
+// Internal interface between the C ABI (capi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace psi {
+
+constexpr int kMaxK = 64;
+constexpr int kStatNV = 8;  // 16-byte vectors per thread in the fp32-grade statistics pass
+
+// Per (row, chunk) record of the fp32-grade statistics pass: chunk maximum of
+// the raw logits and sum of 2^((a - m) * c) with c = log2(e) / T (binary32),
+// accumulated in fp64. s is NaN when the chunk holds a NaN or +inf.
+struct StatRec {
+  float m;
+  uint32_t pad;
+  double s;
+};
+
+// Per (row, chunk) record of the greedy pass: maximum, lowest index holding
+// it, and a flag for NaN / +inf.
+struct ArgRec {
+  float v;
+  int32_t idx;
+  int32_t bad;
+  int32_t pad;
+};
+
+// Per (row, sub-block) record of the fp64-grade draft pass: sub-block maximum
+// and sum of exp((a - m_sb) / T).
+struct DraftRec {
+  float m;
+  uint32_t pad;
+  double s;
+};
+
+// Per (request, sub-block) record of the fp64-grade final-row pass.
+// Residual: sp = sum P-part, sq = sum Q-part, a / bq = the same sums over the
+// entries where the target part exceeds the draft part. Bonus: sp only.
+struct ResRec {
+  double sp, sq, a, bq;
+};
+
+// Per-request decision state written by the decide step.
+struct ReqState {
+  int32_t n;    // accepted prefix length (K = all accepted, bonus row)
+  int32_t err;  // 1 = request error (outputs already written)
+  float mp;     // exact maximum of the final target row
+  float mq;     // exact maximum of the final draft row (residual only)
+  double sp_hat, sq_hat;  // fp32-grade normalisers of those rows
+  double u_final;         // uniform of the final draw
+  double pad[3];
+};
+
+// Rows of one request: np target rows then nq draft rows.
+struct RowMap {
+  const char* p;
+  const char* q;
+  int np, nq;
+  int64_t V;
+  int esz;
+  __device__ __forceinline__ const char* row(int64_t sr) const {
+    const int64_t per = np + nq;
+    const int64_t b = sr / per;
+    const int i = (int)(sr - b * per);
+    return i < np ? p + ((b * np + i) * V) * esz : q + ((b * nq + (i - np)) * V) * esz;
+  }
+};
+
+struct LinCfg {
+  RowMap rows;  // np = K + 1, nq = K (linear) or np = 0, nq = K (draft only)
+  int64_t B;
+  int K;
+  int V;
+  int aligned;  // rows are 16-byte aligned and V is a multiple of the vector width
+  int nvec;     // 16-byte vectors per row (aligned path)
+  int nch32;    // chunks per row in the statistics pass
+  int nsb;      // sub-blocks per row in the fp64-grade passes
+  float c32;    // log2(e) / T rounded to binary32
+  double invT;  // 1 / T
+  Rng rng;
+  int fused;
+  int32_t* draft;
+  int32_t* out_tokens;
+  int32_t* out_len;
+  float* out_probs;
+  double* out_resid;
+  StatRec* st;
+  ArgRec* ar;
+  ReqState* rs;
+  ResRec* res;
+  DraftRec* dr;
+};
+
+// Launchers (linear.hip). Each returns hipSuccess or the launch error.
+hipError_t launch_linear_sampled(const LinCfg& c, int dtype, hipStream_t s);
+hipError_t launch_linear_greedy(const LinCfg& c, int dtype, hipStream_t s);
+hipError_t launch_draft_sampled(const LinCfg& c, int dtype, hipStream_t s);
+hipError_t launch_draft_greedy(const LinCfg& c, int dtype, hipStream_t s);
+
+}  // namespace psi

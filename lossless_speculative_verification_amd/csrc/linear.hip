@@ -1,0 +1,713 @@
+// Linear Psi-Spec verification, draft sampling and greedy mode on gfx950.
+//
+// Method ("Uno" research explainer, §3.3 Psi-Spec and §3.4 Linear Sampler):
+// draft x_i ~ q_i for every block position; accept x_i with probability
+// min(1, p_i(x_i) / q_i(x_i)); keep the longest accepted prefix; at the first
+// rejection draw from the normalised positive part of p - q; when every draft
+// survives draw one more token from the last target row.
+//
+// Pipeline (every kernel enqueued on the caller's stream, nothing allocated):
+//   k_stats32   one workgroup per (row, chunk): exact chunk maximum and the sum
+//               of 2^((a - m) * c) (binary32 exp2, fp64 accumulation) for every
+//               target and draft row -> log-normalisers good to ~1e-7, enough
+//               for the accept test.
+//   k_decide    one workgroup per request: row normalisers, p(x_i), q(x_i),
+//               Philox accept tests, wave ballot -> first rejection n.
+//   k_pass64    (sub-block, request): fp64 pass over the one row pair the
+//               final draw needs (p_n, q_n, or the bonus row p_K), per 1024-
+//               element sub-block sums.
+//   k_final     one workgroup per request: prefix over sub-block sums, fp64
+//               rescan of one sub-block, inverse-CDF pick, outputs.
+// Draft sampling uses k_draftpass (fp64 sub-block sums of a draft row) and
+// k_draftfinal (pick). Greedy mode (temperature 0) uses k_argmax and
+// k_greedy_decide. The final draws are done in fp64 because an inverse-CDF
+// pick over 151936 tokens must agree with an fp64 reference to ~1e-12 of the
+// total mass to give the same token; the accept test only needs ~1e-7.
+#include "kernels.hpp"
+
+namespace psi {
+
+// --------------------------------------------------------------- loads --
+// Loads NV vectors of one row: vector k of this thread is vector index
+// vfirst + k * STRIDE (16 bytes each) when aligned, else the same elements one
+// by one. Out-of-row elements read as -inf.
+template <int DT, bool AL, int NV, int STRIDE>
+__device__ __forceinline__ void load_vecs(const char* row, int V, int nvec, int64_t vfirst,
+                                          float (&x)[NV][Elem<DT>::kPerVec]) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  if constexpr (AL) {
+    const uint4* rp = (const uint4*)row;
+    uint4 v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t idx = vfirst + (int64_t)k * STRIDE;
+      v[k] = idx < nvec ? rp[idx] : make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) E::unpack(v[k], x[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const int64_t j = (vfirst + (int64_t)k * STRIDE) * EPV + e;
+        x[k][e] = j < V ? E::load1(row, j) : -INFINITY;
+      }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ float pairwise_sum(const float (&e)[N]) {
+  if constexpr (N == 8) {
+    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  } else {
+    return (e[0] + e[1]) + (e[2] + e[3]);
+  }
+}
+
+__device__ __forceinline__ const char* prow_of(const LinCfg& c, int64_t b, int i) {
+  return c.rows.p + ((b * (c.K + 1) + i) * (int64_t)c.V) * c.rows.esz;
+}
+__device__ __forceinline__ const char* qrow_of(const LinCfg& c, int64_t b, int i) {
+  return c.rows.q + ((b * c.K + i) * (int64_t)c.V) * c.rows.esz;
+}
+
+// ------------------------------------------------------ statistics pass --
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_stats32(LinCfg c) {
+  constexpr int EPV = Elem<DT>::kPerVec;
+  const int64_t item = blockIdx.x;
+  const int chunk = (int)(item % c.nch32);
+  const int64_t sr = item / c.nch32;
+  const char* row = c.rows.row(sr);
+  __shared__ float shf[kWaves];
+  __shared__ double shd[kWaves];
+  float x[kStatNV][EPV];
+  load_vecs<DT, AL, kStatNV, kWG>(row, c.V, c.nvec, (int64_t)chunk * kWG * kStatNV + threadIdx.x, x);
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kStatNV; ++k)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) m = fmaxnan(m, x[k][e]);
+  m = block_max(m, shf);
+  double s = 0.0;
+  if (!is_neg_inf(m)) {
+    // exp2(x*c - round(m*c)) = 2^((x-m)c) * 2^(mc_lo); the common factor
+    // 2^(mc_lo) is removed once per chunk in fp64.
+    const float mc_hi = m * c.c32;
+    const float mc_lo = fmaf(m, c.c32, -mc_hi);
+#pragma unroll
+    for (int k = 0; k < kStatNV; ++k) {
+      float e[EPV];
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(x[k][j], c.c32, -mc_hi));
+      s += (double)pairwise_sum(e);
+    }
+    s = block_sum(s, shd);
+    s *= ::exp2(-(double)mc_lo);
+  }
+  if (threadIdx.x == 0) {
+    StatRec r;
+    r.m = m;
+    r.pad = 0;
+    r.s = s;
+    c.st[item] = r;
+  }
+}
+
+// ---------------------------------------------------------- decide step --
+template <int DT>
+__global__ __launch_bounds__(kWG) void k_decide(LinCfg c) {
+  using E = Elem<DT>;
+  const int64_t b = blockIdx.x;
+  const int K = c.K, R = 2 * K + 1, t = threadIdx.x;
+  __shared__ float s_m[2 * kMaxK + 1];
+  __shared__ double s_S[2 * kMaxK + 1];
+  __shared__ int s_bad, s_n;
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  for (int i = t; i < R; i += kWG) {
+    const StatRec* rec = c.st + (b * R + i) * (int64_t)c.nch32;
+    float m = -INFINITY;
+    for (int ch = 0; ch < c.nch32; ++ch) m = fmaxnan(m, rec[ch].m);
+    double S = 0.0;
+    int bad = isnan(m) || isinf(m);  // NaN, +inf, or an all -inf row
+    if (!bad)
+      for (int ch = 0; ch < c.nch32; ++ch) {
+        const StatRec r = rec[ch];
+        if (isnan(r.s)) bad = 1;
+        else if (!is_neg_inf(r.m)) S += r.s * ::exp2(((double)r.m - (double)m) * (double)c.c32);
+      }
+    if (!(S > 0.0)) bad = 1;
+    s_m[i] = m;
+    s_S[i] = S;
+    if (bad) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  int acc = 1;
+  double P = 0.0, Q = 0.0;
+  if (t < K) {
+    const int x = c.draft[b * K + t];
+    if (x < 0 || x >= c.V) {
+      atomicOr(&s_bad, 1);
+    } else {
+      const float ap = E::load1(prow_of(c, b, t), x);
+      const float aq = E::load1(qrow_of(c, b, t), x);
+      P = ::exp(((double)ap - (double)s_m[t]) * c.invT - ::log(s_S[t]));
+      Q = ::exp(((double)aq - (double)s_m[K + 1 + t]) * c.invT - ::log(s_S[K + 1 + t]));
+      const double u = c.rng.u((uint32_t)b, (uint32_t)t, kDrawAccept);
+      acc = u * Q < P;
+    }
+  }
+  if (t < kWave) {
+    const unsigned long long rej = __ballot(t < K && !acc);
+    if (t == 0) s_n = rej ? (__ffsll((long long)rej) - 1) : K;
+  }
+  __syncthreads();
+  const int n = s_n;
+  if (s_bad) {
+    for (int i = t; i <= K; i += kWG) c.out_tokens[b * (K + 1) + i] = -1;
+    if (c.out_probs)
+      for (int i = t; i < 2 * K; i += kWG) c.out_probs[b * 2 * K + i] = 0.0f;
+    if (c.fused)
+      for (int i = t; i < K; i += kWG) c.draft[b * K + i] = -1;
+    if (t == 0) {
+      c.out_len[b] = -1;
+      if (c.out_resid) c.out_resid[b] = 0.0;
+      ReqState st = {};
+      st.err = 1;
+      c.rs[b] = st;
+    }
+    return;
+  }
+  if (t < K && c.out_probs) {
+    c.out_probs[(b * K + t) * 2 + 0] = (float)P;
+    c.out_probs[(b * K + t) * 2 + 1] = (float)Q;
+  }
+  if (t == 0) {
+    ReqState st = {};
+    st.n = n;
+    st.err = 0;
+    st.mp = s_m[n];
+    st.sp_hat = s_S[n];
+    st.mq = n < K ? s_m[K + 1 + n] : 0.0f;
+    st.sq_hat = n < K ? s_S[K + 1 + n] : 1.0;
+    st.u_final = c.rng.u((uint32_t)b, (uint32_t)n, kDrawFinal);
+    c.rs[b] = st;
+  }
+}
+
+// ------------------------------------------------- fp64 final-row pass --
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_pass64(LinCfg c) {
+  constexpr int EPV = Elem<DT>::kPerVec;
+  constexpr int VPL = kSB / (kWave * EPV);
+  const int64_t b = blockIdx.y;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int sb = blockIdx.x * kWaves + wave;
+  if (sb >= c.nsb) return;
+  const ReqState st = c.rs[b];
+  if (st.err) return;
+  const int K = c.K;
+  const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
+  ResRec out = {0.0, 0.0, 0.0, 0.0};
+  if (st.n == K) {
+    float x[VPL][EPV];
+    load_vecs<DT, AL, VPL, kWave>(prow_of(c, b, K), c.V, c.nvec, vfirst, x);
+    const double mp = st.mp;
+    double s = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) s += exp64(((double)x[v][e] - mp) * c.invT);
+    out.sp = wave_sum(s);
+  } else {
+    float xp[VPL][EPV], xq[VPL][EPV];
+    load_vecs<DT, AL, VPL, kWave>(prow_of(c, b, st.n), c.V, c.nvec, vfirst, xp);
+    load_vecs<DT, AL, VPL, kWave>(qrow_of(c, b, st.n), c.V, c.nvec, vfirst, xq);
+    const double mp = st.mp, mq = st.mq, sph = st.sp_hat, sqh = st.sq_hat;
+    double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const double ep = exp64(((double)xp[v][e] - mp) * c.invT);
+        const double eq = exp64(((double)xq[v][e] - mq) * c.invT);
+        sp += ep;
+        sq += eq;
+        if (ep * sqh > eq * sph) {
+          a += ep;
+          bq += eq;
+        }
+      }
+    out.sp = wave_sum(sp);
+    out.sq = wave_sum(sq);
+    out.a = wave_sum(a);
+    out.bq = wave_sum(bq);
+  }
+  if (lane == 0) c.res[b * c.nsb + sb] = out;
+}
+
+// --------------------------------------------- inverse-CDF pick helper --
+// Picks the smallest index j with (sum of weights up to and including j) >
+// target, given per-sub-block weights wsb(sb) and per-element weights w(j)
+// (fp64, index order). Sub-blocks are 1024 elements. Rounding differences
+// between the sub-block sums and the rescan are handled by falling back to
+// the last positive weight. Returns -1 only if every weight is zero.
+template <class WSB, class WEL>
+__device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, double* sh) {
+  __shared__ int s_sel;
+  __shared__ double s_pref;
+  const int t = threadIdx.x;
+  const int per = (nsb + kWG - 1) / kWG;
+  const int s0 = min(nsb, t * per), s1 = min(nsb, s0 + per);
+  double mine = 0.0;
+  for (int sb = s0; sb < s1; ++sb) mine += wsb(sb);
+  double total;
+  const double excl = block_exclusive_scan(mine, sh, &total);
+  if (t == 0) s_sel = 0x7fffffff;
+  __syncthreads();
+  {
+    double acc = excl;
+    for (int sb = s0; sb < s1; ++sb) {
+      const double w = wsb(sb);
+      if (w > 0.0 && acc + w > target) {
+        atomicMin(&s_sel, sb);
+        break;
+      }
+      acc += w;
+    }
+  }
+  __syncthreads();
+  if (s_sel == 0x7fffffff) {
+    // rounding left no crossing: take the last sub-block with positive weight
+    __syncthreads();
+    if (t == 0) s_sel = -1;
+    __syncthreads();
+    for (int sb = s0; sb < s1; ++sb)
+      if (wsb(sb) > 0.0) atomicMax(&s_sel, sb);
+    __syncthreads();
+    if (s_sel < 0) return -1;
+  }
+  const int sel = s_sel;
+  // exact prefix before the chosen sub-block, recomputed in one fixed order
+  if (sel >= s0 && sel < s1) {
+    double acc = excl;
+    for (int sb = s0; sb < sel; ++sb) acc += wsb(sb);
+    s_pref = acc;
+  }
+  __syncthreads();
+  const double tin = target - s_pref;
+  // rescan: thread t owns elements [sel*1024 + 4t, +4)
+  constexpr int EPT = kSB / kWG;
+  const int64_t j0 = (int64_t)sel * kSB + (int64_t)t * EPT;
+  double w[EPT];
+  double mine2 = 0.0;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    w[k] = (j0 + k < V) ? wel(j0 + k) : 0.0;
+    mine2 += w[k];
+  }
+  double tot2;
+  const double excl2 = block_exclusive_scan(mine2, sh, &tot2);
+  if (t == 0) s_sel = 0x7fffffff;
+  __syncthreads();
+  {
+    double acc = excl2;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      if (w[k] > 0.0 && acc + w[k] > tin) {
+        atomicMin(&s_sel, (int)(j0 + k));
+        break;
+      }
+      acc += w[k];
+    }
+  }
+  __syncthreads();
+  int j = s_sel;
+  if (j == 0x7fffffff) {
+    __syncthreads();
+    if (t == 0) s_sel = -1;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      if (w[k] > 0.0) atomicMax(&s_sel, (int)(j0 + k));
+    __syncthreads();
+    j = s_sel;
+  }
+  __syncthreads();
+  return j;
+}
+
+// ----------------------------------------------------------- final step --
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
+  using E = Elem<DT>;
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x, K = c.K;
+  const ReqState st = c.rs[b];
+  if (st.err) return;
+  const int n = st.n;
+  const bool bonus = n == K;
+  const int nsb = c.nsb;
+  const ResRec* rr = c.res + b * nsb;
+  __shared__ double sh[kWG + kWaves];
+  double Sp = 1.0, Sq = 1.0;
+  if (!bonus) {
+    double a = 0.0, q = 0.0;
+    for (int sb = t; sb < nsb; sb += kWG) {
+      a += rr[sb].sp;
+      q += rr[sb].sq;
+    }
+    Sp = block_sum(a, sh);
+    Sq = block_sum(q, sh);
+  }
+  const char* prow = prow_of(c, b, n);
+  const char* qrow = bonus ? prow : qrow_of(c, b, n);
+  const double mp = st.mp, mq = st.mq, invT = c.invT;
+  double resid = 0.0;
+  int mode = 0;  // 0: weights exp((a - mp)/T) of prow; 1: residual; 2: residual vanished -> P
+  if (!bonus) {
+    double mine = 0.0;
+    for (int sb = t; sb < nsb; sb += kWG) mine += fmax(0.0, rr[sb].a / Sp - rr[sb].bq / Sq);
+    resid = block_sum(mine, sh);
+    mode = resid > 0.0 ? 1 : 2;
+  }
+  int y;
+  if (mode == 1) {
+    y = pick_index(
+        nsb, c.V, st.u_final * resid, [&](int sb) { return fmax(0.0, rr[sb].a / Sp - rr[sb].bq / Sq); },
+        [&](int64_t j) {
+          const double ep = exp64(((double)E::load1(prow, j) - mp) * invT);
+          const double eq = exp64(((double)E::load1(qrow, j) - mq) * invT);
+          return fmax(0.0, ep / Sp - eq / Sq);
+        },
+        sh);
+  } else {
+    double W = 0.0;
+    {
+      double mine = 0.0;
+      for (int sb = t; sb < nsb; sb += kWG) mine += rr[sb].sp;
+      W = block_sum(mine, sh);
+    }
+    y = pick_index(
+        nsb, c.V, st.u_final * W, [&](int sb) { return rr[sb].sp; },
+        [&](int64_t j) { return exp64(((double)E::load1(prow, j) - mp) * invT); }, sh);
+  }
+  for (int i = t; i <= K; i += kWG) {
+    int v = -1;
+    if (i < n) v = c.draft[b * K + i];
+    else if (i == n) v = y;
+    c.out_tokens[b * (K + 1) + i] = v;
+  }
+  if (t == 0) {
+    c.out_len[b] = n;
+    if (c.out_resid) c.out_resid[b] = resid;
+  }
+}
+
+// ----------------------------------------------------- draft sampling --
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_draftpass(LinCfg c) {
+  constexpr int EPV = Elem<DT>::kPerVec;
+  constexpr int VPL = kSB / (kWave * EPV);
+  const int64_t qr = blockIdx.y;  // draft row in [0, B*K)
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int sb = blockIdx.x * kWaves + wave;
+  if (sb >= c.nsb) return;
+  const char* row = c.rows.q + (qr * (int64_t)c.V) * c.rows.esz;
+  float x[VPL][EPV];
+  load_vecs<DT, AL, VPL, kWave>(row, c.V, c.nvec, (int64_t)sb * (kSB / EPV) + lane, x);
+  float m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) m = fmaxnan(m, x[v][e]);
+  m = wave_max(m);
+  double s = 0.0;
+  if (!is_neg_inf(m)) {
+    const double md = m;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) s += exp64(((double)x[v][e] - md) * c.invT);
+    s = wave_sum(s);
+  }
+  if (lane == 0) {
+    DraftRec r;
+    r.m = m;
+    r.pad = 0;
+    r.s = s;
+    c.dr[qr * c.nsb + sb] = r;
+  }
+}
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_draftfinal(LinCfg c) {
+  using E = Elem<DT>;
+  const int64_t qr = blockIdx.x;
+  const int K = c.K, nsb = c.nsb, t = threadIdx.x;
+  const int64_t b = qr / K;
+  const int i = (int)(qr - b * K);
+  __shared__ int s_alive[kMaxK];
+  __shared__ int s_bad;
+  __shared__ float shf[kWaves];
+  __shared__ double sh[kWG + kWaves];
+  if (t < K) s_alive[t] = 0;
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  // every draft row of the request must be valid
+  const DraftRec* req = c.dr + b * K * (int64_t)nsb;
+  for (int idx = t; idx < K * nsb; idx += kWG) {
+    const DraftRec r = req[idx];
+    if (isnan(r.m) || (isinf(r.m) && r.m > 0.0f) || isnan(r.s)) atomicOr(&s_bad, 1);
+    if (!is_neg_inf(r.m)) atomicOr(&s_alive[idx / nsb], 1);
+  }
+  __syncthreads();
+  int bad = s_bad;
+  for (int k = 0; k < K; ++k) bad |= !s_alive[k];
+  if (bad) {
+    if (t == 0) c.draft[qr] = -1;
+    return;
+  }
+  const DraftRec* rec = c.dr + qr * nsb;
+  float m = -INFINITY;
+  for (int sb = t; sb < nsb; sb += kWG) m = fmaxnan(m, rec[sb].m);
+  m = block_max(m, shf);
+  const double md = m, invT = c.invT;
+  const char* row = c.rows.q + (qr * (int64_t)c.V) * c.rows.esz;
+  auto wsb = [&](int sb) {
+    const DraftRec r = rec[sb];
+    return is_neg_inf(r.m) ? 0.0 : r.s * exp64(((double)r.m - md) * invT);
+  };
+  double W;
+  {
+    double mine = 0.0;
+    for (int sb = t; sb < nsb; sb += kWG) mine += wsb(sb);
+    W = block_sum(mine, sh);
+  }
+  const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
+  const int y = pick_index(
+      nsb, c.V, u * W, wsb,
+      [&](int64_t j) {
+        const DraftRec r = rec[j / kSB];
+        const double f = exp64(((double)r.m - md) * invT);
+        return exp64(((double)E::load1(row, j) - (double)r.m) * invT) * f;
+      },
+      sh);
+  if (t == 0) c.draft[qr] = y;
+}
+
+// ------------------------------------------------------------- greedy --
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_argmax(LinCfg c) {
+  constexpr int EPV = Elem<DT>::kPerVec;
+  const int64_t item = blockIdx.x;
+  const int chunk = (int)(item % c.nch32);
+  const int64_t sr = item / c.nch32;
+  const char* row = c.rows.row(sr);
+  float x[kStatNV][EPV];
+  const int64_t vfirst = (int64_t)chunk * kWG * kStatNV + threadIdx.x;
+  load_vecs<DT, AL, kStatNV, kWG>(row, c.V, c.nvec, vfirst, x);
+  float best = -INFINITY;
+  int idx = 0x7fffffff, bad = 0;
+#pragma unroll
+  for (int k = 0; k < kStatNV; ++k)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const float v = x[k][e];
+      const int j = (int)((vfirst + (int64_t)k * kWG) * EPV + e);
+      bad |= isnan(v) || (isinf(v) && v > 0.0f);
+      if (v > best) {
+        best = v;
+        idx = j;
+      }
+    }
+  // workgroup reduction: larger value first, then lower index
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(best, o);
+    const int oi = __shfl_xor(idx, o);
+    if (ov > best || (ov == best && oi < idx)) {
+      best = ov;
+      idx = oi;
+    }
+  }
+  bad = wave_or(bad);
+  __shared__ float sv[kWaves];
+  __shared__ int si[kWaves], sb_[kWaves];
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sv[w] = best;
+    si[w] = idx;
+    sb_[w] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ArgRec r;
+    r.v = sv[0];
+    r.idx = si[0];
+    r.bad = sb_[0];
+    for (int k = 1; k < kWaves; ++k) {
+      if (sv[k] > r.v || (sv[k] == r.v && si[k] < r.idx)) {
+        r.v = sv[k];
+        r.idx = si[k];
+      }
+      r.bad |= sb_[k];
+    }
+    r.pad = 0;
+    c.ar[item] = r;
+  }
+}
+
+// combine the chunk records of one row: argmax (lowest index on ties), bad flag
+__device__ __forceinline__ int row_argmax(const ArgRec* rec, int nch, int* bad) {
+  float v = -INFINITY;
+  int idx = 0x7fffffff, bd = 0;
+  for (int ch = 0; ch < nch; ++ch) {
+    const ArgRec r = rec[ch];
+    bd |= r.bad;
+    if (r.v > v || (r.v == v && r.idx < idx)) {
+      v = r.v;
+      idx = r.idx;
+    }
+  }
+  if (is_neg_inf(v)) bd = 1;  // entirely -inf
+  *bad = bd;
+  return idx;
+}
+
+__global__ __launch_bounds__(kWG) void k_greedy_decide(LinCfg c) {
+  const int64_t b = blockIdx.x;
+  const int K = c.K, R = 2 * K + 1, t = threadIdx.x;
+  __shared__ int s_g[2 * kMaxK + 1];
+  __shared__ int s_bad, s_n;
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  for (int i = t; i < R; i += kWG) {
+    int bad;
+    s_g[i] = row_argmax(c.ar + (b * R + i) * (int64_t)c.nch32, c.nch32, &bad);
+    if (bad) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  int acc = 1, x = 0;
+  if (t < K) {
+    x = c.fused ? s_g[K + 1 + t] : c.draft[b * K + t];
+    if (x < 0 || x >= c.V) atomicOr(&s_bad, 1);
+    acc = x == s_g[t];
+  }
+  if (t < kWave) {
+    const unsigned long long rej = __ballot(t < K && !acc);
+    if (t == 0) s_n = rej ? (__ffsll((long long)rej) - 1) : K;
+  }
+  __syncthreads();
+  if (s_bad) {
+    for (int i = t; i <= K; i += kWG) c.out_tokens[b * (K + 1) + i] = -1;
+    if (c.out_probs)
+      for (int i = t; i < 2 * K; i += kWG) c.out_probs[b * 2 * K + i] = 0.0f;
+    if (c.fused)
+      for (int i = t; i < K; i += kWG) c.draft[b * K + i] = -1;
+    if (t == 0) {
+      c.out_len[b] = -1;
+      if (c.out_resid) c.out_resid[b] = 0.0;
+    }
+    return;
+  }
+  const int n = s_n;
+  if (t < K) {
+    if (c.fused) c.draft[b * K + t] = x;
+    if (c.out_probs) {
+      c.out_probs[(b * K + t) * 2 + 0] = x == s_g[t] ? 1.0f : 0.0f;
+      c.out_probs[(b * K + t) * 2 + 1] = x == s_g[K + 1 + t] ? 1.0f : 0.0f;
+    }
+  }
+  __syncthreads();
+  for (int i = t; i <= K; i += kWG) {
+    int v = -1;
+    if (i < n) v = c.fused ? s_g[K + 1 + i] : c.draft[b * K + i];
+    else if (i == n) v = s_g[n];
+    c.out_tokens[b * (K + 1) + i] = v;
+  }
+  if (t == 0) {
+    c.out_len[b] = n;
+    if (c.out_resid) c.out_resid[b] = 0.0;
+  }
+}
+
+__global__ __launch_bounds__(kWG) void k_greedy_draft(LinCfg c) {
+  const int64_t b = blockIdx.x;
+  const int K = c.K, t = threadIdx.x;
+  __shared__ int s_bad;
+  __shared__ int s_g[kMaxK];
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  for (int i = t; i < K; i += kWG) {
+    int bad;
+    s_g[i] = row_argmax(c.ar + (b * K + i) * (int64_t)c.nch32, c.nch32, &bad);
+    if (bad) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  for (int i = t; i < K; i += kWG) c.draft[b * K + i] = s_bad ? -1 : s_g[i];
+}
+
+// ------------------------------------------------------------ launchers --
+template <int DT, bool AL>
+static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
+  if (c.fused) {
+    LinCfg d = c;
+    d.rows.np = 0;
+    hipLaunchKernelGGL((k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)(c.B * c.K)), dim3(kWG),
+                       0, s, d);
+    hipLaunchKernelGGL((k_draftfinal<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kWG), 0, s, d);
+  }
+  const int64_t rows = c.B * (2 * c.K + 1);
+  hipLaunchKernelGGL((k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
+  hipLaunchKernelGGL((k_decide<DT>), dim3((unsigned)c.B), dim3(kWG), 0, s, c);
+  hipLaunchKernelGGL((k_pass64<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)c.B), dim3(kWG), 0, s, c);
+  hipLaunchKernelGGL((k_final<DT, AL>), dim3((unsigned)c.B), dim3(kWG), 0, s, c);
+  return hipGetLastError();
+}
+
+template <int DT, bool AL>
+static hipError_t linear_greedy_t(const LinCfg& c, hipStream_t s) {
+  const int64_t rows = c.B * (2 * c.K + 1);
+  hipLaunchKernelGGL((k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
+  hipLaunchKernelGGL(k_greedy_decide, dim3((unsigned)c.B), dim3(kWG), 0, s, c);
+  return hipGetLastError();
+}
+
+template <int DT, bool AL>
+static hipError_t draft_sampled_t(const LinCfg& c, hipStream_t s) {
+  hipLaunchKernelGGL((k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)(c.B * c.K)), dim3(kWG), 0,
+                     s, c);
+  hipLaunchKernelGGL((k_draftfinal<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kWG), 0, s, c);
+  return hipGetLastError();
+}
+
+template <int DT, bool AL>
+static hipError_t draft_greedy_t(const LinCfg& c, hipStream_t s) {
+  const int64_t rows = c.B * c.K;
+  hipLaunchKernelGGL((k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
+  hipLaunchKernelGGL(k_greedy_draft, dim3((unsigned)c.B), dim3(kWG), 0, s, c);
+  return hipGetLastError();
+}
+
+#define PSI_DISPATCH(fn, dtype, aligned, ...)                                      \
+  ((dtype) == kBF16 ? ((aligned) ? fn<kBF16, true>(__VA_ARGS__) : fn<kBF16, false>(__VA_ARGS__)) \
+                    : ((aligned) ? fn<kF32, true>(__VA_ARGS__) : fn<kF32, false>(__VA_ARGS__)))
+
+hipError_t launch_linear_sampled(const LinCfg& c, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(linear_sampled_t, dtype, c.aligned, c, s);
+}
+hipError_t launch_linear_greedy(const LinCfg& c, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(linear_greedy_t, dtype, c.aligned, c, s);
+}
+hipError_t launch_draft_sampled(const LinCfg& c, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(draft_sampled_t, dtype, c.aligned, c, s);
+}
+hipError_t launch_draft_greedy(const LinCfg& c, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(draft_greedy_t, dtype, c.aligned, c, s);
+}
+
+}  // namespace psi

@@ -1,0 +1,109 @@
+"""The C-ABI library loads on a host without a GPU, exports every entry point
+declared in include/psispec.h, and rejects bad arguments synchronously (host
+validation only; no kernel is launched by these tests)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "psispec.h")
+
+
+@pytest.fixture(scope="module")
+def psi():
+    import lossless_speculative_verification_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psispec_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(psi):
+    names = declared_functions()
+    assert {"psispec_draft_sample", "psispec_verify_linear", "psispec_verify_tree",
+            "psispec_workspace_bytes", "psispec_strerror", "psispec_version", "psispec_tree_depth"} <= set(names)
+    lib = ctypes.CDLL(psi.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_params_layout_matches_header(psi):
+    assert ctypes.sizeof(psi.Params) == 32
+    assert psi.Params.seed.offset == 16 and psi.Params.step.offset == 24
+
+
+def test_strerror_and_version(psi):
+    assert psi.strerror(0) == "success"
+    for code in (-1, -2, -3, -4):
+        assert psi.strerror(code) and psi.strerror(code) != "unknown status"
+    assert psi.version() >= 100
+
+
+def test_workspace_bytes(psi):
+    a = psi.workspace_bytes(256, 17, 151936, psi.DTYPE_BF16)
+    assert a > 0 and a % 256 == 0
+    assert psi.workspace_bytes(512, 17, 151936, psi.DTYPE_BF16) > a
+    assert psi.workspace_bytes(0, 17, 151936, 1) == 0
+    assert psi.workspace_bytes(1, 0, 10, 1) == 0
+    assert psi.workspace_bytes(1, 3, 10, 7) == 0
+
+
+def test_tree_depth(psi):
+    import synth
+    assert psi.tree_depth(synth.branch_chain_parent(4, 8)) == 8
+    assert psi.tree_depth([-1, 0, 0, 1]) == 3
+    assert psi.tree_depth([-1, 2]) == psi.EINVAL
+    assert psi.tree_depth(np.arange(-1, 99)) == psi.EUNSUPPORTED  # depth 100 > 64
+
+
+def _call_linear(psi, B=2, K=3, V=64, dtype=1, prm=None, ws_bytes=1 << 20, null=None, ws_addr=1 << 20):
+    prm = prm if prm is not None else psi.make_params()
+    fake = {k: ctypes.c_void_p(0x10000000 + 0x1000 * i) for i, k in
+            enumerate(["p", "q", "d", "tok", "len", "probs", "resid"])}
+    if null:
+        fake[null] = None
+    return psi.lib.psispec_verify_linear(fake["p"], fake["q"], dtype, B, K, V, fake["d"], ctypes.byref(prm),
+                                         fake["tok"], fake["len"], fake["probs"], fake["resid"],
+                                         ctypes.c_void_p(ws_addr), ws_bytes, None)
+
+
+def test_linear_argument_errors(psi):
+    for k in ("p", "q", "d", "tok", "len"):
+        assert _call_linear(psi, null=k) == psi.EINVAL
+    assert _call_linear(psi, B=0) == psi.EINVAL
+    assert _call_linear(psi, K=0) == psi.EINVAL
+    assert _call_linear(psi, V=0) == psi.EINVAL
+    assert _call_linear(psi, K=65) == psi.EUNSUPPORTED
+    assert _call_linear(psi, dtype=5) == psi.EUNSUPPORTED
+    assert _call_linear(psi, prm=psi.make_params(temperature=-1.0)) == psi.EINVAL
+    assert _call_linear(psi, prm=psi.make_params(temperature=float("nan"))) == psi.EINVAL
+    assert _call_linear(psi, prm=psi.make_params(top_p=0.0)) == psi.EINVAL
+    assert _call_linear(psi, prm=psi.make_params(top_p=1.5)) == psi.EINVAL
+    assert _call_linear(psi, prm=psi.make_params(top_k=-2)) == psi.EINVAL
+    assert _call_linear(psi, ws_bytes=16) == psi.EWORKSPACE
+    assert _call_linear(psi, ws_addr=(1 << 20) + 8) == psi.EINVAL
+
+
+def test_draft_argument_errors(psi):
+    prm = psi.make_params()
+    f = ctypes.c_void_p(0x20000000)
+    ws = ctypes.c_void_p(1 << 20)
+    assert psi.lib.psispec_draft_sample(None, 1, 2, 3, 64, ctypes.byref(prm), f, ws, 1 << 20, None) == psi.EINVAL
+    assert psi.lib.psispec_draft_sample(f, 1, 2, 3, 64, None, f, ws, 1 << 20, None) == psi.EINVAL
+    assert psi.lib.psispec_draft_sample(f, 1, 2, 3, 64, ctypes.byref(prm), f, ws, 8, None) == psi.EWORKSPACE
+    assert psi.lib.psispec_draft_sample(f, 1, 2, 99, 64, ctypes.byref(prm), f, ws, 1 << 20, None) == psi.EUNSUPPORTED
+
+
+def test_binding_has_no_fallback(psi):
+    """The binding is marshalling only: it calls the library for every step."""
+    src = open(os.path.join(ROOT, "lossless_speculative_verification_amd", "__init__.py")).read()
+    assert "oracle" not in src
+    assert "softmax" not in src and "torch.exp" not in src
