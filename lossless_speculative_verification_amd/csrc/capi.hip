@@ -3,7 +3,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/psispec.h"
+#include "psispec.h"
 #include "kernels.hpp"
 
 namespace psi {
@@ -79,6 +79,7 @@ inline void fill_common(LinCfg& c, const void* p, const void* q, int dtype, int6
   const double T = (double)prm->temperature;
   c.invT = T > 0.0 ? 1.0 / T : 0.0;
   c.c32 = T > 0.0 ? (float)(1.4426950408889634074 / T) : 0.0f;
+  c.c64 = T > 0.0 ? 1.4426950408889634074 / T : 0.0;
   c.rng.k0 = (uint32_t)(prm->seed & 0xffffffffu);
   c.rng.k1 = (uint32_t)(prm->seed >> 32);
   c.rng.step = prm->step;
@@ -143,8 +144,18 @@ int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype,
   c.out_len = out_len;
   c.out_probs = out_probs;
   c.out_resid = out_resid_mass;
-  const hipError_t e = params->temperature == 0.0f ? launch_linear_greedy(c, dtype, stream)
-                                                   : launch_linear_sampled(c, dtype, stream);
+  hipError_t e;
+  if (params->temperature == 0.0f) {
+    e = launch_linear_greedy(c, dtype, stream);
+  } else {
+    e = hipSuccess;
+    if (c.fused) {
+      LinCfg d = c;
+      d.rows.np = 0;
+      e = launch_draft_sampled(d, dtype, stream);
+    }
+    if (e == hipSuccess) e = launch_linear_sampled(c, dtype, stream);
+  }
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 

@@ -81,6 +81,7 @@ struct LinCfg {
   int nsb;      // sub-blocks per row in the fp64-grade passes
   float c32;    // log2(e) / T rounded to binary32
   double invT;  // 1 / T
+  double c64;   // log2(e) / T in fp64
   Rng rng;
   int fused;
   int32_t* draft;
@@ -100,5 +101,6 @@ hipError_t launch_linear_sampled(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_linear_greedy(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_draft_sampled(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_draft_greedy(const LinCfg& c, int dtype, hipStream_t s);
+
 
 }  // namespace psi

@@ -23,55 +23,9 @@
 // k_greedy_decide. The final draws are done in fp64 because an inverse-CDF
 // pick over 151936 tokens must agree with an fp64 reference to ~1e-12 of the
 // total mass to give the same token; the accept test only needs ~1e-7.
-#include "kernels.hpp"
+#include "rowops.hpp"
 
 namespace psi {
-
-// --------------------------------------------------------------- loads --
-// Loads NV vectors of one row: vector k of this thread is vector index
-// vfirst + k * STRIDE (16 bytes each) when aligned, else the same elements one
-// by one. Out-of-row elements read as -inf.
-template <int DT, bool AL, int NV, int STRIDE>
-__device__ __forceinline__ void load_vecs(const char* row, int V, int nvec, int64_t vfirst,
-                                          float (&x)[NV][Elem<DT>::kPerVec]) {
-  using E = Elem<DT>;
-  constexpr int EPV = E::kPerVec;
-  if constexpr (AL) {
-    const uint4* rp = (const uint4*)row;
-    uint4 v[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int64_t idx = vfirst + (int64_t)k * STRIDE;
-      v[k] = idx < nvec ? rp[idx] : make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
-    }
-#pragma unroll
-    for (int k = 0; k < NV; ++k) E::unpack(v[k], x[k]);
-  } else {
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const int64_t j = (vfirst + (int64_t)k * STRIDE) * EPV + e;
-        x[k][e] = j < V ? E::load1(row, j) : -INFINITY;
-      }
-  }
-}
-
-template <int N>
-__device__ __forceinline__ float pairwise_sum(const float (&e)[N]) {
-  if constexpr (N == 8) {
-    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-  } else {
-    return (e[0] + e[1]) + (e[2] + e[3]);
-  }
-}
-
-__device__ __forceinline__ const char* prow_of(const LinCfg& c, int64_t b, int i) {
-  return c.rows.p + ((b * (c.K + 1) + i) * (int64_t)c.V) * c.rows.esz;
-}
-__device__ __forceinline__ const char* qrow_of(const LinCfg& c, int64_t b, int i) {
-  return c.rows.q + ((b * c.K + i) * (int64_t)c.V) * c.rows.esz;
-}
 
 // ------------------------------------------------------ statistics pass --
 template <int DT, bool AL>
@@ -220,7 +174,7 @@ __global__ __launch_bounds__(kWG) void k_pass64(LinCfg c) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) s += exp64(((double)x[v][e] - mp) * c.invT);
+      for (int e = 0; e < EPV; ++e) s += exp2_poly(((double)x[v][e] - mp) * c.c64);
     out.sp = wave_sum(s);
   } else {
     float xp[VPL][EPV], xq[VPL][EPV];
@@ -232,8 +186,8 @@ __global__ __launch_bounds__(kWG) void k_pass64(LinCfg c) {
     for (int v = 0; v < VPL; ++v)
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
-        const double ep = exp64(((double)xp[v][e] - mp) * c.invT);
-        const double eq = exp64(((double)xq[v][e] - mq) * c.invT);
+        const double ep = exp2_poly(((double)xp[v][e] - mp) * c.c64);
+        const double eq = exp2_poly(((double)xq[v][e] - mq) * c.c64);
         sp += ep;
         sq += eq;
         if (ep * sqh > eq * sph) {
@@ -247,97 +201,6 @@ __global__ __launch_bounds__(kWG) void k_pass64(LinCfg c) {
     out.bq = wave_sum(bq);
   }
   if (lane == 0) c.res[b * c.nsb + sb] = out;
-}
-
-// --------------------------------------------- inverse-CDF pick helper --
-// Picks the smallest index j with (sum of weights up to and including j) >
-// target, given per-sub-block weights wsb(sb) and per-element weights w(j)
-// (fp64, index order). Sub-blocks are 1024 elements. Rounding differences
-// between the sub-block sums and the rescan are handled by falling back to
-// the last positive weight. Returns -1 only if every weight is zero.
-template <class WSB, class WEL>
-__device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, double* sh) {
-  __shared__ int s_sel;
-  __shared__ double s_pref;
-  const int t = threadIdx.x;
-  const int per = (nsb + kWG - 1) / kWG;
-  const int s0 = min(nsb, t * per), s1 = min(nsb, s0 + per);
-  double mine = 0.0;
-  for (int sb = s0; sb < s1; ++sb) mine += wsb(sb);
-  double total;
-  const double excl = block_exclusive_scan(mine, sh, &total);
-  if (t == 0) s_sel = 0x7fffffff;
-  __syncthreads();
-  {
-    double acc = excl;
-    for (int sb = s0; sb < s1; ++sb) {
-      const double w = wsb(sb);
-      if (w > 0.0 && acc + w > target) {
-        atomicMin(&s_sel, sb);
-        break;
-      }
-      acc += w;
-    }
-  }
-  __syncthreads();
-  if (s_sel == 0x7fffffff) {
-    // rounding left no crossing: take the last sub-block with positive weight
-    __syncthreads();
-    if (t == 0) s_sel = -1;
-    __syncthreads();
-    for (int sb = s0; sb < s1; ++sb)
-      if (wsb(sb) > 0.0) atomicMax(&s_sel, sb);
-    __syncthreads();
-    if (s_sel < 0) return -1;
-  }
-  const int sel = s_sel;
-  // exact prefix before the chosen sub-block, recomputed in one fixed order
-  if (sel >= s0 && sel < s1) {
-    double acc = excl;
-    for (int sb = s0; sb < sel; ++sb) acc += wsb(sb);
-    s_pref = acc;
-  }
-  __syncthreads();
-  const double tin = target - s_pref;
-  // rescan: thread t owns elements [sel*1024 + 4t, +4)
-  constexpr int EPT = kSB / kWG;
-  const int64_t j0 = (int64_t)sel * kSB + (int64_t)t * EPT;
-  double w[EPT];
-  double mine2 = 0.0;
-#pragma unroll
-  for (int k = 0; k < EPT; ++k) {
-    w[k] = (j0 + k < V) ? wel(j0 + k) : 0.0;
-    mine2 += w[k];
-  }
-  double tot2;
-  const double excl2 = block_exclusive_scan(mine2, sh, &tot2);
-  if (t == 0) s_sel = 0x7fffffff;
-  __syncthreads();
-  {
-    double acc = excl2;
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      if (w[k] > 0.0 && acc + w[k] > tin) {
-        atomicMin(&s_sel, (int)(j0 + k));
-        break;
-      }
-      acc += w[k];
-    }
-  }
-  __syncthreads();
-  int j = s_sel;
-  if (j == 0x7fffffff) {
-    __syncthreads();
-    if (t == 0) s_sel = -1;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < EPT; ++k)
-      if (w[k] > 0.0) atomicMax(&s_sel, (int)(j0 + k));
-    __syncthreads();
-    j = s_sel;
-  }
-  __syncthreads();
-  return j;
 }
 
 // ----------------------------------------------------------- final step --
@@ -365,7 +228,7 @@ __global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
   }
   const char* prow = prow_of(c, b, n);
   const char* qrow = bonus ? prow : qrow_of(c, b, n);
-  const double mp = st.mp, mq = st.mq, invT = c.invT;
+  const double mp = st.mp, mq = st.mq, c64 = c.c64;
   double resid = 0.0;
   int mode = 0;  // 0: weights exp((a - mp)/T) of prow; 1: residual; 2: residual vanished -> P
   if (!bonus) {
@@ -379,8 +242,8 @@ __global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
     y = pick_index(
         nsb, c.V, st.u_final * resid, [&](int sb) { return fmax(0.0, rr[sb].a / Sp - rr[sb].bq / Sq); },
         [&](int64_t j) {
-          const double ep = exp64(((double)E::load1(prow, j) - mp) * invT);
-          const double eq = exp64(((double)E::load1(qrow, j) - mq) * invT);
+          const double ep = exp2_poly(((double)E::load1(prow, j) - mp) * c64);
+          const double eq = exp2_poly(((double)E::load1(qrow, j) - mq) * c64);
           return fmax(0.0, ep / Sp - eq / Sq);
         },
         sh);
@@ -393,7 +256,7 @@ __global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
     }
     y = pick_index(
         nsb, c.V, st.u_final * W, [&](int sb) { return rr[sb].sp; },
-        [&](int64_t j) { return exp64(((double)E::load1(prow, j) - mp) * invT); }, sh);
+        [&](int64_t j) { return exp2_poly(((double)E::load1(prow, j) - mp) * c64); }, sh);
   }
   for (int i = t; i <= K; i += kWG) {
     int v = -1;
@@ -654,13 +517,6 @@ __global__ __launch_bounds__(kWG) void k_greedy_draft(LinCfg c) {
 // ------------------------------------------------------------ launchers --
 template <int DT, bool AL>
 static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
-  if (c.fused) {
-    LinCfg d = c;
-    d.rows.np = 0;
-    hipLaunchKernelGGL((k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)(c.B * c.K)), dim3(kWG),
-                       0, s, d);
-    hipLaunchKernelGGL((k_draftfinal<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kWG), 0, s, d);
-  }
   const int64_t rows = c.B * (2 * c.K + 1);
   hipLaunchKernelGGL((k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
   hipLaunchKernelGGL((k_decide<DT>), dim3((unsigned)c.B), dim3(kWG), 0, s, c);

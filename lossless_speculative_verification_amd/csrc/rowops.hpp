@@ -1,0 +1,179 @@
+// Row access and inverse-CDF helpers shared by the verification kernels.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace psi {
+
+// --------------------------------------------------------------- loads --
+// Loads NV vectors of one row: vector k of this thread is vector index
+// vfirst + k * STRIDE (16 bytes each) when aligned, else the same elements one
+// by one. Out-of-row elements read as -inf.
+template <int DT, bool AL, int NV, int STRIDE>
+__device__ __forceinline__ void load_vecs(const char* row, int V, int nvec, int64_t vfirst,
+                                          float (&x)[NV][Elem<DT>::kPerVec]) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  if constexpr (AL) {
+    const uint4* rp = (const uint4*)row;
+    uint4 v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t idx = vfirst + (int64_t)k * STRIDE;
+      v[k] = idx < nvec ? rp[idx] : make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) E::unpack(v[k], x[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const int64_t j = (vfirst + (int64_t)k * STRIDE) * EPV + e;
+        x[k][e] = j < V ? E::load1(row, j) : -INFINITY;
+      }
+  }
+}
+
+// Raw 16-byte vectors of one row (same element placement as load_vecs); the
+// unaligned path gathers element by element and packs them the same way.
+template <int DT, bool AL, int NV, int STRIDE>
+__device__ __forceinline__ void load_raw(const char* row, int V, int nvec, int64_t vfirst, uint4 (&v)[NV]) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  if constexpr (AL) {
+    const uint4* rp = (const uint4*)row;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t idx = vfirst + (int64_t)k * STRIDE;
+      v[k] = idx < nvec ? rp[idx] : make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (DT == kBF16) {
+          const int64_t j0 = (vfirst + (int64_t)k * STRIDE) * EPV + 2 * q;
+          const uint32_t lo = j0 < V ? (uint32_t)((const uint16_t*)row)[j0] : 0xff80u;
+          const uint32_t hi = j0 + 1 < V ? (uint32_t)((const uint16_t*)row)[j0 + 1] : 0xff80u;
+          w[q] = lo | (hi << 16);
+        } else {
+          const int64_t j = (vfirst + (int64_t)k * STRIDE) * EPV + q;
+          w[q] = j < V ? ((const uint32_t*)row)[j] : 0xff800000u;
+        }
+      }
+      v[k] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ float pairwise_sum(const float (&e)[N]) {
+  if constexpr (N == 8) {
+    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  } else {
+    return (e[0] + e[1]) + (e[2] + e[3]);
+  }
+}
+
+__device__ __forceinline__ const char* prow_of(const LinCfg& c, int64_t b, int i) {
+  return c.rows.p + ((b * (c.K + 1) + i) * (int64_t)c.V) * c.rows.esz;
+}
+__device__ __forceinline__ const char* qrow_of(const LinCfg& c, int64_t b, int i) {
+  return c.rows.q + ((b * c.K + i) * (int64_t)c.V) * c.rows.esz;
+}
+
+// --------------------------------------------- inverse-CDF pick helper --
+// Picks the smallest index j with (sum of weights up to and including j) >
+// target, given per-sub-block weights wsb(sb) and per-element weights w(j)
+// (fp64, index order). Sub-blocks are 1024 elements. Rounding differences
+// between the sub-block sums and the rescan are handled by falling back to
+// the last positive weight. Returns -1 only if every weight is zero.
+template <class WSB, class WEL>
+__device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, double* sh) {
+  __shared__ int s_sel;
+  __shared__ double s_pref;
+  const int t = threadIdx.x;
+  const int per = (nsb + kWG - 1) / kWG;
+  const int s0 = min(nsb, t * per), s1 = min(nsb, s0 + per);
+  double mine = 0.0;
+  for (int sb = s0; sb < s1; ++sb) mine += wsb(sb);
+  double total;
+  const double excl = block_exclusive_scan(mine, sh, &total);
+  if (t == 0) s_sel = 0x7fffffff;
+  __syncthreads();
+  {
+    double acc = excl;
+    for (int sb = s0; sb < s1; ++sb) {
+      const double w = wsb(sb);
+      if (w > 0.0 && acc + w > target) {
+        atomicMin(&s_sel, sb);
+        break;
+      }
+      acc += w;
+    }
+  }
+  __syncthreads();
+  if (s_sel == 0x7fffffff) {
+    // rounding left no crossing: take the last sub-block with positive weight
+    __syncthreads();
+    if (t == 0) s_sel = -1;
+    __syncthreads();
+    for (int sb = s0; sb < s1; ++sb)
+      if (wsb(sb) > 0.0) atomicMax(&s_sel, sb);
+    __syncthreads();
+    if (s_sel < 0) return -1;
+  }
+  const int sel = s_sel;
+  // exact prefix before the chosen sub-block, recomputed in one fixed order
+  if (sel >= s0 && sel < s1) {
+    double acc = excl;
+    for (int sb = s0; sb < sel; ++sb) acc += wsb(sb);
+    s_pref = acc;
+  }
+  __syncthreads();
+  const double tin = target - s_pref;
+  // rescan: thread t owns elements [sel*1024 + 4t, +4)
+  constexpr int EPT = kSB / kWG;
+  const int64_t j0 = (int64_t)sel * kSB + (int64_t)t * EPT;
+  double w[EPT];
+  double mine2 = 0.0;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    w[k] = (j0 + k < V) ? wel(j0 + k) : 0.0;
+    mine2 += w[k];
+  }
+  double tot2;
+  const double excl2 = block_exclusive_scan(mine2, sh, &tot2);
+  if (t == 0) s_sel = 0x7fffffff;
+  __syncthreads();
+  {
+    double acc = excl2;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      if (w[k] > 0.0 && acc + w[k] > tin) {
+        atomicMin(&s_sel, (int)(j0 + k));
+        break;
+      }
+      acc += w[k];
+    }
+  }
+  __syncthreads();
+  int j = s_sel;
+  if (j == 0x7fffffff) {
+    __syncthreads();
+    if (t == 0) s_sel = -1;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      if (w[k] > 0.0) atomicMax(&s_sel, (int)(j0 + k));
+    __syncthreads();
+    j = s_sel;
+  }
+  __syncthreads();
+  return j;
+}
+
+}  // namespace psi
