@@ -29,8 +29,9 @@
  *             re-entrant when they use distinct workspaces; two calls that
  *             share a workspace must be ordered on one stream.
  * Layout      Logit tensors are contiguous row-major: a row is V consecutive
- *             values of `dtype`. Device pointers must be 16-byte aligned; the
- *             workspace must be 256-byte aligned.
+ *             values of `dtype`. Rows that are 16-byte aligned take the
+ *             vectorised path, others a slower element-wise one; the workspace
+ *             must be 256-byte aligned.
  * dtype       PSISPEC_DTYPE_F32 (IEEE binary32) or PSISPEC_DTYPE_BF16
  *             (bfloat16, upper half of a binary32).
  * Errors      Argument errors are returned synchronously (negative codes
@@ -57,11 +58,12 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define PSISPEC_OK            0
 #define PSISPEC_EINVAL       -1 /* null pointer, size <= 0, temperature < 0 or not finite,
-                                   top_p outside (0, 1], top_k outside [0, V], misaligned
-                                   pointer, malformed tree topology */
+                                   top_p outside (0, 1], top_k < 0, workspace not 256-byte
+                                   aligned, malformed tree topology */
 #define PSISPEC_EUNSUPPORTED -2 /* dtype other than F32/BF16, K or tree depth > 64,
-                                   tree with more than 256 nodes, top_p < 1 with
-                                   top_k == 0 or top_k > 1024 */
+                                   tree with more than 256 nodes, filtered sampling
+                                   (temperature > 0 with top-k or top-p active) whose
+                                   top_k is not in [1, min(V-1, PSISPEC_MAX_TOPK)] */
 #define PSISPEC_EWORKSPACE   -3 /* ws_bytes smaller than psispec_workspace_bytes(...) */
 #define PSISPEC_EHIP         -4 /* a HIP launch failed */
 
@@ -78,7 +80,7 @@ extern "C" {
 /* ---- limits ----------------------------------------------------------------- */
 #define PSISPEC_MAX_K         64   /* draft positions per request (one wave64 ballot) */
 #define PSISPEC_MAX_TREE_NODES 256 /* tree nodes per request */
-#define PSISPEC_MAX_TOPK      1024 /* largest top_k when top-p filtering is on */
+#define PSISPEC_MAX_TOPK      256  /* largest top_k of filtered sampling */
 
 /*
  * Sampling parameters (Uno README, inference controls: temperature, top-p,

@@ -24,7 +24,7 @@ inline int nsb_of(int V) { return (V + kSB - 1) / kSB; }
 
 // Workspace sections, each 256-byte aligned.
 struct Layout {
-  size_t st, rs, res, dr, total;
+  size_t st, rs, res, dr, fh, fe, total;
 };
 
 inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
@@ -39,6 +39,10 @@ inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
   off = align_up(off + (size_t)B * nsb * sizeof(ResRec), 256);
   L.dr = off;
   off = align_up(off + (size_t)B * rows_per_req * nsb * sizeof(DraftRec), 256);
+  L.fh = off;
+  off = align_up(off + (size_t)B * rows_per_req * sizeof(FiltRow), 256);
+  L.fe = off;
+  off = align_up(off + (size_t)B * rows_per_req * kMaxTopK * sizeof(FiltEnt), 256);
   L.total = off;
   return L;
 }
@@ -57,6 +61,25 @@ inline int check_params(const psispec_params* prm, int32_t V) {
 
 inline bool filtered(const psispec_params* prm, int32_t V) {
   return prm->temperature > 0.0f && ((prm->top_k > 0 && prm->top_k < V) || prm->top_p < 1.0f);
+}
+
+// Filtered sampling needs a top-k in [1, kMaxTopK] to bound the kept set.
+inline int check_filter(const psispec_params* prm, int32_t V) {
+  if (!filtered(prm, V)) return PSISPEC_OK;
+  if (prm->top_k <= 0 || prm->top_k >= V) return PSISPEC_EUNSUPPORTED;  // top-p alone over the full vocabulary
+  if (prm->top_k > kMaxTopK) return PSISPEC_EUNSUPPORTED;
+  return PSISPEC_OK;
+}
+
+inline FiltCfg filt_cfg(const psispec_params* prm, void* ws, int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
+  const Layout L = layout(B, rows_per_req, V, dtype);
+  FiltCfg f;
+  f.hdr = (FiltRow*)((char*)ws + L.fh);
+  f.ent = (FiltEnt*)((char*)ws + L.fe);
+  f.kk = prm->top_k;
+  f.T = (double)prm->temperature;
+  f.top_p = (double)prm->top_p;
+  return f;
 }
 
 inline void fill_common(LinCfg& c, const void* p, const void* q, int dtype, int64_t B, int32_t K, int32_t V,
@@ -115,13 +138,15 @@ int psispec_draft_sample(const void* q_logits, int dtype, int64_t B, int32_t K, 
   if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
   if (K > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
   if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
-  if (filtered(params, V)) return PSISPEC_EUNSUPPORTED;
+  if (int rc = check_filter(params, V)) return rc;
   if (ws_bytes < psispec_workspace_bytes(B, K, V, dtype)) return PSISPEC_EWORKSPACE;
   LinCfg c;
   fill_common(c, nullptr, q_logits, dtype, B, K, V, params, workspace, 0);
   c.draft = draft_tokens;
-  const hipError_t e = params->temperature == 0.0f ? launch_draft_greedy(c, dtype, stream)
-                                                   : launch_draft_sampled(c, dtype, stream);
+  hipError_t e;
+  if (params->temperature == 0.0f) e = launch_draft_greedy(c, dtype, stream);
+  else if (filtered(params, V)) e = launch_filtered(c, filt_cfg(params, workspace, B, K, V, dtype), dtype, true, stream);
+  else e = launch_draft_sampled(c, dtype, stream);
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 
@@ -135,7 +160,7 @@ int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype,
   if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
   if (K > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
   if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
-  if (filtered(params, V)) return PSISPEC_EUNSUPPORTED;
+  if (int rc = check_filter(params, V)) return rc;
   if (ws_bytes < psispec_workspace_bytes(B, 2 * K + 1, V, dtype)) return PSISPEC_EWORKSPACE;
   LinCfg c;
   fill_common(c, p_logits, q_logits, dtype, B, K, V, params, workspace, K + 1);
@@ -147,6 +172,8 @@ int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype,
   hipError_t e;
   if (params->temperature == 0.0f) {
     e = launch_linear_greedy(c, dtype, stream);
+  } else if (filtered(params, V)) {
+    e = launch_filtered(c, filt_cfg(params, workspace, B, 2 * K + 1, V, dtype), dtype, false, stream);
   } else {
     e = hipSuccess;
     if (c.fused) {

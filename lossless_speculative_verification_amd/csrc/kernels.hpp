@@ -9,6 +9,7 @@
 namespace psi {
 
 constexpr int kMaxK = 64;
+constexpr int kMaxTopK = 256;  // largest top_k of the filtered path
 constexpr int kStatNV = 8;  // 16-byte vectors per thread in the fp32-grade statistics pass
 
 // Per (row, chunk) record of the fp32-grade statistics pass: chunk maximum of
@@ -53,6 +54,26 @@ struct ReqState {
   double sp_hat, sq_hat;  // fp32-grade normalisers of those rows
   double u_final;         // uniform of the final draw
   double pad[3];
+};
+
+// Filtered row: header and entries (token id order) of the kept set.
+struct FiltRow {
+  int32_t cnt;  // kept tokens (0 for an invalid row)
+  int32_t bad;  // NaN / +inf / all -inf
+  double m;     // max z over the kept set
+  double L;     // log-normaliser over the kept set
+};
+struct FiltEnt {
+  int32_t i;
+  int32_t pad;
+  double z;  // a / T
+};
+struct FiltCfg {
+  FiltRow* hdr;  // [rows]
+  FiltEnt* ent;  // [rows][kMaxTopK]
+  int kk;        // top_k in effect
+  double T;      // temperature (binary32 value)
+  double top_p;  // binary32 value
 };
 
 // Rows of one request: np target rows then nq draft rows.
@@ -101,6 +122,7 @@ hipError_t launch_linear_sampled(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_linear_greedy(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_draft_sampled(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_draft_greedy(const LinCfg& c, int dtype, hipStream_t s);
+hipError_t launch_filtered(const LinCfg& c, const FiltCfg& f, int dtype, bool draft_only, hipStream_t s);
 
 
 }  // namespace psi

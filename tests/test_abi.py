@@ -107,3 +107,10 @@ def test_binding_has_no_fallback(psi):
     src = open(os.path.join(ROOT, "lossless_speculative_verification_amd", "__init__.py")).read()
     assert "oracle" not in src
     assert "softmax" not in src and "torch.exp" not in src
+
+
+def test_filter_limits(psi):
+    # top-p without a top-k bound, and top-k above the supported maximum
+    assert _call_linear(psi, prm=psi.make_params(top_p=0.9)) == psi.EUNSUPPORTED
+    assert _call_linear(psi, V=4096, prm=psi.make_params(top_k=257)) == psi.EUNSUPPORTED
+    assert _call_linear(psi, V=4096, prm=psi.make_params(top_k=256, top_p=0.9), ws_bytes=16) == psi.EWORKSPACE
