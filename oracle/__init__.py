@@ -66,6 +66,9 @@ def lib():
         L.orc_verify_tree.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, P, f64, ctypes.c_int,
                                       f64, u64, u32, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int]
         L.orc_verify_tree.restype = ctypes.c_int
+        L.orc_tree_draft.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, f64, ctypes.c_int, f64, u64,
+                                     u32, P, ctypes.c_int]
+        L.orc_tree_draft.restype = ctypes.c_int
         del i32
         _lib = L
     return _lib
@@ -171,6 +174,21 @@ def verify_linear(p, q, draft_tokens, temperature, top_k=0, top_p=1.0, seed=0, s
     if rc != 0:
         raise ValueError("orc_verify_linear rejected its arguments")
     return dict(tokens=toks, len=ln, probs=probs, resid=resid, margin_acc=ma, margin_cdf=mc, draft=draft)
+
+
+def tree_draft(q, parent, temperature, top_k=0, top_p=1.0, seed=0, step=0, nthreads=1):
+    """Node tokens [B, N] of a candidate tree: the j-th child of row r drawn from
+    row r of q [B, N+1, V] with draw id 0x40000000 + j (argmax when greedy)."""
+    q = np.ascontiguousarray(q)
+    B, R, V = q.shape
+    N = R - 1
+    par = np.ascontiguousarray(parent, dtype=np.int32)
+    out = np.zeros((B, N), dtype=np.int32)
+    rc = lib().orc_tree_draft(_ptr(q), _dtype_code(q), B, N, V, _ptr(par), float(temperature), int(top_k),
+                              float(top_p), int(seed), int(step), _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_tree_draft rejected its arguments")
+    return out
 
 
 def verify_tree(p, q, parent, node_tokens, temperature, top_k=0, top_p=1.0, seed=0, step=0, u_override=None,

@@ -698,6 +698,87 @@ int orc_tree_depth(const int32_t* parent, int N) {
   return D;
 }
 
+/* Tree drafts [UnoX §3.4 Tree Sampler; the rule above is lossless only when
+ * the children of a row are i.i.d. draws from that row's draft distribution]:
+ * node n, the j-th child (ascending id) of row r = parent[n] + 1, is an
+ * inverse-CDF draw from softmax(filter(q_r / T)) with
+ * U(seed, step, b, r, 0x40000000 + j); greedy: argmax q_r. A request with an
+ * invalid draft row gets -1 for every node. */
+typedef struct {
+  const void* q;
+  int dtype, N, V;
+  const int32_t* parent;
+  orc_params pr;
+  int32_t* out;
+  int64_t b0, b1;
+} tree_draft_job;
+
+static void* tree_draft_worker(void* arg) {
+  tree_draft_job* J = (tree_draft_job*)arg;
+  const int N = J->N, V = J->V, R = J->N + 1;
+  double* z = (double*)malloc(sizeof(double) * (size_t)V);
+  double* w = (double*)malloc(sizeof(double) * (size_t)V);
+  keyed* buf = (keyed*)malloc(sizeof(keyed) * (size_t)V);
+  for (int64_t b = J->b0; b < J->b1; ++b) {
+    int bad = 0;
+    for (int r = 0; r < R; ++r) bad |= orc_decode_row(J->q, J->dtype, b * R + r, V, z);
+    for (int r = 0; r < R && !bad; ++r) {
+      int j = 0; /* sibling index within row r */
+      for (int n = 0; n < N; ++n) {
+        if (J->parent[n] != r - 1) continue;
+        orc_decode_row(J->q, J->dtype, b * R + r, V, z);
+        int x;
+        if (J->pr.temperature == 0.0) {
+          x = argmax_row(z, V);
+        } else {
+          filter_row_buf(z, V, J->pr.temperature, J->pr.top_k, J->pr.top_p, buf);
+          double m = -INFINITY;
+          for (int t = 0; t < V; ++t)
+            if (z[t] > m) m = z[t];
+          for (int t = 0; t < V; ++t) w[t] = exp(z[t] - m);
+          x = orc_sample(w, V, uni(&J->pr, b, r, ORC_DRAFT_DRAW + (uint32_t)j, NULL, 0), NULL);
+        }
+        J->out[b * N + n] = x;
+        ++j;
+      }
+    }
+    if (bad)
+      for (int n = 0; n < N; ++n) J->out[b * N + n] = -1;
+  }
+  free(z);
+  free(w);
+  free(buf);
+  return NULL;
+}
+
+int orc_tree_draft(const void* q, int dtype, int64_t B, int N, int V, const int32_t* parent, double temperature,
+                   int top_k, double top_p, uint64_t seed, uint32_t step, int32_t* out, int nthreads) {
+  if (!q || !parent || !out || B <= 0 || V <= 0 || !(temperature >= 0.0)) return -1;
+  if (orc_tree_depth(parent, N) < 0) return -1;
+  nthreads = clamp_threads(nthreads, B);
+  tree_draft_job* jobs = (tree_draft_job*)calloc((size_t)nthreads, sizeof(tree_draft_job));
+  for (int t = 0; t < nthreads; ++t) {
+    tree_draft_job* J = &jobs[t];
+    J->q = q;
+    J->dtype = dtype;
+    J->N = N;
+    J->V = V;
+    J->parent = parent;
+    J->pr.temperature = temperature;
+    J->pr.top_k = top_k;
+    J->pr.top_p = top_p;
+    J->pr.seed = seed;
+    J->pr.step = step;
+    J->out = out;
+    J->b0 = B * t / nthreads;
+    J->b1 = B * (t + 1) / nthreads;
+  }
+  run_jobs(jobs, sizeof(tree_draft_job), nthreads, tree_draft_worker);
+  free(jobs);
+  return 0;
+}
+
+
 int orc_verify_tree(const void* p, const void* q, int dtype, int64_t B, int N, int V, const int32_t* parent,
                     const int32_t* node_tokens, double temperature, int top_k, double top_p, uint64_t seed,
                     uint32_t step, int32_t* out_tokens, int32_t* out_path, int32_t* out_len,

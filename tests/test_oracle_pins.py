@@ -553,3 +553,48 @@ def test_tree_greedy():
     assert r["len"][0] == 2 and list(r["path"][0]) == [1, 3] and list(r["tokens"][0]) == [3, 5, 0]
     r = oracle.verify_tree(a, d, parent, np.array([[1, 2, 4, 5]]), 0.0)
     assert r["len"][0] == 0 and list(r["tokens"][0]) == [3, -1, -1]
+
+
+def test_tree_draft_chain_equals_linear_draft():
+    """On a chain, node i is the only child of row i, so the tree drafts are the
+    linear drafts of rows 0..K-1 (draw id 0x40000000 at every row)."""
+    _, ql = synth.linear_inputs("tiny", seed=3, B=3)
+    K = ql.shape[1]
+    qt = np.concatenate([ql, ql[:, -1:]], axis=1)
+    parent = np.arange(-1, K - 1, dtype=np.int32)
+    for t in range(5):
+        d, _ = oracle.draft_sample(ql, 1.0, seed=9, step=t)
+        assert np.array_equal(oracle.tree_draft(qt, parent, 1.0, seed=9, step=t), d)
+
+
+def test_tree_draft_brute_force():
+    """Several children of one row: child j is the inverse-CDF pick of
+    softmax(filter(q_r / T)) at U(seed, step, b, r, 0x40000000 + j), checked with
+    a numpy cumulative sum; greedy gives the argmax; a bad row gives -1."""
+    rng = np.random.default_rng(4)
+    V = 300
+    parent = np.array([-1, -1, -1, 0, 0, 2], dtype=np.int32)
+    N = len(parent)
+    q = rng.normal(0, 2.0, (2, N + 1, V)).astype(np.float32)
+    rows = parent + 1
+    sib = [int(np.sum(parent[:n] == parent[n])) for n in range(N)]
+    for T, top_k in ((0.8, 0), (1.3, 17)):
+        got = oracle.tree_draft(q, parent, T, top_k=top_k, seed=21, step=2)
+        for b in range(2):
+            for n in range(N):
+                z = q[b, rows[n]].astype(np.float64) / T
+                if top_k:
+                    keep = np.argsort(-z, kind="stable")[:top_k]
+                    zz = np.full(V, -np.inf)
+                    zz[keep] = z[keep]
+                    z = zz
+                w = np.exp(z - z.max())
+                u = oracle.uniform(21, 2, b, int(rows[n]), 0x40000000 + sib[n])
+                want = int(np.argmax(np.cumsum(w) > u * w.sum()))
+                assert got[b, n] == want
+    g = oracle.tree_draft(q, parent, 0.0)
+    assert np.array_equal(g, np.argmax(q[:, rows, :], axis=2))
+    qb = q.copy()
+    qb[1, 6, 5] = np.nan  # a leaf row: still makes the request invalid
+    g = oracle.tree_draft(qb, parent, 1.0)
+    assert np.all(g[1] == -1) and np.all(g[0] >= 0)
