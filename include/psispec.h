@@ -74,7 +74,8 @@ extern "C" {
 /* ---- flags ------------------------------------------------------------------ */
 /* psispec_verify_linear draws the drafts itself from q (exactly as
    psispec_draft_sample with the same params would) and writes them to
-   draft_tokens, instead of reading them from there. */
+   draft_tokens, instead of reading them from there. psispec_verify_tree
+   likewise draws the node tokens (see there) and writes them to node_tokens. */
 #define PSISPEC_FUSED_DRAFT 1u
 
 /* ---- limits ----------------------------------------------------------------- */
@@ -195,14 +196,20 @@ int32_t psispec_tree_depth(const int32_t* parent, int32_t N);
  *                 context after node n.
  *   parent        HOST [N] int32, parent[n] < n, -1 for children of the root;
  *                 shared by every request.
- *   node_tokens   [B, N] int32 candidate token of each node.
+ *   node_tokens   [B, N] int32 candidate token of each node; input, or output
+ *                 with PSISPEC_FUSED_DRAFT: node n, the j-th child (ascending
+ *                 id) of row r, is then drawn from softmax(filter(q_r / T)) by
+ *                 inverse CDF with U(seed, step, b, r, 0x40000000 + j) (argmax
+ *                 of q_r in greedy mode), -1 for every node of a request with
+ *                 an invalid row. The rule is lossless only for children drawn
+ *                 i.i.d. from their row's draft distribution, as these are.
  *   out_tokens    [B, D+1] int32 out (D = psispec_tree_depth): path tokens, the
  *                 final token, then -1 padding.
  *   out_path      [B, D] int32 out: node ids of the accepted path, -1 padding.
  *   out_len       [B] int32 out: accepted path length (or -1 on error).
  */
 int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, int64_t B, int32_t N,
-                        int32_t V, const int32_t* parent, const int32_t* node_tokens,
+                        int32_t V, const int32_t* parent, int32_t* node_tokens,
                         const psispec_params* params, int32_t* out_tokens, int32_t* out_path,
                         int32_t* out_len, void* workspace, size_t ws_bytes, hipStream_t stream);
 

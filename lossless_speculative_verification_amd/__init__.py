@@ -169,10 +169,11 @@ def tree_depth(parent) -> int:
     return int(lib.psispec_tree_depth(par.ctypes.data_as(ctypes.c_void_p), par.size))
 
 
-def verify_tree(p: torch.Tensor, q: torch.Tensor, parent, node_tokens: torch.Tensor, temperature=1.0, top_k=0,
-                top_p=1.0, seed=0, step=0, out=None, workspace=None, stream=None) -> dict:
+def verify_tree(p: torch.Tensor, q: torch.Tensor, parent, node_tokens, temperature=1.0, top_k=0, top_p=1.0,
+                seed=0, step=0, fused=False, out=None, workspace=None, stream=None) -> dict:
     """psispec_verify_tree. p, q [B, N+1, V]; parent: host int sequence [N];
-    node_tokens [B, N] int32. Returns dict(tokens [B, D+1], path [B, D], len [B])."""
+    node_tokens [B, N] int32 (input; output when fused, allocated if None).
+    Returns dict(tokens [B, D+1], path [B, D], len [B], nodes [B, N])."""
     import numpy as np
 
     assert p.is_cuda and q.is_cuda and p.is_contiguous() and q.is_contiguous()
@@ -186,14 +187,19 @@ def verify_tree(p: torch.Tensor, q: torch.Tensor, parent, node_tokens: torch.Ten
         raise PsiSpecError("psispec_tree_depth", D)
     dt = dtype_code(p)
     dev = p.device
+    if node_tokens is None:
+        assert fused, "node_tokens are required unless fused"
+        node_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    assert node_tokens.is_cuda and node_tokens.dtype == torch.int32 and node_tokens.shape == (B, N)
     if out is None:
         out = dict(tokens=torch.empty((B, D + 1), dtype=torch.int32, device=dev),
                    path=torch.empty((B, D), dtype=torch.int32, device=dev),
                    len=torch.empty((B,), dtype=torch.int32, device=dev))
     ws = _workspace(workspace, workspace_bytes(B, 2 * R, V, dt), dev)
-    prm = make_params(temperature, top_k, top_p, seed, step)
+    prm = make_params(temperature, top_k, top_p, seed, step, fused)
     rc = lib.psispec_verify_tree(_ptr(p), _ptr(q), dt, B, N, V, par.ctypes.data_as(ctypes.c_void_p),
                                  _ptr(node_tokens), ctypes.byref(prm), _ptr(out["tokens"]), _ptr(out["path"]),
                                  _ptr(out["len"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("psispec_verify_tree", rc)
+    out["nodes"] = node_tokens
     return out

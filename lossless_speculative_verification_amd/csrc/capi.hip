@@ -22,9 +22,12 @@ inline int nch32_of(int V, int dtype) {
 }
 inline int nsb_of(int V) { return (V + kSB - 1) / kSB; }
 
+// Kept-set entries stored per filtered row (top_k < V and top_k <= kMaxTopK).
+inline int filt_stride(int32_t V) { return V < kMaxTopK ? V : kMaxTopK; }
+
 // Workspace sections, each 256-byte aligned.
 struct Layout {
-  size_t st, rs, res, dr, fh, fe, total;
+  size_t st, rs, res, dr, fh, fe, rst, ts, tres, total;
 };
 
 inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
@@ -42,7 +45,13 @@ inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
   L.fh = off;
   off = align_up(off + (size_t)B * rows_per_req * sizeof(FiltRow), 256);
   L.fe = off;
-  off = align_up(off + (size_t)B * rows_per_req * kMaxTopK * sizeof(FiltEnt), 256);
+  off = align_up(off + (size_t)B * rows_per_req * filt_stride(V) * sizeof(FiltEnt), 256);
+  L.rst = off;
+  off = align_up(off + (size_t)B * rows_per_req * sizeof(RowStat), 256);
+  L.ts = off;
+  off = align_up(off + (size_t)B * sizeof(TreeState), 256);
+  L.tres = off;
+  off = align_up(off + (size_t)B * nsb * sizeof(TreeRes), 256);
   L.total = off;
   return L;
 }
@@ -76,6 +85,7 @@ inline FiltCfg filt_cfg(const psispec_params* prm, void* ws, int64_t B, int32_t 
   FiltCfg f;
   f.hdr = (FiltRow*)((char*)ws + L.fh);
   f.ent = (FiltEnt*)((char*)ws + L.fe);
+  f.stride = filt_stride(V);
   f.kk = prm->top_k;
   f.T = (double)prm->temperature;
   f.top_p = (double)prm->top_p;
@@ -114,6 +124,34 @@ inline void fill_common(LinCfg& c, const void* p, const void* q, int dtype, int6
   c.rs = (ReqState*)(w + L.rs);
   c.res = (ResRec*)(w + L.res);
   c.dr = (DraftRec*)(w + L.dr);
+}
+
+// Children lists of every row from a validated parent array, and the largest
+// number of rejections along one walk that need a new G(c) before the final
+// one: at a row with C children at most C - 1 of them, summed down a path.
+inline int build_topo(const int32_t* parent, int32_t N, int32_t D, TreeTopo& tp) {
+  memset(&tp, 0, sizeof(tp));
+  tp.N = N;
+  tp.D = D;
+  int cnt[kMaxNodes + 1] = {0};
+  for (int n = 0; n < N; ++n) ++cnt[parent[n] + 1];
+  tp.off[0] = 0;
+  for (int r = 0; r <= N; ++r) tp.off[r + 1] = (int16_t)(tp.off[r] + cnt[r]);
+  int fill[kMaxNodes + 1] = {0};
+  for (int n = 0; n < N; ++n) {
+    const int r = parent[n] + 1;
+    tp.prow[n] = (int16_t)r;
+    tp.sib[n] = (uint8_t)fill[r];
+    tp.kids[tp.off[r] + fill[r]++] = (int16_t)n;
+  }
+  int cost[kMaxNodes + 1];
+  int rounds = 0;
+  for (int r = 0; r <= N; ++r) {
+    const int own = cnt[r] > 1 ? cnt[r] - 1 : 0;
+    cost[r] = own + (r == 0 ? 0 : cost[parent[r - 1] + 1]);
+    if (cost[r] > rounds) rounds = cost[r];
+  }
+  return rounds;
 }
 
 }  // namespace
@@ -201,25 +239,41 @@ int32_t psispec_tree_depth(const int32_t* parent, int32_t N) {
 }
 
 int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, int64_t B, int32_t N, int32_t V,
-                        const int32_t* parent, const int32_t* node_tokens, const psispec_params* params,
+                        const int32_t* parent, int32_t* node_tokens, const psispec_params* params,
                         int32_t* out_tokens, int32_t* out_path, int32_t* out_len, void* workspace, size_t ws_bytes,
                         hipStream_t stream) {
-  (void)p_logits;
-  (void)q_logits;
-  (void)dtype;
-  (void)B;
-  (void)N;
-  (void)V;
-  (void)parent;
-  (void)node_tokens;
-  (void)params;
-  (void)out_tokens;
-  (void)out_path;
-  (void)out_len;
-  (void)workspace;
-  (void)ws_bytes;
-  (void)stream;
-  return PSISPEC_EUNSUPPORTED;
+  if (!p_logits || !q_logits || !parent || !node_tokens || !out_tokens || !out_path || !out_len || !workspace)
+    return PSISPEC_EINVAL;
+  if (B <= 0 || N <= 0 || V <= 0) return PSISPEC_EINVAL;
+  if (int rc = check_params(params, V)) return rc;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
+  const int32_t D = psispec_tree_depth(parent, N);
+  if (D < 0) return D;
+  if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
+  if (int rc = check_filter(params, V)) return rc;
+  const int32_t rows = 2 * (N + 1);
+  if (ws_bytes < psispec_workspace_bytes(B, rows, V, dtype)) return PSISPEC_EWORKSPACE;
+  TreeTopo tp;
+  const int rounds = build_topo(parent, N, D, tp);
+  LinCfg c;
+  fill_common(c, p_logits, q_logits, dtype, B, N + 1, V, params, workspace, N + 1);
+  c.out_tokens = out_tokens;
+  c.out_len = out_len;
+  const Layout L = layout(B, rows, V, dtype);
+  char* w = (char*)workspace;
+  TreeCfg tc;
+  tc.tokens = node_tokens;
+  tc.out_path = out_path;
+  tc.rst = (RowStat*)(w + L.rst);
+  tc.ts = (TreeState*)(w + L.ts);
+  tc.tres = (TreeRes*)(w + L.tres);
+  tc.N = N;
+  tc.D = D;
+  hipError_t e;
+  if (params->temperature == 0.0f) e = launch_tree_greedy(c, tp, tc, dtype, stream);
+  else if (filtered(params, V)) e = launch_tree_filtered(c, filt_cfg(params, workspace, B, rows, V, dtype), tp, tc, dtype, stream);
+  else e = launch_tree_sampled(c, tp, tc, rounds, dtype, stream);
+  return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 
 const char* psispec_strerror(int status) {

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kWG) void k_filter_row(LinCfg c, FiltCfg f) {
     f.hdr[sr] = h;
   }
   __syncthreads();
-  FiltEnt* out = f.ent + sr * (int64_t)kMaxTopK;
+  FiltEnt* out = f.ent + sr * (int64_t)f.stride;
   for (int t = threadIdx.x; t < cnt; t += kWG) {
     FiltEnt e;
     e.i = ent[t].i;
@@ -219,47 +219,11 @@ __global__ __launch_bounds__(kWG) void k_filter_row(LinCfg c, FiltCfg f) {
 }
 
 // --------------------------------------------------- per-request decision --
-namespace {
-
-// Probability of token x in a filtered row (0 when filtered out).
-__device__ double filt_prob(const FiltRow& h, const FiltEnt* e, int x) {
-  int lo = 0, hi = h.cnt - 1;
-  while (lo <= hi) {
-    const int mid = (lo + hi) >> 1;
-    const int id = e[mid].i;
-    if (id == x) return ::exp(e[mid].z - h.L);
-    if (id < x) lo = mid + 1;
-    else hi = mid - 1;
-  }
-  return 0.0;
-}
-
-// Inverse-CDF draw over a list of weights in id order: smallest entry whose
-// running sum exceeds u * W, else the last positive one; -1 if W is not positive.
-template <class W>
-__device__ int draw_list(int cnt, double u, W w, const FiltEnt* e) {
-  double tot = 0.0;
-  for (int t = 0; t < cnt; ++t) tot += w(t);
-  if (!(tot > 0.0)) return -1;
-  const double target = u * tot;
-  double acc = 0.0;
-  int last = -1;
-  for (int t = 0; t < cnt; ++t) {
-    const double wt = w(t);
-    acc += wt;
-    if (wt > 0.0) last = t;
-    if (acc > target) return e[t].i;
-  }
-  return last >= 0 ? e[last].i : -1;
-}
-
-}  // namespace
-
 __global__ __launch_bounds__(kWG) void k_filt_decide(LinCfg c, FiltCfg f) {
   const int64_t b = blockIdx.x;
   const int K = c.K, R = 2 * K + 1, t = threadIdx.x;
   const FiltRow* H = f.hdr + b * R;
-  const FiltEnt* Ent = f.ent + b * R * (int64_t)kMaxTopK;
+  const FiltEnt* Ent = f.ent + b * R * (int64_t)f.stride;
   __shared__ int s_bad, s_n;
   __shared__ int s_x[kMaxK];
   if (t == 0) s_bad = 0;
@@ -270,7 +234,7 @@ __global__ __launch_bounds__(kWG) void k_filt_decide(LinCfg c, FiltCfg f) {
     int x;
     if (c.fused) {
       const FiltRow hq = H[K + 1 + t];
-      const FiltEnt* eq = Ent + (K + 1 + t) * (int64_t)kMaxTopK;
+      const FiltEnt* eq = Ent + (K + 1 + t) * (int64_t)f.stride;
       const double u = c.rng.u((uint32_t)b, (uint32_t)t, kDrawDraft);
       x = hq.cnt > 0 ? draw_list(hq.cnt, u, [&](int k) { return ::exp(eq[k].z - hq.m); }, eq) : -1;
     } else {
@@ -284,8 +248,8 @@ __global__ __launch_bounds__(kWG) void k_filt_decide(LinCfg c, FiltCfg f) {
   double P = 0.0, Q = 0.0;
   if (t < K && !s_bad) {
     const int x = s_x[t];
-    P = filt_prob(H[t], Ent + t * (int64_t)kMaxTopK, x);
-    Q = filt_prob(H[K + 1 + t], Ent + (K + 1 + t) * (int64_t)kMaxTopK, x);
+    P = filt_prob(H[t], Ent + t * (int64_t)f.stride, x);
+    Q = filt_prob(H[K + 1 + t], Ent + (K + 1 + t) * (int64_t)f.stride, x);
     const double u = c.rng.u((uint32_t)b, (uint32_t)t, kDrawAccept);
     acc = u * Q < P;
   }
@@ -317,12 +281,12 @@ __global__ __launch_bounds__(kWG) void k_filt_decide(LinCfg c, FiltCfg f) {
   if (t == 0) {
     const double u = c.rng.u((uint32_t)b, (uint32_t)n, kDrawFinal);
     const FiltRow hp = H[n];
-    const FiltEnt* ep = Ent + n * (int64_t)kMaxTopK;
+    const FiltEnt* ep = Ent + n * (int64_t)f.stride;
     int y;
     double resid = 0.0;
     if (n < K) {
       const FiltRow hq = H[K + 1 + n];
-      const FiltEnt* eq = Ent + (K + 1 + n) * (int64_t)kMaxTopK;
+      const FiltEnt* eq = Ent + (K + 1 + n) * (int64_t)f.stride;
       auto w = [&](int k) {
         const double pj = ::exp(ep[k].z - hp.L);
         const double qj = filt_prob(hq, eq, ep[k].i);
@@ -354,7 +318,7 @@ __global__ __launch_bounds__(kWG) void k_filt_draft(LinCfg c, FiltCfg f) {
     int x = -1;
     if (!s_bad) {
       const FiltRow hq = H[i];
-      const FiltEnt* eq = f.ent + (b * K + i) * (int64_t)kMaxTopK;
+      const FiltEnt* eq = f.ent + (b * K + i) * (int64_t)f.stride;
       const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
       x = draw_list(hq.cnt, u, [&](int k) { return ::exp(eq[k].z - hq.m); }, eq);
     }
@@ -370,6 +334,18 @@ static hipError_t filtered_t(const LinCfg& c, const FiltCfg& f, bool draft_only,
   if (draft_only) hipLaunchKernelGGL(k_filt_draft, dim3((unsigned)c.B), dim3(kWG), 0, s, c, f);
   else hipLaunchKernelGGL(k_filt_decide, dim3((unsigned)c.B), dim3(kWG), 0, s, c, f);
   return hipGetLastError();
+}
+
+template <int DT, bool AL>
+static hipError_t filter_rows_t(const LinCfg& c, const FiltCfg& f, int64_t rows, hipStream_t s) {
+  hipLaunchKernelGGL((k_filter_row<DT, AL>), dim3((unsigned)rows), dim3(kWG), 0, s, c, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_filter_rows(const LinCfg& c, const FiltCfg& f, int64_t rows, int dtype, hipStream_t s) {
+  if (dtype == kBF16)
+    return c.aligned ? filter_rows_t<kBF16, true>(c, f, rows, s) : filter_rows_t<kBF16, false>(c, f, rows, s);
+  return c.aligned ? filter_rows_t<kF32, true>(c, f, rows, s) : filter_rows_t<kF32, false>(c, f, rows, s);
 }
 
 hipError_t launch_filtered(const LinCfg& c, const FiltCfg& f, int dtype, bool draft_only, hipStream_t s) {

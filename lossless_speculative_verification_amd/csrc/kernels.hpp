@@ -70,10 +70,60 @@ struct FiltEnt {
 };
 struct FiltCfg {
   FiltRow* hdr;  // [rows]
-  FiltEnt* ent;  // [rows][kMaxTopK]
+  FiltEnt* ent;  // [rows][stride]
+  int stride;    // entries per row: min(V, kMaxTopK) >= any admissible top_k
   int kk;        // top_k in effect
   double T;      // temperature (binary32 value)
   double top_p;  // binary32 value
+};
+
+// Candidate tree topology, passed by value in the kernel arguments. Row 0 is
+// the root context and row n+1 the context after node n; the children of row
+// r are the nodes kids[off[r] .. off[r+1]) in ascending node id.
+constexpr int kMaxNodes = 256;
+struct TreeTopo {
+  int16_t off[kMaxNodes + 2];
+  int16_t kids[kMaxNodes];
+  int16_t prow[kMaxNodes];  // row of node n's parent (parent[n] + 1)
+  uint8_t sib[kMaxNodes];   // index of node n among the children of that row
+  int32_t N, D;
+};
+
+// Per-row normaliser of the tree path: exact maximum and fp32-grade sum of
+// 2^((a - m) * c) (from the statistics pass).
+struct RowStat {
+  float m;
+  int32_t bad;
+  double s;
+};
+
+// Walk state of one request. After j rejections at a row the running target
+// is (P - cj * Q)+ / Gj with c_0 = 0, G_0 = 1 and c_{j+1} = c_j + G(c_j),
+// G(c) = sum_t max(0, P(t) - c Q(t)).
+enum TreePhase : int32_t { kTreeTest = 0, kTreeWaitG = 1, kTreeFinal = 2, kTreeDone = 3 };
+struct TreeState {
+  int32_t row, j, len, phase, has_exact, pad;
+  float mp, mq;      // exact row maxima of the current row pair
+  double sp_hat, sq_hat;  // fp32-grade normalisers of the current row pair
+  double Sp, Sq;          // fp64-grade normalisers (valid when has_exact)
+  double cj, Gj;          // current coefficient and normaliser
+  double c_new, c_old;    // coefficient asked of the next row pass, and the one to fall back to
+};
+
+// Per (request, sub-block) sums of a tree row pass: sp, sq = sums of the
+// unnormalised P and Q parts; (a, bq) = the same over the entries where
+// P > c_new Q; (a0, bq0) = over the entries where P > c_old Q.
+struct TreeRes {
+  double sp, sq, a, bq, a0, bq0;
+};
+
+struct TreeCfg {
+  int32_t* tokens;        // [B, N] node tokens (written first when drafts are fused)
+  int32_t* out_path;      // [B, D]
+  RowStat* rst;           // [B, 2 (N + 1)]
+  TreeState* ts;          // [B]
+  TreeRes* tres;          // [B, nsb]
+  int N, D;
 };
 
 // Rows of one request: np target rows then nq draft rows.
@@ -123,6 +173,23 @@ hipError_t launch_linear_greedy(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_draft_sampled(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_draft_greedy(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_filtered(const LinCfg& c, const FiltCfg& f, int dtype, bool draft_only, hipStream_t s);
+// Tree verification (tree.hip); c.rows holds N + 1 target and N + 1 draft rows
+// per request; `rounds` bounds the rejections that need a new G(c) before the
+// final one along any walk.
+// With c.fused the node tokens are drawn first: the j-th child of row r from
+// row r of q with draw id kDrawDraft + j (argmax when greedy).
+hipError_t launch_tree_sampled(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int rounds, int dtype,
+                               hipStream_t s);
+hipError_t launch_tree_greedy(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int dtype, hipStream_t s);
+hipError_t launch_tree_filtered(const LinCfg& c, const FiltCfg& f, const TreeTopo& tp, const TreeCfg& tc, int dtype,
+                                hipStream_t s);
+// Row passes over the first `rows` rows of c.rows, reused by the tree:
+// filtering (filter.hip), statistics and argmax (linear.hip).
+hipError_t launch_filter_rows(const LinCfg& c, const FiltCfg& f, int64_t rows, int dtype, hipStream_t s);
+hipError_t launch_stats32(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
+hipError_t launch_argmax(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
+// fp64 draft-row sub-block records of the first `rows` rows of c.rows.q (linear.hip).
+hipError_t launch_draftpass(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
 
 
 }  // namespace psi

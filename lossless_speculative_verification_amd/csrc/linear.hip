@@ -334,31 +334,8 @@ __global__ __launch_bounds__(kWG) void k_draftfinal(LinCfg c) {
     if (t == 0) c.draft[qr] = -1;
     return;
   }
-  const DraftRec* rec = c.dr + qr * nsb;
-  float m = -INFINITY;
-  for (int sb = t; sb < nsb; sb += kWG) m = fmaxnan(m, rec[sb].m);
-  m = block_max(m, shf);
-  const double md = m, invT = c.invT;
-  const char* row = c.rows.q + (qr * (int64_t)c.V) * c.rows.esz;
-  auto wsb = [&](int sb) {
-    const DraftRec r = rec[sb];
-    return is_neg_inf(r.m) ? 0.0 : r.s * exp64(((double)r.m - md) * invT);
-  };
-  double W;
-  {
-    double mine = 0.0;
-    for (int sb = t; sb < nsb; sb += kWG) mine += wsb(sb);
-    W = block_sum(mine, sh);
-  }
   const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
-  const int y = pick_index(
-      nsb, c.V, u * W, wsb,
-      [&](int64_t j) {
-        const DraftRec r = rec[j / kSB];
-        const double f = exp64(((double)r.m - md) * invT);
-        return exp64(((double)E::load1(row, j) - (double)r.m) * invT) * f;
-      },
-      sh);
+  const int y = draft_pick<DT>(c, c.rows.q + (qr * (int64_t)c.V) * c.rows.esz, c.dr + qr * nsb, u, shf, sh);
   if (t == 0) c.draft[qr] = y;
 }
 
@@ -422,23 +399,6 @@ __global__ __launch_bounds__(kWG) void k_argmax(LinCfg c) {
     r.pad = 0;
     c.ar[item] = r;
   }
-}
-
-// combine the chunk records of one row: argmax (lowest index on ties), bad flag
-__device__ __forceinline__ int row_argmax(const ArgRec* rec, int nch, int* bad) {
-  float v = -INFINITY;
-  int idx = 0x7fffffff, bd = 0;
-  for (int ch = 0; ch < nch; ++ch) {
-    const ArgRec r = rec[ch];
-    bd |= r.bad;
-    if (r.v > v || (r.v == v && r.idx < idx)) {
-      v = r.v;
-      idx = r.idx;
-    }
-  }
-  if (is_neg_inf(v)) bd = 1;  // entirely -inf
-  *bad = bd;
-  return idx;
 }
 
 __global__ __launch_bounds__(kWG) void k_greedy_decide(LinCfg c) {
@@ -549,6 +509,24 @@ static hipError_t draft_greedy_t(const LinCfg& c, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DT, bool AL>
+static hipError_t stats32_t(const LinCfg& c, int64_t rows, hipStream_t s) {
+  hipLaunchKernelGGL((k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
+  return hipGetLastError();
+}
+
+template <int DT, bool AL>
+static hipError_t draftpass_t(const LinCfg& c, int64_t rows, hipStream_t s) {
+  hipLaunchKernelGGL((k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)rows), dim3(kWG), 0, s, c);
+  return hipGetLastError();
+}
+
+template <int DT, bool AL>
+static hipError_t argmax_t(const LinCfg& c, int64_t rows, hipStream_t s) {
+  hipLaunchKernelGGL((k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
+  return hipGetLastError();
+}
+
 #define PSI_DISPATCH(fn, dtype, aligned, ...)                                      \
   ((dtype) == kBF16 ? ((aligned) ? fn<kBF16, true>(__VA_ARGS__) : fn<kBF16, false>(__VA_ARGS__)) \
                     : ((aligned) ? fn<kF32, true>(__VA_ARGS__) : fn<kF32, false>(__VA_ARGS__)))
@@ -564,6 +542,15 @@ hipError_t launch_draft_sampled(const LinCfg& c, int dtype, hipStream_t s) {
 }
 hipError_t launch_draft_greedy(const LinCfg& c, int dtype, hipStream_t s) {
   return PSI_DISPATCH(draft_greedy_t, dtype, c.aligned, c, s);
+}
+hipError_t launch_stats32(const LinCfg& c, int64_t rows, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(stats32_t, dtype, c.aligned, c, rows, s);
+}
+hipError_t launch_draftpass(const LinCfg& c, int64_t rows, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(draftpass_t, dtype, c.aligned, c, rows, s);
+}
+hipError_t launch_argmax(const LinCfg& c, int64_t rows, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(argmax_t, dtype, c.aligned, c, rows, s);
 }
 
 }  // namespace psi

@@ -176,4 +176,86 @@ __device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, doubl
   return j;
 }
 
+// ------------------------------------------------------- draft pick --
+// Inverse-CDF draw (fp64, token-id order) from softmax(a / T) of one draft row
+// given its per-sub-block records (maximum, sum of exp((a - m_sb) / T)).
+template <int DT>
+__device__ int draft_pick(const LinCfg& c, const char* row, const DraftRec* rec, double u, float* shf, double* sh) {
+  using E = Elem<DT>;
+  const int nsb = c.nsb, t = threadIdx.x;
+  float m = -INFINITY;
+  for (int sb = t; sb < nsb; sb += kWG) m = fmaxnan(m, rec[sb].m);
+  m = block_max(m, shf);
+  const double md = m, invT = c.invT;
+  auto wsb = [&](int sb) {
+    const DraftRec r = rec[sb];
+    return is_neg_inf(r.m) ? 0.0 : r.s * exp64(((double)r.m - md) * invT);
+  };
+  double W;
+  {
+    double mine = 0.0;
+    for (int sb = t; sb < nsb; sb += kWG) mine += wsb(sb);
+    W = block_sum(mine, sh);
+  }
+  return pick_index(
+      nsb, c.V, u * W, wsb,
+      [&](int64_t j) {
+        const DraftRec r = rec[j / kSB];
+        const double f = exp64(((double)r.m - md) * invT);
+        return exp64(((double)E::load1(row, j) - (double)r.m) * invT) * f;
+      },
+      sh);
+}
+
+// ------------------------------------------------------------ greedy --
+// combine the chunk records of one row: argmax (lowest index on ties), bad flag
+__device__ inline int row_argmax(const ArgRec* rec, int nch, int* bad) {
+  float v = -INFINITY;
+  int idx = 0x7fffffff, bd = 0;
+  for (int ch = 0; ch < nch; ++ch) {
+    const ArgRec r = rec[ch];
+    bd |= r.bad;
+    if (r.v > v || (r.v == v && r.idx < idx)) {
+      v = r.v;
+      idx = r.idx;
+    }
+  }
+  if (is_neg_inf(v)) bd = 1;  // entirely -inf
+  *bad = bd;
+  return idx;
+}
+
+// ------------------------------------------------ filtered supports --
+// Probability of token x in a filtered row (0 when filtered out).
+__device__ inline double filt_prob(const FiltRow& h, const FiltEnt* e, int x) {
+  int lo = 0, hi = h.cnt - 1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    const int id = e[mid].i;
+    if (id == x) return ::exp(e[mid].z - h.L);
+    if (id < x) lo = mid + 1;
+    else hi = mid - 1;
+  }
+  return 0.0;
+}
+
+// Inverse-CDF draw over a list of weights in id order: smallest entry whose
+// running sum exceeds u * W, else the last positive one; -1 if W is not positive.
+template <class W>
+__device__ inline int draw_list(int cnt, double u, W w, const FiltEnt* e) {
+  double tot = 0.0;
+  for (int t = 0; t < cnt; ++t) tot += w(t);
+  if (!(tot > 0.0)) return -1;
+  const double target = u * tot;
+  double acc = 0.0;
+  int last = -1;
+  for (int t = 0; t < cnt; ++t) {
+    const double wt = w(t);
+    acc += wt;
+    if (wt > 0.0) last = t;
+    if (acc > target) return e[t].i;
+  }
+  return last >= 0 ? e[last].i : -1;
+}
+
 }  // namespace psi

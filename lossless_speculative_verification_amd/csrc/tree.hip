@@ -1,0 +1,614 @@
+// Tree verification of Psi-Spec on gfx950 ("Uno" research explainer, §3.4
+// Tree Sampler: several candidate continuations are checked in one verify
+// pass).
+//
+// Rule at a row with children c_0 < c_1 < ... (each drawn i.i.d. from the
+// row's draft distribution Q): the running target starts at P; child j is
+// accepted iff u * Q(tok_j) < r(tok_j); after a rejection r <- norm((r - Q)+)
+// (kept when that vanishes); the walk descends into the first accepted child;
+// at a leaf, or once every child is rejected, the final token is drawn from r.
+//
+// The running target after j rejections has the closed form
+//   r_j = (P - c_j Q)+ / G(c_j),  G(c) = sum_t max(0, P(t) - c Q(t)),
+//   c_0 = 0, c_{j+1} = c_j + G(c_j),
+// (induction: (r_j - Q)+ = (P - (c_j + G(c_j)) Q)+ / G(c_j)), so each
+// rejection costs one fp64 pass over the row pair for a scalar G, and every
+// test needs only P(tok), Q(tok) and (c_j, G(c_j)).
+//
+// Pipeline on the caller's stream:
+//   k_stats32          (linear.hip) fp32-grade maxima and sums of every row.
+//   k_tree_walk        one workgroup per request, launched rounds + 1 times:
+//                      the first launch reduces the row statistics and checks
+//                      the request; each launch then walks the tree (accept
+//                      tests) until the next rejection and asks for G(c).
+//   k_tree_pass        (sub-block, request): fp64 sums of the row pair of every
+//                      request waiting for a G(c); run between walks, and once
+//                      more for the final row.
+//   k_tree_pick        one workgroup per request: inverse-CDF draw of the final
+//                      token from r at the stopping row, outputs.
+// Greedy (temperature 0): k_argmax then k_tree_greedy. Filtered sampling:
+// k_filter_row (filter.hip) then k_tree_filt, which runs the recursive update
+// directly on the at most 2 * top_k entry union of the two kept sets.
+#include "rowops.hpp"
+
+namespace psi {
+
+namespace {
+
+__device__ __forceinline__ const char* tree_prow(const LinCfg& c, int64_t b, int r) {
+  return c.rows.p + ((b * c.rows.np + r) * (int64_t)c.V) * c.rows.esz;
+}
+__device__ __forceinline__ const char* tree_qrow(const LinCfg& c, int64_t b, int r) {
+  return c.rows.q + ((b * c.rows.nq + r) * (int64_t)c.V) * c.rows.esz;
+}
+
+// Fills the outputs of one request with -1 (tokens and path) ahead of the walk.
+__device__ __forceinline__ void tree_clear_outputs(const LinCfg& c, const TreeCfg& tc, int64_t b) {
+  const int D = tc.D;
+  for (int i = threadIdx.x; i <= D; i += blockDim.x) c.out_tokens[b * (D + 1) + i] = -1;
+  for (int i = threadIdx.x; i < D; i += blockDim.x) tc.out_path[b * D + i] = -1;
+}
+
+__device__ __forceinline__ void load_row_stats(TreeState& s, const RowStat* rs, int N, int row) {
+  s.mp = rs[row].m;
+  s.sp_hat = rs[row].s;
+  s.mq = rs[N + 1 + row].m;
+  s.sq_hat = rs[N + 1 + row].s;
+  s.has_exact = 0;
+  s.Sp = 0.0;
+  s.Sq = 0.0;
+  s.cj = 0.0;
+  s.Gj = 1.0;
+  s.j = 0;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------- node drafts --
+// Node n, the j-th child of row r, drawn from row r of q with draw id
+// kDrawDraft + j; -1 for every node when any draft row of the request is invalid.
+template <int DT>
+__global__ __launch_bounds__(kWG) void k_tree_draft(LinCfg c, TreeTopo tp, TreeCfg tc) {
+  const int N = tc.N, R = N + 1, nsb = c.nsb, t = threadIdx.x;
+  const int64_t b = blockIdx.x / N;
+  const int n = (int)(blockIdx.x - b * N);
+  __shared__ int s_bad;
+  __shared__ int s_alive[kMaxNodes + 1];
+  __shared__ float shf[kWaves];
+  __shared__ double sh[kWG + kWaves];
+  for (int r = t; r < R; r += kWG) s_alive[r] = 0;
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  const DraftRec* req = c.dr + b * R * (int64_t)nsb;
+  for (int idx = t; idx < R * nsb; idx += kWG) {
+    const DraftRec r = req[idx];
+    if (isnan(r.m) || (isinf(r.m) && r.m > 0.0f) || isnan(r.s)) atomicOr(&s_bad, 1);
+    if (!is_neg_inf(r.m)) atomicOr(&s_alive[idx / nsb], 1);
+  }
+  __syncthreads();
+  int bad = s_bad;
+  for (int r = 0; r < R; ++r) bad |= !s_alive[r];
+  if (bad) {
+    if (t == 0) tc.tokens[b * N + n] = -1;
+    return;
+  }
+  const int row = tp.prow[n];
+  const int64_t qr = b * R + row;
+  const double u = c.rng.u((uint32_t)b, (uint32_t)row, kDrawDraft + (uint32_t)tp.sib[n]);
+  const int y = draft_pick<DT>(c, c.rows.q + (qr * (int64_t)c.V) * c.rows.esz, c.dr + qr * nsb, u, shf, sh);
+  if (t == 0) tc.tokens[b * N + n] = y;
+}
+
+// ------------------------------------------------------------------ walk --
+template <int DT>
+__global__ __launch_bounds__(kWG) void k_tree_walk(LinCfg c, TreeTopo tp, TreeCfg tc, int first) {
+  using E = Elem<DT>;
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x, N = tc.N, R2 = 2 * (N + 1);
+  RowStat* rs = tc.rst + b * R2;
+  __shared__ int s_bad;
+  __shared__ double sh[kWaves];
+  TreeState s;
+  if (first) {
+    if (t == 0) s_bad = 0;
+    __syncthreads();
+    for (int i = t; i < R2; i += kWG) {
+      // same reduction as the linear decide step, so that a chain-shaped tree
+      // reproduces the linear result bit for bit
+      const StatRec* rec = c.st + (b * R2 + i) * (int64_t)c.nch32;
+      float m = -INFINITY;
+      for (int ch = 0; ch < c.nch32; ++ch) m = fmaxnan(m, rec[ch].m);
+      double S = 0.0;
+      int bad = isnan(m) || isinf(m);
+      if (!bad)
+        for (int ch = 0; ch < c.nch32; ++ch) {
+          const StatRec r = rec[ch];
+          if (isnan(r.s)) bad = 1;
+          else if (!is_neg_inf(r.m)) S += r.s * ::exp2(((double)r.m - (double)m) * (double)c.c32);
+        }
+      if (!(S > 0.0)) bad = 1;
+      RowStat o;
+      o.m = m;
+      o.bad = bad;
+      o.s = S;
+      rs[i] = o;
+      if (bad) atomicOr(&s_bad, 1);
+    }
+    for (int n = t; n < N; n += kWG) {
+      const int x = tc.tokens[b * N + n];
+      if (x < 0 || x >= c.V) atomicOr(&s_bad, 1);
+    }
+    tree_clear_outputs(c, tc, b);
+    __syncthreads();
+    if (s_bad) {
+      if (t == 0) {
+        c.out_len[b] = -1;
+        TreeState d = {};
+        d.phase = kTreeDone;
+        tc.ts[b] = d;
+      }
+      return;
+    }
+    if (t != 0) return;
+    s = {};
+    s.row = 0;
+    s.len = 0;
+    s.phase = kTreeTest;
+    load_row_stats(s, rs, N, 0);
+  } else {
+    s = tc.ts[b];
+    if (s.phase != kTreeWaitG) return;
+    // fp64-grade normalisers of the row pair and G(c_new) from the row pass
+    const TreeRes* rr = tc.tres + b * c.nsb;
+    double sp = 0.0, sq = 0.0;
+    for (int sb = t; sb < c.nsb; sb += kWG) {
+      sp += rr[sb].sp;
+      sq += rr[sb].sq;
+    }
+    const double Sp = block_sum(sp, sh);
+    const double Sq = block_sum(sq, sh);
+    double g = 0.0;
+    for (int sb = t; sb < c.nsb; sb += kWG) g += fmax(0.0, rr[sb].a / Sp - s.c_new * rr[sb].bq / Sq);
+    const double G = block_sum(g, sh);
+    if (t != 0) return;
+    s.Sp = Sp;
+    s.Sq = Sq;
+    s.has_exact = 1;
+    if (G > 0.0) {
+      s.cj = s.c_new;
+      s.Gj = G;
+    }
+    s.phase = kTreeTest;
+  }
+  // thread 0: accept tests down the tree until the next rejection
+  const int D = tc.D;
+  for (;;) {
+    const int row = s.row;
+    const int k0 = tp.off[row], nk = tp.off[row + 1] - k0;
+    if (nk == 0) {  // leaf: draw from P
+      s.phase = kTreeFinal;
+      s.c_new = 0.0;
+      s.c_old = 0.0;
+      break;
+    }
+    const int child = tp.kids[k0 + s.j];
+    const int tok = tc.tokens[b * N + child];
+    const float ap = E::load1(tree_prow(c, b, row), tok);
+    const float aq = E::load1(tree_qrow(c, b, row), tok);
+    double P, Q;
+    if (s.has_exact) {
+      P = exp2_poly(((double)ap - (double)s.mp) * c.c64) / s.Sp;
+      Q = exp2_poly(((double)aq - (double)s.mq) * c.c64) / s.Sq;
+    } else {
+      P = ::exp(((double)ap - (double)s.mp) * c.invT - ::log(s.sp_hat));
+      Q = ::exp(((double)aq - (double)s.mq) * c.invT - ::log(s.sq_hat));
+    }
+    const double r = s.cj == 0.0 ? P : fmax(0.0, P - s.cj * Q) / s.Gj;
+    const double u = c.rng.u((uint32_t)b, (uint32_t)row, (uint32_t)(kDrawAccept + s.j));
+    if (u * Q < r) {
+      tc.out_path[b * D + s.len] = child;
+      c.out_tokens[b * (D + 1) + s.len] = tok;
+      ++s.len;
+      s.row = child + 1;
+      load_row_stats(s, rs, N, s.row);
+      continue;
+    }
+    ++s.j;
+    s.c_old = s.cj;
+    s.c_new = s.cj + s.Gj;
+    s.phase = s.j < nk ? kTreeWaitG : kTreeFinal;
+    break;
+  }
+  tc.ts[b] = s;
+}
+
+// -------------------------------------------------------------- row pass --
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_tree_pass(LinCfg c, TreeCfg tc, int final_pass) {
+  constexpr int EPV = Elem<DT>::kPerVec;
+  constexpr int VPL = kSB / (kWave * EPV);
+  const int64_t b = blockIdx.y;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int sb = blockIdx.x * kWaves + wave;
+  if (sb >= c.nsb) return;
+  const TreeState s = tc.ts[b];
+  if (s.phase != (final_pass ? kTreeFinal : kTreeWaitG)) return;
+  const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
+  TreeRes out = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  const double mp = s.mp, mq = s.mq;
+  if (s.c_new == 0.0 && s.c_old == 0.0) {  // draw from P: target row only
+    float x[VPL][EPV];
+    load_vecs<DT, AL, VPL, kWave>(tree_prow(c, b, s.row), c.V, c.nvec, vfirst, x);
+    double sp = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) sp += exp2_poly(((double)x[v][e] - mp) * c.c64);
+    out.sp = wave_sum(sp);
+    out.a = out.sp;
+    out.a0 = out.sp;
+  } else {
+    float xp[VPL][EPV], xq[VPL][EPV];
+    load_vecs<DT, AL, VPL, kWave>(tree_prow(c, b, s.row), c.V, c.nvec, vfirst, xp);
+    load_vecs<DT, AL, VPL, kWave>(tree_qrow(c, b, s.row), c.V, c.nvec, vfirst, xq);
+    // membership of P > c Q is decided with the best normalisers at hand;
+    // entries near the boundary carry almost no weight either way
+    const double sph = s.has_exact ? s.Sp : s.sp_hat, sqh = s.has_exact ? s.Sq : s.sq_hat;
+    const double c1 = s.c_new, c0 = s.c_old;
+    double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0, a0 = 0.0, bq0 = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const double ep = exp2_poly(((double)xp[v][e] - mp) * c.c64);
+        const double eq = exp2_poly(((double)xq[v][e] - mq) * c.c64);
+        sp += ep;
+        sq += eq;
+        if (ep * sqh > c1 * (eq * sph)) {
+          a += ep;
+          bq += eq;
+        }
+        if (ep * sqh > c0 * (eq * sph)) {
+          a0 += ep;
+          bq0 += eq;
+        }
+      }
+    out.sp = wave_sum(sp);
+    out.sq = wave_sum(sq);
+    out.a = wave_sum(a);
+    out.bq = wave_sum(bq);
+    out.a0 = wave_sum(a0);
+    out.bq0 = wave_sum(bq0);
+  }
+  if (lane == 0) tc.tres[b * c.nsb + sb] = out;
+}
+
+// ------------------------------------------------------------ final pick --
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_tree_pick(LinCfg c, TreeCfg tc) {
+  using E = Elem<DT>;
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x;
+  const TreeState s = tc.ts[b];
+  if (s.phase != kTreeFinal) return;
+  const int nsb = c.nsb, D = tc.D;
+  const TreeRes* rr = tc.tres + b * nsb;
+  __shared__ double sh[kWG + kWaves];
+  const char* prow = tree_prow(c, b, s.row);
+  const char* qrow = tree_qrow(c, b, s.row);
+  const double mp = s.mp, mq = s.mq, c64 = c.c64;
+  const double u = c.rng.u((uint32_t)b, (uint32_t)s.row, kDrawFinal);
+  int y;
+  if (s.c_new == 0.0) {
+    // leaf: unnormalised target weights, as for the bonus draw of the linear path
+    double mine = 0.0;
+    for (int sb = t; sb < nsb; sb += kWG) mine += rr[sb].sp;
+    const double W = block_sum(mine, sh);
+    y = pick_index(
+        nsb, c.V, u * W, [&](int sb) { return rr[sb].sp; },
+        [&](int64_t j) { return exp2_poly(((double)E::load1(prow, j) - mp) * c64); }, sh);
+  } else {
+    double a = 0.0, q = 0.0;
+    for (int sb = t; sb < nsb; sb += kWG) {
+      a += rr[sb].sp;
+      q += rr[sb].sq;
+    }
+    const double Sp = block_sum(a, sh);
+    const double Sq = block_sum(q, sh);
+    const double c1 = s.c_new;
+    double mine = 0.0;
+    for (int sb = t; sb < nsb; sb += kWG) mine += fmax(0.0, rr[sb].a / Sp - c1 * rr[sb].bq / Sq);
+    const double G1 = block_sum(mine, sh);
+    if (G1 > 0.0) {
+      y = pick_index(
+          nsb, c.V, u * G1, [&](int sb) { return fmax(0.0, rr[sb].a / Sp - c1 * rr[sb].bq / Sq); },
+          [&](int64_t j) {
+            const double ep = exp2_poly(((double)E::load1(prow, j) - mp) * c64);
+            const double eq = exp2_poly(((double)E::load1(qrow, j) - mq) * c64);
+            return fmax(0.0, ep / Sp - c1 * eq / Sq);
+          },
+          sh);
+    } else if (s.c_old > 0.0) {
+      // (r - Q)+ vanished: r stays (P - c_old Q)+ / G(c_old)
+      const double c0 = s.c_old;
+      double m0 = 0.0;
+      for (int sb = t; sb < nsb; sb += kWG) m0 += fmax(0.0, rr[sb].a0 / Sp - c0 * rr[sb].bq0 / Sq);
+      const double G0 = block_sum(m0, sh);
+      y = pick_index(
+          nsb, c.V, u * G0, [&](int sb) { return fmax(0.0, rr[sb].a0 / Sp - c0 * rr[sb].bq0 / Sq); },
+          [&](int64_t j) {
+            const double ep = exp2_poly(((double)E::load1(prow, j) - mp) * c64);
+            const double eq = exp2_poly(((double)E::load1(qrow, j) - mq) * c64);
+            return fmax(0.0, ep / Sp - c0 * eq / Sq);
+          },
+          sh);
+    } else {
+      // (P - Q)+ vanished: r stays P
+      double m0 = 0.0;
+      for (int sb = t; sb < nsb; sb += kWG) m0 += rr[sb].sp;
+      const double W = block_sum(m0, sh);
+      y = pick_index(
+          nsb, c.V, u * W, [&](int sb) { return rr[sb].sp; },
+          [&](int64_t j) { return exp2_poly(((double)E::load1(prow, j) - mp) * c64); }, sh);
+    }
+  }
+  if (t == 0) {
+    c.out_tokens[b * (D + 1) + s.len] = y;
+    c.out_len[b] = s.len;
+    TreeState d = s;
+    d.phase = kTreeDone;
+    tc.ts[b] = d;
+  }
+}
+
+// ---------------------------------------------------------------- greedy --
+__global__ __launch_bounds__(kWG) void k_tree_greedy(LinCfg c, TreeTopo tp, TreeCfg tc) {
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x, N = tc.N, D = tc.D, R2 = 2 * (N + 1);
+  __shared__ int s_bad, s_badq;
+  __shared__ int s_g[2 * (kMaxNodes + 1)];
+  __shared__ int s_tok[kMaxNodes];
+  if (t == 0) {
+    s_bad = 0;
+    s_badq = 0;
+  }
+  __syncthreads();
+  for (int i = t; i < R2; i += kWG) {
+    int bad;
+    s_g[i] = row_argmax(c.ar + (b * R2 + i) * (int64_t)c.nch32, c.nch32, &bad);
+    if (bad) {
+      atomicOr(&s_bad, 1);
+      if (i > N) atomicOr(&s_badq, 1);
+    }
+  }
+  __syncthreads();
+  for (int n = t; n < N; n += kWG) {
+    int x;
+    if (c.fused) {
+      x = s_badq ? -1 : s_g[N + 1 + tp.prow[n]];  // argmax of the parent row's draft logits
+      tc.tokens[b * N + n] = x;
+    } else {
+      x = tc.tokens[b * N + n];
+    }
+    s_tok[n] = x;
+    if (x < 0 || x >= c.V) atomicOr(&s_bad, 1);
+  }
+  tree_clear_outputs(c, tc, b);
+  __syncthreads();
+  if (t != 0) return;
+  if (s_bad) {
+    c.out_len[b] = -1;
+    return;
+  }
+  int row = 0, len = 0;
+  for (;;) {
+    const int g = s_g[row];
+    int acc = -1;
+    for (int k = tp.off[row]; k < tp.off[row + 1]; ++k)
+      if (s_tok[tp.kids[k]] == g) {
+        acc = tp.kids[k];
+        break;
+      }
+    if (acc < 0) {
+      c.out_tokens[b * (D + 1) + len] = g;
+      break;
+    }
+    tc.out_path[b * D + len] = acc;
+    c.out_tokens[b * (D + 1) + len] = g;
+    ++len;
+    row = acc + 1;
+  }
+  c.out_len[b] = len;
+}
+
+// -------------------------------------------------------------- filtered --
+// Union of the kept sets of a target row and a draft row, in token-id order.
+constexpr int kUnion = 2 * kMaxTopK;
+
+__global__ __launch_bounds__(kWG) void k_tree_filt(LinCfg c, FiltCfg f, TreeTopo tp, TreeCfg tc) {
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x, N = tc.N, D = tc.D, R2 = 2 * (N + 1);
+  const FiltRow* H = f.hdr + b * R2;
+  const FiltEnt* Ent = f.ent + b * R2 * (int64_t)f.stride;
+  __shared__ int s_bad, s_badq;
+  __shared__ int s_id[kUnion];
+  __shared__ int s_tok[kMaxNodes];
+  __shared__ double s_r[kUnion], s_q[kUnion], s_pe[kMaxTopK], s_qe[kMaxTopK];
+  if (t == 0) {
+    s_bad = 0;
+    s_badq = 0;
+  }
+  __syncthreads();
+  for (int i = t; i < R2; i += kWG)
+    if (H[i].bad || H[i].cnt <= 0) {
+      atomicOr(&s_bad, 1);
+      if (i > N) atomicOr(&s_badq, 1);
+    }
+  __syncthreads();
+  for (int n = t; n < N; n += kWG) {
+    int x;
+    if (c.fused) {
+      x = -1;
+      if (!s_badq) {
+        const int r = tp.prow[n];
+        const FiltRow hq = H[N + 1 + r];
+        const FiltEnt* eq = Ent + (N + 1 + r) * (int64_t)f.stride;
+        const double u = c.rng.u((uint32_t)b, (uint32_t)r, kDrawDraft + (uint32_t)tp.sib[n]);
+        x = draw_list(hq.cnt, u, [&](int k) { return ::exp(eq[k].z - hq.m); }, eq);
+      }
+      tc.tokens[b * N + n] = x;
+    } else {
+      x = tc.tokens[b * N + n];
+    }
+    s_tok[n] = x;
+    if (x < 0 || x >= c.V) atomicOr(&s_bad, 1);
+  }
+  tree_clear_outputs(c, tc, b);
+  __syncthreads();
+  if (s_bad) {
+    if (t == 0) c.out_len[b] = -1;
+    return;
+  }
+  int row = 0, len = 0;  // uniform across the workgroup
+  for (;;) {
+    const FiltRow hp = H[row], hq = H[N + 1 + row];
+    const FiltEnt* ep = Ent + row * (int64_t)f.stride;
+    const FiltEnt* eq = Ent + (N + 1 + row) * (int64_t)f.stride;
+    const int k0 = tp.off[row], nk = tp.off[row + 1] - k0;
+    // normalised probabilities of the two kept sets
+    for (int k = t; k < hp.cnt; k += kWG) s_pe[k] = ::exp(ep[k].z - hp.L);
+    for (int k = t; k < hq.cnt; k += kWG) s_qe[k] = ::exp(eq[k].z - hq.L);
+    __syncthreads();
+    __shared__ int s_next, s_y;
+    if (t == 0) {
+      int y = -1, next = -1;
+      if (nk == 0) {
+        const double u = c.rng.u((uint32_t)b, (uint32_t)row, kDrawFinal);
+        y = draw_list(hp.cnt, u, [&](int k) { return s_pe[k]; }, ep);
+      } else {
+        // merge the two id-ordered lists
+        int nu = 0, i = 0, k = 0;
+        while (i < hp.cnt || k < hq.cnt) {
+          const int ip = i < hp.cnt ? ep[i].i : 0x7fffffff;
+          const int iq = k < hq.cnt ? eq[k].i : 0x7fffffff;
+          const int id = min(ip, iq);
+          s_id[nu] = id;
+          s_r[nu] = id == ip ? s_pe[i++] : 0.0;
+          s_q[nu] = id == iq ? s_qe[k++] : 0.0;
+          ++nu;
+        }
+        auto find = [&](int x) {
+          int lo = 0, hi = nu - 1;
+          while (lo <= hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_id[mid] == x) return mid;
+            if (s_id[mid] < x) lo = mid + 1;
+            else hi = mid - 1;
+          }
+          return -1;
+        };
+        for (int j = 0; j < nk; ++j) {
+          const int child = tp.kids[k0 + j];
+          const int tok = s_tok[child];
+          const int at = find(tok);
+          const double Qt = at >= 0 ? s_q[at] : 0.0, rt = at >= 0 ? s_r[at] : 0.0;
+          const double u = c.rng.u((uint32_t)b, (uint32_t)row, (uint32_t)(kDrawAccept + j));
+          if (u * Qt < rt) {
+            next = child;
+            break;
+          }
+          double S = 0.0;
+          for (int e = 0; e < nu; ++e) S += fmax(0.0, s_r[e] - s_q[e]);
+          if (S > 0.0)
+            for (int e = 0; e < nu; ++e) s_r[e] = fmax(0.0, s_r[e] - s_q[e]) / S;
+        }
+        if (next < 0) {
+          const double u = c.rng.u((uint32_t)b, (uint32_t)row, kDrawFinal);
+          double W = 0.0;
+          for (int e = 0; e < nu; ++e) W += s_r[e];
+          const double target = u * W;
+          double acc = 0.0;
+          int last = -1;
+          for (int e = 0; e < nu; ++e) {
+            acc += s_r[e];
+            if (s_r[e] > 0.0) last = e;
+            if (acc > target) {
+              y = s_id[e];
+              break;
+            }
+          }
+          if (y < 0 && last >= 0) y = s_id[last];
+        }
+      }
+      s_next = next;
+      s_y = y;
+    }
+    __syncthreads();
+    const int next = s_next;
+    if (next < 0) {
+      if (t == 0) {
+        c.out_tokens[b * (D + 1) + len] = s_y;
+        c.out_len[b] = len;
+      }
+      return;
+    }
+    if (t == 0) {
+      tc.out_path[b * D + len] = next;
+      c.out_tokens[b * (D + 1) + len] = s_tok[next];
+    }
+    ++len;
+    row = next + 1;
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------- launchers --
+template <int DT, bool AL>
+static hipError_t tree_sampled_t(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int rounds, hipStream_t s) {
+  const dim3 pass_grid((c.nsb + kWaves - 1) / kWaves, (unsigned)c.B);
+  hipLaunchKernelGGL((k_tree_walk<DT>), dim3((unsigned)c.B), dim3(kWG), 0, s, c, tp, tc, 1);
+  for (int r = 0; r < rounds; ++r) {
+    hipLaunchKernelGGL((k_tree_pass<DT, AL>), pass_grid, dim3(kWG), 0, s, c, tc, 0);
+    hipLaunchKernelGGL((k_tree_walk<DT>), dim3((unsigned)c.B), dim3(kWG), 0, s, c, tp, tc, 0);
+  }
+  hipLaunchKernelGGL((k_tree_pass<DT, AL>), pass_grid, dim3(kWG), 0, s, c, tc, 1);
+  hipLaunchKernelGGL((k_tree_pick<DT, AL>), dim3((unsigned)c.B), dim3(kWG), 0, s, c, tc);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_sampled(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int rounds, int dtype,
+                               hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (c.fused) {
+    // node drafts: fp64 sub-block records of every draft row, then one pick per node
+    e = launch_draftpass(c, c.B * (int64_t)(tc.N + 1), dtype, s);
+    if (e != hipSuccess) return e;
+    if (dtype == kBF16) hipLaunchKernelGGL((k_tree_draft<kBF16>), dim3((unsigned)(c.B * tc.N)), dim3(kWG), 0, s, c, tp, tc);
+    else hipLaunchKernelGGL((k_tree_draft<kF32>), dim3((unsigned)(c.B * tc.N)), dim3(kWG), 0, s, c, tp, tc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  e = launch_stats32(c, c.B * (int64_t)(2 * (tc.N + 1)), dtype, s);
+  if (e != hipSuccess) return e;
+  if (dtype == kBF16)
+    return c.aligned ? tree_sampled_t<kBF16, true>(c, tp, tc, rounds, s)
+                     : tree_sampled_t<kBF16, false>(c, tp, tc, rounds, s);
+  return c.aligned ? tree_sampled_t<kF32, true>(c, tp, tc, rounds, s) : tree_sampled_t<kF32, false>(c, tp, tc, rounds, s);
+}
+
+hipError_t launch_tree_greedy(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int dtype, hipStream_t s) {
+  hipError_t e = launch_argmax(c, c.B * (int64_t)(2 * (tc.N + 1)), dtype, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_tree_greedy, dim3((unsigned)c.B), dim3(kWG), 0, s, c, tp, tc);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_filtered(const LinCfg& c, const FiltCfg& f, const TreeTopo& tp, const TreeCfg& tc, int dtype,
+                                hipStream_t s) {
+  hipError_t e = launch_filter_rows(c, f, c.B * (int64_t)(2 * (tc.N + 1)), dtype, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_tree_filt, dim3((unsigned)c.B), dim3(kWG), 0, s, c, f, tp, tc);
+  return hipGetLastError();
+}
+
+}  // namespace psi

@@ -68,3 +68,21 @@ def compare_linear(g: dict, o: dict, check_probs=True, check_resid=True):
     K = ot.shape[1] - 1
     decisions = sum(min(int(n) + 1, K) + 1 for n in ol if n >= 0)
     return excused, max(decisions, 1), int(near.sum())
+
+
+def compare_tree(g: dict, o: dict):
+    """Tree outputs: len, tokens and path identical per request, except requests
+    whose oracle decisions include a near tie. Returns (excused, near_ties)."""
+    gl = g["len"].cpu().numpy()
+    gt = g["tokens"].cpu().numpy()
+    gp = g["path"].cpu().numpy()
+    ol, ot, op = o["len"], o["tokens"], o["path"]
+    near = (o["margin_acc"] < NEAR_TIE_ACCEPT) | (o["margin_cdf"] < NEAR_TIE_CDF)
+    excused = 0
+    for b in range(len(ol)):
+        if gl[b] == ol[b] and np.array_equal(gt[b], ot[b]) and np.array_equal(gp[b], op[b]):
+            continue
+        assert near[b], (f"request {b}: gpu len {gl[b]} path {gp[b].tolist()} tokens {gt[b].tolist()} vs oracle "
+                         f"len {ol[b]} path {op[b].tolist()} tokens {ot[b].tolist()}")
+        excused += 1
+    return excused, int(near.sum())
