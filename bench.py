@@ -1,19 +1,29 @@
 """Benchmark of lossless Psi-Spec block verification on one MI355X.
 
-Workload (high-concurrency linear verification): B=256 requests, K=8 draft
-positions, V=151936 vocabulary, bfloat16 logits, temperature 1, draft/target
-correlation rho swept over {0.5, 0.8, 0.95}; one psispec_verify_linear call per
-decode step, step t using pre-drawn draft set t (drawn on the GPU with
-psispec_draft_sample before the timed region). Inputs are synthetic (seeded,
-see synth/) and resident in HBM before timing starts.
+Headline workload (high-concurrency linear verification): B=256 requests, K=8
+draft positions, V=151936 vocabulary, bfloat16 logits, temperature 1,
+draft/target correlation rho swept over {0.5, 0.8, 0.95}; one
+psispec_verify_linear call per decode step, step t using pre-drawn draft set t
+(drawn on the GPU with psispec_draft_sample before the timed region). Inputs are
+synthetic (seeded, see synth/) and resident in HBM before timing starts.
 
-Prints ONE JSON line: verified (request, position) rows/s over the whole sweep
-(value), emitted tokens/s, the HBM roofline fraction of the verify call, and the
-CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line:
+  value          verified (request, position) rows/s over the whole rho sweep;
+  roofline       the dominant kernel (the statistics pass that streams every
+                 logit once), its duration measured live with HIP events that
+                 the library records around each of its launches;
+  kernels        mean duration of every kernel of the verify call;
+  workloads      the other workloads of the method (fused-draft linear,
+                 filtered, greedy, tree), each timed with HIP events;
+  cpu_baseline   the CPU oracle on a bounded sample of the headline workload.
+
+--calibrate-copy runs only a plain device copy of a known size (for scaling
+the HBM byte counters of a profiler run) and prints its size.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -28,12 +38,45 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, AMD public specification
 B, K, V = 256, 8, 151936
 RHOS = (0.5, 0.8, 0.95)
 T = 1.0
+LINEAR_KERNELS = ("k_stats32", "k_decide", "k_pass64", "k_final")
+PMC_FILE = os.path.join(ROOT, "profiles", "k_stats32_highconc_pmc.txt")
+KERNEL_SOURCES = ("device.hpp", "rowops.hpp", "kernels.hpp", "linear.hip")
 
 
 def bytes_alg(B, K, V, esz=2):
     """Algorithmic HBM bytes of one verify call: every target and draft logit
     read once, draft ids read, output tokens/lengths written."""
     return B * (2 * K + 1) * V * esz + 4 * B * K + 4 * B * (K + 2)
+
+
+def stats_bytes(B, K, V, esz=2):
+    """Algorithmic bytes of one statistics-pass launch: every logit once."""
+    return B * (2 * K + 1) * V * esz
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "lossless_speculative_verification_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic():
+    """HBM bytes per statistics-pass launch from the committed counter summary,
+    or None when it is missing or was taken on other kernel sources."""
+    try:
+        kv = {}
+        with open(PMC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k_, v_ = line.split(":", 1)
+                    kv[k_.strip()] = v_.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(p, q, drafts, seed, budget_s=10.0, threads=16):
@@ -55,14 +98,116 @@ def cpu_baseline(p, q, drafts, seed, budget_s=10.0, threads=16):
                       f"{wall:.1f} s wall"}
 
 
+def to_dev(a, torch, dev):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def time_calls(torch, fn, n, warm, stream):
+    """Mean ms per call over n calls after warm calls, HIP events on `stream`."""
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(warm, warm + n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def other_workloads(torch, psi, synth, dev, stream, steps, seed):
+    """The remaining workloads of the method, each timed over `steps` calls."""
+    res = {}
+
+    def line(name, ms, nbytes, rows, extra):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        d = {"us_per_call": 1e3 * ms, "bytes_alg": nbytes, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+             "rows_per_s": rows / (ms * 1e-3)}
+        d.update(extra)
+        res[name] = d
+        print(f"# {name}: {1e3 * ms:.1f} us/call, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+
+    # Fused-draft linear verify, B=64 K=8 V=151936 bf16, T=0.7; two input copies
+    # rotate so the 330 MB working set does not sit in the 256 MB last-level cache.
+    w = synth.WORKLOADS["qwen"]
+    Bq, Kq, Vq = w["B"], w["K"], w["V"]
+    copies = []
+    for c in range(2):
+        p, q = synth.linear_inputs("qwen", seed=seed + c)
+        copies.append((to_dev(p, torch, dev), to_dev(q, torch, dev)))
+    ws = torch.empty(psi.workspace_bytes(Bq, 2 * Kq + 1, Vq, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+    dr = torch.empty((Bq, Kq), dtype=torch.int32, device=dev)
+    outs = dict(tokens=torch.empty((Bq, Kq + 1), dtype=torch.int32, device=dev),
+                len=torch.empty((Bq,), dtype=torch.int32, device=dev))
+    Tq = float(np.float32(w["temperature"]))
+    ms = time_calls(torch, lambda i: psi.verify_linear(*copies[i % 2], dr, temperature=Tq, seed=seed, step=i,
+                                                         fused=True, out=outs, workspace=ws, stream=stream),
+                    steps, 5, stream)
+    line("qwen_fused_B64_K8_V151936_bf16", ms, bytes_alg(Bq, Kq, Vq), Bq * Kq, {"temperature": Tq})
+    del copies, ws
+    torch.cuda.empty_cache()
+
+    # Filtered (top-k 50, top-p 0.95) and greedy, B=128 K=16 V=128256 fp32, fused drafts.
+    w = synth.WORKLOADS["filtered"]
+    Bf, Kf, Vf = w["B"], w["K"], w["V"]
+    p, q = synth.linear_inputs("filtered", seed=seed)
+    pd, qd = to_dev(p, torch, dev), to_dev(q, torch, dev)
+    del p, q
+    ws = torch.empty(psi.workspace_bytes(Bf, 2 * Kf + 1, Vf, psi.DTYPE_F32), dtype=torch.uint8, device=dev)
+    dr = torch.empty((Bf, Kf), dtype=torch.int32, device=dev)
+    outs = dict(tokens=torch.empty((Bf, Kf + 1), dtype=torch.int32, device=dev),
+                len=torch.empty((Bf,), dtype=torch.int32, device=dev))
+    top_p = float(np.float32(w["top_p"]))
+    ms = time_calls(torch, lambda i: psi.verify_linear(pd, qd, dr, temperature=1.0, top_k=w["top_k"], top_p=top_p,
+                                                         seed=seed, step=i, fused=True, out=outs, workspace=ws,
+                                                         stream=stream), steps, 3, stream)
+    line("filtered_topk50_topp0.95_B128_K16_V128256_f32", ms, bytes_alg(Bf, Kf, Vf, 4), Bf * Kf, {})
+    ms = time_calls(torch, lambda i: psi.verify_linear(pd, qd, dr, temperature=0.0, fused=True, out=outs,
+                                                         workspace=ws, stream=stream), steps, 3, stream)
+    line("greedy_B128_K16_V128256_f32", ms, bytes_alg(Bf, Kf, Vf, 4), Bf * Kf, {})
+    del pd, qd, ws
+    torch.cuda.empty_cache()
+
+    # Tree: 4 branches of 8-node chains, p and q [4, 33, 151936] bf16, fused node
+    # drafts; four input copies rotate (80 MB each).
+    w = synth.WORKLOADS["tree"]
+    Bt, Nt, Vt = w["B"], w["N"], w["V"]
+    parent = synth.branch_chain_parent(4, 8)
+    copies = []
+    for c in range(4):
+        p, q = synth.tree_inputs("tree", seed=seed + c)
+        copies.append((to_dev(p, torch, dev), to_dev(q, torch, dev)))
+    ws = torch.empty(psi.workspace_bytes(Bt, 2 * (Nt + 1), Vt, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+    nodes = torch.empty((Bt, Nt), dtype=torch.int32, device=dev)
+    D = 8
+    outs = dict(tokens=torch.empty((Bt, D + 1), dtype=torch.int32, device=dev),
+                path=torch.empty((Bt, D), dtype=torch.int32, device=dev),
+                len=torch.empty((Bt,), dtype=torch.int32, device=dev))
+    ms = time_calls(torch, lambda i: psi.verify_tree(*copies[i % 4], parent, nodes, temperature=1.0, seed=seed,
+                                                       step=i, fused=True, out=outs, workspace=ws, stream=stream),
+                    steps, 5, stream)
+    line("tree_4x8_B4_N32_V151936_bf16", ms, Bt * 2 * (Nt + 1) * Vt * 2 + 4 * Bt * Nt + 4 * Bt * (2 * D + 2),
+         Bt * (Nt + 1), {"note": "latency-bound: 10 kernel launches per call"})
+    del copies, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--breakdown-steps", type=int, default=200)
+    ap.add_argument("--workload-steps", type=int, default=50)
+    ap.add_argument("--no-workloads", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): verification shards by request "
@@ -71,11 +216,22 @@ def main():
 
     import torch
 
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+        return
+
     import lossless_speculative_verification_amd as psi
     import synth
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     steps, warm = args.steps, args.warmup
     ws = torch.empty(psi.workspace_bytes(B, 2 * K + 1, V, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(psi.workspace_bytes(B, K, V, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
@@ -84,27 +240,29 @@ def main():
     out_probs = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
     out_resid = torch.empty((B,), dtype=torch.float64, device=dev)
     drafts = torch.empty((steps + warm, B, K), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    nb = max(1, min(args.breakdown_steps, steps))
+    timer = psi.KernelTimer(nb * len(RHOS), len(LINEAR_KERNELS) + 1)
 
     per_rho = []
     total_rows = 0
     total_time = 0.0
     total_emitted = 0
-    kernel_ms = []
+    call_ms = []
     host_inputs = None
     p_np = np.empty((B, K + 1, V), dtype=np.uint16)
     q_np = np.empty((B, K, V), dtype=np.uint16)
-    for rho in RHOS:
+    for ri, rho in enumerate(RHOS):
         synth.pair(B, K + 1, K, V, "bf16", seed=args.seed, out_p=p_np, out_q=q_np,
                    **{**synth.RECIPES["highconc"], "rho": rho})
-        p = torch.from_numpy(p_np.view(np.int16)).view(torch.bfloat16).to(dev)
-        q = torch.from_numpy(q_np.view(np.int16)).view(torch.bfloat16).to(dev)
+        p = to_dev(p_np, torch, dev)
+        q = to_dev(q_np, torch, dev)
         # pre-drawn draft sets (untimed): set t is used at step t
         for t in range(steps + warm):
             psi.draft_sample(q, temperature=T, seed=args.seed, step=t, out=drafts[t], workspace=ws_d)
         torch.cuda.synchronize()
         if rho == 0.8 and not args.no_cpu_baseline:
             host_inputs = (p_np.copy(), q_np.copy(), drafts[:64].cpu().numpy())
-        stream = torch.cuda.current_stream()
 
         def call(t):
             psi.verify_linear(p, q, drafts[t], temperature=T, seed=args.seed, step=t,
@@ -127,18 +285,35 @@ def main():
         lens = out_len[warm:warm + steps].cpu().numpy()
         assert (lens >= 0).all()
         emitted = int((lens + 1).sum())
+        # per-kernel breakdown: the library records an event around each launch
+        for i in range(nb):
+            timer.arm(ri * nb + i)
+            call(warm + i)
+            timer.note()
+        timer.disarm()
+        torch.cuda.synchronize()
         per_rho.append({"rho": rho, "ms_per_step": 1e3 * wall / steps, "event_ms_per_step": ev_ms / steps,
                         "rows_per_s": B * K * steps / wall, "emitted_tok_per_s": emitted / wall,
                         "mean_accepted": float(lens.mean()), "mean_emitted": float((lens + 1).mean())})
-        kernel_ms.append(ev_ms / steps)
+        print(f"# rho {rho}: {1e3 * ev_ms / steps:.1f} us/call, mean emitted {float((lens + 1).mean()):.3f}",
+              file=sys.stderr, flush=True)
+        call_ms.append(ev_ms / steps)
         total_rows += B * K * steps
         total_time += wall
         total_emitted += emitted
         del p, q
         torch.cuda.empty_cache()
 
-    call_ms = float(np.mean(kernel_ms))
-    achieved = bytes_alg(B, K, V) / (call_ms * 1e-3) / 1e9
+    dur = timer.durations()  # [calls, kernels] ms
+    kmean = np.nanmean(dur, axis=0)
+    kernels = {name: {"us_mean": 1e3 * float(kmean[j]), "us_median": 1e3 * float(np.nanmedian(dur[:, j]))}
+               for j, name in enumerate(LINEAR_KERNELS)}
+    stats_ms = float(kmean[0])
+    achieved = stats_bytes(B, K, V) / (stats_ms * 1e-3) / 1e9
+    call_avg = float(np.mean(call_ms))
+    call_gbs = bytes_alg(B, K, V) / (call_avg * 1e-3) / 1e9
+    traffic = pmc_traffic()
+
     result = {
         "metric": "verified (req·pos) rows/s + emitted tok/s; % of HBM peak, B=256 K=8 V=151936",
         "value": total_rows / total_time,
@@ -156,13 +331,18 @@ def main():
                    "B": B, "K": K, "V": V, "rho": list(RHOS), "temperature": T,
                    "steps_per_rho": steps, "parallelism": "none"},
         "emitted_tok_per_s": total_emitted / total_time,
-        "hbm_frac": achieved / HBM_PEAK_GBS,
+        "hbm_frac": call_gbs / HBM_PEAK_GBS,
+        "call": {"us_per_call": 1e3 * call_avg, "bytes_alg": bytes_alg(B, K, V), "GB_per_s": call_gbs,
+                 "hbm_frac": call_gbs / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "psispec_verify_linear (whole call)",
-                     "bytes_per_launch": bytes_alg(B, K, V), "avg_launch_ms": call_ms},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "k_stats32",
+                     "bytes_per_launch": stats_bytes(B, K, V), "avg_launch_us": 1e3 * stats_ms,
+                     "launches_timed": int(dur.shape[0])},
+        "kernels": kernels,
         "per_rho": per_rho,
     }
+    if not args.no_workloads:
+        result["workloads"] = other_workloads(torch, psi, synth, dev, stream, args.workload_steps, args.seed)
     if host_inputs is not None:
         result["cpu_baseline"] = cpu_baseline(host_inputs[0], host_inputs[1], host_inputs[2], args.seed,
                                               budget_s=args.cpu_budget)

@@ -213,6 +213,20 @@ int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, i
                         const psispec_params* params, int32_t* out_tokens, int32_t* out_path,
                         int32_t* out_len, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Benchmark timing hook (not part of the method; for measuring each kernel of
+ * a call live on the caller's stream). While armed with n > 0 caller-created
+ * HIP events, every compute entry point records events[0] on its stream before
+ * its first kernel and events[i] right after its i-th kernel launch (i < n),
+ * so hipEventElapsedTime(events[i-1], events[i]) brackets kernel i. The events
+ * stay owned by the caller and must outlive every armed call. The setting is
+ * process-wide and not thread-safe; events == NULL or n <= 0 disarms it.
+ */
+int psispec_set_timing_events(hipEvent_t* events, int n);
+
+/* Number of events recorded by the most recent compute call while armed. */
+int psispec_timing_count(void);
+
 /* Static message for a status code. */
 const char* psispec_strerror(int status);
 

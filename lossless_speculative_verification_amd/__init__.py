@@ -62,10 +62,70 @@ def _load():
     L.psispec_strerror.restype = ctypes.c_char_p
     L.psispec_version.argtypes = []
     L.psispec_version.restype = ctypes.c_int
+    L.psispec_set_timing_events.argtypes = [P, ctypes.c_int]
+    L.psispec_set_timing_events.restype = ctypes.c_int
+    L.psispec_timing_count.argtypes = []
+    L.psispec_timing_count.restype = ctypes.c_int
     return L
 
 
 lib = _load()
+
+
+class KernelTimer:
+    """Per-kernel durations of library calls, measured with HIP events recorded
+    by the library itself on the call's stream (psispec_set_timing_events).
+
+    Holds `calls` rows of `slots` events; `arm(i)` points the library at row i,
+    `disarm()` stops recording, `durations()` returns [calls, slots - 1] ms
+    (kernel j of call i is column j) after the stream has been synchronised.
+    """
+
+    def __init__(self, calls: int, slots: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.calls, self.slots = calls, slots
+        self._ev = (ctypes.c_void_p * (calls * slots))()
+        for i in range(calls * slots):
+            rc = self._hip.hipEventCreate(ctypes.byref(self._ev, i * ctypes.sizeof(ctypes.c_void_p)))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.recorded = [0] * calls
+
+    def arm(self, i: int):
+        self._row = i
+        lib.psispec_set_timing_events(ctypes.byref(self._ev, i * self.slots * ctypes.sizeof(ctypes.c_void_p)),
+                                      self.slots)
+
+    def note(self):
+        """Records how many events the last armed call wrote (call after it)."""
+        self.recorded[self._row] = lib.psispec_timing_count()
+
+    @staticmethod
+    def disarm():
+        lib.psispec_set_timing_events(None, 0)
+
+    def durations(self):
+        import numpy as np
+
+        out = np.full((self.calls, self.slots - 1), np.nan)
+        ms = ctypes.c_float()
+        for i in range(self.calls):
+            for j in range(1, self.recorded[i]):
+                a, b = self._ev[i * self.slots + j - 1], self._ev[i * self.slots + j]
+                if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0:
+                    out[i, j - 1] = ms.value
+        return out
+
+    def __del__(self):
+        try:
+            self.disarm()
+            for i in range(self.calls * self.slots):
+                self._hip.hipEventDestroy(self._ev[i])
+        except Exception:
+            pass
 
 
 def strerror(status: int) -> str:

@@ -7,6 +7,21 @@
 #include "kernels.hpp"
 
 namespace psi {
+
+// Benchmark timing hook: caller-owned events, recorded in order.
+static hipEvent_t* g_timing_events = nullptr;
+static int g_timing_n = 0;
+static int g_timing_next = 0;
+
+void timing_begin(hipStream_t s) {
+  g_timing_next = 0;
+  if (g_timing_events && g_timing_n > 0) hipEventRecord(g_timing_events[g_timing_next++], s);
+}
+
+void timing_mark(hipStream_t s) {
+  if (g_timing_events && g_timing_next < g_timing_n) hipEventRecord(g_timing_events[g_timing_next++], s);
+}
+
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
@@ -181,6 +196,7 @@ int psispec_draft_sample(const void* q_logits, int dtype, int64_t B, int32_t K, 
   LinCfg c;
   fill_common(c, nullptr, q_logits, dtype, B, K, V, params, workspace, 0);
   c.draft = draft_tokens;
+  timing_begin(stream);
   hipError_t e;
   if (params->temperature == 0.0f) e = launch_draft_greedy(c, dtype, stream);
   else if (filtered(params, V)) e = launch_filtered(c, filt_cfg(params, workspace, B, K, V, dtype), dtype, true, stream);
@@ -207,6 +223,7 @@ int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype,
   c.out_len = out_len;
   c.out_probs = out_probs;
   c.out_resid = out_resid_mass;
+  timing_begin(stream);
   hipError_t e;
   if (params->temperature == 0.0f) {
     e = launch_linear_greedy(c, dtype, stream);
@@ -269,6 +286,7 @@ int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, i
   tc.tres = (TreeRes*)(w + L.tres);
   tc.N = N;
   tc.D = D;
+  timing_begin(stream);
   hipError_t e;
   if (params->temperature == 0.0f) e = launch_tree_greedy(c, tp, tc, dtype, stream);
   else if (filtered(params, V)) e = launch_tree_filtered(c, filt_cfg(params, workspace, B, rows, V, dtype), tp, tc, dtype, stream);
@@ -294,5 +312,18 @@ const char* psispec_strerror(int status) {
 }
 
 int psispec_version(void) { return kVersion; }
+
+int psispec_set_timing_events(hipEvent_t* events, int n) {
+  if (events == nullptr || n <= 0) {
+    g_timing_events = nullptr;
+    g_timing_n = 0;
+    return PSISPEC_OK;
+  }
+  g_timing_events = events;
+  g_timing_n = n;
+  return PSISPEC_OK;
+}
+
+int psispec_timing_count(void) { return g_timing_next; }
 
 }  // extern "C"

@@ -330,15 +330,15 @@ __global__ __launch_bounds__(kWG) void k_filt_draft(LinCfg c, FiltCfg f) {
 template <int DT, bool AL>
 static hipError_t filtered_t(const LinCfg& c, const FiltCfg& f, bool draft_only, hipStream_t s) {
   const int64_t rows = c.B * (c.rows.np + c.rows.nq);
-  hipLaunchKernelGGL((k_filter_row<DT, AL>), dim3((unsigned)rows), dim3(kWG), 0, s, c, f);
-  if (draft_only) hipLaunchKernelGGL(k_filt_draft, dim3((unsigned)c.B), dim3(kWG), 0, s, c, f);
-  else hipLaunchKernelGGL(k_filt_decide, dim3((unsigned)c.B), dim3(kWG), 0, s, c, f);
+  PSI_LAUNCH(s, (k_filter_row<DT, AL>), dim3((unsigned)rows), dim3(kWG), c, f);
+  if (draft_only) PSI_LAUNCH(s, k_filt_draft, dim3((unsigned)c.B), dim3(kWG), c, f);
+  else PSI_LAUNCH(s, k_filt_decide, dim3((unsigned)c.B), dim3(kWG), c, f);
   return hipGetLastError();
 }
 
 template <int DT, bool AL>
 static hipError_t filter_rows_t(const LinCfg& c, const FiltCfg& f, int64_t rows, hipStream_t s) {
-  hipLaunchKernelGGL((k_filter_row<DT, AL>), dim3((unsigned)rows), dim3(kWG), 0, s, c, f);
+  PSI_LAUNCH(s, (k_filter_row<DT, AL>), dim3((unsigned)rows), dim3(kWG), c, f);
   return hipGetLastError();
 }
 

@@ -8,6 +8,19 @@
 
 namespace psi {
 
+// Benchmark timing hook (psispec_set_timing_events, capi.hip): when armed,
+// timing_begin records the first event before an entry point's first kernel
+// and timing_mark the next one after every kernel launch.
+void timing_begin(hipStream_t s);
+void timing_mark(hipStream_t s);
+
+// Every kernel launch of the library goes through PSI_LAUNCH.
+#define PSI_LAUNCH(s, kernel, grid, block, ...)                  \
+  do {                                                            \
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, __VA_ARGS__);   \
+    ::psi::timing_mark(s);                                        \
+  } while (0)
+
 constexpr int kMaxK = 64;
 constexpr int kMaxTopK = 256;  // largest top_k of the filtered path
 constexpr int kStatNV = 8;  // 16-byte vectors per thread in the fp32-grade statistics pass

@@ -478,52 +478,51 @@ __global__ __launch_bounds__(kWG) void k_greedy_draft(LinCfg c) {
 template <int DT, bool AL>
 static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
   const int64_t rows = c.B * (2 * c.K + 1);
-  hipLaunchKernelGGL((k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
-  hipLaunchKernelGGL((k_decide<DT>), dim3((unsigned)c.B), dim3(kWG), 0, s, c);
-  hipLaunchKernelGGL((k_pass64<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)c.B), dim3(kWG), 0, s, c);
-  hipLaunchKernelGGL((k_final<DT, AL>), dim3((unsigned)c.B), dim3(kWG), 0, s, c);
+  PSI_LAUNCH(s, (k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
+  PSI_LAUNCH(s, (k_decide<DT>), dim3((unsigned)c.B), dim3(kWG), c);
+  PSI_LAUNCH(s, (k_pass64<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)c.B), dim3(kWG), c);
+  PSI_LAUNCH(s, (k_final<DT, AL>), dim3((unsigned)c.B), dim3(kWG), c);
   return hipGetLastError();
 }
 
 template <int DT, bool AL>
 static hipError_t linear_greedy_t(const LinCfg& c, hipStream_t s) {
   const int64_t rows = c.B * (2 * c.K + 1);
-  hipLaunchKernelGGL((k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
-  hipLaunchKernelGGL(k_greedy_decide, dim3((unsigned)c.B), dim3(kWG), 0, s, c);
+  PSI_LAUNCH(s, (k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
+  PSI_LAUNCH(s, k_greedy_decide, dim3((unsigned)c.B), dim3(kWG), c);
   return hipGetLastError();
 }
 
 template <int DT, bool AL>
 static hipError_t draft_sampled_t(const LinCfg& c, hipStream_t s) {
-  hipLaunchKernelGGL((k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)(c.B * c.K)), dim3(kWG), 0,
-                     s, c);
-  hipLaunchKernelGGL((k_draftfinal<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kWG), 0, s, c);
+  PSI_LAUNCH(s, (k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)(c.B * c.K)), dim3(kWG), c);
+  PSI_LAUNCH(s, (k_draftfinal<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kWG), c);
   return hipGetLastError();
 }
 
 template <int DT, bool AL>
 static hipError_t draft_greedy_t(const LinCfg& c, hipStream_t s) {
   const int64_t rows = c.B * c.K;
-  hipLaunchKernelGGL((k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
-  hipLaunchKernelGGL(k_greedy_draft, dim3((unsigned)c.B), dim3(kWG), 0, s, c);
+  PSI_LAUNCH(s, (k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
+  PSI_LAUNCH(s, k_greedy_draft, dim3((unsigned)c.B), dim3(kWG), c);
   return hipGetLastError();
 }
 
 template <int DT, bool AL>
 static hipError_t stats32_t(const LinCfg& c, int64_t rows, hipStream_t s) {
-  hipLaunchKernelGGL((k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
+  PSI_LAUNCH(s, (k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
   return hipGetLastError();
 }
 
 template <int DT, bool AL>
 static hipError_t draftpass_t(const LinCfg& c, int64_t rows, hipStream_t s) {
-  hipLaunchKernelGGL((k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)rows), dim3(kWG), 0, s, c);
+  PSI_LAUNCH(s, (k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)rows), dim3(kWG), c);
   return hipGetLastError();
 }
 
 template <int DT, bool AL>
 static hipError_t argmax_t(const LinCfg& c, int64_t rows, hipStream_t s) {
-  hipLaunchKernelGGL((k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), 0, s, c);
+  PSI_LAUNCH(s, (k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
   return hipGetLastError();
 }
 

@@ -566,13 +566,13 @@ __global__ __launch_bounds__(kWG) void k_tree_filt(LinCfg c, FiltCfg f, TreeTopo
 template <int DT, bool AL>
 static hipError_t tree_sampled_t(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int rounds, hipStream_t s) {
   const dim3 pass_grid((c.nsb + kWaves - 1) / kWaves, (unsigned)c.B);
-  hipLaunchKernelGGL((k_tree_walk<DT>), dim3((unsigned)c.B), dim3(kWG), 0, s, c, tp, tc, 1);
+  PSI_LAUNCH(s, (k_tree_walk<DT>), dim3((unsigned)c.B), dim3(kWG), c, tp, tc, 1);
   for (int r = 0; r < rounds; ++r) {
-    hipLaunchKernelGGL((k_tree_pass<DT, AL>), pass_grid, dim3(kWG), 0, s, c, tc, 0);
-    hipLaunchKernelGGL((k_tree_walk<DT>), dim3((unsigned)c.B), dim3(kWG), 0, s, c, tp, tc, 0);
+    PSI_LAUNCH(s, (k_tree_pass<DT, AL>), pass_grid, dim3(kWG), c, tc, 0);
+    PSI_LAUNCH(s, (k_tree_walk<DT>), dim3((unsigned)c.B), dim3(kWG), c, tp, tc, 0);
   }
-  hipLaunchKernelGGL((k_tree_pass<DT, AL>), pass_grid, dim3(kWG), 0, s, c, tc, 1);
-  hipLaunchKernelGGL((k_tree_pick<DT, AL>), dim3((unsigned)c.B), dim3(kWG), 0, s, c, tc);
+  PSI_LAUNCH(s, (k_tree_pass<DT, AL>), pass_grid, dim3(kWG), c, tc, 1);
+  PSI_LAUNCH(s, (k_tree_pick<DT, AL>), dim3((unsigned)c.B), dim3(kWG), c, tc);
   return hipGetLastError();
 }
 
@@ -583,8 +583,8 @@ hipError_t launch_tree_sampled(const LinCfg& c, const TreeTopo& tp, const TreeCf
     // node drafts: fp64 sub-block records of every draft row, then one pick per node
     e = launch_draftpass(c, c.B * (int64_t)(tc.N + 1), dtype, s);
     if (e != hipSuccess) return e;
-    if (dtype == kBF16) hipLaunchKernelGGL((k_tree_draft<kBF16>), dim3((unsigned)(c.B * tc.N)), dim3(kWG), 0, s, c, tp, tc);
-    else hipLaunchKernelGGL((k_tree_draft<kF32>), dim3((unsigned)(c.B * tc.N)), dim3(kWG), 0, s, c, tp, tc);
+    if (dtype == kBF16) PSI_LAUNCH(s, (k_tree_draft<kBF16>), dim3((unsigned)(c.B * tc.N)), dim3(kWG), c, tp, tc);
+    else PSI_LAUNCH(s, (k_tree_draft<kF32>), dim3((unsigned)(c.B * tc.N)), dim3(kWG), c, tp, tc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -599,7 +599,7 @@ hipError_t launch_tree_sampled(const LinCfg& c, const TreeTopo& tp, const TreeCf
 hipError_t launch_tree_greedy(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int dtype, hipStream_t s) {
   hipError_t e = launch_argmax(c, c.B * (int64_t)(2 * (tc.N + 1)), dtype, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_tree_greedy, dim3((unsigned)c.B), dim3(kWG), 0, s, c, tp, tc);
+  PSI_LAUNCH(s, k_tree_greedy, dim3((unsigned)c.B), dim3(kWG), c, tp, tc);
   return hipGetLastError();
 }
 
@@ -607,7 +607,7 @@ hipError_t launch_tree_filtered(const LinCfg& c, const FiltCfg& f, const TreeTop
                                 hipStream_t s) {
   hipError_t e = launch_filter_rows(c, f, c.B * (int64_t)(2 * (tc.N + 1)), dtype, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_tree_filt, dim3((unsigned)c.B), dim3(kWG), 0, s, c, f, tp, tc);
+  PSI_LAUNCH(s, k_tree_filt, dim3((unsigned)c.B), dim3(kWG), c, f, tp, tc);
   return hipGetLastError();
 }
 
