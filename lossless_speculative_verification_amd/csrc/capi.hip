@@ -128,6 +128,8 @@ inline void fill_common(LinCfg& c, const void* p, const void* q, int dtype, int6
   c.invT = T > 0.0 ? 1.0 / T : 0.0;
   c.c32 = T > 0.0 ? (float)(1.4426950408889634074 / T) : 0.0f;
   c.c64 = T > 0.0 ? 1.4426950408889634074 / T : 0.0;
+  // the 2^(a c) table covers |a| < 64: keep every entry inside the fp64 range
+  c.tab = (dtype == PSISPEC_DTYPE_BF16 && c.c64 * kTabMaxAbs <= 1000.0) ? 1 : 0;
   c.rng.k0 = (uint32_t)(prm->seed & 0xffffffffu);
   c.rng.k1 = (uint32_t)(prm->seed >> 32);
   c.rng.step = prm->step;

@@ -115,8 +115,11 @@ __device__ __forceinline__ int wave_or(int v) {
   return v;
 }
 
-// Workgroup-wide reductions in a fixed order (deterministic); `sh` needs kWaves slots.
+// Workgroup-wide reductions over NT threads in a fixed order (deterministic);
+// `sh` needs NT / kWave slots.
+template <int NT = kWG>
 __device__ __forceinline__ float block_max(float v, float* sh) {
+  constexpr int NW = NT / kWave;
   v = wave_max(v);
   const int w = threadIdx.x / kWave;
   __syncthreads();
@@ -124,10 +127,12 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
   __syncthreads();
   float r = sh[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = fmaxnan(r, sh[i]);
+  for (int i = 1; i < NW; ++i) r = fmaxnan(r, sh[i]);
   return r;
 }
+template <int NT = kWG>
 __device__ __forceinline__ double block_sum(double v, double* sh) {
+  constexpr int NW = NT / kWave;
   v = wave_sum(v);
   const int w = threadIdx.x / kWave;
   __syncthreads();
@@ -135,28 +140,36 @@ __device__ __forceinline__ double block_sum(double v, double* sh) {
   __syncthreads();
   double r = sh[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) r += sh[i];
+  for (int i = 1; i < NW; ++i) r += sh[i];
   return r;
 }
 
-// Exclusive scan of one double per thread across the workgroup, in thread
-// order; returns the exclusive prefix and writes the total. `sh` needs kWG + kWaves slots.
+// Exclusive scan of one double per thread across NT threads, in thread order;
+// returns the exclusive prefix and writes the total. `sh` needs NT + NT / kWave
+// slots. Each wave scans in registers, then the wave totals are scanned.
+template <int NT = kWG>
 __device__ __forceinline__ double block_exclusive_scan(double v, double* sh, double* total) {
-  const int t = threadIdx.x;
-  __syncthreads();
-  sh[t] = v;
-  __syncthreads();
-  // Hillis-Steele inclusive scan in shared memory (fixed order, deterministic).
-  for (int o = 1; o < kWG; o <<= 1) {
-    double add = t >= o ? sh[t - o] : 0.0;
-    __syncthreads();
-    sh[t] += add;
-    __syncthreads();
+  constexpr int NW = NT / kWave;
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  double incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double up = __shfl_up(incl, o);
+    if (lane >= o) incl += up;
   }
-  const double excl = t ? sh[t - 1] : 0.0;
-  *total = sh[kWG - 1];
   __syncthreads();
-  return excl;
+  if (lane == kWave - 1) sh[w] = incl;
+  __syncthreads();
+  double before = 0.0, all = 0.0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const double x = sh[i];
+    if (i < w) before += x;
+    all += x;
+  }
+  *total = all;
+  __syncthreads();
+  return before + (incl - v);
 }
 
 // fp64-grade exponential (device math library, < 1 ulp).
@@ -186,6 +199,32 @@ __device__ __forceinline__ double exp2_poly(double y) {
 #pragma unroll
   for (int i = 11; i >= 0; --i) p = __builtin_fma(p, f, c[i]);
   return ::ldexp(p, (int)k);
+}
+
+// 2^y in fp64 for y <= 1023 (relative error < 5e-16; y below -1022, -inf
+// included, is taken as -1022, i.e. ~2^-1022). k = the integer nearest y is
+// read from the low word of y + 1.5 * 2^52, f = y - k lies in [-1/2, 1/2],
+// 2^f comes from a degree-10 near-minimax polynomial (Chebyshev interpolation
+// at 11 nodes, coefficients from exp2_coeffs.py), and 2^k is assembled in the
+// exponent field. Only full-rate fp64 and integer operations.
+__device__ __forceinline__ double exp2_fast(double y) {
+  y = fmax(y, -1022.0);
+  constexpr double kMagic = 6755399441055744.0;  // 1.5 * 2^52
+  const double t = y + kMagic;
+  const double f = y - (t - kMagic);
+  const int k = __double2loint(t);
+  double p = 7.072587226569927e-09;
+  p = __builtin_fma(p, f, 1.0208690586037056e-07);
+  p = __builtin_fma(p, f, 1.3215442576793237e-06);
+  p = __builtin_fma(p, f, 1.5252657258547322e-05);
+  p = __builtin_fma(p, f, 0.00015403530441763784);
+  p = __builtin_fma(p, f, 0.001333355823016814);
+  p = __builtin_fma(p, f, 0.00961812910760687);
+  p = __builtin_fma(p, f, 0.055504108664447695);
+  p = __builtin_fma(p, f, 0.24022650695910097);
+  p = __builtin_fma(p, f, 0.69314718055995);
+  p = __builtin_fma(p, f, 1.0);
+  return p * __hiloint2double((k + 1023) << 20, 0);
 }
 
 }  // namespace psi

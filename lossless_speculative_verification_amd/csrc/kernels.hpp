@@ -14,16 +14,23 @@ namespace psi {
 void timing_begin(hipStream_t s);
 void timing_mark(hipStream_t s);
 
-// Every kernel launch of the library goes through PSI_LAUNCH.
-#define PSI_LAUNCH(s, kernel, grid, block, ...)                  \
-  do {                                                            \
-    hipLaunchKernelGGL(kernel, grid, block, 0, s, __VA_ARGS__);   \
-    ::psi::timing_mark(s);                                        \
+// Every kernel launch of the library goes through PSI_LAUNCH (or
+// PSI_LAUNCH_LDS with dynamic LDS bytes).
+#define PSI_LAUNCH_LDS(s, kernel, grid, block, lds, ...)           \
+  do {                                                              \
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, __VA_ARGS__);   \
+    ::psi::timing_mark(s);                                          \
   } while (0)
+#define PSI_LAUNCH(s, kernel, grid, block, ...) PSI_LAUNCH_LDS(s, kernel, grid, block, 0, __VA_ARGS__)
 
 constexpr int kMaxK = 64;
 constexpr int kMaxTopK = 256;  // largest top_k of the filtered path
-constexpr int kStatNV = 8;  // 16-byte vectors per thread in the fp32-grade statistics pass
+constexpr int kStatNV = 8;
+// Window of the per-call 2^(a c) table for bfloat16 logits: magnitude codes
+// [kTabLo, kTabLo + kTabW) = |a| in [2^-26, 64), both signs (64 KB of fp64).
+constexpr uint32_t kTabLo = 101u << 7;
+constexpr int kTabW = 32 * 128;
+constexpr double kTabMaxAbs = 64.0;  // 16-byte vectors per thread in the fp32-grade statistics pass
 
 // Per (row, chunk) record of the fp32-grade statistics pass: chunk maximum of
 // the raw logits and sum of 2^((a - m) * c) with c = log2(e) / T (binary32),
@@ -166,6 +173,7 @@ struct LinCfg {
   float c32;    // log2(e) / T rounded to binary32
   double invT;  // 1 / T
   double c64;   // log2(e) / T in fp64
+  int tab;      // bf16 weights may use the 2^(a c) table (window below); 0 for small T
   Rng rng;
   int fused;
   int32_t* draft;

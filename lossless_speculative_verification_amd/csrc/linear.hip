@@ -11,21 +11,29 @@
 //               of 2^((a - m) * c) (binary32 exp2, fp64 accumulation) for every
 //               target and draft row -> log-normalisers good to ~1e-7, enough
 //               for the accept test.
-//   k_decide    one workgroup per request: row normalisers, p(x_i), q(x_i),
-//               Philox accept tests, wave ballot -> first rejection n.
-//   k_pass64    (sub-block, request): fp64 pass over the one row pair the
-//               final draw needs (p_n, q_n, or the bonus row p_K), per 1024-
-//               element sub-block sums.
-//   k_final     one workgroup per request: prefix over sub-block sums, fp64
-//               rescan of one sub-block, inverse-CDF pick, outputs.
+//   k_resolve   per request (16 waves): row normalisers, p(x_i), q(x_i),
+//               Philox accept tests and a wave ballot for the first rejection
+//               n; then fp64 sums per 1024-element sub-block over the one row
+//               pair the final draw needs (p_n and q_n, or the bonus row p_K);
+//               then, when one workgroup owns the request, the inverse-CDF
+//               pick from those sums and an fp64 rescan of one sub-block.
+//   k_final     the pick, when several workgroups shared a request's sums.
 // Draft sampling uses k_draftpass (fp64 sub-block sums of a draft row) and
 // k_draftfinal (pick). Greedy mode (temperature 0) uses k_argmax and
 // k_greedy_decide. The final draws are done in fp64 because an inverse-CDF
 // pick over 151936 tokens must agree with an fp64 reference to ~1e-12 of the
 // total mass to give the same token; the accept test only needs ~1e-7.
+#include <algorithm>
+
 #include "rowops.hpp"
 
 namespace psi {
+
+// Resolve launch shape: one workgroup per request from this many requests on
+// (256 CUs), else about this many workgroups in total.
+constexpr int64_t kResolveOneWgMinB = 192;
+constexpr int64_t kResolveTargetWgs = 256;
+constexpr size_t kResolveMaxLds = 64 * 1024;
 
 // ------------------------------------------------------ statistics pass --
 template <int DT, bool AL>
@@ -70,19 +78,127 @@ __global__ __launch_bounds__(kWG) void k_stats32(LinCfg c) {
   }
 }
 
-// ---------------------------------------------------------- decide step --
-template <int DT>
-__global__ __launch_bounds__(kWG) void k_decide(LinCfg c) {
+// ------------------------------------------------------------ resolve --
+// Threads of a resolve workgroup: 16 waves, so that one workgroup per request
+// keeps every SIMD of a CU busy through the fp64 final-row pass.
+constexpr int kRT = 1024;
+constexpr int kRWaves = kRT / kWave;
+
+// fp64 sums of this workgroup's sub-blocks [sb0, sb1) of the final row pair
+// (RESID) or the target row alone, one wave per sub-block (16 waves per CU
+// hide each other's load latency). TAB: the pair's weights come from the LDS
+// table.
+template <int DT, bool AL, bool TAB, bool RESID, bool PICK>
+__device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
+                                             int sb0, int sb1, const double* tab, const WRow& wp, const WRow& wq,
+                                             float dx, ResRec* s_rec) {
   using E = Elem<DT>;
-  const int64_t b = blockIdx.x;
+  constexpr int EPV = E::kPerVec;
+  constexpr int VPL = kSB / (kWave * EPV);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const double c64 = c.c64;
+  for (int sb = sb0 + wave; sb < sb1; sb += kRWaves) {
+    uint4 cp[VPL], cq[VPL];
+    load_raw<DT, AL, VPL, kWave>(prow, c.V, c.nvec, (int64_t)sb * (kSB / EPV) + lane, cp);
+    if constexpr (RESID) load_raw<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, (int64_t)sb * (kSB / EPV) + lane, cq);
+    double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      float xp[EPV], xq[EPV];
+      E::unpack(cp[v], xp);
+      if constexpr (RESID) E::unpack(cq[v], xq);
+      if constexpr (TAB) {
+        // table reads, accumulated at once; magnitudes below the window read
+        // the zero slot and get their exact weight in the rare branch below
+        bool tiny = false;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const uint32_t hp = __float_as_uint(xp[e]) >> 16, ip = (hp & 0x7fffu) - kTabLo;
+          const double ep = tab[ip < (uint32_t)kTabW ? (hp >> 15) * kTabW + ip : (uint32_t)kTabZero] * wp.scale;
+          tiny |= (hp & 0x7fffu) < kTabLo;
+          sp += ep;
+          if constexpr (RESID) {
+            const uint32_t hq = __float_as_uint(xq[e]) >> 16, iq = (hq & 0x7fffu) - kTabLo;
+            const double eq = tab[iq < (uint32_t)kTabW ? (hq >> 15) * kTabW + iq : (uint32_t)kTabZero] * wq.scale;
+            tiny |= (hq & 0x7fffu) < kTabLo;
+            sq += eq;
+            const double in = xp[e] - xq[e] > dx ? 1.0 : 0.0;  // target part above draft part
+            a = __builtin_fma(in, ep, a);
+            bq = __builtin_fma(in, eq, bq);
+          }
+        }
+        if (__ballot(tiny)) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const double in = RESID && xp[e] - xq[e] > dx ? 1.0 : 0.0;
+            if (((__float_as_uint(xp[e]) >> 16) & 0x7fffu) < kTabLo) {
+              const double ep = tiny_weight(xp[e], c64, wp.scale);
+              sp += ep;
+              a = __builtin_fma(in, ep, a);
+            }
+            if (RESID && ((__float_as_uint(xq[e]) >> 16) & 0x7fffu) < kTabLo) {
+              const double eq = tiny_weight(xq[e], c64, wq.scale);
+              sq += eq;
+              bq = __builtin_fma(in, eq, bq);
+            }
+          }
+        }
+      } else {
+#pragma unroll 2
+        for (int e = 0; e < EPV; ++e) {
+          const double ep = exp2_fast(__builtin_fma((double)xp[e], c64, -wp.mc));
+          sp += ep;
+          if constexpr (RESID) {
+            const double eq = exp2_fast(__builtin_fma((double)xq[e], c64, -wq.mc));
+            sq += eq;
+            const double in = xp[e] - xq[e] > dx ? 1.0 : 0.0;
+            a = __builtin_fma(in, ep, a);
+            bq = __builtin_fma(in, eq, bq);
+          }
+        }
+      }
+    }
+    ResRec out;
+    out.sp = wave_sum(sp);
+    out.sq = RESID ? wave_sum(sq) : 0.0;
+    out.a = RESID ? wave_sum(a) : 0.0;
+    out.bq = RESID ? wave_sum(bq) : 0.0;
+    if (lane == 0) {
+      if constexpr (PICK) s_rec[sb] = out;
+      else c.res[b * c.nsb + sb] = out;
+    }
+  }
+}
+
+// One resolve workgroup per (request, part): the decision of the request
+// (every part computes it; part 0 publishes it), then per-sub-block fp64 sums
+// over the one row pair the final draw needs (target row n and draft row n at
+// a rejection, the bonus row K otherwise) for this part's sub-blocks. With
+// PICK (one part per request) the workgroup also draws the final token from
+// its sub-block sums kept in LDS; otherwise k_final does.
+template <int DT, bool AL, bool PICK>
+__global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  constexpr int VPL = kSB / (kWave * EPV);
+  extern __shared__ ResRec s_rec[];  // PICK: one record per sub-block
+  const int64_t b = blockIdx.x / parts;
+  const int part = (int)(blockIdx.x - b * parts);
   const int K = c.K, R = 2 * K + 1, t = threadIdx.x;
+  const int wave = t / kWave, lane = t & (kWave - 1);
   __shared__ float s_m[2 * kMaxK + 1];
   __shared__ double s_S[2 * kMaxK + 1];
   __shared__ int s_bad, s_n;
+  __shared__ double sh[kRWaves];
+  __shared__ double s_tab[kTabSize];
+  const bool tab = DT == kBF16 && c.tab;
+  if (tab) fill_tab<kRT>(s_tab, c.c64);  // overlaps the decision's loads
+
+  // ---- decision: row normalisers, accept tests, first rejection
   if (t == 0) s_bad = 0;
   __syncthreads();
-  for (int i = t; i < R; i += kWG) {
-    const StatRec* rec = c.st + (b * R + i) * (int64_t)c.nch32;
+  if (t < R) {
+    const StatRec* rec = c.st + (b * R + t) * (int64_t)c.nch32;
     float m = -INFINITY;
     for (int ch = 0; ch < c.nch32; ++ch) m = fmaxnan(m, rec[ch].m);
     double S = 0.0;
@@ -94,8 +210,8 @@ __global__ __launch_bounds__(kWG) void k_decide(LinCfg c) {
         else if (!is_neg_inf(r.m)) S += r.s * ::exp2(((double)r.m - (double)m) * (double)c.c32);
       }
     if (!(S > 0.0)) bad = 1;
-    s_m[i] = m;
-    s_S[i] = S;
+    s_m[t] = m;
+    s_S[t] = S;
     if (bad) atomicOr(&s_bad, 1);
   }
   __syncthreads();
@@ -119,91 +235,115 @@ __global__ __launch_bounds__(kWG) void k_decide(LinCfg c) {
     if (t == 0) s_n = rej ? (__ffsll((long long)rej) - 1) : K;
   }
   __syncthreads();
-  const int n = s_n;
   if (s_bad) {
-    for (int i = t; i <= K; i += kWG) c.out_tokens[b * (K + 1) + i] = -1;
-    if (c.out_probs)
-      for (int i = t; i < 2 * K; i += kWG) c.out_probs[b * 2 * K + i] = 0.0f;
-    if (c.fused)
-      for (int i = t; i < K; i += kWG) c.draft[b * K + i] = -1;
-    if (t == 0) {
-      c.out_len[b] = -1;
-      if (c.out_resid) c.out_resid[b] = 0.0;
-      ReqState st = {};
-      st.err = 1;
-      c.rs[b] = st;
+    if (part == 0) {
+      for (int i = t; i <= K; i += kRT) c.out_tokens[b * (K + 1) + i] = -1;
+      if (c.out_probs)
+        for (int i = t; i < 2 * K; i += kRT) c.out_probs[b * 2 * K + i] = 0.0f;
+      if (c.fused)
+        for (int i = t; i < K; i += kRT) c.draft[b * K + i] = -1;
+      if (t == 0) {
+        c.out_len[b] = -1;
+        if (c.out_resid) c.out_resid[b] = 0.0;
+        if (!PICK) {
+          ReqState st = {};
+          st.err = 1;
+          c.rs[b] = st;
+        }
+      }
     }
     return;
   }
-  if (t < K && c.out_probs) {
+  const int n = s_n;
+  const bool resid = n < K;
+  if (part == 0 && t < K && c.out_probs) {
     c.out_probs[(b * K + t) * 2 + 0] = (float)P;
     c.out_probs[(b * K + t) * 2 + 1] = (float)Q;
   }
-  if (t == 0) {
+  const float mp = s_m[n], mq = resid ? s_m[K + 1 + n] : 0.0f;
+  const double sph = s_S[n], sqh = resid ? s_S[K + 1 + n] : 1.0;
+  const double c64 = c.c64;
+  WRow wp, wq;
+  wpair(tab, mp, mq, resid, c64, wp, wq);
+  // target part above draft part (ep / sph > eq / sqh) <=> a_p - a_q > dx
+  const float dx = (float)((::log2(sph) - ::log2(sqh) + wp.mc - wq.mc) / c64);
+  const double u_final = c.rng.u((uint32_t)b, (uint32_t)n, kDrawFinal);
+  if (!PICK && part == 0 && t == 0) {
     ReqState st = {};
     st.n = n;
     st.err = 0;
-    st.mp = s_m[n];
-    st.sp_hat = s_S[n];
-    st.mq = n < K ? s_m[K + 1 + n] : 0.0f;
-    st.sq_hat = n < K ? s_S[K + 1 + n] : 1.0;
-    st.u_final = c.rng.u((uint32_t)b, (uint32_t)n, kDrawFinal);
+    st.mp = mp;
+    st.mq = mq;
+    st.sp_hat = sph;
+    st.sq_hat = sqh;
+    st.u_final = u_final;
     c.rs[b] = st;
   }
-}
 
-// ------------------------------------------------- fp64 final-row pass --
-template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_pass64(LinCfg c) {
-  constexpr int EPV = Elem<DT>::kPerVec;
-  constexpr int VPL = kSB / (kWave * EPV);
-  const int64_t b = blockIdx.y;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int sb = blockIdx.x * kWaves + wave;
-  if (sb >= c.nsb) return;
-  const ReqState st = c.rs[b];
-  if (st.err) return;
-  const int K = c.K;
-  const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
-  ResRec out = {0.0, 0.0, 0.0, 0.0};
-  if (st.n == K) {
-    float x[VPL][EPV];
-    load_vecs<DT, AL, VPL, kWave>(prow_of(c, b, K), c.V, c.nvec, vfirst, x);
-    const double mp = st.mp;
-    double s = 0.0;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) s += exp2_poly(((double)x[v][e] - mp) * c.c64);
-    out.sp = wave_sum(s);
+  // ---- fp64 pass over this part's sub-blocks
+  const char* prow = prow_of(c, b, n);
+  const char* qrow = resid ? qrow_of(c, b, n) : prow;
+  const int nsb = c.nsb;
+  const int sb0 = (int)((int64_t)part * nsb / parts), sb1 = (int)((int64_t)(part + 1) * nsb / parts);
+  if (resid) {
+    if (DT == kBF16 && wp.tab) resolve_pass<DT, AL, DT == kBF16, true, PICK>(c, b, prow, qrow, sb0, sb1, s_tab, wp, wq, dx, s_rec);
+    else resolve_pass<DT, AL, false, true, PICK>(c, b, prow, qrow, sb0, sb1, s_tab, wp, wq, dx, s_rec);
   } else {
-    float xp[VPL][EPV], xq[VPL][EPV];
-    load_vecs<DT, AL, VPL, kWave>(prow_of(c, b, st.n), c.V, c.nvec, vfirst, xp);
-    load_vecs<DT, AL, VPL, kWave>(qrow_of(c, b, st.n), c.V, c.nvec, vfirst, xq);
-    const double mp = st.mp, mq = st.mq, sph = st.sp_hat, sqh = st.sq_hat;
-    double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const double ep = exp2_poly(((double)xp[v][e] - mp) * c.c64);
-        const double eq = exp2_poly(((double)xq[v][e] - mq) * c.c64);
-        sp += ep;
-        sq += eq;
-        if (ep * sqh > eq * sph) {
-          a += ep;
-          bq += eq;
-        }
-      }
-    out.sp = wave_sum(sp);
-    out.sq = wave_sum(sq);
-    out.a = wave_sum(a);
-    out.bq = wave_sum(bq);
+    if (DT == kBF16 && wp.tab) resolve_pass<DT, AL, DT == kBF16, false, PICK>(c, b, prow, qrow, sb0, sb1, s_tab, wp, wq, dx, s_rec);
+    else resolve_pass<DT, AL, false, false, PICK>(c, b, prow, qrow, sb0, sb1, s_tab, wp, wq, dx, s_rec);
   }
-  if (lane == 0) c.res[b * c.nsb + sb] = out;
+  if constexpr (PICK) {
+    __syncthreads();
+    // ---- final draw (inverse CDF, fp64) from the sub-block sums in LDS
+    double Sp = 1.0, Sq = 1.0, resid_mass = 0.0;
+    int mode = 0;  // 0: target weights of the final row; 1: residual; 2: residual vanished -> target
+    if (resid) {
+      double a = 0.0, q = 0.0;
+      for (int i = t; i < nsb; i += kRT) {
+        a += s_rec[i].sp;
+        q += s_rec[i].sq;
+      }
+      Sp = block_sum<kRT>(a, sh);
+      Sq = block_sum<kRT>(q, sh);
+      double mine = 0.0;
+      for (int i = t; i < nsb; i += kRT) mine += fmax(0.0, s_rec[i].a / Sp - s_rec[i].bq / Sq);
+      resid_mass = block_sum<kRT>(mine, sh);
+      mode = resid_mass > 0.0 ? 1 : 2;
+    }
+    int y;
+    if (mode == 1) {
+      y = pick_index<kRT>(
+          nsb, c.V, u_final * resid_mass,
+          [&](int i) { return fmax(0.0, s_rec[i].a / Sp - s_rec[i].bq / Sq); },
+          [&](int64_t j) {
+            const double ep = fweight<DT>(E::load1(prow, j), wp, c64, s_tab);
+            const double eq = fweight<DT>(E::load1(qrow, j), wq, c64, s_tab);
+            return fmax(0.0, ep / Sp - eq / Sq);
+          },
+          sh);
+    } else {
+      double mine = 0.0;
+      for (int i = t; i < nsb; i += kRT) mine += s_rec[i].sp;
+      const double W = block_sum<kRT>(mine, sh);
+      y = pick_index<kRT>(
+          nsb, c.V, u_final * W, [&](int i) { return s_rec[i].sp; },
+          [&](int64_t j) { return fweight<DT>(E::load1(prow, j), wp, c64, s_tab); }, sh);
+    }
+    for (int i = t; i <= K; i += kRT) {
+      int v = -1;
+      if (i < n) v = c.draft[b * K + i];
+      else if (i == n) v = y;
+      c.out_tokens[b * (K + 1) + i] = v;
+    }
+    if (t == 0) {
+      c.out_len[b] = n;
+      if (c.out_resid) c.out_resid[b] = resid_mass;
+    }
+  }
 }
 
 // ----------------------------------------------------------- final step --
+// Final draw when a request's sub-blocks were summed by several workgroups.
 template <int DT, bool AL>
 __global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
   using E = Elem<DT>;
@@ -215,48 +355,47 @@ __global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
   const bool bonus = n == K;
   const int nsb = c.nsb;
   const ResRec* rr = c.res + b * nsb;
-  __shared__ double sh[kWG + kWaves];
+  __shared__ double sh[kWaves];
   double Sp = 1.0, Sq = 1.0;
   if (!bonus) {
     double a = 0.0, q = 0.0;
-    for (int sb = t; sb < nsb; sb += kWG) {
-      a += rr[sb].sp;
-      q += rr[sb].sq;
+    for (int i = t; i < nsb; i += kWG) {
+      a += rr[i].sp;
+      q += rr[i].sq;
     }
     Sp = block_sum(a, sh);
     Sq = block_sum(q, sh);
   }
   const char* prow = prow_of(c, b, n);
   const char* qrow = bonus ? prow : qrow_of(c, b, n);
-  const double mp = st.mp, mq = st.mq, c64 = c.c64;
+  const double c64 = c.c64;
+  WRow wp, wq;
+  wpair(DT == kBF16 && c.tab, st.mp, st.mq, !bonus, c64, wp, wq);
   double resid = 0.0;
-  int mode = 0;  // 0: weights exp((a - mp)/T) of prow; 1: residual; 2: residual vanished -> P
+  int mode = 0;  // 0: target weights of the final row; 1: residual; 2: residual vanished -> target
   if (!bonus) {
     double mine = 0.0;
-    for (int sb = t; sb < nsb; sb += kWG) mine += fmax(0.0, rr[sb].a / Sp - rr[sb].bq / Sq);
+    for (int i = t; i < nsb; i += kWG) mine += fmax(0.0, rr[i].a / Sp - rr[i].bq / Sq);
     resid = block_sum(mine, sh);
     mode = resid > 0.0 ? 1 : 2;
   }
   int y;
   if (mode == 1) {
     y = pick_index(
-        nsb, c.V, st.u_final * resid, [&](int sb) { return fmax(0.0, rr[sb].a / Sp - rr[sb].bq / Sq); },
+        nsb, c.V, st.u_final * resid, [&](int i) { return fmax(0.0, rr[i].a / Sp - rr[i].bq / Sq); },
         [&](int64_t j) {
-          const double ep = exp2_poly(((double)E::load1(prow, j) - mp) * c64);
-          const double eq = exp2_poly(((double)E::load1(qrow, j) - mq) * c64);
+          const double ep = fweight<DT>(E::load1(prow, j), wp, c64, nullptr);
+          const double eq = fweight<DT>(E::load1(qrow, j), wq, c64, nullptr);
           return fmax(0.0, ep / Sp - eq / Sq);
         },
         sh);
   } else {
-    double W = 0.0;
-    {
-      double mine = 0.0;
-      for (int sb = t; sb < nsb; sb += kWG) mine += rr[sb].sp;
-      W = block_sum(mine, sh);
-    }
+    double mine = 0.0;
+    for (int i = t; i < nsb; i += kWG) mine += rr[i].sp;
+    const double W = block_sum(mine, sh);
     y = pick_index(
-        nsb, c.V, st.u_final * W, [&](int sb) { return rr[sb].sp; },
-        [&](int64_t j) { return exp2_poly(((double)E::load1(prow, j) - mp) * c64); }, sh);
+        nsb, c.V, st.u_final * W, [&](int i) { return rr[i].sp; },
+        [&](int64_t j) { return fweight<DT>(E::load1(prow, j), wp, c64, nullptr); }, sh);
   }
   for (int i = t; i <= K; i += kWG) {
     int v = -1;
@@ -479,9 +618,18 @@ template <int DT, bool AL>
 static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
   const int64_t rows = c.B * (2 * c.K + 1);
   PSI_LAUNCH(s, (k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
-  PSI_LAUNCH(s, (k_decide<DT>), dim3((unsigned)c.B), dim3(kWG), c);
-  PSI_LAUNCH(s, (k_pass64<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)c.B), dim3(kWG), c);
-  PSI_LAUNCH(s, (k_final<DT, AL>), dim3((unsigned)c.B), dim3(kWG), c);
+  // One resolve workgroup per request when there are enough requests to fill
+  // the chip (and its sub-block records fit in LDS); otherwise several per
+  // request and a separate final step.
+  const size_t lds = (size_t)c.nsb * sizeof(ResRec);
+  if (c.B >= kResolveOneWgMinB && lds <= kResolveMaxLds) {
+    PSI_LAUNCH_LDS(s, (k_resolve<DT, AL, true>), dim3((unsigned)c.B), dim3(kRT), lds, c, 1);
+  } else {
+    const int parts = (int)std::min<int64_t>(std::max<int64_t>(1, (kResolveTargetWgs + c.B - 1) / c.B),
+                                             std::max(1, c.nsb / kRWaves));
+    PSI_LAUNCH(s, (k_resolve<DT, AL, false>), dim3((unsigned)(c.B * parts)), dim3(kRT), c, parts);
+    PSI_LAUNCH(s, (k_final<DT, AL>), dim3((unsigned)c.B), dim3(kWG), c);
+  }
   return hipGetLastError();
 }
 

@@ -85,23 +85,128 @@ __device__ __forceinline__ const char* qrow_of(const LinCfg& c, int64_t b, int i
   return c.rows.q + ((b * c.K + i) * (int64_t)c.V) * c.rows.esz;
 }
 
+// ------------------------------------------------ final-row weights --
+// fp64 weight 2^((a - m) c) of one logit a of a row with maximum m (c =
+// log2(e) / T). For bfloat16 rows with |m| < 64 and (m + 64) c >= 100 (WRow.tab)
+// the weights come from a per-call table of 2^(a c) over the magnitude window
+// [2^-26, 64), times scale = 2^(-m c):
+//   |a| in the window  tab(a) * scale, tab(a) = exp2_fast(a * c);
+//   |a| below 2^-26    scale * (1 + t + t^2/2), t = a c ln 2 (exact to 1e-21);
+//   a <= -64 or -inf   0 (such a weight is below 2^-100 of the row maximum).
+// Every other row takes exp2_fast(a c - m c). The rule depends only on a and
+// the row, so sub-block sums and rescans of the same elements agree bit for
+// bit, whether the table entry is read from LDS or recomputed.
+constexpr int kTabZero = 2 * kTabW;  // table slot holding 0.0
+constexpr int kTabSize = 2 * kTabW + 1;
+
+struct WRow {
+  double mc, scale;
+  bool tab;
+};
+
+__device__ __forceinline__ WRow wrow(bool bf16_tab, float m, double c64) {
+  WRow w;
+  w.mc = (double)m * c64;
+  w.tab = bf16_tab && m < 64.0f && ((double)m + 64.0) * c64 >= 100.0;
+  w.scale = w.tab ? exp2_fast(-w.mc) : 0.0;
+  return w;
+}
+
+// Weights of the row pair a final draw reads: the target row alone (bonus),
+// or target and draft rows together, which use the table only if both rows
+// qualify, so that the pair is evaluated under one rule.
+__device__ __forceinline__ void wpair(bool bf16_tab, float mp, float mq, bool resid, double c64, WRow& wp,
+                                      WRow& wq) {
+  wp = wrow(bf16_tab, mp, c64);
+  wq = wrow(bf16_tab && resid, mq, c64);
+  if (resid && !(wp.tab && wq.tab)) {
+    wp = wrow(false, mp, c64);
+    wq = wrow(false, mq, c64);
+  }
+}
+
+__device__ __forceinline__ double tab_entry(uint32_t code, double c64) {
+  return exp2_fast((double)__uint_as_float(code << 16) * c64);
+}
+
+__device__ __forceinline__ double tiny_weight(float a, double c64, double scale) {
+  const double t = (double)a * (c64 * 0.69314718055994530942);
+  return scale * __builtin_fma(t, __builtin_fma(t, 0.5, 1.0), 1.0);
+}
+
+// Fills the kTabSize-entry table (positive codes, negative codes, zero slot)
+// with the workgroup's NT threads.
+template <int NT>
+__device__ __forceinline__ void fill_tab(double* tab, double c64) {
+  for (int i = threadIdx.x; i < kTabSize; i += NT) {
+    const uint32_t code = ((uint32_t)(i / kTabW) << 15) | (kTabLo + (uint32_t)(i % kTabW));
+    tab[i] = i < kTabZero ? tab_entry(code, c64) : 0.0;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ double fweight(float a, const WRow& w, double c64, const double* tab) {
+  if constexpr (DT == kBF16) {
+    if (w.tab) {
+      const uint32_t h = __float_as_uint(a) >> 16, mag = h & 0x7fffu;
+      if (mag < kTabLo) return tiny_weight(a, c64, w.scale);
+      const uint32_t idx = mag - kTabLo;
+      if (idx >= (uint32_t)kTabW) return 0.0;
+      return (tab ? tab[(h >> 15) * kTabW + idx] : tab_entry(h, c64)) * w.scale;
+    }
+  }
+  return exp2_fast(__builtin_fma((double)a, c64, -w.mc));
+}
+
+// fweight of one unpacked 16-byte vector of a table row, table in LDS: one
+// table read per logit, and the (rare) sub-2^-26 magnitudes redone in a branch
+// that only a wave holding one takes.
+template <int EPV>
+__device__ __forceinline__ void fweight_tab_vec(const float (&x)[EPV], const double* tab, double c64, double scale,
+                                                double (&w)[EPV]) {
+  bool tiny = false;
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) {
+    const uint32_t h = __float_as_uint(x[e]) >> 16, mag = h & 0x7fffu;
+    const uint32_t idx = mag - kTabLo;
+    w[e] = tab[idx < (uint32_t)kTabW ? (h >> 15) * kTabW + idx : (uint32_t)kTabZero] * scale;
+    tiny |= mag < kTabLo;
+  }
+  if (__ballot(tiny)) {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e)
+      if (((__float_as_uint(x[e]) >> 16) & 0x7fffu) < kTabLo) w[e] = tiny_weight(x[e], c64, scale);
+  }
+}
+
+// fweight of one unpacked vector of a row that does not use the table.
+// (Two exponentials in flight per lane: enough ILP with several waves per
+// SIMD, and a register footprint that leaves the table path unconstrained.)
+template <int EPV>
+__device__ __forceinline__ void fweight_direct_vec(const float (&x)[EPV], double c64, double mc, double (&w)[EPV]) {
+#pragma unroll 2
+  for (int e = 0; e < EPV; ++e) w[e] = exp2_fast(__builtin_fma((double)x[e], c64, -mc));
+}
+
 // --------------------------------------------- inverse-CDF pick helper --
 // Picks the smallest index j with (sum of weights up to and including j) >
 // target, given per-sub-block weights wsb(sb) and per-element weights w(j)
-// (fp64, index order). Sub-blocks are 1024 elements. Rounding differences
-// between the sub-block sums and the rescan are handled by falling back to
-// the last positive weight. Returns -1 only if every weight is zero.
-template <class WSB, class WEL>
+// (fp64, index order), with a workgroup of NT threads. Sub-blocks are 1024
+// elements. Rounding differences between the sub-block sums and the rescan are
+// handled by falling back to the last positive weight. Returns -1 only if
+// every weight is zero. `sh` needs NT / kWave doubles.
+template <int NT = kWG, class WSB, class WEL>
 __device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, double* sh) {
+  static_assert(kSB % NT == 0, "a sub-block must split evenly over the workgroup");
   __shared__ int s_sel;
   __shared__ double s_pref;
   const int t = threadIdx.x;
-  const int per = (nsb + kWG - 1) / kWG;
+  const int per = (nsb + NT - 1) / NT;
   const int s0 = min(nsb, t * per), s1 = min(nsb, s0 + per);
   double mine = 0.0;
   for (int sb = s0; sb < s1; ++sb) mine += wsb(sb);
   double total;
-  const double excl = block_exclusive_scan(mine, sh, &total);
+  const double excl = block_exclusive_scan<NT>(mine, sh, &total);
   if (t == 0) s_sel = 0x7fffffff;
   __syncthreads();
   {
@@ -135,8 +240,8 @@ __device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, doubl
   }
   __syncthreads();
   const double tin = target - s_pref;
-  // rescan: thread t owns elements [sel*1024 + 4t, +4)
-  constexpr int EPT = kSB / kWG;
+  // rescan: thread t owns elements [sel*1024 + EPT*t, +EPT)
+  constexpr int EPT = kSB / NT;
   const int64_t j0 = (int64_t)sel * kSB + (int64_t)t * EPT;
   double w[EPT];
   double mine2 = 0.0;
@@ -146,7 +251,7 @@ __device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, doubl
     mine2 += w[k];
   }
   double tot2;
-  const double excl2 = block_exclusive_scan(mine2, sh, &tot2);
+  const double excl2 = block_exclusive_scan<NT>(mine2, sh, &tot2);
   if (t == 0) s_sel = 0x7fffffff;
   __syncthreads();
   {

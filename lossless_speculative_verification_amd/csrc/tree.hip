@@ -197,8 +197,10 @@ __global__ __launch_bounds__(kWG) void k_tree_walk(LinCfg c, TreeTopo tp, TreeCf
     const float aq = E::load1(tree_qrow(c, b, row), tok);
     double P, Q;
     if (s.has_exact) {
-      P = exp2_poly(((double)ap - (double)s.mp) * c.c64) / s.Sp;
-      Q = exp2_poly(((double)aq - (double)s.mq) * c.c64) / s.Sq;
+      WRow wp, wq;  // exact sums come from a residual-type pass over this row pair
+      wpair(DT == kBF16 && c.tab, s.mp, s.mq, true, c.c64, wp, wq);
+      P = fweight<DT>(ap, wp, c.c64, nullptr) / s.Sp;
+      Q = fweight<DT>(aq, wq, c.c64, nullptr) / s.Sq;
     } else {
       P = ::exp(((double)ap - (double)s.mp) * c.invT - ::log(s.sp_hat));
       Q = ::exp(((double)aq - (double)s.mq) * c.invT - ::log(s.sq_hat));
@@ -235,15 +237,18 @@ __global__ __launch_bounds__(kWG) void k_tree_pass(LinCfg c, TreeCfg tc, int fin
   if (s.phase != (final_pass ? kTreeFinal : kTreeWaitG)) return;
   const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
   TreeRes out = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-  const double mp = s.mp, mq = s.mq;
-  if (s.c_new == 0.0 && s.c_old == 0.0) {  // draw from P: target row only
+  const double c64 = c.c64;
+  const bool leaf = s.c_new == 0.0 && s.c_old == 0.0;
+  WRow wp, wq;
+  wpair(DT == kBF16 && c.tab, s.mp, s.mq, !leaf, c64, wp, wq);
+  if (leaf) {  // draw from P: target row only
     float x[VPL][EPV];
     load_vecs<DT, AL, VPL, kWave>(tree_prow(c, b, s.row), c.V, c.nvec, vfirst, x);
     double sp = 0.0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) sp += exp2_poly(((double)x[v][e] - mp) * c.c64);
+      for (int e = 0; e < EPV; ++e) sp += fweight<DT>(x[v][e], wp, c64, nullptr);
     out.sp = wave_sum(sp);
     out.a = out.sp;
     out.a0 = out.sp;
@@ -251,27 +256,27 @@ __global__ __launch_bounds__(kWG) void k_tree_pass(LinCfg c, TreeCfg tc, int fin
     float xp[VPL][EPV], xq[VPL][EPV];
     load_vecs<DT, AL, VPL, kWave>(tree_prow(c, b, s.row), c.V, c.nvec, vfirst, xp);
     load_vecs<DT, AL, VPL, kWave>(tree_qrow(c, b, s.row), c.V, c.nvec, vfirst, xq);
-    // membership of P > c Q is decided with the best normalisers at hand;
-    // entries near the boundary carry almost no weight either way
+    // P > c Q <=> ep / sph > c eq / sqh <=> a_p - a_q > dx(c), with the best
+    // normalisers at hand; entries near the boundary carry almost no weight
     const double sph = s.has_exact ? s.Sp : s.sp_hat, sqh = s.has_exact ? s.Sq : s.sq_hat;
     const double c1 = s.c_new, c0 = s.c_old;
+    const float dx1 = (float)((::log2(sph) - ::log2(sqh) + ::log2(c1) + wp.mc - wq.mc) / c64);
+    const float dx0 = (float)((::log2(sph) - ::log2(sqh) + ::log2(c0) + wp.mc - wq.mc) / c64);
     double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0, a0 = 0.0, bq0 = 0.0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
-        const double ep = exp2_poly(((double)xp[v][e] - mp) * c.c64);
-        const double eq = exp2_poly(((double)xq[v][e] - mq) * c.c64);
+        const double ep = fweight<DT>(xp[v][e], wp, c64, nullptr);
+        const double eq = fweight<DT>(xq[v][e], wq, c64, nullptr);
         sp += ep;
         sq += eq;
-        if (ep * sqh > c1 * (eq * sph)) {
-          a += ep;
-          bq += eq;
-        }
-        if (ep * sqh > c0 * (eq * sph)) {
-          a0 += ep;
-          bq0 += eq;
-        }
+        const double in1 = xp[v][e] - xq[v][e] > dx1 ? 1.0 : 0.0;
+        a = __builtin_fma(in1, ep, a);
+        bq = __builtin_fma(in1, eq, bq);
+        const double in0 = xp[v][e] - xq[v][e] > dx0 ? 1.0 : 0.0;
+        a0 = __builtin_fma(in0, ep, a0);
+        bq0 = __builtin_fma(in0, eq, bq0);
       }
     out.sp = wave_sum(sp);
     out.sq = wave_sum(sq);
@@ -296,7 +301,11 @@ __global__ __launch_bounds__(kWG) void k_tree_pick(LinCfg c, TreeCfg tc) {
   __shared__ double sh[kWG + kWaves];
   const char* prow = tree_prow(c, b, s.row);
   const char* qrow = tree_qrow(c, b, s.row);
-  const double mp = s.mp, mq = s.mq, c64 = c.c64;
+  const double c64 = c.c64;
+  WRow rwp, rwq;
+  wpair(DT == kBF16 && c.tab, s.mp, s.mq, s.c_new != 0.0, c64, rwp, rwq);
+  auto wp = [&](int64_t j) { return fweight<DT>(E::load1(prow, j), rwp, c64, nullptr); };
+  auto wq = [&](int64_t j) { return fweight<DT>(E::load1(qrow, j), rwq, c64, nullptr); };
   const double u = c.rng.u((uint32_t)b, (uint32_t)s.row, kDrawFinal);
   int y;
   if (s.c_new == 0.0) {
@@ -306,7 +315,7 @@ __global__ __launch_bounds__(kWG) void k_tree_pick(LinCfg c, TreeCfg tc) {
     const double W = block_sum(mine, sh);
     y = pick_index(
         nsb, c.V, u * W, [&](int sb) { return rr[sb].sp; },
-        [&](int64_t j) { return exp2_poly(((double)E::load1(prow, j) - mp) * c64); }, sh);
+        wp, sh);
   } else {
     double a = 0.0, q = 0.0;
     for (int sb = t; sb < nsb; sb += kWG) {
@@ -323,8 +332,7 @@ __global__ __launch_bounds__(kWG) void k_tree_pick(LinCfg c, TreeCfg tc) {
       y = pick_index(
           nsb, c.V, u * G1, [&](int sb) { return fmax(0.0, rr[sb].a / Sp - c1 * rr[sb].bq / Sq); },
           [&](int64_t j) {
-            const double ep = exp2_poly(((double)E::load1(prow, j) - mp) * c64);
-            const double eq = exp2_poly(((double)E::load1(qrow, j) - mq) * c64);
+            const double ep = wp(j), eq = wq(j);
             return fmax(0.0, ep / Sp - c1 * eq / Sq);
           },
           sh);
@@ -337,8 +345,7 @@ __global__ __launch_bounds__(kWG) void k_tree_pick(LinCfg c, TreeCfg tc) {
       y = pick_index(
           nsb, c.V, u * G0, [&](int sb) { return fmax(0.0, rr[sb].a0 / Sp - c0 * rr[sb].bq0 / Sq); },
           [&](int64_t j) {
-            const double ep = exp2_poly(((double)E::load1(prow, j) - mp) * c64);
-            const double eq = exp2_poly(((double)E::load1(qrow, j) - mq) * c64);
+            const double ep = wp(j), eq = wq(j);
             return fmax(0.0, ep / Sp - c0 * eq / Sq);
           },
           sh);
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(kWG) void k_tree_pick(LinCfg c, TreeCfg tc) {
       const double W = block_sum(m0, sh);
       y = pick_index(
           nsb, c.V, u * W, [&](int sb) { return rr[sb].sp; },
-          [&](int64_t j) { return exp2_poly(((double)E::load1(prow, j) - mp) * c64); }, sh);
+          wp, sh);
     }
   }
   if (t == 0) {
