@@ -109,6 +109,24 @@ __device__ __forceinline__ double wave_sum(double v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
+// Sums of four values over the wave with one butterfly: after exchanging
+// halves at lane distance 32 and 16, each 16-lane group holds partial sums of
+// one value and finishes it alone. Lanes 0-15 end with sum(v0), 16-31 with
+// sum(v1), 32-47 with sum(v2), 48-63 with sum(v3). 14 lane permutes instead
+// of 48 for four separate reductions.
+__device__ __forceinline__ double wave_sum4(double v0, double v1, double v2, double v3) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool hi32 = lane & 32, hi16 = lane & 16;
+  const double r0 = __shfl_xor(hi32 ? v0 : v2, 32), r1 = __shfl_xor(hi32 ? v1 : v3, 32);
+  const double k0 = (hi32 ? v2 : v0) + r0, k1 = (hi32 ? v3 : v1) + r1;
+  double k = (hi16 ? k1 : k0) + __shfl_xor(hi16 ? k0 : k1, 16);
+  k += __shfl_xor(k, 8);
+  k += __shfl_xor(k, 4);
+  k += __shfl_xor(k, 2);
+  k += __shfl_xor(k, 1);
+  return k;
+}
+
 __device__ __forceinline__ int wave_or(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);

@@ -25,7 +25,7 @@ void timing_mark(hipStream_t s);
 
 constexpr int kMaxK = 64;
 constexpr int kMaxTopK = 256;  // largest top_k of the filtered path
-constexpr int kStatNV = 8;
+constexpr int kStatNV = 16;
 // Window of the per-call 2^(a c) table for bfloat16 logits: magnitude codes
 // [kTabLo, kTabLo + kTabW) = |a| in [2^-26, 64), both signs (64 KB of fp64).
 constexpr uint32_t kTabLo = 101u << 7;

@@ -84,66 +84,108 @@ __global__ __launch_bounds__(kWG) void k_stats32(LinCfg c) {
 constexpr int kRT = 1024;
 constexpr int kRWaves = kRT / kWave;
 
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Weights of the logits of one 16-byte bfloat16 vector pair whose magnitude is
+// below the table window (they read a zero slot in the pass): returns their
+// sums in the layout of ResRec (sp, sq, and the parts where the target part
+// exceeds the draft part).
+__device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool resid, double c64, double scp,
+                                                       double scq, float dx) {
+  float xp[8], xq[8];
+  Elem<kBF16>::unpack(rp, xp);
+  Elem<kBF16>::unpack(rq, xq);
+  ResRec f = {0.0, 0.0, 0.0, 0.0};
+  for (int e = 0; e < 8; ++e) {
+    const double in = resid && xp[e] - xq[e] > dx ? 1.0 : 0.0;
+    if (tab_tiny(__float_as_uint(xp[e]) >> 16)) {
+      const double ep = tiny_weight(xp[e], c64, scp);
+      f.sp += ep;
+      f.a = __builtin_fma(in, ep, f.a);
+    }
+    if (resid && tab_tiny(__float_as_uint(xq[e]) >> 16)) {
+      const double eq = tiny_weight(xq[e], c64, scq);
+      f.sq += eq;
+      f.bq = __builtin_fma(in, eq, f.bq);
+    }
+  }
+  return f;
+}
+
 // fp64 sums of this workgroup's sub-blocks [sb0, sb1) of the final row pair
-// (RESID) or the target row alone, one wave per sub-block (16 waves per CU
-// hide each other's load latency). TAB: the pair's weights come from the LDS
-// table.
+// (RESID) or the target row alone, one wave per sub-block, with the following
+// sub-blocks' logits in flight while the current one is reduced. TAB: weights
+// are read from the pre-scaled LDS tables tp / tq (bfloat16 only).
 template <int DT, bool AL, bool TAB, bool RESID, bool PICK>
 __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
-                                             int sb0, int sb1, const double* tab, const WRow& wp, const WRow& wq,
-                                             float dx, ResRec* s_rec) {
+                                             int sb0, int sb1, const double* tp, const double* tq, const WRow& wp,
+                                             const WRow& wq, float dx, ResRec* s_rec) {
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec;
   constexpr int VPL = kSB / (kWave * EPV);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const double c64 = c.c64;
-  for (int sb = sb0 + wave; sb < sb1; sb += kRWaves) {
-    uint4 cp[VPL], cq[VPL];
-    load_raw<DT, AL, VPL, kWave>(prow, c.V, c.nvec, (int64_t)sb * (kSB / EPV) + lane, cp);
-    if constexpr (RESID) load_raw<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, (int64_t)sb * (kSB / EPV) + lane, cq);
+  // sub-blocks in flight per wave beyond the current one: two for bfloat16
+  // (16 VGPRs each), one for fp32 (32 each)
+  constexpr int AHEAD = DT == kBF16 ? 2 : 1;
+  auto load_sb = [&](int s, uint4(&xp)[VPL], uint4(&xq)[VPL]) {
+    if (s < sb1) {
+      load_raw<DT, AL, VPL, kWave>(prow, c.V, c.nvec, (int64_t)s * (kSB / EPV) + lane, xp);
+      if constexpr (RESID) load_raw<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, (int64_t)s * (kSB / EPV) + lane, xq);
+    }
+  };
+  uint4 cp[VPL], cq[VPL], np_[VPL], nq_[VPL];
+  int sb = sb0 + wave;
+  load_sb(sb, cp, cq);
+  if constexpr (AHEAD == 2) load_sb(sb + kRWaves, np_, nq_);
+  for (; sb < sb1; sb += kRWaves) {
+    uint4 fp_[VPL], fq_[VPL];
+    if constexpr (AHEAD == 2) load_sb(sb + 2 * kRWaves, fp_, fq_);
+    else load_sb(sb + kRWaves, np_, nq_);
     double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      float xp[EPV], xq[EPV];
-      E::unpack(cp[v], xp);
-      if constexpr (RESID) E::unpack(cq[v], xq);
       if constexpr (TAB) {
-        // table reads, accumulated at once; magnitudes below the window read
-        // the zero slot and get their exact weight in the rare branch below
+        // two bfloat16 codes per word; logits below the window read a zero
+        // slot and get their exact weight in the rare call below
         bool tiny = false;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const uint32_t hp = __float_as_uint(xp[e]) >> 16, ip = (hp & 0x7fffu) - kTabLo;
-          const double ep = tab[ip < (uint32_t)kTabW ? (hp >> 15) * kTabW + ip : (uint32_t)kTabZero] * wp.scale;
-          tiny |= (hp & 0x7fffu) < kTabLo;
-          sp += ep;
-          if constexpr (RESID) {
-            const uint32_t hq = __float_as_uint(xq[e]) >> 16, iq = (hq & 0x7fffu) - kTabLo;
-            const double eq = tab[iq < (uint32_t)kTabW ? (hq >> 15) * kTabW + iq : (uint32_t)kTabZero] * wq.scale;
-            tiny |= (hq & 0x7fffu) < kTabLo;
-            sq += eq;
-            const double in = xp[e] - xq[e] > dx ? 1.0 : 0.0;  // target part above draft part
-            a = __builtin_fma(in, ep, a);
-            bq = __builtin_fma(in, eq, bq);
-          }
-        }
-        if (__ballot(tiny)) {
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t wpw = word_of(cp[v], i), wqw = RESID ? word_of(cq[v], i) : 0u;
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) {
-            const double in = RESID && xp[e] - xq[e] > dx ? 1.0 : 0.0;
-            if (((__float_as_uint(xp[e]) >> 16) & 0x7fffu) < kTabLo) {
-              const double ep = tiny_weight(xp[e], c64, wp.scale);
-              sp += ep;
-              a = __builtin_fma(in, ep, a);
-            }
-            if (RESID && ((__float_as_uint(xq[e]) >> 16) & 0x7fffu) < kTabLo) {
-              const double eq = tiny_weight(xq[e], c64, wq.scale);
+          for (int hf = 0; hf < 2; ++hf) {
+            const uint32_t hp = hf ? wpw >> 16 : wpw & 0xffffu;
+            const double ep = tp[tab_slot(hp)];
+            tiny |= tab_tiny(hp);
+            sp += ep;
+            if constexpr (RESID) {
+              const uint32_t hq = hf ? wqw >> 16 : wqw & 0xffffu;
+              const double eq = tq[tab_slot(hq)];
+              tiny |= tab_tiny(hq);
               sq += eq;
+              const float xp = __uint_as_float(hf ? wpw & 0xffff0000u : wpw << 16);
+              const float xq = __uint_as_float(hf ? wqw & 0xffff0000u : wqw << 16);
+              const double in = xp - xq > dx ? 1.0 : 0.0;  // target part above draft part
+              a = __builtin_fma(in, ep, a);
               bq = __builtin_fma(in, eq, bq);
             }
           }
         }
+        if (__ballot(tiny)) {
+          // a call, so that this rare work stays out of the common path
+          const ResRec f = tiny_fixup(cp[v], RESID ? cq[v] : make_uint4(0, 0, 0, 0), RESID, c64, wp.scale,
+                                      wq.scale, dx);
+          sp += f.sp;
+          sq += f.sq;
+          a += f.a;
+          bq += f.bq;
+        }
       } else {
+        float xp[EPV], xq[EPV];
+        E::unpack(cp[v], xp);
+        if constexpr (RESID) E::unpack(cq[v], xq);
 #pragma unroll 2
         for (int e = 0; e < EPV; ++e) {
           const double ep = exp2_fast(__builtin_fma((double)xp[e], c64, -wp.mc));
@@ -158,15 +200,46 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
         }
       }
     }
-    ResRec out;
-    out.sp = wave_sum(sp);
-    out.sq = RESID ? wave_sum(sq) : 0.0;
-    out.a = RESID ? wave_sum(a) : 0.0;
-    out.bq = RESID ? wave_sum(bq) : 0.0;
-    if (lane == 0) {
-      if constexpr (PICK) s_rec[sb] = out;
-      else c.res[b * c.nsb + sb] = out;
+    ResRec* const rec = PICK ? s_rec + sb : c.res + b * c.nsb + sb;
+    if constexpr (RESID) {
+      // lanes 0, 16, 32, 48 hold the sums of sp, sq, a, bq
+      const double tot = wave_sum4(sp, sq, a, bq);
+      if ((lane & 15) == 0) reinterpret_cast<double*>(rec)[lane >> 4] = tot;  // ResRec is four doubles
+    } else {
+      const double tot = wave_sum(sp);
+      if (lane == 0) *rec = ResRec{tot, 0.0, 0.0, 0.0};
     }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      cp[v] = np_[v];
+      if constexpr (RESID) cq[v] = nq_[v];
+      if constexpr (AHEAD == 2) {
+        np_[v] = fp_[v];
+        if constexpr (RESID) nq_[v] = fq_[v];
+      }
+    }
+  }
+}
+
+// Weights of the 16 consecutive logits j0 .. j0+15 of one row (0 past V), for
+// the rescan of the final pick: one or two 16-byte loads when aligned.
+template <int DT, bool AL>
+__device__ __forceinline__ void row16(const LinCfg& c, const char* row, int64_t j0, const WRow& w,
+                                      const double* tab_scaled, double (&out)[16]) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  if (AL && j0 + 16 <= c.V) {
+    const uint4* rp = (const uint4*)row + j0 / EPV;
+#pragma unroll
+    for (int v = 0; v < 16 / EPV; ++v) {
+      float x[EPV];
+      E::unpack(rp[v], x);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) out[v * EPV + e] = fweight<DT>(x[e], w, c.c64, tab_scaled);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) out[k] = j0 + k < c.V ? fweight<DT>(E::load1(row, j0 + k), w, c.c64, tab_scaled) : 0.0;
   }
 }
 
@@ -179,8 +252,6 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
 template <int DT, bool AL, bool PICK>
 __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   using E = Elem<DT>;
-  constexpr int EPV = E::kPerVec;
-  constexpr int VPL = kSB / (kWave * EPV);
   extern __shared__ ResRec s_rec[];  // PICK: one record per sub-block
   const int64_t b = blockIdx.x / parts;
   const int part = (int)(blockIdx.x - b * parts);
@@ -189,46 +260,54 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   __shared__ float s_m[2 * kMaxK + 1];
   __shared__ double s_S[2 * kMaxK + 1];
   __shared__ int s_bad, s_n;
-  __shared__ double sh[kRWaves];
-  __shared__ double s_tab[kTabSize];
+  // the 2^(a c) table, then the same multiplied by 2^(-m_p c) (first half)
+  // and by 2^(-m_q c) (second half) once the final rows are known
+  __shared__ double s_tab[2 * kTabSize];
   const bool tab = DT == kBF16 && c.tab;
-  if (tab) fill_tab<kRT>(s_tab, c.c64);  // overlaps the decision's loads
 
-  // ---- decision: row normalisers, accept tests, first rejection
+  // ---- decision: row normalisers, accept tests, first rejection. Wave 0
+  // gathers the drafted tokens' logits while waves 2.. reduce the statistics
+  // records of the 2K+1 rows; the table fill overlaps both.
   if (t == 0) s_bad = 0;
   __syncthreads();
-  if (t < R) {
-    const StatRec* rec = c.st + (b * R + t) * (int64_t)c.nch32;
+  int x = -1;
+  float ap = 0.0f, aq = 0.0f;
+  if (t < K) {
+    x = c.draft[b * K + t];
+    if (x < 0 || x >= c.V) {
+      atomicOr(&s_bad, 1);
+    } else {
+      ap = E::load1(prow_of(c, b, t), x);
+      aq = E::load1(qrow_of(c, b, t), x);
+    }
+  }
+  const int r = t - 2 * kWave;
+  if (r >= 0 && r < R) {
+    const StatRec* rec = c.st + (b * R + r) * (int64_t)c.nch32;
     float m = -INFINITY;
     for (int ch = 0; ch < c.nch32; ++ch) m = fmaxnan(m, rec[ch].m);
     double S = 0.0;
     int bad = isnan(m) || isinf(m);  // NaN, +inf, or an all -inf row
     if (!bad)
       for (int ch = 0; ch < c.nch32; ++ch) {
-        const StatRec r = rec[ch];
-        if (isnan(r.s)) bad = 1;
-        else if (!is_neg_inf(r.m)) S += r.s * ::exp2(((double)r.m - (double)m) * (double)c.c32);
+        const StatRec rc = rec[ch];
+        if (isnan(rc.s)) bad = 1;
+        else if (!is_neg_inf(rc.m)) S += rc.s * ::exp2(((double)rc.m - (double)m) * (double)c.c32);
       }
     if (!(S > 0.0)) bad = 1;
-    s_m[t] = m;
-    s_S[t] = S;
+    s_m[r] = m;
+    s_S[r] = S;
     if (bad) atomicOr(&s_bad, 1);
   }
+  if (tab) fill_tab<kRT>(s_tab, c.c64);
   __syncthreads();
   int acc = 1;
   double P = 0.0, Q = 0.0;
-  if (t < K) {
-    const int x = c.draft[b * K + t];
-    if (x < 0 || x >= c.V) {
-      atomicOr(&s_bad, 1);
-    } else {
-      const float ap = E::load1(prow_of(c, b, t), x);
-      const float aq = E::load1(qrow_of(c, b, t), x);
-      P = ::exp(((double)ap - (double)s_m[t]) * c.invT - ::log(s_S[t]));
-      Q = ::exp(((double)aq - (double)s_m[K + 1 + t]) * c.invT - ::log(s_S[K + 1 + t]));
-      const double u = c.rng.u((uint32_t)b, (uint32_t)t, kDrawAccept);
-      acc = u * Q < P;
-    }
+  if (t < K && x >= 0 && x < c.V) {
+    P = ::exp(((double)ap - (double)s_m[t]) * c.invT - ::log(s_S[t]));
+    Q = ::exp(((double)aq - (double)s_m[K + 1 + t]) * c.invT - ::log(s_S[K + 1 + t]));
+    const double u = c.rng.u((uint32_t)b, (uint32_t)t, kDrawAccept);
+    acc = u * Q < P;
   }
   if (t < kWave) {
     const unsigned long long rej = __ballot(t < K && !acc);
@@ -279,6 +358,16 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
     st.u_final = u_final;
     c.rs[b] = st;
   }
+  double* const tabp = s_tab;
+  double* const tabq = s_tab + kTabSize;
+  if (DT == kBF16 && wp.tab) {
+    for (int i = t; i < kTabSize; i += kRT) {
+      const double e = s_tab[i];
+      if (resid) tabq[i] = e * wq.scale;
+      tabp[i] = e * wp.scale;
+    }
+    __syncthreads();
+  }
 
   // ---- fp64 pass over this part's sub-blocks
   const char* prow = prow_of(c, b, n);
@@ -286,56 +375,59 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   const int nsb = c.nsb;
   const int sb0 = (int)((int64_t)part * nsb / parts), sb1 = (int)((int64_t)(part + 1) * nsb / parts);
   if (resid) {
-    if (DT == kBF16 && wp.tab) resolve_pass<DT, AL, DT == kBF16, true, PICK>(c, b, prow, qrow, sb0, sb1, s_tab, wp, wq, dx, s_rec);
-    else resolve_pass<DT, AL, false, true, PICK>(c, b, prow, qrow, sb0, sb1, s_tab, wp, wq, dx, s_rec);
+    if (DT == kBF16 && wp.tab)
+      resolve_pass<DT, AL, DT == kBF16, true, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec);
+    else resolve_pass<DT, AL, false, true, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec);
   } else {
-    if (DT == kBF16 && wp.tab) resolve_pass<DT, AL, DT == kBF16, false, PICK>(c, b, prow, qrow, sb0, sb1, s_tab, wp, wq, dx, s_rec);
-    else resolve_pass<DT, AL, false, false, PICK>(c, b, prow, qrow, sb0, sb1, s_tab, wp, wq, dx, s_rec);
+    if (DT == kBF16 && wp.tab)
+      resolve_pass<DT, AL, DT == kBF16, false, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec);
+    else resolve_pass<DT, AL, false, false, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec);
   }
   if constexpr (PICK) {
     __syncthreads();
-    // ---- final draw (inverse CDF, fp64) from the sub-block sums in LDS
-    double Sp = 1.0, Sq = 1.0, resid_mass = 0.0;
-    int mode = 0;  // 0: target weights of the final row; 1: residual; 2: residual vanished -> target
-    if (resid) {
-      double a = 0.0, q = 0.0;
-      for (int i = t; i < nsb; i += kRT) {
-        a += s_rec[i].sp;
-        q += s_rec[i].sq;
-      }
-      Sp = block_sum<kRT>(a, sh);
-      Sq = block_sum<kRT>(q, sh);
-      double mine = 0.0;
-      for (int i = t; i < nsb; i += kRT) mine += fmax(0.0, s_rec[i].a / Sp - s_rec[i].bq / Sq);
-      resid_mass = block_sum<kRT>(mine, sh);
-      mode = resid_mass > 0.0 ? 1 : 2;
-    }
+    // ---- final draw (inverse CDF, fp64) from the sub-block sums in LDS, by wave 0
+    if (wave != 0) return;
+    const double* const tps = wp.tab ? tabp : nullptr;
+    const double* const tqs = wq.tab ? tabq : nullptr;
+    double resid_mass = 0.0;
     int y;
-    if (mode == 1) {
-      y = pick_index<kRT>(
-          nsb, c.V, u_final * resid_mass,
-          [&](int i) { return fmax(0.0, s_rec[i].a / Sp - s_rec[i].bq / Sq); },
-          [&](int64_t j) {
-            const double ep = fweight<DT>(E::load1(prow, j), wp, c64, s_tab);
-            const double eq = fweight<DT>(E::load1(qrow, j), wq, c64, s_tab);
-            return fmax(0.0, ep / Sp - eq / Sq);
-          },
-          sh);
-    } else {
+    if (resid) {
+      double sa = 0.0, sb_ = 0.0;
+      for (int i = lane; i < nsb; i += kWave) {
+        sa += s_rec[i].sp;
+        sb_ += s_rec[i].sq;
+      }
+      const double iSp = 1.0 / wave_sum(sa), iSq = 1.0 / wave_sum(sb_);
       double mine = 0.0;
-      for (int i = t; i < nsb; i += kRT) mine += s_rec[i].sp;
-      const double W = block_sum<kRT>(mine, sh);
-      y = pick_index<kRT>(
-          nsb, c.V, u_final * W, [&](int i) { return s_rec[i].sp; },
-          [&](int64_t j) { return fweight<DT>(E::load1(prow, j), wp, c64, s_tab); }, sh);
+      for (int i = lane; i < nsb; i += kWave) mine += fmax(0.0, s_rec[i].a * iSp - s_rec[i].bq * iSq);
+      resid_mass = wave_sum(mine);
+      if (resid_mass > 0.0) {
+        y = wave_pick(
+            nsb, c.V, u_final * resid_mass, [&](int i) { return fmax(0.0, s_rec[i].a * iSp - s_rec[i].bq * iSq); },
+            [&](int64_t j0, double(&w)[16]) {
+              double wq16[16];
+              row16<DT, AL>(c, prow, j0, wp, tps, w);
+              row16<DT, AL>(c, qrow, j0, wq, tqs, wq16);
+#pragma unroll
+              for (int k = 0; k < 16; ++k) w[k] = fmax(0.0, w[k] * iSp - wq16[k] * iSq);
+            });
+      }
     }
-    for (int i = t; i <= K; i += kRT) {
+    if (!resid || !(resid_mass > 0.0)) {  // bonus row, or a residual that vanished: the target row
+      double mine = 0.0;
+      for (int i = lane; i < nsb; i += kWave) mine += s_rec[i].sp;
+      const double W = wave_sum(mine);
+      y = wave_pick(
+          nsb, c.V, u_final * W, [&](int i) { return s_rec[i].sp; },
+          [&](int64_t j0, double(&w)[16]) { row16<DT, AL>(c, prow, j0, wp, tps, w); });
+    }
+    for (int i = lane; i <= K; i += kWave) {
       int v = -1;
       if (i < n) v = c.draft[b * K + i];
       else if (i == n) v = y;
       c.out_tokens[b * (K + 1) + i] = v;
     }
-    if (t == 0) {
+    if (lane == 0) {
       c.out_len[b] = n;
       if (c.out_resid) c.out_resid[b] = resid_mass;
     }
@@ -375,18 +467,18 @@ __global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
   int mode = 0;  // 0: target weights of the final row; 1: residual; 2: residual vanished -> target
   if (!bonus) {
     double mine = 0.0;
-    for (int i = t; i < nsb; i += kWG) mine += fmax(0.0, rr[i].a / Sp - rr[i].bq / Sq);
+    for (int i = t; i < nsb; i += kWG) mine += fmax(0.0, rr[i].a * (1.0 / Sp) - rr[i].bq * (1.0 / Sq));
     resid = block_sum(mine, sh);
     mode = resid > 0.0 ? 1 : 2;
   }
   int y;
   if (mode == 1) {
     y = pick_index(
-        nsb, c.V, st.u_final * resid, [&](int i) { return fmax(0.0, rr[i].a / Sp - rr[i].bq / Sq); },
+        nsb, c.V, st.u_final * resid, [&](int i) { return fmax(0.0, rr[i].a * (1.0 / Sp) - rr[i].bq * (1.0 / Sq)); },
         [&](int64_t j) {
           const double ep = fweight<DT>(E::load1(prow, j), wp, c64, nullptr);
           const double eq = fweight<DT>(E::load1(qrow, j), wq, c64, nullptr);
-          return fmax(0.0, ep / Sp - eq / Sq);
+          return fmax(0.0, ep * (1.0 / Sp) - eq * (1.0 / Sq));
         },
         sh);
   } else {

@@ -6,6 +6,14 @@
 namespace psi {
 
 // --------------------------------------------------------------- loads --
+// Logits are streamed once: 16-byte loads with the nontemporal hint, so that
+// they do not displace reusable lines from the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Loads NV vectors of one row: vector k of this thread is vector index
 // vfirst + k * STRIDE (16 bytes each) when aligned, else the same elements one
 // by one. Out-of-row elements read as -inf.
@@ -20,7 +28,7 @@ __device__ __forceinline__ void load_vecs(const char* row, int V, int nvec, int6
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int64_t idx = vfirst + (int64_t)k * STRIDE;
-      v[k] = idx < nvec ? rp[idx] : make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+      v[k] = idx < nvec ? stream_load(rp + idx) : make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
     }
 #pragma unroll
     for (int k = 0; k < NV; ++k) E::unpack(v[k], x[k]);
@@ -46,7 +54,7 @@ __device__ __forceinline__ void load_raw(const char* row, int V, int nvec, int64
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int64_t idx = vfirst + (int64_t)k * STRIDE;
-      v[k] = idx < nvec ? rp[idx] : make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+      v[k] = idx < nvec ? stream_load(rp + idx) : make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
     }
   } else {
 #pragma unroll
@@ -87,7 +95,7 @@ __device__ __forceinline__ const char* qrow_of(const LinCfg& c, int64_t b, int i
 
 // ------------------------------------------------ final-row weights --
 // fp64 weight 2^((a - m) c) of one logit a of a row with maximum m (c =
-// log2(e) / T). For bfloat16 rows with |m| < 64 and (m + 64) c >= 100 (WRow.tab)
+// log2(e) / T). For bfloat16 rows with m < 64 and (m + 64) c >= 100 (WRow.tab)
 // the weights come from a per-call table of 2^(a c) over the magnitude window
 // [2^-26, 64), times scale = 2^(-m c):
 //   |a| in the window  tab(a) * scale, tab(a) = exp2_fast(a * c);
@@ -95,9 +103,18 @@ __device__ __forceinline__ const char* qrow_of(const LinCfg& c, int64_t b, int i
 //   a <= -64 or -inf   0 (such a weight is below 2^-100 of the row maximum).
 // Every other row takes exp2_fast(a c - m c). The rule depends only on a and
 // the row, so sub-block sums and rescans of the same elements agree bit for
-// bit, whether the table entry is read from LDS or recomputed.
-constexpr int kTabZero = 2 * kTabW;  // table slot holding 0.0
-constexpr int kTabSize = 2 * kTabW + 1;
+// bit, whether the (pre-scaled) table entry is read from LDS or recomputed.
+//
+// Table layout, one slot per 16-bit code h: positive window codes at
+// [0, kTabW), a zero slot at kTabW, negative window codes at
+// [kTabW + 1, 2 kTabW + 1), a zero slot at 2 kTabW + 1.
+constexpr int kTabSize = 2 * (kTabW + 1);
+
+__device__ __forceinline__ uint32_t tab_slot(uint32_t h) {
+  const uint32_t idx = min((h & 0x7fffu) - kTabLo, (uint32_t)kTabW);  // below or above the window -> kTabW
+  return idx + (h >> 15) * (uint32_t)(kTabW + 1);
+}
+__device__ __forceinline__ bool tab_tiny(uint32_t h) { return (h & 0x7fffu) < kTabLo; }
 
 struct WRow {
   double mc, scale;
@@ -134,58 +151,29 @@ __device__ __forceinline__ double tiny_weight(float a, double c64, double scale)
   return scale * __builtin_fma(t, __builtin_fma(t, 0.5, 1.0), 1.0);
 }
 
-// Fills the kTabSize-entry table (positive codes, negative codes, zero slot)
-// with the workgroup's NT threads.
+// Fills the unscaled kTabSize-entry table with the workgroup's NT threads.
 template <int NT>
 __device__ __forceinline__ void fill_tab(double* tab, double c64) {
   for (int i = threadIdx.x; i < kTabSize; i += NT) {
-    const uint32_t code = ((uint32_t)(i / kTabW) << 15) | (kTabLo + (uint32_t)(i % kTabW));
-    tab[i] = i < kTabZero ? tab_entry(code, c64) : 0.0;
+    const int half = i / (kTabW + 1), j = i - half * (kTabW + 1);
+    tab[i] = j < kTabW ? tab_entry(((uint32_t)half << 15) | (kTabLo + (uint32_t)j), c64) : 0.0;
   }
 }
 
+// fweight with an optional table already multiplied by w.scale (nullptr:
+// recompute the entry).
 template <int DT>
-__device__ __forceinline__ double fweight(float a, const WRow& w, double c64, const double* tab) {
+__device__ __forceinline__ double fweight(float a, const WRow& w, double c64, const double* tab_scaled) {
   if constexpr (DT == kBF16) {
     if (w.tab) {
-      const uint32_t h = __float_as_uint(a) >> 16, mag = h & 0x7fffu;
-      if (mag < kTabLo) return tiny_weight(a, c64, w.scale);
-      const uint32_t idx = mag - kTabLo;
-      if (idx >= (uint32_t)kTabW) return 0.0;
-      return (tab ? tab[(h >> 15) * kTabW + idx] : tab_entry(h, c64)) * w.scale;
+      const uint32_t h = __float_as_uint(a) >> 16;
+      if (tab_tiny(h)) return tiny_weight(a, c64, w.scale);
+      const uint32_t k = tab_slot(h);
+      if (k == (uint32_t)kTabW || k == (uint32_t)(2 * kTabW + 1)) return 0.0;
+      return tab_scaled ? tab_scaled[k] : tab_entry(h, c64) * w.scale;
     }
   }
   return exp2_fast(__builtin_fma((double)a, c64, -w.mc));
-}
-
-// fweight of one unpacked 16-byte vector of a table row, table in LDS: one
-// table read per logit, and the (rare) sub-2^-26 magnitudes redone in a branch
-// that only a wave holding one takes.
-template <int EPV>
-__device__ __forceinline__ void fweight_tab_vec(const float (&x)[EPV], const double* tab, double c64, double scale,
-                                                double (&w)[EPV]) {
-  bool tiny = false;
-#pragma unroll
-  for (int e = 0; e < EPV; ++e) {
-    const uint32_t h = __float_as_uint(x[e]) >> 16, mag = h & 0x7fffu;
-    const uint32_t idx = mag - kTabLo;
-    w[e] = tab[idx < (uint32_t)kTabW ? (h >> 15) * kTabW + idx : (uint32_t)kTabZero] * scale;
-    tiny |= mag < kTabLo;
-  }
-  if (__ballot(tiny)) {
-#pragma unroll
-    for (int e = 0; e < EPV; ++e)
-      if (((__float_as_uint(x[e]) >> 16) & 0x7fffu) < kTabLo) w[e] = tiny_weight(x[e], c64, scale);
-  }
-}
-
-// fweight of one unpacked vector of a row that does not use the table.
-// (Two exponentials in flight per lane: enough ILP with several waves per
-// SIMD, and a register footprint that leaves the table path unconstrained.)
-template <int EPV>
-__device__ __forceinline__ void fweight_direct_vec(const float (&x)[EPV], double c64, double mc, double (&w)[EPV]) {
-#pragma unroll 2
-  for (int e = 0; e < EPV; ++e) w[e] = exp2_fast(__builtin_fma((double)x[e], c64, -mc));
 }
 
 // --------------------------------------------- inverse-CDF pick helper --
@@ -279,6 +267,85 @@ __device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, doubl
   }
   __syncthreads();
   return j;
+}
+
+// Inclusive sum over the lanes of a wave, in lane order.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double up = __shfl_up(v, o);
+    if (lane >= o) v += up;
+  }
+  return v;
+}
+
+// The pick of pick_index done by one whole wave (all 64 lanes active), with
+// no workgroup barrier: lane l owns a run of consecutive sub-blocks, then 16
+// consecutive elements of the chosen sub-block, whose weights welb(j0, w)
+// writes (w[k] = weight of element j0 + k, 0 past the end of the row). Same
+// contract: the smallest j whose running weight exceeds target, the last
+// positive weight if rounding leaves none, -1 if every weight is zero.
+// Returns j on every lane.
+template <class WSB, class WELB>
+__device__ int wave_pick(int nsb, int V, double target, WSB wsb, WELB welb) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int per = (nsb + kWave - 1) / kWave;
+  const int s0 = min(nsb, lane * per), s1 = min(nsb, s0 + per);
+  double mine = 0.0;
+  for (int sb = s0; sb < s1; ++sb) mine += wsb(sb);
+  const double excl = wave_incl_scan(mine) - mine;
+  int sel = -1, last = -1;
+  double pref = 0.0, lpref = 0.0;
+  {
+    double acc = excl;
+    for (int sb = s0; sb < s1; ++sb) {
+      const double w = wsb(sb);
+      if (w > 0.0) {
+        if (sel < 0 && acc + w > target) {
+          sel = sb;
+          pref = acc;
+        }
+        last = sb;
+        lpref = acc;
+      }
+      acc += w;
+    }
+  }
+  unsigned long long m = __ballot(sel >= 0);
+  int src;
+  if (m) {
+    src = __ffsll((long long)m) - 1;
+  } else {  // rounding left no crossing: the last sub-block with positive weight
+    m = __ballot(last >= 0);
+    if (!m) return -1;
+    src = 63 - __clzll((long long)m);
+    sel = last;
+    pref = lpref;
+  }
+  const int sbsel = __shfl(sel, src);
+  const double tin = target - __shfl(pref, src);
+  constexpr int EPL = kSB / kWave;
+  const int64_t j0 = (int64_t)sbsel * kSB + (int64_t)lane * EPL;
+  double w[EPL];
+  welb(j0, w);
+  double loc = 0.0;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) loc += w[k];
+  double acc = wave_incl_scan(loc) - loc;
+  int jj = -1, jl = -1;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    if (w[k] > 0.0) {
+      if (jj < 0 && acc + w[k] > tin) jj = (int)(j0 + k);
+      jl = (int)(j0 + k);
+    }
+    acc += w[k];
+  }
+  m = __ballot(jj >= 0);
+  if (m) return __shfl(jj, __ffsll((long long)m) - 1);
+  m = __ballot(jl >= 0);
+  return m ? __shfl(jl, 63 - __clzll((long long)m)) : -1;
 }
 
 // ------------------------------------------------------- draft pick --
