@@ -25,12 +25,14 @@ void timing_mark(hipStream_t s);
 
 constexpr int kMaxK = 64;
 constexpr int kMaxTopK = 256;  // largest top_k of the filtered path
-constexpr int kStatNV = 16;
+constexpr int kStatNV = 16;  // 16-byte vectors per thread in the fp32-grade statistics pass
 // Window of the per-call 2^(a c) table for bfloat16 logits: magnitude codes
-// [kTabLo, kTabLo + kTabW) = |a| in [2^-26, 64), both signs (64 KB of fp64).
+// [kTabLo, kTabLo + kTabW) = |a| in [2^-26, 63.5], both signs (64 KB of fp64
+// with the two zero slots; 8 * (2 kTabW + 1) < 2^16, so slot byte offsets
+// fit 16-bit lanes).
 constexpr uint32_t kTabLo = 101u << 7;
-constexpr int kTabW = 32 * 128;
-constexpr double kTabMaxAbs = 64.0;  // 16-byte vectors per thread in the fp32-grade statistics pass
+constexpr int kTabW = 32 * 128 - 1;
+constexpr double kTabMaxAbs = 63.5;  // the largest magnitude in the window
 
 // Per (row, chunk) record of the fp32-grade statistics pass: chunk maximum of
 // the raw logits and sum of 2^((a - m) * c) with c = log2(e) / T (binary32),

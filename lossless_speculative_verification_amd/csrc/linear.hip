@@ -115,8 +115,10 @@ __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool 
 }
 
 // fp64 sums of this workgroup's sub-blocks [sb0, sb1) of the final row pair
-// (RESID) or the target row alone, one wave per sub-block, with the following
-// sub-blocks' logits in flight while the current one is reduced. TAB: weights
+// (RESID) or the target row alone, one wave per sub-block (sb0 + wave, then
+// every kRWaves-th). Software-pipelined over NBUF register buffers that change
+// roles each step (no copies, so loads stay in flight across steps): bfloat16
+// keeps the next two sub-blocks in flight, fp32 the next one. TAB: weights
 // are read from the pre-scaled LDS tables tp / tq (bfloat16 only).
 template <int DT, bool AL, bool TAB, bool RESID, bool PICK>
 __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
@@ -125,45 +127,57 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec;
   constexpr int VPL = kSB / (kWave * EPV);
+  constexpr int NBUF = DT == kBF16 ? 3 : 2;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const double c64 = c.c64;
-  // sub-blocks in flight per wave beyond the current one: two for bfloat16
-  // (16 VGPRs each), one for fp32 (32 each)
-  constexpr int AHEAD = DT == kBF16 ? 2 : 1;
-  auto load_sb = [&](int s, uint4(&xp)[VPL], uint4(&xq)[VPL]) {
-    if (s < sb1) {
-      load_raw<DT, AL, VPL, kWave>(prow, c.V, c.nvec, (int64_t)s * (kSB / EPV) + lane, xp);
-      if constexpr (RESID) load_raw<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, (int64_t)s * (kSB / EPV) + lane, xq);
+  struct Buf {
+    uint4 p[VPL], q[VPL];
+  };
+  // Loads are issued unconditionally, so that the compiler can count the
+  // ones in flight: a sub-block past this part's range re-reads the part's
+  // last sub-block (never reduced), and vectors past the end of an aligned
+  // row re-read its last vector and are replaced by -inf.
+  auto load = [&](int s, Buf& x) {
+    const int sc = min(s, sb1 - 1);
+    const int64_t v0 = (int64_t)sc * (kSB / EPV) + lane;
+    if constexpr (AL) {
+      const uint4 ninf = make_uint4(E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int64_t idx = v0 + (int64_t)v * kWave, ic = min(idx, (int64_t)c.nvec - 1);
+        const uint4 lp = stream_load((const uint4*)prow + ic);
+        x.p[v] = idx < c.nvec ? lp : ninf;
+        if constexpr (RESID) {
+          const uint4 lq = stream_load((const uint4*)qrow + ic);
+          x.q[v] = idx < c.nvec ? lq : ninf;
+        }
+      }
+    } else {
+      load_raw<DT, AL, VPL, kWave>(prow, c.V, c.nvec, v0, x.p);
+      if constexpr (RESID) load_raw<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, v0, x.q);
     }
   };
-  uint4 cp[VPL], cq[VPL], np_[VPL], nq_[VPL];
-  int sb = sb0 + wave;
-  load_sb(sb, cp, cq);
-  if constexpr (AHEAD == 2) load_sb(sb + kRWaves, np_, nq_);
-  for (; sb < sb1; sb += kRWaves) {
-    uint4 fp_[VPL], fq_[VPL];
-    if constexpr (AHEAD == 2) load_sb(sb + 2 * kRWaves, fp_, fq_);
-    else load_sb(sb + kRWaves, np_, nq_);
+  auto reduce = [&](int s, const Buf& x) {
     double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       if constexpr (TAB) {
         // two bfloat16 codes per word; logits below the window read a zero
         // slot and get their exact weight in the rare call below
-        bool tiny = false;
+        uint32_t low = 0;
+        const char* const tpb = (const char*)tp;
+        const char* const tqb = (const char*)tq;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t wpw = word_of(cp[v], i), wqw = RESID ? word_of(cq[v], i) : 0u;
+          const uint32_t wpw = word_of(x.p[v], i), wqw = RESID ? word_of(x.q[v], i) : 0u;
+          const uint32_t op = tab_offsets2(wpw, low);
+          const uint32_t oq = RESID ? tab_offsets2(wqw, low) : 0u;
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const uint32_t hp = hf ? wpw >> 16 : wpw & 0xffffu;
-            const double ep = tp[tab_slot(hp)];
-            tiny |= tab_tiny(hp);
+            const double ep = *(const double*)(tpb + (hf ? op >> 16 : op & 0xffffu));
             sp += ep;
             if constexpr (RESID) {
-              const uint32_t hq = hf ? wqw >> 16 : wqw & 0xffffu;
-              const double eq = tq[tab_slot(hq)];
-              tiny |= tab_tiny(hq);
+              const double eq = *(const double*)(tqb + (hf ? oq >> 16 : oq & 0xffffu));
               sq += eq;
               const float xp = __uint_as_float(hf ? wpw & 0xffff0000u : wpw << 16);
               const float xq = __uint_as_float(hf ? wqw & 0xffff0000u : wqw << 16);
@@ -173,9 +187,10 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
             }
           }
         }
+        const bool tiny = (low & 0x80008000u) != 0u;
         if (__ballot(tiny)) {
           // a call, so that this rare work stays out of the common path
-          const ResRec f = tiny_fixup(cp[v], RESID ? cq[v] : make_uint4(0, 0, 0, 0), RESID, c64, wp.scale,
+          const ResRec f = tiny_fixup(x.p[v], RESID ? x.q[v] : make_uint4(0, 0, 0, 0), RESID, c64, wp.scale,
                                       wq.scale, dx);
           sp += f.sp;
           sq += f.sq;
@@ -184,8 +199,8 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
         }
       } else {
         float xp[EPV], xq[EPV];
-        E::unpack(cp[v], xp);
-        if constexpr (RESID) E::unpack(cq[v], xq);
+        E::unpack(x.p[v], xp);
+        if constexpr (RESID) E::unpack(x.q[v], xq);
 #pragma unroll 2
         for (int e = 0; e < EPV; ++e) {
           const double ep = exp2_fast(__builtin_fma((double)xp[e], c64, -wp.mc));
@@ -200,7 +215,7 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
         }
       }
     }
-    ResRec* const rec = PICK ? s_rec + sb : c.res + b * c.nsb + sb;
+    ResRec* const rec = PICK ? s_rec + s : c.res + b * c.nsb + s;
     if constexpr (RESID) {
       // lanes 0, 16, 32, 48 hold the sums of sp, sq, a, bq
       const double tot = wave_sum4(sp, sq, a, bq);
@@ -209,14 +224,31 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
       const double tot = wave_sum(sp);
       if (lane == 0) *rec = ResRec{tot, 0.0, 0.0, 0.0};
     }
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      cp[v] = np_[v];
-      if constexpr (RESID) cq[v] = nq_[v];
-      if constexpr (AHEAD == 2) {
-        np_[v] = fp_[v];
-        if constexpr (RESID) nq_[v] = fq_[v];
-      }
+  };
+  constexpr int W = kRWaves;
+  Buf x0, x1, x2;
+  int s = sb0 + wave;
+  if (s >= sb1) return;
+  load(s, x0);
+  if constexpr (NBUF == 3) {
+    load(s + W, x1);
+    for (; s < sb1; s += 3 * W) {
+      load(s + 2 * W, x2);
+      reduce(s, x0);
+      if (s + W >= sb1) break;
+      load(s + 3 * W, x0);
+      reduce(s + W, x1);
+      if (s + 2 * W >= sb1) break;
+      load(s + 4 * W, x1);
+      reduce(s + 2 * W, x2);
+    }
+  } else {
+    for (; s < sb1; s += 2 * W) {
+      load(s + W, x1);
+      reduce(s, x0);
+      if (s + W >= sb1) break;
+      load(s + 2 * W, x0);
+      reduce(s + W, x1);
     }
   }
 }

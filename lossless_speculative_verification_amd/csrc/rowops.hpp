@@ -9,8 +9,9 @@ namespace psi {
 // Logits are streamed once: 16-byte loads with the nontemporal hint, so that
 // they do not displace reusable lines from the caches.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t global_u32x4_t;
 __device__ __forceinline__ uint4 stream_load(const uint4* p) {
-  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  const u32x4_t v = __builtin_nontemporal_load((global_u32x4_t*)p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -97,10 +98,10 @@ __device__ __forceinline__ const char* qrow_of(const LinCfg& c, int64_t b, int i
 // fp64 weight 2^((a - m) c) of one logit a of a row with maximum m (c =
 // log2(e) / T). For bfloat16 rows with m < 64 and (m + 64) c >= 100 (WRow.tab)
 // the weights come from a per-call table of 2^(a c) over the magnitude window
-// [2^-26, 64), times scale = 2^(-m c):
+// [2^-26, 63.5], times scale = 2^(-m c):
 //   |a| in the window  tab(a) * scale, tab(a) = exp2_fast(a * c);
 //   |a| below 2^-26    scale * (1 + t + t^2/2), t = a c ln 2 (exact to 1e-21);
-//   a <= -64 or -inf   0 (such a weight is below 2^-100 of the row maximum).
+//   a < -63.5 or -inf  0 (such a weight is below 2^-100 of the row maximum).
 // Every other row takes exp2_fast(a c - m c). The rule depends only on a and
 // the row, so sub-block sums and rescans of the same elements agree bit for
 // bit, whether the (pre-scaled) table entry is read from LDS or recomputed.
@@ -116,6 +117,20 @@ __device__ __forceinline__ uint32_t tab_slot(uint32_t h) {
 }
 __device__ __forceinline__ bool tab_tiny(uint32_t h) { return (h & 0x7fffu) < kTabLo; }
 
+// Byte offsets (8 * slot) of the two codes packed in a 32-bit word, in the
+// matching 16-bit halves, computed two at a time with packed 16-bit ops. Also
+// ORs the wrapped differences into `low`: bit 15 of a half is set iff that
+// code lies below the window.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t tab_offsets2(uint32_t w, uint32_t& low) {
+  const u16x2_t code = __builtin_bit_cast(u16x2_t, w);
+  const u16x2_t d = (code & (u16x2_t)0x7fff) - (u16x2_t)kTabLo;
+  low |= __builtin_bit_cast(uint32_t, d);
+  const u16x2_t idx = __builtin_elementwise_min(d, (u16x2_t)kTabW);
+  const u16x2_t off = (code >> (u16x2_t)15) * (u16x2_t)(8 * (kTabW + 1)) + (idx << (u16x2_t)3);
+  return __builtin_bit_cast(uint32_t, off);
+}
+
 struct WRow {
   double mc, scale;
   bool tab;
@@ -124,7 +139,7 @@ struct WRow {
 __device__ __forceinline__ WRow wrow(bool bf16_tab, float m, double c64) {
   WRow w;
   w.mc = (double)m * c64;
-  w.tab = bf16_tab && m < 64.0f && ((double)m + 64.0) * c64 >= 100.0;
+  w.tab = bf16_tab && m <= (float)kTabMaxAbs && ((double)m + kTabMaxAbs) * c64 >= 100.0;
   w.scale = w.tab ? exp2_fast(-w.mc) : 0.0;
   return w;
 }
