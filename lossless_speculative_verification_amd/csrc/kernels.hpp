@@ -27,12 +27,16 @@ constexpr int kMaxK = 64;
 constexpr int kMaxTopK = 256;  // largest top_k of the filtered path
 constexpr int kStatNV = 16;  // 16-byte vectors per thread in the fp32-grade statistics pass
 // Window of the per-call 2^(a c) table for bfloat16 logits: magnitude codes
-// [kTabLo, kTabLo + kTabW) = |a| in [2^-26, 63.5], both signs (64 KB of fp64
-// with the two zero slots; 8 * (2 kTabW + 1) < 2^16, so slot byte offsets
-// fit 16-bit lanes).
+// [kTabLo, kTabLo + kTabW) = |a| in [2^-26, 63.25], both signs. Positive codes
+// take slots [0, kTabW), negative ones [kTabNeg, kTabNeg + kTabW); slot kTabW
+// of each half is a zero slot. 8 * kTabSize < 2^16, so the byte offset of a
+// slot fits a 16-bit lane (the sign is its bit 15) and a second table placed
+// right after the first is reached through the LDS immediate offset.
 constexpr uint32_t kTabLo = 101u << 7;
-constexpr int kTabW = 32 * 128 - 1;
-constexpr double kTabMaxAbs = 63.5;  // the largest magnitude in the window
+constexpr int kTabW = 4094;
+constexpr int kTabNeg = 4096;
+constexpr int kTabSize = kTabNeg + kTabW + 1;
+constexpr double kTabMaxAbs = 63.25;  // the largest magnitude in the window
 
 // Per (row, chunk) record of the fp32-grade statistics pass: chunk maximum of
 // the raw logits and sum of 2^((a - m) * c) with c = log2(e) / T (binary32),

@@ -88,27 +88,31 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Weights of the logits of one 16-byte bfloat16 vector pair whose magnitude is
-// below the table window (they read a zero slot in the pass): returns their
-// sums in the layout of ResRec (sp, sq, and the parts where the target part
-// exceeds the draft part).
+// Corrections for one 16-byte bfloat16 vector pair holding logits whose
+// magnitude is below the table window: the pass read a zero slot for them and
+// classified the element by the slot values. Returns, in the layout of ResRec
+// (sp, sq, and the parts where the target part exceeds the draft part), what
+// the exact weights add minus what the slot values added.
 __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool resid, double c64, double scp,
-                                                       double scq, float dx) {
+                                                       double scq, const double* tp, const double* tq) {
   float xp[8], xq[8];
   Elem<kBF16>::unpack(rp, xp);
   Elem<kBF16>::unpack(rq, xq);
   ResRec f = {0.0, 0.0, 0.0, 0.0};
   for (int e = 0; e < 8; ++e) {
-    const double in = resid && xp[e] - xq[e] > dx ? 1.0 : 0.0;
-    if (tab_tiny(__float_as_uint(xp[e]) >> 16)) {
-      const double ep = tiny_weight(xp[e], c64, scp);
-      f.sp += ep;
-      f.a = __builtin_fma(in, ep, f.a);
-    }
-    if (resid && tab_tiny(__float_as_uint(xq[e]) >> 16)) {
-      const double eq = tiny_weight(xq[e], c64, scq);
-      f.sq += eq;
-      f.bq = __builtin_fma(in, eq, f.bq);
+    const uint32_t hp = __float_as_uint(xp[e]) >> 16, hq = __float_as_uint(xq[e]) >> 16;
+    const bool tp_ = tab_tiny(hp), tq_ = resid && tab_tiny(hq);
+    if (!tp_ && !tq_) continue;
+    const double ep_s = tp[tab_slot(hp)];
+    const double ep = tp_ ? tiny_weight(xp[e], c64, scp) : ep_s;
+    if (tp_) f.sp += ep;
+    if (resid) {
+      const double eq_s = tq[tab_slot(hq)];
+      const double eq = tq_ ? tiny_weight(xq[e], c64, scq) : eq_s;
+      if (tq_) f.sq += eq;
+      const bool in = ep > eq, in_s = ep_s > eq_s;
+      f.a += (in ? ep : 0.0) - (in_s ? ep_s : 0.0);
+      f.bq += (in ? eq : 0.0) - (in_s ? eq_s : 0.0);
     }
   }
   return f;
@@ -119,7 +123,9 @@ __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool 
 // every kRWaves-th). Software-pipelined over NBUF register buffers that change
 // roles each step (no copies, so loads stay in flight across steps): bfloat16
 // keeps the next two sub-blocks in flight, fp32 the next one. TAB: weights
-// are read from the pre-scaled LDS tables tp / tq (bfloat16 only).
+// are read from the pre-scaled LDS tables tp / tq (bfloat16 only), whose
+// values estimate the probabilities, so the target part is above the draft
+// part where ep > eq; otherwise where a_p - a_q > dx.
 template <int DT, bool AL, bool TAB, bool RESID, bool PICK>
 __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
                                              int sb0, int sb1, const double* tp, const double* tq, const WRow& wp,
@@ -179,9 +185,7 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
             if constexpr (RESID) {
               const double eq = *(const double*)(tqb + (hf ? oq >> 16 : oq & 0xffffu));
               sq += eq;
-              const float xp = __uint_as_float(hf ? wpw & 0xffff0000u : wpw << 16);
-              const float xq = __uint_as_float(hf ? wqw & 0xffff0000u : wqw << 16);
-              const double in = xp - xq > dx ? 1.0 : 0.0;  // target part above draft part
+              const double in = ep > eq ? 1.0 : 0.0;  // target part above draft part
               a = __builtin_fma(in, ep, a);
               bq = __builtin_fma(in, eq, bq);
             }
@@ -191,7 +195,7 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
         if (__ballot(tiny)) {
           // a call, so that this rare work stays out of the common path
           const ResRec f = tiny_fixup(x.p[v], RESID ? x.q[v] : make_uint4(0, 0, 0, 0), RESID, c64, wp.scale,
-                                      wq.scale, dx);
+                                      wq.scale, tp, tq);
           sp += f.sp;
           sq += f.sq;
           a += f.a;
@@ -376,6 +380,7 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   const double c64 = c.c64;
   WRow wp, wq;
   wpair(tab, mp, mq, resid, c64, wp, wq);
+  norm_pair(wp, wq, resid, sph, sqh);
   // target part above draft part (ep / sph > eq / sqh) <=> a_p - a_q > dx
   const float dx = (float)((::log2(sph) - ::log2(sqh) + wp.mc - wq.mc) / c64);
   const double u_final = c.rng.u((uint32_t)b, (uint32_t)n, kDrawFinal);
@@ -495,6 +500,7 @@ __global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
   const double c64 = c.c64;
   WRow wp, wq;
   wpair(DT == kBF16 && c.tab, st.mp, st.mq, !bonus, c64, wp, wq);
+  norm_pair(wp, wq, !bonus, st.sp_hat, st.sq_hat);
   double resid = 0.0;
   int mode = 0;  // 0: target weights of the final row; 1: residual; 2: residual vanished -> target
   if (!bonus) {

@@ -98,23 +98,20 @@ __device__ __forceinline__ const char* qrow_of(const LinCfg& c, int64_t b, int i
 // fp64 weight 2^((a - m) c) of one logit a of a row with maximum m (c =
 // log2(e) / T). For bfloat16 rows with m < 64 and (m + 64) c >= 100 (WRow.tab)
 // the weights come from a per-call table of 2^(a c) over the magnitude window
-// [2^-26, 63.5], times scale = 2^(-m c):
+// [2^-26, 63.25], times scale = 2^(-m c):
 //   |a| in the window  tab(a) * scale, tab(a) = exp2_fast(a * c);
 //   |a| below 2^-26    scale * (1 + t + t^2/2), t = a c ln 2 (exact to 1e-21);
-//   a < -63.5 or -inf  0 (such a weight is below 2^-100 of the row maximum).
+//   a < -63.25 or -inf 0 (such a weight is below 2^-100 of the row maximum).
 // Every other row takes exp2_fast(a c - m c). The rule depends only on a and
 // the row, so sub-block sums and rescans of the same elements agree bit for
 // bit, whether the (pre-scaled) table entry is read from LDS or recomputed.
 //
-// Table layout, one slot per 16-bit code h: positive window codes at
-// [0, kTabW), a zero slot at kTabW, negative window codes at
-// [kTabW + 1, 2 kTabW + 1), a zero slot at 2 kTabW + 1.
-constexpr int kTabSize = 2 * (kTabW + 1);
-
-__device__ __forceinline__ uint32_t tab_slot(uint32_t h) {
-  const uint32_t idx = min((h & 0x7fffu) - kTabLo, (uint32_t)kTabW);  // below or above the window -> kTabW
-  return idx + (h >> 15) * (uint32_t)(kTabW + 1);
+// Table slot of the 16-bit code h (layout next to kTabLo): codes outside the
+// window read the zero slot of their sign.
+__device__ __forceinline__ uint32_t tab_idx(uint32_t h) {
+  return min((h & 0x7fffu) - kTabLo, (uint32_t)kTabW);  // below or above the window -> kTabW
 }
+__device__ __forceinline__ uint32_t tab_slot(uint32_t h) { return tab_idx(h) + (h >> 15) * (uint32_t)kTabNeg; }
 __device__ __forceinline__ bool tab_tiny(uint32_t h) { return (h & 0x7fffu) < kTabLo; }
 
 // Byte offsets (8 * slot) of the two codes packed in a 32-bit word, in the
@@ -127,8 +124,8 @@ __device__ __forceinline__ uint32_t tab_offsets2(uint32_t w, uint32_t& low) {
   const u16x2_t d = (code & (u16x2_t)0x7fff) - (u16x2_t)kTabLo;
   low |= __builtin_bit_cast(uint32_t, d);
   const u16x2_t idx = __builtin_elementwise_min(d, (u16x2_t)kTabW);
-  const u16x2_t off = (code >> (u16x2_t)15) * (u16x2_t)(8 * (kTabW + 1)) + (idx << (u16x2_t)3);
-  return __builtin_bit_cast(uint32_t, off);
+  static_assert(8 * kTabNeg == 0x8000 && 8 * kTabW < 0x8000, "sign must be bit 15 of the byte offset");
+  return (w & 0x80008000u) | __builtin_bit_cast(uint32_t, idx << (u16x2_t)3);
 }
 
 struct WRow {
@@ -157,6 +154,16 @@ __device__ __forceinline__ void wpair(bool bf16_tab, float mp, float mq, bool re
   }
 }
 
+// The final draw of a linear block divides the pre-scale of a table row pair
+// by the rows' normaliser estimates, so that the scaled table values are
+// estimates of the probabilities themselves and compare directly.
+__device__ __forceinline__ void norm_pair(WRow& wp, WRow& wq, bool resid, double sph, double sqh) {
+  if (wp.tab) {
+    wp.scale = wp.scale / sph;
+    if (resid) wq.scale = wq.scale / sqh;
+  }
+}
+
 __device__ __forceinline__ double tab_entry(uint32_t code, double c64) {
   return exp2_fast((double)__uint_as_float(code << 16) * c64);
 }
@@ -170,7 +177,7 @@ __device__ __forceinline__ double tiny_weight(float a, double c64, double scale)
 template <int NT>
 __device__ __forceinline__ void fill_tab(double* tab, double c64) {
   for (int i = threadIdx.x; i < kTabSize; i += NT) {
-    const int half = i / (kTabW + 1), j = i - half * (kTabW + 1);
+    const int half = i >= kTabNeg, j = i - half * kTabNeg;
     tab[i] = j < kTabW ? tab_entry(((uint32_t)half << 15) | (kTabLo + (uint32_t)j), c64) : 0.0;
   }
 }
@@ -183,9 +190,8 @@ __device__ __forceinline__ double fweight(float a, const WRow& w, double c64, co
     if (w.tab) {
       const uint32_t h = __float_as_uint(a) >> 16;
       if (tab_tiny(h)) return tiny_weight(a, c64, w.scale);
-      const uint32_t k = tab_slot(h);
-      if (k == (uint32_t)kTabW || k == (uint32_t)(2 * kTabW + 1)) return 0.0;
-      return tab_scaled ? tab_scaled[k] : tab_entry(h, c64) * w.scale;
+      if (tab_idx(h) == (uint32_t)kTabW) return 0.0;
+      return tab_scaled ? tab_scaled[tab_slot(h)] : tab_entry(h, c64) * w.scale;
     }
   }
   return exp2_fast(__builtin_fma((double)a, c64, -w.mc));

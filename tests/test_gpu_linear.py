@@ -167,6 +167,51 @@ def test_request_errors_and_special_rows():
     compare_linear(g, o)
 
 
+def _bf16_bits(f: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even."""
+    u = np.ascontiguousarray(f, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _bf16_float(h: np.ndarray) -> np.ndarray:
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_bf16_weight_window_edges(T):
+    """bfloat16 rows full of logits that are zero or below 2^-26 in magnitude
+    (weights outside the table, corrected exactly), logits at the edges of the
+    table window (+-63.25 inside, -63.5 and beyond outside), rows whose
+    maximum disables the table (above 63.25, or too small a spread), and
+    pairs that mix both kinds: lengths, tokens and residual masses match."""
+    B, K, V = 32, 4, 4096
+    p, q = synth.pair(B, K + 1, K, V, "bf16", seed=21, sd_a=2.0, mode=0, sd_noise=1.0)
+    fp, fq = _bf16_float(p).copy(), _bf16_float(q).copy()
+    rng = np.random.default_rng(77)
+    tiny = np.array([0.0, -0.0, 2.0 ** -30, -(2.0 ** -30), 2.0 ** -27, -(2.0 ** -40)], np.float32)
+    edge = np.array([-63.25, -63.5, -64.0, -70.0, -1.0e4], np.float32)
+    for f in (fp, fq):
+        m = rng.random(f.shape) < 0.08
+        f[m] = rng.choice(tiny, size=int(m.sum()))
+        m = rng.random(f.shape) < 0.01
+        f[m] = rng.choice(edge, size=int(m.sum()))
+    for b in range(B):
+        kind = b % 4
+        if kind == 1:  # draft rows peak at the top of the window
+            fq[b, :, 5] = 63.25
+        elif kind == 2:  # target rows peak above the window: no table for the pair
+            fp[b, :, 9] = 63.5
+        elif kind == 3:  # too small a spread for the table
+            fp[b] *= np.float32(0.25)
+            fq[b] *= np.float32(0.25)
+    p, q = _bf16_bits(fp), _bf16_bits(fq)
+    for step in range(3):
+        g, o = _run_pair(p, q, None, T, 4, step, True)
+        ex, dec, _ = compare_linear(g, o)
+        assert ex <= 1
+        assert int((o["len"] < K).sum()) > 0  # residual draws happen
+
+
 def test_greedy_parity():
     """Greedy mode (temperature 0) on the filtered/greedy workload shape, fused
     drafts (argmax of q) and given drafts."""
