@@ -22,6 +22,10 @@ void timing_mark(hipStream_t s);
     ::psi::timing_mark(s);                                          \
   } while (0)
 #define PSI_LAUNCH(s, kernel, grid, block, ...) PSI_LAUNCH_LDS(s, kernel, grid, block, 0, __VA_ARGS__)
+// Calls the instance fn<dtype, aligned> of a launcher template.
+#define PSI_DISPATCH(fn, dtype, aligned, ...)                                                    \
+  ((dtype) == kBF16 ? ((aligned) ? fn<kBF16, true>(__VA_ARGS__) : fn<kBF16, false>(__VA_ARGS__)) \
+                    : ((aligned) ? fn<kF32, true>(__VA_ARGS__) : fn<kF32, false>(__VA_ARGS__)))
 
 constexpr int kMaxK = 64;
 constexpr int kMaxTopK = 256;  // largest top_k of the filtered path

@@ -7,10 +7,9 @@
 // survives draw one more token from the last target row.
 //
 // Pipeline (every kernel enqueued on the caller's stream, nothing allocated):
-//   k_stats32   one workgroup per (row, chunk): exact chunk maximum and the sum
-//               of 2^((a - m) * c) (binary32 exp2, fp64 accumulation) for every
-//               target and draft row -> log-normalisers good to ~1e-7, enough
-//               for the accept test.
+//   k_stats32   (stats.hip) chunk maxima and sums of every target and draft
+//               row -> log-normalisers good to ~1e-7, enough for the accept
+//               test.
 //   k_resolve   per request (16 waves): row normalisers, p(x_i), q(x_i),
 //               Philox accept tests and a wave ballot for the first rejection
 //               n; then fp64 sums per 1024-element sub-block over the one row
@@ -34,49 +33,6 @@ namespace psi {
 constexpr int64_t kResolveOneWgMinB = 192;
 constexpr int64_t kResolveTargetWgs = 256;
 constexpr size_t kResolveMaxLds = 64 * 1024;
-
-// ------------------------------------------------------ statistics pass --
-template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_stats32(LinCfg c) {
-  constexpr int EPV = Elem<DT>::kPerVec;
-  const int64_t item = blockIdx.x;
-  const int chunk = (int)(item % c.nch32);
-  const int64_t sr = item / c.nch32;
-  const char* row = c.rows.row(sr);
-  __shared__ float shf[kWaves];
-  __shared__ double shd[kWaves];
-  float x[kStatNV][EPV];
-  load_vecs<DT, AL, kStatNV, kWG>(row, c.V, c.nvec, (int64_t)chunk * kWG * kStatNV + threadIdx.x, x);
-  float m = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kStatNV; ++k)
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) m = fmaxnan(m, x[k][e]);
-  m = block_max(m, shf);
-  double s = 0.0;
-  if (!is_neg_inf(m)) {
-    // exp2(x*c - round(m*c)) = 2^((x-m)c) * 2^(mc_lo); the common factor
-    // 2^(mc_lo) is removed once per chunk in fp64.
-    const float mc_hi = m * c.c32;
-    const float mc_lo = fmaf(m, c.c32, -mc_hi);
-#pragma unroll
-    for (int k = 0; k < kStatNV; ++k) {
-      float e[EPV];
-#pragma unroll
-      for (int j = 0; j < EPV; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(x[k][j], c.c32, -mc_hi));
-      s += (double)pairwise_sum(e);
-    }
-    s = block_sum(s, shd);
-    s *= ::exp2(-(double)mc_lo);
-  }
-  if (threadIdx.x == 0) {
-    StatRec r;
-    r.m = m;
-    r.pad = 0;
-    r.s = s;
-    c.st[item] = r;
-  }
-}
 
 // ------------------------------------------------------------ resolve --
 // Threads of a resolve workgroup: 16 waves, so that one workgroup per request
@@ -747,7 +703,8 @@ __global__ __launch_bounds__(kWG) void k_greedy_draft(LinCfg c) {
 template <int DT, bool AL>
 static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
   const int64_t rows = c.B * (2 * c.K + 1);
-  PSI_LAUNCH(s, (k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
+  const hipError_t e = launch_stats32(c, rows, DT, s);
+  if (e != hipSuccess) return e;
   // One resolve workgroup per request when there are enough requests to fill
   // the chip (and its sub-block records fit in LDS); otherwise several per
   // request and a separate final step.
@@ -787,12 +744,6 @@ static hipError_t draft_greedy_t(const LinCfg& c, hipStream_t s) {
 }
 
 template <int DT, bool AL>
-static hipError_t stats32_t(const LinCfg& c, int64_t rows, hipStream_t s) {
-  PSI_LAUNCH(s, (k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
-  return hipGetLastError();
-}
-
-template <int DT, bool AL>
 static hipError_t draftpass_t(const LinCfg& c, int64_t rows, hipStream_t s) {
   PSI_LAUNCH(s, (k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)rows), dim3(kWG), c);
   return hipGetLastError();
@@ -803,10 +754,6 @@ static hipError_t argmax_t(const LinCfg& c, int64_t rows, hipStream_t s) {
   PSI_LAUNCH(s, (k_argmax<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
   return hipGetLastError();
 }
-
-#define PSI_DISPATCH(fn, dtype, aligned, ...)                                      \
-  ((dtype) == kBF16 ? ((aligned) ? fn<kBF16, true>(__VA_ARGS__) : fn<kBF16, false>(__VA_ARGS__)) \
-                    : ((aligned) ? fn<kF32, true>(__VA_ARGS__) : fn<kF32, false>(__VA_ARGS__)))
 
 hipError_t launch_linear_sampled(const LinCfg& c, int dtype, hipStream_t s) {
   return PSI_DISPATCH(linear_sampled_t, dtype, c.aligned, c, s);
@@ -819,9 +766,6 @@ hipError_t launch_draft_sampled(const LinCfg& c, int dtype, hipStream_t s) {
 }
 hipError_t launch_draft_greedy(const LinCfg& c, int dtype, hipStream_t s) {
   return PSI_DISPATCH(draft_greedy_t, dtype, c.aligned, c, s);
-}
-hipError_t launch_stats32(const LinCfg& c, int64_t rows, int dtype, hipStream_t s) {
-  return PSI_DISPATCH(stats32_t, dtype, c.aligned, c, rows, s);
 }
 hipError_t launch_draftpass(const LinCfg& c, int64_t rows, int dtype, hipStream_t s) {
   return PSI_DISPATCH(draftpass_t, dtype, c.aligned, c, rows, s);
