@@ -42,8 +42,10 @@ inline int filt_stride(int32_t V) { return V < kMaxTopK ? V : kMaxTopK; }
 
 // Workspace sections, each 256-byte aligned.
 struct Layout {
-  size_t st, rs, res, dr, fh, fe, rst, ts, tres, total;
+  size_t st, rs, res, dr, fh, fe, fk, fc, rst, ts, tres, total;
 };
+
+inline int nchf_of(int32_t V) { return (V + kFiltChunk - 1) / kFiltChunk; }
 
 inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
   Layout L;
@@ -61,6 +63,10 @@ inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
   off = align_up(off + (size_t)B * rows_per_req * sizeof(FiltRow), 256);
   L.fe = off;
   off = align_up(off + (size_t)B * rows_per_req * filt_stride(V) * sizeof(FiltEnt), 256);
+  L.fk = off;
+  off = align_up(off + (size_t)B * rows_per_req * nchf_of(V) * sizeof(FiltChunk), 256);
+  L.fc = off;
+  off = align_up(off + (size_t)B * rows_per_req * nchf_of(V) * kFiltChunkCap * sizeof(FiltCand), 256);
   L.rst = off;
   off = align_up(off + (size_t)B * rows_per_req * sizeof(RowStat), 256);
   L.ts = off;
@@ -100,7 +106,10 @@ inline FiltCfg filt_cfg(const psispec_params* prm, void* ws, int64_t B, int32_t 
   FiltCfg f;
   f.hdr = (FiltRow*)((char*)ws + L.fh);
   f.ent = (FiltEnt*)((char*)ws + L.fe);
+  f.chk = (FiltChunk*)((char*)ws + L.fk);
+  f.fc = (FiltCand*)((char*)ws + L.fc);
   f.stride = filt_stride(V);
+  f.nchf = nchf_of(V);
   f.kk = prm->top_k;
   f.T = (double)prm->temperature;
   f.top_p = (double)prm->top_p;

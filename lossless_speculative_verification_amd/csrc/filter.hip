@@ -3,45 +3,47 @@
 // applied identically to every target and draft row, then Psi-Spec verification
 // ("Uno" research explainer, §3.3) on the filtered distributions.
 //
-//   k_filter_row   one workgroup per row: streams the row once, keeping an exact
-//                  running top-k in LDS (an element enters only if it exceeds the
-//                  current k-th value; rows are streamed in index order, so ties
-//                  go to the lower id), compacts with a bitonic sort when the
-//                  buffer fills, then applies top-p and the log-normaliser in
-//                  fp64 over the kept set, in the same order as the plain
-//                  definition (sums in token-id order, cumulative sum in
-//                  probability order).
-//   k_filt_decide  one workgroup per request: fused draft draws, p(x)/q(x),
-//                  accept tests, first rejection, residual or bonus draw over the
-//                  (at most top_k entry) supports, outputs.
-//   k_filt_draft   one workgroup per draft row: draft draw only.
+//   k_filt_chunk   one workgroup per (row, 16384-logit chunk), logits kept in
+//                  registers: a lower bound tau of the chunk's k-th largest
+//                  logit (each wave's ceil(k/4)-th largest per-thread maximum,
+//                  the smallest of the four: at least k logits are >= tau),
+//                  then every finite logit >= tau is a candidate. Every
+//                  logit of the chunk's exact top-k, ties included, is one.
+//   k_filt_merge   one workgroup per row: the row bound is the largest chunk
+//                  bound; the candidates >= it (a chunk with too many stored
+//                  none and is read again) are sorted by (logit desc, id asc)
+//                  and the first k kept, exactly as the plain definition
+//                  orders them; then top-p over that order and the
+//                  log-normaliser, in fp64, and the kept set in id order.
+//                  More candidates than LDS holds: the row is streamed again
+//                  with a running exact top-k.
+//   k_filt_decide  one workgroup per request: fused draft draws (one wave per
+//                  row), p(x)/q(x), accept tests, first rejection, residual or
+//                  bonus draw over the kept set staged in LDS, outputs.
+//   k_filt_draft   draft draws only.
 #include "rowops.hpp"
 
 namespace psi {
 
 namespace {
 
-constexpr int kSortCap = 4096;  // LDS sort capacity (power of two)
-
-struct KeyIdx {
-  float v;
-  int32_t i;
-};
+constexpr int kSortCap = 4096;  // LDS candidate capacity of the row merge (power of two)
+constexpr int kMaxOvf = 64;     // chunks read again per row before the whole row is
 
 // (value desc, index asc): true if a comes first.
-__device__ __forceinline__ bool before(const KeyIdx& a, const KeyIdx& b) {
+__device__ __forceinline__ bool before(const FiltCand& a, const FiltCand& b) {
   return a.v > b.v || (a.v == b.v && a.i < b.i);
 }
 
 // In-LDS bitonic sort of n (power of two, <= kSortCap) entries in "before" order.
-__device__ void bitonic_sort(KeyIdx* a, int n) {
+__device__ void bitonic_sort(FiltCand* a, int n) {
   for (int k = 2; k <= n; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int t = threadIdx.x; t < n; t += blockDim.x) {
         const int p = t ^ j;
         if (p > t) {
           const bool up = (t & k) == 0;
-          const KeyIdx x = a[t], y = a[p];
+          const FiltCand x = a[t], y = a[p];
           if (up ? before(y, x) : before(x, y)) {
             a[t] = y;
             a[p] = x;
@@ -59,190 +61,364 @@ __device__ __forceinline__ int pow2_at_least(int n) {
   return p;
 }
 
-// Sorts the first `cnt` candidates and keeps the best `kk`; returns the new count.
-__device__ int compact(KeyIdx* cand, int cnt, int kk) {
+// Pads cand[cnt .. pow2) with entries that sort last, sorts, and returns the
+// number kept (at most kk).
+__device__ int sort_keep(FiltCand* cand, int cnt, int kk) {
   const int n = pow2_at_least(cnt < 2 ? 2 : cnt);
-  for (int t = cnt + threadIdx.x; t < n; t += blockDim.x) cand[t] = KeyIdx{-INFINITY, 0x7fffffff};
+  for (int t = cnt + threadIdx.x; t < n; t += blockDim.x) cand[t] = FiltCand{-INFINITY, 0x7fffffff};
   __syncthreads();
   bitonic_sort(cand, n);
   return cnt < kk ? cnt : kk;
 }
 
-// Double-precision entries of a filtered row, sorted by token id.
-struct DEnt {
-  double z;
-  int32_t i;
-  int32_t pad;
-};
+// Exclusive scan of one int per thread over the workgroup, in thread order;
+// writes the total. `sh` needs kWaves slots.
+__device__ int block_scan_int(int v, int* sh, int* total) {
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int up = __shfl_up(incl, o);
+    if (lane >= o) incl += up;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) sh[w] = incl;
+  __syncthreads();
+  int before_ = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int x = sh[i];
+    if (i < w) before_ += x;
+    all += x;
+  }
+  *total = all;
+  return before_ + incl - v;
+}
 
-}  // namespace
+// Sorts one value per lane across the wave, largest at lane 0 (bitonic).
+__device__ __forceinline__ float wave_sort_desc(float v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float o = __shfl_xor(v, j);
+      const bool lower = (lane & j) == 0, desc = (lane & k) == 0;
+      v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
+    }
+  }
+  return v;
+}
 
-// -------------------------------------------------------------- row filter --
+// Running exact top-k of a whole row streamed in token order: an element
+// enters the LDS buffer only if it exceeds the current k-th value (so a later
+// equal element loses its tie), and a full buffer is sorted and cut back to k.
+// Leaves the kept entries sorted in cand[0 .. returned count).
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_filter_row(LinCfg c, FiltCfg f) {
+__device__ int stream_topk(const LinCfg& c, const char* row, int kk, FiltCand* cand, int* s_cnt, float* s_tau) {
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec;
-  constexpr int NV = 4;  // 16-byte vectors per thread per tile
-  const int64_t sr = blockIdx.x;
-  const char* row = c.rows.row(sr);
-  const int kk = f.kk;
-  const int cap = kSortCap;
-  __shared__ KeyIdx cand[kSortCap];
-  __shared__ int s_cnt, s_bad, s_any;
-  __shared__ float s_tau;
+  constexpr int NV = 4;
   if (threadIdx.x == 0) {
-    s_cnt = 0;
-    s_bad = 0;
-    s_any = 0;
-    s_tau = -INFINITY;
+    *s_cnt = 0;
+    *s_tau = -INFINITY;
   }
   __syncthreads();
   const int64_t nvec = (c.V + EPV - 1) / EPV;
   const int64_t tile_vec = (int64_t)kWG * NV;
   const int64_t ntiles = (nvec + tile_vec - 1) / tile_vec;
-  int bad = 0, any = 0;
   for (int64_t tl = 0; tl < ntiles; ++tl) {
     uint4 v[NV];
     load_raw<DT, AL, NV, kWG>(row, c.V, c.nvec, tl * tile_vec + threadIdx.x, v);
-    // sub-tile k = vectors [k*kWG, (k+1)*kWG) of the tile: sub-tiles are in token
-    // order, so a value equal to the current threshold always loses its tie
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       float x[EPV];
       E::unpack(v[k], x);
-      const float tau = s_tau;
+      const float tau = *s_tau;
       const int64_t j0 = (tl * tile_vec + (int64_t)k * kWG + threadIdx.x) * EPV;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
-        const float xe = x[e];
-        bad |= isnan(xe) || (isinf(xe) && xe > 0.0f);
-        any |= xe > -INFINITY;
-        if (xe > tau) {
-          const int slot = atomicAdd(&s_cnt, 1);
-          if (slot < cap) cand[slot] = KeyIdx{xe, (int32_t)(j0 + e)};
+        if (x[e] > tau) {
+          const int slot = atomicAdd(s_cnt, 1);
+          if (slot < kSortCap) cand[slot] = FiltCand{x[e], (int32_t)(j0 + e)};
         }
       }
       __syncthreads();
-      if (s_cnt > cap - kWG * EPV) {
-        const int kept = compact(cand, s_cnt < cap ? s_cnt : cap, kk);
+      if (*s_cnt > kSortCap - kWG * EPV) {
+        const int kept = sort_keep(cand, *s_cnt < kSortCap ? *s_cnt : kSortCap, kk);
         if (threadIdx.x == 0) {
-          s_cnt = kept;
-          if (kept >= kk) s_tau = cand[kk - 1].v;
+          *s_cnt = kept;
+          if (kept >= kk) *s_tau = cand[kk - 1].v;
         }
       }
       __syncthreads();
     }
   }
-  if (bad) atomicOr(&s_bad, 1);
-  if (any) atomicOr(&s_any, 1);
+  const int cnt = *s_cnt;
   __syncthreads();
-  int cnt = compact(cand, s_cnt, kk);
-  __syncthreads();
-  // ---- fp64 filter over the kept set ----
-  // cand[0..cnt) is sorted by (value desc, id asc), which is also the order of
-  // probability desc / id asc because z = a / T is strictly increasing in a.
-  __shared__ DEnt ent[kMaxTopK];
-  __shared__ KeyIdx byid[kMaxTopK];
-  __shared__ int s_keep;
-  const double T = f.T;
-  const int n2 = pow2_at_least(cnt < 2 ? 2 : cnt);
-  for (int t = threadIdx.x; t < n2; t += kWG) byid[t] = t < cnt ? KeyIdx{0.0f, cand[t].i} : KeyIdx{-INFINITY, 0x7fffffff};
-  __syncthreads();
-  bitonic_sort(byid, n2);  // equal keys -> ascending token id
-  for (int t = threadIdx.x; t < cnt; t += kWG) {
-    const int id = byid[t].i;
-    float val = 0.0f;
-    for (int u = 0; u < cnt; ++u)
-      if (cand[u].i == id) val = cand[u].v;
-    ent[t].z = (double)val / T;
-    ent[t].i = id;
-    ent[t].pad = 0;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int keep = cnt;
-    if (f.top_p < 1.0 && cnt > 0) {
-      double m = -INFINITY;
-      for (int t = 0; t < cnt; ++t) m = fmax(m, ent[t].z);
-      double S = 0.0;
-      for (int t = 0; t < cnt; ++t) S += ::exp(ent[t].z - m);  // id order
-      double cum = 0.0;
-      for (int t = 0; t < cnt; ++t) {  // probability order
-        cum += ::exp((double)cand[t].v / T - m) / S;
-        if (cum >= f.top_p) {
-          keep = t + 1;
-          break;
-        }
-      }
+  return sort_keep(cand, cnt, kk);
+}
+
+}  // namespace
+
+// ------------------------------------------------------- chunk candidates --
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_filt_chunk(LinCfg c, FiltCfg f) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec, NV = kFiltVals / EPV;
+  const int64_t item = blockIdx.x;
+  const int64_t sr = item / f.nchf;
+  const int ch = (int)(item - sr * f.nchf);
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const char* row = c.rows.row(sr);
+  const int64_t v0 = (int64_t)ch * kWG * NV + t;
+  float x[NV][EPV];
+  load_vecs<DT, AL, NV, kWG>(row, c.V, c.nvec, v0, x);
+  int bad = 0, any = 0;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const float xe = x[k][e];
+      bad |= isnan(xe) || xe == INFINITY;
+      any |= xe > -INFINITY;
+      mx = fmaxf(mx, xe);
     }
-    // final set: the first `keep` candidates, listed in id order
+  // Each wave has kq threads whose maximum is >= its kq-th largest thread
+  // maximum, so the smallest of the four wave values bounds the chunk's
+  // (4 kq >= kk)-th largest logit from below.
+  __shared__ float s_w[kWaves];
+  __shared__ int s_sc[kWaves];
+  const int kq = (f.kk + kWaves - 1) / kWaves;
+  const float wq = __shfl(wave_sort_desc(mx), kq - 1);
+  if (lane == 0) s_w[wave] = wq;
+  bad = __syncthreads_or(bad);
+  any = __syncthreads_or(any);
+  float tau = s_w[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) tau = fminf(tau, s_w[i]);
+  int n = 0;
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) n += (x[k][e] >= tau && x[k][e] > -INFINITY) ? 1 : 0;
+  int total;
+  const int off = block_scan_int(n, s_sc, &total);
+  if (total <= kFiltChunkCap) {
+    FiltCand* out = f.fc + item * kFiltChunkCap + off;
     int w = 0;
-    if (keep < cnt) {
-      const KeyIdx last = cand[keep - 1];
-      for (int t = 0; t < cnt; ++t) {
-        const int id = ent[t].i;
-        float val = 0.0f;
-        for (int u = 0; u < cnt; ++u)
-          if (cand[u].i == id) val = cand[u].v;
-        const KeyIdx me = KeyIdx{val, id};
-        if (!before(last, me)) ent[w++] = ent[t];
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e)
+        if (x[k][e] >= tau && x[k][e] > -INFINITY) out[w++] = FiltCand{x[k][e], (int32_t)((v0 + (int64_t)k * kWG) * EPV + e)};
+  }
+  if (t == 0) f.chk[item] = FiltChunk{tau, total, (bad ? 1 : 0) | (any ? 2 : 0), 0};
+}
+
+// -------------------------------------------------------------- row merge --
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_filt_merge(LinCfg c, FiltCfg f) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec, NV = kFiltVals / EPV;
+  const int64_t sr = blockIdx.x;
+  const int t = threadIdx.x;
+  const int kk = f.kk;
+  __shared__ FiltCand cand[kSortCap];
+  __shared__ int s_cnt, s_novf, s_first;
+  __shared__ float s_tau;
+  __shared__ int s_ovf[kMaxOvf];
+  __shared__ float shf[kWaves];
+  __shared__ double shd[kWG + kWaves];
+  const FiltChunk* rec = f.chk + sr * f.nchf;
+  FiltRow* hdr = f.hdr + sr;
+  if (t == 0) {
+    s_cnt = 0;
+    s_novf = 0;
+  }
+  // row bound and validity from the chunk records
+  float tl = -INFINITY;
+  int fl = 0;
+  for (int ch = t; ch < f.nchf; ch += kWG) {
+    const FiltChunk r = rec[ch];
+    tl = fmaxf(tl, r.tau);
+    fl |= r.flags;
+  }
+  const float tau = block_max(tl, shf);
+  const int bad = __syncthreads_or(fl & 1);
+  const int any = __syncthreads_or(fl & 2);
+  if (bad || !any) {
+    if (t == 0) *hdr = FiltRow{0, 1, -INFINITY, -INFINITY};
+    return;
+  }
+  // gather every stored candidate >= tau; note the chunks that stored none
+  auto push = [&](float v, int32_t i) {
+    const int slot = atomicAdd(&s_cnt, 1);
+    if (slot < kSortCap) cand[slot] = FiltCand{v, i};
+  };
+  const FiltCand* src = f.fc + sr * f.nchf * (int64_t)kFiltChunkCap;
+  for (int s = t; s < f.nchf * kFiltChunkCap; s += kWG) {
+    const int ch = s / kFiltChunkCap, i = s - ch * kFiltChunkCap;
+    const int n = rec[ch].cnt;
+    if (n <= kFiltChunkCap) {
+      if (i < n) {
+        const FiltCand e = src[s];
+        if (e.v >= tau) push(e.v, e.i);
       }
-    } else {
-      w = cnt;
+    } else if (i == 0) {
+      const int k = atomicAdd(&s_novf, 1);
+      if (k < kMaxOvf) s_ovf[k] = ch;
     }
-    s_keep = w;
   }
   __syncthreads();
-  cnt = s_keep;
-  // log-normaliser over the final set (id order)
-  if (threadIdx.x == 0) {
-    double m = -INFINITY;
-    for (int t = 0; t < cnt; ++t) m = fmax(m, ent[t].z);
-    double S = 0.0;
-    for (int t = 0; t < cnt; ++t) S += ::exp(ent[t].z - m);
-    FiltRow h;
-    h.cnt = cnt;
-    h.bad = s_bad || !s_any;
-    h.m = m;
-    h.L = cnt > 0 ? m + ::log(S) : -INFINITY;
-    f.hdr[sr] = h;
+  const int novf = s_novf;
+  const char* row = c.rows.row(sr);
+  if (novf <= kMaxOvf) {
+    for (int k = 0; k < novf; ++k) {
+      const int ch = s_ovf[k];
+      const int64_t v0 = (int64_t)ch * kWG * NV + t;
+      float x[NV][EPV];
+      load_vecs<DT, AL, NV, kWG>(row, c.V, c.nvec, v0, x);
+#pragma unroll
+      for (int q = 0; q < NV; ++q)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+          if (x[q][e] >= tau && x[q][e] > -INFINITY) push(x[q][e], (int32_t)((v0 + (int64_t)q * kWG) * EPV + e));
+    }
   }
   __syncthreads();
-  FiltEnt* out = f.ent + sr * (int64_t)f.stride;
-  for (int t = threadIdx.x; t < cnt; t += kWG) {
-    FiltEnt e;
-    e.i = ent[t].i;
-    e.pad = 0;
-    e.z = ent[t].z;
-    out[t] = e;
+  const int total = s_cnt;
+  __syncthreads();
+  int cnt;
+  if (novf > kMaxOvf || total > kSortCap) cnt = stream_topk<DT, AL>(c, row, kk, cand, &s_cnt, &s_tau);
+  else cnt = sort_keep(cand, total, kk);
+  // ---- fp64 filter over cand[0 .. cnt), ordered by (logit desc, id asc),
+  // which is the order of probability desc / id asc since z = a / T is
+  // increasing in a. One entry per thread (cnt <= kMaxTopK = kWG).
+  const double T = f.T;
+  const double m = (double)cand[0].v / T;
+  const bool mine = t < cnt;
+  double z = 0.0, e = 0.0;
+  if (mine) {
+    z = (double)cand[t].v / T;
+    e = ::exp(z - m);
+  }
+  int keep = cnt;
+  if (f.top_p < 1.0) {
+    const double S = block_sum(e, shd);
+    const double p = mine ? e / S : 0.0;
+    double tot;
+    const double incl = block_exclusive_scan(p, shd, &tot) + p;
+    if (t == 0) s_first = 0x7fffffff;
+    __syncthreads();
+    if (mine && incl >= f.top_p) atomicMin(&s_first, t);
+    __syncthreads();
+    if (s_first < cnt) keep = s_first + 1;
+  }
+  const double S = block_sum(t < keep ? e : 0.0, shd);
+  if (t == 0) *hdr = FiltRow{keep, 0, m, m + ::log(S)};
+  if (t < keep) {
+    // position in token-id order
+    const int id = cand[t].i;
+    int rank = 0;
+    for (int s = 0; s < keep; ++s) rank += cand[s].i < id ? 1 : 0;
+    FiltEnt* out = f.ent + sr * (int64_t)f.stride;
+    out[rank] = FiltEnt{id, 0, z};
   }
 }
 
 // --------------------------------------------------- per-request decision --
+namespace {
+
+// Inverse-CDF draw over a kept list (cnt <= 4 * 64 entries in token-id order)
+// by one whole wave, lane l owning entries 4l .. 4l+3: the smallest entry
+// whose running sum exceeds u * W, else the last positive one; -1 if W is not
+// positive. Returns the entry's position on every lane.
+template <class W>
+__device__ int wave_draw(int cnt, double u, W w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  double wl[4], loc = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int k = lane * 4 + j;
+    wl[j] = k < cnt ? w(k) : 0.0;
+    loc += wl[j];
+  }
+  const double incl = wave_incl_scan(loc);
+  const double tot = __shfl(incl, kWave - 1);
+  if (!(tot > 0.0)) return -1;
+  const double target = u * tot;
+  double acc = incl - loc;
+  int jj = -1, jl = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (wl[j] > 0.0) {
+      if (jj < 0 && acc + wl[j] > target) jj = lane * 4 + j;
+      jl = lane * 4 + j;
+    }
+    acc += wl[j];
+  }
+  unsigned long long m = __ballot(jj >= 0);
+  if (m) return __shfl(jj, __ffsll((long long)m) - 1);
+  m = __ballot(jl >= 0);
+  return m ? __shfl(jl, 63 - __clzll((long long)m)) : -1;
+}
+
+// Probability of token x under a kept set held in LDS (id order).
+__device__ __forceinline__ double lds_prob(const FiltEnt* e, int cnt, double L, int x) {
+  int lo = 0, hi = cnt - 1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    const int id = e[mid].i;
+    if (id == x) return ::exp(e[mid].z - L);
+    if (id < x) lo = mid + 1;
+    else hi = mid - 1;
+  }
+  return 0.0;
+}
+
+// Draft draws of request b by the workgroup's waves, one draft row per wave
+// at a time; writes s_x[i] (-1 for an invalid row).
+__device__ void filt_drafts(const LinCfg& c, const FiltCfg& f, int64_t b, const FiltRow* Hq, const FiltEnt* Eq,
+                            int K, int* s_x) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  for (int i = wave; i < K; i += kWaves) {
+    const FiltRow hq = Hq[i];
+    const FiltEnt* eq = Eq + i * (int64_t)f.stride;
+    int x = -1;
+    if (!hq.bad && hq.cnt > 0) {
+      const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
+      const int k = wave_draw(hq.cnt, u, [&](int j) { return ::exp(eq[j].z - hq.m); });
+      x = k >= 0 ? eq[k].i : -1;
+    }
+    if (lane == 0) s_x[i] = x;
+  }
+}
+
+}  // namespace
+
 __global__ __launch_bounds__(kWG) void k_filt_decide(LinCfg c, FiltCfg f) {
   const int64_t b = blockIdx.x;
   const int K = c.K, R = 2 * K + 1, t = threadIdx.x;
   const FiltRow* H = f.hdr + b * R;
   const FiltEnt* Ent = f.ent + b * R * (int64_t)f.stride;
-  __shared__ int s_bad, s_n;
+  __shared__ int s_bad, s_n, s_sel;
   __shared__ int s_x[kMaxK];
+  __shared__ FiltEnt s_ep[kMaxTopK], s_eq[kMaxTopK];
+  __shared__ double shd[kWG + kWaves];
   if (t == 0) s_bad = 0;
   __syncthreads();
   for (int i = t; i < R; i += kWG)
     if (H[i].bad || H[i].cnt <= 0) atomicOr(&s_bad, 1);
-  if (t < K) {
-    int x;
-    if (c.fused) {
-      const FiltRow hq = H[K + 1 + t];
-      const FiltEnt* eq = Ent + (K + 1 + t) * (int64_t)f.stride;
-      const double u = c.rng.u((uint32_t)b, (uint32_t)t, kDrawDraft);
-      x = hq.cnt > 0 ? draw_list(hq.cnt, u, [&](int k) { return ::exp(eq[k].z - hq.m); }, eq) : -1;
-    } else {
-      x = c.draft[b * K + t];
-    }
-    if (x < 0 || x >= c.V) atomicOr(&s_bad, 1);
-    s_x[t] = x;
+  if (c.fused) {
+    filt_drafts(c, f, b, H + K + 1, Ent + (K + 1) * (int64_t)f.stride, K, s_x);
+  } else {
+    for (int i = t; i < K; i += kWG) s_x[i] = c.draft[b * K + i];
   }
+  __syncthreads();
+  for (int i = t; i < K; i += kWG)
+    if (s_x[i] < 0 || s_x[i] >= c.V) atomicOr(&s_bad, 1);
   __syncthreads();
   int acc = 1;
   double P = 0.0, Q = 0.0;
@@ -278,29 +454,41 @@ __global__ __launch_bounds__(kWG) void k_filt_decide(LinCfg c, FiltCfg f) {
       c.out_probs[(b * K + t) * 2 + 1] = (float)Q;
     }
   }
+  // ---- final draw over the kept set of target row n (one entry per thread)
+  const bool resid = n < K;
+  const FiltRow hp = H[n];
+  const FiltRow hq = resid ? H[K + 1 + n] : FiltRow{0, 0, 0.0, 0.0};
+  if (t < hp.cnt) s_ep[t] = Ent[n * (int64_t)f.stride + t];
+  if (resid && t < hq.cnt) s_eq[t] = Ent[(K + 1 + n) * (int64_t)f.stride + t];
+  __syncthreads();
+  const bool mine = t < hp.cnt;
+  const double pj = mine ? ::exp(s_ep[t].z - hp.L) : 0.0;
+  double w = pj, mass = 0.0;
+  if (resid) {
+    w = mine ? fmax(0.0, pj - lds_prob(s_eq, hq.cnt, hq.L, s_ep[t].i)) : 0.0;
+    mass = block_sum(w, shd);
+    if (!(mass > 0.0)) w = pj;  // the residual vanished: draw from the target
+  }
+  const double u = c.rng.u((uint32_t)b, (uint32_t)n, kDrawFinal);
+  double tot;
+  const double excl = block_exclusive_scan(w, shd, &tot);
+  const double target = u * tot;
+  if (t == 0) s_sel = 0x7fffffff;
+  __syncthreads();
+  if (w > 0.0 && excl + w > target) atomicMin(&s_sel, t);
+  __syncthreads();
+  if (s_sel == 0x7fffffff) {  // rounding left no crossing: the last positive weight
+    __syncthreads();
+    if (t == 0) s_sel = -1;
+    __syncthreads();
+    if (w > 0.0) atomicMax(&s_sel, t);
+    __syncthreads();
+  }
   if (t == 0) {
-    const double u = c.rng.u((uint32_t)b, (uint32_t)n, kDrawFinal);
-    const FiltRow hp = H[n];
-    const FiltEnt* ep = Ent + n * (int64_t)f.stride;
-    int y;
-    double resid = 0.0;
-    if (n < K) {
-      const FiltRow hq = H[K + 1 + n];
-      const FiltEnt* eq = Ent + (K + 1 + n) * (int64_t)f.stride;
-      auto w = [&](int k) {
-        const double pj = ::exp(ep[k].z - hp.L);
-        const double qj = filt_prob(hq, eq, ep[k].i);
-        return fmax(0.0, pj - qj);
-      };
-      for (int k = 0; k < hp.cnt; ++k) resid += w(k);
-      if (resid > 0.0) y = draw_list(hp.cnt, u, w, ep);
-      else y = draw_list(hp.cnt, u, [&](int k) { return ::exp(ep[k].z - hp.L); }, ep);
-    } else {
-      y = draw_list(hp.cnt, u, [&](int k) { return ::exp(ep[k].z - hp.L); }, ep);
-    }
+    const int y = s_sel >= 0 ? s_ep[s_sel].i : -1;
     for (int i = 0; i <= K; ++i) c.out_tokens[b * (K + 1) + i] = i < n ? s_x[i] : (i == n ? y : -1);
     c.out_len[b] = n;
-    if (c.out_resid) c.out_resid[b] = resid;
+    if (c.out_resid) c.out_resid[b] = mass;
   }
 }
 
@@ -309,49 +497,34 @@ __global__ __launch_bounds__(kWG) void k_filt_draft(LinCfg c, FiltCfg f) {
   const int K = c.K, t = threadIdx.x;
   const FiltRow* H = f.hdr + b * K;
   __shared__ int s_bad;
+  __shared__ int s_x[kMaxK];
   if (t == 0) s_bad = 0;
   __syncthreads();
   for (int i = t; i < K; i += kWG)
     if (H[i].bad || H[i].cnt <= 0) atomicOr(&s_bad, 1);
+  filt_drafts(c, f, b, H, f.ent + b * K * (int64_t)f.stride, K, s_x);
   __syncthreads();
-  for (int i = t; i < K; i += kWG) {
-    int x = -1;
-    if (!s_bad) {
-      const FiltRow hq = H[i];
-      const FiltEnt* eq = f.ent + (b * K + i) * (int64_t)f.stride;
-      const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
-      x = draw_list(hq.cnt, u, [&](int k) { return ::exp(eq[k].z - hq.m); }, eq);
-    }
-    c.draft[b * K + i] = x;
-  }
+  for (int i = t; i < K; i += kWG) c.draft[b * K + i] = s_bad ? -1 : s_x[i];
 }
 
 // ------------------------------------------------------------ launchers --
 template <int DT, bool AL>
-static hipError_t filtered_t(const LinCfg& c, const FiltCfg& f, bool draft_only, hipStream_t s) {
-  const int64_t rows = c.B * (c.rows.np + c.rows.nq);
-  PSI_LAUNCH(s, (k_filter_row<DT, AL>), dim3((unsigned)rows), dim3(kWG), c, f);
-  if (draft_only) PSI_LAUNCH(s, k_filt_draft, dim3((unsigned)c.B), dim3(kWG), c, f);
-  else PSI_LAUNCH(s, k_filt_decide, dim3((unsigned)c.B), dim3(kWG), c, f);
-  return hipGetLastError();
-}
-
-template <int DT, bool AL>
 static hipError_t filter_rows_t(const LinCfg& c, const FiltCfg& f, int64_t rows, hipStream_t s) {
-  PSI_LAUNCH(s, (k_filter_row<DT, AL>), dim3((unsigned)rows), dim3(kWG), c, f);
+  PSI_LAUNCH(s, (k_filt_chunk<DT, AL>), dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
+  PSI_LAUNCH(s, (k_filt_merge<DT, AL>), dim3((unsigned)rows), dim3(kWG), c, f);
   return hipGetLastError();
 }
 
 hipError_t launch_filter_rows(const LinCfg& c, const FiltCfg& f, int64_t rows, int dtype, hipStream_t s) {
-  if (dtype == kBF16)
-    return c.aligned ? filter_rows_t<kBF16, true>(c, f, rows, s) : filter_rows_t<kBF16, false>(c, f, rows, s);
-  return c.aligned ? filter_rows_t<kF32, true>(c, f, rows, s) : filter_rows_t<kF32, false>(c, f, rows, s);
+  return PSI_DISPATCH(filter_rows_t, dtype, c.aligned, c, f, rows, s);
 }
 
 hipError_t launch_filtered(const LinCfg& c, const FiltCfg& f, int dtype, bool draft_only, hipStream_t s) {
-  if (dtype == kBF16)
-    return c.aligned ? filtered_t<kBF16, true>(c, f, draft_only, s) : filtered_t<kBF16, false>(c, f, draft_only, s);
-  return c.aligned ? filtered_t<kF32, true>(c, f, draft_only, s) : filtered_t<kF32, false>(c, f, draft_only, s);
+  const hipError_t e = launch_filter_rows(c, f, c.B * (c.rows.np + c.rows.nq), dtype, s);
+  if (e != hipSuccess) return e;
+  if (draft_only) PSI_LAUNCH(s, k_filt_draft, dim3((unsigned)c.B), dim3(kWG), c, f);
+  else PSI_LAUNCH(s, k_filt_decide, dim3((unsigned)c.B), dim3(kWG), c, f);
+  return hipGetLastError();
 }
 
 }  // namespace psi

@@ -98,13 +98,33 @@ struct FiltEnt {
   int32_t pad;
   double z;  // a / T
 };
+// Top-k candidates of one row chunk (kFiltChunk logits, 64 per thread): tau
+// is a lower bound of the chunk's kk-th largest logit, and the chunk's
+// candidates are all its finite logits >= tau (cnt of them; more than
+// kFiltChunkCap are not stored and the chunk is read again).
+constexpr int kFiltVals = 64;
+constexpr int kFiltChunk = 256 * kFiltVals;
+constexpr int kFiltChunkCap = 128;
+struct FiltChunk {
+  float tau;
+  int32_t cnt;
+  int32_t flags;  // bit 0: NaN or +inf seen; bit 1: a finite logit seen
+  int32_t pad;
+};
+struct FiltCand {
+  float v;
+  int32_t i;
+};
 struct FiltCfg {
-  FiltRow* hdr;  // [rows]
-  FiltEnt* ent;  // [rows][stride]
-  int stride;    // entries per row: min(V, kMaxTopK) >= any admissible top_k
-  int kk;        // top_k in effect
-  double T;      // temperature (binary32 value)
-  double top_p;  // binary32 value
+  FiltRow* hdr;     // [rows]
+  FiltEnt* ent;     // [rows][stride]
+  FiltChunk* chk;   // [rows][nchf]
+  FiltCand* fc;     // [rows][nchf][kFiltChunkCap]
+  int stride;       // entries per row: min(V, kMaxTopK) >= any admissible top_k
+  int nchf;         // chunks per row
+  int kk;           // top_k in effect
+  double T;         // temperature (binary32 value)
+  double top_p;     // binary32 value
 };
 
 // Candidate tree topology, passed by value in the kernel arguments. Row 0 is

@@ -66,6 +66,29 @@ def test_filtered_ties():
         assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
 
 
+def test_filtered_candidate_overflow():
+    """Rows whose top-k candidates overflow: constant rows (every logit ties,
+    so every chunk is read again and the whole row is streamed) and rows with
+    300 copies of their maximum spread over three chunks (the lowest ids win
+    the ties across chunks)."""
+    B, K, V = 8, 3, 40000
+    p, q = synth.pair(B, K + 1, K, V, "f32", seed=13, sd_a=2.0, mode=0, sd_noise=0.5)
+    rng = np.random.default_rng(3)
+    p[0] = 1.5
+    q[0] = 1.5
+    for r in range(K + 1):
+        p[1, r, rng.choice(V, 300, replace=False)] = p[1, r].max() + 1.0
+    for r in range(K):
+        q[1, r, rng.choice(V, 300, replace=False)] = q[1, r].max() + 1.0
+    q[2] = -0.25
+    for step in range(3):
+        g, o = _run(p, q, None, 1.0, 20, 0.53, 5, step, True)
+        assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
+        compare_linear(g, o)
+        assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
+        assert int(g["len"][0]) == K  # identical constant rows always accept
+
+
 def test_top_k_one_matches_greedy():
     """top_k = 1 stochastic verification with fused drafts equals greedy mode."""
     psi = _psi()
