@@ -42,7 +42,7 @@ inline int filt_stride(int32_t V) { return V < kMaxTopK ? V : kMaxTopK; }
 
 // Workspace sections, each 256-byte aligned.
 struct Layout {
-  size_t st, rs, res, dr, fh, fe, fk, fc, rst, ts, tres, total;
+  size_t st, rs, res, dr, fh, fe, fk, fc, ff, rst, ts, tres, total;
 };
 
 inline int nchf_of(int32_t V) { return (V + kFiltChunk - 1) / kFiltChunk; }
@@ -67,6 +67,8 @@ inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
   off = align_up(off + (size_t)B * rows_per_req * nchf_of(V) * sizeof(FiltChunk), 256);
   L.fc = off;
   off = align_up(off + (size_t)B * rows_per_req * nchf_of(V) * kFiltChunkCap * sizeof(FiltCand), 256);
+  L.ff = off;
+  off = align_up(off + ((size_t)B * rows_per_req + 1) * sizeof(int32_t), 256);
   L.rst = off;
   off = align_up(off + (size_t)B * rows_per_req * sizeof(RowStat), 256);
   L.ts = off;
@@ -108,6 +110,8 @@ inline FiltCfg filt_cfg(const psispec_params* prm, void* ws, int64_t B, int32_t 
   f.ent = (FiltEnt*)((char*)ws + L.fe);
   f.chk = (FiltChunk*)((char*)ws + L.fk);
   f.fc = (FiltCand*)((char*)ws + L.fc);
+  f.nfall = (int32_t*)((char*)ws + L.ff);
+  f.fall = f.nfall + 1;
   f.stride = filt_stride(V);
   f.nchf = nchf_of(V);
   f.kk = prm->top_k;

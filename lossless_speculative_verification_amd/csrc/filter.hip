@@ -7,16 +7,20 @@
 //                  registers: a lower bound tau of the chunk's k-th largest
 //                  logit (each wave's ceil(k/4)-th largest per-thread maximum,
 //                  the smallest of the four: at least k logits are >= tau),
-//                  then every finite logit >= tau is a candidate. Every
-//                  logit of the chunk's exact top-k, ties included, is one.
-//   k_filt_merge   one workgroup per row: the row bound is the largest chunk
+//                  then every finite logit >= tau is a candidate (with too
+//                  many, tau is raised by bisection). Every logit of the
+//                  chunk's exact top-k, ties included, is one.
+//   k_filt_mergew  one wave per row: the row bound is the largest chunk
 //                  bound; the candidates >= it (a chunk with too many stored
-//                  none and is read again) are sorted by (logit desc, id asc)
-//                  and the first k kept, exactly as the plain definition
-//                  orders them; then top-p over that order and the
-//                  log-normaliser, in fp64, and the kept set in id order.
-//                  More candidates than LDS holds: the row is streamed again
-//                  with a running exact top-k.
+//                  none and is read again) are cut again by the same bound
+//                  over the candidates, then each survivor's position in
+//                  (logit desc, id asc) order, the plain definition's order,
+//                  is counted and the first k kept; then top-p over that
+//                  order and the log-normaliser, in fp64, and the kept set in
+//                  id order. Rows that do not fit a wave go to
+//   k_filt_fallback  the same merge by a whole workgroup, which reads chunks
+//                  again and, beyond LDS, streams the row with a running
+//                  exact top-k.
 //   k_filt_decide  one workgroup per request: fused draft draws (one wave per
 //                  row), p(x)/q(x), accept tests, first rejection, residual or
 //                  bonus draw over the kept set staged in LDS, outputs.
@@ -95,6 +99,15 @@ __device__ int block_scan_int(int v, int* sh, int* total) {
   return before_ + incl - v;
 }
 
+// Unsigned keys in the order of the float values (-0 before +0) and back.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // Sorts one value per lane across the wave, largest at lane 0 (bitonic).
 __device__ __forceinline__ float wave_sort_desc(float v) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -108,6 +121,20 @@ __device__ __forceinline__ float wave_sort_desc(float v) {
     }
   }
   return v;
+}
+
+// Appends one entry for every lane of the (converged) wave whose pred is set:
+// one LDS atomic per wave. Returns this lane's slot (meaningful where pred).
+__device__ __forceinline__ int wave_append(bool pred, int* counter) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const unsigned long long m = __ballot(pred);
+  int base = 0;
+  if (m) {
+    const int leader = __ffsll((long long)m) - 1;
+    if (lane == leader) base = atomicAdd(counter, __popcll(m));
+    base = __shfl(base, leader);
+  }
+  return base + __popcll(m & ((1ull << lane) - 1ull));
 }
 
 // Running exact top-k of a whole row streamed in token order: an element
@@ -163,7 +190,7 @@ __device__ int stream_topk(const LinCfg& c, const char* row, int kk, FiltCand* c
 
 // ------------------------------------------------------- chunk candidates --
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_filt_chunk(LinCfg c, FiltCfg f) {
+__device__ __forceinline__ void filt_chunk(const LinCfg& c, const FiltCfg& f) {
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec, NV = kFiltVals / EPV;
   const int64_t item = blockIdx.x;
@@ -204,7 +231,38 @@ __global__ __launch_bounds__(kWG) void k_filt_chunk(LinCfg c, FiltCfg f) {
 #pragma unroll
     for (int e = 0; e < EPV; ++e) n += (x[k][e] >= tau && x[k][e] > -INFINITY) ? 1 : 0;
   int total;
-  const int off = block_scan_int(n, s_sc, &total);
+  int off = block_scan_int(n, s_sc, &total);
+  if (total > kFiltChunkCap && !bad && 2 * f.kk <= kFiltChunkCap) {
+    // Too many candidates: raise tau by bisection over the order of the
+    // logits while at least kk logits stay >= it, until at most
+    // kFiltChunkCap do (many equal logits can keep the count above it).
+    __shared__ float shm[kWaves];
+    uint32_t lo = order_key(tau), hi = order_key(block_max(mx, shm)) + 1u;
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      const float fm = from_order_key(mid);
+      int cm = 0;
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) cm += (x[k][e] >= fm && x[k][e] > -INFINITY) ? 1 : 0;
+      int all;
+      block_scan_int(cm, s_sc, &all);
+      if (all >= f.kk) {
+        lo = mid;
+        if (all <= kFiltChunkCap) break;
+      } else {
+        hi = mid;
+      }
+    }
+    tau = from_order_key(lo);
+    n = 0;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) n += (x[k][e] >= tau && x[k][e] > -INFINITY) ? 1 : 0;
+    off = block_scan_int(n, s_sc, &total);
+  }
   if (total <= kFiltChunkCap) {
     FiltCand* out = f.fc + item * kFiltChunkCap + off;
     int w = 0;
@@ -215,17 +273,31 @@ __global__ __launch_bounds__(kWG) void k_filt_chunk(LinCfg c, FiltCfg f) {
         if (x[k][e] >= tau && x[k][e] > -INFINITY) out[w++] = FiltCand{x[k][e], (int32_t)((v0 + (int64_t)k * kWG) * EPV + e)};
   }
   if (t == 0) f.chk[item] = FiltChunk{tau, total, (bad ? 1 : 0) | (any ? 2 : 0), 0};
+  if (item == 0 && t == 0) *f.nfall = 0;
 }
 
-// -------------------------------------------------------------- row merge --
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_filt_merge(LinCfg c, FiltCfg f) {
+__global__ __launch_bounds__(kWG) void k_filt_chunk(LinCfg c, FiltCfg f) {
+  filt_chunk<DT, AL>(c, f);
+}
+// Aligned fp32 rows: held to 96 registers (five waves per SIMD), which it
+// meets without spilling.
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(5))) void k_filt_chunk_f32(LinCfg c, FiltCfg f) {
+  filt_chunk<kF32, true>(c, f);
+}
+
+// ------------------------------------------------- row merge, workgroup --
+// The merge of one row by a whole workgroup: any number of chunks read again,
+// up to kSortCap candidates in LDS, else the row streamed again.
+template <int DT, bool AL>
+__device__ void merge_row_wg(const LinCfg& c, const FiltCfg& f, int64_t sr) {
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec, NV = kFiltVals / EPV;
-  const int64_t sr = blockIdx.x;
-  const int t = threadIdx.x;
+  constexpr int PER = kSortCap / kWG;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int kk = f.kk;
   __shared__ FiltCand cand[kSortCap];
+  __shared__ FiltCand kept[kMaxTopK];
   __shared__ int s_cnt, s_novf, s_first;
   __shared__ float s_tau;
   __shared__ int s_ovf[kMaxOvf];
@@ -250,26 +322,31 @@ __global__ __launch_bounds__(kWG) void k_filt_merge(LinCfg c, FiltCfg f) {
   const int any = __syncthreads_or(fl & 2);
   if (bad || !any) {
     if (t == 0) *hdr = FiltRow{0, 1, -INFINITY, -INFINITY};
+    __syncthreads();
     return;
   }
   // gather every stored candidate >= tau; note the chunks that stored none
-  auto push = [&](float v, int32_t i) {
-    const int slot = atomicAdd(&s_cnt, 1);
-    if (slot < kSortCap) cand[slot] = FiltCand{v, i};
-  };
   const FiltCand* src = f.fc + sr * f.nchf * (int64_t)kFiltChunkCap;
-  for (int s = t; s < f.nchf * kFiltChunkCap; s += kWG) {
-    const int ch = s / kFiltChunkCap, i = s - ch * kFiltChunkCap;
-    const int n = rec[ch].cnt;
-    if (n <= kFiltChunkCap) {
-      if (i < n) {
-        const FiltCand e = src[s];
-        if (e.v >= tau) push(e.v, e.i);
+  const int nslot = f.nchf * kFiltChunkCap;
+  for (int s0 = 0; s0 < nslot; s0 += kWG) {
+    const int s = s0 + t;
+    FiltCand e = {-INFINITY, 0};
+    bool take = false;
+    if (s < nslot) {
+      const int ch = s / kFiltChunkCap, i = s - ch * kFiltChunkCap;
+      const int n = rec[ch].cnt;
+      if (n <= kFiltChunkCap) {
+        if (i < n) {
+          e = src[s];
+          take = e.v >= tau;
+        }
+      } else if (i == 0) {
+        const int k = atomicAdd(&s_novf, 1);
+        if (k < kMaxOvf) s_ovf[k] = ch;
       }
-    } else if (i == 0) {
-      const int k = atomicAdd(&s_novf, 1);
-      if (k < kMaxOvf) s_ovf[k] = ch;
     }
+    const int slot = wave_append(take, &s_cnt);
+    if (take && slot < kSortCap) cand[slot] = e;
   }
   __syncthreads();
   const int novf = s_novf;
@@ -283,36 +360,83 @@ __global__ __launch_bounds__(kWG) void k_filt_merge(LinCfg c, FiltCfg f) {
 #pragma unroll
       for (int q = 0; q < NV; ++q)
 #pragma unroll
-        for (int e = 0; e < EPV; ++e)
-          if (x[q][e] >= tau && x[q][e] > -INFINITY) push(x[q][e], (int32_t)((v0 + (int64_t)q * kWG) * EPV + e));
+        for (int e = 0; e < EPV; ++e) {
+          const bool take = x[q][e] >= tau && x[q][e] > -INFINITY;
+          const int slot = wave_append(take, &s_cnt);
+          if (take && slot < kSortCap) cand[slot] = FiltCand{x[q][e], (int32_t)((v0 + (int64_t)q * kWG) * EPV + e)};
+        }
     }
   }
   __syncthreads();
   const int total = s_cnt;
   __syncthreads();
   int cnt;
-  if (novf > kMaxOvf || total > kSortCap) cnt = stream_topk<DT, AL>(c, row, kk, cand, &s_cnt, &s_tau);
-  else cnt = sort_keep(cand, total, kk);
-  // ---- fp64 filter over cand[0 .. cnt), ordered by (logit desc, id asc),
+  if (novf > kMaxOvf || total > kSortCap) {
+    cnt = stream_topk<DT, AL>(c, row, kk, cand, &s_cnt, &s_tau);
+    if (t < cnt) kept[t] = cand[t];
+  } else {
+    // Second bound over the candidates (same argument as in the chunks): at
+    // least kk candidates are >= tau2.
+    FiltCand mine[PER];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int i = t + r * kWG;
+      mine[r] = i < total ? cand[i] : FiltCand{-INFINITY, 0x7fffffff};
+      tmax = fmaxf(tmax, mine[r].v);
+    }
+    const int kq = (kk + kWaves - 1) / kWaves;
+    const float wq = __shfl(wave_sort_desc(tmax), kq - 1);
+    if (lane == 0) shf[wave] = wq;
+    if (t == 0) s_cnt = 0;
+    __syncthreads();
+    float tau2 = shf[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) tau2 = fminf(tau2, shf[i]);
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const bool take = mine[r].v >= tau2 && mine[r].v > -INFINITY;
+      const int slot = wave_append(take, &s_cnt);
+      if (take) cand[slot] = mine[r];
+    }
+    __syncthreads();
+    const int n2 = s_cnt;
+    __syncthreads();
+    if (n2 <= 4 * kWG) {
+      // exact position of each survivor in (logit desc, id asc) order
+      for (int i = t; i < n2; i += kWG) {
+        const FiltCand me = cand[i];
+        int rank = 0;
+        for (int j = 0; j < n2; ++j) rank += before(cand[j], me) ? 1 : 0;
+        if (rank < kk) kept[rank] = me;
+      }
+      cnt = n2 < kk ? n2 : kk;
+    } else {
+      cnt = sort_keep(cand, n2, kk);
+      if (t < cnt) kept[t] = cand[t];
+    }
+  }
+  __syncthreads();
+  // ---- fp64 filter over kept[0 .. cnt), ordered by (logit desc, id asc),
   // which is the order of probability desc / id asc since z = a / T is
   // increasing in a. One entry per thread (cnt <= kMaxTopK = kWG).
   const double T = f.T;
-  const double m = (double)cand[0].v / T;
-  const bool mine = t < cnt;
+  const double m = (double)kept[0].v / T;
+  const bool own = t < cnt;
   double z = 0.0, e = 0.0;
-  if (mine) {
-    z = (double)cand[t].v / T;
+  if (own) {
+    z = (double)kept[t].v / T;
     e = ::exp(z - m);
   }
   int keep = cnt;
   if (f.top_p < 1.0) {
     const double S = block_sum(e, shd);
-    const double p = mine ? e / S : 0.0;
+    const double p = own ? e / S : 0.0;
     double tot;
     const double incl = block_exclusive_scan(p, shd, &tot) + p;
     if (t == 0) s_first = 0x7fffffff;
     __syncthreads();
-    if (mine && incl >= f.top_p) atomicMin(&s_first, t);
+    if (own && incl >= f.top_p) atomicMin(&s_first, t);
     __syncthreads();
     if (s_first < cnt) keep = s_first + 1;
   }
@@ -320,12 +444,297 @@ __global__ __launch_bounds__(kWG) void k_filt_merge(LinCfg c, FiltCfg f) {
   if (t == 0) *hdr = FiltRow{keep, 0, m, m + ::log(S)};
   if (t < keep) {
     // position in token-id order
-    const int id = cand[t].i;
+    const int id = kept[t].i;
     int rank = 0;
-    for (int s = 0; s < keep; ++s) rank += cand[s].i < id ? 1 : 0;
+    for (int s = 0; s < keep; ++s) rank += kept[s].i < id ? 1 : 0;
     FiltEnt* out = f.ent + sr * (int64_t)f.stride;
     out[rank] = FiltEnt{id, 0, z};
   }
+  __syncthreads();
+}
+
+// ------------------------------------------------------ row merge, wave --
+namespace {
+
+constexpr int kWCap = 512;    // candidates one wave merges in LDS
+constexpr int kFastCh = 12;   // chunks per row whose candidates a wave holds in registers
+constexpr int kFallWgs = 64;  // workgroups of the fallback merge
+
+// The four largest values seen (a multiset, largest first).
+struct Top4 {
+  float t0 = -INFINITY, t1 = -INFINITY, t2 = -INFINITY, t3 = -INFINITY;
+  __device__ __forceinline__ void add(float v) {
+    if (!(v > t3)) return;
+    if (v > t0) {
+      t3 = t2; t2 = t1; t1 = t0; t0 = v;
+    } else if (v > t1) {
+      t3 = t2; t2 = t1; t1 = v;
+    } else if (v > t2) {
+      t3 = t2; t2 = v;
+    } else {
+      t3 = v;
+    }
+  }
+  // the j-th largest, 1 <= j <= 4
+  __device__ __forceinline__ float nth(int j) const { return j == 1 ? t0 : j == 2 ? t1 : j == 3 ? t2 : t3; }
+};
+
+// Orders the LDS accesses of one wave around this point (the wave's LDS
+// operations complete in issue order; this keeps the compiler from moving
+// them across it).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Sorts 128 entries held two per lane (entry 2l + r is lane l's e[r]) so
+// that first(e_i, e_j) for every i < j (bitonic network; entries that are
+// mutually not first may end in either order).
+template <class First>
+__device__ __forceinline__ void wave_sort2(FiltCand (&e)[2], First first) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int k = 2; k <= 2 * kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j == 1) {
+        const bool up = ((2 * lane) & k) == 0;
+        if (up ? first(e[1], e[0]) : first(e[0], e[1])) {
+          const FiltCand x = e[0];
+          e[0] = e[1];
+          e[1] = x;
+        }
+      } else {
+        const int lj = j >> 1;
+        const bool lower = (lane & lj) == 0;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const FiltCand o = {__shfl_xor(e[r].v, lj), __shfl_xor(e[r].i, lj)};
+          const bool up = ((2 * lane + r) & k) == 0;
+          const FiltCand lo = lower ? e[r] : o, hi = lower ? o : e[r];
+          const bool swap = up ? first(hi, lo) : first(lo, hi);
+          if (swap) e[r] = o;
+        }
+      }
+    }
+  }
+}
+
+// fp64 top-p and log-normaliser over the kept entries held two per lane
+// (position 2l + r in lane l's e[r], cnt of them, sorted by logit desc, id
+// asc); writes the row header and the kept set in token-id order.
+__device__ void finish_row_wave2(const FiltCfg& f, int64_t sr, FiltCand (&e)[2], int cnt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const double T = f.T;
+  const double m = (double)__shfl(e[0].v, 0) / T;
+  double ez[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) ez[r] = 2 * lane + r < cnt ? ::exp((double)e[r].v / T - m) : 0.0;
+  int keep = cnt;
+  if (f.top_p < 1.0) {
+    const double S = wave_sum(ez[0] + ez[1]);
+    const double p0 = ez[0] / S, p1 = ez[1] / S;
+    const double c0 = wave_incl_scan(p0 + p1) - (p0 + p1) + p0, c1 = c0 + p1;
+    int first = -1;
+    if (2 * lane < cnt && c0 >= f.top_p) first = 2 * lane;
+    else if (2 * lane + 1 < cnt && c1 >= f.top_p) first = 2 * lane + 1;
+    const unsigned long long hit = __ballot(first >= 0);
+    if (hit) keep = __shfl(first, __ffsll((long long)hit) - 1) + 1;
+  }
+  const double S = wave_sum((2 * lane < keep ? ez[0] : 0.0) + (2 * lane + 1 < keep ? ez[1] : 0.0));
+  if (lane == 0) f.hdr[sr] = FiltRow{keep, 0, m, m + ::log(S)};
+  // the kept set in token-id order
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (2 * lane + r >= keep) e[r] = FiltCand{-INFINITY, 0x7fffffff};
+  wave_sort2(e, [](const FiltCand& a, const FiltCand& b) { return a.i < b.i; });
+  FiltEnt* out = f.ent + sr * (int64_t)f.stride;
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (2 * lane + r < keep) out[2 * lane + r] = FiltEnt{e[r].i, 0, (double)e[r].v / T};
+}
+
+// fp64 top-p and log-normaliser over kept[0 .. cnt) (sorted by logit desc,
+// id asc) by one wave, lane l owning kept[4l .. 4l+3]; writes the row header
+// and the kept set in token-id order.
+__device__ void finish_row_wave(const FiltCfg& f, int64_t sr, const FiltCand* kept, int cnt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const double T = f.T;
+  const double m = (double)kept[0].v / T;
+  double z[4], e[4], loc = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = lane * 4 + q;
+    z[q] = j < cnt ? (double)kept[j].v / T : 0.0;
+    e[q] = j < cnt ? ::exp(z[q] - m) : 0.0;
+    loc += e[q];
+  }
+  int keep = cnt;
+  if (f.top_p < 1.0) {
+    const double S = wave_sum(loc);
+    double p[4], lp = 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      p[q] = e[q] / S;
+      lp += p[q];
+    }
+    double acc = wave_incl_scan(lp) - lp;
+    int first = -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc += p[q];
+      const int j = lane * 4 + q;
+      if (first < 0 && j < cnt && acc >= f.top_p) first = j;
+    }
+    const unsigned long long hit = __ballot(first >= 0);
+    if (hit) keep = __shfl(first, __ffsll((long long)hit) - 1) + 1;
+  }
+  double ls = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ls += lane * 4 + q < keep ? e[q] : 0.0;
+  const double S = wave_sum(ls);
+  if (lane == 0) f.hdr[sr] = FiltRow{keep, 0, m, m + ::log(S)};
+  FiltEnt* out = f.ent + sr * (int64_t)f.stride;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = lane * 4 + q;
+    if (j < keep) {
+      const int id = kept[j].i;
+      int rank = 0;
+      for (int s = 0; s < keep; ++s) rank += kept[s].i < id ? 1 : 0;
+      out[rank] = FiltEnt{id, 0, z[q]};
+    }
+  }
+}
+
+}  // namespace
+
+// One wave per row: the row bound and validity from the chunk records, a
+// second bound from the stored candidates >= it, the candidates >= both
+// gathered into the wave's LDS buffer, exact positions by counting, then the
+// fp64 finish.
+// Rows with a chunk whose candidates overflowed its store, more than kWCap
+// candidates >= both bounds, or more than 64 chunks are listed for the
+// workgroup merge.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_filt_mergew(LinCfg c, FiltCfg f, int64_t rows) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int64_t sr = blockIdx.x * (int64_t)kWaves + wave;
+  if (sr >= rows) return;  // the whole wave; no workgroup barrier below
+  __shared__ FiltCand s_cand[kWaves][kWCap];
+  __shared__ FiltCand s_kept[kWaves][kMaxTopK];
+  FiltCand* cand = s_cand[wave];
+  FiltCand* kept = s_kept[wave];
+  const FiltChunk* rec = f.chk + sr * f.nchf;
+  const int kk = f.kk;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  float tl = -INFINITY;
+  int fl = 0, mycnt = 0;
+  for (int ch = lane; ch < f.nchf; ch += kWave) {
+    const FiltChunk r = rec[ch];
+    tl = fmaxf(tl, r.tau);
+    fl |= r.flags;
+    mycnt = r.cnt;
+  }
+  const float tau = wave_max(tl);
+  fl = wave_or(fl);
+  if ((fl & 1) || !(fl & 2)) {
+    if (lane == 0) f.hdr[sr] = FiltRow{0, 1, -INFINITY, -INFINITY};
+    return;
+  }
+  bool fall = f.nchf > kWave || __ballot(mycnt > kFiltChunkCap) != 0;
+  // Pass 1 over the stored candidates >= tau: each lane keeps its jj largest
+  // (jj = ceil(kk / 64) <= 4); ceil(kk / jj) lanes then hold jj candidates
+  // each >= tau2, the ceil(kk / jj)-th largest of the lanes' jj-th values.
+  const int jj = (kk + kWave - 1) / kWave, ll = (kk + jj - 1) / jj;
+  float tau2 = tau;
+  int n2 = 0;
+  if (!fall && f.nchf <= kFastCh) {
+    // every stored candidate loaded at once: lane l holds slots l and l + 64
+    // of each chunk
+    FiltCand buf[2 * kFastCh];
+    const FiltCand* src = f.fc + sr * f.nchf * (int64_t)kFiltChunkCap;
+#pragma unroll
+    for (int r = 0; r < 2 * kFastCh; ++r) {
+      const int ch = r >> 1, i = (r & 1) * kWave + lane;
+      const int cc = ch < f.nchf ? __shfl(mycnt, ch) : 0;
+      buf[r] = i < cc ? src[ch * kFiltChunkCap + i] : FiltCand{-INFINITY, 0x7fffffff};
+    }
+    Top4 top;
+#pragma unroll
+    for (int r = 0; r < 2 * kFastCh; ++r) {
+      const float v = buf[r].v;
+      if (v >= tau) top.add(v);
+    }
+    tau2 = fmaxf(tau, __shfl(wave_sort_desc(top.nth(jj)), ll - 1));
+#pragma unroll
+    for (int r = 0; r < 2 * kFastCh; ++r) {
+      const bool take = buf[r].v >= tau2 && buf[r].v > -INFINITY;
+      const unsigned long long m = __ballot(take);
+      const int slot = n2 + __popcll(m & lt);
+      if (take && slot < kWCap) cand[slot] = buf[r];
+      n2 += __popcll(m);
+    }
+    fall = n2 > kWCap;
+  } else if (!fall) {
+    Top4 top;
+    for (int ch = 0; ch < f.nchf; ++ch) {
+      const int cc = __shfl(mycnt, ch);
+      const FiltCand* src = f.fc + (sr * f.nchf + ch) * kFiltChunkCap;
+      for (int i = lane; i < cc; i += kWave) {
+        const float v = src[i].v;
+        if (v >= tau) top.add(v);
+      }
+    }
+    tau2 = fmaxf(tau, __shfl(wave_sort_desc(top.nth(jj)), ll - 1));
+    // Pass 2: gather the candidates >= tau2.
+    for (int ch = 0; ch < f.nchf; ++ch) {
+      const int cc = __shfl(mycnt, ch);
+      const FiltCand* src = f.fc + (sr * f.nchf + ch) * kFiltChunkCap;
+      for (int i0 = 0; i0 < cc; i0 += kWave) {
+        const int i = i0 + lane;
+        FiltCand e = {-INFINITY, 0};
+        if (i < cc) e = src[i];
+        const bool take = i < cc && e.v >= tau2;
+        const unsigned long long m = __ballot(take);
+        const int slot = n2 + __popcll(m & lt);
+        if (take && slot < kWCap) cand[slot] = e;
+        n2 += __popcll(m);
+      }
+    }
+    fall = n2 > kWCap;
+  }
+  if (fall) {
+    if (lane == 0) f.fall[atomicAdd(f.nfall, 1)] = (int32_t)sr;
+    return;
+  }
+  wave_sync();
+  if (n2 <= 2 * kWave) {
+    // up to 128 survivors: sorted in registers
+    FiltCand e[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) e[r] = 2 * lane + r < n2 ? cand[2 * lane + r] : FiltCand{-INFINITY, 0x7fffffff};
+    wave_sort2(e, [](const FiltCand& a, const FiltCand& b) { return before(a, b); });
+    finish_row_wave2(f, sr, e, n2 < kk ? n2 : kk);
+    return;
+  }
+  // exact position of each survivor in (logit desc, id asc) order
+  for (int i = lane; i < n2; i += kWave) {
+    const FiltCand me = cand[i];
+    int rank = 0;
+    for (int j = 0; j < n2; ++j) rank += before(cand[j], me) ? 1 : 0;
+    if (rank < kk) kept[rank] = me;
+  }
+  wave_sync();
+  finish_row_wave(f, sr, kept, n2 < kk ? n2 : kk);
+}
+
+// The listed rows, one workgroup each.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_filt_fallback(LinCfg c, FiltCfg f) {
+  const int n = *f.nfall;
+  for (int i = blockIdx.x; i < n; i += gridDim.x) merge_row_wg<DT, AL>(c, f, f.fall[i]);
 }
 
 // --------------------------------------------------- per-request decision --
@@ -510,8 +919,10 @@ __global__ __launch_bounds__(kWG) void k_filt_draft(LinCfg c, FiltCfg f) {
 // ------------------------------------------------------------ launchers --
 template <int DT, bool AL>
 static hipError_t filter_rows_t(const LinCfg& c, const FiltCfg& f, int64_t rows, hipStream_t s) {
-  PSI_LAUNCH(s, (k_filt_chunk<DT, AL>), dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
-  PSI_LAUNCH(s, (k_filt_merge<DT, AL>), dim3((unsigned)rows), dim3(kWG), c, f);
+  if constexpr (DT == kF32 && AL) PSI_LAUNCH(s, k_filt_chunk_f32, dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
+  else PSI_LAUNCH(s, (k_filt_chunk<DT, AL>), dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
+  PSI_LAUNCH(s, (k_filt_mergew<DT, AL>), dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(kWG), c, f, rows);
+  PSI_LAUNCH(s, (k_filt_fallback<DT, AL>), dim3((unsigned)kFallWgs), dim3(kWG), c, f);
   return hipGetLastError();
 }
 

@@ -120,6 +120,8 @@ struct FiltCfg {
   FiltEnt* ent;     // [rows][stride]
   FiltChunk* chk;   // [rows][nchf]
   FiltCand* fc;     // [rows][nchf][kFiltChunkCap]
+  int32_t* nfall;   // rows left to the workgroup merge, then their indices
+  int32_t* fall;    // [rows]
   int stride;       // entries per row: min(V, kMaxTopK) >= any admissible top_k
   int nchf;         // chunks per row
   int kk;           // top_k in effect

@@ -89,6 +89,27 @@ def test_filtered_candidate_overflow():
         assert int(g["len"][0]) == K  # identical constant rows always accept
 
 
+def test_filtered_chunk_bound_raised():
+    """Chunks whose large logits sit in a few threads' elements: the first
+    bound admits hundreds of candidates and is raised by bisection (distinct
+    values) or leaves the chunk to be read again (tied values)."""
+    B, K, V = 4, 2, 40000
+    p, q = synth.pair(B, K + 1, K, V, "f32", seed=17, sd_a=2.0, mode=0, sd_noise=0.5)
+    # fp32 chunk of 16384 logits: thread t holds vectors t + 256 k (k < 16) of
+    # 4 logits, i.e. logits (t + 256 k) * 4 + e
+    idx = np.array([(t + 256 * k) * 4 + e for t in range(13) for k in range(16) for e in range(4)])
+    for b in range(B):
+        for r in range(K + 1):
+            for ch in (0, 1):
+                vals = 9.0 + 0.001 * np.arange(idx.size) if (b + r) % 2 == 0 else np.full(idx.size, 9.5)
+                p[b, r, ch * 16384 + idx] = vals.astype(np.float32)
+    for step in range(3):
+        g, o = _run(p, q, None, 1.0, 50, 0.9, 8, step, True)
+        assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
+        compare_linear(g, o)
+        assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
+
+
 def test_top_k_one_matches_greedy():
     """top_k = 1 stochastic verification with fused drafts equals greedy mode."""
     psi = _psi()
