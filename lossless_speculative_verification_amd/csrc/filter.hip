@@ -39,6 +39,11 @@ __device__ __forceinline__ bool before(const FiltCand& a, const FiltCand& b) {
   return a.v > b.v || (a.v == b.v && a.i < b.i);
 }
 
+// Branch-free form of before() for counting loops.
+__device__ __forceinline__ int before_i(const FiltCand& a, const FiltCand& b) {
+  return (int)(a.v > b.v) | ((int)(a.v == b.v) & (int)(a.i < b.i));
+}
+
 // In-LDS bitonic sort of n (power of two, <= kSortCap) entries in "before" order.
 __device__ void bitonic_sort(FiltCand* a, int n) {
   for (int k = 2; k <= n; k <<= 1) {
@@ -108,19 +113,27 @@ __device__ __forceinline__ float from_order_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Sorts one value per lane across the wave, largest at lane 0 (bitonic).
-__device__ __forceinline__ float wave_sort_desc(float v) {
-  const int lane = threadIdx.x & (kWave - 1);
+// The k-th largest of the R * 64 values a wave holds (R per lane; 1 <= k;
+// not NaN; -inf allowed): bisection over the order keys of the floats, each
+// step counting with ballots. If fewer than k values are finite, -inf.
+template <int R>
+__device__ __forceinline__ float wave_kth_largest(const float (&x)[R], int k) {
+  uint32_t lo = 0x007fffffu;  // key of -inf: every value is >= it
+  uint32_t hi = 0xff800001u;  // one past the key of +inf: no value is >= it
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    const float t = from_order_key(mid);
+    int n = 0;
 #pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float o = __shfl_xor(v, j);
-      const bool lower = (lane & j) == 0, desc = (lane & k) == 0;
-      v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
-    }
+    for (int r = 0; r < R; ++r) n += __popcll(__ballot(x[r] >= t));
+    if (n >= k) lo = mid;
+    else hi = mid;
   }
-  return v;
+  return from_order_key(lo);
+}
+__device__ __forceinline__ float wave_kth_largest(float x, int k) {
+  const float v[1] = {x};
+  return wave_kth_largest<1>(v, k);
 }
 
 // Appends one entry for every lane of the (converged) wave whose pred is set:
@@ -218,7 +231,7 @@ __device__ __forceinline__ void filt_chunk(const LinCfg& c, const FiltCfg& f) {
   __shared__ float s_w[kWaves];
   __shared__ int s_sc[kWaves];
   const int kq = (f.kk + kWaves - 1) / kWaves;
-  const float wq = __shfl(wave_sort_desc(mx), kq - 1);
+  const float wq = wave_kth_largest(mx, kq);
   if (lane == 0) s_w[wave] = wq;
   bad = __syncthreads_or(bad);
   any = __syncthreads_or(any);
@@ -386,7 +399,7 @@ __device__ void merge_row_wg(const LinCfg& c, const FiltCfg& f, int64_t sr) {
       tmax = fmaxf(tmax, mine[r].v);
     }
     const int kq = (kk + kWaves - 1) / kWaves;
-    const float wq = __shfl(wave_sort_desc(tmax), kq - 1);
+    const float wq = wave_kth_largest(tmax, kq);
     if (lane == 0) shf[wave] = wq;
     if (t == 0) s_cnt = 0;
     __syncthreads();
@@ -463,17 +476,15 @@ constexpr int kFallWgs = 64;  // workgroups of the fallback merge
 // The four largest values seen (a multiset, largest first).
 struct Top4 {
   float t0 = -INFINITY, t1 = -INFINITY, t2 = -INFINITY, t3 = -INFINITY;
+  // inserts v and drops the smallest (a min/max network, no branches)
   __device__ __forceinline__ void add(float v) {
-    if (!(v > t3)) return;
-    if (v > t0) {
-      t3 = t2; t2 = t1; t1 = t0; t0 = v;
-    } else if (v > t1) {
-      t3 = t2; t2 = t1; t1 = v;
-    } else if (v > t2) {
-      t3 = t2; t2 = v;
-    } else {
-      t3 = v;
-    }
+    const float v1 = fminf(t0, v);
+    t0 = fmaxf(t0, v);
+    const float v2 = fminf(t1, v1);
+    t1 = fmaxf(t1, v1);
+    const float v3 = fminf(t2, v2);
+    t2 = fmaxf(t2, v2);
+    t3 = fmaxf(t3, v3);
   }
   // the j-th largest, 1 <= j <= 4
   __device__ __forceinline__ float nth(int j) const { return j == 1 ? t0 : j == 2 ? t1 : j == 3 ? t2 : t3; }
@@ -488,77 +499,55 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Sorts 128 entries held two per lane (entry 2l + r is lane l's e[r]) so
-// that first(e_i, e_j) for every i < j (bitonic network; entries that are
-// mutually not first may end in either order).
-template <class First>
-__device__ __forceinline__ void wave_sort2(FiltCand (&e)[2], First first) {
+// The top kk of cand[0 .. n) (n > kk, n <= R * 64) under (logit desc, id
+// asc), written unordered to out[0 .. kk): ts = the kk-th largest logit;
+// every entry above ts, then the entries equal to ts in id order.
+template <int R>
+__device__ void select_topk(const FiltCand* cand, int n, int kk, FiltCand* out) {
   const int lane = threadIdx.x & (kWave - 1);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  FiltCand e[R];
+  float v[R];
 #pragma unroll
-  for (int k = 2; k <= 2 * kWave; k <<= 1) {
+  for (int r = 0; r < R; ++r) {
+    const int i = lane + r * kWave;
+    e[r] = i < n ? cand[i] : FiltCand{-INFINITY, 0x7fffffff};
+    v[r] = e[r].v;
+  }
+  const float ts = wave_kth_largest<R>(v, kk);
+  int above = 0;
 #pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j == 1) {
-        const bool up = ((2 * lane) & k) == 0;
-        if (up ? first(e[1], e[0]) : first(e[0], e[1])) {
-          const FiltCand x = e[0];
-          e[0] = e[1];
-          e[1] = x;
-        }
-      } else {
-        const int lj = j >> 1;
-        const bool lower = (lane & lj) == 0;
+  for (int r = 0; r < R; ++r) above += __popcll(__ballot(e[r].v > ts));
+  const int need = kk - above;  // >= 1 entries equal to ts
+  // rank of each entry equal to ts among those, by id
+  int trank[R];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const FiltCand o = {__shfl_xor(e[r].v, lj), __shfl_xor(e[r].i, lj)};
-          const bool up = ((2 * lane + r) & k) == 0;
-          const FiltCand lo = lower ? e[r] : o, hi = lower ? o : e[r];
-          const bool swap = up ? first(hi, lo) : first(lo, hi);
-          if (swap) e[r] = o;
-        }
-      }
+  for (int r = 0; r < R; ++r) trank[r] = 0;
+#pragma unroll
+  for (int r2 = 0; r2 < R; ++r2) {
+    unsigned long long m = __ballot(e[r2].v == ts);
+    while (m) {
+      const int src = __ffsll((long long)m) - 1;
+      m &= m - 1ull;
+      const int oid = __builtin_amdgcn_readlane(e[r2].i, src);
+#pragma unroll
+      for (int r = 0; r < R; ++r) trank[r] += (e[r].v == ts && oid < e[r].i) ? 1 : 0;
     }
   }
-}
-
-// fp64 top-p and log-normaliser over the kept entries held two per lane
-// (position 2l + r in lane l's e[r], cnt of them, sorted by logit desc, id
-// asc); writes the row header and the kept set in token-id order.
-__device__ void finish_row_wave2(const FiltCfg& f, int64_t sr, FiltCand (&e)[2], int cnt) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const double T = f.T;
-  const double m = (double)__shfl(e[0].v, 0) / T;
-  double ez[2];
+  int w = 0;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) ez[r] = 2 * lane + r < cnt ? ::exp((double)e[r].v / T - m) : 0.0;
-  int keep = cnt;
-  if (f.top_p < 1.0) {
-    const double S = wave_sum(ez[0] + ez[1]);
-    const double p0 = ez[0] / S, p1 = ez[1] / S;
-    const double c0 = wave_incl_scan(p0 + p1) - (p0 + p1) + p0, c1 = c0 + p1;
-    int first = -1;
-    if (2 * lane < cnt && c0 >= f.top_p) first = 2 * lane;
-    else if (2 * lane + 1 < cnt && c1 >= f.top_p) first = 2 * lane + 1;
-    const unsigned long long hit = __ballot(first >= 0);
-    if (hit) keep = __shfl(first, __ffsll((long long)hit) - 1) + 1;
+  for (int r = 0; r < R; ++r) {
+    const bool take = e[r].v > ts || (e[r].v == ts && trank[r] < need);
+    const unsigned long long m = __ballot(take);
+    if (take) out[w + __popcll(m & lt)] = e[r];
+    w += __popcll(m);
   }
-  const double S = wave_sum((2 * lane < keep ? ez[0] : 0.0) + (2 * lane + 1 < keep ? ez[1] : 0.0));
-  if (lane == 0) f.hdr[sr] = FiltRow{keep, 0, m, m + ::log(S)};
-  // the kept set in token-id order
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-    if (2 * lane + r >= keep) e[r] = FiltCand{-INFINITY, 0x7fffffff};
-  wave_sort2(e, [](const FiltCand& a, const FiltCand& b) { return a.i < b.i; });
-  FiltEnt* out = f.ent + sr * (int64_t)f.stride;
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-    if (2 * lane + r < keep) out[2 * lane + r] = FiltEnt{e[r].i, 0, (double)e[r].v / T};
 }
 
 // fp64 top-p and log-normaliser over kept[0 .. cnt) (sorted by logit desc,
 // id asc) by one wave, lane l owning kept[4l .. 4l+3]; writes the row header
 // and the kept set in token-id order.
-__device__ void finish_row_wave(const FiltCfg& f, int64_t sr, const FiltCand* kept, int cnt) {
+__device__ void finish_row_wave(const FiltCfg& f, int64_t sr, FiltCand* kept, int cnt) {
   const int lane = threadIdx.x & (kWave - 1);
   const double T = f.T;
   const double m = (double)kept[0].v / T;
@@ -595,25 +584,35 @@ __device__ void finish_row_wave(const FiltCfg& f, int64_t sr, const FiltCand* ke
   for (int q = 0; q < 4; ++q) ls += lane * 4 + q < keep ? e[q] : 0.0;
   const double S = wave_sum(ls);
   if (lane == 0) f.hdr[sr] = FiltRow{keep, 0, m, m + ::log(S)};
+  // position in token-id order, counted over kept[0 .. keep) padded to a
+  // multiple of 8 with ids that count for nobody (kept has room for them)
+  int id[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) id[q] = lane * 4 + q < keep ? kept[lane * 4 + q].i : 0;
+  wave_sync();
+  const int keep8 = (keep + 7) & ~7;
+  if (lane < keep8 - keep) kept[keep + lane].i = 0x7fffffff;
+  wave_sync();
+  int rank[4] = {0, 0, 0, 0};
+#pragma unroll 8
+  for (int s = 0; s < keep8; ++s) {
+    const int o = kept[s].i;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rank[q] += o < id[q] ? 1 : 0;
+  }
   FiltEnt* out = f.ent + sr * (int64_t)f.stride;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int j = lane * 4 + q;
-    if (j < keep) {
-      const int id = kept[j].i;
-      int rank = 0;
-      for (int s = 0; s < keep; ++s) rank += kept[s].i < id ? 1 : 0;
-      out[rank] = FiltEnt{id, 0, z[q]};
-    }
-  }
+  for (int q = 0; q < 4; ++q)
+    if (lane * 4 + q < keep) out[rank[q]] = FiltEnt{id[q], 0, z[q]};
 }
 
 }  // namespace
 
 // One wave per row: the row bound and validity from the chunk records, a
 // second bound from the stored candidates >= it, the candidates >= both
-// gathered into the wave's LDS buffer, exact positions by counting, then the
-// fp64 finish.
+// gathered into the wave's LDS buffer, the exact top k cut by bisection on
+// the k-th largest logit, its order by counting (LDS broadcast reads), then
+// the fp64 finish.
 // Rows with a chunk whose candidates overflowed its store, more than kWCap
 // candidates >= both bounds, or more than 64 chunks are listed for the
 // workgroup merge.
@@ -622,8 +621,8 @@ __global__ __launch_bounds__(kWG) void k_filt_mergew(LinCfg c, FiltCfg f, int64_
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int64_t sr = blockIdx.x * (int64_t)kWaves + wave;
   if (sr >= rows) return;  // the whole wave; no workgroup barrier below
-  __shared__ FiltCand s_cand[kWaves][kWCap];
-  __shared__ FiltCand s_kept[kWaves][kMaxTopK];
+  __shared__ FiltCand s_cand[kWaves][kWCap + 8];
+  __shared__ FiltCand s_kept[kWaves][kMaxTopK + 8];
   FiltCand* cand = s_cand[wave];
   FiltCand* kept = s_kept[wave];
   const FiltChunk* rec = f.chk + sr * f.nchf;
@@ -651,29 +650,29 @@ __global__ __launch_bounds__(kWG) void k_filt_mergew(LinCfg c, FiltCfg f, int64_
   float tau2 = tau;
   int n2 = 0;
   if (!fall && f.nchf <= kFastCh) {
-    // every stored candidate loaded at once: lane l holds slots l and l + 64
-    // of each chunk
-    FiltCand buf[2 * kFastCh];
+    // the logits of every stored candidate loaded at once: lane l holds slots
+    // l and l + 64 of each chunk (ids are read again for the survivors)
+    float bv[2 * kFastCh];
     const FiltCand* src = f.fc + sr * f.nchf * (int64_t)kFiltChunkCap;
 #pragma unroll
     for (int r = 0; r < 2 * kFastCh; ++r) {
       const int ch = r >> 1, i = (r & 1) * kWave + lane;
       const int cc = ch < f.nchf ? __shfl(mycnt, ch) : 0;
-      buf[r] = i < cc ? src[ch * kFiltChunkCap + i] : FiltCand{-INFINITY, 0x7fffffff};
+      bv[r] = i < cc ? src[ch * kFiltChunkCap + i].v : -INFINITY;
     }
     Top4 top;
 #pragma unroll
-    for (int r = 0; r < 2 * kFastCh; ++r) {
-      const float v = buf[r].v;
-      if (v >= tau) top.add(v);
-    }
-    tau2 = fmaxf(tau, __shfl(wave_sort_desc(top.nth(jj)), ll - 1));
+    for (int r = 0; r < 2 * kFastCh; ++r) top.add(bv[r] >= tau ? bv[r] : -INFINITY);
+    tau2 = fmaxf(tau, wave_kth_largest(top.nth(jj), ll));
 #pragma unroll
     for (int r = 0; r < 2 * kFastCh; ++r) {
-      const bool take = buf[r].v >= tau2 && buf[r].v > -INFINITY;
+      const bool take = bv[r] >= tau2 && bv[r] > -INFINITY;
       const unsigned long long m = __ballot(take);
       const int slot = n2 + __popcll(m & lt);
-      if (take && slot < kWCap) cand[slot] = buf[r];
+      if (take && slot < kWCap) {
+        const int ch = r >> 1, i = (r & 1) * kWave + lane;
+        cand[slot] = FiltCand{bv[r], src[ch * kFiltChunkCap + i].i};
+      }
       n2 += __popcll(m);
     }
     fall = n2 > kWCap;
@@ -684,10 +683,10 @@ __global__ __launch_bounds__(kWG) void k_filt_mergew(LinCfg c, FiltCfg f, int64_
       const FiltCand* src = f.fc + (sr * f.nchf + ch) * kFiltChunkCap;
       for (int i = lane; i < cc; i += kWave) {
         const float v = src[i].v;
-        if (v >= tau) top.add(v);
+        top.add(v >= tau ? v : -INFINITY);
       }
     }
-    tau2 = fmaxf(tau, __shfl(wave_sort_desc(top.nth(jj)), ll - 1));
+    tau2 = fmaxf(tau, wave_kth_largest(top.nth(jj), ll));
     // Pass 2: gather the candidates >= tau2.
     for (int ch = 0; ch < f.nchf; ++ch) {
       const int cc = __shfl(mycnt, ch);
@@ -710,24 +709,46 @@ __global__ __launch_bounds__(kWG) void k_filt_mergew(LinCfg c, FiltCfg f, int64_
     return;
   }
   wave_sync();
-  if (n2 <= 2 * kWave) {
-    // up to 128 survivors: sorted in registers
-    FiltCand e[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) e[r] = 2 * lane + r < n2 ? cand[2 * lane + r] : FiltCand{-INFINITY, 0x7fffffff};
-    wave_sort2(e, [](const FiltCand& a, const FiltCand& b) { return before(a, b); });
-    finish_row_wave2(f, sr, e, n2 < kk ? n2 : kk);
+  FiltCand* sel = cand;  // the kept set, unordered
+  FiltCand* ord = kept;  // the kept set in (logit desc, id asc) order
+  int cnt = n2;
+  if (n2 > kk && n2 <= 2 * kWave) {
+    cnt = kk;
+    select_topk<2>(cand, n2, kk, kept);
+    sel = kept;
+    ord = cand;
+  } else if (n2 > kk) {
+    // a cut among more than 128: every survivor's position, by counting
+    const int n28 = (n2 + 7) & ~7;
+    if (lane < n28 - n2) cand[n2 + lane] = FiltCand{-INFINITY, 0x7fffffff};
+    wave_sync();
+    for (int i0 = 0; i0 < n2; i0 += kWave) {
+      const int i = i0 + lane;
+      const FiltCand me = i < n2 ? cand[i] : FiltCand{-INFINITY, 0x7fffffff};
+      int rank = 0;
+#pragma unroll 8
+      for (int j = 0; j < n28; ++j) rank += before_i(cand[j], me);
+      if (i < n2 && rank < kk) kept[rank] = me;
+    }
+    wave_sync();
+    finish_row_wave(f, sr, kept, kk);
     return;
   }
-  // exact position of each survivor in (logit desc, id asc) order
-  for (int i = lane; i < n2; i += kWave) {
-    const FiltCand me = cand[i];
+  // exact position of each kept entry in (logit desc, id asc) order, counted
+  // over sel[0 .. cnt) padded to a multiple of 8 with entries that come last
+  const int c8 = (cnt + 7) & ~7;
+  if (lane < c8 - cnt) sel[cnt + lane] = FiltCand{-INFINITY, 0x7fffffff};
+  wave_sync();
+  for (int i0 = 0; i0 < cnt; i0 += kWave) {
+    const int i = i0 + lane;
+    const FiltCand me = i < cnt ? sel[i] : FiltCand{-INFINITY, 0x7fffffff};
     int rank = 0;
-    for (int j = 0; j < n2; ++j) rank += before(cand[j], me) ? 1 : 0;
-    if (rank < kk) kept[rank] = me;
+#pragma unroll 8
+    for (int j = 0; j < c8; ++j) rank += before_i(sel[j], me);
+    if (i < cnt) ord[rank] = me;
   }
   wave_sync();
-  finish_row_wave(f, sr, kept, n2 < kk ? n2 : kk);
+  finish_row_wave(f, sr, ord, cnt);
 }
 
 // The listed rows, one workgroup each.
