@@ -245,13 +245,7 @@ int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype,
   } else if (filtered(params, V)) {
     e = launch_filtered(c, filt_cfg(params, workspace, B, 2 * K + 1, V, dtype), dtype, false, stream);
   } else {
-    e = hipSuccess;
-    if (c.fused) {
-      LinCfg d = c;
-      d.rows.np = 0;
-      e = launch_draft_sampled(d, dtype, stream);
-    }
-    if (e == hipSuccess) e = launch_linear_sampled(c, dtype, stream);
+    e = launch_linear_sampled(c, dtype, stream);  // draws the drafts itself when fused
   }
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }

@@ -219,14 +219,14 @@ __device__ __forceinline__ double exp2_poly(double y) {
   return ::ldexp(p, (int)k);
 }
 
-// 2^y in fp64 for y <= 1023 (relative error < 5e-16; y below -1022, -inf
-// included, is taken as -1022, i.e. ~2^-1022). k = the integer nearest y is
+// 2^y in fp64 for y <= 1023 (relative error < 5e-16; 0 for y below -1022,
+// -inf and NaN included). k = the integer nearest y is
 // read from the low word of y + 1.5 * 2^52, f = y - k lies in [-1/2, 1/2],
 // 2^f comes from a degree-10 near-minimax polynomial (Chebyshev interpolation
 // at 11 nodes, coefficients from exp2_coeffs.py), and 2^k is assembled in the
 // exponent field. Only full-rate fp64 and integer operations.
-__device__ __forceinline__ double exp2_fast(double y) {
-  y = fmax(y, -1022.0);
+__device__ __forceinline__ double exp2_fast(double y0) {
+  const double y = fmax(y0, -1022.0);
   constexpr double kMagic = 6755399441055744.0;  // 1.5 * 2^52
   const double t = y + kMagic;
   const double f = y - (t - kMagic);
@@ -242,7 +242,8 @@ __device__ __forceinline__ double exp2_fast(double y) {
   p = __builtin_fma(p, f, 0.24022650695910097);
   p = __builtin_fma(p, f, 0.69314718055995);
   p = __builtin_fma(p, f, 1.0);
-  return p * __hiloint2double((k + 1023) << 20, 0);
+  const double r = p * __hiloint2double((k + 1023) << 20, 0);
+  return y0 >= -1022.0 ? r : 0.0;
 }
 
 }  // namespace psi

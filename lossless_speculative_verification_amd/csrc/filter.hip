@@ -214,38 +214,70 @@ __device__ __forceinline__ void filt_chunk(const LinCfg& c, const FiltCfg& f) {
   const int64_t v0 = (int64_t)ch * kWG * NV + t;
   float x[NV][EPV];
   load_vecs<DT, AL, NV, kWG>(row, c.V, c.nvec, v0, x);
-  int bad = 0, any = 0;
+  bool tbad = false, tany = false;
   float mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NV; ++k)
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
       const float xe = x[k][e];
-      bad |= isnan(xe) || xe == INFINITY;
-      any |= xe > -INFINITY;
+      tbad |= isnan(xe) || xe == INFINITY;
+      tany |= xe > -INFINITY;
       mx = fmaxf(mx, xe);
     }
   // Each wave has kq threads whose maximum is >= its kq-th largest thread
   // maximum, so the smallest of the four wave values bounds the chunk's
   // (4 kq >= kk)-th largest logit from below.
   __shared__ float s_w[kWaves];
+  __shared__ int s_f[kWaves];
   __shared__ int s_sc[kWaves];
+  __shared__ int s_cnt;
+  __shared__ FiltCand s_out[kFiltChunkCap];
   const int kq = (f.kk + kWaves - 1) / kWaves;
   const float wq = wave_kth_largest(mx, kq);
-  if (lane == 0) s_w[wave] = wq;
-  bad = __syncthreads_or(bad);
-  any = __syncthreads_or(any);
+  const int wf = (__ballot(tbad) ? 1 : 0) | (__ballot(tany) ? 2 : 0);
+  if (lane == 0) {
+    s_w[wave] = wq;
+    s_f[wave] = wf;
+  }
+  if (t == 0) s_cnt = 0;
+  __syncthreads();
   float tau = s_w[0];
+  int flags = s_f[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) tau = fminf(tau, s_w[i]);
-  int n = 0;
+  for (int i = 1; i < kWaves; ++i) {
+    tau = fminf(tau, s_w[i]);
+    flags |= s_f[i];
+  }
+  // Candidates (finite logits >= tau) staged in LDS: a thread that has some
+  // reserves its slots with one LDS atomic (candidates are sparse), and each
+  // 16-byte vector is tested once before its logits are.
+  auto stage = [&](float th) {
+    int n = 0;
 #pragma unroll
-  for (int k = 0; k < NV; ++k)
+    for (int k = 0; k < NV; ++k)
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) n += (x[k][e] >= tau && x[k][e] > -INFINITY) ? 1 : 0;
-  int total;
-  int off = block_scan_int(n, s_sc, &total);
-  if (total > kFiltChunkCap && !bad && 2 * f.kk <= kFiltChunkCap) {
+      for (int e = 0; e < EPV; ++e) n += (x[k][e] >= th && x[k][e] > -INFINITY) ? 1 : 0;
+    int w = n > 0 ? atomicAdd(&s_cnt, n) : 0;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      bool anyk = false;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) anyk |= x[k][e] >= th && x[k][e] > -INFINITY;
+      if (anyk) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+          if (x[k][e] >= th && x[k][e] > -INFINITY) {
+            if (w < kFiltChunkCap) s_out[w] = FiltCand{x[k][e], (int32_t)((v0 + (int64_t)k * kWG) * EPV + e)};
+            ++w;
+          }
+      }
+    }
+    __syncthreads();
+  };
+  stage(tau);
+  int total = s_cnt;
+  if (total > kFiltChunkCap && !(flags & 1) && 2 * f.kk <= kFiltChunkCap) {
     // Too many candidates: raise tau by bisection over the order of the
     // logits while at least kk logits stay >= it, until at most
     // kFiltChunkCap do (many equal logits can keep the count above it).
@@ -269,22 +301,13 @@ __device__ __forceinline__ void filt_chunk(const LinCfg& c, const FiltCfg& f) {
       }
     }
     tau = from_order_key(lo);
-    n = 0;
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) n += (x[k][e] >= tau && x[k][e] > -INFINITY) ? 1 : 0;
-    off = block_scan_int(n, s_sc, &total);
+    if (t == 0) s_cnt = 0;
+    __syncthreads();
+    stage(tau);
+    total = s_cnt;
   }
-  if (total <= kFiltChunkCap) {
-    FiltCand* out = f.fc + item * kFiltChunkCap + off;
-    int w = 0;
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-#pragma unroll
-      for (int e = 0; e < EPV; ++e)
-        if (x[k][e] >= tau && x[k][e] > -INFINITY) out[w++] = FiltCand{x[k][e], (int32_t)((v0 + (int64_t)k * kWG) * EPV + e)};
-  }
+  if (total <= kFiltChunkCap && t < total) f.fc[item * kFiltChunkCap + t] = s_out[t];
+  const bool bad = flags & 1, any = flags & 2;
   if (t == 0) f.chk[item] = FiltChunk{tau, total, (bad ? 1 : 0) | (any ? 2 : 0), 0};
   if (item == 0 && t == 0) *f.nfall = 0;
 }

@@ -10,6 +10,9 @@
 //   k_stats32   (stats.hip) chunk maxima and sums of every target and draft
 //               row -> log-normalisers good to ~1e-7, enough for the accept
 //               test.
+//   k_draftrow  with drafts drawn inside the call: per draft row, fp64
+//               sub-block sums under the final-draw weight rule and the
+//               inverse-CDF pick of the draft.
 //   k_resolve   per request (16 waves): row normalisers, p(x_i), q(x_i),
 //               Philox accept tests and a wave ballot for the first rejection
 //               n; then fp64 sums per 1024-element sub-block over the one row
@@ -17,8 +20,8 @@
 //               then, when one workgroup owns the request, the inverse-CDF
 //               pick from those sums and an fp64 rescan of one sub-block.
 //   k_final     the pick, when several workgroups shared a request's sums.
-// Draft sampling uses k_draftpass (fp64 sub-block sums of a draft row) and
-// k_draftfinal (pick). Greedy mode (temperature 0) uses k_argmax and
+// Draft sampling alone runs k_stats32 over the draft rows, then k_draftrow.
+// Greedy mode (temperature 0) uses k_argmax and
 // k_greedy_decide. The final draws are done in fp64 because an inverse-CDF
 // pick over 151936 tokens must agree with an fp64 reference to ~1e-12 of the
 // total mass to give the same token; the accept test only needs ~1e-7.
@@ -76,13 +79,13 @@ __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool 
 
 // fp64 sums of this workgroup's sub-blocks [sb0, sb1) of the final row pair
 // (RESID) or the target row alone, one wave per sub-block (sb0 + wave, then
-// every kRWaves-th). Software-pipelined over NBUF register buffers that change
+// every NW-th, NW the workgroup's waves). Software-pipelined over NBUF register buffers that change
 // roles each step (no copies, so loads stay in flight across steps): bfloat16
 // keeps the next two sub-blocks in flight, fp32 the next one. TAB: weights
 // are read from the pre-scaled LDS tables tp / tq (bfloat16 only), whose
 // values estimate the probabilities, so the target part is above the draft
 // part where ep > eq; otherwise where a_p - a_q > dx.
-template <int DT, bool AL, bool TAB, bool RESID, bool PICK>
+template <int DT, bool AL, bool TAB, bool RESID, bool PICK, int NW = kRWaves>
 __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
                                              int sb0, int sb1, const double* tp, const double* tq, const WRow& wp,
                                              const WRow& wq, float dx, ResRec* s_rec) {
@@ -185,7 +188,7 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
       if (lane == 0) *rec = ResRec{tot, 0.0, 0.0, 0.0};
     }
   };
-  constexpr int W = kRWaves;
+  constexpr int W = NW;
   Buf x0, x1, x2;
   int s = sb0 + wave;
   if (s >= sb1) return;
@@ -496,6 +499,87 @@ __global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
 }
 
 // ----------------------------------------------------- draft sampling --
+// One workgroup per draft row, after the statistics pass: the row maximum m
+// and validity from the row's chunk records, then the fp64 weights of the
+// row under the rule of the final draws (for a bfloat16 row that qualifies,
+// an LDS table of 2^(a c) scaled by 2^(-m c)), summed per sub-block in LDS,
+// then wave 0 draws x ~ q by inverse CDF over the sub-block sums and a rescan
+// of the chosen sub-block ("Uno" research explainer, §3.3: the drafts of a
+// block are drawn from the draft distributions). -1 for an invalid row.
+constexpr int kDT = 512;
+constexpr int kDWaves = kDT / kWave;
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(kDT) void k_draftrow(LinCfg c) {
+  extern __shared__ ResRec s_rec[];  // one record per sub-block
+  __shared__ double s_tab[kTabSize];
+  __shared__ int s_bad;
+  __shared__ float s_m;
+  const int64_t qr = blockIdx.x;  // draft row in [0, B*K)
+  const int K = c.K, t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
+  const int64_t b = qr / K;
+  const int i = (int)(qr - b * K);
+  const char* row = qrow_of(c, b, i);
+  // row maximum and validity from the statistics records (NaN, +inf, all -inf)
+  if (wave == 0) {
+    const StatRec* rec = c.st + (b * (c.rows.np + c.rows.nq) + c.rows.np + i) * (int64_t)c.nch32;
+    float m = -INFINITY;
+    int bad = 0;
+    for (int ch = lane; ch < c.nch32; ch += kWave) {
+      const StatRec rc = rec[ch];
+      m = fmaxnan(m, rc.m);
+      bad |= isnan(rc.s) ? 1 : 0;
+    }
+    m = wave_max(m);
+    bad = wave_or(bad);
+    if (lane == 0) {
+      s_m = m;
+      s_bad = bad || isnan(m) || isinf(m);
+    }
+  }
+  const bool tab = DT == kBF16 && c.tab;
+  if (tab) fill_tab<kDT>(s_tab, c.c64);
+  __syncthreads();
+  if (s_bad) {
+    if (t == 0) c.draft[qr] = -1;
+    return;
+  }
+  const WRow w = wrow(tab, s_m, c.c64);
+  if (DT == kBF16 && w.tab) {
+    for (int j = t; j < kTabSize; j += kDT) s_tab[j] *= w.scale;
+    __syncthreads();
+    resolve_pass<DT, AL, DT == kBF16, false, true, kDWaves>(c, b, row, row, 0, c.nsb, s_tab, s_tab, w, w, 0.0f,
+                                                            s_rec);
+  } else {
+    resolve_pass<DT, AL, false, false, true, kDWaves>(c, b, row, row, 0, c.nsb, s_tab, s_tab, w, w, 0.0f, s_rec);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const double* const tps = w.tab ? s_tab : nullptr;
+  double mine = 0.0;
+  for (int sb = lane; sb < c.nsb; sb += kWave) mine += s_rec[sb].sp;
+  const double W = wave_sum(mine);
+  const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
+  const int x = wave_pick(
+      c.nsb, c.V, u * W, [&](int sb) { return s_rec[sb].sp; },
+      [&](int64_t j0, double(&wt)[16]) { row16<DT, AL>(c, row, j0, w, tps, wt); });
+  if (lane == 0) c.draft[qr] = x;
+}
+
+// Draft sampling alone: a request with an invalid draft row gets -1 for all
+// its drafts.
+__global__ __launch_bounds__(kWave) void k_draft_fix(LinCfg c) {
+  const int64_t b = blockIdx.x;
+  const int K = c.K, lane = threadIdx.x;
+  int bad = 0;
+  for (int i = lane; i < K; i += kWave) bad |= c.draft[b * K + i] < 0 ? 1 : 0;
+  bad = wave_or(bad);
+  if (bad)
+    for (int i = lane; i < K; i += kWave) c.draft[b * K + i] = -1;
+}
+
+// fp64 sub-block sums (with per-sub-block maxima) of draft rows, for the node
+// drafts of tree verification.
 template <int DT, bool AL>
 __global__ __launch_bounds__(kWG) void k_draftpass(LinCfg c) {
   constexpr int EPV = Elem<DT>::kPerVec;
@@ -519,7 +603,7 @@ __global__ __launch_bounds__(kWG) void k_draftpass(LinCfg c) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) s += exp64(((double)x[v][e] - md) * c.invT);
+      for (int e = 0; e < EPV; ++e) s += exp2_fast(((double)x[v][e] - md) * c.c64);
     s = wave_sum(s);
   }
   if (lane == 0) {
@@ -529,39 +613,6 @@ __global__ __launch_bounds__(kWG) void k_draftpass(LinCfg c) {
     r.s = s;
     c.dr[qr * c.nsb + sb] = r;
   }
-}
-
-template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_draftfinal(LinCfg c) {
-  using E = Elem<DT>;
-  const int64_t qr = blockIdx.x;
-  const int K = c.K, nsb = c.nsb, t = threadIdx.x;
-  const int64_t b = qr / K;
-  const int i = (int)(qr - b * K);
-  __shared__ int s_alive[kMaxK];
-  __shared__ int s_bad;
-  __shared__ float shf[kWaves];
-  __shared__ double sh[kWG + kWaves];
-  if (t < K) s_alive[t] = 0;
-  if (t == 0) s_bad = 0;
-  __syncthreads();
-  // every draft row of the request must be valid
-  const DraftRec* req = c.dr + b * K * (int64_t)nsb;
-  for (int idx = t; idx < K * nsb; idx += kWG) {
-    const DraftRec r = req[idx];
-    if (isnan(r.m) || (isinf(r.m) && r.m > 0.0f) || isnan(r.s)) atomicOr(&s_bad, 1);
-    if (!is_neg_inf(r.m)) atomicOr(&s_alive[idx / nsb], 1);
-  }
-  __syncthreads();
-  int bad = s_bad;
-  for (int k = 0; k < K; ++k) bad |= !s_alive[k];
-  if (bad) {
-    if (t == 0) c.draft[qr] = -1;
-    return;
-  }
-  const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
-  const int y = draft_pick<DT>(c, c.rows.q + (qr * (int64_t)c.V) * c.rows.esz, c.dr + qr * nsb, u, shf, sh);
-  if (t == 0) c.draft[qr] = y;
 }
 
 // ------------------------------------------------------------- greedy --
@@ -705,6 +756,9 @@ static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
   const int64_t rows = c.B * (2 * c.K + 1);
   const hipError_t e = launch_stats32(c, rows, DT, s);
   if (e != hipSuccess) return e;
+  // drafts drawn inside the call, from the statistics of their rows
+  if (c.fused)
+    PSI_LAUNCH_LDS(s, (k_draftrow<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c);
   // One resolve workgroup per request when there are enough requests to fill
   // the chip (and its sub-block records fit in LDS); otherwise several per
   // request and a separate final step.
@@ -730,8 +784,10 @@ static hipError_t linear_greedy_t(const LinCfg& c, hipStream_t s) {
 
 template <int DT, bool AL>
 static hipError_t draft_sampled_t(const LinCfg& c, hipStream_t s) {
-  PSI_LAUNCH(s, (k_draftpass<DT, AL>), dim3((c.nsb + kWaves - 1) / kWaves, (unsigned)(c.B * c.K)), dim3(kWG), c);
-  PSI_LAUNCH(s, (k_draftfinal<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kWG), c);
+  const hipError_t e = launch_stats32(c, c.B * c.K, DT, s);
+  if (e != hipSuccess) return e;
+  PSI_LAUNCH_LDS(s, (k_draftrow<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c);
+  PSI_LAUNCH(s, k_draft_fix, dim3((unsigned)c.B), dim3(kWave), c);
   return hipGetLastError();
 }
 

@@ -290,10 +290,10 @@ __device__ int draft_pick(const LinCfg& c, const char* row, const DraftRec* rec,
   float m = -INFINITY;
   for (int sb = t; sb < nsb; sb += kWG) m = fmaxnan(m, rec[sb].m);
   m = block_max(m, shf);
-  const double md = m, invT = c.invT;
+  const double md = m, c64 = c.c64;
   auto wsb = [&](int sb) {
     const DraftRec r = rec[sb];
-    return is_neg_inf(r.m) ? 0.0 : r.s * exp64(((double)r.m - md) * invT);
+    return is_neg_inf(r.m) ? 0.0 : r.s * exp2_fast(((double)r.m - md) * c64);
   };
   double W;
   {
@@ -305,8 +305,8 @@ __device__ int draft_pick(const LinCfg& c, const char* row, const DraftRec* rec,
       nsb, c.V, u * W, wsb,
       [&](int64_t j) {
         const DraftRec r = rec[j / kSB];
-        const double f = exp64(((double)r.m - md) * invT);
-        return exp64(((double)E::load1(row, j) - (double)r.m) * invT) * f;
+        const double f = exp2_fast(((double)r.m - md) * c64);
+        return exp2_fast(((double)E::load1(row, j) - (double)r.m) * c64) * f;
       },
       sh);
 }
