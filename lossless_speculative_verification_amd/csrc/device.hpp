@@ -104,6 +104,31 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxnan(v, __shfl_xor(v, o));
   return v;
 }
+// fp64 lane moves inside the VALU (DPP), for scans and sums without LDS
+// permutes: CTRL is a DPP control (row_shr:n = 0x110 + n, row_bcast:15 =
+// 0x142, row_bcast:31 = 0x143), ROWS the rows of 16 lanes that receive; lanes
+// that receive nothing read 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xf, true);
+  return __hiloint2double(hi, lo);
+}
+
+// Inclusive sum over the lanes of a wave, in lane order: within each row of
+// 16 by shifts of 1, 2, 4, 8, then across rows by broadcasting lane 15 of
+// rows 0 and 2 and lane 31 (Hillis-Steele on DPP).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  v += dpp_f64<0x111, 0xf>(v);
+  v += dpp_f64<0x112, 0xf>(v);
+  v += dpp_f64<0x114, 0xf>(v);
+  v += dpp_f64<0x118, 0xf>(v);
+  v += dpp_f64<0x142, 0xa>(v);
+  v += dpp_f64<0x143, 0xc>(v);
+  return v;
+}
+
+// Sum over the wave, the same on every lane (butterfly).
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -169,12 +194,7 @@ template <int NT = kWG>
 __device__ __forceinline__ double block_exclusive_scan(double v, double* sh, double* total) {
   constexpr int NW = NT / kWave;
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-  double incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double up = __shfl_up(incl, o);
-    if (lane >= o) incl += up;
-  }
+  const double incl = wave_incl_scan(v);
   __syncthreads();
   if (lane == kWave - 1) sh[w] = incl;
   __syncthreads();

@@ -201,17 +201,6 @@ __device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, doubl
   return j;
 }
 
-// Inclusive sum over the lanes of a wave, in lane order.
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double up = __shfl_up(v, o);
-    if (lane >= o) v += up;
-  }
-  return v;
-}
-
 // The pick of pick_index done by one whole wave (all 64 lanes active), with
 // no workgroup barrier: lane l owns a run of consecutive sub-blocks, then 16
 // consecutive elements of the chosen sub-block, whose weights welb(j0, w)
