@@ -23,7 +23,6 @@ the HBM byte counters of a profiler run) and prints its size.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -41,8 +40,9 @@ T = 1.0
 # launches of one headline verify call (one resolve workgroup per request)
 LINEAR_KERNELS = ("k_stats32", "k_resolve")
 PMC_FILE = os.path.join(ROOT, "profiles", "k_stats32_highconc_pmc.txt")
-# the sources k_stats32 is built from: its HBM counters stay valid while these do
-KERNEL_SOURCES = ("stats.hip", "rowload.hpp", "kernels.hpp", "device.hpp")
+CODE_JSON = os.path.join(ROOT, "lossless_speculative_verification_amd", "kernel_code.json")
+# the k_stats32 instance of the headline workload (bfloat16, aligned rows)
+STATS_KERNEL = "_ZN3psi9k_stats32ILi1ELb1EEEvNS_6LinCfgE"
 
 
 def bytes_alg(B, K, V, esz=2):
@@ -56,17 +56,19 @@ def stats_bytes(B, K, V, esz=2):
     return B * (2 * K + 1) * V * esz
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "lossless_speculative_verification_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def kernel_code_hash():
+    """Hash of the gfx950 code of the headline k_stats32 instance, as written by
+    the package build (None when the build did not record it)."""
+    try:
+        with open(CODE_JSON) as f:
+            return json.load(f).get(STATS_KERNEL)
+    except (OSError, ValueError):
+        return None
 
 
 def pmc_traffic():
     """HBM bytes per statistics-pass launch from the committed counter summary,
-    or None when it is missing or was taken on other kernel sources."""
+    or None when it is missing or was taken on other kernel code."""
     try:
         kv = {}
         with open(PMC_FILE) as f:
@@ -74,7 +76,8 @@ def pmc_traffic():
                 if ":" in line and not line.startswith("#"):
                     k_, v_ = line.split(":", 1)
                     kv[k_.strip()] = v_.strip()
-        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        code = kernel_code_hash()
+        if code is None or kv.get("kernel_code_sha256_16") != code:
             return None
         return float(kv["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):

@@ -3,11 +3,18 @@
 Every .hip file under csrc/ is compiled for gfx950 only, in parallel, then
 linked into lossless_speculative_verification_amd/libpsispec.so. Packed FP32
 instruction selection is disabled for every source.
+
+It also writes kernel_code.json beside the library: a hash of the gfx950
+assembly of each k_stats32 instance, so that measurements taken on that
+kernel (its HBM byte counters) can be matched to the code that runs.
 """
 from __future__ import annotations
 
 import glob
+import hashlib
+import json
 import os
+import re
 import subprocess
 import sys
 
@@ -16,6 +23,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "psispec")
 LIB = os.path.join(HERE, "libpsispec.so")
+CODE_JSON = os.path.join(HERE, "kernel_code.json")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -54,7 +62,40 @@ def build(verbose: bool = False) -> str:
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    write_code_hashes()
     return LIB
+
+
+def function_hashes(asm: str, pattern: str) -> dict:
+    """sha256 (16 hex digits) of the instructions of every function whose
+    mangled name matches `pattern`, comments and blank lines dropped."""
+    out = {}
+    lines = asm.splitlines()
+    for i, line in enumerate(lines):
+        m = re.match(r"^(_Z\S+):", line)
+        if not m or not re.search(pattern, m.group(1)):
+            continue
+        body = []
+        for l in lines[i + 1:]:
+            if l.startswith(".Lfunc_end"):
+                break
+            l = l.split(";", 1)[0].strip()
+            if l:
+                body.append(l)
+        out[m.group(1)] = hashlib.sha256("\n".join(body).encode()).hexdigest()[:16]
+    return out
+
+
+def write_code_hashes() -> None:
+    os.makedirs(BUILD, exist_ok=True)
+    asm = os.path.join(BUILD, "stats.s")
+    cmd = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], "--cuda-device-only", "-S",
+           os.path.join(CSRC, "stats.hip"), "-o", asm]
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    with open(asm) as f:
+        hashes = function_hashes(f.read(), r"k_stats32")
+    with open(CODE_JSON, "w") as f:
+        json.dump(hashes, f, indent=1, sort_keys=True)
 
 
 if __name__ == "__main__":
