@@ -69,6 +69,12 @@ def lib():
         L.orc_tree_draft.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, f64, ctypes.c_int, f64, u64,
                                      u32, P, ctypes.c_int]
         L.orc_tree_draft.restype = ctypes.c_int
+        L.orc_tree_candidates.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, f64, ctypes.c_int,
+                                          ctypes.c_int, P, P, P, ctypes.c_int]
+        L.orc_tree_candidates.restype = ctypes.c_int
+        L.orc_verify_tree_det.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, P, f64, u64, u32,
+                                          P, P, P, P, P, ctypes.c_int]
+        L.orc_verify_tree_det.restype = ctypes.c_int
         del i32
         _lib = L
     return _lib
@@ -222,4 +228,44 @@ def verify_tree(p, q, parent, node_tokens, temperature, top_k=0, top_p=1.0, seed
                                _ptr(ma), _ptr(mc), _ptr(ovr), maxC, int(nthreads))
     if rc != 0:
         raise ValueError("orc_verify_tree rejected its arguments")
+    return dict(tokens=toks, path=path, len=ln, margin_acc=ma, margin_cdf=mc)
+
+
+def tree_candidates(q, cands, nodes, temperature, nthreads=1):
+    """Tree Sampler candidates from draft logits q [B, K, V]: per request the
+    `nodes` best prefixes over the top-`cands` tokens of each position.
+
+    Returns (parent [B, nodes], tokens [B, nodes], margin [B]); margin is the
+    smallest log-score gap of any choice made (see oracle.c)."""
+    q = np.ascontiguousarray(q)
+    B, K, V = q.shape
+    par = np.zeros((B, nodes), dtype=np.int32)
+    tok = np.zeros((B, nodes), dtype=np.int32)
+    mg = np.zeros(B, dtype=np.float64)
+    rc = lib().orc_tree_candidates(_ptr(q), _dtype_code(q), B, K, V, float(temperature), int(cands), int(nodes),
+                                   _ptr(par), _ptr(tok), _ptr(mg), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_tree_candidates rejected its arguments")
+    return par, tok, mg
+
+
+def verify_tree_det(p, parent, node_tokens, temperature, seed=0, step=0, nthreads=1):
+    """Verification of deterministic candidates: p [B, N+1, V], per-request
+    parent [B, N] and node_tokens [B, N]. Returns a dict with tokens [B, N+1],
+    path [B, N], len [B], margin_acc, margin_cdf."""
+    p = np.ascontiguousarray(p)
+    B, R, V = p.shape
+    N = R - 1
+    par = np.ascontiguousarray(parent, dtype=np.int32).reshape(B, N)
+    nt = np.ascontiguousarray(node_tokens, dtype=np.int32).reshape(B, N)
+    toks = np.zeros((B, N + 1), dtype=np.int32)
+    path = np.zeros((B, N), dtype=np.int32)
+    ln = np.zeros(B, dtype=np.int32)
+    ma = np.zeros(B, dtype=np.float64)
+    mc = np.zeros(B, dtype=np.float64)
+    rc = lib().orc_verify_tree_det(_ptr(p), _dtype_code(p), B, N, V, _ptr(par), _ptr(nt), float(temperature),
+                                   int(seed), int(step), _ptr(toks), _ptr(path), _ptr(ln), _ptr(ma), _ptr(mc),
+                                   int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_verify_tree_det rejected its arguments")
     return dict(tokens=toks, path=path, len=ln, margin_acc=ma, margin_cdf=mc)

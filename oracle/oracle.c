@@ -827,3 +827,305 @@ int orc_verify_tree(const void* p, const void* q, int dtype, int64_t B, int N, i
   free(jobs);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Tree Sampler candidates [UnoX §3.4 Tree Sampler: each position keeps its
+ * top-K tokens, then the V most probable prefixes are kept and verified in
+ * one pass; UnoX §6.3 uses (block, K, V) = (16, 32, 32)]. Reading of the
+ * construction (the pages give no formula):
+ *   q_i = softmax(d_i / T) for draft position i (full row, fp64);
+ *   C_i = the `cands` tokens with the largest q_i, ties to the lower id, in
+ *         that order (rank 0 first);
+ *   a prefix (t_0 .. t_{l-1}), t_i in C_i, has log score
+ *         sum_i (z_i(t_i) - L_i), z = d / T, L_i = log sum exp z_i;
+ *   the kept prefixes are the first `nodes` ones in the order
+ *         log score descending, then length ascending, then the position of
+ *         the parent prefix in this order ascending (the empty prefix first),
+ *         then the rank of the last token in C ascending.
+ * A parent's score is at least its child's and comes first on a tie, so the
+ * kept set is closed under taking prefixes. Node n is the n-th kept prefix,
+ * parent[n] the node of its parent (-1 for length 1), tokens[n] its last
+ * token, so parent[n] < n. Enumerated best first: at each step every kept
+ * prefix (and the empty one) offers its best child not yet kept, and the best
+ * offer in the order is kept. *margin = the smallest log-score gap between
+ * the kept offer and any other offer of the same step (0 for exact ties
+ * across parents). A request with an invalid draft row gets -1 in every
+ * parent and token. */
+typedef struct {
+  const void* q;
+  int dtype, K, V, cands, nodes;
+  double temperature;
+  int32_t *out_parent, *out_tokens;
+  double* out_margin;
+  int64_t b0, b1;
+} cand_job;
+
+static void* cand_worker(void* arg) {
+  cand_job* J = (cand_job*)arg;
+  const int K = J->K, V = J->V, C = J->cands, NN = J->nodes;
+  double* z = (double*)malloc(sizeof(double) * (size_t)V);
+  keyed* buf = (keyed*)malloc(sizeof(keyed) * (size_t)V);
+  int32_t* ctok = (int32_t*)malloc(sizeof(int32_t) * (size_t)K * C);
+  double* clq = (double*)malloc(sizeof(double) * (size_t)K * C);
+  double* ls = (double*)malloc(sizeof(double) * (size_t)(NN + 1));
+  int* depth = (int*)malloc(sizeof(int) * (size_t)(NN + 1));
+  int* next = (int*)malloc(sizeof(int) * (size_t)(NN + 1));
+  for (int64_t b = J->b0; b < J->b1; ++b) {
+    int32_t* par = J->out_parent + b * NN;
+    int32_t* tok = J->out_tokens + b * NN;
+    int bad = 0;
+    for (int i = 0; i < K && !bad; ++i) {
+      bad |= orc_decode_row(J->q, J->dtype, b * K + i, V, z);
+      if (bad) break;
+      for (int j = 0; j < V; ++j) z[j] /= J->temperature;
+      const double L = orc_logsumexp(z, V);
+      for (int j = 0; j < V; ++j) {
+        buf[j].key = z[j];
+        buf[j].idx = j;
+      }
+      qsort(buf, (size_t)V, sizeof(keyed), cmp_desc_then_idx);
+      for (int r = 0; r < C; ++r) {
+        ctok[i * C + r] = buf[r].idx;
+        clq[i * C + r] = buf[r].key - L;
+      }
+    }
+    if (bad) {
+      for (int n = 0; n < NN; ++n) par[n] = tok[n] = -1;
+      if (J->out_margin) J->out_margin[b] = 1.0;
+      continue;
+    }
+    /* slot 0 is the empty prefix; slot n + 1 is node n */
+    ls[0] = 0.0;
+    depth[0] = 0;
+    next[0] = 0;
+    double margin = INFINITY;
+    for (int n = 0; n < NN; ++n) {
+      int best = -1;
+      double bls = 0.0;
+      for (int s = 0; s <= n; ++s) {
+        if (depth[s] >= K || next[s] >= C) continue; /* nothing to offer */
+        const double o = ls[s] + clq[depth[s] * C + next[s]];
+        int better;
+        if (best < 0) better = 1;
+        else if (o != bls) better = o > bls;
+        else if (depth[s] != depth[best]) better = depth[s] < depth[best];
+        else better = 0; /* same score and length: the earlier parent (smaller slot) wins */
+        if (better) {
+          best = s;
+          bls = o;
+        }
+      }
+      if (best < 0) { /* fewer prefixes than nodes */
+        for (int m = n; m < NN; ++m) par[m] = tok[m] = -1;
+        break;
+      }
+      for (int s = 0; s <= n; ++s) {
+        if (s == best || depth[s] >= K || next[s] >= C) continue;
+        const double gap = bls - (ls[s] + clq[depth[s] * C + next[s]]);
+        if (gap < margin) margin = gap;
+      }
+      par[n] = best - 1;
+      tok[n] = ctok[depth[best] * C + next[best]];
+      ls[n + 1] = bls;
+      depth[n + 1] = depth[best] + 1;
+      next[n + 1] = 0;
+      ++next[best];
+    }
+    if (J->out_margin) J->out_margin[b] = isinf(margin) ? 1.0 : margin;
+  }
+  free(z);
+  free(buf);
+  free(ctok);
+  free(clq);
+  free(ls);
+  free(depth);
+  free(next);
+  return NULL;
+}
+
+int orc_tree_candidates(const void* q, int dtype, int64_t B, int K, int V, double temperature, int cands,
+                        int nodes, int32_t* out_parent, int32_t* out_tokens, double* out_margin, int nthreads) {
+  if (!q || !out_parent || !out_tokens || B <= 0 || K <= 0 || V <= 0 || !(temperature > 0.0)) return -1;
+  if (cands < 1 || cands > V || nodes < 1) return -1;
+  nthreads = clamp_threads(nthreads, B);
+  cand_job* jobs = (cand_job*)calloc((size_t)nthreads, sizeof(cand_job));
+  for (int t = 0; t < nthreads; ++t) {
+    cand_job* J = &jobs[t];
+    J->q = q;
+    J->dtype = dtype;
+    J->K = K;
+    J->V = V;
+    J->cands = cands;
+    J->nodes = nodes;
+    J->temperature = temperature;
+    J->out_parent = out_parent;
+    J->out_tokens = out_tokens;
+    J->out_margin = out_margin;
+    J->b0 = B * t / nthreads;
+    J->b1 = B * (t + 1) / nthreads;
+  }
+  run_jobs(jobs, sizeof(cand_job), nthreads, cand_worker);
+  free(jobs);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Verification of deterministic candidates (the Tree Sampler's candidates of
+ * [UnoX §3.4] are chosen, not drawn; the pages state no rule for them, and
+ * this is the plain lossless one). Per request, with its own tree (parent,
+ * tokens [N], parent[n] < n): the walk starts at row 0 (row n + 1 follows node
+ * n); at a row, r = P = softmax(a / T) and E = 0; its children are tested in
+ * ascending node id, the j-th with u = U(seed, step, b, row, 1 + j): a point
+ * mass proposal at tok is accepted with probability r(tok), i.e. iff
+ * u * (1 - E) < P(tok) when tok is not yet removed (never when it is); on a
+ * rejection tok is removed from r (E += P(tok)) and r renormalised. The walk
+ * descends into the first accepted child; at a leaf or once every child is
+ * rejected, the final token is an inverse-CDF draw from P without the removed
+ * tokens, U(seed, step, b, row, 0) (from P itself if nothing remains).
+ * Temperature 0: accept iff tok is the target argmax (lowest id on ties);
+ * final token = the argmax. Any malformed parent, token out of range or
+ * invalid target row makes the request an error. Outputs [N + 1] tokens and
+ * [N] path entries per request, -1 past the end. */
+typedef struct {
+  const void* p;
+  int dtype, N, V;
+  const int32_t *parent, *tokens;
+  orc_params pr;
+  int32_t *out_tokens, *out_path, *out_len;
+  double *out_margin_acc, *out_margin_cdf;
+  int64_t b0, b1;
+} dtree_job;
+
+static void dtree_one(dtree_job* J, int64_t b, double* z, double* P, double* w, unsigned char* removed) {
+  const int N = J->N, V = J->V, R = N + 1;
+  const orc_params* pr = &J->pr;
+  const int32_t* par = J->parent + b * N;
+  const int32_t* ntk = J->tokens + b * N;
+  int32_t* toks = J->out_tokens + b * R;
+  int32_t* path = J->out_path + b * N;
+  for (int i = 0; i < R; ++i) toks[i] = -1;
+  for (int i = 0; i < N; ++i) path[i] = -1;
+  if (J->out_margin_acc) J->out_margin_acc[b] = 1.0;
+  if (J->out_margin_cdf) J->out_margin_cdf[b] = 1.0;
+  int bad = 0;
+  for (int n = 0; n < N; ++n) {
+    if (par[n] < -1 || par[n] >= n) bad = 1;
+    if (ntk[n] < 0 || ntk[n] >= V) bad = 1;
+  }
+  for (int r = 0; r < R && !bad; ++r) bad |= orc_decode_row(J->p, J->dtype, b * R + r, V, z);
+  if (bad) {
+    J->out_len[b] = -1;
+    return;
+  }
+  double margin_acc = 1.0, margin_cdf = 1.0;
+  const int greedy = pr->temperature == 0.0;
+  int row = 0, len = 0, y = -1;
+  for (;;) {
+    orc_decode_row(J->p, J->dtype, b * R + row, V, z);
+    int accepted = -1;
+    if (greedy) {
+      const int g = argmax_row(z, V);
+      for (int c = 0; c < N && accepted < 0; ++c)
+        if (par[c] == row - 1 && ntk[c] == g) accepted = c;
+      if (accepted < 0) {
+        y = g;
+        break;
+      }
+    } else {
+      for (int t = 0; t < V; ++t) z[t] /= pr->temperature;
+      const double L = orc_logsumexp(z, V);
+      for (int t = 0; t < V; ++t) {
+        P[t] = exp(z[t] - L);
+        removed[t] = 0;
+      }
+      double E = 0.0;
+      int j = 0;
+      for (int c = 0; c < N; ++c) {
+        if (par[c] != row - 1) continue;
+        const int tk = ntk[c];
+        const double u = orc_uniform(pr->seed, pr->step, (uint32_t)b, (uint32_t)row, 1u + (uint32_t)j);
+        const double pt = removed[tk] ? 0.0 : P[tk];
+        if (1.0 - E > 0.0) {
+          const double mg = fabs(u - pt / (1.0 - E));
+          if (mg < margin_acc) margin_acc = mg;
+        }
+        if (u * (1.0 - E) < pt) {
+          accepted = c;
+          break;
+        }
+        if (!removed[tk]) {
+          removed[tk] = 1;
+          E += P[tk];
+        }
+        ++j;
+      }
+      if (accepted < 0) {
+        double S = 0.0;
+        for (int t = 0; t < V; ++t) {
+          w[t] = removed[t] ? 0.0 : P[t];
+          S += w[t];
+        }
+        const double u = orc_uniform(pr->seed, pr->step, (uint32_t)b, (uint32_t)row, 0u);
+        double mg;
+        y = orc_sample(S > 0.0 ? w : P, V, u, &mg);
+        if (mg < margin_cdf) margin_cdf = mg;
+        break;
+      }
+    }
+    path[len] = accepted;
+    toks[len] = ntk[accepted];
+    ++len;
+    row = accepted + 1;
+  }
+  toks[len] = y;
+  J->out_len[b] = len;
+  if (J->out_margin_acc) J->out_margin_acc[b] = margin_acc;
+  if (J->out_margin_cdf) J->out_margin_cdf[b] = margin_cdf;
+}
+
+static void* dtree_worker(void* arg) {
+  dtree_job* J = (dtree_job*)arg;
+  const size_t V = (size_t)J->V;
+  double* z = (double*)malloc(sizeof(double) * V);
+  double* P = (double*)malloc(sizeof(double) * V);
+  double* w = (double*)malloc(sizeof(double) * V);
+  unsigned char* removed = (unsigned char*)malloc(V);
+  for (int64_t b = J->b0; b < J->b1; ++b) dtree_one(J, b, z, P, w, removed);
+  free(z);
+  free(P);
+  free(w);
+  free(removed);
+  return NULL;
+}
+
+int orc_verify_tree_det(const void* p, int dtype, int64_t B, int N, int V, const int32_t* parent,
+                        const int32_t* node_tokens, double temperature, uint64_t seed, uint32_t step,
+                        int32_t* out_tokens, int32_t* out_path, int32_t* out_len, double* out_margin_acc,
+                        double* out_margin_cdf, int nthreads) {
+  if (!p || !parent || !node_tokens || !out_tokens || !out_path || !out_len) return -1;
+  if (B <= 0 || N <= 0 || V <= 0 || !(temperature >= 0.0)) return -1;
+  nthreads = clamp_threads(nthreads, B);
+  dtree_job* jobs = (dtree_job*)calloc((size_t)nthreads, sizeof(dtree_job));
+  for (int t = 0; t < nthreads; ++t) {
+    dtree_job* J = &jobs[t];
+    J->p = p;
+    J->dtype = dtype;
+    J->N = N;
+    J->V = V;
+    J->parent = parent;
+    J->tokens = node_tokens;
+    J->pr.temperature = temperature;
+    J->pr.seed = seed;
+    J->pr.step = step;
+    J->out_tokens = out_tokens;
+    J->out_path = out_path;
+    J->out_len = out_len;
+    J->out_margin_acc = out_margin_acc;
+    J->out_margin_cdf = out_margin_cdf;
+    J->b0 = B * t / nthreads;
+    J->b1 = B * (t + 1) / nthreads;
+  }
+  run_jobs(jobs, sizeof(dtree_job), nthreads, dtree_worker);
+  free(jobs);
+  return 0;
+}

@@ -598,3 +598,160 @@ def test_tree_draft_brute_force():
     qb[1, 6, 5] = np.nan  # a leaf row: still makes the request invalid
     g = oracle.tree_draft(qb, parent, 1.0)
     assert np.all(g[1] == -1) and np.all(g[0] >= 0)
+
+
+# ------------------------------------------- Tree Sampler (deterministic) --
+def _brute_candidates(q, cands, nodes, T):
+    """Every prefix over the top-`cands` tokens of each position, sorted by the
+    recursive key (-log score, length, key of the parent, rank), first `nodes`."""
+    K, V = q.shape
+    z = q.astype(np.float64) / T
+    lq = z - sp_logsumexp(z, axis=1, keepdims=True)
+    ranks = [sorted(range(V), key=lambda j, i=i: (-z[i, j], j))[:cands] for i in range(K)]
+    keys = {(): ()}
+    score = {(): 0.0}
+    items = []
+    frontier = [()]
+    for length in range(1, K + 1):
+        nxt = []
+        for pre in frontier:
+            for r in range(cands):
+                path = pre + (r,)
+                score[path] = score[pre] + lq[length - 1, ranks[length - 1][r]]
+                keys[path] = (-score[path], length, keys[pre], r)
+                items.append(path)
+                nxt.append(path)
+        frontier = nxt
+    items.sort(key=lambda p: keys[p])
+    kept = items[:nodes]
+    pos = {p: n for n, p in enumerate(kept)}
+    parent = [pos[p[:-1]] if len(p) > 1 else -1 for p in kept]
+    tokens = [ranks[len(p) - 1][p[-1]] for p in kept]
+    return np.array(parent), np.array(tokens)
+
+
+@pytest.mark.parametrize("K,cands,nodes,seed", [(3, 3, 10, 0), (4, 2, 12, 1), (2, 4, 9, 2), (3, 3, 27, 3),
+                                                (5, 2, 20, 4)])
+def test_tree_candidates_brute_force(K, cands, nodes, seed):
+    """The best-first enumeration keeps exactly the first `nodes` prefixes of
+    the stated order, as a sort of every prefix does."""
+    rng = np.random.default_rng(seed)
+    V = 7
+    q = rng.normal(0.0, 2.0, (3, K, V)).astype(np.float32)
+    par, tok, mg = oracle.tree_candidates(q, cands, nodes, 0.8)
+    for b in range(3):
+        bp, bt = _brute_candidates(q[b], cands, nodes, np.float64(0.8))
+        assert np.array_equal(par[b], bp) and np.array_equal(tok[b], bt)
+        assert mg[b] > 0.0
+
+
+def test_tree_candidates_special_cases():
+    rng = np.random.default_rng(9)
+    q = rng.normal(0.0, 2.0, (2, 4, 50)).astype(np.float32)
+    # one position: its top tokens in order, all children of the root
+    par, tok, _ = oracle.tree_candidates(q[:, :1], 6, 5, 1.0)
+    for b in range(2):
+        order = sorted(range(50), key=lambda j: (-q[b, 0, j], j))
+        assert list(tok[b]) == order[:5] and list(par[b]) == [-1] * 5
+    # one candidate per position: the chain of per-position argmaxes
+    par, tok, _ = oracle.tree_candidates(q, 1, 4, 1.0)
+    for b in range(2):
+        assert list(par[b]) == [-1, 0, 1, 2]
+        assert list(tok[b]) == [int(np.argmax(q[b, i])) for i in range(4)]
+    # more nodes than prefixes exist: the rest are -1
+    par, tok, _ = oracle.tree_candidates(q[:, :2], 2, 9, 1.0)
+    assert (par[:, 6:] == -1).all() and (tok[:, 6:] == -1).all() and (par[:, :6] >= -1).all()
+    # invariants: parent before child, scores non-increasing
+    par, tok, _ = oracle.tree_candidates(q, 8, 40, 0.7)
+    z = q.astype(np.float64) / np.float64(0.7)
+    lq = z - sp_logsumexp(z, axis=2, keepdims=True)
+    for b in range(2):
+        depth, sc = [], []
+        for n in range(40):
+            assert -1 <= par[b, n] < n
+            d = 0 if par[b, n] < 0 else depth[par[b, n]] + 1
+            depth.append(d)
+            sc.append((0.0 if par[b, n] < 0 else sc[par[b, n]]) + lq[b, d, tok[b, n]])
+        assert all(sc[n] >= sc[n + 1] - 1e-12 for n in range(39))
+
+
+def test_tree_candidates_ties():
+    """Equal logits: siblings are ordered by token id, and a parent's equal-score
+    child comes after it (the kept set stays prefix-closed)."""
+    q = np.zeros((1, 3, 5), dtype=np.float32)  # every token equally likely at every position
+    par, tok, _ = oracle.tree_candidates(q, 2, 6, 1.0)
+    bp, bt = _brute_candidates(q[0], 2, 6, np.float64(1.0))
+    assert np.array_equal(par[0], bp) and np.array_equal(tok[0], bt)
+    assert list(par[0]) == [-1, -1, 0, 0, 1, 1] and list(tok[0]) == [0, 1, 0, 1, 0, 1]
+
+
+def test_tree_det_chain_equals_linear_point_mass():
+    """A chain of deterministic candidates is linear verification with drafts
+    that are point masses at those tokens: same decisions, same draws (the
+    draw ids coincide), bit for bit."""
+    rng = np.random.default_rng(5)
+    B, K, V = 6, 4, 40
+    p = rng.normal(0.0, 2.0, (B, K + 1, V)).astype(np.float32)
+    toks = rng.integers(0, V, (B, K)).astype(np.int32)
+    p[np.arange(B)[:, None], np.arange(K)[None, :], toks] += 6.0  # let many drafts be accepted
+    q = np.full((B, K, V), -np.inf, dtype=np.float32)
+    q[np.arange(B)[:, None], np.arange(K)[None, :], toks] = 0.0
+    parent = np.tile(np.arange(-1, K - 1, dtype=np.int32), (B, 1))
+    lens = []
+    for step in range(8):
+        for T in (1.0, 0.6):
+            d = oracle.verify_tree_det(p, parent, toks, T, seed=3, step=step)
+            lin = oracle.verify_linear(p, q, toks, T, seed=3, step=step)
+            assert np.array_equal(d["len"], lin["len"])
+            assert np.array_equal(d["tokens"][:, :K + 1], lin["tokens"])
+            lens.extend(d["len"].tolist())
+    assert len(set(lens)) >= 3
+
+
+def test_tree_det_first_token_law():
+    """Root with three deterministic candidates (one of them at a -inf logit):
+    the first emitted token follows P_root, and after candidate c the next one
+    follows the row of c (lossless, chi-square over 20,000 draws)."""
+    rng = np.random.default_rng(11)
+    V = 6
+    p = rng.normal(0.0, 1.0, (1, 4, V)).astype(np.float32)
+    p[0, 0, 5] = -np.inf
+    parent = np.array([[-1, -1, -1]], dtype=np.int32)
+    toks = np.array([[2, 0, 5]], dtype=np.int32)
+    P0 = probs(p[0, 0])
+    n = 20000
+    first = np.zeros(V)
+    second = {c: np.zeros(V) for c in range(3)}
+    reps = 200
+    pr = np.repeat(p, reps, axis=0)
+    par = np.repeat(parent, reps, axis=0)
+    tk = np.repeat(toks, reps, axis=0)
+    for step in range(n // reps):
+        o = oracle.verify_tree_det(pr, par, tk, 1.0, seed=7, step=step)
+        for b in range(reps):
+            first[o["tokens"][b, 0]] += 1
+            if o["len"][b] == 1:
+                second[o["path"][b, 0]][o["tokens"][b, 1]] += 1
+    assert first[5] == 0
+    assert chi2_pvalue(first, n * P0) > 1e-3
+    for c in range(2):
+        m = second[c].sum()
+        assert m > 500
+        assert chi2_pvalue(second[c], m * probs(p[0, c + 1])) > 1e-3
+
+
+def test_tree_det_greedy_and_errors():
+    rng = np.random.default_rng(2)
+    V = 9
+    p = rng.normal(0.0, 1.0, (3, 4, V)).astype(np.float32)
+    g0 = [int(np.argmax(p[b, 0])) for b in range(3)]
+    parent = np.array([[-1, -1, 1]] * 3, dtype=np.int32)
+    toks = np.array([[(g0[0] + 1) % V, g0[0], 3], [(g0[1] + 1) % V, (g0[1] + 2) % V, 1], [0, 1, 2]],
+                    dtype=np.int32)
+    parent[2, 2] = 2  # malformed: parent not before the node
+    o = oracle.verify_tree_det(p, parent, toks, 0.0)
+    assert o["len"][0] >= 1 and o["path"][0, 0] == 1 and o["tokens"][0, 0] == g0[0]
+    g2 = int(np.argmax(p[0, 2]))
+    assert o["tokens"][0, 1] == (3 if g2 == 3 else g2) and o["len"][0] == (2 if g2 == 3 else 1)
+    assert o["len"][1] == 0 and o["tokens"][1, 0] == g0[1]
+    assert o["len"][2] == -1 and (o["tokens"][2] == -1).all()
