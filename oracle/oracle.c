@@ -847,10 +847,11 @@ int orc_verify_tree(const void* p, const void* q, int dtype, int64_t B, int N, i
  * parent[n] the node of its parent (-1 for length 1), tokens[n] its last
  * token, so parent[n] < n. Enumerated best first: at each step every kept
  * prefix (and the empty one) offers its best child not yet kept, and the best
- * offer in the order is kept. *margin = the smallest log-score gap between
- * the kept offer and any other offer of the same step (0 for exact ties
- * across parents). A request with an invalid draft row gets -1 in every
- * parent and token. */
+ * offer in the order is kept; a prefix of probability zero is never kept
+ * (nodes past the last prefix of positive probability get -1). *margin = the
+ * smallest log-score gap between the kept offer and any other offer of the
+ * same step (0 for exact ties across parents). A request with an invalid
+ * draft row gets -1 in every parent and token. */
 typedef struct {
   const void* q;
   int dtype, K, V, cands, nodes;
@@ -905,6 +906,7 @@ static void* cand_worker(void* arg) {
       for (int s = 0; s <= n; ++s) {
         if (depth[s] >= K || next[s] >= C) continue; /* nothing to offer */
         const double o = ls[s] + clq[depth[s] * C + next[s]];
+        if (isinf(o)) continue; /* zero probability: never kept (later ranks are no better) */
         int better;
         if (best < 0) better = 1;
         else if (o != bls) better = o > bls;
@@ -922,7 +924,7 @@ static void* cand_worker(void* arg) {
       for (int s = 0; s <= n; ++s) {
         if (s == best || depth[s] >= K || next[s] >= C) continue;
         const double gap = bls - (ls[s] + clq[depth[s] * C + next[s]]);
-        if (gap < margin) margin = gap;
+        if (gap < margin) margin = gap; /* an offer of zero probability gives +inf */
       }
       par[n] = best - 1;
       tok[n] = ctok[depth[best] * C + next[best]];

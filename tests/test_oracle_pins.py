@@ -661,6 +661,12 @@ def test_tree_candidates_special_cases():
     # more nodes than prefixes exist: the rest are -1
     par, tok, _ = oracle.tree_candidates(q[:, :2], 2, 9, 1.0)
     assert (par[:, 6:] == -1).all() and (tok[:, 6:] == -1).all() and (par[:, :6] >= -1).all()
+    # prefixes of probability zero are never kept: two finite tokens per position
+    q2 = np.full((1, 2, 6), -np.inf, dtype=np.float32)
+    q2[0, :, :2] = [[1.0, 0.5], [0.0, -1.0]]
+    par, tok, _ = oracle.tree_candidates(q2, 4, 9, 1.0)
+    # log scores: [0] -0.474, [0,0] -0.787, [1] -0.974, [1,0] -1.287, [0,1] -1.787, [1,1] -2.287
+    assert list(par[0]) == [-1, 0, -1, 2, 0, 2, -1, -1, -1] and list(tok[0]) == [0, 0, 1, 0, 1, 1, -1, -1, -1]
     # invariants: parent before child, scores non-increasing
     par, tok, _ = oracle.tree_candidates(q, 8, 40, 0.7)
     z = q.astype(np.float64) / np.float64(0.7)
