@@ -73,7 +73,7 @@ def lib():
                                           ctypes.c_int, P, P, P, ctypes.c_int]
         L.orc_tree_candidates.restype = ctypes.c_int
         L.orc_verify_tree_det.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, P, f64, u64, u32,
-                                          P, P, P, P, P, ctypes.c_int]
+                                          P, P, P, P, P, P, ctypes.c_int, ctypes.c_int]
         L.orc_verify_tree_det.restype = ctypes.c_int
         del i32
         _lib = L
@@ -249,10 +249,13 @@ def tree_candidates(q, cands, nodes, temperature, nthreads=1):
     return par, tok, mg
 
 
-def verify_tree_det(p, parent, node_tokens, temperature, seed=0, step=0, nthreads=1):
+def verify_tree_det(p, parent, node_tokens, temperature, seed=0, step=0, u_override=None, max_children=None,
+                    nthreads=1):
     """Verification of deterministic candidates: p [B, N+1, V], per-request
-    parent [B, N] and node_tokens [B, N]. Returns a dict with tokens [B, N+1],
-    path [B, N], len [B], margin_acc, margin_cdf."""
+    parent [B, N] and node_tokens [B, N]. u_override: optional
+    [B, N+1, 1+max_children] uniforms (slot 0 final draw, slot 1+j accept test
+    of child j) replacing the Philox stream. Returns a dict with tokens
+    [B, N+1], path [B, N], len [B], margin_acc, margin_cdf."""
     p = np.ascontiguousarray(p)
     B, R, V = p.shape
     N = R - 1
@@ -263,9 +266,13 @@ def verify_tree_det(p, parent, node_tokens, temperature, seed=0, step=0, nthread
     ln = np.zeros(B, dtype=np.int32)
     ma = np.zeros(B, dtype=np.float64)
     mc = np.zeros(B, dtype=np.float64)
+    ovr, maxC = None, 0
+    if u_override is not None:
+        maxC = int(max_children)
+        ovr = np.ascontiguousarray(u_override, dtype=np.float64).reshape(B, N + 1, 1 + maxC)
     rc = lib().orc_verify_tree_det(_ptr(p), _dtype_code(p), B, N, V, _ptr(par), _ptr(nt), float(temperature),
                                    int(seed), int(step), _ptr(toks), _ptr(path), _ptr(ln), _ptr(ma), _ptr(mc),
-                                   int(nthreads))
+                                   _ptr(ovr), maxC, int(nthreads))
     if rc != 0:
         raise ValueError("orc_verify_tree_det rejected its arguments")
     return dict(tokens=toks, path=path, len=ln, margin_acc=ma, margin_cdf=mc)

@@ -995,6 +995,8 @@ typedef struct {
   orc_params pr;
   int32_t *out_tokens, *out_path, *out_len;
   double *out_margin_acc, *out_margin_cdf;
+  const double* ovr; /* [B][N+1][1+maxC]: slot 0 = d=0, slot 1+j = d=1+j */
+  int maxC;
   int64_t b0, b1;
 } dtree_job;
 
@@ -1045,7 +1047,8 @@ static void dtree_one(dtree_job* J, int64_t b, double* z, double* P, double* w, 
       for (int c = 0; c < N; ++c) {
         if (par[c] != row - 1) continue;
         const int tk = ntk[c];
-        const double u = orc_uniform(pr->seed, pr->step, (uint32_t)b, (uint32_t)row, 1u + (uint32_t)j);
+        const double u = uni(pr, b, row, 1u + (uint32_t)j, J->ovr,
+                             J->ovr ? (size_t)((b * R + row) * (1 + J->maxC) + 1 + j) : 0);
         const double pt = removed[tk] ? 0.0 : P[tk];
         if (1.0 - E > 0.0) {
           const double mg = fabs(u - pt / (1.0 - E));
@@ -1067,7 +1070,7 @@ static void dtree_one(dtree_job* J, int64_t b, double* z, double* P, double* w, 
           w[t] = removed[t] ? 0.0 : P[t];
           S += w[t];
         }
-        const double u = orc_uniform(pr->seed, pr->step, (uint32_t)b, (uint32_t)row, 0u);
+        const double u = uni(pr, b, row, 0u, J->ovr, J->ovr ? (size_t)((b * R + row) * (1 + J->maxC)) : 0);
         double mg;
         y = orc_sample(S > 0.0 ? w : P, V, u, &mg);
         if (mg < margin_cdf) margin_cdf = mg;
@@ -1103,9 +1106,18 @@ static void* dtree_worker(void* arg) {
 int orc_verify_tree_det(const void* p, int dtype, int64_t B, int N, int V, const int32_t* parent,
                         const int32_t* node_tokens, double temperature, uint64_t seed, uint32_t step,
                         int32_t* out_tokens, int32_t* out_path, int32_t* out_len, double* out_margin_acc,
-                        double* out_margin_cdf, int nthreads) {
+                        double* out_margin_cdf, const double* u_override, int maxC, int nthreads) {
   if (!p || !parent || !node_tokens || !out_tokens || !out_path || !out_len) return -1;
   if (B <= 0 || N <= 0 || V <= 0 || !(temperature >= 0.0)) return -1;
+  if (u_override) {
+    /* every row's child count must fit the override table */
+    for (int64_t b = 0; b < B; ++b)
+      for (int r = 0; r <= N; ++r) {
+        int nc = 0;
+        for (int c = 0; c < N; ++c) nc += parent[b * N + c] == r - 1;
+        if (nc > maxC) return -1;
+      }
+  }
   nthreads = clamp_threads(nthreads, B);
   dtree_job* jobs = (dtree_job*)calloc((size_t)nthreads, sizeof(dtree_job));
   for (int t = 0; t < nthreads; ++t) {
@@ -1124,6 +1136,8 @@ int orc_verify_tree_det(const void* p, int dtype, int64_t B, int N, int V, const
     J->out_len = out_len;
     J->out_margin_acc = out_margin_acc;
     J->out_margin_cdf = out_margin_cdf;
+    J->ovr = u_override;
+    J->maxC = maxC;
     J->b0 = B * t / nthreads;
     J->b1 = B * (t + 1) / nthreads;
   }

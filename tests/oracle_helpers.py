@@ -163,3 +163,34 @@ class FastTree:
         assert rc == 0
         n = int(self.olen[0])
         return n, tuple(int(t) for t in self.otok[0, :n + 1]), tuple(int(x) for x in self.opath[0, :n])
+
+
+class FastDetTree:
+    """Repeated oracle calls of the verification of deterministic candidates
+    (one request) on fixed logits and tree, with uniform overrides."""
+
+    def __init__(self, p, parent, max_children, temperature=1.0):
+        self.p = np.ascontiguousarray(p)
+        _, R, self.V = self.p.shape
+        self.N = R - 1
+        self.parent = np.ascontiguousarray(parent, dtype=np.int32).reshape(1, self.N)
+        self.maxC = int(max_children)
+        self.T = float(temperature)
+        self.tokens = np.zeros((1, self.N), dtype=np.int32)
+        self.otok = np.zeros((1, self.N + 1), dtype=np.int32)
+        self.opath = np.zeros((1, self.N), dtype=np.int32)
+        self.olen = np.zeros(1, dtype=np.int32)
+        self.ovr = np.zeros((1, R, 1 + self.maxC), dtype=np.float64)
+        self.dtype = oracle._dtype_code(self.p)
+
+    def run(self, tokens, ovr):
+        self.tokens[...] = np.asarray(tokens, dtype=np.int32).reshape(1, self.N)
+        self.ovr[...] = ovr
+        P = ctypes.c_void_p
+        rc = oracle.lib().orc_verify_tree_det(
+            self.p.ctypes.data_as(P), self.dtype, 1, self.N, self.V, self.parent.ctypes.data_as(P),
+            self.tokens.ctypes.data_as(P), self.T, 0, 0, self.otok.ctypes.data_as(P), self.opath.ctypes.data_as(P),
+            self.olen.ctypes.data_as(P), None, None, self.ovr.ctypes.data_as(P), self.maxC, 1)
+        assert rc == 0
+        n = int(self.olen[0])
+        return n, tuple(int(t) for t in self.otok[0, :n + 1]), tuple(int(x) for x in self.opath[0, :n])

@@ -15,7 +15,8 @@ from scipy.special import logsumexp as sp_logsumexp
 
 import oracle
 import synth
-from oracle_helpers import (FastLinear, FastTree, alpha, chi2_pvalue, probs, residual, step_measure, threshold)
+from oracle_helpers import (FastDetTree, FastLinear, FastTree, alpha, chi2_pvalue, probs, residual, step_measure,
+                            threshold)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -744,6 +745,66 @@ def test_tree_det_first_token_law():
         m = second[c].sum()
         assert m > 500
         assert chi2_pvalue(second[c], m * probs(p[0, c + 1])) > 1e-3
+
+
+@pytest.mark.parametrize("toks", [(2, 5, 1), (3, 3, 4), (0, 0, 0), (6, 7, 6), (4, 1, 2)])
+def test_tree_det_root_exact(toks):
+    """Exact enumeration over the uniforms (bisection on each accept test,
+    measure of each final token over the final uniform): for a root with three
+    fixed candidates, repeated tokens included (token 7's logit is -inf), the
+    first emitted token follows P_root exactly; below an accepted first child
+    with one fixed grandchild, the next token follows that child's row."""
+    V = 8
+    rng = np.random.default_rng(13)
+    parent = np.array([-1, -1, -1, 0, 1, 2], dtype=np.int32)
+    N = len(parent)
+    p = rng.normal(0.0, 1.2, (1, N + 1, V)).astype(np.float32)
+    p[0, 0, 7] = -np.inf
+    P = [probs(p[0, r]) for r in range(N + 1)]
+    HI = np.nextafter(1.0, 0.0)
+    ft = FastDetTree(p, parent, max_children=3)
+
+    def ovr_of(ua, uf_root, child_u=0.5, child_uf=0.5):
+        o = np.zeros((1, N + 1, 4))
+        o[0, 0, 1:4] = ua
+        o[0, 0, 0] = uf_root
+        o[0, 1:, 1] = child_u
+        o[0, 1:, 0] = child_uf
+        return o
+
+    tk = [toks[0], toks[1], toks[2], 0, 0, 0]
+
+    def took(ua, node):
+        path = ft.run(tk, ovr_of(ua, 0.5))[2]
+        return len(path) >= 1 and path[0] == node
+
+    r_a = threshold(lambda u: took([u, HI, HI], 0))
+    r_b = threshold(lambda u: took([HI, u, HI], 1))
+    r_c = threshold(lambda u: took([HI, HI, u], 2))
+    first = np.zeros(V)
+    first[toks[0]] += r_a
+    first[toks[1]] += (1 - r_a) * r_b
+    first[toks[2]] += (1 - r_a) * (1 - r_b) * r_c
+    rest = (1 - r_a) * (1 - r_b) * (1 - r_c)
+    if rest > 0:
+        for t, m in step_measure(lambda u: ft.run(tk, ovr_of([HI, HI, HI], u))[1][0]).items():
+            first[t] += rest * m
+    assert np.max(np.abs(first - P[0])) < 1e-12
+    if toks[1] == toks[0]:
+        assert r_b == 0.0  # a rejected token has probability 0 for its later siblings
+
+    # second level: below an accepted child 0 (row 1), its fixed child node 3
+    second = np.zeros(V)
+    for g in range(V):
+        tk2 = [toks[0], toks[1], toks[2], g, 0, 0]
+        r_g = threshold(lambda u: ft.run(tk2, ovr_of([0.0, HI, HI], 0.5, child_u=u))[0] >= 2)
+        sec = np.zeros(V)
+        sec[g] += r_g
+        if r_g < 1:
+            meas = step_measure(lambda u: ft.run(tk2, ovr_of([0.0, HI, HI], 0.5, child_u=HI, child_uf=u))[1][1])
+            for t, m in meas.items():
+                sec[t] += (1 - r_g) * m
+        assert np.max(np.abs(sec - P[1])) < 1e-12, g
 
 
 def test_tree_det_greedy_and_errors():
