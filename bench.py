@@ -198,6 +198,36 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed):
          Bt * (Nt + 1), {"note": "latency-bound: 10 kernel launches per call"})
     del copies, ws
     torch.cuda.empty_cache()
+
+    # Tree Sampler: candidates from q [4, 16, 151936] (32 per position, 32 kept
+    # prefixes), then their verification against p [4, 33, 151936], bf16, T=1;
+    # six input copies rotate (60 MB each).
+    w = synth.WORKLOADS["treesampler"]
+    Bs, Ks, Cs, Ns, Vs = w["B"], w["K"], w["cands"], w["nodes"], w["V"]
+    copies = []
+    for c in range(6):
+        p, q = synth.treesampler_inputs(seed=seed + c)
+        copies.append((to_dev(p, torch, dev), to_dev(q, torch, dev)))
+    wsc = torch.empty(psi.workspace_bytes(Bs, Ks, Vs, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+    wsv = torch.empty(psi.workspace_bytes(Bs, Ns + 1, Vs, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+    cand = dict(parent=torch.empty((Bs, Ns), dtype=torch.int32, device=dev),
+                tokens=torch.empty((Bs, Ns), dtype=torch.int32, device=dev))
+    outs = dict(tokens=torch.empty((Bs, Ns + 1), dtype=torch.int32, device=dev),
+                path=torch.empty((Bs, Ns), dtype=torch.int32, device=dev),
+                len=torch.empty((Bs,), dtype=torch.int32, device=dev))
+    Ts = float(np.float32(w["temperature"]))
+
+    def sampler_step(i):
+        p_, q_ = copies[i % 6]
+        psi.tree_candidates(q_, Cs, Ns, temperature=Ts, out=cand, workspace=wsc, stream=stream)
+        psi.verify_tree_det(p_, cand["parent"], cand["tokens"], temperature=Ts, seed=seed, step=i, out=outs,
+                            workspace=wsv, stream=stream)
+
+    ms = time_calls(torch, sampler_step, steps, 5, stream)
+    line("treesampler_16_32_32_B4_V151936_bf16", ms, (Bs * Ks + Bs * (Ns + 1)) * Vs * 2, Bs * (Ks + Ns + 1),
+         {"note": "candidates (4 launches) + verification of deterministic candidates (4 launches)"})
+    del copies, wsc, wsv
+    torch.cuda.empty_cache()
     return res
 
 

@@ -131,6 +131,8 @@ typedef struct psispec_params {
  *   psispec_draft_sample   rows_per_req = K
  *   psispec_verify_linear  rows_per_req = 2*K + 1
  *   psispec_verify_tree    rows_per_req = 2*(N + 1)
+ *   psispec_tree_candidates rows_per_req = K
+ *   psispec_verify_tree_det rows_per_req = N + 1
  * Returns 0 for arguments out of range. Pure host function.
  */
 size_t psispec_workspace_bytes(int64_t B, int32_t rows_per_req, int32_t V, int dtype);
@@ -212,6 +214,70 @@ int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, i
                         int32_t V, const int32_t* parent, int32_t* node_tokens,
                         const psispec_params* params, int32_t* out_tokens, int32_t* out_path,
                         int32_t* out_len, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Tree Sampler candidates (Uno explainer §3.4 "Tree Sampler": every draft
+ * position keeps its top-K tokens and only the most probable prefixes over
+ * them are verified in one pass; §6.3 uses block 16, K = 32 and 32 kept
+ * prefixes). The pages give no formula; this call computes, per request:
+ *   q_i = softmax(q_logits_i / T) over the full row, for position i < K;
+ *   C_i = the `cands` tokens of largest q_i (ties: lower id first), rank 0 first;
+ *   score(t_0 .. t_{l-1}) = sum_i log q_i(t_i), t_i in C_i, l <= K;
+ *   the kept prefixes: the first `nodes` in the order score descending, then
+ *   length ascending, then the position of the parent prefix in this same
+ *   order (the empty prefix first), then the rank of the last token in C.
+ * A parent's score is at least its child's, so the kept set is closed under
+ * taking prefixes. Prefixes of probability zero are never kept.
+ *   q_logits     [B, K, V] draft logits (K draft positions, K <= 64).
+ *   params       temperature > 0 (no greedy mode); top_k / top_p must be
+ *                disabled (0 and 1); seed, step and flags are not used.
+ *   cands        tokens per position, 1 <= cands <= min(V, PSISPEC_MAX_TOPK),
+ *                K * cands <= PSISPEC_MAX_CAND_ENTRIES.
+ *   nodes        kept prefixes, 1 <= nodes <= PSISPEC_MAX_TREE_NODES.
+ *   out_parent   [B, nodes] int32 out: node n is the n-th kept prefix; its
+ *                parent is the node of its prefix one shorter (-1 at length 1),
+ *                so out_parent[b, n] < n.
+ *   out_tokens   [B, nodes] int32 out: the last token of prefix n.
+ * Nodes past the last prefix of positive probability, and every node of a
+ * request with an invalid draft row, get -1 in both outputs.
+ * Workspace: psispec_workspace_bytes(B, K, V, dtype).
+ */
+#define PSISPEC_MAX_CAND_ENTRIES 4096 /* K * cands */
+int psispec_tree_candidates(const void* q_logits, int dtype, int64_t B, int32_t K, int32_t V,
+                            const psispec_params* params, int32_t cands, int32_t nodes, int32_t* out_parent,
+                            int32_t* out_tokens, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Verification of deterministic candidates, one tree per request (Uno
+ * explainer §3.4 "Tree Sampler": the candidates are chosen, not drawn, so the
+ * draft-ratio test of psispec_verify_tree does not apply; the pages state no
+ * rule for them and this is the plain lossless one for point-mass proposals).
+ * At a row with children c_0 < c_1 < ... (ascending node id), r = P =
+ * softmax(p_row / T) and E = 0; child j with token tok is accepted iff
+ *   U(seed, step, b, row, 1 + j) * (1 - E) < P(tok),
+ * with P(tok) counted as 0 when tok was already rejected at this row; after a
+ * rejection tok is removed from r (E += P(tok)). The walk descends into the
+ * first accepted child; at a leaf, or once every child is rejected, the final
+ * token is an inverse-CDF draw in token-id order with U(seed, step, b, row, 0)
+ * from P without the removed tokens (from P itself if nothing remains).
+ * Greedy mode (T == 0): a child is accepted iff its token is the argmax of the
+ * row (lowest id on ties), and the final token is that argmax.
+ *   p_logits     [B, N+1, V] target logits; row 0 is the root context, row
+ *                n+1 the context after node n.
+ *   parent       [B, N] int32, per request: parent[b, n] in [-1, n-1].
+ *   node_tokens  [B, N] int32 candidate token of each node.
+ *   params       top_k / top_p must be disabled (0 and 1).
+ *   out_tokens   [B, N+1] int32 out: path tokens, the final token, -1 padding.
+ *   out_path     [B, N] int32 out: node ids of the accepted path, -1 padding.
+ *   out_len      [B] int32 out: accepted path length, or -1 for a request
+ *                error (a parent outside [-1, n-1], a token outside [0, V),
+ *                an invalid target row).
+ * Workspace: psispec_workspace_bytes(B, N + 1, V, dtype). N <= 256.
+ */
+int psispec_verify_tree_det(const void* p_logits, int dtype, int64_t B, int32_t N, int32_t V,
+                            const int32_t* parent, const int32_t* node_tokens, const psispec_params* params,
+                            int32_t* out_tokens, int32_t* out_path, int32_t* out_len, void* workspace,
+                            size_t ws_bytes, hipStream_t stream);
 
 /*
  * Benchmark timing hook (not part of the method; for measuring each kernel of

@@ -9,6 +9,8 @@ Function names mirror the C ABI in include/psispec.h:
   draft_sample   psispec_draft_sample
   verify_linear  psispec_verify_linear
   verify_tree    psispec_verify_tree
+  tree_candidates  psispec_tree_candidates
+  verify_tree_det  psispec_verify_tree_det
 """
 from __future__ import annotations
 
@@ -58,6 +60,12 @@ def _load():
     L.psispec_verify_tree.argtypes = [P, P, ctypes.c_int, i64, i32, i32, P, P, ctypes.POINTER(Params), P, P, P, P,
                                       sz, P]
     L.psispec_verify_tree.restype = ctypes.c_int
+    L.psispec_tree_candidates.argtypes = [P, ctypes.c_int, i64, i32, i32, ctypes.POINTER(Params), i32, i32, P, P,
+                                          P, sz, P]
+    L.psispec_tree_candidates.restype = ctypes.c_int
+    L.psispec_verify_tree_det.argtypes = [P, ctypes.c_int, i64, i32, i32, P, P, ctypes.POINTER(Params), P, P, P,
+                                          P, sz, P]
+    L.psispec_verify_tree_det.restype = ctypes.c_int
     L.psispec_strerror.argtypes = [ctypes.c_int]
     L.psispec_strerror.restype = ctypes.c_char_p
     L.psispec_version.argtypes = []
@@ -262,4 +270,49 @@ def verify_tree(p: torch.Tensor, q: torch.Tensor, parent, node_tokens, temperatu
                                  _ptr(out["len"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("psispec_verify_tree", rc)
     out["nodes"] = node_tokens
+    return out
+
+
+def tree_candidates(q: torch.Tensor, cands: int, nodes: int, temperature=1.0, out=None, workspace=None,
+                    stream=None) -> dict:
+    """psispec_tree_candidates. q [B, K, V] draft logits. Returns dict(parent
+    [B, nodes], tokens [B, nodes]) int32: the `nodes` most probable prefixes over
+    the top-`cands` tokens of every position, best first."""
+    assert q.is_cuda and q.is_contiguous() and q.dim() == 3
+    B, K, V = q.shape
+    dt = dtype_code(q)
+    if out is None:
+        out = dict(parent=torch.empty((B, nodes), dtype=torch.int32, device=q.device),
+                   tokens=torch.empty((B, nodes), dtype=torch.int32, device=q.device))
+    ws = _workspace(workspace, workspace_bytes(B, K, V, dt), q.device)
+    prm = make_params(temperature)
+    rc = lib.psispec_tree_candidates(_ptr(q), dt, B, K, V, ctypes.byref(prm), int(cands), int(nodes),
+                                     _ptr(out["parent"]), _ptr(out["tokens"]), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check("psispec_tree_candidates", rc)
+    return out
+
+
+def verify_tree_det(p: torch.Tensor, parent: torch.Tensor, node_tokens: torch.Tensor, temperature=1.0, seed=0,
+                    step=0, out=None, workspace=None, stream=None) -> dict:
+    """psispec_verify_tree_det. p [B, N+1, V]; parent and node_tokens [B, N]
+    int32 device tensors (one tree per request). Returns dict(tokens [B, N+1],
+    path [B, N], len [B])."""
+    assert p.is_cuda and p.is_contiguous() and p.dim() == 3
+    B, R, V = p.shape
+    N = R - 1
+    for t in (parent, node_tokens):
+        assert t.is_cuda and t.dtype == torch.int32 and t.is_contiguous() and t.shape == (B, N)
+    dt = dtype_code(p)
+    dev = p.device
+    if out is None:
+        out = dict(tokens=torch.empty((B, N + 1), dtype=torch.int32, device=dev),
+                   path=torch.empty((B, N), dtype=torch.int32, device=dev),
+                   len=torch.empty((B,), dtype=torch.int32, device=dev))
+    ws = _workspace(workspace, workspace_bytes(B, R, V, dt), dev)
+    prm = make_params(temperature, seed=seed, step=step)
+    rc = lib.psispec_verify_tree_det(_ptr(p), dt, B, N, V, _ptr(parent), _ptr(node_tokens), ctypes.byref(prm),
+                                     _ptr(out["tokens"]), _ptr(out["path"]), _ptr(out["len"]), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check("psispec_verify_tree_det", rc)
     return out

@@ -115,6 +115,7 @@ inline FiltCfg filt_cfg(const psispec_params* prm, void* ws, int64_t B, int32_t 
   f.stride = filt_stride(V);
   f.nchf = nchf_of(V);
   f.kk = prm->top_k;
+  f.by_rank = 0;
   f.T = (double)prm->temperature;
   f.top_p = (double)prm->top_p;
   return f;
@@ -300,6 +301,72 @@ int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, i
   if (params->temperature == 0.0f) e = launch_tree_greedy(c, tp, tc, dtype, stream);
   else if (filtered(params, V)) e = launch_tree_filtered(c, filt_cfg(params, workspace, B, rows, V, dtype), tp, tc, dtype, stream);
   else e = launch_tree_sampled(c, tp, tc, rounds, dtype, stream);
+  return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+}
+
+static_assert(PSISPEC_MAX_CAND_ENTRIES == kMaxCandEntries && PSISPEC_MAX_TOPK == kMaxTopK &&
+                  PSISPEC_MAX_TREE_NODES == kMaxNodes,
+              "public limits match the kernels");
+
+int psispec_tree_candidates(const void* q_logits, int dtype, int64_t B, int32_t K, int32_t V,
+                            const psispec_params* params, int32_t cands, int32_t nodes, int32_t* out_parent,
+                            int32_t* out_tokens, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!q_logits || !out_parent || !out_tokens || !workspace) return PSISPEC_EINVAL;
+  if (B <= 0 || K <= 0 || V <= 0 || cands <= 0 || nodes <= 0) return PSISPEC_EINVAL;
+  if (int rc = check_params(params, V)) return rc;
+  if (!(params->temperature > 0.0f)) return PSISPEC_EINVAL;
+  if (params->top_k != 0 || params->top_p != 1.0f) return PSISPEC_EUNSUPPORTED;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
+  if (K > PSISPEC_MAX_K || cands > V || cands > kMaxTopK || (int64_t)K * cands > kMaxCandEntries ||
+      nodes > kMaxNodes)
+    return PSISPEC_EUNSUPPORTED;
+  if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
+  if (ws_bytes < psispec_workspace_bytes(B, K, V, dtype)) return PSISPEC_EWORKSPACE;
+  LinCfg c;
+  fill_common(c, nullptr, q_logits, dtype, B, K, V, params, workspace, 0);
+  psispec_params fp = *params;
+  fp.top_k = cands;
+  FiltCfg f = filt_cfg(&fp, workspace, B, K, V, dtype);
+  f.by_rank = 1;
+  CandCfg cc;
+  cc.cands = cands;
+  cc.nodes = nodes;
+  cc.out_parent = out_parent;
+  cc.out_tokens = out_tokens;
+  timing_begin(stream);
+  const hipError_t e = launch_tree_candidates(c, f, cc, dtype, stream);
+  return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+}
+
+int psispec_verify_tree_det(const void* p_logits, int dtype, int64_t B, int32_t N, int32_t V,
+                            const int32_t* parent, const int32_t* node_tokens, const psispec_params* params,
+                            int32_t* out_tokens, int32_t* out_path, int32_t* out_len, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  if (!p_logits || !parent || !node_tokens || !out_tokens || !out_path || !out_len || !workspace)
+    return PSISPEC_EINVAL;
+  if (B <= 0 || N <= 0 || V <= 0) return PSISPEC_EINVAL;
+  if (int rc = check_params(params, V)) return rc;
+  if (params->top_k != 0 || params->top_p != 1.0f) return PSISPEC_EUNSUPPORTED;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
+  if (N > PSISPEC_MAX_TREE_NODES) return PSISPEC_EUNSUPPORTED;
+  if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
+  const int32_t rows = N + 1;
+  if (ws_bytes < psispec_workspace_bytes(B, rows, V, dtype)) return PSISPEC_EWORKSPACE;
+  LinCfg c;
+  fill_common(c, p_logits, nullptr, dtype, B, 0, V, params, workspace, rows);
+  c.out_len = out_len;
+  const Layout L = layout(B, rows, V, dtype);
+  char* w = (char*)workspace;
+  DTreeCfg d;
+  d.N = N;
+  d.parent = parent;
+  d.tokens = node_tokens;
+  d.out_tokens = out_tokens;
+  d.out_path = out_path;
+  d.state = w + L.ts;
+  d.rem = (int32_t*)(w + L.rst);
+  timing_begin(stream);
+  const hipError_t e = launch_verify_tree_det(c, d, dtype, stream);
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 

@@ -152,6 +152,28 @@ __device__ __forceinline__ double wave_sum4(double v0, double v1, double v2, dou
   return k;
 }
 
+// Orders the LDS accesses of one wave around this point (the wave's LDS
+// operations complete in issue order; this keeps the compiler from moving
+// them across it).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Maximum of an unsigned value over the wave, on every lane: within rows of 16
+// by shifts of 1, 2, 4, 8, across rows by the row broadcasts (as in
+// wave_incl_scan), then lane 63 is read.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, true));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
 __device__ __forceinline__ int wave_or(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o);

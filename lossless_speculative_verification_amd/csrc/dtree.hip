@@ -1,0 +1,506 @@
+// Tree Sampler on gfx950 ("Uno" research explainer, §3.4 Tree Sampler: every
+// draft position keeps its top-K tokens, only the most probable prefixes over
+// them are kept, and the resulting tree is verified in one pass; §6.3 uses
+// block 16, K = 32 and 32 kept prefixes).
+//
+// Candidates, per request:
+//   q_i = softmax(d_i / T), C_i = the `cands` most probable tokens of
+//   position i (ties: lower id), score of a prefix = sum of log q_i(t_i);
+//   keep the `nodes` best prefixes under (score desc, length asc, position of
+//   the parent prefix asc, rank of the last token asc).
+// Pipeline: k_stats32 (maximum and sum of every draft row, for log q), the
+// filter kernels with top_k = cands storing each kept set in rank order, then
+// k_cand_tree: one workgroup per request turns the kept sets into log q
+// values in LDS and one wave enumerates the prefixes best first (every kept
+// prefix offers its best child not yet kept; the best offer is kept).
+//
+// Verification of deterministic candidates (a point-mass proposal at tok is
+// accepted with probability r(tok)), per request with its own tree:
+//   at a row r = P, E = 0; children in ascending node id, child j accepted iff
+//   U(b, row, 1 + j) * (1 - E) < P(tok) (0 if tok was already removed), a
+//   rejection removes tok (E += P(tok)); the walk descends into the first
+//   accepted child; at a leaf or once every child is rejected the final token
+//   is drawn from P without the removed tokens with U(b, row, 0).
+// Pipeline: k_stats32 over the N + 1 target rows; k_dtree_walk (one workgroup
+// per request: row normalisers, every node's P(tok), sibling order and
+// uniforms in parallel, then the walk by one thread over LDS); k_dtree_pass
+// (sub-block sums of the final row with and without the removed tokens);
+// k_dtree_pick (inverse-CDF draw). Greedy: k_argmax then k_dtree_greedy.
+#include "rowops.hpp"
+
+namespace psi {
+
+namespace {
+
+constexpr int kSlots = kMaxNodes + 1;                       // the empty prefix, then one per node
+constexpr int kSlotsPerLane = (kSlots + kWave - 1) / kWave;  // slot s lives on lane s % 64
+
+// Unsigned key increasing with the double x; its upper 32 bits order the
+// values up to ties within 2^-20 relative.
+__device__ __forceinline__ uint32_t order_hi(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t k = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  return (uint32_t)(k >> 32);
+}
+
+__device__ __forceinline__ double rd_lane(double v, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+  return __hiloint2double(hi, lo);
+}
+
+// Row normaliser of one row from its statistics records: exact maximum m and
+// S ~ sum_t 2^((a_t - m) c). Returns false for an invalid row.
+__device__ __forceinline__ bool row_norm(const StatRec* rec, int nch, float c32, float* m_out, double* S_out) {
+  float m = -INFINITY;
+  for (int ch = 0; ch < nch; ++ch) m = fmaxnan(m, rec[ch].m);
+  double S = 0.0;
+  bool bad = isnan(m) || isinf(m);
+  if (!bad)
+    for (int ch = 0; ch < nch; ++ch) {
+      const StatRec r = rec[ch];
+      if (isnan(r.s)) bad = true;
+      else if (!is_neg_inf(r.m)) S += r.s * ::exp2(((double)r.m - (double)m) * (double)c32);
+    }
+  if (!(S > 0.0)) bad = true;
+  *m_out = m;
+  *S_out = S;
+  return !bad;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ candidates --
+// Selection state of slot s (0 = the empty prefix, n + 1 = node n) on lane
+// s % 64, register j = s / 64: its log score, length, the rank of its best
+// child not yet kept, that child's offer (-inf when none), and the log q of
+// the next two ranks at its child position (prefetched).
+__global__ __launch_bounds__(kWG) void k_cand_tree(LinCfg c, FiltCfg f, CandCfg cc) {
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  const int K = c.K, C = cc.cands, NN = cc.nodes;
+  __shared__ double s_lq[kMaxCandEntries];  // [K][C] log q of rank r at position i, -inf past the kept set
+  __shared__ double s_L[kMaxK];
+  __shared__ int s_cnt[kMaxK];
+  __shared__ int s_ent[kMaxNodes];  // entry (position * C + rank) of node n, -1 when not kept
+  __shared__ int s_par[kMaxNodes];
+  __shared__ int s_bad;
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  for (int i = t; i < K; i += kWG) {
+    const int64_t sr = b * K + i;
+    const FiltRow h = f.hdr[sr];
+    float m;
+    double S;
+    const bool ok = row_norm(c.st + sr * c.nch32, c.nch32, c.c32, &m, &S);
+    if (!ok || h.bad || h.cnt <= 0) atomicOr(&s_bad, 1);
+    // log of the full-row normaliser of z = a / T
+    s_L[i] = (double)m / f.T + ::log(S);
+    s_cnt[i] = h.cnt;
+  }
+  __syncthreads();
+  if (s_bad) {
+    for (int n = t; n < NN; n += kWG) {
+      cc.out_parent[b * NN + n] = -1;
+      cc.out_tokens[b * NN + n] = -1;
+    }
+    return;
+  }
+  const FiltEnt* ent = f.ent + b * K * (int64_t)f.stride;
+  for (int e = t; e < K * C; e += kWG) {
+    const int i = e / C, r = e - i * C;
+    s_lq[e] = r < s_cnt[i] ? ent[i * (int64_t)f.stride + r].z - s_L[i] : -INFINITY;
+  }
+  __syncthreads();
+  if (t >= kWave) return;
+
+  // ---- best-first enumeration by wave 0
+  auto lq_at = [&](int d, int r) { return r < C ? s_lq[d * C + r] : -INFINITY; };
+  // rank 0 and rank 1 of every position, lane d holding position d
+  const double lq0 = lane < K ? lq_at(lane, 0) : -INFINITY;
+  const double lq1 = lane < K ? lq_at(lane, 1) : -INFINITY;
+  double ls[kSlotsPerLane], off[kSlotsPerLane], nx1[kSlotsPerLane], nx2[kSlotsPerLane];
+  int dep[kSlotsPerLane], nxt[kSlotsPerLane];
+#pragma unroll
+  for (int j = 0; j < kSlotsPerLane; ++j) {
+    ls[j] = 0.0;
+    off[j] = -INFINITY;
+    nx1[j] = -INFINITY;
+    nx2[j] = -INFINITY;
+    dep[j] = 0;
+    nxt[j] = 0;
+  }
+  if (lane == 0) {  // the empty prefix: its children are the position-0 candidates
+    off[0] = lq_at(0, 0);
+    nx1[0] = lq_at(0, 1);
+    nx2[0] = lq_at(0, 2);
+  }
+  int n = 0;
+  for (; n < NN; ++n) {
+    // best offer of this lane: (score desc, length asc, slot asc)
+    double bo = -INFINITY;
+    int bk = 0x7fffffff, be = 0, bj = 0;
+#pragma unroll
+    for (int j = 0; j < kSlotsPerLane; ++j) {
+      const int key = dep[j] * 512 + lane + kWave * j;
+      const bool better = off[j] > bo || (off[j] == bo && off[j] > -INFINITY && key < bk);
+      if (better) {
+        bo = off[j];
+        bk = key;
+        be = dep[j] * C + nxt[j];
+        bj = j;
+      }
+    }
+    const bool valid = bo > -INFINITY;
+    const uint32_t hi = valid ? order_hi(bo) : 0u;
+    const uint32_t M = wave_max_u32(hi);
+    if (M == 0u) break;  // no prefix of positive probability is left
+    unsigned long long cand = __ballot(hi == M);
+    int w = __ffsll((long long)cand) - 1;
+    if (__popcll(cand) > 1) {  // upper words tie: compare in full
+      double wo = rd_lane(bo, w);
+      int wk = __builtin_amdgcn_readlane(bk, w);
+      cand &= cand - 1;
+      while (cand) {
+        const int l = __ffsll((long long)cand) - 1;
+        cand &= cand - 1;
+        const double o = rd_lane(bo, l);
+        const int k = __builtin_amdgcn_readlane(bk, l);
+        if (o > wo || (o == wo && k < wk)) {
+          w = l;
+          wo = o;
+          wk = k;
+        }
+      }
+    }
+    const double wo = rd_lane(bo, w);
+    const int wk = __builtin_amdgcn_readlane(bk, w);
+    const int ws = wk & 511, wd = wk >> 9;
+    if (lane == 0) {
+      s_par[n] = ws - 1;
+      s_ent[n] = __builtin_amdgcn_readlane(be, w);
+    }
+    // the kept slot offers its next child; the new slot (node n) its first
+    const int sn = n + 1;
+    const double f0 = rd_lane(lq0, min(wd + 1, kWave - 1));
+    const double f1 = rd_lane(lq1, min(wd + 1, kWave - 1));
+    const bool deeper = wd + 1 < K;
+#pragma unroll
+    for (int j = 0; j < kSlotsPerLane; ++j) {
+      if (lane == w && j == bj) {
+        ++nxt[j];
+        off[j] = ls[j] + nx1[j];
+        nx1[j] = nx2[j];
+        nx2[j] = lq_at(dep[j], nxt[j] + 2);
+      }
+      if (lane == (sn & (kWave - 1)) && j == (sn >> 6)) {
+        ls[j] = wo;
+        dep[j] = wd + 1;
+        nxt[j] = 0;
+        off[j] = deeper ? wo + f0 : -INFINITY;
+        nx1[j] = deeper ? f1 : -INFINITY;
+        nx2[j] = deeper ? lq_at(wd + 1, 2) : -INFINITY;
+      }
+    }
+  }
+  if (lane == 0)
+    for (int m = n; m < NN; ++m) {
+      s_par[m] = -1;
+      s_ent[m] = -1;
+    }
+  wave_sync();
+  for (int m = lane; m < NN; m += kWave) {
+    const int e = s_ent[m];
+    int tok = -1;
+    if (e >= 0) {
+      const int i = e / C, r = e - i * C;
+      tok = ent[i * (int64_t)f.stride + r].i;
+    }
+    cc.out_parent[b * NN + m] = s_par[m];
+    cc.out_tokens[b * NN + m] = tok;
+  }
+}
+
+// ---------------------------------------------------------- verification --
+// Walk outcome of one request, for the final-row pass and pick.
+struct DTreeState {
+  int32_t row;   // final row
+  int32_t len;   // accepted path length; -1 = request error (outputs written)
+  int32_t nrem;  // removed tokens (the final row's children when it has any)
+  int32_t pad;
+  float m;       // exact maximum of the final row
+  float pad2;
+};
+static_assert(sizeof(DTreeState) <= sizeof(TreeState), "DTreeState lives in the tree-state section");
+
+namespace {
+__device__ __forceinline__ const char* det_row(const LinCfg& c, int64_t b, int r) {
+  return c.rows.p + ((b * c.rows.np + r) * (int64_t)c.V) * c.rows.esz;
+}
+}  // namespace
+
+struct DTreeWs {
+  DTreeState* st;  // [B]
+  int32_t* rem;    // [B, N] removed tokens of the final row
+};
+
+// Validates the request and, for node n: parent row, token, sibling index j
+// (ascending node id among the children of that row), whether an earlier
+// sibling carries the same token, and the child lists in node order.
+// Returns false (after writing the request error) for a malformed request.
+__device__ bool det_topology(const LinCfg& c, const DTreeCfg& d, int64_t b, int* s_par, int* s_tok, int* s_sib,
+                             int* s_dup, int* s_off, int* s_kid, int* s_bad) {
+  const int t = threadIdx.x, N = d.N;
+  for (int n = t; n < N; n += kWG) {
+    const int p = d.parent[b * N + n], x = d.tokens[b * N + n];
+    if (p < -1 || p >= n || x < 0 || x >= c.V) atomicOr(s_bad, 1);
+    s_par[n] = p;
+    s_tok[n] = x;
+  }
+  for (int i = t; i <= N; i += kWG) d.out_tokens[b * (N + 1) + i] = -1;
+  for (int i = t; i < N; i += kWG) d.out_path[b * N + i] = -1;
+  __syncthreads();
+  if (*s_bad) {
+    if (t == 0) c.out_len[b] = -1;
+    return false;
+  }
+  // off[r] = nodes whose parent row is below r; sibling index and duplicates
+  for (int r = t; r <= N; r += kWG) {
+    int k = 0;
+    for (int m = 0; m < N; ++m) k += s_par[m] + 1 < r ? 1 : 0;
+    s_off[r] = k;
+  }
+  for (int n = t; n < N; n += kWG) {
+    const int p = s_par[n], x = s_tok[n];
+    int j = 0, dup = 0;
+    for (int m = 0; m < n; ++m)
+      if (s_par[m] == p) {
+        ++j;
+        dup |= s_tok[m] == x;
+      }
+    s_sib[n] = j;
+    s_dup[n] = dup;
+  }
+  __syncthreads();
+  for (int n = t; n < N; n += kWG) s_kid[s_off[s_par[n] + 1] + s_sib[n]] = n;
+  __syncthreads();
+  return true;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kWG) void k_dtree_walk(LinCfg c, DTreeCfg d, DTreeWs dw) {
+  using E = Elem<DT>;
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x, N = d.N, R = N + 1;
+  __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_sib[kMaxNodes], s_dup[kMaxNodes], s_kid[kMaxNodes];
+  __shared__ int s_off[kMaxNodes + 1];
+  __shared__ double s_P[kMaxNodes], s_u[kMaxNodes];
+  __shared__ float s_m[kMaxNodes + 1];
+  __shared__ double s_S[kMaxNodes + 1];
+  __shared__ int s_bad;
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  for (int r = t; r < R; r += kWG) {
+    float m;
+    double S;
+    if (!row_norm(c.st + (b * R + r) * (int64_t)c.nch32, c.nch32, c.c32, &m, &S)) atomicOr(&s_bad, 1);
+    s_m[r] = m;
+    s_S[r] = S;
+  }
+  if (!det_topology(c, d, b, s_par, s_tok, s_sib, s_dup, s_off, s_kid, &s_bad)) {
+    if (t == 0) dw.st[b] = DTreeState{0, -1, 0, 0, 0.0f, 0.0f};
+    return;
+  }
+  // P(tok) of every node at its parent row and the uniform of its test
+  for (int n = t; n < N; n += kWG) {
+    const int row = s_par[n] + 1;
+    const float a = E::load1(det_row(c, b, row), s_tok[n]);
+    s_P[n] = ::exp(((double)a - (double)s_m[row]) * c.invT - ::log(s_S[row]));
+    s_u[n] = c.rng.u((uint32_t)b, (uint32_t)row, kDrawAccept + (uint32_t)s_sib[n]);
+  }
+  __syncthreads();
+  if (t != 0) return;
+  int row = 0, len = 0, k0 = 0, nk = 0;
+  for (;;) {
+    k0 = s_off[row];
+    nk = (row < N ? s_off[row + 1] : N) - k0;
+    double E = 0.0;  // probability removed at this row
+    int acc = -1;
+    for (int k = 0; k < nk; ++k) {
+      const int n = s_kid[k0 + k];
+      const double pt = s_dup[n] ? 0.0 : s_P[n];
+      if (s_u[n] * (1.0 - E) < pt) {
+        acc = n;
+        break;
+      }
+      E += pt;
+    }
+    if (acc < 0) break;
+    d.out_path[b * N + len] = acc;
+    d.out_tokens[b * (N + 1) + len] = s_tok[acc];
+    ++len;
+    row = acc + 1;
+  }
+  for (int k = 0; k < nk; ++k) dw.rem[b * N + k] = s_tok[s_kid[k0 + k]];
+  dw.st[b] = DTreeState{row, len, nk, 0, s_m[row], 0.0f};
+}
+
+// Sub-block sums of the final row's weights 2^((a - m) c): res.sp without the
+// removed tokens, res.sq over the whole row. One wave per sub-block.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_dtree_pass(LinCfg c, DTreeCfg d, DTreeWs dw) {
+  constexpr int EPV = Elem<DT>::kPerVec;
+  constexpr int VPL = kSB / (kWave * EPV);
+  static_assert(VPL * EPV <= 32, "one mask bit per element of a lane");
+  const int64_t b = blockIdx.y;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int sb = blockIdx.x * kWaves + wave;
+  if (sb >= c.nsb) return;
+  const DTreeState s = dw.st[b];
+  if (s.len < 0) return;
+  const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
+  float x[VPL][EPV];
+  load_vecs<DT, AL, VPL, kWave>(det_row(c, b, s.row), c.V, c.nvec, vfirst, x);
+  // removed tokens held by this lane: element (vfirst + v * 64) * EPV + e is bit v * EPV + e
+  uint32_t gone = 0;
+  const int32_t* rem = dw.rem + b * d.N;
+  for (int k = 0; k < s.nrem; ++k) {
+    const int rel = rem[k] - sb * kSB;
+    if (rel >= 0 && rel < kSB) {
+      const int vec = rel / EPV;
+      if ((vec & (kWave - 1)) == lane) gone |= 1u << ((vec >> 6) * EPV + rel % EPV);
+    }
+  }
+  const WRow wr = wrow(DT == kBF16 && c.tab, s.m, c.c64);
+  double all = 0.0, kept = 0.0;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const double w = fweight<DT>(x[v][e], wr, c.c64, nullptr);
+      all += w;
+      kept += (gone >> (v * EPV + e)) & 1u ? 0.0 : w;
+    }
+  all = wave_sum(all);
+  kept = wave_sum(kept);
+  if (lane == 0) c.res[b * c.nsb + sb] = ResRec{kept, all, 0.0, 0.0};
+}
+
+template <int DT>
+__global__ __launch_bounds__(kWG) void k_dtree_pick(LinCfg c, DTreeCfg d, DTreeWs dw) {
+  using E = Elem<DT>;
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x, nsb = c.nsb, N = d.N;
+  const DTreeState s = dw.st[b];
+  if (s.len < 0) return;
+  __shared__ double sh[kWG + kWaves];
+  __shared__ int s_rem[kMaxNodes];
+  for (int k = t; k < s.nrem; k += kWG) s_rem[k] = dw.rem[b * N + k];
+  const ResRec* rr = c.res + b * nsb;
+  double mine = 0.0;
+  for (int sb = t; sb < nsb; sb += kWG) mine += rr[sb].sp;
+  const double W = block_sum(mine, sh);  // also orders the s_rem writes before their reads
+  const char* row = det_row(c, b, s.row);
+  const WRow wr = wrow(DT == kBF16 && c.tab, s.m, c.c64);
+  const double u = c.rng.u((uint32_t)b, (uint32_t)s.row, kDrawFinal);
+  int y;
+  if (W > 0.0) {
+    y = pick_index(
+        nsb, c.V, u * W, [&](int sb) { return rr[sb].sp; },
+        [&](int64_t j) {
+          for (int k = 0; k < s.nrem; ++k)
+            if (s_rem[k] == (int)j) return 0.0;
+          return fweight<DT>(E::load1(row, j), wr, c.c64, nullptr);
+        },
+        sh);
+  } else {  // every token of positive probability was removed: draw from P
+    double all = 0.0;
+    for (int sb = t; sb < nsb; sb += kWG) all += rr[sb].sq;
+    const double Wa = block_sum(all, sh);
+    y = pick_index(
+        nsb, c.V, u * Wa, [&](int sb) { return rr[sb].sq; },
+        [&](int64_t j) { return fweight<DT>(E::load1(row, j), wr, c.c64, nullptr); }, sh);
+  }
+  if (t == 0) {
+    d.out_tokens[b * (N + 1) + s.len] = y;
+    c.out_len[b] = s.len;
+  }
+}
+
+// Temperature 0: a child is accepted iff its token is its row's argmax.
+__global__ __launch_bounds__(kWG) void k_dtree_greedy(LinCfg c, DTreeCfg d) {
+  const int64_t b = blockIdx.x;
+  const int t = threadIdx.x, N = d.N, R = N + 1;
+  __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_sib[kMaxNodes], s_dup[kMaxNodes], s_kid[kMaxNodes];
+  __shared__ int s_off[kMaxNodes + 1];
+  __shared__ int s_g[kMaxNodes + 1];
+  __shared__ int s_bad;
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  for (int r = t; r < R; r += kWG) {
+    int bad;
+    s_g[r] = row_argmax(c.ar + (b * R + r) * (int64_t)c.nch32, c.nch32, &bad);
+    if (bad) atomicOr(&s_bad, 1);
+  }
+  if (!det_topology(c, d, b, s_par, s_tok, s_sib, s_dup, s_off, s_kid, &s_bad)) return;
+  if (t != 0) return;
+  int row = 0, len = 0;
+  for (;;) {
+    const int g = s_g[row];
+    const int k0 = s_off[row], nk = (row < N ? s_off[row + 1] : N) - k0;
+    int acc = -1;
+    for (int k = 0; k < nk && acc < 0; ++k)
+      if (s_tok[s_kid[k0 + k]] == g) acc = s_kid[k0 + k];
+    if (acc < 0) {
+      d.out_tokens[b * (N + 1) + len] = g;
+      break;
+    }
+    d.out_path[b * N + len] = acc;
+    d.out_tokens[b * (N + 1) + len] = g;
+    ++len;
+    row = acc + 1;
+  }
+  c.out_len[b] = len;
+}
+
+// ------------------------------------------------------------- launchers --
+template <int DT, bool AL>
+static hipError_t cand_t(const LinCfg& c, const FiltCfg& f, const CandCfg& cc, hipStream_t s) {
+  hipError_t e = launch_stats32(c, c.B * c.K, DT, s);
+  if (e != hipSuccess) return e;
+  e = launch_filter_rows(c, f, c.B * c.K, DT, s);
+  if (e != hipSuccess) return e;
+  PSI_LAUNCH(s, k_cand_tree, dim3((unsigned)c.B), dim3(kWG), c, f, cc);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_candidates(const LinCfg& c, const FiltCfg& f, const CandCfg& cc, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(cand_t, dtype, c.aligned, c, f, cc, s);
+}
+
+template <int DT, bool AL>
+static hipError_t dtree_t(const LinCfg& c, const DTreeCfg& d, hipStream_t s) {
+  const int64_t rows = c.B * (d.N + 1);
+  if (c.c64 == 0.0) {
+    hipError_t e = launch_argmax(c, rows, DT, s);
+    if (e != hipSuccess) return e;
+    PSI_LAUNCH(s, k_dtree_greedy, dim3((unsigned)c.B), dim3(kWG), c, d);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_stats32(c, rows, DT, s);
+  if (e != hipSuccess) return e;
+  DTreeWs dw;
+  dw.st = (DTreeState*)d.state;
+  dw.rem = d.rem;
+  PSI_LAUNCH(s, k_dtree_walk<DT>, dim3((unsigned)c.B), dim3(kWG), c, d, dw);
+  PSI_LAUNCH(s, (k_dtree_pass<DT, AL>), dim3((unsigned)((c.nsb + kWaves - 1) / kWaves), (unsigned)c.B), dim3(kWG),
+             c, d, dw);
+  PSI_LAUNCH(s, k_dtree_pick<DT>, dim3((unsigned)c.B), dim3(kWG), c, d, dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_tree_det(const LinCfg& c, const DTreeCfg& d, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(dtree_t, dtype, c.aligned, c, d, s);
+}
+
+}  // namespace psi

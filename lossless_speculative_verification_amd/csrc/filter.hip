@@ -479,10 +479,13 @@ __device__ void merge_row_wg(const LinCfg& c, const FiltCfg& f, int64_t sr) {
   const double S = block_sum(t < keep ? e : 0.0, shd);
   if (t == 0) *hdr = FiltRow{keep, 0, m, m + ::log(S)};
   if (t < keep) {
-    // position in token-id order
+    // position in token-id order (or the rank order of kept)
     const int id = kept[t].i;
-    int rank = 0;
-    for (int s = 0; s < keep; ++s) rank += kept[s].i < id ? 1 : 0;
+    int rank = t;
+    if (!f.by_rank) {
+      rank = 0;
+      for (int s = 0; s < keep; ++s) rank += kept[s].i < id ? 1 : 0;
+    }
     FiltEnt* out = f.ent + sr * (int64_t)f.stride;
     out[rank] = FiltEnt{id, 0, z};
   }
@@ -513,14 +516,6 @@ struct Top4 {
   __device__ __forceinline__ float nth(int j) const { return j == 1 ? t0 : j == 2 ? t1 : j == 3 ? t2 : t3; }
 };
 
-// Orders the LDS accesses of one wave around this point (the wave's LDS
-// operations complete in issue order; this keeps the compiler from moving
-// them across it).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // The top kk of cand[0 .. n) (n > kk, n <= R * 64) under (logit desc, id
 // asc), written unordered to out[0 .. kk): ts = the kk-th largest logit;
@@ -612,6 +607,13 @@ __device__ void finish_row_wave(const FiltCfg& f, int64_t sr, FiltCand* kept, in
   int id[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) id[q] = lane * 4 + q < keep ? kept[lane * 4 + q].i : 0;
+  FiltEnt* out = f.ent + sr * (int64_t)f.stride;
+  if (f.by_rank) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (lane * 4 + q < keep) out[lane * 4 + q] = FiltEnt{id[q], 0, z[q]};
+    return;
+  }
   wave_sync();
   const int keep8 = (keep + 7) & ~7;
   if (lane < keep8 - keep) kept[keep + lane].i = 0x7fffffff;
@@ -623,7 +625,6 @@ __device__ void finish_row_wave(const FiltCfg& f, int64_t sr, FiltCand* kept, in
 #pragma unroll
     for (int q = 0; q < 4; ++q) rank[q] += o < id[q] ? 1 : 0;
   }
-  FiltEnt* out = f.ent + sr * (int64_t)f.stride;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (lane * 4 + q < keep) out[rank[q]] = FiltEnt{id[q], 0, z[q]};

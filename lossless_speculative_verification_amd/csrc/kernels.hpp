@@ -86,7 +86,8 @@ struct ReqState {
   double pad[3];
 };
 
-// Filtered row: header and entries (token id order) of the kept set.
+// Filtered row: header and entries of the kept set (token-id order, or rank
+// order with FiltCfg::by_rank).
 struct FiltRow {
   int32_t cnt;  // kept tokens (0 for an invalid row)
   int32_t bad;  // NaN / +inf / all -inf
@@ -125,6 +126,7 @@ struct FiltCfg {
   int stride;       // entries per row: min(V, kMaxTopK) >= any admissible top_k
   int nchf;         // chunks per row
   int kk;           // top_k in effect
+  int by_rank;      // 1: kept set stored by (logit desc, id asc) instead of token-id order
   double T;         // temperature (binary32 value)
   double top_p;     // binary32 value
 };
@@ -176,6 +178,24 @@ struct TreeCfg {
   TreeState* ts;          // [B]
   TreeRes* tres;          // [B, nsb]
   int N, D;
+};
+
+// Tree Sampler: candidate prefixes from the draft rows, and the verification
+// of deterministic candidates with a tree per request.
+constexpr int kMaxCandEntries = 4096;  // draft positions x candidates per position
+struct CandCfg {
+  int cands, nodes;
+  int32_t* out_parent;  // [B, nodes]
+  int32_t* out_tokens;  // [B, nodes]
+};
+struct DTreeCfg {
+  int N;
+  const int32_t* parent;  // [B, N]
+  const int32_t* tokens;  // [B, N]
+  int32_t* out_tokens;    // [B, N + 1]
+  int32_t* out_path;      // [B, N]
+  void* state;            // [B] walk outcome (tree-state workspace section)
+  int32_t* rem;           // [B, N] removed tokens of the final row
 };
 
 // Rows of one request: np target rows then nq draft rows.
@@ -239,6 +259,11 @@ hipError_t launch_tree_filtered(const LinCfg& c, const FiltCfg& f, const TreeTop
 // Row passes over the first `rows` rows of c.rows, reused by the tree:
 // filtering (filter.hip), statistics and argmax (linear.hip).
 hipError_t launch_filter_rows(const LinCfg& c, const FiltCfg& f, int64_t rows, int dtype, hipStream_t s);
+// Tree Sampler (dtree.hip): candidates (c.rows: the K draft rows of each
+// request) and the verification of deterministic candidates (c.rows: the N + 1
+// target rows of each request).
+hipError_t launch_tree_candidates(const LinCfg& c, const FiltCfg& f, const CandCfg& cc, int dtype, hipStream_t s);
+hipError_t launch_verify_tree_det(const LinCfg& c, const DTreeCfg& d, int dtype, hipStream_t s);
 hipError_t launch_stats32(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
 hipError_t launch_argmax(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
 // fp64 draft-row sub-block records of the first `rows` rows of c.rows.q (linear.hip).

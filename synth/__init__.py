@@ -66,6 +66,7 @@ RECIPES = {
     "highconc": dict(sd_a=3.0, n_heavy=20, boost=8.0, mode=1, rho=0.8, sd_noise=3.0),
     "filtered": dict(sd_a=2.0, n_heavy=0, boost=0.0, mode=0, rho=0.0, sd_noise=0.5),
     "tree": dict(sd_a=3.0, n_heavy=20, boost=8.0, mode=1, rho=0.85, sd_noise=3.0),
+    "treesampler": dict(sd_a=3.0, n_heavy=20, boost=8.0, mode=1, rho=0.85, sd_noise=3.0),
 }
 
 # Shapes and sampling parameters per workload.
@@ -76,6 +77,9 @@ WORKLOADS = {
     "filtered": dict(B=128, K=16, V=128256, dtype="f32", temperature=1.0, top_k=50, top_p=0.95, fused=True),
     "greedy": dict(B=128, K=16, V=128256, dtype="f32", temperature=0.0, top_k=0, top_p=1.0, fused=True),
     "tree": dict(B=4, N=32, V=151936, dtype="bf16", temperature=1.0, top_k=0, top_p=1.0),
+    # Tree Sampler: a block of 16 draft positions, 32 candidates per position,
+    # 32 kept prefixes, verified against one target row per prefix plus the root
+    "treesampler": dict(B=4, K=16, cands=32, nodes=32, V=151936, dtype="bf16", temperature=1.0),
 }
 WORKLOADS_RECIPE = {"greedy": "filtered"}
 
@@ -125,6 +129,18 @@ def tree_inputs(workload="tree", seed=0, B=None, N=None, V=None, rho=None, nthre
     N = N or w["N"]
     V = V or w["V"]
     return pair(B, N + 1, N + 1, V, w["dtype"], seed=seed, nthreads=nthreads, **r)
+
+
+def treesampler_inputs(seed=0, B=None, K=None, nodes=None, V=None, nthreads=None):
+    """(p [B, nodes+1, V], q [B, K, V]) for the Tree Sampler workload: draft
+    rows per block position and target rows per kept prefix (plus the root),
+    row i of p correlated with row i of q for i < K."""
+    w = WORKLOADS["treesampler"]
+    B = B or w["B"]
+    K = K or w["K"]
+    nodes = nodes or w["nodes"]
+    V = V or w["V"]
+    return pair(B, nodes + 1, K, V, w["dtype"], seed=seed, nthreads=nthreads, **RECIPES["treesampler"])
 
 
 def branch_chain_parent(branches=4, depth=8):

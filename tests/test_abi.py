@@ -114,3 +114,56 @@ def test_filter_limits(psi):
     assert _call_linear(psi, prm=psi.make_params(top_p=0.9)) == psi.EUNSUPPORTED
     assert _call_linear(psi, V=4096, prm=psi.make_params(top_k=257)) == psi.EUNSUPPORTED
     assert _call_linear(psi, V=4096, prm=psi.make_params(top_k=256, top_p=0.9), ws_bytes=16) == psi.EWORKSPACE
+
+
+def _call_cands(psi, B=2, K=15, V=1000, dtype=1, prm=None, cands=32, nodes=32, ws_bytes=1 << 30, ws_addr=1 << 20,
+                null=None):
+    prm = prm if prm is not None else psi.make_params()
+    fake = {k: ctypes.c_void_p(0x10000000 + 0x1000 * i) for i, k in enumerate(["q", "par", "tok"])}
+    if null:
+        fake[null] = None
+    return psi.lib.psispec_tree_candidates(fake["q"], dtype, B, K, V, ctypes.byref(prm), cands, nodes, fake["par"],
+                                           fake["tok"], ctypes.c_void_p(ws_addr), ws_bytes, None)
+
+
+def test_tree_candidates_argument_errors(psi):
+    for k in ("q", "par", "tok"):
+        assert _call_cands(psi, null=k) == psi.EINVAL
+    assert _call_cands(psi, B=0) == psi.EINVAL
+    assert _call_cands(psi, cands=0) == psi.EINVAL
+    assert _call_cands(psi, nodes=0) == psi.EINVAL
+    assert _call_cands(psi, prm=psi.make_params(temperature=0.0)) == psi.EINVAL  # no greedy candidates
+    assert _call_cands(psi, prm=psi.make_params(top_k=8)) == psi.EUNSUPPORTED
+    assert _call_cands(psi, prm=psi.make_params(top_p=0.5)) == psi.EUNSUPPORTED
+    assert _call_cands(psi, V=20, cands=21) == psi.EUNSUPPORTED
+    assert _call_cands(psi, V=4096, cands=257) == psi.EUNSUPPORTED
+    assert _call_cands(psi, K=64, cands=65) == psi.EUNSUPPORTED  # K * cands > 4096
+    assert _call_cands(psi, K=65, cands=8) == psi.EUNSUPPORTED
+    assert _call_cands(psi, nodes=257) == psi.EUNSUPPORTED
+    assert _call_cands(psi, ws_bytes=16) == psi.EWORKSPACE
+    assert _call_cands(psi, ws_addr=(1 << 20) + 8) == psi.EINVAL
+
+
+def _call_det(psi, B=2, N=31, V=1000, dtype=1, prm=None, ws_bytes=1 << 30, ws_addr=1 << 20, null=None):
+    prm = prm if prm is not None else psi.make_params()
+    fake = {k: ctypes.c_void_p(0x10000000 + 0x1000 * i) for i, k in
+            enumerate(["p", "par", "ntok", "tok", "path", "len"])}
+    if null:
+        fake[null] = None
+    return psi.lib.psispec_verify_tree_det(fake["p"], dtype, B, N, V, fake["par"], fake["ntok"], ctypes.byref(prm),
+                                           fake["tok"], fake["path"], fake["len"], ctypes.c_void_p(ws_addr),
+                                           ws_bytes, None)
+
+
+def test_verify_tree_det_argument_errors(psi):
+    for k in ("p", "par", "ntok", "tok", "path", "len"):
+        assert _call_det(psi, null=k) == psi.EINVAL
+    assert _call_det(psi, N=0) == psi.EINVAL
+    assert _call_det(psi, V=0) == psi.EINVAL
+    assert _call_det(psi, N=257) == psi.EUNSUPPORTED
+    assert _call_det(psi, dtype=3) == psi.EUNSUPPORTED
+    assert _call_det(psi, prm=psi.make_params(temperature=-0.5)) == psi.EINVAL
+    assert _call_det(psi, prm=psi.make_params(top_k=4)) == psi.EUNSUPPORTED
+    assert _call_det(psi, prm=psi.make_params(top_p=0.9)) == psi.EUNSUPPORTED
+    assert _call_det(psi, ws_bytes=16) == psi.EWORKSPACE
+    assert _call_det(psi, ws_addr=(1 << 20) + 4) == psi.EINVAL
