@@ -71,10 +71,91 @@ __device__ __forceinline__ bool row_norm(const StatRec* rec, int nch, float c32,
 }  // namespace
 
 // ------------------------------------------------------------ candidates --
-// Selection state of slot s (0 = the empty prefix, n + 1 = node n) on lane
-// s % 64, register j = s / 64: its log score, length, the rank of its best
-// child not yet kept, that child's offer (-inf when none), and the log q of
-// the next two ranks at its child position (prefetched).
+// Best-first enumeration by one whole wave. Slot s (0 = the empty prefix,
+// n + 1 = node n) lives on lane s % 64, register j = s / 64 (SPL registers per
+// lane): its log score, length, the rank of its best child not yet kept, and
+// that child's offer (-inf when none). Per step: each lane's best offer under
+// (score desc, length asc, slot asc), the wave maximum of the upper 32 bits of
+// the scores' order keys (DPP), a ballot, and a full compare only when upper
+// words tie; the kept slot then offers its next child and the new slot its
+// first, from two broadcast LDS reads. Writes s_par[n] and s_ent[n] (position
+// * C + rank) for n < NN, -1 past the last prefix of positive probability.
+template <int SPL>
+__device__ void cand_enumerate(const double* s_lq, int K, int C, int NN, int* s_par, int* s_ent) {
+  const int lane = threadIdx.x & (kWave - 1);
+  double ls[SPL], off[SPL];
+  int dep[SPL], nxt[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) {
+    ls[j] = 0.0;
+    off[j] = -INFINITY;
+    dep[j] = 0;
+    nxt[j] = 0;
+  }
+  if (lane == 0) off[0] = s_lq[0];  // the empty prefix offers the best position-0 candidate
+  int n = 0;
+  for (; n < NN; ++n) {
+    double bo = off[0], bl = ls[0];
+    int bk = dep[0] * 512 + lane, bn = nxt[0];
+#pragma unroll
+    for (int j = 1; j < SPL; ++j) {
+      const int key = dep[j] * 512 + lane + kWave * j;
+      const bool better = off[j] > bo || (off[j] == bo && key < bk);
+      bo = better ? off[j] : bo;
+      bl = better ? ls[j] : bl;
+      bk = better ? key : bk;
+      bn = better ? nxt[j] : bn;
+    }
+    const uint32_t hi = bo > -INFINITY ? order_hi(bo) : 0u;
+    const uint32_t M = wave_max_u32(hi);
+    if (M == 0u) break;  // no prefix of positive probability is left
+    unsigned long long cand = __ballot(hi == M);
+    int w = __ffsll((long long)cand) - 1;
+    if (__popcll(cand) > 1) {  // upper words tie: compare in full
+      double wo = rd_lane(bo, w);
+      int wk = __builtin_amdgcn_readlane(bk, w);
+      cand &= cand - 1;
+      while (cand) {
+        const int l = __ffsll((long long)cand) - 1;
+        cand &= cand - 1;
+        const double o = rd_lane(bo, l);
+        const int k = __builtin_amdgcn_readlane(bk, l);
+        if (o > wo || (o == wo && k < wk)) {
+          w = l;
+          wo = o;
+          wk = k;
+        }
+      }
+    }
+    const double wo = rd_lane(bo, w);
+    const double wl = rd_lane(bl, w);
+    const int wk = __builtin_amdgcn_readlane(bk, w);
+    const int wn = __builtin_amdgcn_readlane(bn, w);
+    const int ws = wk & 511, wd = wk >> 9;
+    if (lane == 0) {
+      s_par[n] = ws - 1;
+      s_ent[n] = wd * C + wn;
+    }
+    const double x1 = wn + 1 < C ? s_lq[wd * C + wn + 1] : -INFINITY;  // the kept slot's next child
+    const double x0 = wd + 1 < K ? s_lq[(wd + 1) * C] : -INFINITY;     // the new slot's first child
+    const int sn = n + 1;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const bool kept = j == (ws >> 6) && lane == (ws & (kWave - 1));
+      const bool born = j == (sn >> 6) && lane == (sn & (kWave - 1));
+      nxt[j] = kept ? wn + 1 : (born ? 0 : nxt[j]);
+      off[j] = kept ? wl + x1 : (born ? wo + x0 : off[j]);
+      ls[j] = born ? wo : ls[j];
+      dep[j] = born ? wd + 1 : dep[j];
+    }
+  }
+  if (lane == 0)
+    for (int m = n; m < NN; ++m) {
+      s_par[m] = -1;
+      s_ent[m] = -1;
+    }
+}
+
 __global__ __launch_bounds__(kWG) void k_cand_tree(LinCfg c, FiltCfg f, CandCfg cc) {
   const int64_t b = blockIdx.x;
   const int t = threadIdx.x, lane = t & (kWave - 1);
@@ -82,7 +163,7 @@ __global__ __launch_bounds__(kWG) void k_cand_tree(LinCfg c, FiltCfg f, CandCfg 
   __shared__ double s_lq[kMaxCandEntries];  // [K][C] log q of rank r at position i, -inf past the kept set
   __shared__ double s_L[kMaxK];
   __shared__ int s_cnt[kMaxK];
-  __shared__ int s_ent[kMaxNodes];  // entry (position * C + rank) of node n, -1 when not kept
+  __shared__ int s_ent[kMaxNodes];
   __shared__ int s_par[kMaxNodes];
   __shared__ int s_bad;
   if (t == 0) s_bad = 0;
@@ -113,101 +194,13 @@ __global__ __launch_bounds__(kWG) void k_cand_tree(LinCfg c, FiltCfg f, CandCfg 
   }
   __syncthreads();
   if (t >= kWave) return;
-
-  // ---- best-first enumeration by wave 0
-  auto lq_at = [&](int d, int r) { return r < C ? s_lq[d * C + r] : -INFINITY; };
-  // rank 0 and rank 1 of every position, lane d holding position d
-  const double lq0 = lane < K ? lq_at(lane, 0) : -INFINITY;
-  const double lq1 = lane < K ? lq_at(lane, 1) : -INFINITY;
-  double ls[kSlotsPerLane], off[kSlotsPerLane], nx1[kSlotsPerLane], nx2[kSlotsPerLane];
-  int dep[kSlotsPerLane], nxt[kSlotsPerLane];
-#pragma unroll
-  for (int j = 0; j < kSlotsPerLane; ++j) {
-    ls[j] = 0.0;
-    off[j] = -INFINITY;
-    nx1[j] = -INFINITY;
-    nx2[j] = -INFINITY;
-    dep[j] = 0;
-    nxt[j] = 0;
+  switch ((NN + kWave) / kWave) {  // slots per lane: ceil((NN + 1) / 64)
+    case 1: cand_enumerate<1>(s_lq, K, C, NN, s_par, s_ent); break;
+    case 2: cand_enumerate<2>(s_lq, K, C, NN, s_par, s_ent); break;
+    case 3: cand_enumerate<3>(s_lq, K, C, NN, s_par, s_ent); break;
+    case 4: cand_enumerate<4>(s_lq, K, C, NN, s_par, s_ent); break;
+    default: cand_enumerate<5>(s_lq, K, C, NN, s_par, s_ent); break;
   }
-  if (lane == 0) {  // the empty prefix: its children are the position-0 candidates
-    off[0] = lq_at(0, 0);
-    nx1[0] = lq_at(0, 1);
-    nx2[0] = lq_at(0, 2);
-  }
-  int n = 0;
-  for (; n < NN; ++n) {
-    // best offer of this lane: (score desc, length asc, slot asc)
-    double bo = -INFINITY;
-    int bk = 0x7fffffff, be = 0, bj = 0;
-#pragma unroll
-    for (int j = 0; j < kSlotsPerLane; ++j) {
-      const int key = dep[j] * 512 + lane + kWave * j;
-      const bool better = off[j] > bo || (off[j] == bo && off[j] > -INFINITY && key < bk);
-      if (better) {
-        bo = off[j];
-        bk = key;
-        be = dep[j] * C + nxt[j];
-        bj = j;
-      }
-    }
-    const bool valid = bo > -INFINITY;
-    const uint32_t hi = valid ? order_hi(bo) : 0u;
-    const uint32_t M = wave_max_u32(hi);
-    if (M == 0u) break;  // no prefix of positive probability is left
-    unsigned long long cand = __ballot(hi == M);
-    int w = __ffsll((long long)cand) - 1;
-    if (__popcll(cand) > 1) {  // upper words tie: compare in full
-      double wo = rd_lane(bo, w);
-      int wk = __builtin_amdgcn_readlane(bk, w);
-      cand &= cand - 1;
-      while (cand) {
-        const int l = __ffsll((long long)cand) - 1;
-        cand &= cand - 1;
-        const double o = rd_lane(bo, l);
-        const int k = __builtin_amdgcn_readlane(bk, l);
-        if (o > wo || (o == wo && k < wk)) {
-          w = l;
-          wo = o;
-          wk = k;
-        }
-      }
-    }
-    const double wo = rd_lane(bo, w);
-    const int wk = __builtin_amdgcn_readlane(bk, w);
-    const int ws = wk & 511, wd = wk >> 9;
-    if (lane == 0) {
-      s_par[n] = ws - 1;
-      s_ent[n] = __builtin_amdgcn_readlane(be, w);
-    }
-    // the kept slot offers its next child; the new slot (node n) its first
-    const int sn = n + 1;
-    const double f0 = rd_lane(lq0, min(wd + 1, kWave - 1));
-    const double f1 = rd_lane(lq1, min(wd + 1, kWave - 1));
-    const bool deeper = wd + 1 < K;
-#pragma unroll
-    for (int j = 0; j < kSlotsPerLane; ++j) {
-      if (lane == w && j == bj) {
-        ++nxt[j];
-        off[j] = ls[j] + nx1[j];
-        nx1[j] = nx2[j];
-        nx2[j] = lq_at(dep[j], nxt[j] + 2);
-      }
-      if (lane == (sn & (kWave - 1)) && j == (sn >> 6)) {
-        ls[j] = wo;
-        dep[j] = wd + 1;
-        nxt[j] = 0;
-        off[j] = deeper ? wo + f0 : -INFINITY;
-        nx1[j] = deeper ? f1 : -INFINITY;
-        nx2[j] = deeper ? lq_at(wd + 1, 2) : -INFINITY;
-      }
-    }
-  }
-  if (lane == 0)
-    for (int m = n; m < NN; ++m) {
-      s_par[m] = -1;
-      s_ent[m] = -1;
-    }
   wave_sync();
   for (int m = lane; m < NN; m += kWave) {
     const int e = s_ent[m];
@@ -222,7 +215,7 @@ __global__ __launch_bounds__(kWG) void k_cand_tree(LinCfg c, FiltCfg f, CandCfg 
 }
 
 // ---------------------------------------------------------- verification --
-// Walk outcome of one request, for the final-row pass and pick.
+// Walk outcome of one request, for the final pick.
 struct DTreeState {
   int32_t row;   // final row
   int32_t len;   // accepted path length; -1 = request error (outputs written)
@@ -234,43 +227,48 @@ struct DTreeState {
 static_assert(sizeof(DTreeState) <= sizeof(TreeState), "DTreeState lives in the tree-state section");
 
 namespace {
+
 __device__ __forceinline__ const char* det_row(const LinCfg& c, int64_t b, int r) {
   return c.rows.p + ((b * c.rows.np + r) * (int64_t)c.V) * c.rows.esz;
 }
+
+// Bit k of the result: element j0 + k (k < 32) is one of the removed tokens.
+__device__ __forceinline__ uint32_t removed_mask(const int32_t* rem, int nrem, int64_t j0) {
+  uint32_t gone = 0;
+  for (int k = 0; k < nrem; ++k) {
+    const int64_t rel = (int64_t)rem[k] - j0;
+    if (rel >= 0 && rel < 32) gone |= 1u << rel;
+  }
+  return gone;
+}
+
 }  // namespace
 
-struct DTreeWs {
-  DTreeState* st;  // [B]
-  int32_t* rem;    // [B, N] removed tokens of the final row
-};
-
-// Validates the request and, for node n: parent row, token, sibling index j
-// (ascending node id among the children of that row), whether an earlier
-// sibling carries the same token, and the child lists in node order.
-// Returns false (after writing the request error) for a malformed request.
-__device__ bool det_topology(const LinCfg& c, const DTreeCfg& d, int64_t b, int* s_par, int* s_tok, int* s_sib,
-                             int* s_dup, int* s_off, int* s_kid, int* s_bad) {
+// Validates the request and, for node n: sibling index j (ascending node id
+// among the children of its parent row), whether an earlier sibling carries
+// the same token, and the child lists in node order (s_par / s_tok filled and
+// *s_bad set by the caller before). The writer workgroup clears the outputs
+// and reports a malformed request. Returns false for one.
+template <int NT>
+__device__ bool det_topology(const LinCfg& c, const DTreeCfg& d, int64_t b, bool writer, const int* s_par,
+                             const int* s_tok, int* s_sib, int* s_dup, int* s_off, int* s_kid, int* s_bad) {
   const int t = threadIdx.x, N = d.N;
-  for (int n = t; n < N; n += kWG) {
-    const int p = d.parent[b * N + n], x = d.tokens[b * N + n];
-    if (p < -1 || p >= n || x < 0 || x >= c.V) atomicOr(s_bad, 1);
-    s_par[n] = p;
-    s_tok[n] = x;
+  if (writer) {
+    for (int i = t; i <= N; i += NT) d.out_tokens[b * (N + 1) + i] = -1;
+    for (int i = t; i < N; i += NT) d.out_path[b * N + i] = -1;
   }
-  for (int i = t; i <= N; i += kWG) d.out_tokens[b * (N + 1) + i] = -1;
-  for (int i = t; i < N; i += kWG) d.out_path[b * N + i] = -1;
   __syncthreads();
   if (*s_bad) {
-    if (t == 0) c.out_len[b] = -1;
+    if (writer && t == 0) c.out_len[b] = -1;
     return false;
   }
   // off[r] = nodes whose parent row is below r; sibling index and duplicates
-  for (int r = t; r <= N; r += kWG) {
+  for (int r = t; r <= N; r += NT) {
     int k = 0;
     for (int m = 0; m < N; ++m) k += s_par[m] + 1 < r ? 1 : 0;
     s_off[r] = k;
   }
-  for (int n = t; n < N; n += kWG) {
+  for (int n = t; n < N; n += NT) {
     const int p = s_par[n], x = s_tok[n];
     int j = 0, dup = 0;
     for (int m = 0; m < n; ++m)
@@ -282,24 +280,49 @@ __device__ bool det_topology(const LinCfg& c, const DTreeCfg& d, int64_t b, int*
     s_dup[n] = dup;
   }
   __syncthreads();
-  for (int n = t; n < N; n += kWG) s_kid[s_off[s_par[n] + 1] + s_sib[n]] = n;
+  for (int n = t; n < N; n += NT) s_kid[s_off[s_par[n] + 1] + s_sib[n]] = n;
   __syncthreads();
   return true;
 }
 
-template <int DT>
-__global__ __launch_bounds__(kWG) void k_dtree_walk(LinCfg c, DTreeCfg d, DTreeWs dw) {
+// Grid (sub-block groups, request). Every workgroup of a request repeats the
+// walk (row normalisers from the statistics records, every node's P(tok) and
+// uniform, the walk by thread 0 over LDS); workgroup 0 writes the path and the
+// walk outcome. Then each wave sums one sub-block of the final row under the
+// final-draw weight rule: res.sp without the removed tokens, res.sq over all.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_dtree_walkpass(LinCfg c, DTreeCfg d) {
   using E = Elem<DT>;
-  const int64_t b = blockIdx.x;
-  const int t = threadIdx.x, N = d.N, R = N + 1;
+  constexpr int EPV = E::kPerVec;
+  constexpr int VPL = kSB / (kWave * EPV);
+  const int64_t b = blockIdx.y;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int N = d.N, R = N + 1;
+  const bool writer = blockIdx.x == 0;
   __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_sib[kMaxNodes], s_dup[kMaxNodes], s_kid[kMaxNodes];
   __shared__ int s_off[kMaxNodes + 1];
   __shared__ double s_P[kMaxNodes], s_u[kMaxNodes];
   __shared__ float s_m[kMaxNodes + 1];
   __shared__ double s_S[kMaxNodes + 1];
-  __shared__ int s_bad;
+  __shared__ int s_rem[kMaxNodes];
+  __shared__ int s_bad, s_row, s_nrem;
   if (t == 0) s_bad = 0;
   __syncthreads();
+  // node data, and the logit of each node's token at its parent row
+  float a_node[(kMaxNodes + kWG - 1) / kWG];
+#pragma unroll
+  for (int k = 0; k < (kMaxNodes + kWG - 1) / kWG; ++k) {
+    const int n = t + k * kWG;
+    a_node[k] = 0.0f;
+    if (n < N) {
+      const int p = d.parent[b * N + n], x = d.tokens[b * N + n];
+      const bool ok = p >= -1 && p < n && x >= 0 && x < c.V;
+      if (!ok) atomicOr(&s_bad, 1);
+      s_par[n] = p;
+      s_tok[n] = x;
+      if (ok) a_node[k] = E::load1(det_row(c, b, p + 1), x);
+    }
+  }
   for (int r = t; r < R; r += kWG) {
     float m;
     double S;
@@ -307,71 +330,64 @@ __global__ __launch_bounds__(kWG) void k_dtree_walk(LinCfg c, DTreeCfg d, DTreeW
     s_m[r] = m;
     s_S[r] = S;
   }
-  if (!det_topology(c, d, b, s_par, s_tok, s_sib, s_dup, s_off, s_kid, &s_bad)) {
-    if (t == 0) dw.st[b] = DTreeState{0, -1, 0, 0, 0.0f, 0.0f};
+  if (!det_topology<kWG>(c, d, b, writer, s_par, s_tok, s_sib, s_dup, s_off, s_kid, &s_bad)) {
+    if (writer && t == 0) ((DTreeState*)d.state)[b] = DTreeState{0, -1, 0, 0, 0.0f, 0.0f};
     return;
   }
-  // P(tok) of every node at its parent row and the uniform of its test
-  for (int n = t; n < N; n += kWG) {
-    const int row = s_par[n] + 1;
-    const float a = E::load1(det_row(c, b, row), s_tok[n]);
-    s_P[n] = ::exp(((double)a - (double)s_m[row]) * c.invT - ::log(s_S[row]));
-    s_u[n] = c.rng.u((uint32_t)b, (uint32_t)row, kDrawAccept + (uint32_t)s_sib[n]);
+#pragma unroll
+  for (int k = 0; k < (kMaxNodes + kWG - 1) / kWG; ++k) {
+    const int n = t + k * kWG;
+    if (n < N) {
+      const int row = s_par[n] + 1;
+      s_P[n] = ::exp(((double)a_node[k] - (double)s_m[row]) * c.invT - ::log(s_S[row]));
+      s_u[n] = c.rng.u((uint32_t)b, (uint32_t)row, kDrawAccept + (uint32_t)s_sib[n]);
+    }
   }
   __syncthreads();
-  if (t != 0) return;
-  int row = 0, len = 0, k0 = 0, nk = 0;
-  for (;;) {
-    k0 = s_off[row];
-    nk = (row < N ? s_off[row + 1] : N) - k0;
-    double E = 0.0;  // probability removed at this row
-    int acc = -1;
-    for (int k = 0; k < nk; ++k) {
-      const int n = s_kid[k0 + k];
-      const double pt = s_dup[n] ? 0.0 : s_P[n];
-      if (s_u[n] * (1.0 - E) < pt) {
-        acc = n;
-        break;
+  if (t == 0) {
+    int row = 0, len = 0, k0 = 0, nk = 0;
+    for (;;) {
+      k0 = s_off[row];
+      nk = (row < N ? s_off[row + 1] : N) - k0;
+      double E = 0.0;  // probability removed at this row
+      int acc = -1;
+      for (int k = 0; k < nk; ++k) {
+        const int n = s_kid[k0 + k];
+        const double pt = s_dup[n] ? 0.0 : s_P[n];
+        if (s_u[n] * (1.0 - E) < pt) {
+          acc = n;
+          break;
+        }
+        E += pt;
       }
-      E += pt;
+      if (acc < 0) break;
+      if (writer) {
+        d.out_path[b * N + len] = acc;
+        d.out_tokens[b * (N + 1) + len] = s_tok[acc];
+      }
+      ++len;
+      row = acc + 1;
     }
-    if (acc < 0) break;
-    d.out_path[b * N + len] = acc;
-    d.out_tokens[b * (N + 1) + len] = s_tok[acc];
-    ++len;
-    row = acc + 1;
+    for (int k = 0; k < nk; ++k) s_rem[k] = s_tok[s_kid[k0 + k]];
+    s_row = row;
+    s_nrem = nk;
+    if (writer) ((DTreeState*)d.state)[b] = DTreeState{row, len, nk, 0, s_m[row], 0.0f};
   }
-  for (int k = 0; k < nk; ++k) dw.rem[b * N + k] = s_tok[s_kid[k0 + k]];
-  dw.st[b] = DTreeState{row, len, nk, 0, s_m[row], 0.0f};
-}
-
-// Sub-block sums of the final row's weights 2^((a - m) c): res.sp without the
-// removed tokens, res.sq over the whole row. One wave per sub-block.
-template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_dtree_pass(LinCfg c, DTreeCfg d, DTreeWs dw) {
-  constexpr int EPV = Elem<DT>::kPerVec;
-  constexpr int VPL = kSB / (kWave * EPV);
-  static_assert(VPL * EPV <= 32, "one mask bit per element of a lane");
-  const int64_t b = blockIdx.y;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  __syncthreads();
+  const int row = s_row, nrem = s_nrem;
+  if (writer)
+    for (int k = t; k < nrem; k += kWG) d.rem[b * N + k] = s_rem[k];
   const int sb = blockIdx.x * kWaves + wave;
   if (sb >= c.nsb) return;
-  const DTreeState s = dw.st[b];
-  if (s.len < 0) return;
   const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
   float x[VPL][EPV];
-  load_vecs<DT, AL, VPL, kWave>(det_row(c, b, s.row), c.V, c.nvec, vfirst, x);
+  load_vecs<DT, AL, VPL, kWave>(det_row(c, b, row), c.V, c.nvec, vfirst, x);
   // removed tokens held by this lane: element (vfirst + v * 64) * EPV + e is bit v * EPV + e
   uint32_t gone = 0;
-  const int32_t* rem = dw.rem + b * d.N;
-  for (int k = 0; k < s.nrem; ++k) {
-    const int rel = rem[k] - sb * kSB;
-    if (rel >= 0 && rel < kSB) {
-      const int vec = rel / EPV;
-      if ((vec & (kWave - 1)) == lane) gone |= 1u << ((vec >> 6) * EPV + rel % EPV);
-    }
-  }
-  const WRow wr = wrow(DT == kBF16 && c.tab, s.m, c.c64);
+#pragma unroll
+  for (int v = 0; v < VPL; ++v)
+    gone |= (removed_mask(s_rem, nrem, (vfirst + (int64_t)v * kWave) * EPV) & ((1u << EPV) - 1u)) << (v * EPV);
+  const WRow wr = wrow(DT == kBF16 && c.tab, s_m[row], c.c64);
   double all = 0.0, kept = 0.0;
 #pragma unroll
   for (int v = 0; v < VPL; ++v)
@@ -386,42 +402,42 @@ __global__ __launch_bounds__(kWG) void k_dtree_pass(LinCfg c, DTreeCfg d, DTreeW
   if (lane == 0) c.res[b * c.nsb + sb] = ResRec{kept, all, 0.0, 0.0};
 }
 
+// One wave per request: inverse-CDF draw from the final row's weights without
+// the removed tokens (from all of them if nothing is left), then the outputs.
 template <int DT>
-__global__ __launch_bounds__(kWG) void k_dtree_pick(LinCfg c, DTreeCfg d, DTreeWs dw) {
+__global__ __launch_bounds__(kWave) void k_dtree_pick(LinCfg c, DTreeCfg d) {
   using E = Elem<DT>;
+  constexpr int EPL = kSB / kWave;
   const int64_t b = blockIdx.x;
-  const int t = threadIdx.x, nsb = c.nsb, N = d.N;
-  const DTreeState s = dw.st[b];
+  const int lane = threadIdx.x, nsb = c.nsb, N = d.N;
+  const DTreeState s = ((const DTreeState*)d.state)[b];
   if (s.len < 0) return;
-  __shared__ double sh[kWG + kWaves];
-  __shared__ int s_rem[kMaxNodes];
-  for (int k = t; k < s.nrem; k += kWG) s_rem[k] = dw.rem[b * N + k];
+  const int32_t* rem = d.rem + b * N;
   const ResRec* rr = c.res + b * nsb;
-  double mine = 0.0;
-  for (int sb = t; sb < nsb; sb += kWG) mine += rr[sb].sp;
-  const double W = block_sum(mine, sh);  // also orders the s_rem writes before their reads
+  double W = 0.0, W0 = 0.0;
+  for (int sb = lane; sb < nsb; sb += kWave) {
+    const ResRec r = rr[sb];
+    W += r.sp;
+    W0 += r.sq;
+  }
+  W = wave_sum(W);
+  W0 = wave_sum(W0);
   const char* row = det_row(c, b, s.row);
   const WRow wr = wrow(DT == kBF16 && c.tab, s.m, c.c64);
   const double u = c.rng.u((uint32_t)b, (uint32_t)s.row, kDrawFinal);
-  int y;
-  if (W > 0.0) {
-    y = pick_index(
-        nsb, c.V, u * W, [&](int sb) { return rr[sb].sp; },
-        [&](int64_t j) {
-          for (int k = 0; k < s.nrem; ++k)
-            if (s_rem[k] == (int)j) return 0.0;
-          return fweight<DT>(E::load1(row, j), wr, c.c64, nullptr);
-        },
-        sh);
-  } else {  // every token of positive probability was removed: draw from P
-    double all = 0.0;
-    for (int sb = t; sb < nsb; sb += kWG) all += rr[sb].sq;
-    const double Wa = block_sum(all, sh);
-    y = pick_index(
-        nsb, c.V, u * Wa, [&](int sb) { return rr[sb].sq; },
-        [&](int64_t j) { return fweight<DT>(E::load1(row, j), wr, c.c64, nullptr); }, sh);
-  }
-  if (t == 0) {
+  const bool none_left = !(W > 0.0);  // every token of positive probability was removed: draw from P
+  const int y = wave_pick(
+      nsb, c.V, u * (none_left ? W0 : W), [&](int sb) { return none_left ? rr[sb].sq : rr[sb].sp; },
+      [&](int64_t j0, double (&w)[EPL]) {
+        const uint32_t gone = none_left ? 0u : removed_mask(rem, s.nrem, j0);
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+          const int64_t j = j0 + k;
+          const double e = j < c.V ? fweight<DT>(E::load1(row, j), wr, c.c64, nullptr) : 0.0;
+          w[k] = (gone >> k) & 1u ? 0.0 : e;
+        }
+      });
+  if (lane == 0) {
     d.out_tokens[b * (N + 1) + s.len] = y;
     c.out_len[b] = s.len;
   }
@@ -442,7 +458,13 @@ __global__ __launch_bounds__(kWG) void k_dtree_greedy(LinCfg c, DTreeCfg d) {
     s_g[r] = row_argmax(c.ar + (b * R + r) * (int64_t)c.nch32, c.nch32, &bad);
     if (bad) atomicOr(&s_bad, 1);
   }
-  if (!det_topology(c, d, b, s_par, s_tok, s_sib, s_dup, s_off, s_kid, &s_bad)) return;
+  for (int n = t; n < N; n += kWG) {
+    const int p = d.parent[b * N + n], x = d.tokens[b * N + n];
+    if (p < -1 || p >= n || x < 0 || x >= c.V) atomicOr(&s_bad, 1);
+    s_par[n] = p;
+    s_tok[n] = x;
+  }
+  if (!det_topology<kWG>(c, d, b, true, s_par, s_tok, s_sib, s_dup, s_off, s_kid, &s_bad)) return;
   if (t != 0) return;
   int row = 0, len = 0;
   for (;;) {
@@ -489,13 +511,9 @@ static hipError_t dtree_t(const LinCfg& c, const DTreeCfg& d, hipStream_t s) {
   }
   hipError_t e = launch_stats32(c, rows, DT, s);
   if (e != hipSuccess) return e;
-  DTreeWs dw;
-  dw.st = (DTreeState*)d.state;
-  dw.rem = d.rem;
-  PSI_LAUNCH(s, k_dtree_walk<DT>, dim3((unsigned)c.B), dim3(kWG), c, d, dw);
-  PSI_LAUNCH(s, (k_dtree_pass<DT, AL>), dim3((unsigned)((c.nsb + kWaves - 1) / kWaves), (unsigned)c.B), dim3(kWG),
-             c, d, dw);
-  PSI_LAUNCH(s, k_dtree_pick<DT>, dim3((unsigned)c.B), dim3(kWG), c, d, dw);
+  PSI_LAUNCH(s, (k_dtree_walkpass<DT, AL>), dim3((unsigned)((c.nsb + kWaves - 1) / kWaves), (unsigned)c.B),
+             dim3(kWG), c, d);
+  PSI_LAUNCH(s, k_dtree_pick<DT>, dim3((unsigned)c.B), dim3(kWave), c, d);
   return hipGetLastError();
 }
 
