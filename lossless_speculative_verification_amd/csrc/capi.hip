@@ -116,6 +116,7 @@ inline FiltCfg filt_cfg(const psispec_params* prm, void* ws, int64_t B, int32_t 
   f.nchf = nchf_of(V);
   f.kk = prm->top_k;
   f.by_rank = 0;
+  f.cst = nullptr;
   f.T = (double)prm->temperature;
   f.top_p = (double)prm->top_p;
   return f;
@@ -328,6 +329,8 @@ int psispec_tree_candidates(const void* q_logits, int dtype, int64_t B, int32_t 
   fp.top_k = cands;
   FiltCfg f = filt_cfg(&fp, workspace, B, K, V, dtype);
   f.by_rank = 1;
+  f.cst = (StatRec*)((char*)workspace + layout(B, K, V, dtype).dr);  // nchf <= nsb records per row
+  static_assert(sizeof(StatRec) == sizeof(DraftRec) && kFiltChunk >= kSB, "chunk statistics fit the draft section");
   CandCfg cc;
   cc.cands = cands;
   cc.nodes = nodes;

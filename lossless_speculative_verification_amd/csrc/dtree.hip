@@ -8,8 +8,9 @@
 //   position i (ties: lower id), score of a prefix = sum of log q_i(t_i);
 //   keep the `nodes` best prefixes under (score desc, length asc, position of
 //   the parent prefix asc, rank of the last token asc).
-// Pipeline: k_stats32 (maximum and sum of every draft row, for log q), the
-// filter kernels with top_k = cands storing each kept set in rank order, then
+// Pipeline: the filter kernels with top_k = cands, whose chunk pass also
+// stores each chunk's maximum and sum of 2^((a - m) c) (for log q) and whose
+// merge stores each kept set in rank order, then
 // k_cand_tree: one workgroup per request turns the kept sets into log q
 // values in LDS and one wave enumerates the prefixes best first (every kept
 // prefix offers its best child not yet kept; the best offer is kept).
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kWG) void k_cand_tree(LinCfg c, FiltCfg f, CandCfg 
     const FiltRow h = f.hdr[sr];
     float m;
     double S;
-    const bool ok = row_norm(c.st + sr * c.nch32, c.nch32, c.c32, &m, &S);
+    const bool ok = row_norm(f.cst + sr * f.nchf, f.nchf, c.c32, &m, &S);
     if (!ok || h.bad || h.cnt <= 0) atomicOr(&s_bad, 1);
     // log of the full-row normaliser of z = a / T
     s_L[i] = (double)m / f.T + ::log(S);
@@ -410,9 +411,12 @@ __global__ __launch_bounds__(kWave) void k_dtree_pick(LinCfg c, DTreeCfg d) {
   constexpr int EPL = kSB / kWave;
   const int64_t b = blockIdx.x;
   const int lane = threadIdx.x, nsb = c.nsb, N = d.N;
+  __shared__ int32_t s_rem[kMaxNodes];
+  for (int k = lane; k < N; k += kWave) s_rem[k] = d.rem[b * N + k];  // entries past nrem are not read
   const DTreeState s = ((const DTreeState*)d.state)[b];
   if (s.len < 0) return;
-  const int32_t* rem = d.rem + b * N;
+  wave_sync();
+  const int32_t* rem = s_rem;
   const ResRec* rr = c.res + b * nsb;
   double W = 0.0, W0 = 0.0;
   for (int sb = lane; sb < nsb; sb += kWave) {
@@ -488,9 +492,7 @@ __global__ __launch_bounds__(kWG) void k_dtree_greedy(LinCfg c, DTreeCfg d) {
 // ------------------------------------------------------------- launchers --
 template <int DT, bool AL>
 static hipError_t cand_t(const LinCfg& c, const FiltCfg& f, const CandCfg& cc, hipStream_t s) {
-  hipError_t e = launch_stats32(c, c.B * c.K, DT, s);
-  if (e != hipSuccess) return e;
-  e = launch_filter_rows(c, f, c.B * c.K, DT, s);
+  hipError_t e = launch_filter_rows(c, f, c.B * c.K, DT, s);  // with the chunk statistics (f.cst)
   if (e != hipSuccess) return e;
   PSI_LAUNCH(s, k_cand_tree, dim3((unsigned)c.B), dim3(kWG), c, f, cc);
   return hipGetLastError();

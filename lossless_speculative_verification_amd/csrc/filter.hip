@@ -202,7 +202,9 @@ __device__ int stream_topk(const LinCfg& c, const char* row, int kk, FiltCand* c
 }  // namespace
 
 // ------------------------------------------------------- chunk candidates --
-template <int DT, bool AL>
+// With STATS the chunk's maximum and fp32-grade sum of 2^((a - m) c) are
+// stored too (f.cst), for the full-row log-normaliser of the Tree Sampler.
+template <int DT, bool AL, bool STATS = false>
 __device__ __forceinline__ void filt_chunk(const LinCfg& c, const FiltCfg& f) {
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec, NV = kFiltVals / EPV;
@@ -236,12 +238,48 @@ __device__ __forceinline__ void filt_chunk(const LinCfg& c, const FiltCfg& f) {
   const int kq = (f.kk + kWaves - 1) / kWaves;
   const float wq = wave_kth_largest(mx, kq);
   const int wf = (__ballot(tbad) ? 1 : 0) | (__ballot(tany) ? 2 : 0);
+  __shared__ float s_sm[kWaves];
+  __shared__ double s_ss[kWaves];
+  if constexpr (STATS) {
+    double st = 0.0;
+    if (mx > -INFINITY)
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        float y[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) y[e] = exp2f((x[k][e] - mx) * c.c32);
+        st += (double)pairwise_sum<EPV>(y);  // one vector in binary32, then fp64
+      }
+    const float mw = wave_max(mx);
+    double sw = mx > -INFINITY ? st * (double)exp2f((mx - mw) * c.c32) : 0.0;
+    sw = wave_sum(sw);
+    if (lane == 0) {
+      s_sm[wave] = mw;
+      s_ss[wave] = sw;
+    }
+  }
   if (lane == 0) {
     s_w[wave] = wq;
     s_f[wave] = wf;
   }
   if (t == 0) s_cnt = 0;
   __syncthreads();
+  if constexpr (STATS) {
+    if (t == 0) {
+      float m = s_sm[0];
+#pragma unroll
+      for (int i = 1; i < kWaves; ++i) m = fmaxf(m, s_sm[i]);
+      double sum = 0.0;
+      if (m > -INFINITY)
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i)
+          if (s_sm[i] > -INFINITY) sum += s_ss[i] * ::exp2(((double)s_sm[i] - (double)m) * (double)c.c32);
+      bool bad = false;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) bad |= s_f[i] & 1;
+      f.cst[item] = bad ? StatRec{NAN, 0u, NAN} : StatRec{m, 0u, sum};
+    }
+  }
   float tau = s_w[0];
   int flags = s_f[0];
 #pragma unroll
@@ -312,9 +350,9 @@ __device__ __forceinline__ void filt_chunk(const LinCfg& c, const FiltCfg& f) {
   if (item == 0 && t == 0) *f.nfall = 0;
 }
 
-template <int DT, bool AL>
+template <int DT, bool AL, bool STATS>
 __global__ __launch_bounds__(kWG) void k_filt_chunk(LinCfg c, FiltCfg f) {
-  filt_chunk<DT, AL>(c, f);
+  filt_chunk<DT, AL, STATS>(c, f);
 }
 // Aligned fp32 rows: held to 96 registers (five waves per SIMD), which it
 // meets without spilling.
@@ -964,8 +1002,12 @@ __global__ __launch_bounds__(kWG) void k_filt_draft(LinCfg c, FiltCfg f) {
 // ------------------------------------------------------------ launchers --
 template <int DT, bool AL>
 static hipError_t filter_rows_t(const LinCfg& c, const FiltCfg& f, int64_t rows, hipStream_t s) {
-  if constexpr (DT == kF32 && AL) PSI_LAUNCH(s, k_filt_chunk_f32, dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
-  else PSI_LAUNCH(s, (k_filt_chunk<DT, AL>), dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
+  if constexpr (DT == kF32 && AL) {
+    if (f.cst) PSI_LAUNCH(s, (k_filt_chunk<DT, AL, true>), dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
+    else PSI_LAUNCH(s, k_filt_chunk_f32, dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
+  }
+  else if (f.cst) PSI_LAUNCH(s, (k_filt_chunk<DT, AL, true>), dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
+  else PSI_LAUNCH(s, (k_filt_chunk<DT, AL, false>), dim3((unsigned)(rows * f.nchf)), dim3(kWG), c, f);
   PSI_LAUNCH(s, (k_filt_mergew<DT, AL>), dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(kWG), c, f, rows);
   PSI_LAUNCH(s, (k_filt_fallback<DT, AL>), dim3((unsigned)kFallWgs), dim3(kWG), c, f);
   return hipGetLastError();

@@ -123,6 +123,7 @@ struct FiltCfg {
   FiltCand* fc;     // [rows][nchf][kFiltChunkCap]
   int32_t* nfall;   // rows left to the workgroup merge, then their indices
   int32_t* fall;    // [rows]
+  StatRec* cst;     // [rows][nchf] chunk statistics, stored by the chunk pass when not null
   int stride;       // entries per row: min(V, kMaxTopK) >= any admissible top_k
   int nchf;         // chunks per row
   int kk;           // top_k in effect
