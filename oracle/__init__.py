@@ -75,6 +75,8 @@ def lib():
         L.orc_verify_tree_det.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, P, f64, u64, u32,
                                           P, P, P, P, P, P, ctypes.c_int, ctypes.c_int]
         L.orc_verify_tree_det.restype = ctypes.c_int
+        L.orc_tv_loss.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, f64, P, P, P, ctypes.c_int]
+        L.orc_tv_loss.restype = ctypes.c_int
         del i32
         _lib = L
     return _lib
@@ -276,3 +278,23 @@ def verify_tree_det(p, parent, node_tokens, temperature, seed=0, step=0, u_overr
     if rc != 0:
         raise ValueError("orc_verify_tree_det rejected its arguments")
     return dict(tokens=toks, path=path, len=ln, margin_acc=ma, margin_cdf=mc)
+
+
+def tv_loss(p, q, temperature=1.0, row_weights=None, grad=True, nthreads=1):
+    """Total-variation distillation loss of teacher logits p and student logits
+    q ([R, V] or [..., V], float32 or uint16 bf16 bits): loss [R] = 1/2 sum |p - q|
+    of the two softmaxes, and (grad=True) its gradient [R, V] with respect to the
+    student logits, each row scaled by row_weights (default 1). fp64."""
+    p = np.ascontiguousarray(p)
+    q = np.ascontiguousarray(q)
+    assert p.shape == q.shape and p.dtype == q.dtype
+    V = p.shape[-1]
+    R = int(np.prod(p.shape[:-1]))
+    loss = np.zeros(R, dtype=np.float64)
+    g = np.zeros((R, V), dtype=np.float64) if grad else None
+    w = None if row_weights is None else np.ascontiguousarray(row_weights, dtype=np.float64).reshape(R)
+    rc = lib().orc_tv_loss(_ptr(p), _ptr(q), _dtype_code(p), R, V, float(temperature), _ptr(w), _ptr(loss), _ptr(g),
+                           int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_tv_loss rejected its arguments")
+    return loss, g

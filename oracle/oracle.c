@@ -9,6 +9,10 @@
  *
  * Everything is scalar C in IEEE double, in the order the method states it.
  * Sources (web pages on Uno, a diffusion-augmented LLM):
+ *   [UnoX §3.2]  "Uno" research explainer, §3.2 Diffusion Distillation: one
+ *                forward gives frozen-teacher and student logits; the TV term
+ *                minimises the total-variation distance of the two token
+ *                distributions (it governs the expected acceptance).
  *   [UnoX §3.3]  "Uno" research explainer, §3.3 Psi-Spec: drafts x_i ~ q_i in
  *                parallel; acceptance probability a_i = min(1, p(x_i)/q(x_i));
  *                the longest accepted prefix is kept; at the first rejection one
@@ -1142,6 +1146,94 @@ int orc_verify_tree_det(const void* p, int dtype, int64_t B, int N, int V, const
     J->b1 = B * (t + 1) / nthreads;
   }
   run_jobs(jobs, sizeof(dtree_job), nthreads, dtree_worker);
+  free(jobs);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Total-variation distillation loss [UnoX §3.2 Diffusion Distillation: one
+ * forward gives the frozen AR teacher's logits and the diffusion student's;
+ * the TV term minimises the total-variation distance between the two token
+ * distributions of a position]. Per row r (a position):
+ *   p = softmax(a_r / T) (teacher), q = softmax(d_r / T) (student),
+ *   loss_r = 1/2 sum_v |p_v - q_v|.
+ * Gradient with respect to the student logits, scaled by the row weight w_r
+ * (the upstream gradient of loss_r; the teacher is frozen, so it gets none):
+ *   dloss/dq_v = g_v = sign(q_v - p_v) / 2 (0 where q_v == p_v),
+ *   dq_v/dd_j  = q_v (delta_vj - q_j) / T,
+ *   grad_j     = w_r q_j (g_j - sum_v g_v q_v) / T.
+ * A row with a NaN or +inf logit, or entirely -inf, gets a NaN loss and a NaN
+ * gradient row. out_grad may be NULL (forward only); row_w NULL means w_r = 1. */
+typedef struct {
+  const void *p, *q;
+  int dtype, V;
+  double T;
+  const double* w;
+  double *loss, *grad;
+  int64_t r0, r1;
+} tv_job;
+
+static void* tv_worker(void* arg) {
+  tv_job* J = (tv_job*)arg;
+  const int V = J->V;
+  double* a = (double*)malloc(sizeof(double) * (size_t)V);
+  double* d = (double*)malloc(sizeof(double) * (size_t)V);
+  for (int64_t r = J->r0; r < J->r1; ++r) {
+    double* gr = J->grad ? J->grad + r * (int64_t)V : NULL;
+    const int bad = orc_decode_row(J->p, J->dtype, r, V, a) | orc_decode_row(J->q, J->dtype, r, V, d);
+    if (bad) {
+      J->loss[r] = NAN;
+      if (gr)
+        for (int j = 0; j < V; ++j) gr[j] = NAN;
+      continue;
+    }
+    for (int j = 0; j < V; ++j) {
+      a[j] /= J->T;
+      d[j] /= J->T;
+    }
+    const double La = orc_logsumexp(a, V), Ld = orc_logsumexp(d, V);
+    double l1 = 0.0, gbar = 0.0;
+    for (int j = 0; j < V; ++j) {
+      const double P = exp(a[j] - La), Q = exp(d[j] - Ld);
+      const double g = Q > P ? 0.5 : (Q < P ? -0.5 : 0.0);
+      l1 += fabs(P - Q);
+      gbar += g * Q;
+      a[j] = P; /* keep P and Q for the gradient */
+      d[j] = Q;
+    }
+    J->loss[r] = 0.5 * l1;
+    if (gr) {
+      const double w = J->w ? J->w[r] : 1.0;
+      for (int j = 0; j < V; ++j) {
+        const double g = d[j] > a[j] ? 0.5 : (d[j] < a[j] ? -0.5 : 0.0);
+        gr[j] = w * d[j] * (g - gbar) / J->T;
+      }
+    }
+  }
+  free(a);
+  free(d);
+  return NULL;
+}
+
+int orc_tv_loss(const void* p, const void* q, int dtype, int64_t R, int V, double temperature, const double* row_w,
+                double* out_loss, double* out_grad, int nthreads) {
+  if (!p || !q || !out_loss || R <= 0 || V <= 0 || !(temperature > 0.0)) return -1;
+  nthreads = clamp_threads(nthreads, R);
+  tv_job* jobs = (tv_job*)calloc((size_t)nthreads, sizeof(tv_job));
+  for (int t = 0; t < nthreads; ++t) {
+    tv_job* J = &jobs[t];
+    J->p = p;
+    J->q = q;
+    J->dtype = dtype;
+    J->V = V;
+    J->T = temperature;
+    J->w = row_w;
+    J->loss = out_loss;
+    J->grad = out_grad;
+    J->r0 = R * t / nthreads;
+    J->r1 = R * (t + 1) / nthreads;
+  }
+  run_jobs(jobs, sizeof(tv_job), nthreads, tv_worker);
   free(jobs);
   return 0;
 }

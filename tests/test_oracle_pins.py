@@ -822,3 +822,89 @@ def test_tree_det_greedy_and_errors():
     assert o["tokens"][0, 1] == (3 if g2 == 3 else g2) and o["len"][0] == (2 if g2 == 3 else 1)
     assert o["len"][1] == 0 and o["tokens"][1, 0] == g0[1]
     assert o["len"][2] == -1 and (o["tokens"][2] == -1).all()
+
+
+# ------------------------------------------------------ TV distillation loss --
+def _tv_ref(a, d, T=1.0):
+    """scipy softmaxes; TV = 1 - sum min(p, q) (an identity, not the oracle's sum)."""
+    P, Q = probs(a, T), probs(d, T)
+    return 1.0 - np.minimum(P, Q).sum()
+
+
+def test_tv_loss_closed_forms():
+    rng = np.random.default_rng(3)
+    a = rng.normal(0, 2, (3, 50)).astype(np.float32)
+    loss, g = oracle.tv_loss(a, a.copy(), 1.0)
+    assert np.all(loss == 0.0) and np.all(g == 0.0)  # identical rows
+    p = np.full((2, 10), -np.inf, dtype=np.float32)
+    q = np.full((2, 10), -np.inf, dtype=np.float32)
+    p[:, :4] = rng.normal(0, 1, (2, 4))
+    q[:, 4:] = rng.normal(0, 1, (2, 6))
+    loss, _ = oracle.tv_loss(p, q, 1.0)
+    assert np.allclose(loss, 1.0, rtol=0, atol=1e-15)  # disjoint supports
+    # two tokens: TV = |sigmoid(x / T) - sigmoid(y / T)|
+    from scipy.special import expit
+    xs = rng.normal(0, 3, 20).astype(np.float32)
+    ys = rng.normal(0, 3, 20).astype(np.float32)
+    z = np.zeros(20, dtype=np.float32)
+    for T in (1.0, 0.6):
+        loss, _ = oracle.tv_loss(np.stack([xs, z], 1), np.stack([ys, z], 1), T)
+        ref = np.abs(expit(xs.astype(np.float64) / T) - expit(ys.astype(np.float64) / T))
+        assert np.allclose(loss, ref, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("dtype,T", [("f32", 1.0), ("bf16", 1.0), ("f32", 0.7)])
+def test_tv_loss_is_one_minus_acceptance(dtype, T):
+    """TV(p, q) = 1 - sum min(p, q): one minus the acceptance probability of a
+    drawn draft (the quantity the TV term is chosen to govern)."""
+    p, q = synth.pair(4, 3, 3, 3000, dtype, seed=8, sd_a=2.0, mode=0, sd_noise=1.0)
+    loss, _ = oracle.tv_loss(p, q, T, grad=False)
+    a, d = _as64(p).reshape(12, -1), _as64(q).reshape(12, -1)
+    ref = np.array([_tv_ref(a[r], d[r], T) for r in range(12)])
+    assert np.allclose(loss, ref, rtol=1e-12, atol=1e-14)
+
+
+def _as64(x):
+    return (synth.bf16_to_f32(x) if x.dtype == np.uint16 else x).astype(np.float64)
+
+
+def test_tv_grad_finite_differences():
+    """The gradient with respect to the student logits against central
+    differences of the loss (scipy softmaxes in fp64) at random points away
+    from the kinks p_v = q_v."""
+    rng = np.random.default_rng(4)
+    R, V = 5, 9
+    a = rng.normal(0, 1.5, (R, V)).astype(np.float32)
+    d = rng.normal(0, 1.5, (R, V)).astype(np.float32)
+    w = rng.uniform(0.5, 2.0, R)
+    for T in (1.0, 0.8):
+        _, g = oracle.tv_loss(a, d, T, row_weights=w)
+        h = 1e-6
+        for r in range(R):
+            fd = np.zeros(V)
+            for j in range(V):
+                dp = d[r].astype(np.float64).copy()
+                dm = dp.copy()
+                dp[j] += h
+                dm[j] -= h
+                fd[j] = (_tv_ref(a[r], dp, T) - _tv_ref(a[r], dm, T)) / (2 * h)
+            assert np.allclose(g[r], w[r] * fd, rtol=1e-6, atol=1e-8), (r, g[r], w[r] * fd)
+
+
+def test_tv_grad_invariants_and_errors():
+    p, q = synth.pair(3, 2, 2, 500, "bf16", seed=5, sd_a=2.0, mode=0, sd_noise=1.0)
+    loss, g = oracle.tv_loss(p, q, 1.0)
+    assert np.allclose(g.sum(axis=1), 0.0, atol=1e-15)  # adding a constant to a row changes nothing
+    assert np.all((loss > 0) & (loss < 1))
+    _, g2 = oracle.tv_loss(p, q, 1.0, row_weights=np.full(6, 3.0))
+    assert np.allclose(g2, 3.0 * g, rtol=1e-15, atol=0)
+    qf = synth.bf16_to_f32(q).copy()
+    qf[0, 1, 7] = np.nan
+    qf[1, 0, :] = -np.inf
+    pf = synth.bf16_to_f32(p).copy()
+    pf[2, 1, 3] = np.inf
+    loss, g = oracle.tv_loss(pf, qf, 1.0)
+    bad = [1, 2, 5]
+    assert np.all(np.isnan(loss[bad])) and np.all(np.isnan(g[bad]))
+    ok = [0, 3, 4]
+    assert np.all(np.isfinite(loss[ok])) and np.all(np.isfinite(g[ok]))
