@@ -228,6 +228,24 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed):
          {"note": "candidates (4 launches) + verification of deterministic candidates (4 launches)"})
     del copies, wsc, wsv
     torch.cuda.empty_cache()
+
+    # TV distillation loss, forward and backward: teacher and student logits
+    # [2048, 151936] bf16 (8 sequences x 256 positions), gradient in bf16.
+    w = synth.WORKLOADS["tvloss"]
+    Rt, Vt = w["R"], w["V"]
+    p, q = synth.tv_inputs(seed=seed)
+    pd, qd = to_dev(p, torch, dev), to_dev(q, torch, dev)
+    del p, q
+    wts = torch.full((Rt,), 1.0 / Rt, dtype=torch.float32, device=dev)
+    ws = torch.empty(psi.workspace_bytes(Rt, 2, Vt, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+    outs = dict(loss=torch.empty((Rt,), dtype=torch.float64, device=dev),
+                grad=torch.empty((Rt, Vt), dtype=torch.bfloat16, device=dev))
+    ms = time_calls(torch, lambda i: psi.tv_loss(pd, qd, temperature=1.0, row_weights=wts, out=outs, workspace=ws,
+                                                  stream=stream), max(steps // 5, 5), 2, stream)
+    line("tvloss_fwd_bwd_R2048_V151936_bf16", ms, Rt * Vt * 6, Rt,
+         {"note": "algorithmic bytes: teacher and student logits read once, bf16 gradient written once"})
+    del pd, qd, ws, outs
+    torch.cuda.empty_cache()
     return res
 
 

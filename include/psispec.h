@@ -133,6 +133,7 @@ typedef struct psispec_params {
  *   psispec_verify_tree    rows_per_req = 2*(N + 1)
  *   psispec_tree_candidates rows_per_req = K
  *   psispec_verify_tree_det rows_per_req = N + 1
+ *   psispec_tv_loss         B = R, rows_per_req = 2
  * Returns 0 for arguments out of range. Pure host function.
  */
 size_t psispec_workspace_bytes(int64_t B, int32_t rows_per_req, int32_t V, int dtype);
@@ -278,6 +279,31 @@ int psispec_verify_tree_det(const void* p_logits, int dtype, int64_t B, int32_t 
                             const int32_t* parent, const int32_t* node_tokens, const psispec_params* params,
                             int32_t* out_tokens, int32_t* out_path, int32_t* out_len, void* workspace,
                             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Total-variation distillation loss (Uno explainer §3.2, Diffusion
+ * Distillation: one forward gives the frozen AR teacher's logits and the
+ * diffusion student's; the TV term minimises the total-variation distance of
+ * the two token distributions of every position, which governs the verifier's
+ * acceptance since sum_v min(p_v, q_v) = 1 - TV).
+ *   p_logits     [R, V] teacher logits; q_logits [R, V] student logits.
+ *   temperature  > 0: p = softmax(p_logits / T), q = softmax(q_logits / T).
+ *   row_weights  nullable [R] float: upstream gradient of each row's loss
+ *                (e.g. 1/R for a mean); NULL means 1.
+ *   out_loss     [R] double out: 1/2 sum_v |p_v - q_v|.
+ *   out_grad     nullable [R, V] out, in the logits' dtype (bf16: rounded to
+ *                nearest even): the gradient of w_r * loss_r with respect to
+ *                the student logits, w_r q_j (g_j - sum_v g_v q_v) / T with
+ *                g_v = sign(q_v - p_v) / 2 (0 where q_v == p_v). The teacher is
+ *                frozen and gets no gradient. NULL computes the loss only.
+ * p and q are evaluated in binary32 from binary32-grade normalisers (about
+ * 1e-7 relative); the loss is accumulated in fp64. A row with a NaN or +inf
+ * logit, or entirely -inf, gets a NaN loss and a NaN gradient row.
+ * Workspace: psispec_workspace_bytes(R, 2, V, dtype).
+ */
+int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64_t R, int32_t V, float temperature,
+                    const float* row_weights, double* out_loss, void* out_grad, void* workspace, size_t ws_bytes,
+                    hipStream_t stream);
 
 /*
  * Benchmark timing hook (not part of the method; for measuring each kernel of

@@ -11,6 +11,7 @@ Function names mirror the C ABI in include/psispec.h:
   verify_tree    psispec_verify_tree
   tree_candidates  psispec_tree_candidates
   verify_tree_det  psispec_verify_tree_det
+  tv_loss          psispec_tv_loss
 """
 from __future__ import annotations
 
@@ -45,7 +46,7 @@ class Params(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libpsispec.so is not built ({LIB_PATH}); run "
-                          "`python -m lossless_speculative_verification_amd.build`")
+                          "`python lossless_speculative_verification_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.psispec_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
@@ -66,6 +67,8 @@ def _load():
     L.psispec_verify_tree_det.argtypes = [P, ctypes.c_int, i64, i32, i32, P, P, ctypes.POINTER(Params), P, P, P,
                                           P, sz, P]
     L.psispec_verify_tree_det.restype = ctypes.c_int
+    L.psispec_tv_loss.argtypes = [P, P, ctypes.c_int, i64, i32, ctypes.c_float, P, P, P, P, sz, P]
+    L.psispec_tv_loss.restype = ctypes.c_int
     L.psispec_strerror.argtypes = [ctypes.c_int]
     L.psispec_strerror.restype = ctypes.c_char_p
     L.psispec_version.argtypes = []
@@ -315,4 +318,27 @@ def verify_tree_det(p: torch.Tensor, parent: torch.Tensor, node_tokens: torch.Te
                                      _ptr(out["tokens"]), _ptr(out["path"]), _ptr(out["len"]), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream))
     _check("psispec_verify_tree_det", rc)
+    return out
+
+
+def tv_loss(p: torch.Tensor, q: torch.Tensor, temperature=1.0, row_weights: torch.Tensor | None = None, grad=True,
+            out=None, workspace=None, stream=None) -> dict:
+    """psispec_tv_loss. Teacher logits p and student logits q [..., V] (same
+    shape and dtype). Returns dict(loss [R] float64, grad [R, V] in the logits'
+    dtype or None), R = the product of the leading dimensions."""
+    assert p.is_cuda and q.is_cuda and p.is_contiguous() and q.is_contiguous()
+    assert p.shape == q.shape and p.dtype == q.dtype
+    V = p.shape[-1]
+    R = p.numel() // V
+    dt = dtype_code(p)
+    dev = p.device
+    if row_weights is not None:
+        assert row_weights.is_cuda and row_weights.dtype == torch.float32 and row_weights.numel() == R
+    if out is None:
+        out = dict(loss=torch.empty((R,), dtype=torch.float64, device=dev),
+                   grad=torch.empty((R, V), dtype=p.dtype, device=dev) if grad else None)
+    ws = _workspace(workspace, workspace_bytes(R, 2, V, dt), dev)
+    rc = lib.psispec_tv_loss(_ptr(p), _ptr(q), dt, R, V, float(temperature), _ptr(row_weights), _ptr(out["loss"]),
+                             _ptr(out.get("grad")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("psispec_tv_loss", rc)
     return out

@@ -373,6 +373,25 @@ int psispec_verify_tree_det(const void* p_logits, int dtype, int64_t B, int32_t 
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 
+int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64_t R, int32_t V, float temperature,
+                    const float* row_weights, double* out_loss, void* out_grad, void* workspace, size_t ws_bytes,
+                    hipStream_t stream) {
+  if (!p_logits || !q_logits || !out_loss || !workspace) return PSISPEC_EINVAL;
+  if (R <= 0 || V <= 0 || !(temperature > 0.0f) || !isfinite(temperature)) return PSISPEC_EINVAL;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
+  if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
+  if (ws_bytes < psispec_workspace_bytes(R, 2, V, dtype)) return PSISPEC_EWORKSPACE;
+  psispec_params prm = {};
+  prm.temperature = temperature;
+  prm.top_p = 1.0f;
+  LinCfg c;
+  fill_common(c, p_logits, q_logits, dtype, R, 1, V, &prm, workspace, 1);
+  c.aligned = c.aligned && (out_grad == nullptr || aligned16(out_grad));
+  timing_begin(stream);
+  const hipError_t e = launch_tv_loss(c, row_weights, out_loss, out_grad, (double)temperature, dtype, stream);
+  return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+}
+
 const char* psispec_strerror(int status) {
   switch (status) {
     case PSISPEC_OK:

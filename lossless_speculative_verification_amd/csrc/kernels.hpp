@@ -266,6 +266,10 @@ hipError_t launch_filter_rows(const LinCfg& c, const FiltCfg& f, int64_t rows, i
 hipError_t launch_tree_candidates(const LinCfg& c, const FiltCfg& f, const CandCfg& cc, int dtype, hipStream_t s);
 hipError_t launch_verify_tree_det(const LinCfg& c, const DTreeCfg& d, int dtype, hipStream_t s);
 hipError_t launch_stats32(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
+// Total-variation distillation loss (tv.hip): c.rows holds one teacher (p) and
+// one student (q) row per loss row (c.B rows).
+hipError_t launch_tv_loss(const LinCfg& c, const float* w_row, double* loss, void* grad, double T, int dtype,
+                          hipStream_t s);
 hipError_t launch_argmax(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
 // fp64 draft-row sub-block records of the first `rows` rows of c.rows.q (linear.hip).
 hipError_t launch_draftpass(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);

@@ -67,6 +67,7 @@ RECIPES = {
     "filtered": dict(sd_a=2.0, n_heavy=0, boost=0.0, mode=0, rho=0.0, sd_noise=0.5),
     "tree": dict(sd_a=3.0, n_heavy=20, boost=8.0, mode=1, rho=0.85, sd_noise=3.0),
     "treesampler": dict(sd_a=3.0, n_heavy=20, boost=8.0, mode=1, rho=0.85, sd_noise=3.0),
+    "tvloss": dict(sd_a=3.0, n_heavy=20, boost=8.0, mode=1, rho=0.85, sd_noise=3.0),
 }
 
 # Shapes and sampling parameters per workload.
@@ -80,6 +81,9 @@ WORKLOADS = {
     # Tree Sampler: a block of 16 draft positions, 32 candidates per position,
     # 32 kept prefixes, verified against one target row per prefix plus the root
     "treesampler": dict(B=4, K=16, cands=32, nodes=32, V=151936, dtype="bf16", temperature=1.0),
+    # TV distillation loss: 8 sequences x 256 noisy positions, teacher and
+    # student logits per position, forward and backward
+    "tvloss": dict(R=2048, V=151936, dtype="bf16", temperature=1.0),
 }
 WORKLOADS_RECIPE = {"greedy": "filtered"}
 
@@ -141,6 +145,16 @@ def treesampler_inputs(seed=0, B=None, K=None, nodes=None, V=None, nthreads=None
     nodes = nodes or w["nodes"]
     V = V or w["V"]
     return pair(B, nodes + 1, K, V, w["dtype"], seed=seed, nthreads=nthreads, **RECIPES["treesampler"])
+
+
+def tv_inputs(seed=0, R=None, V=None, nthreads=None):
+    """(teacher p [R, V], student q [R, V]) for the TV-loss workload; row r of
+    q is correlated with row r of p."""
+    w = WORKLOADS["tvloss"]
+    R = R or w["R"]
+    V = V or w["V"]
+    p, q = pair(R, 1, 1, V, w["dtype"], seed=seed, nthreads=nthreads, **RECIPES["tvloss"])
+    return p.reshape(R, V), q.reshape(R, V)
 
 
 def branch_chain_parent(branches=4, depth=8):

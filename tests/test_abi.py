@@ -167,3 +167,24 @@ def test_verify_tree_det_argument_errors(psi):
     assert _call_det(psi, prm=psi.make_params(top_p=0.9)) == psi.EUNSUPPORTED
     assert _call_det(psi, ws_bytes=16) == psi.EWORKSPACE
     assert _call_det(psi, ws_addr=(1 << 20) + 4) == psi.EINVAL
+
+
+def test_tv_loss_argument_errors(psi):
+    f = {k: ctypes.c_void_p(0x10000000 + 0x1000 * i) for i, k in enumerate(["p", "q", "loss", "grad"])}
+
+    def call(R=4, V=100, dtype=1, T=1.0, ws_bytes=1 << 30, ws_addr=1 << 20, null=None):
+        a = dict(f)
+        if null:
+            a[null] = None
+        return psi.lib.psispec_tv_loss(a["p"], a["q"], dtype, R, V, T, None, a["loss"], a["grad"],
+                                       ctypes.c_void_p(ws_addr), ws_bytes, None)
+
+    for k in ("p", "q", "loss"):
+        assert call(null=k) == psi.EINVAL
+    assert call(R=0) == psi.EINVAL
+    assert call(V=0) == psi.EINVAL
+    assert call(T=0.0) == psi.EINVAL
+    assert call(T=float("inf")) == psi.EINVAL
+    assert call(dtype=2) == psi.EUNSUPPORTED
+    assert call(ws_bytes=8) == psi.EWORKSPACE
+    assert call(ws_addr=(1 << 20) + 16) == psi.EINVAL
