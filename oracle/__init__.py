@@ -298,3 +298,60 @@ def tv_loss(p, q, temperature=1.0, row_weights=None, grad=True, nthreads=1):
     if rc != 0:
         raise ValueError("orc_tv_loss rejected its arguments")
     return loss, g
+
+
+def generate(model, prompt, block, V, temperature, seed, rounds, nthreads=1):
+    """Multi-round Psi-Spec generation ("Uno" research explainer, §3.3): each
+    round draws the block's first token from the AR (target) model at the
+    committed context (it is always kept), draws the other block - 1 positions
+    from the drafter in parallel, scores them with the target model in one
+    pass, verifies them (linear rule) and commits the first token, the
+    accepted drafts and the final token; rejected drafts are dropped. So a
+    round commits between 2 and block + 1 tokens and, with one draft pass and
+    one verify pass per round, tokens per forward pass lie in [1, (block+1)/2].
+
+    model(kind, ctx [rows, 2] int32, pos [rows] int32 or None) -> logits
+    [rows, V] (float32 or bf16 bits): kind 0 is the target at context (t1, t2)
+    (the last two tokens), kind 1 the drafter at block position pos.
+    prompt [B, 2] int32: the last two tokens of each request's context.
+    Random numbers: the first token of round r is drawn as draft 0 of a
+    one-row draft call with step 2r; the drafts and the verification use
+    step 2r + 1. Returns dict(seq [B, rounds * (block + 1)] (-1 padded),
+    len [B], round_tokens [B, rounds], margin_acc [B, rounds] (the smallest
+    |u - min(1, p/q)| of the round's accept tests) and margin_cdf [B, rounds]
+    (the smallest inverse-CDF margin of the round's draws))."""
+    prompt = np.ascontiguousarray(prompt, dtype=np.int32).reshape(-1, 2)
+    B = prompt.shape[0]
+    K = block - 1
+    L = rounds * (block + 1)
+    seq = np.full((B, L), -1, dtype=np.int32)
+    ln = np.zeros(B, dtype=np.int32)
+    rt = np.zeros((B, rounds), dtype=np.int32)
+    ma = np.ones((B, rounds), dtype=np.float64)
+    mc = np.ones((B, rounds), dtype=np.float64)
+    t1, t2 = prompt[:, 0].copy(), prompt[:, 1].copy()
+    for r in range(rounds):
+        # first position: the target model itself
+        p0 = model(0, np.stack([t1, t2], 1), None).reshape(B, 1, V)
+        x0, m0 = draft_sample(p0, temperature, seed=seed, step=2 * r, nthreads=nthreads)
+        x0 = x0[:, 0]
+        # drafts at positions 1 .. K, from the committed context and x0
+        cq = np.repeat(np.stack([t2, x0], 1), K, axis=0)
+        pq = np.tile(np.arange(1, K + 1, dtype=np.int32), B)
+        q = model(1, cq, pq).reshape(B, K, V)
+        d, md = draft_sample(q, temperature, seed=seed, step=2 * r + 1, nthreads=nthreads)
+        # target rows: row i scores draft i given (prefix, x0, d_0 .. d_{i-1}); row K is the bonus row
+        hist = np.concatenate([t2[:, None], x0[:, None], d], axis=1)  # [B, K + 2]
+        cp = np.stack([hist[:, :K + 1], hist[:, 1:K + 2]], axis=2).reshape(-1, 2)
+        p = model(0, cp, None).reshape(B, K + 1, V)
+        v = verify_linear(p, q, d, temperature, seed=seed, step=2 * r + 1, nthreads=nthreads)
+        for b in range(B):
+            n = int(v["len"][b])
+            toks = [int(x0[b])] + [int(t) for t in v["tokens"][b, :n + 1]]
+            seq[b, ln[b]:ln[b] + len(toks)] = toks
+            ln[b] += len(toks)
+            rt[b, r] = len(toks)
+            ma[b, r] = float(v["margin_acc"][b])
+            mc[b, r] = min(float(m0[b, 0]), float(md[b].min()), float(v["margin_cdf"][b]))
+            t1[b], t2[b] = seq[b, ln[b] - 2], seq[b, ln[b] - 1]
+    return dict(seq=seq, len=ln, round_tokens=rt, margin_acc=ma, margin_cdf=mc)

@@ -13,6 +13,8 @@ accept-length range the correlation knob is meant to cover):
   highconc   B=256, K=8,  V=151936, bf16, same as qwen,                       rho in {0.5, 0.8, 0.95}
   filtered   B=128, K=16, V=128256, fp32, a ~ N(0, 2^2),                     d = a + N(0, 0.5^2)
   tree       B=4,   N=32, V=151936, bf16, same as qwen,                       rho = 0.85
+  toy model  an order-2 synthetic language model (target and drafter logits from
+             the last two tokens) for multi-round generation; see syn_toy_logits
 """
 from __future__ import annotations
 
@@ -28,7 +30,8 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 
 def build() -> str:
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared", "-o", _LIB, _SRC, "-lm", "-lpthread"]
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fPIC", "-shared", "-o", _LIB, _SRC, "-lm",
+           "-lpthread"]
     subprocess.run(cmd, check=True)
     return _LIB
 
@@ -51,6 +54,10 @@ def lib():
         L.syn_randint.restype = ctypes.c_int
         L.syn_normal.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64, P]
         L.syn_normal.restype = ctypes.c_int
+        L.syn_toy_logits.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, P, P, ctypes.c_int,
+                                     ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                     ctypes.c_int, P]
+        L.syn_toy_logits.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -190,3 +197,29 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return u.astype(np.uint16)
+
+
+# Toy order-2 model of the multi-round generation workload: target logits
+# sd * z + boost on about n_heavy / 1024 of the tokens per context; the drafter
+# rho * a + noise * z' per block position.
+TOY_MODEL = dict(seed=1234, sd=2.0, n_heavy=1, boost=6.0, rho=0.8, noise=1.5)
+
+
+def toy_logits(ctx, pos=None, V=32768, kind=0, dtype="bf16", model=None):
+    """Toy-model logits [rows, V]: ctx [rows, 2] int32 (last two tokens), pos
+    [rows] int32 block positions (draft kind only). kind 0 = target, 1 = draft.
+    float32, or uint16 bfloat16 bits."""
+    m = dict(TOY_MODEL)
+    m.update(model or {})
+    ctx = np.ascontiguousarray(ctx, dtype=np.int32).reshape(-1, 2)
+    rows = ctx.shape[0]
+    pp = None if pos is None else np.ascontiguousarray(pos, dtype=np.int32).reshape(rows)
+    bf16 = dtype == "bf16"
+    out = np.empty((rows, V), dtype=np.uint16 if bf16 else np.float32)
+    rc = lib().syn_toy_logits(int(m["seed"]), rows, int(V), ctx.ctypes.data_as(ctypes.c_void_p),
+                              None if pp is None else pp.ctypes.data_as(ctypes.c_void_p), int(kind), float(m["sd"]),
+                              int(m["n_heavy"]), float(m["boost"]), float(m["rho"]), float(m["noise"]), int(bf16),
+                              out.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError("syn_toy_logits rejected its arguments")
+    return out

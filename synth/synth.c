@@ -172,3 +172,52 @@ int syn_normal(uint64_t seed, uint64_t stream, int64_t count, double* out) {
   for (int64_t i = 0; i < count; ++i) out[i] = normal_at(seed, stream, (uint64_t)i);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Toy order-2 language model, a synthetic stand-in for the AR target and the
+ * diffusion drafter of a multi-round generation loop. Integer mixing and
+ * fixed-order double arithmetic only, so that a GPU implementation written
+ * from this definition gives the same bits:
+ *   ctx  = (uint32 t1 << 32) | uint32 t2   (the last two tokens)
+ *   r    = bits64(seed, ctx, v)            (SplitMix64 construction above)
+ *   z(r) = ((sum of the four 16-bit fields of r) / 65536 - 2) * sqrt(3)
+ *          (an Irwin-Hall approximation of a standard normal)
+ *   target a(v | ctx) = float(sd * z(r) + (top 10 bits of splitmix64(r) < n_heavy ? boost : 0))
+ *   draft  d(v | ctx, i) = float(rho * a + noise * z(bits64(seed ^ K_DRAFT, ctx * 64 + i, v)))
+ * with every double operation rounded on its own (no fused multiply-add),
+ * then bfloat16 by round-to-nearest-even (or float32 kept). */
+#define TOY_DRAFT_KEY 0xA5A5A5A55A5A5A5Aull
+static inline double toy_z(uint64_t r) {
+  const uint64_t s = (r & 0xffffull) + ((r >> 16) & 0xffffull) + ((r >> 32) & 0xffffull) + (r >> 48);
+  const double u = (double)s / 65536.0 - 2.0;
+  return u * 1.7320508075688772;
+}
+
+static inline float toy_target(uint64_t seed, uint64_t ctx, int v, double sd, int n_heavy, double boost) {
+  const uint64_t r = bits64(seed, ctx, (uint64_t)v);
+  double a = sd * toy_z(r);
+  if ((int)(splitmix64(r) >> 54) < n_heavy) a = a + boost;
+  return (float)a;
+}
+
+/* Logits of `rows` rows: row k has context ctx[2k], ctx[2k+1] (t1, t2); kind 0
+ * gives the target, kind 1 the draft at position pos[k]. */
+int syn_toy_logits(uint64_t seed, int64_t rows, int V, const int32_t* ctx, const int32_t* pos, int kind, float sd,
+                   int n_heavy, float boost, float rho, float noise, int bf16, void* out) {
+  if (rows <= 0 || V <= 0 || !ctx || !out || (kind == 1 && !pos)) return -1;
+  for (int64_t k = 0; k < rows; ++k) {
+    const uint64_t c = ((uint64_t)(uint32_t)ctx[2 * k] << 32) | (uint64_t)(uint32_t)ctx[2 * k + 1];
+    for (int v = 0; v < V; ++v) {
+      const float a = toy_target(seed, c, v, (double)sd, n_heavy, (double)boost);
+      float x = a;
+      if (kind == 1) {
+        const double zn = toy_z(bits64(seed ^ TOY_DRAFT_KEY, c * 64u + (uint64_t)(uint32_t)pos[k], (uint64_t)v));
+        const double t1 = (double)rho * (double)a;
+        const double t2 = (double)noise * zn;
+        x = (float)(t1 + t2);
+      }
+      store(out, bf16, (size_t)k * (size_t)V + (size_t)v, x);
+    }
+  }
+  return 0;
+}

@@ -908,3 +908,67 @@ def test_tv_grad_invariants_and_errors():
     assert np.all(np.isnan(loss[bad])) and np.all(np.isnan(g[bad]))
     ok = [0, 3, 4]
     assert np.all(np.isfinite(loss[ok])) and np.all(np.isfinite(g[ok]))
+
+
+# ------------------------------------------------- multi-round generation --
+def _toy(V, dtype="f32"):
+    return lambda kind, ctx, pos: synth.toy_logits(ctx, pos, V=V, kind=kind, dtype=dtype)
+
+
+@pytest.mark.parametrize("T,block", [(1.0, 4), (0.7, 3)])
+def test_generate_law(T, block):
+    """Losslessness across rounds: the joint law of the first three generated
+    tokens of 30,000 independent requests equals the toy target model's own
+    autoregressive law (chi-square over the 125 outcomes, exact probabilities
+    from scipy softmaxes of the target logits)."""
+    V, B = 5, 30000
+    model = _toy(V)
+    prompt = np.tile(np.array([[3, 1]], dtype=np.int32), (B, 1))
+    g = oracle.generate(model, prompt, block, V, T, seed=21, rounds=2, nthreads=8)
+    assert np.all(g["len"] >= 3)
+    s = g["seq"][:, :3]
+    counts = np.zeros(V ** 3)
+    np.add.at(counts, s[:, 0] * V * V + s[:, 1] * V + s[:, 2], 1)
+    exp = np.zeros(V ** 3)
+    for a in range(V):
+        pa = probs(model(0, np.array([[3, 1]]), None)[0], T)[a]
+        for b in range(V):
+            pb = probs(model(0, np.array([[1, a]]), None)[0], T)[b]
+            pc = probs(model(0, np.array([[a, b]]), None)[0], T)
+            exp[a * V * V + b * V:a * V * V + b * V + V] = pa * pb * pc
+    assert abs(exp.sum() - 1.0) < 1e-12
+    assert chi2_pvalue(counts, B * exp) > 1e-3
+
+
+def test_generate_round_bounds():
+    """Each round commits between 2 and block + 1 tokens (so tokens per forward
+    pass, with one draft and one verify pass per round, lie in [1, (block+1)/2]),
+    and the committed sequence is the concatenation of the rounds."""
+    V, B, block, R = 300, 64, 8, 6
+    g = oracle.generate(_toy(V, "bf16"), synth.randint(4, 0, 2 * B, V).reshape(B, 2), block, V, 1.0, seed=5,
+                        rounds=R, nthreads=8)
+    rt = g["round_tokens"]
+    assert rt.min() >= 2 and rt.max() <= block + 1 and len(set(rt.ravel().tolist())) >= 3
+    assert np.array_equal(g["len"], rt.sum(axis=1))
+    tpf = g["len"].sum() / (2 * R * B)
+    assert 1.0 <= tpf <= (block + 1) / 2
+    for b in range(B):
+        assert np.all(g["seq"][b, :g["len"][b]] >= 0) and np.all(g["seq"][b, g["len"][b]:] == -1)
+
+
+def test_generate_greedy_is_the_argmax_chain():
+    """Temperature 0: the generated sequence is the target's greedy chain
+    (argmax of the toy target at each context, lowest id on ties)."""
+    V, B, block, R = 200, 8, 5, 4
+    model = _toy(V)
+    prompt = synth.randint(9, 0, 2 * B, V).reshape(B, 2)
+    g = oracle.generate(model, prompt, block, V, 0.0, seed=0, rounds=R)
+    for b in range(B):
+        t1, t2 = int(prompt[b, 0]), int(prompt[b, 1])
+        chain = []
+        while len(chain) < g["len"][b]:
+            a = model(0, np.array([[t1, t2]]), None)[0]
+            x = int(np.argmax(a))
+            chain.append(x)
+            t1, t2 = t2, x
+        assert chain == g["seq"][b, :g["len"][b]].tolist()
