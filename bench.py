@@ -246,6 +246,32 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed):
          {"note": "algorithmic bytes: teacher and student logits read once, bf16 gradient written once"})
     del pd, qd, ws, outs
     torch.cuda.empty_cache()
+
+    # Multi-round generation on the toy order-2 model: 64 requests, block 8
+    # (7 drafts), V=32768 bf16, T=1, 32 rounds per call; every step (toy model
+    # passes, draft sampling, verification, commit) runs on the device.
+    Bg, blk, Vg, Rg = 64, 8, 32768, 32
+    prompt = torch.from_numpy(synth.randint(seed, 0, 2 * Bg, Vg).reshape(Bg, 2)).to(dev)
+    m = synth.TOY_MODEL
+    tm = psi.toy_model(m["seed"], m["sd"], m["n_heavy"], m["boost"], m["rho"], m["noise"])
+    wsg = torch.empty(int(psi.lib.psispec_generate_workspace_bytes(Bg, blk, Vg, psi.DTYPE_BF16)), dtype=torch.uint8,
+                      device=dev)
+    outs = dict(seq=torch.empty((Bg, Rg * (blk + 1)), dtype=torch.int32, device=dev),
+                len=torch.empty((Bg,), dtype=torch.int32, device=dev),
+                round_tokens=torch.empty((Bg, Rg), dtype=torch.int32, device=dev))
+    ms = time_calls(torch, lambda i: psi.generate_toy(prompt, blk, Vg, Rg, temperature=1.0, seed=seed, step=2 * Rg * i,
+                                                       model=tm, out=outs, workspace=wsg, stream=stream),
+                    max(steps // 10, 3), 1, stream)
+    toks = int(outs["len"].sum().item())
+    res["generate_toy_B64_block8_V32768_bf16"] = {
+        "us_per_call": 1e3 * ms, "rounds": Rg, "us_per_round": 1e3 * ms / Rg, "tokens_per_s": toks / (ms * 1e-3),
+        "tpf": toks / (2.0 * Rg * Bg), "tpf_bounds": [1.0, (blk + 1) / 2.0],
+        "note": "toy order-2 model; per round: target row, drafter rows, target rows, draft sampling, "
+                "verification, commit"}
+    print(f"# generate_toy: {1e3 * ms / Rg:.1f} us/round, TPF {toks / (2.0 * Rg * Bg):.3f}", file=sys.stderr,
+          flush=True)
+    del wsg, outs
+    torch.cuda.empty_cache()
     return res
 
 

@@ -306,6 +306,68 @@ int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64
                     hipStream_t stream);
 
 /*
+ * Synthetic order-2 toy language model: a stand-in for the AR target and the
+ * diffusion drafter in tests and benchmarks of multi-round generation (it is
+ * not part of the method). Logits depend on the last two tokens (t1, t2):
+ *   ctx  = (uint32 t1 << 32) | uint32 t2
+ *   bits(s, stream, i) = mix(mix(s ^ mix(stream * 0x632BE59BD9B4E019 + 0x2545F4914F6CDD1D))
+ *                            ^ (i * 0xD1B54A32D192ED03)),  mix = SplitMix64 (Steele, Lea,
+ *                        Flood, OOPSLA 2014)
+ *   z(r) = ((sum of the four 16-bit fields of r) / 65536 - 2) * sqrt(3)
+ *   target a(v) = float(sd * z(bits(seed, ctx, v)) + (top 10 bits of mix(r) < n_heavy ? boost : 0))
+ *   drafter at block position i:
+ *          d(v) = float(rho * a(v) + noise * z(bits(seed ^ 0xA5A5A5A55A5A5A5A, ctx * 64 + i, v)))
+ * every double operation rounded on its own, then bfloat16 (round to nearest
+ * even) or float32.
+ */
+typedef struct psispec_toy_model {
+  uint64_t seed;
+  float sd;
+  int32_t n_heavy; /* out of 1024 tokens, on average, get the boost */
+  float boost;
+  float rho;
+  float noise;
+  uint32_t reserved; /* must be 0 */
+} psispec_toy_model;
+
+/*
+ * Toy-model logits of `rows` rows into out [rows, V] (dtype): ctx [rows, 2]
+ * int32 (t1, t2) and, for kind 1 (drafter), pos [rows] int32 block positions;
+ * kind 0 is the target. Device pointers; enqueued on `stream`.
+ */
+int psispec_toy_logits(int64_t rows, int32_t V, const int32_t* ctx, const int32_t* pos, int kind,
+                       const psispec_toy_model* model, int dtype, void* out, hipStream_t stream);
+
+/*
+ * Multi-round Psi-Spec generation (Uno explainer §3.3: each round is one draft
+ * pass and one verify pass; the block's first position comes from the AR
+ * weights and is always kept; the other block - 1 positions are proposed in
+ * parallel; the verifier keeps the longest accepted prefix and adds the
+ * residual or bonus token, and the rejected drafts are dropped; tokens per
+ * forward pass lie in [1, (block + 1) / 2]) on the toy model, all requests in
+ * parallel, every step on the device. Round r:
+ *   x0    = psispec_draft_sample of the target row at (t1, t2), step + 2r;
+ *   d     = psispec_draft_sample of the drafter rows at (t2, x0), positions
+ *           1 .. block - 1, step + 2r + 1;
+ *   p     = target rows at (h_i, h_{i+1}), h = (t2, x0, d_0 .. d_{block-2});
+ *   verify = psispec_verify_linear(p, drafter rows, d), step + 2r + 1;
+ *   commit x0, the accepted drafts and the final token; (t1, t2) advance.
+ *   params       temperature (0 = greedy), seed and step (top_k / top_p must
+ *                be disabled).
+ *   prompt       [B, 2] int32 (t1, t2) of each request.
+ *   block        2 .. 65 (so block - 1 <= PSISPEC_MAX_K drafts).
+ *   out_seq      [B, rounds * (block + 1)] int32 out: the committed tokens, -1 padded.
+ *   out_len      [B] int32 out: committed tokens (-1 after a verification error).
+ *   out_round_tokens [B, rounds] int32 out: tokens committed by each round.
+ * Workspace: psispec_generate_workspace_bytes(B, block, V, dtype).
+ */
+size_t psispec_generate_workspace_bytes(int64_t B, int32_t block, int32_t V, int dtype);
+int psispec_generate_toy(int64_t B, int32_t block, int32_t V, int dtype, const psispec_toy_model* model,
+                         const psispec_params* params, const int32_t* prompt, int32_t rounds, int32_t* out_seq,
+                         int32_t* out_len, int32_t* out_round_tokens, void* workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
  * Benchmark timing hook (not part of the method; for measuring each kernel of
  * a call live on the caller's stream). While armed with n > 0 caller-created
  * HIP events, every compute entry point records events[0] on its stream before

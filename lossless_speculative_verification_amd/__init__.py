@@ -12,6 +12,8 @@ Function names mirror the C ABI in include/psispec.h:
   tree_candidates  psispec_tree_candidates
   verify_tree_det  psispec_verify_tree_det
   tv_loss          psispec_tv_loss
+  toy_logits       psispec_toy_logits (synthetic stand-in model)
+  generate_toy     psispec_generate_toy
 """
 from __future__ import annotations
 
@@ -43,6 +45,14 @@ class Params(ctypes.Structure):
                 ("reserved", ctypes.c_uint32)]
 
 
+class ToyModel(ctypes.Structure):
+    """psispec_toy_model (include/psispec.h)."""
+
+    _fields_ = [("seed", ctypes.c_uint64), ("sd", ctypes.c_float), ("n_heavy", ctypes.c_int32),
+                ("boost", ctypes.c_float), ("rho", ctypes.c_float), ("noise", ctypes.c_float),
+                ("reserved", ctypes.c_uint32)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libpsispec.so is not built ({LIB_PATH}); run "
@@ -69,6 +79,13 @@ def _load():
     L.psispec_verify_tree_det.restype = ctypes.c_int
     L.psispec_tv_loss.argtypes = [P, P, ctypes.c_int, i64, i32, ctypes.c_float, P, P, P, P, sz, P]
     L.psispec_tv_loss.restype = ctypes.c_int
+    L.psispec_toy_logits.argtypes = [i64, i32, P, P, ctypes.c_int, ctypes.POINTER(ToyModel), ctypes.c_int, P, P]
+    L.psispec_toy_logits.restype = ctypes.c_int
+    L.psispec_generate_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
+    L.psispec_generate_workspace_bytes.restype = sz
+    L.psispec_generate_toy.argtypes = [i64, i32, i32, ctypes.c_int, ctypes.POINTER(ToyModel),
+                                       ctypes.POINTER(Params), P, i32, P, P, P, P, sz, P]
+    L.psispec_generate_toy.restype = ctypes.c_int
     L.psispec_strerror.argtypes = [ctypes.c_int]
     L.psispec_strerror.restype = ctypes.c_char_p
     L.psispec_version.argtypes = []
@@ -341,4 +358,45 @@ def tv_loss(p: torch.Tensor, q: torch.Tensor, temperature=1.0, row_weights: torc
     rc = lib.psispec_tv_loss(_ptr(p), _ptr(q), dt, R, V, float(temperature), _ptr(row_weights), _ptr(out["loss"]),
                              _ptr(out.get("grad")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("psispec_tv_loss", rc)
+    return out
+
+
+def toy_model(seed=1234, sd=2.0, n_heavy=1, boost=6.0, rho=0.8, noise=1.5) -> ToyModel:
+    return ToyModel(int(seed) & (2**64 - 1), float(sd), int(n_heavy), float(boost), float(rho), float(noise), 0)
+
+
+def toy_logits(ctx: torch.Tensor, V: int, pos: torch.Tensor | None = None, kind=0, dtype=torch.bfloat16,
+               model: ToyModel | None = None, out=None, stream=None) -> torch.Tensor:
+    """psispec_toy_logits: ctx [rows, 2] int32 (and pos [rows] for kind 1) ->
+    logits [rows, V] of the synthetic toy model."""
+    assert ctx.is_cuda and ctx.dtype == torch.int32 and ctx.is_contiguous()
+    rows = ctx.numel() // 2
+    m = model if model is not None else toy_model()
+    out = out if out is not None else torch.empty((rows, V), dtype=dtype, device=ctx.device)
+    rc = lib.psispec_toy_logits(rows, int(V), _ptr(ctx), _ptr(pos), int(kind), ctypes.byref(m), dtype_code(out),
+                                _ptr(out), _stream(stream))
+    _check("psispec_toy_logits", rc)
+    return out
+
+
+def generate_toy(prompt: torch.Tensor, block: int, V: int, rounds: int, temperature=1.0, seed=0, step=0,
+                 dtype=torch.bfloat16, model: ToyModel | None = None, out=None, workspace=None, stream=None) -> dict:
+    """psispec_generate_toy: prompt [B, 2] int32 -> dict(seq [B, rounds*(block+1)],
+    len [B], round_tokens [B, rounds])."""
+    assert prompt.is_cuda and prompt.dtype == torch.int32 and prompt.is_contiguous()
+    B = prompt.numel() // 2
+    dev = prompt.device
+    m = model if model is not None else toy_model()
+    dt = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
+    if out is None:
+        out = dict(seq=torch.empty((B, rounds * (block + 1)), dtype=torch.int32, device=dev),
+                   len=torch.empty((B,), dtype=torch.int32, device=dev),
+                   round_tokens=torch.empty((B, rounds), dtype=torch.int32, device=dev))
+    nbytes = int(lib.psispec_generate_workspace_bytes(B, int(block), int(V), dt))
+    ws = _workspace(workspace, nbytes, dev)
+    prm = make_params(temperature, seed=seed, step=step)
+    rc = lib.psispec_generate_toy(B, int(block), int(V), dt, ctypes.byref(m), ctypes.byref(prm), _ptr(prompt),
+                                  int(rounds), _ptr(out["seq"]), _ptr(out["len"]), _ptr(out["round_tokens"]),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("psispec_generate_toy", rc)
     return out

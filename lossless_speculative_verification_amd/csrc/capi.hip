@@ -392,6 +392,66 @@ int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 
+int psispec_toy_logits(int64_t rows, int32_t V, const int32_t* ctx, const int32_t* pos, int kind,
+                       const psispec_toy_model* model, int dtype, void* out, hipStream_t stream) {
+  if (!ctx || !model || !out || rows <= 0 || V <= 0 || (kind != 0 && kind != 1) || (kind == 1 && !pos))
+    return PSISPEC_EINVAL;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
+  const hipError_t e = launch_toy_logits(rows, V, ctx, pos, kind, *model, dtype, out, stream);
+  return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+}
+
+size_t psispec_generate_workspace_bytes(int64_t B, int32_t block, int32_t V, int dtype) {
+  if (B <= 0 || block < 2 || block - 1 > PSISPEC_MAX_K || V <= 0) return 0;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return 0;
+  const int K = block - 1;
+  return gen_layout(B, K, V, elem_bytes(dtype), psispec_workspace_bytes(B, 2 * K + 1, V, dtype)).total;
+}
+
+int psispec_generate_toy(int64_t B, int32_t block, int32_t V, int dtype, const psispec_toy_model* model,
+                         const psispec_params* params, const int32_t* prompt, int32_t rounds, int32_t* out_seq,
+                         int32_t* out_len, int32_t* out_round_tokens, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (!model || !prompt || !out_seq || !out_len || !out_round_tokens || !workspace) return PSISPEC_EINVAL;
+  if (B <= 0 || V <= 0 || rounds <= 0 || block < 2) return PSISPEC_EINVAL;
+  if (int rc = check_params(params, V)) return rc;
+  if (params->top_k != 0 || params->top_p != 1.0f) return PSISPEC_EUNSUPPORTED;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
+  if (block - 1 > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
+  if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
+  if (ws_bytes < psispec_generate_workspace_bytes(B, block, V, dtype)) return PSISPEC_EWORKSPACE;
+  const int K = block - 1;
+  const int max_len = rounds * (block + 1);
+  const GenLayout L = gen_layout(B, K, V, elem_bytes(dtype), psispec_workspace_bytes(B, 2 * K + 1, V, dtype));
+  char* w = (char*)workspace;
+  const GenState g = gen_state(workspace, L, B, K);
+  void* first = w + L.first;
+  void* q = w + L.q;
+  void* p = w + L.p;
+  void* inner = w + L.inner;
+  psispec_params prm = *params;
+  prm.flags = 0;
+  hipError_t e = launch_gen_init(B, prompt, g, out_len, out_seq, max_len, stream);
+  for (int r = 0; r < rounds && e == hipSuccess; ++r) {
+    int rc = PSISPEC_OK;
+    prm.step = params->step + 2u * (uint32_t)r;
+    if ((e = launch_round_ctx(B, K, 0, g, stream)) != hipSuccess) break;
+    if ((e = launch_toy_logits(B, V, g.ctx, nullptr, 0, *model, dtype, first, stream)) != hipSuccess) break;
+    if ((rc = psispec_draft_sample(first, dtype, B, 1, V, &prm, g.x0, inner, L.inner_bytes, stream))) return rc;
+    prm.step = params->step + 2u * (uint32_t)r + 1u;
+    if ((e = launch_round_ctx(B, K, 1, g, stream)) != hipSuccess) break;
+    if ((e = launch_toy_logits(B * K, V, g.ctx, g.pos, 1, *model, dtype, q, stream)) != hipSuccess) break;
+    if ((rc = psispec_draft_sample(q, dtype, B, K, V, &prm, g.drafts, inner, L.inner_bytes, stream))) return rc;
+    if ((e = launch_round_ctx(B, K, 2, g, stream)) != hipSuccess) break;
+    if ((e = launch_toy_logits(B * (K + 1), V, g.ctx, nullptr, 0, *model, dtype, p, stream)) != hipSuccess) break;
+    if ((rc = psispec_verify_linear(p, q, dtype, B, K, V, g.drafts, &prm, g.vtok, g.vlen, nullptr, nullptr, inner,
+                                    L.inner_bytes, stream)))
+      return rc;
+    e = launch_commit(B, K, r, rounds, max_len, g, out_seq, out_len, out_round_tokens, stream);
+  }
+  return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+}
+
 const char* psispec_strerror(int status) {
   switch (status) {
     case PSISPEC_OK:

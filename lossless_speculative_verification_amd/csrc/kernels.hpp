@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "device.hpp"
+#include "psispec.h"
 
 namespace psi {
 
@@ -271,6 +272,28 @@ hipError_t launch_stats32(const LinCfg& c, int64_t rows, int dtype, hipStream_t 
 hipError_t launch_tv_loss(const LinCfg& c, const float* w_row, double* loss, void* grad, double T, int dtype,
                           hipStream_t s);
 hipError_t launch_argmax(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
+// Multi-round generation on the toy model (driver.hip).
+struct GenState {
+  int32_t* t12;     // [B, 2] last two committed tokens
+  int32_t* x0;      // [B] the block's first token
+  int32_t* drafts;  // [B, K]
+  int32_t* vtok;    // [B, K + 1]
+  int32_t* vlen;    // [B]
+  int32_t* ctx;     // [B (K + 1), 2]
+  int32_t* pos;     // [B K]
+};
+struct GenLayout {
+  size_t first, q, p, inner, inner_bytes, st, total;
+};
+GenLayout gen_layout(int64_t B, int K, int V, int esz, size_t inner_bytes);
+GenState gen_state(void* ws, const GenLayout& L, int64_t B, int K);
+hipError_t launch_gen_init(int64_t B, const int32_t* prompt, const GenState& g, int32_t* len, int32_t* seq,
+                           int max_len, hipStream_t s);
+hipError_t launch_round_ctx(int64_t B, int K, int kind, const GenState& g, hipStream_t s);
+hipError_t launch_commit(int64_t B, int K, int r, int rounds, int max_len, const GenState& g, int32_t* seq,
+                         int32_t* len, int32_t* round_tokens, hipStream_t s);
+hipError_t launch_toy_logits(int64_t rows, int V, const int32_t* ctx, const int32_t* pos, int kind,
+                             const psispec_toy_model& m, int dtype, void* out, hipStream_t s);
 // fp64 draft-row sub-block records of the first `rows` rows of c.rows.q (linear.hip).
 hipError_t launch_draftpass(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
 

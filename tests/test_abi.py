@@ -188,3 +188,28 @@ def test_tv_loss_argument_errors(psi):
     assert call(dtype=2) == psi.EUNSUPPORTED
     assert call(ws_bytes=8) == psi.EWORKSPACE
     assert call(ws_addr=(1 << 20) + 16) == psi.EINVAL
+
+
+def test_generate_argument_errors(psi):
+    m = psi.toy_model()
+    prm = psi.make_params()
+    f = ctypes.c_void_p(0x10000000)
+
+    def call(B=4, block=8, V=100, dtype=1, rounds=3, prm_=prm, ws_bytes=1 << 30, ws_addr=1 << 20, model=m, prompt=f):
+        return psi.lib.psispec_generate_toy(B, block, V, dtype, ctypes.byref(model) if model else None,
+                                            ctypes.byref(prm_), prompt, rounds, f, f, f, ctypes.c_void_p(ws_addr),
+                                            ws_bytes, None)
+
+    assert call(model=None) == psi.EINVAL
+    assert call(prompt=None) == psi.EINVAL
+    assert call(B=0) == psi.EINVAL
+    assert call(rounds=0) == psi.EINVAL
+    assert call(block=1) == psi.EINVAL
+    assert call(block=66) == psi.EUNSUPPORTED
+    assert call(dtype=4) == psi.EUNSUPPORTED
+    assert call(prm_=psi.make_params(top_k=5)) == psi.EUNSUPPORTED
+    assert call(ws_bytes=64) == psi.EWORKSPACE
+    assert call(ws_addr=(1 << 20) + 64) == psi.EINVAL
+    assert psi.lib.psispec_generate_workspace_bytes(4, 1, 100, 1) == 0
+    assert psi.lib.psispec_toy_logits(4, 100, None, None, 0, ctypes.byref(m), 1, f, None) == psi.EINVAL
+    assert psi.lib.psispec_toy_logits(4, 100, f, None, 1, ctypes.byref(m), 1, f, None) == psi.EINVAL  # drafter needs pos
