@@ -306,6 +306,33 @@ int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64
                     hipStream_t stream);
 
 /*
+ * Linear verification fused with the LM head (Uno explainer §3.1: the AR path
+ * and the diffusion path share the base model's output head; §3.3: the
+ * verification rule of psispec_verify_linear). The logits are products of
+ * hidden states with the vocabulary matrix, p_logits = h_target W^T and
+ * q_logits = h_draft W^T, computed on bf16 matrix cores (fp32 accumulation)
+ * tile by tile and reduced as they are produced: the K + 1 target and K draft
+ * rows are never written out; only the final residual or bonus rows are
+ * formed again for the draw.
+ *   h_target      [B, K+1, H] bf16 target hidden states (row K: the bonus row).
+ *   h_draft       [B, K, H] bf16 draft hidden states.
+ *   w_vocab       [V, H] bf16 vocabulary matrix (row v gives token v's logit).
+ *   draft_tokens  [B, K] int32 drafts (input).
+ *   params        temperature > 0; top_k / top_p disabled; seed, step as for
+ *                 psispec_verify_linear, whose decision rules apply unchanged
+ *                 to these logits.
+ *   out_tokens    [B, K+1], out_len [B]: as psispec_verify_linear.
+ * H must be a multiple of 64 and the three inputs 16-byte aligned. The logits
+ * carry the fp32 accumulation error of an H-term dot product.
+ * Workspace: psispec_lmhead_workspace_bytes(B, K, V).
+ */
+size_t psispec_lmhead_workspace_bytes(int64_t B, int32_t K, int32_t V);
+int psispec_verify_lmhead(const void* h_target, const void* h_draft, const void* w_vocab, int64_t B, int32_t K,
+                          int32_t H, int32_t V, const int32_t* draft_tokens, const psispec_params* params,
+                          int32_t* out_tokens, int32_t* out_len, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
  * Synthetic order-2 toy language model: a stand-in for the AR target and the
  * diffusion drafter in tests and benchmarks of multi-round generation (it is
  * not part of the method). Logits depend on the last two tokens (t1, t2):

@@ -12,6 +12,7 @@ Function names mirror the C ABI in include/psispec.h:
   tree_candidates  psispec_tree_candidates
   verify_tree_det  psispec_verify_tree_det
   tv_loss          psispec_tv_loss
+  verify_lmhead    psispec_verify_lmhead
   toy_logits       psispec_toy_logits (synthetic stand-in model)
   generate_toy     psispec_generate_toy
 """
@@ -86,6 +87,10 @@ def _load():
     L.psispec_generate_toy.argtypes = [i64, i32, i32, ctypes.c_int, ctypes.POINTER(ToyModel),
                                        ctypes.POINTER(Params), P, i32, P, P, P, P, sz, P]
     L.psispec_generate_toy.restype = ctypes.c_int
+    L.psispec_lmhead_workspace_bytes.argtypes = [i64, i32, i32]
+    L.psispec_lmhead_workspace_bytes.restype = sz
+    L.psispec_verify_lmhead.argtypes = [P, P, P, i64, i32, i32, i32, P, ctypes.POINTER(Params), P, P, P, sz, P]
+    L.psispec_verify_lmhead.restype = ctypes.c_int
     L.psispec_strerror.argtypes = [ctypes.c_int]
     L.psispec_strerror.restype = ctypes.c_char_p
     L.psispec_version.argtypes = []
@@ -399,4 +404,28 @@ def generate_toy(prompt: torch.Tensor, block: int, V: int, rounds: int, temperat
                                   int(rounds), _ptr(out["seq"]), _ptr(out["len"]), _ptr(out["round_tokens"]),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("psispec_generate_toy", rc)
+    return out
+
+
+def verify_lmhead(h_target: torch.Tensor, h_draft: torch.Tensor, w_vocab: torch.Tensor, draft_tokens: torch.Tensor,
+                  temperature=1.0, seed=0, step=0, out=None, workspace=None, stream=None) -> dict:
+    """psispec_verify_lmhead. h_target [B, K+1, H], h_draft [B, K, H], w_vocab
+    [V, H] (bf16), draft_tokens [B, K] int32. Returns dict(tokens [B, K+1], len [B])."""
+    for t in (h_target, h_draft, w_vocab):
+        assert t.is_cuda and t.is_contiguous() and t.dtype == torch.bfloat16
+    B, K1, H = h_target.shape
+    K = K1 - 1
+    V = w_vocab.shape[0]
+    assert h_draft.shape == (B, K, H) and w_vocab.shape == (V, H)
+    assert draft_tokens.is_cuda and draft_tokens.dtype == torch.int32 and draft_tokens.shape == (B, K)
+    dev = h_target.device
+    if out is None:
+        out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                   len=torch.empty((B,), dtype=torch.int32, device=dev))
+    ws = _workspace(workspace, int(lib.psispec_lmhead_workspace_bytes(B, K, V)), dev)
+    prm = make_params(temperature, seed=seed, step=step)
+    rc = lib.psispec_verify_lmhead(_ptr(h_target), _ptr(h_draft), _ptr(w_vocab), B, K, H, V, _ptr(draft_tokens),
+                                   ctypes.byref(prm), _ptr(out["tokens"]), _ptr(out["len"]), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream))
+    _check("psispec_verify_lmhead", rc)
     return out

@@ -452,6 +452,107 @@ int psispec_generate_toy(int64_t B, int32_t block, int32_t V, int dtype, const p
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 
+namespace psi {
+namespace {
+constexpr int kLmhTileN = 256, kLmhTileM = 128, kLmhStepK = 64;
+struct LmhLayout {
+  size_t st, glog, fin, ts, tres, out, total;
+};
+inline LmhLayout lmh_layout(int64_t B, int32_t K, int32_t V) {
+  LmhLayout L;
+  const int64_t rows = B * (2 * (int64_t)K + 1);
+  const int64_t ntn = (V + kLmhTileN - 1) / kLmhTileN;
+  size_t off = 0;
+  L.st = off;
+  off = align_up(off + (size_t)(rows * ntn) * sizeof(StatRec), 256);
+  L.glog = off;
+  off = align_up(off + (size_t)rows * sizeof(float), 256);
+  L.fin = off;
+  off = align_up(off + (size_t)(2 * B) * sizeof(int32_t), 256);
+  L.ts = off;
+  off = align_up(off + (size_t)B * sizeof(TreeState), 256);
+  L.tres = off;
+  off = align_up(off + (size_t)B * nsb_of(V) * sizeof(TreeRes), 256);
+  L.out = off;
+  off = align_up(off + (size_t)(2 * B) * V * sizeof(float), 256);
+  L.total = off;
+  return L;
+}
+}  // namespace
+}  // namespace psi
+
+size_t psispec_lmhead_workspace_bytes(int64_t B, int32_t K, int32_t V) {
+  if (B <= 0 || K <= 0 || K > PSISPEC_MAX_K || V <= 0) return 0;
+  return lmh_layout(B, K, V).total;
+}
+
+int psispec_verify_lmhead(const void* h_target, const void* h_draft, const void* w_vocab, int64_t B, int32_t K,
+                          int32_t H, int32_t V, const int32_t* draft_tokens, const psispec_params* params,
+                          int32_t* out_tokens, int32_t* out_len, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (!h_target || !h_draft || !w_vocab || !draft_tokens || !out_tokens || !out_len || !workspace)
+    return PSISPEC_EINVAL;
+  if (B <= 0 || K <= 0 || H <= 0 || V <= 0) return PSISPEC_EINVAL;
+  if (int rc = check_params(params, V)) return rc;
+  if (!(params->temperature > 0.0f) || params->top_k != 0 || params->top_p != 1.0f) return PSISPEC_EUNSUPPORTED;
+  if (K > PSISPEC_MAX_K || H % kLmhStepK != 0) return PSISPEC_EUNSUPPORTED;
+  if (!aligned16(h_target) || !aligned16(h_draft) || !aligned16(w_vocab)) return PSISPEC_EINVAL;
+  if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
+  if (ws_bytes < psispec_lmhead_workspace_bytes(B, K, V)) return PSISPEC_EWORKSPACE;
+  const LmhLayout L = lmh_layout(B, K, V);
+  char* w = (char*)workspace;
+  LmhCfg g;
+  memset(&g, 0, sizeof(g));
+  g.hp = (const uint16_t*)h_target;
+  g.hq = (const uint16_t*)h_draft;
+  g.w = (const uint16_t*)w_vocab;
+  g.Mp = B * (K + 1);
+  g.Mq = B * K;
+  g.B = B;
+  g.K = K;
+  g.H = H;
+  g.V = V;
+  g.ntn = (V + kLmhTileN - 1) / kLmhTileN;
+  g.draft = draft_tokens;
+  g.c32 = (float)(1.4426950408889634074 / (double)params->temperature);
+  g.st = (StatRec*)(w + L.st);
+  g.glog = (float*)(w + L.glog);
+  g.fin = (int32_t*)(w + L.fin);
+  g.out = (float*)(w + L.out);
+  // the draw over the final rows: target rows [B, V] then draft rows [B, V] (fp32)
+  psispec_params prm = *params;
+  prm.flags = 0;
+  LinCfg c;
+  fill_common(c, g.out, g.out + (size_t)B * V, PSISPEC_DTYPE_F32, B, 1, V, &prm, workspace, 1);
+  c.st = nullptr;  // the draw uses only the tree-state sections below
+  c.ar = nullptr;
+  c.rs = nullptr;
+  c.res = nullptr;
+  c.dr = nullptr;
+  c.K = K;
+  c.out_tokens = out_tokens;
+  c.out_len = out_len;
+  TreeCfg tc;
+  memset(&tc, 0, sizeof(tc));
+  tc.ts = (TreeState*)(w + L.ts);
+  tc.tres = (TreeRes*)(w + L.tres);
+  tc.N = K;
+  tc.D = K;
+  timing_begin(stream);
+  LmhCfg gs = g;
+  gs.M = g.Mp + g.Mq;
+  gs.ntm = (int)((gs.M + kLmhTileM - 1) / kLmhTileM);
+  hipError_t e = launch_lmh_stats(gs, stream);
+  if (e == hipSuccess) e = launch_lmh_decide(gs, c, tc, stream);
+  LmhCfg gl = g;
+  gl.M = 2 * B;
+  gl.ntm = (int)((gl.M + kLmhTileM - 1) / kLmhTileM);
+  gl.rows = g.fin;
+  if (e == hipSuccess) e = launch_lmh_logits(gl, stream);
+  if (e == hipSuccess) e = launch_tree_final(c, tc, PSISPEC_DTYPE_F32, stream);
+  return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+}
+
 const char* psispec_strerror(int status) {
   switch (status) {
     case PSISPEC_OK:

@@ -158,7 +158,8 @@ struct RowStat {
 // G(c) = sum_t max(0, P(t) - c Q(t)).
 enum TreePhase : int32_t { kTreeTest = 0, kTreeWaitG = 1, kTreeFinal = 2, kTreeDone = 3 };
 struct TreeState {
-  int32_t row, j, len, phase, has_exact, pad;
+  int32_t row, j, len, phase, has_exact;
+  int32_t urow1;          // row of the final draw's uniform + 1 when it differs from row (0: row)
   float mp, mq;      // exact row maxima of the current row pair
   double sp_hat, sq_hat;  // fp32-grade normalisers of the current row pair
   double Sp, Sq;          // fp64-grade normalisers (valid when has_exact)
@@ -294,6 +295,31 @@ hipError_t launch_commit(int64_t B, int K, int r, int rounds, int max_len, const
                          int32_t* len, int32_t* round_tokens, hipStream_t s);
 hipError_t launch_toy_logits(int64_t rows, int V, const int32_t* ctx, const int32_t* pos, int kind,
                              const psispec_toy_model& m, int dtype, void* out, hipStream_t s);
+// Linear verification fused with the LM head (lmhead.hip).
+enum LmhMode { kLmhStats = 0, kLmhLogits = 1 };
+struct LmhCfg {
+  const uint16_t* hp;     // [Mp, H] target hidden states (bf16 bits)
+  const uint16_t* hq;     // [Mq, H] draft hidden states
+  const uint16_t* w;      // [V, H] vocabulary matrix
+  int64_t Mp, Mq;         // B (K + 1) target rows, B K draft rows
+  int64_t M;              // rows of this product
+  int64_t B;
+  int K, H, V;
+  int ntm, ntn;           // row tiles, vocabulary tiles
+  const int32_t* rows;    // combined row index of each row of this product (nullptr: the identity)
+  const int32_t* draft;   // [B, K]
+  float c32;
+  StatRec* st;            // [Mp + Mq][ntn] per (row, vocabulary tile)
+  float* glog;            // [Mp + Mq] logit of each row's drafted token
+  int32_t* fin;           // [2 B] final rows: target row n of each request, then draft row n
+  float* out;             // [M][V] logits (final-row product)
+};
+hipError_t launch_lmh_stats(const LmhCfg& g, hipStream_t s);
+hipError_t launch_lmh_decide(const LmhCfg& g, const LinCfg& c, const TreeCfg& tc, hipStream_t s);
+hipError_t launch_lmh_logits(const LmhCfg& g, hipStream_t s);
+// The final draw of a tree-state row pair (tree.hip): the fp64 pass over the
+// rows in c.rows and the pick, for every request whose state is kTreeFinal.
+hipError_t launch_tree_final(const LinCfg& c, const TreeCfg& tc, int dtype, hipStream_t s);
 // fp64 draft-row sub-block records of the first `rows` rows of c.rows.q (linear.hip).
 hipError_t launch_draftpass(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
 

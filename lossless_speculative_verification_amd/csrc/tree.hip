@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kWG) void k_tree_pick(LinCfg c, TreeCfg tc) {
   wpair(DT == kBF16 && c.tab, s.mp, s.mq, s.c_new != 0.0, c64, rwp, rwq);
   auto wp = [&](int64_t j) { return fweight<DT>(E::load1(prow, j), rwp, c64, nullptr); };
   auto wq = [&](int64_t j) { return fweight<DT>(E::load1(qrow, j), rwq, c64, nullptr); };
-  const double u = c.rng.u((uint32_t)b, (uint32_t)s.row, kDrawFinal);
+  const double u = c.rng.u((uint32_t)b, (uint32_t)(s.urow1 > 0 ? s.urow1 - 1 : s.row), kDrawFinal);
   int y;
   if (s.c_new == 0.0) {
     // leaf: unnormalised target weights, as for the bonus draw of the linear path
@@ -601,6 +601,18 @@ hipError_t launch_tree_sampled(const LinCfg& c, const TreeTopo& tp, const TreeCf
     return c.aligned ? tree_sampled_t<kBF16, true>(c, tp, tc, rounds, s)
                      : tree_sampled_t<kBF16, false>(c, tp, tc, rounds, s);
   return c.aligned ? tree_sampled_t<kF32, true>(c, tp, tc, rounds, s) : tree_sampled_t<kF32, false>(c, tp, tc, rounds, s);
+}
+
+template <int DT, bool AL>
+static hipError_t tree_final_t(const LinCfg& c, const TreeCfg& tc, hipStream_t s) {
+  PSI_LAUNCH(s, (k_tree_pass<DT, AL>), dim3((unsigned)((c.nsb + kWaves - 1) / kWaves), (unsigned)c.B), dim3(kWG), c,
+             tc, 1);
+  PSI_LAUNCH(s, (k_tree_pick<DT, AL>), dim3((unsigned)c.B), dim3(kWG), c, tc);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_final(const LinCfg& c, const TreeCfg& tc, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(tree_final_t, dtype, c.aligned, c, tc, s);
 }
 
 hipError_t launch_tree_greedy(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int dtype, hipStream_t s) {

@@ -355,3 +355,25 @@ def generate(model, prompt, block, V, temperature, seed, rounds, nthreads=1):
             mc[b, r] = min(float(m0[b, 0]), float(md[b].min()), float(v["margin_cdf"][b]))
             t1[b], t2[b] = seq[b, ln[b] - 2], seq[b, ln[b] - 1]
     return dict(seq=seq, len=ln, round_tokens=rt, margin_acc=ma, margin_cdf=mc)
+
+
+def lmhead_logits(h, w, chunk=16384):
+    """Logits of hidden states through the shared output head ("Uno" research
+    explainer, §3.1: the AR and diffusion paths share the base model and its
+    head): z = h W^T, h [..., H] and w [V, H] in bf16 bits (uint16) or float32,
+    exact products summed in fp64 (numpy matmul), returned rounded to float32.
+    The vocabulary is processed `chunk` rows at a time."""
+    def f64(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            x = (x.astype(np.uint32) << 16).view(np.float32)
+        return x.astype(np.float64)
+
+    hh = f64(h)
+    lead, H = hh.shape[:-1], hh.shape[-1]
+    hh = hh.reshape(-1, H)
+    V = w.shape[0]
+    out = np.empty((hh.shape[0], V), dtype=np.float32)
+    for v0 in range(0, V, chunk):
+        out[:, v0:v0 + chunk] = (hh @ f64(w[v0:v0 + chunk]).T).astype(np.float32)
+    return out.reshape(*lead, V)

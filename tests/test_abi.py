@@ -213,3 +213,24 @@ def test_generate_argument_errors(psi):
     assert psi.lib.psispec_generate_workspace_bytes(4, 1, 100, 1) == 0
     assert psi.lib.psispec_toy_logits(4, 100, None, None, 0, ctypes.byref(m), 1, f, None) == psi.EINVAL
     assert psi.lib.psispec_toy_logits(4, 100, f, None, 1, ctypes.byref(m), 1, f, None) == psi.EINVAL  # drafter needs pos
+
+
+def test_lmhead_argument_errors(psi):
+    prm = psi.make_params()
+    f = ctypes.c_void_p(0x10000000)
+    u = ctypes.c_void_p(0x10000008)  # not 16-byte aligned
+
+    def call(B=2, K=3, H=128, V=1000, prm_=prm, ws_bytes=1 << 30, ws_addr=1 << 20, ht=f, hd=f, w=f):
+        return psi.lib.psispec_verify_lmhead(ht, hd, w, B, K, H, V, f, ctypes.byref(prm_), f, f,
+                                             ctypes.c_void_p(ws_addr), ws_bytes, None)
+
+    assert call(ht=None) == psi.EINVAL
+    assert call(B=0) == psi.EINVAL
+    assert call(H=0) == psi.EINVAL
+    assert call(H=96) == psi.EUNSUPPORTED          # not a multiple of 64
+    assert call(K=65) == psi.EUNSUPPORTED
+    assert call(prm_=psi.make_params(temperature=0.0)) == psi.EUNSUPPORTED
+    assert call(prm_=psi.make_params(top_k=10)) == psi.EUNSUPPORTED
+    assert call(w=u) == psi.EINVAL
+    assert call(ws_bytes=1024) == psi.EWORKSPACE
+    assert psi.lib.psispec_lmhead_workspace_bytes(2, 3, 1000) > 0

@@ -972,3 +972,21 @@ def test_generate_greedy_is_the_argmax_chain():
             chain.append(x)
             t1, t2 = t2, x
         assert chain == g["seq"][b, :g["len"][b]].tolist()
+
+
+def test_lmhead_logits_small_loops():
+    """z[r, v] = sum_k h[r, k] w[v, k] on a non-square case, written as loops
+    over bf16 inputs (catches a transposed operand or a wrong decode)."""
+    rng = np.random.default_rng(14)
+    h = synth.f32_to_bf16(rng.normal(0, 1, (2, 3, 16)).astype(np.float32))
+    w = synth.f32_to_bf16(rng.normal(0, 0.5, (7, 16)).astype(np.float32))
+    z = oracle.lmhead_logits(h, w, chunk=3)
+    hf, wf = synth.bf16_to_f32(h).astype(np.float64), synth.bf16_to_f32(w).astype(np.float64)
+    assert z.shape == (2, 3, 7) and z.dtype == np.float32
+    for a in range(2):
+        for r in range(3):
+            for v in range(7):
+                ref = 0.0
+                for k in range(16):
+                    ref += hf[a, r, k] * wf[v, k]
+                assert z[a, r, v] == np.float32(ref)
