@@ -454,7 +454,6 @@ int psispec_generate_toy(int64_t B, int32_t block, int32_t V, int dtype, const p
 
 namespace psi {
 namespace {
-constexpr int kLmhTileN = 256, kLmhTileM = 128, kLmhStepK = 64;
 struct LmhLayout {
   size_t st, glog, fin, ts, tres, out, total;
 };

@@ -20,8 +20,9 @@
 // GEMM: C[M, V] = A[M, H] * W[V, H]^T, A rows from the target and draft hidden
 // states. A workgroup computes a 128-row x 256-token tile with four waves (2 x
 // 2, 64 x 128 each, as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16), stepping over
-// H by 64 with both operand tiles double-buffered in LDS (rows padded by 16
-// bytes so that the 16-byte fragment reads of a wave do not collide in banks).
+// H by 32 with both operand tiles double-buffered in LDS (rows padded by 16
+// bytes so that the 16-byte fragment reads of a wave do not collide in banks),
+// the global loads issued two steps ahead and two workgroups per CU.
 // Block operand layout of the instruction (checked on the device): lane l
 // holds A[l % 32][8 (l / 32) .. +7] and W[col l % 32][8 (l / 32) .. +7]; result
 // element i of lane l is C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
@@ -33,7 +34,9 @@ namespace psi {
 
 namespace {
 
-constexpr int kLmhBM = 128, kLmhBN = 256, kLmhBK = 64;
+constexpr int kLmhBM = kLmhTileM, kLmhBN = kLmhTileN, kLmhBK = 32;
+static_assert(kLmhBM == 128 && kLmhBN == 256, "four 64 x 128 wave tiles");
+static_assert(kLmhStepK % kLmhBK == 0, "the hidden size is a multiple of the step");
 constexpr int kLmhPad = 8;                      // bf16 elements of padding per LDS row
 constexpr int kLmhLd = kLmhBK + kLmhPad;        // LDS row stride (elements)
 constexpr int kXcds = 8;
@@ -59,7 +62,7 @@ __device__ __forceinline__ int lmh_token(const LmhCfg& g, int64_t r) {
 }  // namespace
 
 template <int MODE>
-__global__ __launch_bounds__(kWG) void k_lmh_gemm(LmhCfg g) {
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void k_lmh_gemm(LmhCfg g) {
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kLmhBM * kLmhLd];
   __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kLmhBN * kLmhLd];
   __shared__ int64_t s_row[kLmhBM];  // combined row index of each tile row (-1 past the end)
@@ -84,44 +87,48 @@ __global__ __launch_bounds__(kWG) void k_lmh_gemm(LmhCfg g) {
   }
   __syncthreads();
 
-  // global -> register staging: A 4 and W 8 16-byte vectors per thread per
-  // step; thread t always loads the 16-byte column t % 8 of tile rows
-  // t / 8 + 32 j, whose addresses are formed once here (nullptr: zeros)
-  // (rows past the end read a valid row and are zeroed: no branches)
-  const int kv = t & 7;
-  const uint16_t* pa[4];
-  const uint16_t* pb[8];
-  uint32_t live = 0;  // bit j: A row j valid; bit 4 + j: W row j valid
+  // global -> register staging: thread t always loads the 16-byte column
+  // t % VPR of tile rows t / VPR + RPP j (VPR vectors per row of the step,
+  // RPP rows per pass of the workgroup), addresses formed once here; rows
+  // past the end read a valid row and are zeroed (no branches)
+  constexpr int VPR = kLmhBK / 8, RPP = kWG / VPR;
+  constexpr int NA = kLmhBM / RPP, NB = kLmhBN / RPP;
+  const int kv = t % VPR, r0 = t / VPR;
+  const uint16_t* pa[NA];
+  const uint16_t* pb[NB];
+  uint32_t live = 0;  // bit j: A row j valid; bit NA + j: W row j valid
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t r = s_row[(t >> 3) + 32 * j];
+  for (int j = 0; j < NA; ++j) {
+    const int64_t r = s_row[r0 + RPP * j];
     live |= r >= 0 ? 1u << j : 0u;
     pa[j] = lmh_arow(g, r >= 0 ? r : 0) + kv * 8;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t n = n0 + (t >> 3) + 32 * j;
-    live |= n < g.V ? 1u << (4 + j) : 0u;
+  for (int j = 0; j < NB; ++j) {
+    const int64_t n = n0 + r0 + RPP * j;
+    live |= n < g.V ? 1u << (NA + j) : 0u;
     pb[j] = g.w + (n < g.V ? n : 0) * (int64_t)g.H + kv * 8;
   }
-  uint4 ra[4], rb[8];
-  auto load_step = [&](int k0) {
+  // two register sets: the loads of step s + 2 are issued while step s is
+  // multiplied, and step s + 1 (loaded during step s - 1) is stored to LDS
+  uint4 ra0[NA], rb0[NB], ra1[NA], rb1[NB];
+  auto load_step = [&](int k0, uint4 (&ra)[NA], uint4 (&rb)[NB]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NA; ++j) {
       const uint4 x = *(const uint4*)(pa[j] + k0);
       ra[j] = (live >> j) & 1u ? x : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const uint4 x = *(const uint4*)(pb[j] + k0);
-      rb[j] = (live >> (4 + j)) & 1u ? x : make_uint4(0, 0, 0, 0);
+      rb[j] = (live >> (NA + j)) & 1u ? x : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_step = [&](int buf) {
+  auto store_step = [&](int buf, const uint4 (&ra)[NA], const uint4 (&rb)[NB]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(uint4*)&s_a[buf][((t >> 3) + 32 * j) * kLmhLd + kv * 8] = ra[j];
+    for (int j = 0; j < NA; ++j) *(uint4*)&s_a[buf][(r0 + RPP * j) * kLmhLd + kv * 8] = ra[j];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *(uint4*)&s_b[buf][((t >> 3) + 32 * j) * kLmhLd + kv * 8] = rb[j];
+    for (int j = 0; j < NB; ++j) *(uint4*)&s_b[buf][(r0 + RPP * j) * kLmhLd + kv * 8] = rb[j];
   };
 
   f32x16_t acc[2][4];
@@ -133,9 +140,6 @@ __global__ __launch_bounds__(kWG) void k_lmh_gemm(LmhCfg g) {
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.0f;
 
   const int steps = g.H / kLmhBK;
-  load_step(0);
-  store_step(0);
-  __syncthreads();
   const int fr = lane & 31, fk = (lane >> 5) * 8;
   // operand fragments of one 16-deep slice, read one slice ahead of the MFMAs
   bf16x8_t fa[2][2], fb[2][4];
@@ -147,10 +151,9 @@ __global__ __launch_bounds__(kWG) void k_lmh_gemm(LmhCfg g) {
     for (int bj = 0; bj < 4; ++bj)
       fb[slot][bj] = *(const bf16x8_t*)&s_b[buf][(wn * 128 + bj * 32 + fr) * kLmhLd + kk + fk];
   };
-  read_frag(0, 0, 0);
-  for (int s = 0; s < steps; ++s) {
+  auto step = [&](int s, uint4 (&la)[NA], uint4 (&lb)[NB], const uint4 (&sa)[NA], const uint4 (&sb)[NB]) {
     const int buf = s & 1;
-    if (s + 1 < steps) load_step((s + 1) * kLmhBK);
+    if (s + 2 < steps) load_step((s + 2) * kLmhBK, la, lb);
 #pragma unroll
     for (int q = 0; q < kLmhBK / 16; ++q) {
       if (q + 1 < kLmhBK / 16) read_frag(buf, (q + 1) * 16, (q + 1) & 1);
@@ -160,9 +163,18 @@ __global__ __launch_bounds__(kWG) void k_lmh_gemm(LmhCfg g) {
         for (int bj = 0; bj < 4; ++bj)
           acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q & 1][bi], fb[q & 1][bj], acc[bi][bj], 0, 0, 0);
     }
-    if (s + 1 < steps) store_step(buf ^ 1);
+    if (s + 1 < steps) store_step(buf ^ 1, sa, sb);
     __syncthreads();
     if (s + 1 < steps) read_frag(buf ^ 1, 0, 0);
+  };
+  load_step(0, ra0, rb0);
+  store_step(0, ra0, rb0);
+  if (steps > 1) load_step(kLmhBK, ra1, rb1);
+  __syncthreads();
+  read_frag(0, 0, 0);
+  for (int s = 0; s < steps; s += 2) {
+    step(s, ra0, rb0, ra1, rb1);  // loads step s + 2 into set 0, stores step s + 1 from set 1
+    if (s + 1 < steps) step(s + 1, ra1, rb1, ra0, rb0);
   }
 
   // ---- epilogue. Element e of block (bi, bj) on this lane: tile row
