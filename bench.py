@@ -272,6 +272,33 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed):
           flush=True)
     del wsg, outs
     torch.cuda.empty_cache()
+
+    # Linear verification fused with the LM head: hidden states [64, 9, 4096]
+    # and [64, 8, 4096], vocabulary matrix [151936, 4096] (the Qwen3-8B head
+    # shape), bf16, seeded on the device; drafts uniform.
+    Bl, Kl, Hl, Vl = 64, 8, 4096, 151936
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    ht = torch.randn((Bl, Kl + 1, Hl), device=dev, generator=gen).to(torch.bfloat16)
+    hd = (ht[:, :Kl].float() + 0.3 * torch.randn((Bl, Kl, Hl), device=dev, generator=gen)).to(torch.bfloat16)
+    hd = hd.contiguous()
+    wv = (0.05 * torch.randn((Vl, Hl), device=dev, generator=gen)).to(torch.bfloat16)
+    xl = torch.randint(0, Vl, (Bl, Kl), device=dev, generator=gen, dtype=torch.int32)
+    wsl = torch.empty(int(psi.lib.psispec_lmhead_workspace_bytes(Bl, Kl, Vl)), dtype=torch.uint8, device=dev)
+    outs = dict(tokens=torch.empty((Bl, Kl + 1), dtype=torch.int32, device=dev),
+                len=torch.empty((Bl,), dtype=torch.int32, device=dev))
+    ms = time_calls(torch, lambda i: psi.verify_lmhead(ht, hd, wv, xl, temperature=1.0, seed=seed, step=i, out=outs,
+                                                        workspace=wsl, stream=stream), max(steps // 10, 3), 1, stream)
+    flops = 2.0 * (Bl * (2 * Kl + 1) + 2 * Bl) * Hl * Vl
+    tfs = flops / (ms * 1e-3) / 1e12
+    res["lmhead_verify_B64_K8_H4096_V151936_bf16"] = {
+        "us_per_call": 1e3 * ms, "flops": flops, "TFLOP_per_s": tfs, "mfma_bf16_frac": tfs / 2500.0,
+        "rows_per_s": Bl * Kl / (ms * 1e-3),
+        "note": "all 17 rows per request through the head once (stats epilogue) plus the 2 final rows again; "
+                "logits never written except the final rows"}
+    print(f"# lmhead_verify: {1e3 * ms:.0f} us/call, {tfs:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    del ht, hd, wv, wsl
+    torch.cuda.empty_cache()
     return res
 
 
