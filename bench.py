@@ -123,9 +123,16 @@ def time_calls(torch, fn, n, warm, stream):
     return e0.elapsed_time(e1) / n
 
 
-def other_workloads(torch, psi, synth, dev, stream, steps, seed):
-    """The remaining workloads of the method, each timed over `steps` calls."""
+WORKLOAD_NAMES = ("qwen", "filtered", "tree", "treesampler", "tvloss", "generate", "lmhead")
+
+
+def other_workloads(torch, psi, synth, dev, stream, steps, seed, only=None):
+    """The remaining workloads of the method, each timed over `steps` calls
+    (`only`: the names of WORKLOAD_NAMES to run; all by default)."""
     res = {}
+
+    def want(name):
+        return only is None or name in only
 
     def line(name, ms, nbytes, rows, extra):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -135,170 +142,177 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed):
         res[name] = d
         print(f"# {name}: {1e3 * ms:.1f} us/call, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
-    # Fused-draft linear verify, B=64 K=8 V=151936 bf16, T=0.7; two input copies
-    # rotate so the 330 MB working set does not sit in the 256 MB last-level cache.
-    w = synth.WORKLOADS["qwen"]
-    Bq, Kq, Vq = w["B"], w["K"], w["V"]
-    copies = []
-    for c in range(2):
-        p, q = synth.linear_inputs("qwen", seed=seed + c)
-        copies.append((to_dev(p, torch, dev), to_dev(q, torch, dev)))
-    ws = torch.empty(psi.workspace_bytes(Bq, 2 * Kq + 1, Vq, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
-    dr = torch.empty((Bq, Kq), dtype=torch.int32, device=dev)
-    outs = dict(tokens=torch.empty((Bq, Kq + 1), dtype=torch.int32, device=dev),
-                len=torch.empty((Bq,), dtype=torch.int32, device=dev))
-    Tq = float(np.float32(w["temperature"]))
-    ms = time_calls(torch, lambda i: psi.verify_linear(*copies[i % 2], dr, temperature=Tq, seed=seed, step=i,
-                                                         fused=True, out=outs, workspace=ws, stream=stream),
-                    steps, 5, stream)
-    line("qwen_fused_B64_K8_V151936_bf16", ms, bytes_alg(Bq, Kq, Vq), Bq * Kq, {"temperature": Tq})
-    del copies, ws
-    torch.cuda.empty_cache()
+    if want("qwen"):
+        # Fused-draft linear verify, B=64 K=8 V=151936 bf16, T=0.7; two input copies
+        # rotate so the 330 MB working set does not sit in the 256 MB last-level cache.
+        w = synth.WORKLOADS["qwen"]
+        Bq, Kq, Vq = w["B"], w["K"], w["V"]
+        copies = []
+        for c in range(2):
+            p, q = synth.linear_inputs("qwen", seed=seed + c)
+            copies.append((to_dev(p, torch, dev), to_dev(q, torch, dev)))
+        ws = torch.empty(psi.workspace_bytes(Bq, 2 * Kq + 1, Vq, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+        dr = torch.empty((Bq, Kq), dtype=torch.int32, device=dev)
+        outs = dict(tokens=torch.empty((Bq, Kq + 1), dtype=torch.int32, device=dev),
+                    len=torch.empty((Bq,), dtype=torch.int32, device=dev))
+        Tq = float(np.float32(w["temperature"]))
+        ms = time_calls(torch, lambda i: psi.verify_linear(*copies[i % 2], dr, temperature=Tq, seed=seed, step=i,
+                                                             fused=True, out=outs, workspace=ws, stream=stream),
+                        steps, 5, stream)
+        line("qwen_fused_B64_K8_V151936_bf16", ms, bytes_alg(Bq, Kq, Vq), Bq * Kq, {"temperature": Tq})
+        del copies, ws
+        torch.cuda.empty_cache()
 
-    # Filtered (top-k 50, top-p 0.95) and greedy, B=128 K=16 V=128256 fp32, fused drafts.
-    w = synth.WORKLOADS["filtered"]
-    Bf, Kf, Vf = w["B"], w["K"], w["V"]
-    p, q = synth.linear_inputs("filtered", seed=seed)
-    pd, qd = to_dev(p, torch, dev), to_dev(q, torch, dev)
-    del p, q
-    ws = torch.empty(psi.workspace_bytes(Bf, 2 * Kf + 1, Vf, psi.DTYPE_F32), dtype=torch.uint8, device=dev)
-    dr = torch.empty((Bf, Kf), dtype=torch.int32, device=dev)
-    outs = dict(tokens=torch.empty((Bf, Kf + 1), dtype=torch.int32, device=dev),
-                len=torch.empty((Bf,), dtype=torch.int32, device=dev))
-    top_p = float(np.float32(w["top_p"]))
-    ms = time_calls(torch, lambda i: psi.verify_linear(pd, qd, dr, temperature=1.0, top_k=w["top_k"], top_p=top_p,
-                                                         seed=seed, step=i, fused=True, out=outs, workspace=ws,
-                                                         stream=stream), steps, 3, stream)
-    line("filtered_topk50_topp0.95_B128_K16_V128256_f32", ms, bytes_alg(Bf, Kf, Vf, 4), Bf * Kf, {})
-    ms = time_calls(torch, lambda i: psi.verify_linear(pd, qd, dr, temperature=0.0, fused=True, out=outs,
-                                                         workspace=ws, stream=stream), steps, 3, stream)
-    line("greedy_B128_K16_V128256_f32", ms, bytes_alg(Bf, Kf, Vf, 4), Bf * Kf, {})
-    del pd, qd, ws
-    torch.cuda.empty_cache()
+    if want("filtered"):
+        # Filtered (top-k 50, top-p 0.95) and greedy, B=128 K=16 V=128256 fp32, fused drafts.
+        w = synth.WORKLOADS["filtered"]
+        Bf, Kf, Vf = w["B"], w["K"], w["V"]
+        p, q = synth.linear_inputs("filtered", seed=seed)
+        pd, qd = to_dev(p, torch, dev), to_dev(q, torch, dev)
+        del p, q
+        ws = torch.empty(psi.workspace_bytes(Bf, 2 * Kf + 1, Vf, psi.DTYPE_F32), dtype=torch.uint8, device=dev)
+        dr = torch.empty((Bf, Kf), dtype=torch.int32, device=dev)
+        outs = dict(tokens=torch.empty((Bf, Kf + 1), dtype=torch.int32, device=dev),
+                    len=torch.empty((Bf,), dtype=torch.int32, device=dev))
+        top_p = float(np.float32(w["top_p"]))
+        ms = time_calls(torch, lambda i: psi.verify_linear(pd, qd, dr, temperature=1.0, top_k=w["top_k"], top_p=top_p,
+                                                             seed=seed, step=i, fused=True, out=outs, workspace=ws,
+                                                             stream=stream), steps, 3, stream)
+        line("filtered_topk50_topp0.95_B128_K16_V128256_f32", ms, bytes_alg(Bf, Kf, Vf, 4), Bf * Kf, {})
+        ms = time_calls(torch, lambda i: psi.verify_linear(pd, qd, dr, temperature=0.0, fused=True, out=outs,
+                                                             workspace=ws, stream=stream), steps, 3, stream)
+        line("greedy_B128_K16_V128256_f32", ms, bytes_alg(Bf, Kf, Vf, 4), Bf * Kf, {})
+        del pd, qd, ws
+        torch.cuda.empty_cache()
 
-    # Tree: 4 branches of 8-node chains, p and q [4, 33, 151936] bf16, fused node
-    # drafts; four input copies rotate (80 MB each).
-    w = synth.WORKLOADS["tree"]
-    Bt, Nt, Vt = w["B"], w["N"], w["V"]
-    parent = synth.branch_chain_parent(4, 8)
-    copies = []
-    for c in range(4):
-        p, q = synth.tree_inputs("tree", seed=seed + c)
-        copies.append((to_dev(p, torch, dev), to_dev(q, torch, dev)))
-    ws = torch.empty(psi.workspace_bytes(Bt, 2 * (Nt + 1), Vt, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
-    nodes = torch.empty((Bt, Nt), dtype=torch.int32, device=dev)
-    D = 8
-    outs = dict(tokens=torch.empty((Bt, D + 1), dtype=torch.int32, device=dev),
-                path=torch.empty((Bt, D), dtype=torch.int32, device=dev),
-                len=torch.empty((Bt,), dtype=torch.int32, device=dev))
-    ms = time_calls(torch, lambda i: psi.verify_tree(*copies[i % 4], parent, nodes, temperature=1.0, seed=seed,
-                                                       step=i, fused=True, out=outs, workspace=ws, stream=stream),
-                    steps, 5, stream)
-    line("tree_4x8_B4_N32_V151936_bf16", ms, Bt * 2 * (Nt + 1) * Vt * 2 + 4 * Bt * Nt + 4 * Bt * (2 * D + 2),
-         Bt * (Nt + 1), {"note": "latency-bound: 10 kernel launches per call"})
-    del copies, ws
-    torch.cuda.empty_cache()
+    if want("tree"):
+        # Tree: 4 branches of 8-node chains, p and q [4, 33, 151936] bf16, fused node
+        # drafts; four input copies rotate (80 MB each).
+        w = synth.WORKLOADS["tree"]
+        Bt, Nt, Vt = w["B"], w["N"], w["V"]
+        parent = synth.branch_chain_parent(4, 8)
+        copies = []
+        for c in range(4):
+            p, q = synth.tree_inputs("tree", seed=seed + c)
+            copies.append((to_dev(p, torch, dev), to_dev(q, torch, dev)))
+        ws = torch.empty(psi.workspace_bytes(Bt, 2 * (Nt + 1), Vt, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+        nodes = torch.empty((Bt, Nt), dtype=torch.int32, device=dev)
+        D = 8
+        outs = dict(tokens=torch.empty((Bt, D + 1), dtype=torch.int32, device=dev),
+                    path=torch.empty((Bt, D), dtype=torch.int32, device=dev),
+                    len=torch.empty((Bt,), dtype=torch.int32, device=dev))
+        ms = time_calls(torch, lambda i: psi.verify_tree(*copies[i % 4], parent, nodes, temperature=1.0, seed=seed,
+                                                           step=i, fused=True, out=outs, workspace=ws, stream=stream),
+                        steps, 5, stream)
+        line("tree_4x8_B4_N32_V151936_bf16", ms, Bt * 2 * (Nt + 1) * Vt * 2 + 4 * Bt * Nt + 4 * Bt * (2 * D + 2),
+             Bt * (Nt + 1), {"note": "latency-bound: 10 kernel launches per call"})
+        del copies, ws
+        torch.cuda.empty_cache()
 
-    # Tree Sampler: candidates from q [4, 16, 151936] (32 per position, 32 kept
-    # prefixes), then their verification against p [4, 33, 151936], bf16, T=1;
-    # six input copies rotate (60 MB each).
-    w = synth.WORKLOADS["treesampler"]
-    Bs, Ks, Cs, Ns, Vs = w["B"], w["K"], w["cands"], w["nodes"], w["V"]
-    copies = []
-    for c in range(6):
-        p, q = synth.treesampler_inputs(seed=seed + c)
-        copies.append((to_dev(p, torch, dev), to_dev(q, torch, dev)))
-    wsc = torch.empty(psi.workspace_bytes(Bs, Ks, Vs, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
-    wsv = torch.empty(psi.workspace_bytes(Bs, Ns + 1, Vs, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
-    cand = dict(parent=torch.empty((Bs, Ns), dtype=torch.int32, device=dev),
-                tokens=torch.empty((Bs, Ns), dtype=torch.int32, device=dev))
-    outs = dict(tokens=torch.empty((Bs, Ns + 1), dtype=torch.int32, device=dev),
-                path=torch.empty((Bs, Ns), dtype=torch.int32, device=dev),
-                len=torch.empty((Bs,), dtype=torch.int32, device=dev))
-    Ts = float(np.float32(w["temperature"]))
+    if want("treesampler"):
+        # Tree Sampler: candidates from q [4, 16, 151936] (32 per position, 32 kept
+        # prefixes), then their verification against p [4, 33, 151936], bf16, T=1;
+        # six input copies rotate (60 MB each).
+        w = synth.WORKLOADS["treesampler"]
+        Bs, Ks, Cs, Ns, Vs = w["B"], w["K"], w["cands"], w["nodes"], w["V"]
+        copies = []
+        for c in range(6):
+            p, q = synth.treesampler_inputs(seed=seed + c)
+            copies.append((to_dev(p, torch, dev), to_dev(q, torch, dev)))
+        wsc = torch.empty(psi.workspace_bytes(Bs, Ks, Vs, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+        wsv = torch.empty(psi.workspace_bytes(Bs, Ns + 1, Vs, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+        cand = dict(parent=torch.empty((Bs, Ns), dtype=torch.int32, device=dev),
+                    tokens=torch.empty((Bs, Ns), dtype=torch.int32, device=dev))
+        outs = dict(tokens=torch.empty((Bs, Ns + 1), dtype=torch.int32, device=dev),
+                    path=torch.empty((Bs, Ns), dtype=torch.int32, device=dev),
+                    len=torch.empty((Bs,), dtype=torch.int32, device=dev))
+        Ts = float(np.float32(w["temperature"]))
 
-    def sampler_step(i):
-        p_, q_ = copies[i % 6]
-        psi.tree_candidates(q_, Cs, Ns, temperature=Ts, out=cand, workspace=wsc, stream=stream)
-        psi.verify_tree_det(p_, cand["parent"], cand["tokens"], temperature=Ts, seed=seed, step=i, out=outs,
-                            workspace=wsv, stream=stream)
+        def sampler_step(i):
+            p_, q_ = copies[i % 6]
+            psi.tree_candidates(q_, Cs, Ns, temperature=Ts, out=cand, workspace=wsc, stream=stream)
+            psi.verify_tree_det(p_, cand["parent"], cand["tokens"], temperature=Ts, seed=seed, step=i, out=outs,
+                                workspace=wsv, stream=stream)
 
-    ms = time_calls(torch, sampler_step, steps, 5, stream)
-    line("treesampler_16_32_32_B4_V151936_bf16", ms, (Bs * Ks + Bs * (Ns + 1)) * Vs * 2, Bs * (Ks + Ns + 1),
-         {"note": "candidates (4 launches) + verification of deterministic candidates (4 launches)"})
-    del copies, wsc, wsv
-    torch.cuda.empty_cache()
+        ms = time_calls(torch, sampler_step, steps, 5, stream)
+        line("treesampler_16_32_32_B4_V151936_bf16", ms, (Bs * Ks + Bs * (Ns + 1)) * Vs * 2, Bs * (Ks + Ns + 1),
+             {"note": "candidates (4 launches) + verification of deterministic candidates (4 launches)"})
+        del copies, wsc, wsv
+        torch.cuda.empty_cache()
 
-    # TV distillation loss, forward and backward: teacher and student logits
-    # [2048, 151936] bf16 (8 sequences x 256 positions), gradient in bf16.
-    w = synth.WORKLOADS["tvloss"]
-    Rt, Vt = w["R"], w["V"]
-    p, q = synth.tv_inputs(seed=seed)
-    pd, qd = to_dev(p, torch, dev), to_dev(q, torch, dev)
-    del p, q
-    wts = torch.full((Rt,), 1.0 / Rt, dtype=torch.float32, device=dev)
-    ws = torch.empty(psi.workspace_bytes(Rt, 2, Vt, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
-    outs = dict(loss=torch.empty((Rt,), dtype=torch.float64, device=dev),
-                grad=torch.empty((Rt, Vt), dtype=torch.bfloat16, device=dev))
-    ms = time_calls(torch, lambda i: psi.tv_loss(pd, qd, temperature=1.0, row_weights=wts, out=outs, workspace=ws,
-                                                  stream=stream), max(steps // 5, 5), 2, stream)
-    line("tvloss_fwd_bwd_R2048_V151936_bf16", ms, Rt * Vt * 6, Rt,
-         {"note": "algorithmic bytes: teacher and student logits read once, bf16 gradient written once"})
-    del pd, qd, ws, outs
-    torch.cuda.empty_cache()
+    if want("tvloss"):
+        # TV distillation loss, forward and backward: teacher and student logits
+        # [2048, 151936] bf16 (8 sequences x 256 positions), gradient in bf16.
+        w = synth.WORKLOADS["tvloss"]
+        Rt, Vt = w["R"], w["V"]
+        p, q = synth.tv_inputs(seed=seed)
+        pd, qd = to_dev(p, torch, dev), to_dev(q, torch, dev)
+        del p, q
+        wts = torch.full((Rt,), 1.0 / Rt, dtype=torch.float32, device=dev)
+        ws = torch.empty(psi.workspace_bytes(Rt, 2, Vt, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+        outs = dict(loss=torch.empty((Rt,), dtype=torch.float64, device=dev),
+                    grad=torch.empty((Rt, Vt), dtype=torch.bfloat16, device=dev))
+        ms = time_calls(torch, lambda i: psi.tv_loss(pd, qd, temperature=1.0, row_weights=wts, out=outs, workspace=ws,
+                                                      stream=stream), max(steps // 5, 5), 2, stream)
+        line("tvloss_fwd_bwd_R2048_V151936_bf16", ms, Rt * Vt * 6, Rt,
+             {"note": "algorithmic bytes: teacher and student logits read once, bf16 gradient written once"})
+        del pd, qd, ws, outs
+        torch.cuda.empty_cache()
 
-    # Multi-round generation on the toy order-2 model: 64 requests, block 8
-    # (7 drafts), V=32768 bf16, T=1, 32 rounds per call; every step (toy model
-    # passes, draft sampling, verification, commit) runs on the device.
-    Bg, blk, Vg, Rg = 64, 8, 32768, 32
-    prompt = torch.from_numpy(synth.randint(seed, 0, 2 * Bg, Vg).reshape(Bg, 2)).to(dev)
-    m = synth.TOY_MODEL
-    tm = psi.toy_model(m["seed"], m["sd"], m["n_heavy"], m["boost"], m["rho"], m["noise"])
-    wsg = torch.empty(int(psi.lib.psispec_generate_workspace_bytes(Bg, blk, Vg, psi.DTYPE_BF16)), dtype=torch.uint8,
-                      device=dev)
-    outs = dict(seq=torch.empty((Bg, Rg * (blk + 1)), dtype=torch.int32, device=dev),
-                len=torch.empty((Bg,), dtype=torch.int32, device=dev),
-                round_tokens=torch.empty((Bg, Rg), dtype=torch.int32, device=dev))
-    ms = time_calls(torch, lambda i: psi.generate_toy(prompt, blk, Vg, Rg, temperature=1.0, seed=seed, step=2 * Rg * i,
-                                                       model=tm, out=outs, workspace=wsg, stream=stream),
-                    max(steps // 10, 3), 1, stream)
-    toks = int(outs["len"].sum().item())
-    res["generate_toy_B64_block8_V32768_bf16"] = {
-        "us_per_call": 1e3 * ms, "rounds": Rg, "us_per_round": 1e3 * ms / Rg, "tokens_per_s": toks / (ms * 1e-3),
-        "tpf": toks / (2.0 * Rg * Bg), "tpf_bounds": [1.0, (blk + 1) / 2.0],
-        "note": "toy order-2 model; per round: target row, drafter rows, target rows, draft sampling, "
-                "verification, commit"}
-    print(f"# generate_toy: {1e3 * ms / Rg:.1f} us/round, TPF {toks / (2.0 * Rg * Bg):.3f}", file=sys.stderr,
-          flush=True)
-    del wsg, outs
-    torch.cuda.empty_cache()
+    if want("generate"):
+        # Multi-round generation on the toy order-2 model: 64 requests, block 8
+        # (7 drafts), V=32768 bf16, T=1, 32 rounds per call; every step (toy model
+        # passes, draft sampling, verification, commit) runs on the device.
+        Bg, blk, Vg, Rg = 64, 8, 32768, 32
+        prompt = torch.from_numpy(synth.randint(seed, 0, 2 * Bg, Vg).reshape(Bg, 2)).to(dev)
+        m = synth.TOY_MODEL
+        tm = psi.toy_model(m["seed"], m["sd"], m["n_heavy"], m["boost"], m["rho"], m["noise"])
+        wsg = torch.empty(int(psi.lib.psispec_generate_workspace_bytes(Bg, blk, Vg, psi.DTYPE_BF16)), dtype=torch.uint8,
+                          device=dev)
+        outs = dict(seq=torch.empty((Bg, Rg * (blk + 1)), dtype=torch.int32, device=dev),
+                    len=torch.empty((Bg,), dtype=torch.int32, device=dev),
+                    round_tokens=torch.empty((Bg, Rg), dtype=torch.int32, device=dev))
+        ms = time_calls(torch, lambda i: psi.generate_toy(prompt, blk, Vg, Rg, temperature=1.0, seed=seed, step=2 * Rg * i,
+                                                           model=tm, out=outs, workspace=wsg, stream=stream),
+                        max(steps // 10, 3), 1, stream)
+        toks = int(outs["len"].sum().item())
+        res["generate_toy_B64_block8_V32768_bf16"] = {
+            "us_per_call": 1e3 * ms, "rounds": Rg, "us_per_round": 1e3 * ms / Rg, "tokens_per_s": toks / (ms * 1e-3),
+            "tpf": toks / (2.0 * Rg * Bg), "tpf_bounds": [1.0, (blk + 1) / 2.0],
+            "note": "toy order-2 model; per round: target row, drafter rows, target rows, draft sampling, "
+                    "verification, commit"}
+        print(f"# generate_toy: {1e3 * ms / Rg:.1f} us/round, TPF {toks / (2.0 * Rg * Bg):.3f}", file=sys.stderr,
+              flush=True)
+        del wsg, outs
+        torch.cuda.empty_cache()
 
-    # Linear verification fused with the LM head: hidden states [64, 9, 4096]
-    # and [64, 8, 4096], vocabulary matrix [151936, 4096] (the Qwen3-8B head
-    # shape), bf16, seeded on the device; drafts uniform.
-    Bl, Kl, Hl, Vl = 64, 8, 4096, 151936
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(seed)
-    ht = torch.randn((Bl, Kl + 1, Hl), device=dev, generator=gen).to(torch.bfloat16)
-    hd = (ht[:, :Kl].float() + 0.3 * torch.randn((Bl, Kl, Hl), device=dev, generator=gen)).to(torch.bfloat16)
-    hd = hd.contiguous()
-    wv = (0.05 * torch.randn((Vl, Hl), device=dev, generator=gen)).to(torch.bfloat16)
-    xl = torch.randint(0, Vl, (Bl, Kl), device=dev, generator=gen, dtype=torch.int32)
-    wsl = torch.empty(int(psi.lib.psispec_lmhead_workspace_bytes(Bl, Kl, Vl)), dtype=torch.uint8, device=dev)
-    outs = dict(tokens=torch.empty((Bl, Kl + 1), dtype=torch.int32, device=dev),
-                len=torch.empty((Bl,), dtype=torch.int32, device=dev))
-    ms = time_calls(torch, lambda i: psi.verify_lmhead(ht, hd, wv, xl, temperature=1.0, seed=seed, step=i, out=outs,
-                                                        workspace=wsl, stream=stream), max(steps // 10, 3), 1, stream)
-    flops = 2.0 * (Bl * (2 * Kl + 1) + 2 * Bl) * Hl * Vl
-    tfs = flops / (ms * 1e-3) / 1e12
-    res["lmhead_verify_B64_K8_H4096_V151936_bf16"] = {
-        "us_per_call": 1e3 * ms, "flops": flops, "TFLOP_per_s": tfs, "mfma_bf16_frac": tfs / 2500.0,
-        "rows_per_s": Bl * Kl / (ms * 1e-3),
-        "note": "all 17 rows per request through the head once (stats epilogue) plus the 2 final rows again; "
-                "logits never written except the final rows"}
-    print(f"# lmhead_verify: {1e3 * ms:.0f} us/call, {tfs:.0f} TFLOP/s", file=sys.stderr, flush=True)
-    del ht, hd, wv, wsl
-    torch.cuda.empty_cache()
+    if want("lmhead"):
+        # Linear verification fused with the LM head: hidden states [64, 9, 4096]
+        # and [64, 8, 4096], vocabulary matrix [151936, 4096] (the Qwen3-8B head
+        # shape), bf16, seeded on the device; drafts uniform.
+        Bl, Kl, Hl, Vl = 64, 8, 4096, 151936
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        ht = torch.randn((Bl, Kl + 1, Hl), device=dev, generator=gen).to(torch.bfloat16)
+        hd = (ht[:, :Kl].float() + 0.3 * torch.randn((Bl, Kl, Hl), device=dev, generator=gen)).to(torch.bfloat16)
+        hd = hd.contiguous()
+        wv = (0.05 * torch.randn((Vl, Hl), device=dev, generator=gen)).to(torch.bfloat16)
+        xl = torch.randint(0, Vl, (Bl, Kl), device=dev, generator=gen, dtype=torch.int32)
+        wsl = torch.empty(int(psi.lib.psispec_lmhead_workspace_bytes(Bl, Kl, Vl)), dtype=torch.uint8, device=dev)
+        outs = dict(tokens=torch.empty((Bl, Kl + 1), dtype=torch.int32, device=dev),
+                    len=torch.empty((Bl,), dtype=torch.int32, device=dev))
+        ms = time_calls(torch, lambda i: psi.verify_lmhead(ht, hd, wv, xl, temperature=1.0, seed=seed, step=i, out=outs,
+                                                            workspace=wsl, stream=stream), max(steps // 10, 3), 1, stream)
+        flops = 2.0 * (Bl * (2 * Kl + 1) + 2 * Bl) * Hl * Vl
+        tfs = flops / (ms * 1e-3) / 1e12
+        res["lmhead_verify_B64_K8_H4096_V151936_bf16"] = {
+            "us_per_call": 1e3 * ms, "flops": flops, "TFLOP_per_s": tfs, "mfma_bf16_frac": tfs / 2500.0,
+            "rows_per_s": Bl * Kl / (ms * 1e-3),
+            "note": "all 17 rows per request through the head once (stats epilogue) plus the 2 final rows again; "
+                    "logits never written except the final rows"}
+        print(f"# lmhead_verify: {1e3 * ms:.0f} us/call, {tfs:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        del ht, hd, wv, wsl
+        torch.cuda.empty_cache()
     return res
 
 
@@ -314,6 +328,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--only", action="append", choices=WORKLOAD_NAMES,
+                    help="run only these other workloads (no headline); prints their results as one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): verification shards by request "
@@ -324,6 +340,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only:
+        import lossless_speculative_verification_amd as psi
+        import synth
+
+        stream = torch.cuda.current_stream()
+        res = other_workloads(torch, psi, synth, dev, stream, args.workload_steps, args.seed, only=set(args.only))
+        print(json.dumps({"workloads": res}), flush=True)
+        return
 
     if args.calibrate_copy:
         n = 1 << 30
