@@ -298,7 +298,7 @@ hipError_t launch_toy_logits(int64_t rows, int V, const int32_t* ctx, const int3
 // Linear verification fused with the LM head (lmhead.hip).
 enum LmhMode { kLmhStats = 0, kLmhLogits = 1 };
 constexpr int kLmhTileM = 128;  // rows of a product tile
-constexpr int kLmhTileN = 256;  // vocabulary entries of a product tile
+constexpr int kLmhTileN = 512;  // vocabulary entries of a product tile
 constexpr int kLmhStepK = 64;   // the hidden size must be a multiple of this
 struct LmhCfg {
   const uint16_t* hp;     // [Mp, H] target hidden states (bf16 bits)

@@ -7,7 +7,7 @@
 // the K + 1 target and K draft rows never reach HBM.
 //
 // Pipeline on the caller's stream:
-//   k_lmh_gemm<kLmhStats>   every target and draft row against every 256-token
+//   k_lmh_gemm<kLmhStats>   every target and draft row against every 512-token
 //                           vocabulary tile: per (row, tile) the maximum and a
 //                           binary32-grade sum of 2^((z - m) c), and the logit
 //                           of the row's drafted token;
@@ -18,11 +18,18 @@
 //   k_tree_pass, k_tree_pick (tree.hip) the fp64 residual / bonus draw over them.
 //
 // GEMM: C[M, V] = A[M, H] * W[V, H]^T, A rows from the target and draft hidden
-// states. A workgroup computes a 128-row x 256-token tile with four waves (2 x
-// 2, 64 x 128 each, as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16), stepping over
-// H by 32 with both operand tiles double-buffered in LDS (rows padded by 16
-// bytes so that the 16-byte fragment reads of a wave do not collide in banks),
-// the global loads issued two steps ahead and two workgroups per CU.
+// states. A workgroup computes a 128-row x 512-token tile with four waves, each
+// owning 128 tokens of the tile (all 128 rows): 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16, 256 accumulator registers, one wave per SIMD.
+// Operand tiles of 32 hidden elements per step go from global memory straight
+// into LDS (16-byte direct loads, no register staging) through a three-stage
+// ring, two steps ahead of the step being multiplied; a step's loads are
+// issued one between each pair of its products. A tile row is 64 bytes in
+// LDS: its four 16-byte slots are permuted by an XOR of row bits 2..3, so that
+// the 16-byte fragment reads of a wave do not conflict in the LDS banks. The
+// tile epilogue reduces each row over the wave's 128 columns with a butterfly
+// across the half-wave (every stage halves the rows a lane carries), then
+// over the four waves through LDS.
 // Block operand layout of the instruction (checked on the device): lane l
 // holds A[l % 32][8 (l / 32) .. +7] and W[col l % 32][8 (l / 32) .. +7]; result
 // element i of lane l is C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
@@ -35,14 +42,31 @@ namespace psi {
 namespace {
 
 constexpr int kLmhBM = kLmhTileM, kLmhBN = kLmhTileN, kLmhBK = 32;
-static_assert(kLmhBM == 128 && kLmhBN == 256, "four 64 x 128 wave tiles");
+static_assert(kLmhBM == 128 && kLmhBN == 512, "four 128 x 128 wave tiles side by side");
 static_assert(kLmhStepK % kLmhBK == 0, "the hidden size is a multiple of the step");
-constexpr int kLmhPad = 8;                      // bf16 elements of padding per LDS row
-constexpr int kLmhLd = kLmhBK + kLmhPad;        // LDS row stride (elements)
+constexpr int kStages = 3;                        // ring depth: loads run kStages - 1 steps ahead
+constexpr int kRowB = kLmhBK * 2;                 // bytes of a tile row per step
+constexpr int kAStage = kLmhBM * kRowB;           // 8 KB
+constexpr int kBStage = kLmhBN * kRowB;           // 32 KB
+constexpr int kStage = kAStage + kBStage;
+constexpr int kLoadB = kWave * 16;                // bytes of one wave-wide direct load
+constexpr int kRowsPerLoad = kLoadB / kRowB;      // 16 rows of 4 slots
+constexpr int kIA = kAStage / kLoadB / kWaves;    // direct loads per wave per step: A
+constexpr int kIB = kBStage / kLoadB / kWaves;    //                               W
+constexpr int kLoads = kIA + kIB;
+static_assert(kIA * kLoadB * kWaves == kAStage && kIB * kLoadB * kWaves == kBStage, "whole loads");
+static_assert(kRowsPerLoad == 16 && kLoads <= 16, "a load covers 16 rows of 4 slots; one per product");
 constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Slot permutation of tile row r (its 4 16-byte slots, by bits 2..3 of r: a
+// function of r % 16, the same for every load of a lane). With it the 16-byte
+// fragment reads of a wave, 32 rows at one logical slot, are free of LDS bank
+// conflicts (measured).
+__device__ __forceinline__ int lmh_swz(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ const uint16_t* lmh_arow(const LmhCfg& g, int64_t r) {
   return r < g.Mp ? g.hp + r * (int64_t)g.H : g.hq + (r - g.Mp) * (int64_t)g.H;
@@ -59,18 +83,43 @@ __device__ __forceinline__ int lmh_token(const LmhCfg& g, int64_t r) {
   return g.draft[r - g.Mp];
 }
 
+// One wave-wide direct load: 16 bytes per lane from gptr into LDS at
+// lds + 16 * lane. Written as an asm statement so that the compiler does not
+// add a full vmcnt wait before every LDS read of the ring (it cannot tell the
+// stages apart); the ring's waits are explicit (wait_vm) and the statement
+// has no register output. The LDS base goes through M0, which the compiler
+// does not otherwise use in these kernels (M0 is a reserved register and
+// cannot be listed as clobbered).
+__device__ __forceinline__ void lmh_dma16(const uint16_t* gptr, const unsigned char* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(la)
+               : "memory");
+}
+// Waits until at most N direct loads of this wave are outstanding (vmcnt; the
+// other counters are left alone).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field (bits 3:0 and 15:14)");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// Workgroup barrier with no memory fence: the direct loads are waited for
+// explicitly; the asm statements keep the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void lmh_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace
 
 template <int MODE>
-__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void k_lmh_gemm(LmhCfg g) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kLmhBM * kLmhLd];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kLmhBN * kLmhLd];
-  __shared__ int64_t s_row[kLmhBM];  // combined row index of each tile row (-1 past the end)
-  __shared__ int s_tok[kLmhBM];
-  __shared__ float s_wm[2][kLmhBM];
-  __shared__ float s_ws[2][kLmhBM];
-  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k_lmh_gemm(LmhCfg g) {
+  // ring of operand tiles; after the main loop the start of it
+  // holds the epilogue's row tables
+  __shared__ __attribute__((aligned(1024))) unsigned char s_mem[kStages * kStage];
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
   // tile order: row tiles of one vocabulary tile consecutive on one XCD
   // (workgroup g runs on XCD g % 8; the grid is a multiple of 8)
   const int64_t per = (int64_t)gridDim.x / kXcds;
@@ -78,153 +127,197 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void k
   if (lt >= (int64_t)g.ntm * g.ntn) return;  // the whole workgroup
   const int64_t tn = lt / g.ntm, tm = lt - tn * g.ntm;
   const int64_t m0 = tm * kLmhBM, n0 = tn * kLmhBN;
-  if (t < kLmhBM) {
-    const int64_t i = m0 + t;
-    int64_t r = -1;
-    if (i < g.M) r = g.rows ? (int64_t)g.rows[i] : i;
-    s_row[t] = r;
-    s_tok[t] = (MODE == kLmhStats && r >= 0) ? lmh_token(g, r) : -1;
-  }
-  __syncthreads();
-
-  // global -> register staging: thread t always loads the 16-byte column
-  // t % VPR of tile rows t / VPR + RPP j (VPR vectors per row of the step,
-  // RPP rows per pass of the workgroup), addresses formed once here; rows
-  // past the end read a valid row and are zeroed (no branches)
-  constexpr int VPR = kLmhBK / 8, RPP = kWG / VPR;
-  constexpr int NA = kLmhBM / RPP, NB = kLmhBN / RPP;
-  const int kv = t % VPR, r0 = t / VPR;
-  const uint16_t* pa[NA];
-  const uint16_t* pb[NB];
-  uint32_t live = 0;  // bit j: A row j valid; bit NA + j: W row j valid
-#pragma unroll
-  for (int j = 0; j < NA; ++j) {
-    const int64_t r = s_row[r0 + RPP * j];
-    live |= r >= 0 ? 1u << j : 0u;
-    pa[j] = lmh_arow(g, r >= 0 ? r : 0) + kv * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int64_t n = n0 + r0 + RPP * j;
-    live |= n < g.V ? 1u << (NA + j) : 0u;
-    pb[j] = g.w + (n < g.V ? n : 0) * (int64_t)g.H + kv * 8;
-  }
-  // two register sets: the loads of step s + 2 are issued while step s is
-  // multiplied, and step s + 1 (loaded during step s - 1) is stored to LDS
-  uint4 ra0[NA], rb0[NB], ra1[NA], rb1[NB];
-  auto load_step = [&](int k0, uint4 (&ra)[NA], uint4 (&rb)[NB]) {
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const uint4 x = *(const uint4*)(pa[j] + k0);
-      ra[j] = (live >> j) & 1u ? x : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const uint4 x = *(const uint4*)(pb[j] + k0);
-      rb[j] = (live >> (NA + j)) & 1u ? x : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_step = [&](int buf, const uint4 (&ra)[NA], const uint4 (&rb)[NB]) {
-#pragma unroll
-    for (int j = 0; j < NA; ++j) *(uint4*)&s_a[buf][(r0 + RPP * j) * kLmhLd + kv * 8] = ra[j];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) *(uint4*)&s_b[buf][(r0 + RPP * j) * kLmhLd + kv * 8] = rb[j];
+  auto combined_row = [&](int row) -> int64_t {  // combined row index of tile row `row` (-1 past the end)
+    const int64_t i = m0 + row;
+    if (i >= g.M) return -1;
+    return g.rows ? (int64_t)g.rows[i] : i;
   };
 
-  f32x16_t acc[2][4];
+  // direct loads: load j of this wave fills 16 tile rows; lane l writes LDS
+  // slot l % 4 of row l / 4 of them, i.e. logical slot (l % 4) ^ swz(row),
+  // swz(row) = swz(l / 4). Rows past the end read a valid row (their results
+  // are never used).
+  const int lr = lane >> 2;
+  const int kvo = ((lane & 3) ^ lmh_swz(lr)) * 8;  // element offset of this lane's slot
+  const uint16_t* src[kLoads];                     // loads 0 .. kIA - 1: A rows; then W rows
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int j = 0; j < kIA; ++j) {
+    const int64_t r = combined_row((wave * kIA + j) * kRowsPerLoad + lr);
+    src[j] = lmh_arow(g, r >= 0 ? r : 0) + kvo;
+  }
+#pragma unroll
+  for (int j = 0; j < kIB; ++j) {
+    const int64_t n = n0 + (int64_t)(wave * kIB + j) * kRowsPerLoad + lr;
+    src[kIA + j] = g.w + (n < g.V ? n : (int64_t)g.V - 1) * g.H + kvo;
+  }
+  auto dst = [&](unsigned char* st, int j) {
+    return j < kIA ? st + (wave * kIA + j) * kLoadB : st + kAStage + (wave * kIB + (j - kIA)) * kLoadB;
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.0f;
 
+  // fragment reads: lane l reads row (block + l % 32), logical slot
+  // 2 q + l / 32 of slice q; swz(row) = swz(l % 16)
+  const int fr = lane & 31, half = lane >> 5;
+  const int frow = fr * kRowB;
+  const int fsw = lmh_swz(fr);
+  const int bw = kAStage + wave * 128 * kRowB;  // this wave's W rows in a stage
+  bf16x8_t fa[2][4], fb[2][4];
+  auto read_frag = [&](const unsigned char* st, int q, int slot) {
+    const int fo = frow + (((2 * q + half) ^ fsw) * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[slot][i] = *(const bf16x8_t*)(st + i * 32 * kRowB + fo);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fb[slot][i] = *(const bf16x8_t*)(st + bw + i * 32 * kRowB + fo);
+  };
+  auto mfma1 = [&](int slot, int i) {
+    acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i >> 2], fb[slot][i & 3], acc[i >> 2][i & 3],
+                                                                 0, 0, 0);
+  };
+  auto mfma = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mfma1(slot, i);
+  };
+
   const int steps = g.H / kLmhBK;
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
-  // operand fragments of one 16-deep slice, read one slice ahead of the MFMAs
-  bf16x8_t fa[2][2], fb[2][4];
-  auto read_frag = [&](int buf, int kk, int slot) {
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-      fa[slot][bi] = *(const bf16x8_t*)&s_a[buf][(wm * 64 + bi * 32 + fr) * kLmhLd + kk + fk];
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-      fb[slot][bj] = *(const bf16x8_t*)&s_b[buf][(wn * 128 + bj * 32 + fr) * kLmhLd + kk + fk];
+  auto ring = [&](int i) { return s_mem + i * kStage; };
+  // wait until a step's loads are in, leaving those of the min(later, cap)
+  // steps issued after it in flight
+  auto wait_steps = [&](int later, int cap) {
+    const int k = later < cap ? later : cap;
+    if (k <= 0) wait_vm<0>();
+    else if (k == 1) wait_vm<kLoads>();
+    else if (k == 2) wait_vm<2 * kLoads>();
+    else wait_vm<3 * kLoads>();
   };
-  auto step = [&](int s, uint4 (&la)[NA], uint4 (&lb)[NB], const uint4 (&sa)[NA], const uint4 (&sb)[NB]) {
-    const int buf = s & 1;
-    if (s + 2 < steps) load_step((s + 2) * kLmhBK, la, lb);
+  static_assert(kStages <= 4, "wait_steps covers up to three later steps");
+  // prologue: steps 0 .. kStages - 1 in flight, wait for step 0
 #pragma unroll
-    for (int q = 0; q < kLmhBK / 16; ++q) {
-      if (q + 1 < kLmhBK / 16) read_frag(buf, (q + 1) * 16, (q + 1) & 1);
+  for (int p = 0; p < kStages; ++p)
+    if (p < steps)
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
+      for (int j = 0; j < kLoads; ++j) lmh_dma16(src[j] + p * kLmhBK, dst(ring(p), j));
+  wait_steps(steps - 1, kStages - 1);
+  lmh_barrier();
+  read_frag(ring(0), 0, 0);
+  int cur = 0;  // ring slot of step s
+  for (int s = 0; s < steps; ++s) {
+    unsigned char* st = ring(cur);
+    const int nxt = cur == kStages - 1 ? 0 : cur + 1;
+    // slice 0 of step s is in fa[0] / fb[0]
+    read_frag(st, 1, 1);
+    mfma(0);
+    wait_steps(steps - s - 2, kStages - 2);  // step s + 1 is in; later steps may stay in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of this stage are done
+    lmh_barrier();
+    if (s + 1 < steps) read_frag(ring(nxt), 0, 0);
+    // slice 1 of step s, with the loads of step s + kStages into this stage
+    // spread between its products
+    const bool refill = s + kStages < steps;
+    const int k0 = (s + kStages) * kLmhBK;
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
-          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q & 1][bi], fb[q & 1][bj], acc[bi][bj], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) {
+      mfma1(1, i);
+      if (i < kLoads && refill) lmh_dma16(src[i] + k0, dst(st, i));
     }
-    if (s + 1 < steps) store_step(buf ^ 1, sa, sb);
+    cur = nxt;
+  }
+
+  // epilogue row tables (the ring is no longer read: every wave passed the
+  // last step's barrier after its last read)
+  int64_t* s_row = (int64_t*)s_mem;                     // combined row index of each tile row
+  int* s_tok = (int*)(s_mem + kLmhBM * sizeof(int64_t));  // drafted token of each tile row (-1: none)
+  float(*s_wm)[kLmhBM] = (float(*)[kLmhBM])(s_mem + 2048);
+  float(*s_ws)[kLmhBM] = (float(*)[kLmhBM])(s_mem + 2048 + kWaves * kLmhBM * sizeof(float));
+  if constexpr (MODE == kLmhStats) {
+    if (t < kLmhBM) {
+      const int64_t r = combined_row(t);
+      s_row[t] = r;
+      s_tok[t] = r >= 0 ? lmh_token(g, r) : -1;
+    }
     __syncthreads();
-    if (s + 1 < steps) read_frag(buf ^ 1, 0, 0);
-  };
-  load_step(0, ra0, rb0);
-  store_step(0, ra0, rb0);
-  if (steps > 1) load_step(kLmhBK, ra1, rb1);
-  __syncthreads();
-  read_frag(0, 0, 0);
-  for (int s = 0; s < steps; s += 2) {
-    step(s, ra0, rb0, ra1, rb1);  // loads step s + 2 into set 0, stores step s + 1 from set 1
-    if (s + 1 < steps) step(s + 1, ra1, rb1, ra0, rb0);
   }
 
   // ---- epilogue. Element e of block (bi, bj) on this lane: tile row
-  // wm 64 + bi 32 + 8 (e / 4) + 4 (lane / 32) + e % 4, tile column
-  // wn 128 + bj 32 + lane % 32.
-  const int half = lane >> 5;
+  // bi 32 + 8 (e / 4) + 4 (lane / 32) + e % 4, tile column
+  // wave 128 + bj 32 + lane % 32.
   if constexpr (MODE == kLmhLogits) {
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = wm * 64 + bi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        const int row = bi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
         const int64_t i = m0 + row;
         if (i >= g.M) continue;
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
-          const int64_t n = n0 + wn * 128 + bj * 32 + fr;
+          const int64_t n = n0 + wave * 128 + bj * 32 + fr;
           if (n < g.V) g.out[i * (int64_t)g.V + n] = acc[bi][bj][e];
         }
       }
   } else {
     const float c32 = g.c32;
+    // Per row of the tile (item it = 16 bi + e of this lane: row
+    // 32 bi + 8 (e / 4) + 4 (lane / 32) + e % 4): the maximum and the sum of
+    // 2^((z - m) c) over this lane's 4 columns, then over the 32 lanes of the
+    // half-wave by a butterfly that halves the items at every stage (at offset
+    // o a lane keeps the items whose index bit matches its lane bit and sends
+    // the others), so that lane l ends with items 2 (l % 32) and 2 (l % 32) + 1.
+    float im[64], is[64];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int it = 0; it < 64; ++it) {
+      const int bi = it >> 4, e = it & 15;
+      float m = -INFINITY;
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+        if (n0 + wave * 128 + bj * 32 + fr < g.V) m = fmaxnan(m, acc[bi][bj][e]);
+      float sl = 0.0f;
+      if (!is_neg_inf(m)) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+          if (n0 + wave * 128 + bj * 32 + fr < g.V) sl += __builtin_amdgcn_exp2f((acc[bi][bj][e] - m) * c32);
+      }
+      im[it] = m;
+      is[it] = sl;
+    }
+    auto part = [&](float mx, float sx, float m) {  // sx 2^((mx - m) c), 0 for an empty part
+      return is_neg_inf(mx) ? 0.0f : sx * __builtin_amdgcn_exp2f((mx - m) * c32);
+    };
+#pragma unroll
+    for (int stg = 0; stg < 5; ++stg) {
+      const int off = 16 >> stg, n = 32 >> stg;
+      const bool up = (fr & off) != 0;
+#pragma unroll
+      for (int i = 0; i < n; ++i) {
+        const float mk = up ? im[i + n] : im[i], sk = up ? is[i + n] : is[i];
+        const float mo = up ? im[i] : im[i + n], so = up ? is[i] : is[i + n];
+        const float mr = __shfl_xor(mo, off), sr = __shfl_xor(so, off);
+        const float m = fmaxnan(mk, mr);
+        im[i] = m;
+        is[i] = is_neg_inf(m) ? 0.0f : part(mk, sk, m) + part(mr, sr, m);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int it = 2 * fr + i, bi = it >> 4, e = it & 15;
+      const int row = bi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+      s_wm[wave][row] = im[i];
+      s_ws[wave][row] = is[i];
+    }
+    // the drafted token's logit, from the lane that holds its column
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = wm * 64 + bi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-        float m = -INFINITY;
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const int64_t n = n0 + wn * 128 + bj * 32 + fr;
-          if (n < g.V) m = fmaxnan(m, acc[bi][bj][e]);
-        }
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) m = fmaxnan(m, __shfl_xor(m, o));  // within the 32-lane half
-        float sl = 0.0f;
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const int64_t n = n0 + wn * 128 + bj * 32 + fr;
-          if (n < g.V) sl += __builtin_amdgcn_exp2f((acc[bi][bj][e] - m) * c32);
-        }
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) sl += __shfl_xor(sl, o);
-        if (fr == 0) {
-          s_wm[wn][row] = m;
-          s_ws[wn][row] = sl;
-        }
-        // the drafted token's logit, from the lane that holds its column
+        const int row = bi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
         const int x = s_tok[row];
-        const int64_t rel = (int64_t)x - (n0 + wn * 128);
+        const int64_t rel = (int64_t)x - (n0 + wave * 128);
         if (x >= 0 && rel >= 0 && rel < 128 && (int)(rel & 31) == fr) {
           const int bj = (int)(rel >> 5);
           const float z = bj == 0 ? acc[bi][0][e] : bj == 1 ? acc[bi][1][e] : bj == 2 ? acc[bi][2][e] : acc[bi][3][e];
@@ -235,12 +328,16 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (t < kLmhBM) {
       const int64_t r = s_row[t];
       if (r >= 0) {
-        const float ma = s_wm[0][t], mb = s_wm[1][t];
-        const float m = fmaxnan(ma, mb);
+        float m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) m = fmaxnan(m, s_wm[w][t]);
         double s = 0.0;
         if (!is_neg_inf(m)) {
-          if (!is_neg_inf(ma)) s += (double)s_ws[0][t] * ::exp2(((double)ma - (double)m) * (double)c32);
-          if (!is_neg_inf(mb)) s += (double)s_ws[1][t] * ::exp2(((double)mb - (double)m) * (double)c32);
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) {
+            const float mw = s_wm[w][t];
+            if (!is_neg_inf(mw)) s += (double)s_ws[w][t] * ::exp2(((double)mw - (double)m) * (double)c32);
+          }
         }
         if (isnan(m) || isinf(m)) s = NAN;
         g.st[r * (int64_t)g.ntn + tn] = StatRec{m, 0u, s};
@@ -252,16 +349,17 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(2))) void k
 // Per request (one workgroup): the row normalisers of the K + 1 target and K
 // draft rows from the tile records (a wave per row), the accept tests, the
 // first rejection n, the accepted tokens, and the state of the final draw.
-__global__ __launch_bounds__(kWG) void k_lmh_decide(LmhCfg g, LinCfg c, TreeCfg tc) {
+constexpr int kDecideWG = 1024;  // 16 waves: about one row of the request per wave
+__global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, TreeCfg tc) {
   const int64_t b = blockIdx.x;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int K = g.K;
   __shared__ float s_m[2 * kMaxK + 1];
   __shared__ double s_S[2 * kMaxK + 1];
-  __shared__ int s_bad, s_n;
+  __shared__ int s_bad;
   if (t == 0) s_bad = 0;
   __syncthreads();
-  for (int j = wave; j < 2 * K + 1; j += kWaves) {
+  for (int j = wave; j < 2 * K + 1; j += kDecideWG / kWave) {
     const int64_t r = j <= K ? b * (K + 1) + j : g.Mp + b * K + (j - K - 1);
     const StatRec* rec = g.st + r * (int64_t)g.ntn;
     float m = -INFINITY;
@@ -286,7 +384,7 @@ __global__ __launch_bounds__(kWG) void k_lmh_decide(LmhCfg g, LinCfg c, TreeCfg 
       if (bad || isnan(m) || isinf(m) || !(S > 0.0)) atomicOr(&s_bad, 1);
     }
   }
-  for (int i = t; i < K; i += kWG) {
+  for (int i = t; i < K; i += kDecideWG) {
     const int x = g.draft[b * K + i];
     if (x < 0 || x >= g.V) atomicOr(&s_bad, 1);
   }
@@ -344,7 +442,7 @@ hipError_t launch_lmh_stats(const LmhCfg& g, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_lmh_decide(const LmhCfg& g, const LinCfg& c, const TreeCfg& tc, hipStream_t s) {
-  PSI_LAUNCH(s, k_lmh_decide, dim3((unsigned)g.B), dim3(kWG), g, c, tc);
+  PSI_LAUNCH(s, k_lmh_decide, dim3((unsigned)g.B), dim3(kDecideWG), g, c, tc);
   return hipGetLastError();
 }
 hipError_t launch_lmh_logits(const LmhCfg& g, hipStream_t s) {
