@@ -455,7 +455,7 @@ int psispec_generate_toy(int64_t B, int32_t block, int32_t V, int dtype, const p
 namespace psi {
 namespace {
 struct LmhLayout {
-  size_t st, glog, fin, ts, tres, out, total;
+  size_t st, fin, ts, tres, out, total;
 };
 inline LmhLayout lmh_layout(int64_t B, int32_t K, int32_t V) {
   LmhLayout L;
@@ -464,8 +464,6 @@ inline LmhLayout lmh_layout(int64_t B, int32_t K, int32_t V) {
   size_t off = 0;
   L.st = off;
   off = align_up(off + (size_t)(rows * ntn) * sizeof(StatRec), 256);
-  L.glog = off;
-  off = align_up(off + (size_t)rows * sizeof(float), 256);
   L.fin = off;
   off = align_up(off + (size_t)(2 * B) * sizeof(int32_t), 256);
   L.ts = off;
@@ -515,7 +513,6 @@ int psispec_verify_lmhead(const void* h_target, const void* h_draft, const void*
   g.draft = draft_tokens;
   g.c32 = (float)(1.4426950408889634074 / (double)params->temperature);
   g.st = (StatRec*)(w + L.st);
-  g.glog = (float*)(w + L.glog);
   g.fin = (int32_t*)(w + L.fin);
   g.out = (float*)(w + L.out);
   // the draw over the final rows: target rows [B, V] then draft rows [B, V] (fp32)

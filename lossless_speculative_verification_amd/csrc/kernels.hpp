@@ -313,7 +313,6 @@ struct LmhCfg {
   const int32_t* draft;   // [B, K]
   float c32;
   StatRec* st;            // [Mp + Mq][ntn] per (row, vocabulary tile)
-  float* glog;            // [Mp + Mq] logit of each row's drafted token
   int32_t* fin;           // [2 B] final rows: target row n of each request, then draft row n
   float* out;             // [M][V] logits (final-row product)
 };

@@ -44,7 +44,7 @@ namespace {
 constexpr int kLmhBM = kLmhTileM, kLmhBN = kLmhTileN, kLmhBK = 32;
 static_assert(kLmhBM == 128 && kLmhBN == 512, "four 128 x 128 wave tiles side by side");
 static_assert(kLmhStepK % kLmhBK == 0, "the hidden size is a multiple of the step");
-constexpr int kStages = 3;                        // ring depth: loads run kStages - 1 steps ahead
+constexpr int kStages = 4;                        // ring depth (160 KB): loads of step s + 3 spread over step s
 constexpr int kRowB = kLmhBK * 2;                 // bytes of a tile row per step
 constexpr int kAStage = kLmhBM * kRowB;           // 8 KB
 constexpr int kBStage = kLmhBN * kRowB;           // 32 KB
@@ -55,7 +55,8 @@ constexpr int kIA = kAStage / kLoadB / kWaves;    // direct loads per wave per s
 constexpr int kIB = kBStage / kLoadB / kWaves;    //                               W
 constexpr int kLoads = kIA + kIB;
 static_assert(kIA * kLoadB * kWaves == kAStage && kIB * kLoadB * kWaves == kBStage, "whole loads");
-static_assert(kRowsPerLoad == 16 && kLoads <= 16, "a load covers 16 rows of 4 slots; one per product");
+static_assert(kRowsPerLoad == 16 && kLoads == 10, "a load covers 16 rows of 4 slots; 5 loads per half step");
+constexpr int kHalfLoads = kLoads / 2;
 constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -70,17 +71,6 @@ __device__ __forceinline__ int lmh_swz(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ const uint16_t* lmh_arow(const LmhCfg& g, int64_t r) {
   return r < g.Mp ? g.hp + r * (int64_t)g.H : g.hq + (r - g.Mp) * (int64_t)g.H;
-}
-
-// Drafted token of combined row r (target rows b (K + 1) + i, then draft rows
-// b K + i); -1 for a bonus row.
-__device__ __forceinline__ int lmh_token(const LmhCfg& g, int64_t r) {
-  if (r < g.Mp) {
-    const int64_t b = r / (g.K + 1);
-    const int i = (int)(r - b * (g.K + 1));
-    return i < g.K ? g.draft[b * g.K + i] : -1;
-  }
-  return g.draft[r - g.Mp];
 }
 
 // One wave-wide direct load: 16 bytes per lane from gptr into LDS at
@@ -180,69 +170,62 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i >> 2], fb[slot][i & 3], acc[i >> 2][i & 3],
                                                                  0, 0, 0);
   };
-  auto mfma = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mfma1(slot, i);
-  };
+
 
   const int steps = g.H / kLmhBK;
   auto ring = [&](int i) { return s_mem + i * kStage; };
-  // wait until a step's loads are in, leaving those of the min(later, cap)
-  // steps issued after it in flight
-  auto wait_steps = [&](int later, int cap) {
-    const int k = later < cap ? later : cap;
-    if (k <= 0) wait_vm<0>();
-    else if (k == 1) wait_vm<kLoads>();
-    else if (k == 2) wait_vm<2 * kLoads>();
-    else wait_vm<3 * kLoads>();
+  // Waits until at most n direct loads of this wave are outstanding.
+  auto wait_loads = [&](int n) {
+    if (n >= 3 * kHalfLoads) wait_vm<3 * kHalfLoads>();
+    else if (n >= 2 * kHalfLoads) wait_vm<2 * kHalfLoads>();
+    else if (n >= kHalfLoads) wait_vm<kHalfLoads>();
+    else wait_vm<0>();
   };
-  static_assert(kStages <= 4, "wait_steps covers up to three later steps");
-  // prologue: steps 0 .. kStages - 1 in flight, wait for step 0
+  // prologue: steps 0 .. 2 in flight, wait for step 0
 #pragma unroll
-  for (int p = 0; p < kStages; ++p)
+  for (int p = 0; p < kStages - 1; ++p)
     if (p < steps)
 #pragma unroll
       for (int j = 0; j < kLoads; ++j) lmh_dma16(src[j] + p * kLmhBK, dst(ring(p), j));
-  wait_steps(steps - 1, kStages - 1);
+  wait_loads(((steps > 1) + (steps > 2)) * kLoads);
   lmh_barrier();
   read_frag(ring(0), 0, 0);
   int cur = 0;  // ring slot of step s
   for (int s = 0; s < steps; ++s) {
     unsigned char* st = ring(cur);
     const int nxt = cur == kStages - 1 ? 0 : cur + 1;
+    // The loads of step s + 3 go to the slot of step s - 1, free since the
+    // middle of step s - 1; they are spread over the products of step s, one
+    // between each pair (the load unit takes them as fast as they come).
+    unsigned char* fill = ring(cur == 0 ? kStages - 1 : cur - 1);
+    const bool refill = s + 3 < steps;
+    const int k0 = (s + 3) * kLmhBK;
     // slice 0 of step s is in fa[0] / fb[0]
     read_frag(st, 1, 1);
-    mfma(0);
-    wait_steps(steps - s - 2, kStages - 2);  // step s + 1 is in; later steps may stay in flight
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mfma1(0, i);
+      if ((i & 1) && i / 2 < kHalfLoads && refill) lmh_dma16(src[i / 2] + k0, dst(fill, i / 2));
+    }
+    // step s + 1 is in; the loads of step s + 2 and the first half of step
+    // s + 3 may stay in flight
+    wait_loads((s + 2 < steps ? kLoads : 0) + (refill ? kHalfLoads : 0));
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of this stage are done
     lmh_barrier();
     if (s + 1 < steps) read_frag(ring(nxt), 0, 0);
-    // slice 1 of step s, with the loads of step s + kStages into this stage
-    // spread between its products
-    const bool refill = s + kStages < steps;
-    const int k0 = (s + kStages) * kLmhBK;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mfma1(1, i);
-      if (i < kLoads && refill) lmh_dma16(src[i] + k0, dst(st, i));
+      if ((i & 1) && i / 2 < kHalfLoads && refill)
+        lmh_dma16(src[kHalfLoads + i / 2] + k0, dst(fill, kHalfLoads + i / 2));
     }
     cur = nxt;
   }
 
-  // epilogue row tables (the ring is no longer read: every wave passed the
-  // last step's barrier after its last read)
-  int64_t* s_row = (int64_t*)s_mem;                     // combined row index of each tile row
-  int* s_tok = (int*)(s_mem + kLmhBM * sizeof(int64_t));  // drafted token of each tile row (-1: none)
-  float(*s_wm)[kLmhBM] = (float(*)[kLmhBM])(s_mem + 2048);
-  float(*s_ws)[kLmhBM] = (float(*)[kLmhBM])(s_mem + 2048 + kWaves * kLmhBM * sizeof(float));
-  if constexpr (MODE == kLmhStats) {
-    if (t < kLmhBM) {
-      const int64_t r = combined_row(t);
-      s_row[t] = r;
-      s_tok[t] = r >= 0 ? lmh_token(g, r) : -1;
-    }
-    __syncthreads();
-  }
+  // epilogue tables at the start of the ring (no longer read: every wave
+  // passed the last step's barrier after its last read)
+  float(*s_wm)[kLmhBM] = (float(*)[kLmhBM])s_mem;
+  float(*s_ws)[kLmhBM] = (float(*)[kLmhBM])(s_mem + kWaves * kLmhBM * sizeof(float));
 
   // ---- epilogue. Element e of block (bi, bj) on this lane: tile row
   // bi 32 + 8 (e / 4) + 4 (lane / 32) + e % 4, tile column
@@ -269,20 +252,20 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     // half-wave by a butterfly that halves the items at every stage (at offset
     // o a lane keeps the items whose index bit matches its lane bit and sends
     // the others), so that lane l ends with items 2 (l % 32) and 2 (l % 32) + 1.
+    bool vcol[4];  // this lane's column of block bj is inside the vocabulary
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) vcol[bj] = n0 + wave * 128 + bj * 32 + fr < g.V;
     float im[64], is[64];
 #pragma unroll
     for (int it = 0; it < 64; ++it) {
       const int bi = it >> 4, e = it & 15;
       float m = -INFINITY;
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
-        if (n0 + wave * 128 + bj * 32 + fr < g.V) m = fmaxnan(m, acc[bi][bj][e]);
+      for (int bj = 0; bj < 4; ++bj) m = vcol[bj] ? fmaxnan(m, acc[bi][bj][e]) : m;
+      const float mo = is_neg_inf(m) ? 0.0f : m;  // an empty part sums to 0
       float sl = 0.0f;
-      if (!is_neg_inf(m)) {
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
-          if (n0 + wave * 128 + bj * 32 + fr < g.V) sl += __builtin_amdgcn_exp2f((acc[bi][bj][e] - m) * c32);
-      }
+      for (int bj = 0; bj < 4; ++bj) sl += vcol[bj] ? __builtin_amdgcn_exp2f((acc[bi][bj][e] - mo) * c32) : 0.0f;
       im[it] = m;
       is[it] = sl;
     }
@@ -310,23 +293,9 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
       s_wm[wave][row] = im[i];
       s_ws[wave][row] = is[i];
     }
-    // the drafted token's logit, from the lane that holds its column
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = bi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const int x = s_tok[row];
-        const int64_t rel = (int64_t)x - (n0 + wave * 128);
-        if (x >= 0 && rel >= 0 && rel < 128 && (int)(rel & 31) == fr) {
-          const int bj = (int)(rel >> 5);
-          const float z = bj == 0 ? acc[bi][0][e] : bj == 1 ? acc[bi][1][e] : bj == 2 ? acc[bi][2][e] : acc[bi][3][e];
-          g.glog[s_row[row]] = z;
-        }
-      }
     __syncthreads();
     if (t < kLmhBM) {
-      const int64_t r = s_row[t];
+      const int64_t r = combined_row(t);
       if (r >= 0) {
         float m = -INFINITY;
 #pragma unroll
@@ -347,8 +316,11 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
 }
 
 // Per request (one workgroup): the row normalisers of the K + 1 target and K
-// draft rows from the tile records (a wave per row), the accept tests, the
-// first rejection n, the accepted tokens, and the state of the final draw.
+// draft rows from the tile records (a wave per row), the logits of the drafted
+// tokens as dot products of the hidden states with the tokens' rows of W (fp32
+// products, summed per lane in order and across lanes in fp64), the accept
+// tests, the first rejection n, the accepted tokens, and the state of the
+// final draw.
 constexpr int kDecideWG = 1024;  // 16 waves: about one row of the request per wave
 __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, TreeCfg tc) {
   const int64_t b = blockIdx.x;
@@ -356,11 +328,30 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
   const int K = g.K;
   __shared__ float s_m[2 * kMaxK + 1];
   __shared__ double s_S[2 * kMaxK + 1];
+  __shared__ float s_z[2 * kMaxK + 1];  // logit of the row's drafted token
   __shared__ int s_bad;
   if (t == 0) s_bad = 0;
   __syncthreads();
   for (int j = wave; j < 2 * K + 1; j += kDecideWG / kWave) {
     const int64_t r = j <= K ? b * (K + 1) + j : g.Mp + b * K + (j - K - 1);
+    if (j != K) {  // row K is the bonus row: no drafted token
+      const int x = g.draft[b * K + (j < K ? j : j - K - 1)];
+      float z = NAN;
+      if (x >= 0 && x < g.V) {
+        const uint4* hv = (const uint4*)lmh_arow(g, r);
+        const uint4* wv = (const uint4*)(g.w + (int64_t)x * g.H);
+        float a = 0.0f;
+        for (int v = lane; v < g.H / 8; v += kWave) {
+          float h8[8], w8[8];
+          Elem<kBF16>::unpack(hv[v], h8);
+          Elem<kBF16>::unpack(wv[v], w8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a = __builtin_fmaf(h8[e], w8[e], a);
+        }
+        z = (float)wave_sum((double)a);
+      }
+      if (lane == 0) s_z[j] = z;
+    }
     const StatRec* rec = g.st + r * (int64_t)g.ntn;
     float m = -INFINITY;
     int bad = 0;
@@ -393,8 +384,8 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
   int n = K;
   if (!s_bad) {
     for (int i = 0; i < K; ++i) {
-      const double P = ::exp(((double)g.glog[b * (K + 1) + i] - (double)s_m[i]) * c.invT - ::log(s_S[i]));
-      const double Q = ::exp(((double)g.glog[g.Mp + b * K + i] - (double)s_m[K + 1 + i]) * c.invT -
+      const double P = ::exp(((double)s_z[i] - (double)s_m[i]) * c.invT - ::log(s_S[i]));
+      const double Q = ::exp(((double)s_z[K + 1 + i] - (double)s_m[K + 1 + i]) * c.invT -
                              ::log(s_S[K + 1 + i]));
       const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawAccept);
       if (!(u * Q < P)) {
