@@ -35,6 +35,8 @@
 // element i of lane l is C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
 // Tiles are ordered so that the row tiles of one vocabulary tile run one after
 // another on the same XCD and share its L2 copy of the W tile.
+#include <type_traits>
+
 #include "rowops.hpp"
 
 namespace psi {
@@ -191,36 +193,47 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
   lmh_barrier();
   read_frag(ring(0), 0, 0);
   int cur = 0;  // ring slot of step s
-  for (int s = 0; s < steps; ++s) {
+  // One step; REFILL: the loads of step s + 3 are issued (every step but the
+  // last three, which run a copy of the body without them).
+  auto step = [&](int s, auto refill_tag) {
+    constexpr bool kRefill = decltype(refill_tag)::value;
     unsigned char* st = ring(cur);
     const int nxt = cur == kStages - 1 ? 0 : cur + 1;
     // The loads of step s + 3 go to the slot of step s - 1, free since the
     // middle of step s - 1; they are spread over the products of step s, one
     // between each pair (the load unit takes them as fast as they come).
     unsigned char* fill = ring(cur == 0 ? kStages - 1 : cur - 1);
-    const bool refill = s + 3 < steps;
     const int k0 = (s + 3) * kLmhBK;
-    // slice 0 of step s is in fa[0] / fb[0]
-    read_frag(st, 1, 1);
+    // slice 0 of step s is in fa[0] / fb[0]; slice 1 is read after the first
+    // product (so that the wait for slice 0 does not include its reads)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mfma1(0, i);
-      if ((i & 1) && i / 2 < kHalfLoads && refill) lmh_dma16(src[i / 2] + k0, dst(fill, i / 2));
+      if (i == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_frag(st, 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kRefill && (i & 1) && i / 2 < kHalfLoads) lmh_dma16(src[i / 2] + k0, dst(fill, i / 2));
     }
     // step s + 1 is in; the loads of step s + 2 and the first half of step
     // s + 3 may stay in flight
-    wait_loads((s + 2 < steps ? kLoads : 0) + (refill ? kHalfLoads : 0));
+    if (kRefill) wait_vm<kLoads + kHalfLoads>();
+    else wait_loads(s + 2 < steps ? kLoads : 0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of this stage are done
     lmh_barrier();
     if (s + 1 < steps) read_frag(ring(nxt), 0, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mfma1(1, i);
-      if ((i & 1) && i / 2 < kHalfLoads && refill)
+      if (kRefill && (i & 1) && i / 2 < kHalfLoads)
         lmh_dma16(src[kHalfLoads + i / 2] + k0, dst(fill, kHalfLoads + i / 2));
     }
     cur = nxt;
-  }
+  };
+  int s = 0;
+  for (; s + 3 < steps; ++s) step(s, std::true_type{});
+  for (; s < steps; ++s) step(s, std::false_type{});
 
   // epilogue tables at the start of the ring (no longer read: every wave
   // passed the last step's barrier after its last read)
