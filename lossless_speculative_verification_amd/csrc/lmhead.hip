@@ -9,9 +9,9 @@
 // Pipeline on the caller's stream:
 //   k_lmh_gemm<kLmhStats>   every target and draft row against every 512-token
 //                           vocabulary tile: per (row, tile) the maximum and a
-//                           binary32-grade sum of 2^((z - m) c), and the logit
-//                           of the row's drafted token;
-//   k_lmh_decide            per request: row normalisers, accept tests
+//                           binary32-grade sum of 2^((z - m) c);
+//   k_lmh_decide            per request: row normalisers, the drafted tokens'
+//                           logits (dot products), accept tests
 //                           u * Q(x) < P(x), first rejection n; the draw state;
 //   k_lmh_gemm<kLmhLogits>  the final rows only (target row n and draft row n,
 //                           or the bonus row): fp32 logits;
@@ -22,9 +22,9 @@
 // owning 128 tokens of the tile (all 128 rows): 4 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16, 256 accumulator registers, one wave per SIMD.
 // Operand tiles of 32 hidden elements per step go from global memory straight
-// into LDS (16-byte direct loads, no register staging) through a three-stage
-// ring, two steps ahead of the step being multiplied; a step's loads are
-// issued one between each pair of its products. A tile row is 64 bytes in
+// into LDS (16-byte direct loads, no register staging) through a four-stage
+// ring: the loads of step s + 3 are issued during step s, one between each
+// pair of its products, into the slot step s - 1 has left. A tile row is 64 bytes in
 // LDS: its four 16-byte slots are permuted by an XOR of row bits 2..3, so that
 // the 16-byte fragment reads of a wave do not conflict in the LDS banks. The
 // tile epilogue reduces each row over the wave's 128 columns with a butterfly
