@@ -249,7 +249,7 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed, only=None):
         pd, qd = to_dev(p, torch, dev), to_dev(q, torch, dev)
         del p, q
         wts = torch.full((Rt,), 1.0 / Rt, dtype=torch.float32, device=dev)
-        ws = torch.empty(psi.workspace_bytes(Rt, 2, Vt, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(psi.tv_workspace_bytes(Rt, Vt, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
         outs = dict(loss=torch.empty((Rt,), dtype=torch.float64, device=dev),
                     grad=torch.empty((Rt, Vt), dtype=torch.bfloat16, device=dev))
         ms = time_calls(torch, lambda i: psi.tv_loss(pd, qd, temperature=1.0, row_weights=wts, out=outs, workspace=ws,

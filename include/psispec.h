@@ -133,7 +133,7 @@ typedef struct psispec_params {
  *   psispec_verify_tree    rows_per_req = 2*(N + 1)
  *   psispec_tree_candidates rows_per_req = K
  *   psispec_verify_tree_det rows_per_req = N + 1
- *   psispec_tv_loss         B = R, rows_per_req = 2
+ * (psispec_tv_loss has its own: psispec_tv_workspace_bytes.)
  * Returns 0 for arguments out of range. Pure host function.
  */
 size_t psispec_workspace_bytes(int64_t B, int32_t rows_per_req, int32_t V, int dtype);
@@ -299,8 +299,11 @@ int psispec_verify_tree_det(const void* p_logits, int dtype, int64_t B, int32_t 
  * p and q are evaluated in binary32 from binary32-grade normalisers (about
  * 1e-7 relative); the loss is accumulated in fp64. A row with a NaN or +inf
  * logit, or entirely -inf, gets a NaN loss and a NaN gradient row.
- * Workspace: psispec_workspace_bytes(R, 2, V, dtype).
+ * Workspace: psispec_tv_workspace_bytes(R, V, dtype): the statistics and
+ * partial sums of the passes, and two bits per logit for the sign of q - p
+ * (written by the second pass, read by the gradient pass instead of p).
  */
+size_t psispec_tv_workspace_bytes(int64_t R, int32_t V, int dtype);
 int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64_t R, int32_t V, float temperature,
                     const float* row_weights, double* out_loss, void* out_grad, void* workspace, size_t ws_bytes,
                     hipStream_t stream);

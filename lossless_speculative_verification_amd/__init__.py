@@ -62,6 +62,8 @@ def _load():
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.psispec_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
     L.psispec_workspace_bytes.restype = sz
+    L.psispec_tv_workspace_bytes.argtypes = [i64, i32, ctypes.c_int]
+    L.psispec_tv_workspace_bytes.restype = sz
     L.psispec_draft_sample.argtypes = [P, ctypes.c_int, i64, i32, i32, ctypes.POINTER(Params), P, P, sz, P]
     L.psispec_draft_sample.restype = ctypes.c_int
     L.psispec_verify_linear.argtypes = [P, P, ctypes.c_int, i64, i32, i32, P, ctypes.POINTER(Params), P, P, P, P,
@@ -179,6 +181,10 @@ def dtype_code(t: torch.Tensor) -> int:
 
 def workspace_bytes(B: int, rows_per_req: int, V: int, dtype: int) -> int:
     return int(lib.psispec_workspace_bytes(int(B), int(rows_per_req), int(V), int(dtype)))
+
+
+def tv_workspace_bytes(R: int, V: int, dtype: int) -> int:
+    return int(lib.psispec_tv_workspace_bytes(int(R), int(V), int(dtype)))
 
 
 def make_params(temperature=1.0, top_k=0, top_p=1.0, seed=0, step=0, fused=False) -> Params:
@@ -359,7 +365,7 @@ def tv_loss(p: torch.Tensor, q: torch.Tensor, temperature=1.0, row_weights: torc
     if out is None:
         out = dict(loss=torch.empty((R,), dtype=torch.float64, device=dev),
                    grad=torch.empty((R, V), dtype=p.dtype, device=dev) if grad else None)
-    ws = _workspace(workspace, workspace_bytes(R, 2, V, dt), dev)
+    ws = _workspace(workspace, tv_workspace_bytes(R, V, dt), dev)
     rc = lib.psispec_tv_loss(_ptr(p), _ptr(q), dt, R, V, float(temperature), _ptr(row_weights), _ptr(out["loss"]),
                              _ptr(out.get("grad")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("psispec_tv_loss", rc)

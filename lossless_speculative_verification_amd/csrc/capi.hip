@@ -373,6 +373,12 @@ int psispec_verify_tree_det(const void* p_logits, int dtype, int64_t B, int32_t 
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 
+size_t psispec_tv_workspace_bytes(int64_t R, int32_t V, int dtype) {
+  if (R <= 0 || V <= 0 || (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16)) return 0;
+  const int64_t nv = ((int64_t)V + per_vec(dtype) - 1) / per_vec(dtype);
+  return layout(R, 2, V, dtype).total + align_up((size_t)(R * nv) * sizeof(uint16_t), 256);
+}
+
 int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64_t R, int32_t V, float temperature,
                     const float* row_weights, double* out_loss, void* out_grad, void* workspace, size_t ws_bytes,
                     hipStream_t stream) {
@@ -380,15 +386,16 @@ int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64
   if (R <= 0 || V <= 0 || !(temperature > 0.0f) || !isfinite(temperature)) return PSISPEC_EINVAL;
   if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
   if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
-  if (ws_bytes < psispec_workspace_bytes(R, 2, V, dtype)) return PSISPEC_EWORKSPACE;
+  if (ws_bytes < psispec_tv_workspace_bytes(R, V, dtype)) return PSISPEC_EWORKSPACE;
   psispec_params prm = {};
   prm.temperature = temperature;
   prm.top_p = 1.0f;
   LinCfg c;
   fill_common(c, p_logits, q_logits, dtype, R, 1, V, &prm, workspace, 1);
   c.aligned = c.aligned && (out_grad == nullptr || aligned16(out_grad));
+  uint16_t* sgn = (uint16_t*)((char*)workspace + layout(R, 2, V, dtype).total);
   timing_begin(stream);
-  const hipError_t e = launch_tv_loss(c, row_weights, out_loss, out_grad, (double)temperature, dtype, stream);
+  const hipError_t e = launch_tv_loss(c, sgn, row_weights, out_loss, out_grad, (double)temperature, dtype, stream);
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 

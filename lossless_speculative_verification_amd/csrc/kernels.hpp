@@ -269,9 +269,10 @@ hipError_t launch_tree_candidates(const LinCfg& c, const FiltCfg& f, const CandC
 hipError_t launch_verify_tree_det(const LinCfg& c, const DTreeCfg& d, int dtype, hipStream_t s);
 hipError_t launch_stats32(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
 // Total-variation distillation loss (tv.hip): c.rows holds one teacher (p) and
-// one student (q) row per loss row (c.B rows).
-hipError_t launch_tv_loss(const LinCfg& c, const float* w_row, double* loss, void* grad, double T, int dtype,
-                          hipStream_t s);
+// one student (q) row per loss row (c.B rows); sgn: ceil(V / per-vector) 16-bit
+// sign words per row (written by the first pass when a gradient is asked for).
+hipError_t launch_tv_loss(const LinCfg& c, uint16_t* sgn, const float* w_row, double* loss, void* grad, double T,
+                          int dtype, hipStream_t s);
 hipError_t launch_argmax(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
 // Multi-round generation on the toy model (driver.hip).
 struct GenState {

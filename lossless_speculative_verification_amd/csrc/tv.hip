@@ -11,9 +11,12 @@
 // Pipeline on the caller's stream (streaming the rows in chunks that fit the
 // last-level cache between the passes measured slower than whole passes):
 //   k_stats32   maxima and binary32-grade sums of every teacher and student row;
-//   k_tv_pass   (sub-block, row): sum |p - q| and sum g q per 1,024 logits;
+//   k_tv_pass   (sub-block, row): sum |p - q| and sum g q per 1,024 logits,
+//               and (with a gradient) the sign of q - p of every logit, two
+//               bits each, 16 bits per 16-byte vector;
 //   k_tv_grad   (sub-block, row): the row's loss and gbar from those records,
-//               then the gradient, written in the logits' dtype.
+//               then the gradient from q and the stored signs (p is not read
+//               again), written in the logits' dtype.
 // p and q are evaluated as 2^((a - m) c) / S in binary32 from the same
 // statistics in both passes, so the signs g_v of the two passes agree.
 #include "rowops.hpp"
@@ -79,7 +82,6 @@ __device__ __forceinline__ void tv_probs(const TvRow& t, float c32, float a, flo
   Q = __builtin_amdgcn_exp2f(__builtin_fmaf(d, c32, -t.mcq)) * t.iq;
 }
 
-__device__ __forceinline__ float tv_sign(float P, float Q) { return Q > P ? 0.5f : (Q < P ? -0.5f : 0.0f); }
 
 constexpr int kTvSpw = 4;  // sub-blocks per wave (the row normalisers are read once per wave)
 
@@ -87,14 +89,18 @@ constexpr int kTvSpw = 4;  // sub-blocks per wave (the row normalisers are read 
 
 // c.rows: np = 1 teacher row and nq = 1 student row per "request" (= row of
 // the loss); row blockIdx.y.
+// Sign code of q - p: 0 tie, 1 positive (g = +1/2), 2 negative (g = -1/2).
+__device__ __forceinline__ float tv_code_g(uint32_t code) { return code == 1u ? 0.5f : (code == 2u ? -0.5f : 0.0f); }
+
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_tv_pass(LinCfg c) {
+__global__ __launch_bounds__(kWG) void k_tv_pass(LinCfg c, uint16_t* sgn) {
   constexpr int EPV = Elem<DT>::kPerVec;
   constexpr int VPL = kSB / (kWave * EPV);
   const int64_t r = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int sb0 = (blockIdx.x * kWaves + wave) * kTvSpw;
   if (sb0 >= c.nsb) return;
+  const int64_t nv = ((int64_t)c.V + EPV - 1) / EPV;  // sign words per row
   const TvRow t = tv_row(c, r);
   const char* prow = c.rows.p + (r * (int64_t)c.V) * c.rows.esz;
   const char* qrow = c.rows.q + (r * (int64_t)c.V) * c.rows.esz;
@@ -105,14 +111,20 @@ __global__ __launch_bounds__(kWG) void k_tv_pass(LinCfg c) {
     load_vecs<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, vfirst, xd);
     float l1 = 0.0f, gq = 0.0f;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
+    for (int v = 0; v < VPL; ++v) {
+      uint32_t code = 0;
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
         float P, Q;
         tv_probs(t, c.c32, xa[v][e], xd[v][e], P, Q);
         l1 += fabsf(P - Q);
-        gq = __builtin_fmaf(tv_sign(P, Q), Q, gq);
+        const bool gt = Q > P, lt = Q < P;  // the sign and its code share the compares
+        gq = __builtin_fmaf(gt ? 0.5f : (lt ? -0.5f : 0.0f), Q, gq);
+        code |= ((gt ? 1u : 0u) | (lt ? 2u : 0u)) << (2 * e);
       }
+      const int64_t vec = vfirst + (int64_t)v * kWave;
+      if (sgn != nullptr && vec < nv) sgn[r * nv + vec] = (uint16_t)code;
+    }
     const double L1 = wave_sum((double)l1), GQ = wave_sum((double)gq);
     if (lane == 0) c.res[r * c.nsb + sb] = ResRec{L1, GQ, 0.0, 0.0};
   }
@@ -157,16 +169,19 @@ __device__ __forceinline__ uint4 pack_grad<kBF16>(const float (&x)[8]) {
 }
 
 // The row's loss and gbar from its sub-block records (every wave of the row
-// computes them), then the gradient of one sub-block per wave. With grad ==
-// nullptr only the loss is written (grid x = 1).
+// computes them), then the gradient of one sub-block per wave from q and the
+// sign codes of the first pass. With grad == nullptr only the loss is written
+// (grid x = 1).
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const float* w_row, double* loss, void* grad, double T) {
+__global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const uint16_t* sgn, const float* w_row, double* loss,
+                                                 void* grad, double T) {
   constexpr int EPV = Elem<DT>::kPerVec;
   constexpr int VPL = kSB / (kWave * EPV);
   const int64_t r = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int sb0 = (blockIdx.x * kWaves + wave) * kTvSpw;
   if (sb0 >= c.nsb) return;
+  const int64_t nv = ((int64_t)c.V + EPV - 1) / EPV;
   const TvRow t = tv_row(c, r);
   double L1 = 0.0, GQ = 0.0;
   for (int i = lane; i < c.nsb; i += kWave) {
@@ -180,21 +195,24 @@ __global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const float* w_row, d
   if (grad == nullptr) return;
   const float gbar = (float)GQ;
   const float scale = t.ok ? (float)((w_row ? (double)w_row[r] : 1.0) / T) : NAN;
-  const char* prow = c.rows.p + (r * (int64_t)c.V) * c.rows.esz;
   const char* qrow = c.rows.q + (r * (int64_t)c.V) * c.rows.esz;
   for (int sb = sb0; sb < sb0 + kTvSpw && sb < c.nsb; ++sb) {
     const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
-    float xa[VPL][EPV], xd[VPL][EPV];
-    load_vecs<DT, AL, VPL, kWave>(prow, c.V, c.nvec, vfirst, xa);
+    float xd[VPL][EPV];
+    uint32_t codes[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int64_t vec = vfirst + (int64_t)v * kWave;
+      codes[v] = vec < nv ? (uint32_t)sgn[r * nv + vec] : 0u;
+    }
     load_vecs<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, vfirst, xd);
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       float gout[EPV];
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
-        float P, Q;
-        tv_probs(t, c.c32, xa[v][e], xd[v][e], P, Q);
-        gout[e] = scale * Q * (tv_sign(P, Q) - gbar);
+        const float Q = __builtin_amdgcn_exp2f(__builtin_fmaf(xd[v][e], c.c32, -t.mcq)) * t.iq;
+        gout[e] = scale * Q * (tv_code_g((codes[v] >> (2 * e)) & 3u) - gbar);
       }
       const int64_t vec = vfirst + (int64_t)v * kWave;
       if constexpr (AL) {
@@ -211,18 +229,20 @@ __global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const float* w_row, d
 }
 
 template <int DT, bool AL>
-static hipError_t tv_t(const LinCfg& c, const float* w_row, double* loss, void* grad, double T, hipStream_t s) {
+static hipError_t tv_t(const LinCfg& c, uint16_t* sgn, const float* w_row, double* loss, void* grad, double T,
+                       hipStream_t s) {
   const unsigned gx = (unsigned)((c.nsb + kWaves * kTvSpw - 1) / (kWaves * kTvSpw));
   hipError_t e = launch_stats32(c, 2 * c.B, DT, s);
   if (e != hipSuccess) return e;
-  PSI_LAUNCH(s, (k_tv_pass<DT, AL>), dim3(gx, (unsigned)c.B), dim3(kWG), c);
-  PSI_LAUNCH(s, (k_tv_grad<DT, AL>), dim3(grad ? gx : 1u, (unsigned)c.B), dim3(kWG), c, w_row, loss, grad, T);
+  PSI_LAUNCH(s, (k_tv_pass<DT, AL>), dim3(gx, (unsigned)c.B), dim3(kWG), c, grad ? sgn : nullptr);
+  PSI_LAUNCH(s, (k_tv_grad<DT, AL>), dim3(grad ? gx : 1u, (unsigned)c.B), dim3(kWG), c, (const uint16_t*)sgn, w_row,
+             loss, grad, T);
   return hipGetLastError();
 }
 
-hipError_t launch_tv_loss(const LinCfg& c, const float* w_row, double* loss, void* grad, double T, int dtype,
-                          hipStream_t s) {
-  return PSI_DISPATCH(tv_t, dtype, c.aligned, c, w_row, loss, grad, T, s);
+hipError_t launch_tv_loss(const LinCfg& c, uint16_t* sgn, const float* w_row, double* loss, void* grad, double T,
+                          int dtype, hipStream_t s) {
+  return PSI_DISPATCH(tv_t, dtype, c.aligned, c, sgn, w_row, loss, grad, T, s);
 }
 
 }  // namespace psi

@@ -188,6 +188,12 @@ def test_tv_loss_argument_errors(psi):
     assert call(dtype=2) == psi.EUNSUPPORTED
     assert call(ws_bytes=8) == psi.EWORKSPACE
     assert call(ws_addr=(1 << 20) + 16) == psi.EINVAL
+    # the generic workspace lacks the sign words of the gradient pass
+    for R, V, dtype in ((4, 100, 1), (2048, 151936, 1), (3, 3001, 0)):
+        need = psi.tv_workspace_bytes(R, V, dtype)
+        assert need >= psi.workspace_bytes(R, 2, V, dtype) + R * -(-V // (8 if dtype == 1 else 4)) * 2
+        assert call(R=R, V=V, dtype=dtype, ws_bytes=need - 1) == psi.EWORKSPACE
+    assert psi.tv_workspace_bytes(0, 100, 1) == 0 and psi.tv_workspace_bytes(4, 100, 2) == 0
 
 
 def test_generate_argument_errors(psi):
