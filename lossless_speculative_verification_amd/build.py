@@ -6,7 +6,10 @@ instruction selection is disabled for every source.
 
 It also writes kernel_code.json beside the library: a hash of the gfx950
 assembly of each k_stats32 instance, so that measurements taken on that
-kernel (its HBM byte counters) can be matched to the code that runs.
+kernel (its HBM byte counters) can be matched to the code that runs. And it
+checks the assembly of lmhead.hip: its direct global-to-LDS loads set M0 in
+asm statements, which is only safe while the compiler itself leaves M0 alone
+in that file (M0 cannot be declared clobbered).
 """
 from __future__ import annotations
 
@@ -63,6 +66,7 @@ def build(verbose: bool = False) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     write_code_hashes()
+    check_m0()
     return LIB
 
 
@@ -96,6 +100,33 @@ def write_code_hashes() -> None:
         hashes = function_hashes(f.read(), r"k_stats32")
     with open(CODE_JSON, "w") as f:
         json.dump(hashes, f, indent=1, sort_keys=True)
+
+
+def m0_violations(asm: str) -> list:
+    """Instructions that touch M0 other than the direct-load sequence
+    `s_mov_b32 m0, sN` / `s_nop 0` / `global_load_lds_dwordx4`."""
+    lines = [l.split(";", 1)[0].strip() for l in asm.splitlines()]
+    lines = [l for l in lines if l and not l.startswith((".", "_")) and not l.endswith(":")]
+    bad = []
+    for i, l in enumerate(lines):
+        if not re.search(r"\bm0\b", l):
+            continue
+        ok = (re.match(r"^s_mov_b32\s+m0,\s*s\d+$", l) and i + 2 < len(lines) and lines[i + 1] == "s_nop 0"
+              and lines[i + 2].startswith("global_load_lds_dwordx4"))
+        if not ok:
+            bad.append(l)
+    return bad
+
+
+def check_m0() -> None:
+    asm = os.path.join(BUILD, "lmhead.s")
+    cmd = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], "--cuda-device-only", "-S",
+           os.path.join(CSRC, "lmhead.hip"), "-o", asm]
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    with open(asm) as f:
+        bad = m0_violations(f.read())
+    if bad:
+        raise RuntimeError("lmhead.hip: M0 used outside the direct-load sequence: " + "; ".join(bad[:5]))
 
 
 if __name__ == "__main__":
