@@ -107,8 +107,8 @@ __device__ __forceinline__ void lmh_barrier() {
 
 template <int MODE>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k_lmh_gemm(LmhCfg g) {
-  // ring of operand tiles; after the main loop the start of it
-  // holds the epilogue's row tables
+  // ring of operand tiles; after the main loop its start holds the
+  // epilogue's per-wave row maxima and sums
   __shared__ __attribute__((aligned(1024))) unsigned char s_mem[kStages * kStage];
   const int t = threadIdx.x, lane = t & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
@@ -173,7 +173,6 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
                                                                  0, 0, 0);
   };
 
-
   const int steps = g.H / kLmhBK;
   auto ring = [&](int i) { return s_mem + i * kStage; };
   // Waits until at most n direct loads of this wave are outstanding.
@@ -183,7 +182,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     else if (n >= kHalfLoads) wait_vm<kHalfLoads>();
     else wait_vm<0>();
   };
-  // prologue: steps 0 .. 2 in flight, wait for step 0
+  // prologue: steps 0 .. kStages - 2 in flight, wait for step 0
 #pragma unroll
   for (int p = 0; p < kStages - 1; ++p)
     if (p < steps)
