@@ -168,9 +168,13 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
 #pragma unroll
     for (int i = 0; i < 4; ++i) fb[slot][i] = *(const bf16x8_t*)(st + bw + i * 32 * kRowB + fo);
   };
+  // row blocks of 32 that hold rows of the product (a last row tile may be
+  // partial: its empty blocks are not multiplied)
+  const int mblocks = (int)((g.M - m0 + 31) / 32 < 4 ? (g.M - m0 + 31) / 32 : 4);
   auto mfma1 = [&](int slot, int i) {
-    acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i >> 2], fb[slot][i & 3], acc[i >> 2][i & 3],
-                                                                 0, 0, 0);
+    if ((i >> 2) < mblocks)
+      acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i >> 2], fb[slot][i & 3],
+                                                                   acc[i >> 2][i & 3], 0, 0, 0);
   };
 
   const int steps = g.H / kLmhBK;
