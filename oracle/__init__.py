@@ -49,31 +49,31 @@ def lib():
         L.orc_uniform.restype = f64
         L.orc_decode_row.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, P]
         L.orc_decode_row.restype = ctypes.c_int
-        L.orc_filter_row.argtypes = [P, ctypes.c_int, f64, ctypes.c_int, f64]
+        L.orc_filter_row.argtypes = [P, ctypes.c_int, f64, ctypes.c_int, f64, P]
         L.orc_filter_row.restype = None
         L.orc_logsumexp.argtypes = [P, ctypes.c_int]
         L.orc_logsumexp.restype = f64
-        L.orc_sample.argtypes = [P, ctypes.c_int, f64, P]
+        L.orc_sample.argtypes = [P, ctypes.c_int, f64, P, P]
         L.orc_sample.restype = ctypes.c_int
         L.orc_tree_depth.argtypes = [P, ctypes.c_int]
         L.orc_tree_depth.restype = ctypes.c_int
         L.orc_draft_sample.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, f64, ctypes.c_int, f64,
-                                       u64, u32, P, P, P, ctypes.c_int]
+                                       u64, u32, P, P, P, P, P, ctypes.c_int]
         L.orc_draft_sample.restype = ctypes.c_int
         L.orc_verify_linear.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, f64, ctypes.c_int,
-                                        f64, u64, u32, ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int]
+                                        f64, u64, u32, ctypes.c_int, P, P, P, P, P, P, ctypes.c_int]
         L.orc_verify_linear.restype = ctypes.c_int
         L.orc_verify_tree.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, P, f64, ctypes.c_int,
-                                      f64, u64, u32, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int]
+                                      f64, u64, u32, P, P, P, P, P, ctypes.c_int, ctypes.c_int]
         L.orc_verify_tree.restype = ctypes.c_int
         L.orc_tree_draft.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, f64, ctypes.c_int, f64, u64,
-                                     u32, P, ctypes.c_int]
+                                     u32, P, P, P, P, ctypes.c_int]
         L.orc_tree_draft.restype = ctypes.c_int
         L.orc_tree_candidates.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, f64, ctypes.c_int,
                                           ctypes.c_int, P, P, P, ctypes.c_int]
         L.orc_tree_candidates.restype = ctypes.c_int
         L.orc_verify_tree_det.argtypes = [P, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, P, P, f64, u64, u32,
-                                          P, P, P, P, P, P, ctypes.c_int, ctypes.c_int]
+                                          P, P, P, P, P, ctypes.c_int, ctypes.c_int]
         L.orc_verify_tree_det.restype = ctypes.c_int
         L.orc_tv_loss.argtypes = [P, P, ctypes.c_int, i64, ctypes.c_int, f64, P, P, P, ctypes.c_int]
         L.orc_tv_loss.restype = ctypes.c_int
@@ -84,6 +84,18 @@ def lib():
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class _LinMargins(ctypes.Structure):
+    # orc_lin_margins: acc, draft, fin, filter (double*), draft_alt, fin_alt (int32_t*)
+    _fields_ = [("acc", ctypes.c_void_p), ("draft", ctypes.c_void_p), ("fin", ctypes.c_void_p),
+                ("filter", ctypes.c_void_p), ("draft_alt", ctypes.c_void_p), ("fin_alt", ctypes.c_void_p)]
+
+
+class _TreeMargins(ctypes.Structure):
+    # orc_tree_margins: acc, fin, filter (double*), fin_alt (int32_t*)
+    _fields_ = [("acc", ctypes.c_void_p), ("fin", ctypes.c_void_p), ("filter", ctypes.c_void_p),
+                ("fin_alt", ctypes.c_void_p)]
 
 
 def _dtype_code(a: np.ndarray) -> int:
@@ -112,18 +124,23 @@ def logsumexp(z) -> float:
 
 
 def sample(w, u):
-    """Inverse-CDF draw; returns (index, margin)."""
+    """Inverse-CDF draw; returns (index, margin, alt): margin is the distance
+    of u*W to the nearer edge of the chosen interval over W, alt the token
+    across that edge (-1 if none)."""
     w = np.ascontiguousarray(w, dtype=np.float64)
     m = ctypes.c_double(0.0)
-    j = lib().orc_sample(_ptr(w), w.size, float(u), ctypes.byref(m))
-    return j, m.value
+    a = ctypes.c_int(0)
+    j = lib().orc_sample(_ptr(w), w.size, float(u), ctypes.byref(m), ctypes.byref(a))
+    return j, m.value, a.value
 
 
-def filter_row(a, temperature, top_k=0, top_p=1.0):
-    """Temperature, top-k, top-p on one row of logits; returns z (removed -> -inf)."""
+def filter_row(a, temperature, top_k=0, top_p=1.0, with_margin=False):
+    """Temperature, top-k, top-p on one row of logits; returns z (removed ->
+    -inf), and with_margin=True also the top-p cut's margin (+inf if none)."""
     z = np.array(a, dtype=np.float64, copy=True)
-    lib().orc_filter_row(_ptr(z), z.size, float(temperature), int(top_k), float(top_p))
-    return z
+    m = ctypes.c_double(0.0)
+    lib().orc_filter_row(_ptr(z), z.size, float(temperature), int(top_k), float(top_p), ctypes.byref(m))
+    return (z, m.value) if with_margin else z
 
 
 def decode_row(logits, row):
@@ -141,17 +158,23 @@ def tree_depth(parent) -> int:
 
 
 def draft_sample(q, temperature, top_k=0, top_p=1.0, seed=0, step=0, u_override=None, nthreads=1):
-    """q: [B, K, V] float32 or uint16 (bf16 bits). Returns (tokens [B,K], margins [B,K])."""
+    """q: [B, K, V] float32 or uint16 (bf16 bits). Returns (tokens [B,K], m)
+    where m holds per-draft arrays [B,K]: "cdf" the draw's margin, "alt" the
+    token across its nearer edge, "filter" its row's top-p cut margin (+inf
+    where there is no such decision)."""
     q = np.ascontiguousarray(q)
     B, K, V = q.shape
     out = np.zeros((B, K), dtype=np.int32)
     mg = np.zeros((B, K), dtype=np.float64)
+    alt = np.zeros((B, K), dtype=np.int32)
+    mf = np.zeros((B, K), dtype=np.float64)
     ovr = None if u_override is None else np.ascontiguousarray(u_override, dtype=np.float64).reshape(B, K)
     rc = lib().orc_draft_sample(_ptr(q), _dtype_code(q), B, K, V, float(temperature), int(top_k), float(top_p),
-                                int(seed), int(step), _ptr(out), _ptr(mg), _ptr(ovr), int(nthreads))
+                                int(seed), int(step), _ptr(out), _ptr(mg), _ptr(alt), _ptr(mf), _ptr(ovr),
+                                int(nthreads))
     if rc != 0:
         raise ValueError("orc_draft_sample rejected its arguments")
-    return out, mg
+    return out, dict(cdf=mg, alt=alt, filter=mf)
 
 
 def verify_linear(p, q, draft_tokens, temperature, top_k=0, top_p=1.0, seed=0, step=0, fused=False,
@@ -160,7 +183,11 @@ def verify_linear(p, q, draft_tokens, temperature, top_k=0, top_p=1.0, seed=0, s
 
     u_override: optional [B, K+1, 3] uniforms (slot 0 final draw, 1 accept test,
     2 draft draw at each row) replacing the Philox stream.
-    Returns a dict with tokens, len, probs, resid, margin_acc, margin_cdf, draft.
+    Returns a dict with tokens, len, probs, resid, draft and the margins of
+    every decision: m_acc [B,K] (accept tests; +inf where none was taken),
+    m_draft / alt_draft [B,K] (drafts drawn in the call), m_final / alt_final
+    [B] (final draw) and m_filter [B] (smallest top-p cut margin of the
+    request's rows).
     """
     p = np.ascontiguousarray(p)
     q = np.ascontiguousarray(q)
@@ -173,30 +200,48 @@ def verify_linear(p, q, draft_tokens, temperature, top_k=0, top_p=1.0, seed=0, s
     ln = np.zeros(B, dtype=np.int32)
     probs = np.zeros((B, K, 2), dtype=np.float64)
     resid = np.zeros(B, dtype=np.float64)
-    ma = np.zeros(B, dtype=np.float64)
-    mc = np.zeros(B, dtype=np.float64)
+    r = dict(m_acc=np.zeros((B, K)), m_draft=np.zeros((B, K)), alt_draft=np.zeros((B, K), dtype=np.int32),
+             m_final=np.zeros(B), alt_final=np.zeros(B, dtype=np.int32), m_filter=np.zeros(B))
+    mg = _LinMargins(_ptr(r["m_acc"]).value, _ptr(r["m_draft"]).value, _ptr(r["m_final"]).value,
+                     _ptr(r["m_filter"]).value, _ptr(r["alt_draft"]).value, _ptr(r["alt_final"]).value)
     ovr = None if u_override is None else np.ascontiguousarray(u_override, dtype=np.float64).reshape(B, K + 1, 3)
     rc = lib().orc_verify_linear(_ptr(p), _ptr(q), _dtype_code(p), B, K, V, _ptr(draft), float(temperature),
                                  int(top_k), float(top_p), int(seed), int(step), int(bool(fused)), _ptr(toks),
-                                 _ptr(ln), _ptr(probs), _ptr(resid), _ptr(ma), _ptr(mc), _ptr(ovr), int(nthreads))
+                                 _ptr(ln), _ptr(probs), _ptr(resid), ctypes.byref(mg), _ptr(ovr), int(nthreads))
     if rc != 0:
         raise ValueError("orc_verify_linear rejected its arguments")
-    return dict(tokens=toks, len=ln, probs=probs, resid=resid, margin_acc=ma, margin_cdf=mc, draft=draft)
+    r.update(tokens=toks, len=ln, probs=probs, resid=resid, draft=draft)
+    return r
 
 
-def tree_draft(q, parent, temperature, top_k=0, top_p=1.0, seed=0, step=0, nthreads=1):
+def tree_draft(q, parent, temperature, top_k=0, top_p=1.0, seed=0, step=0, nthreads=1, margins=False):
     """Node tokens [B, N] of a candidate tree: the j-th child of row r drawn from
-    row r of q [B, N+1, V] with draw id 0x40000000 + j (argmax when greedy)."""
+    row r of q [B, N+1, V] with draw id 0x40000000 + j (argmax when greedy).
+    margins=True also returns a dict of per-node arrays [B, N]: "cdf" the
+    draw's margin, "alt" the token across its nearer edge, "filter" the top-p
+    cut margin of its row."""
     q = np.ascontiguousarray(q)
     B, R, V = q.shape
     N = R - 1
     par = np.ascontiguousarray(parent, dtype=np.int32)
     out = np.zeros((B, N), dtype=np.int32)
+    mg = np.zeros((B, N))
+    alt = np.zeros((B, N), dtype=np.int32)
+    mf = np.zeros((B, N))
     rc = lib().orc_tree_draft(_ptr(q), _dtype_code(q), B, N, V, _ptr(par), float(temperature), int(top_k),
-                              float(top_p), int(seed), int(step), _ptr(out), int(nthreads))
+                              float(top_p), int(seed), int(step), _ptr(out), _ptr(mg), _ptr(alt), _ptr(mf),
+                              int(nthreads))
     if rc != 0:
         raise ValueError("orc_tree_draft rejected its arguments")
-    return out
+    return (out, dict(cdf=mg, alt=alt, filter=mf)) if margins else out
+
+
+def _tree_margin_arrays(B, N):
+    r = dict(m_acc=np.zeros((B, N)), m_final=np.zeros(B), alt_final=np.zeros(B, dtype=np.int32),
+             m_filter=np.zeros(B))
+    mg = _TreeMargins(_ptr(r["m_acc"]).value, _ptr(r["m_final"]).value, _ptr(r["m_filter"]).value,
+                      _ptr(r["alt_final"]).value)
+    return r, mg
 
 
 def verify_tree(p, q, parent, node_tokens, temperature, top_k=0, top_p=1.0, seed=0, step=0, u_override=None,
@@ -204,7 +249,9 @@ def verify_tree(p, q, parent, node_tokens, temperature, top_k=0, top_p=1.0, seed
     """p, q: [B, N+1, V]; parent [N]; node_tokens [B, N].
 
     u_override: optional [B, N+1, 1+max_children] (slot 0 final draw, slot 1+j
-    accept test of child j). Returns a dict with tokens, path, len, margin_acc, margin_cdf.
+    accept test of child j). Returns a dict with tokens, path, len and the
+    margins: m_acc [B,N] (the accept test of each node, +inf if never tested),
+    m_final / alt_final [B] (final draw), m_filter [B] (top-p cuts).
     """
     p = np.ascontiguousarray(p)
     q = np.ascontiguousarray(q)
@@ -218,8 +265,7 @@ def verify_tree(p, q, parent, node_tokens, temperature, top_k=0, top_p=1.0, seed
     toks = np.zeros((B, D + 1), dtype=np.int32)
     path = np.zeros((B, D), dtype=np.int32)
     ln = np.zeros(B, dtype=np.int32)
-    ma = np.zeros(B, dtype=np.float64)
-    mc = np.zeros(B, dtype=np.float64)
+    r, mg = _tree_margin_arrays(B, N)
     maxC = 0
     ovr = None
     if u_override is not None:
@@ -227,23 +273,25 @@ def verify_tree(p, q, parent, node_tokens, temperature, top_k=0, top_p=1.0, seed
         ovr = np.ascontiguousarray(u_override, dtype=np.float64).reshape(B, R, 1 + maxC)
     rc = lib().orc_verify_tree(_ptr(p), _ptr(q), _dtype_code(p), B, N, V, _ptr(par), _ptr(nt), float(temperature),
                                int(top_k), float(top_p), int(seed), int(step), _ptr(toks), _ptr(path), _ptr(ln),
-                               _ptr(ma), _ptr(mc), _ptr(ovr), maxC, int(nthreads))
+                               ctypes.byref(mg), _ptr(ovr), maxC, int(nthreads))
     if rc != 0:
         raise ValueError("orc_verify_tree rejected its arguments")
-    return dict(tokens=toks, path=path, len=ln, margin_acc=ma, margin_cdf=mc)
+    r.update(tokens=toks, path=path, len=ln)
+    return r
 
 
 def tree_candidates(q, cands, nodes, temperature, nthreads=1):
     """Tree Sampler candidates from draft logits q [B, K, V]: per request the
     `nodes` best prefixes over the top-`cands` tokens of each position.
 
-    Returns (parent [B, nodes], tokens [B, nodes], margin [B]); margin is the
-    smallest log-score gap of any choice made (see oracle.c)."""
+    Returns (parent [B, nodes], tokens [B, nodes], gap [B, nodes]); gap[b, n]
+    is the smallest log-score gap between the offer kept as node n and any
+    other offer of that step (+inf when there was no other offer)."""
     q = np.ascontiguousarray(q)
     B, K, V = q.shape
     par = np.zeros((B, nodes), dtype=np.int32)
     tok = np.zeros((B, nodes), dtype=np.int32)
-    mg = np.zeros(B, dtype=np.float64)
+    mg = np.zeros((B, nodes), dtype=np.float64)
     rc = lib().orc_tree_candidates(_ptr(q), _dtype_code(q), B, K, V, float(temperature), int(cands), int(nodes),
                                    _ptr(par), _ptr(tok), _ptr(mg), int(nthreads))
     if rc != 0:
@@ -257,7 +305,8 @@ def verify_tree_det(p, parent, node_tokens, temperature, seed=0, step=0, u_overr
     parent [B, N] and node_tokens [B, N]. u_override: optional
     [B, N+1, 1+max_children] uniforms (slot 0 final draw, slot 1+j accept test
     of child j) replacing the Philox stream. Returns a dict with tokens
-    [B, N+1], path [B, N], len [B], margin_acc, margin_cdf."""
+    [B, N+1], path [B, N], len [B] and the margins m_acc [B, N], m_final /
+    alt_final [B] (m_filter is +inf: no filters)."""
     p = np.ascontiguousarray(p)
     B, R, V = p.shape
     N = R - 1
@@ -266,18 +315,18 @@ def verify_tree_det(p, parent, node_tokens, temperature, seed=0, step=0, u_overr
     toks = np.zeros((B, N + 1), dtype=np.int32)
     path = np.zeros((B, N), dtype=np.int32)
     ln = np.zeros(B, dtype=np.int32)
-    ma = np.zeros(B, dtype=np.float64)
-    mc = np.zeros(B, dtype=np.float64)
+    r, mg = _tree_margin_arrays(B, N)
     ovr, maxC = None, 0
     if u_override is not None:
         maxC = int(max_children)
         ovr = np.ascontiguousarray(u_override, dtype=np.float64).reshape(B, N + 1, 1 + maxC)
     rc = lib().orc_verify_tree_det(_ptr(p), _dtype_code(p), B, N, V, _ptr(par), _ptr(nt), float(temperature),
-                                   int(seed), int(step), _ptr(toks), _ptr(path), _ptr(ln), _ptr(ma), _ptr(mc),
+                                   int(seed), int(step), _ptr(toks), _ptr(path), _ptr(ln), ctypes.byref(mg),
                                    _ptr(ovr), maxC, int(nthreads))
     if rc != 0:
         raise ValueError("orc_verify_tree_det rejected its arguments")
-    return dict(tokens=toks, path=path, len=ln, margin_acc=ma, margin_cdf=mc)
+    r.update(tokens=toks, path=path, len=ln)
+    return r
 
 
 def tv_loss(p, q, temperature=1.0, row_weights=None, grad=True, nthreads=1):
@@ -317,9 +366,11 @@ def generate(model, prompt, block, V, temperature, seed, rounds, nthreads=1):
     Random numbers: the first token of round r is drawn as draft 0 of a
     one-row draft call with step 2r; the drafts and the verification use
     step 2r + 1. Returns dict(seq [B, rounds * (block + 1)] (-1 padded),
-    len [B], round_tokens [B, rounds], margin_acc [B, rounds] (the smallest
-    |u - min(1, p/q)| of the round's accept tests) and margin_cdf [B, rounds]
-    (the smallest inverse-CDF margin of the round's draws))."""
+    len [B], round_tokens [B, rounds], n [B, rounds] (accepted drafts) and the
+    margins of every decision of every round: m_first / alt_first [B, rounds]
+    (the first token's draw), m_draft / alt_draft [B, rounds, block - 1] (the
+    drafts), m_acc [B, rounds, block - 1] (accept tests, +inf where none was
+    taken) and m_final / alt_final [B, rounds] (the final draw))."""
     prompt = np.ascontiguousarray(prompt, dtype=np.int32).reshape(-1, 2)
     B = prompt.shape[0]
     K = block - 1
@@ -327,8 +378,11 @@ def generate(model, prompt, block, V, temperature, seed, rounds, nthreads=1):
     seq = np.full((B, L), -1, dtype=np.int32)
     ln = np.zeros(B, dtype=np.int32)
     rt = np.zeros((B, rounds), dtype=np.int32)
-    ma = np.ones((B, rounds), dtype=np.float64)
-    mc = np.ones((B, rounds), dtype=np.float64)
+    nacc = np.zeros((B, rounds), dtype=np.int32)
+    mf, af = np.zeros((B, rounds)), np.zeros((B, rounds), dtype=np.int32)
+    md_, ad_ = np.zeros((B, rounds, K)), np.zeros((B, rounds, K), dtype=np.int32)
+    ma = np.zeros((B, rounds, K))
+    mfin, afin = np.zeros((B, rounds)), np.zeros((B, rounds), dtype=np.int32)
     t1, t2 = prompt[:, 0].copy(), prompt[:, 1].copy()
     for r in range(rounds):
         # first position: the target model itself
@@ -345,16 +399,19 @@ def generate(model, prompt, block, V, temperature, seed, rounds, nthreads=1):
         cp = np.stack([hist[:, :K + 1], hist[:, 1:K + 2]], axis=2).reshape(-1, 2)
         p = model(0, cp, None).reshape(B, K + 1, V)
         v = verify_linear(p, q, d, temperature, seed=seed, step=2 * r + 1, nthreads=nthreads)
+        mf[:, r], af[:, r] = m0["cdf"][:, 0], m0["alt"][:, 0]
+        md_[:, r], ad_[:, r] = md["cdf"], md["alt"]
+        ma[:, r], mfin[:, r], afin[:, r] = v["m_acc"], v["m_final"], v["alt_final"]
         for b in range(B):
             n = int(v["len"][b])
             toks = [int(x0[b])] + [int(t) for t in v["tokens"][b, :n + 1]]
             seq[b, ln[b]:ln[b] + len(toks)] = toks
             ln[b] += len(toks)
             rt[b, r] = len(toks)
-            ma[b, r] = float(v["margin_acc"][b])
-            mc[b, r] = min(float(m0[b, 0]), float(md[b].min()), float(v["margin_cdf"][b]))
+            nacc[b, r] = n
             t1[b], t2[b] = seq[b, ln[b] - 2], seq[b, ln[b] - 1]
-    return dict(seq=seq, len=ln, round_tokens=rt, margin_acc=ma, margin_cdf=mc)
+    return dict(seq=seq, len=ln, round_tokens=rt, n=nacc, m_first=mf, alt_first=af, m_draft=md_, alt_draft=ad_,
+                m_acc=ma, m_final=mfin, alt_final=afin)
 
 
 def lmhead_logits(h, w, chunk=16384):

@@ -152,8 +152,13 @@ static void filter_top_k(double* z, int V, int top_k, keyed* buf) {
 
 /* Top-p over the surviving tokens: softmax over them (sum in id order), sort
  * by probability (desc, ties lower id), keep the shortest prefix whose running
- * sum reaches top_p (at least one token). top_p >= 1 disables it. */
-static void filter_top_p(double* z, int V, double top_p, keyed* buf) {
+ * sum reaches top_p (at least one token). top_p >= 1 disables it.
+ * *margin (may be NULL) = how far the cut decision is from going the other
+ * way: the distance of top_p to the running sum on either side of the cut,
+ * min(cum_t - top_p, top_p - cum_{t-1}) with cum_{-1} = 0 (probabilities sum
+ * to 1, so this is a fraction of the kept mass); +inf when nothing is cut. */
+static void filter_top_p(double* z, int V, double top_p, keyed* buf, double* margin) {
+  if (margin) *margin = INFINITY;
   if (!(top_p < 1.0)) return;
   double m = -INFINITY;
   for (int j = 0; j < V; ++j)
@@ -170,31 +175,33 @@ static void filter_top_p(double* z, int V, double top_p, keyed* buf) {
     ++n;
   }
   qsort(buf, (size_t)n, sizeof(keyed), cmp_desc_then_idx);
-  double cum = 0.0;
+  double cum = 0.0, prev = 0.0;
   int keep = n;
   for (int t = 0; t < n; ++t) {
+    prev = cum;
     cum += buf[t].key;
     if (cum >= top_p) {
       keep = t + 1;
       break;
     }
   }
+  if (margin) *margin = fmin(fabs(cum - top_p), top_p - prev);
   for (int t = keep; t < n; ++t) z[buf[t].idx] = -INFINITY;
 }
 
-/* Temperature then filters, in place: z = a / T, top-k, top-p. */
-void orc_filter_row(double* z, int V, double temperature, int top_k, double top_p) {
+/* Temperature then filters, in place: z = a / T, top-k, top-p. *margin (may
+ * be NULL): the top-p cut's margin (+inf without a top-p cut). */
+static void filter_row_buf(double* z, int V, double temperature, int top_k, double top_p, keyed* buf,
+                           double* margin) {
   for (int j = 0; j < V; ++j) z[j] = z[j] / temperature;
-  keyed* buf = (keyed*)malloc(sizeof(keyed) * (size_t)V);
   filter_top_k(z, V, top_k, buf);
-  filter_top_p(z, V, top_p, buf);
-  free(buf);
+  filter_top_p(z, V, top_p, buf, margin);
 }
 
-static void filter_row_buf(double* z, int V, double temperature, int top_k, double top_p, keyed* buf) {
-  for (int j = 0; j < V; ++j) z[j] = z[j] / temperature;
-  filter_top_k(z, V, top_k, buf);
-  filter_top_p(z, V, top_p, buf);
+void orc_filter_row(double* z, int V, double temperature, int top_k, double top_p, double* margin) {
+  keyed* buf = (keyed*)malloc(sizeof(keyed) * (size_t)V);
+  filter_row_buf(z, V, temperature, top_k, top_p, buf, margin);
+  free(buf);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -212,27 +219,46 @@ double orc_logsumexp(const double* z, int V) {
 
 /* Inverse-CDF draw with one uniform u in [0, 1): W = sum w (id order), return
  * the smallest j with C_j = w_0 + ... + w_j > u * W; if rounding leaves none,
- * the largest j with w_j > 0. *margin = distance of u*W to the nearer edge of
- * the chosen interval, divided by W. Returns -1 when W is not positive. */
-int orc_sample(const double* w, int V, double u, double* margin) {
+ * the largest j with w_j > 0. Returns -1 when W is not positive.
+ * *margin (may be NULL) = distance of u*W to the nearer edge of the chosen
+ * interval [C_{j-1}, C_j), divided by W; *alt (may be NULL) = the token a draw
+ * lands on when that edge moves past u*W: below a lower edge the previous
+ * index with positive weight, beyond an upper edge the next one (-1 if there
+ * is none). The rounding fallback gives margin 0 and alt = j. */
+int orc_sample(const double* w, int V, double u, double* margin, int* alt) {
   double W = 0.0;
   for (int j = 0; j < V; ++j) W += w[j];
-  if (!(W > 0.0)) {
-    if (margin) *margin = 0.0;
-    return -1;
-  }
+  if (margin) *margin = 0.0;
+  if (alt) *alt = -1;
+  if (!(W > 0.0)) return -1;
   double t = u * W, c = 0.0;
   for (int j = 0; j < V; ++j) {
     double prev = c;
     c += w[j];
     if (c > t) {
-      if (margin) *margin = fmin(t - prev, c - t) / W;
+      const double lo = t - prev, hi = c - t;
+      if (margin) *margin = fmin(lo, hi) / W;
+      if (alt) {
+        if (lo <= hi) {
+          for (int k = j - 1; k >= 0; --k)
+            if (w[k] > 0.0) {
+              *alt = k;
+              break;
+            }
+        } else {
+          for (int k = j + 1; k < V; ++k)
+            if (w[k] > 0.0) {
+              *alt = k;
+              break;
+            }
+        }
+      }
       return j;
     }
   }
   for (int j = V - 1; j >= 0; --j)
     if (w[j] > 0.0) {
-      if (margin) *margin = 0.0;
+      if (alt) *alt = j;
       return j;
     }
   return -1;
@@ -265,7 +291,9 @@ static double uni(const orc_params* pr, int64_t b, int r, uint32_t d, const doub
 /* ------------------------------------------------------------------------ */
 /* Draft sampling [UnoX §3.3]: x_i drawn from softmax(filter(q_i / T)) by an
  * inverse-CDF draw over exp(z - max z) with U(seed, step, b, i, 0x40000000);
- * greedy: argmax q_i. */
+ * greedy: argmax q_i. Per draft: the draw's margin and alternative token (see
+ * orc_sample) and the margin of its row's top-p cut (+inf where there is no
+ * such decision). */
 typedef struct {
   const void* q;
   int dtype;
@@ -273,6 +301,8 @@ typedef struct {
   orc_params pr;
   int32_t* out;
   double* out_margin;
+  int32_t* out_alt;
+  double* out_margin_filter;
   const double* ovr; /* [B][K] */
   int64_t b0, b1;
 } draft_job;
@@ -287,24 +317,26 @@ static void* draft_worker(void* arg) {
     int bad = 0;
     for (int i = 0; i < K; ++i) bad |= orc_decode_row(J->q, J->dtype, b * K + i, V, z);
     for (int i = 0; i < K; ++i) {
-      double margin = 1.0;
-      int x = -1;
+      double margin = INFINITY, fmargin = INFINITY;
+      int x = -1, alt = -1;
       if (!bad) {
         orc_decode_row(J->q, J->dtype, b * K + i, V, z);
         if (J->pr.temperature == 0.0) {
           x = argmax_row(z, V);
         } else {
-          filter_row_buf(z, V, J->pr.temperature, J->pr.top_k, J->pr.top_p, buf);
+          filter_row_buf(z, V, J->pr.temperature, J->pr.top_k, J->pr.top_p, buf, &fmargin);
           double m = -INFINITY;
           for (int j = 0; j < V; ++j)
             if (z[j] > m) m = z[j];
           for (int j = 0; j < V; ++j) w[j] = exp(z[j] - m);
           double u = uni(&J->pr, b, i, ORC_DRAFT_DRAW, J->ovr, J->ovr ? (size_t)(b * K + i) : 0);
-          x = orc_sample(w, V, u, &margin);
+          x = orc_sample(w, V, u, &margin, &alt);
         }
       }
       J->out[b * K + i] = x;
       if (J->out_margin) J->out_margin[b * K + i] = margin;
+      if (J->out_alt) J->out_alt[b * K + i] = alt;
+      if (J->out_margin_filter) J->out_margin_filter[b * K + i] = fmargin;
     }
   }
   free(z);
@@ -332,8 +364,8 @@ static int clamp_threads(int nthreads, int64_t B) {
 }
 
 int orc_draft_sample(const void* q, int dtype, int64_t B, int K, int V, double temperature, int top_k,
-                     double top_p, uint64_t seed, uint32_t step, int32_t* out, double* out_margin,
-                     const double* u_override, int nthreads) {
+                     double top_p, uint64_t seed, uint32_t step, int32_t* out, double* out_margin, int32_t* out_alt,
+                     double* out_margin_filter, const double* u_override, int nthreads) {
   if (!q || !out || B <= 0 || K <= 0 || V <= 0 || !(temperature >= 0.0)) return -1;
   nthreads = clamp_threads(nthreads, B);
   draft_job* jobs = (draft_job*)calloc((size_t)nthreads, sizeof(draft_job));
@@ -350,6 +382,8 @@ int orc_draft_sample(const void* q, int dtype, int64_t B, int K, int V, double t
     J->pr.step = step;
     J->out = out;
     J->out_margin = out_margin;
+    J->out_alt = out_alt;
+    J->out_margin_filter = out_margin_filter;
     J->ovr = u_override;
     J->b0 = B * t / nthreads;
     J->b1 = B * (t + 1) / nthreads;
@@ -361,6 +395,23 @@ int orc_draft_sample(const void* q, int dtype, int64_t B, int K, int V, double t
 
 /* ------------------------------------------------------------------------ */
 /* Linear verification [UnoX §3.3, §3.4 Linear Sampler]. */
+
+/* Margins of the decisions of one verification, so that a comparison with a
+ * finite-precision implementation can tell which decision parted first and
+ * how close it was (any pointer may be NULL):
+ *   acc [B][K]        |u - min(1, P/Q)| of each accept test taken; +inf at
+ *                     positions never tested, for Q(x) = 0, and in greedy mode;
+ *   draft [B][K]      inverse-CDF margin of each draft drawn inside the call
+ *                     (+inf when drafts are given or greedy), draft_alt the
+ *                     token across its nearer edge (orc_sample);
+ *   fin [B], fin_alt  the same for the final (residual or bonus) draw;
+ *   filter [B]        the smallest top-p cut margin over the request's
+ *                     2K + 1 rows (+inf without a top-p cut). */
+typedef struct {
+  double *acc, *draft, *fin, *filter;
+  int32_t *draft_alt, *fin_alt;
+} orc_lin_margins;
+
 typedef struct {
   const void *p, *q;
   int dtype, K, V, fused;
@@ -370,8 +421,7 @@ typedef struct {
   int32_t* out_len;
   double* out_probs;
   double* out_resid;
-  double* out_margin_acc;
-  double* out_margin_cdf;
+  orc_lin_margins mg;
   const double* ovr; /* [B][K+1][3]: final (d=0), accept (d=1), draft (d=0x40000000) */
   int64_t b0, b1;
 } linear_job;
@@ -379,11 +429,18 @@ typedef struct {
 static void linear_one(linear_job* J, int64_t b, double* zp, double* zq, double* w, keyed* buf) {
   const int K = J->K, V = J->V;
   const orc_params* pr = &J->pr;
+  const orc_lin_margins* M = &J->mg;
   int32_t* toks = J->out_tokens + b * (K + 1);
   for (int i = 0; i <= K; ++i) toks[i] = -1;
   if (J->out_resid) J->out_resid[b] = 0.0;
-  if (J->out_margin_acc) J->out_margin_acc[b] = 1.0;
-  if (J->out_margin_cdf) J->out_margin_cdf[b] = 1.0;
+  for (int i = 0; i < K; ++i) {
+    if (M->acc) M->acc[b * K + i] = INFINITY;
+    if (M->draft) M->draft[b * K + i] = INFINITY;
+    if (M->draft_alt) M->draft_alt[b * K + i] = -1;
+  }
+  if (M->fin) M->fin[b] = INFINITY;
+  if (M->fin_alt) M->fin_alt[b] = -1;
+  if (M->filter) M->filter[b] = INFINITY;
   if (J->out_probs)
     for (int i = 0; i < 2 * K; ++i) J->out_probs[b * 2 * K + i] = 0.0;
 
@@ -403,7 +460,6 @@ static void linear_one(linear_job* J, int64_t b, double* zp, double* zq, double*
     return;
   }
 
-  double margin_acc = 1.0, margin_cdf = 1.0;
   int n = K, y = -1;
   if (pr->temperature == 0.0) {
     /* greedy */
@@ -426,14 +482,18 @@ static void linear_one(linear_job* J, int64_t b, double* zp, double* zq, double*
     y = g[n];
   } else {
     double Lp[PSI_MAXK_ORACLE_PLUS1], Lq[PSI_MAXK_ORACLE_PLUS1];
+    double fmin_all = INFINITY, fm;
     for (int i = 0; i <= K; ++i) {
-      filter_row_buf(zp + (size_t)i * V, V, pr->temperature, pr->top_k, pr->top_p, buf);
+      filter_row_buf(zp + (size_t)i * V, V, pr->temperature, pr->top_k, pr->top_p, buf, &fm);
+      fmin_all = fmin(fmin_all, fm);
       Lp[i] = orc_logsumexp(zp + (size_t)i * V, V);
     }
     for (int i = 0; i < K; ++i) {
-      filter_row_buf(zq + (size_t)i * V, V, pr->temperature, pr->top_k, pr->top_p, buf);
+      filter_row_buf(zq + (size_t)i * V, V, pr->temperature, pr->top_k, pr->top_p, buf, &fm);
+      fmin_all = fmin(fmin_all, fm);
       Lq[i] = orc_logsumexp(zq + (size_t)i * V, V);
     }
+    if (M->filter) M->filter[b] = fmin_all;
     if (J->fused) {
       for (int i = 0; i < K; ++i) {
         const double* z = zq + (size_t)i * V;
@@ -443,8 +503,10 @@ static void linear_one(linear_job* J, int64_t b, double* zp, double* zq, double*
         for (int j = 0; j < V; ++j) w[j] = exp(z[j] - m);
         double u = uni(pr, b, i, ORC_DRAFT_DRAW, J->ovr, J->ovr ? (size_t)((b * (K + 1) + i) * 3 + 2) : 0);
         double mg;
-        J->draft[b * K + i] = orc_sample(w, V, u, &mg);
-        if (mg < margin_cdf) margin_cdf = mg;
+        int alt;
+        J->draft[b * K + i] = orc_sample(w, V, u, &mg, &alt);
+        if (M->draft) M->draft[b * K + i] = mg;
+        if (M->draft_alt) M->draft_alt[b * K + i] = alt;
       }
     }
     /* per-position target and draft probability of the draft token */
@@ -464,15 +526,14 @@ static void linear_one(linear_job* J, int64_t b, double* zp, double* zq, double*
     for (int i = 0; i < K; ++i) {
       double u = uni(pr, b, i, 1u, J->ovr, J->ovr ? (size_t)((b * (K + 1) + i) * 3 + 1) : 0);
       int acc = u * Q[i] < P[i];
-      double ratio = (Q[i] > 0.0) ? fmin(1.0, P[i] / Q[i]) : 1.0;
-      double mg = (Q[i] > 0.0) ? fabs(u - ratio) : 1.0;
-      if (mg < margin_acc) margin_acc = mg;
+      if (M->acc && Q[i] > 0.0) M->acc[b * K + i] = fabs(u - fmin(1.0, P[i] / Q[i]));
       if (!acc) {
         n = i;
         break;
       }
     }
-    double mg = 1.0;
+    double mg;
+    int alt;
     if (n < K) {
       /* residual max(0, p_n - q_n), falling back to p_n when it sums to 0 */
       const double* a = zp + (size_t)n * V;
@@ -488,21 +549,20 @@ static void linear_one(linear_job* J, int64_t b, double* zp, double* zq, double*
       if (!(W > 0.0))
         for (int j = 0; j < V; ++j) w[j] = exp(a[j] - Lp[n]);
       double u = uni(pr, b, n, 0u, J->ovr, J->ovr ? (size_t)((b * (K + 1) + n) * 3 + 0) : 0);
-      y = orc_sample(w, V, u, &mg);
+      y = orc_sample(w, V, u, &mg, &alt);
     } else {
       /* bonus token from the last target row */
       const double* a = zp + (size_t)K * V;
       for (int j = 0; j < V; ++j) w[j] = exp(a[j] - Lp[K]);
       double u = uni(pr, b, K, 0u, J->ovr, J->ovr ? (size_t)((b * (K + 1) + K) * 3 + 0) : 0);
-      y = orc_sample(w, V, u, &mg);
+      y = orc_sample(w, V, u, &mg, &alt);
     }
-    if (mg < margin_cdf) margin_cdf = mg;
+    if (M->fin) M->fin[b] = mg;
+    if (M->fin_alt) M->fin_alt[b] = alt;
   }
   for (int i = 0; i < n; ++i) toks[i] = J->draft[b * K + i];
   toks[n] = y;
   J->out_len[b] = n;
-  if (J->out_margin_acc) J->out_margin_acc[b] = margin_acc;
-  if (J->out_margin_cdf) J->out_margin_cdf[b] = margin_cdf;
 }
 
 static void* linear_worker(void* arg) {
@@ -523,7 +583,7 @@ static void* linear_worker(void* arg) {
 int orc_verify_linear(const void* p, const void* q, int dtype, int64_t B, int K, int V, int32_t* draft_tokens,
                       double temperature, int top_k, double top_p, uint64_t seed, uint32_t step, int fused,
                       int32_t* out_tokens, int32_t* out_len, double* out_probs, double* out_resid,
-                      double* out_margin_acc, double* out_margin_cdf, const double* u_override, int nthreads) {
+                      const orc_lin_margins* margins, const double* u_override, int nthreads) {
   if (!p || !q || !draft_tokens || !out_tokens || !out_len) return -1;
   if (B <= 0 || K <= 0 || K >= PSI_MAXK_ORACLE_PLUS1 || V <= 0 || !(temperature >= 0.0)) return -1;
   nthreads = clamp_threads(nthreads, B);
@@ -546,8 +606,7 @@ int orc_verify_linear(const void* p, const void* q, int dtype, int64_t B, int K,
     J->out_len = out_len;
     J->out_probs = out_probs;
     J->out_resid = out_resid;
-    J->out_margin_acc = out_margin_acc;
-    J->out_margin_cdf = out_margin_cdf;
+    if (margins) J->mg = *margins;
     J->ovr = u_override;
     J->b0 = B * t / nthreads;
     J->b1 = B * (t + 1) / nthreads;
@@ -562,6 +621,16 @@ int orc_verify_linear(const void* p, const void* q, int dtype, int64_t B, int K,
  * i.i.d. draws from the node's draft row Q, tested in ascending node id
  * against a running target r (starting at P): accept iff u * Q(tok) < r(tok);
  * after a rejection r <- norm(max(0, r - Q)) (kept when that sums to 0). */
+/* Margins of a tree verification (any pointer may be NULL): acc [B][N] the
+ * accept test of node n at its parent row, |u - min(1, r(tok)/Q(tok))| with r
+ * the running target (+inf for nodes never tested, Q(tok) = 0, greedy);
+ * fin [B] and fin_alt [B] the final draw (orc_sample); filter [B] the smallest
+ * top-p cut margin over the rows the walk filtered (+inf without top-p). */
+typedef struct {
+  double *acc, *fin, *filter;
+  int32_t* fin_alt;
+} orc_tree_margins;
+
 typedef struct {
   const void *p, *q;
   int dtype, N, V, maxC;
@@ -569,7 +638,7 @@ typedef struct {
   const int32_t* tokens;
   orc_params pr;
   int32_t *out_tokens, *out_path, *out_len;
-  double *out_margin_acc, *out_margin_cdf;
+  orc_tree_margins mg;
   const double* ovr; /* [B][N+1][1+maxC]: slot 0 = d=0, slot 1+j = d=1+j */
   int D;
   int64_t b0, b1;
@@ -579,12 +648,16 @@ static void tree_one(tree_job* J, int64_t b, double* zp, double* zq, double* rt,
                      keyed* buf) {
   const int N = J->N, V = J->V, R = J->N + 1, D = J->D;
   const orc_params* pr = &J->pr;
+  const orc_tree_margins* M = &J->mg;
   int32_t* toks = J->out_tokens + b * (D + 1);
   int32_t* path = J->out_path + b * D;
   for (int i = 0; i <= D; ++i) toks[i] = -1;
   for (int i = 0; i < D; ++i) path[i] = -1;
-  if (J->out_margin_acc) J->out_margin_acc[b] = 1.0;
-  if (J->out_margin_cdf) J->out_margin_cdf[b] = 1.0;
+  if (M->acc)
+    for (int n = 0; n < N; ++n) M->acc[b * N + n] = INFINITY;
+  if (M->fin) M->fin[b] = INFINITY;
+  if (M->fin_alt) M->fin_alt[b] = -1;
+  if (M->filter) M->filter[b] = INFINITY;
   int bad = 0;
   for (int r = 0; r < R; ++r) {
     bad |= orc_decode_row(J->p, J->dtype, b * R + r, V, zp + (size_t)r * V);
@@ -598,7 +671,7 @@ static void tree_one(tree_job* J, int64_t b, double* zp, double* zq, double* rt,
     J->out_len[b] = -1;
     return;
   }
-  double margin_acc = 1.0, margin_cdf = 1.0;
+  double fmin_all = INFINITY;
   int greedy = pr->temperature == 0.0;
   int row = 0, len = 0, y = -1;
   for (;;) {
@@ -623,8 +696,11 @@ static void tree_one(tree_job* J, int64_t b, double* zp, double* zq, double* rt,
       /* target and draft distributions of this row, after filtering */
       memcpy(rt, a, sizeof(double) * (size_t)V);
       memcpy(Qv, d, sizeof(double) * (size_t)V);
-      filter_row_buf(rt, V, pr->temperature, pr->top_k, pr->top_p, buf);
-      filter_row_buf(Qv, V, pr->temperature, pr->top_k, pr->top_p, buf);
+      double fm;
+      filter_row_buf(rt, V, pr->temperature, pr->top_k, pr->top_p, buf, &fm);
+      fmin_all = fmin(fmin_all, fm);
+      filter_row_buf(Qv, V, pr->temperature, pr->top_k, pr->top_p, buf, &fm);
+      fmin_all = fmin(fmin_all, fm);
       double Lp = orc_logsumexp(rt, V), Lq = orc_logsumexp(Qv, V);
       for (int t = 0; t < V; ++t) {
         rt[t] = exp(rt[t] - Lp);
@@ -635,9 +711,7 @@ static void tree_one(tree_job* J, int64_t b, double* zp, double* zq, double* rt,
         int tok = J->tokens[b * N + c];
         double u = uni(pr, b, row, 1u + (uint32_t)j, J->ovr,
                        J->ovr ? (size_t)((b * R + row) * (1 + J->maxC) + 1 + j) : 0);
-        double ratio = (Qv[tok] > 0.0) ? fmin(1.0, rt[tok] / Qv[tok]) : 1.0;
-        double mg = (Qv[tok] > 0.0) ? fabs(u - ratio) : 1.0;
-        if (mg < margin_acc) margin_acc = mg;
+        if (M->acc && Qv[tok] > 0.0) M->acc[b * N + c] = fabs(u - fmin(1.0, rt[tok] / Qv[tok]));
         if (u * Qv[tok] < rt[tok]) {
           accepted = c;
           break;
@@ -654,8 +728,10 @@ static void tree_one(tree_job* J, int64_t b, double* zp, double* zq, double* rt,
       if (accepted < 0) {
         double u = uni(pr, b, row, 0u, J->ovr, J->ovr ? (size_t)((b * R + row) * (1 + J->maxC)) : 0);
         double mg;
-        y = orc_sample(rt, V, u, &mg);
-        if (mg < margin_cdf) margin_cdf = mg;
+        int alt;
+        y = orc_sample(rt, V, u, &mg, &alt);
+        if (M->fin) M->fin[b] = mg;
+        if (M->fin_alt) M->fin_alt[b] = alt;
         break;
       }
     }
@@ -666,8 +742,7 @@ static void tree_one(tree_job* J, int64_t b, double* zp, double* zq, double* rt,
   }
   toks[len] = y;
   J->out_len[b] = len;
-  if (J->out_margin_acc) J->out_margin_acc[b] = margin_acc;
-  if (J->out_margin_cdf) J->out_margin_cdf[b] = margin_cdf;
+  if (M->filter) M->filter[b] = fmin_all;
 }
 
 static void* tree_worker(void* arg) {
@@ -707,13 +782,17 @@ int orc_tree_depth(const int32_t* parent, int N) {
  * node n, the j-th child (ascending id) of row r = parent[n] + 1, is an
  * inverse-CDF draw from softmax(filter(q_r / T)) with
  * U(seed, step, b, r, 0x40000000 + j); greedy: argmax q_r. A request with an
- * invalid draft row gets -1 for every node. */
+ * invalid draft row gets -1 for every node. Per node (any may be NULL): the
+ * draw's margin and alternative token (orc_sample) and the top-p cut margin
+ * of its row (+inf where there is no such decision). */
 typedef struct {
   const void* q;
   int dtype, N, V;
   const int32_t* parent;
   orc_params pr;
   int32_t* out;
+  double *out_margin, *out_margin_filter;
+  int32_t* out_alt;
   int64_t b0, b1;
 } tree_draft_job;
 
@@ -724,6 +803,11 @@ static void* tree_draft_worker(void* arg) {
   double* w = (double*)malloc(sizeof(double) * (size_t)V);
   keyed* buf = (keyed*)malloc(sizeof(keyed) * (size_t)V);
   for (int64_t b = J->b0; b < J->b1; ++b) {
+    for (int n = 0; n < N; ++n) {
+      if (J->out_margin) J->out_margin[b * N + n] = INFINITY;
+      if (J->out_margin_filter) J->out_margin_filter[b * N + n] = INFINITY;
+      if (J->out_alt) J->out_alt[b * N + n] = -1;
+    }
     int bad = 0;
     for (int r = 0; r < R; ++r) bad |= orc_decode_row(J->q, J->dtype, b * R + r, V, z);
     for (int r = 0; r < R && !bad; ++r) {
@@ -735,12 +819,17 @@ static void* tree_draft_worker(void* arg) {
         if (J->pr.temperature == 0.0) {
           x = argmax_row(z, V);
         } else {
-          filter_row_buf(z, V, J->pr.temperature, J->pr.top_k, J->pr.top_p, buf);
+          double fm, mg;
+          int alt;
+          filter_row_buf(z, V, J->pr.temperature, J->pr.top_k, J->pr.top_p, buf, &fm);
           double m = -INFINITY;
           for (int t = 0; t < V; ++t)
             if (z[t] > m) m = z[t];
           for (int t = 0; t < V; ++t) w[t] = exp(z[t] - m);
-          x = orc_sample(w, V, uni(&J->pr, b, r, ORC_DRAFT_DRAW + (uint32_t)j, NULL, 0), NULL);
+          x = orc_sample(w, V, uni(&J->pr, b, r, ORC_DRAFT_DRAW + (uint32_t)j, NULL, 0), &mg, &alt);
+          if (J->out_margin) J->out_margin[b * N + n] = mg;
+          if (J->out_margin_filter) J->out_margin_filter[b * N + n] = fm;
+          if (J->out_alt) J->out_alt[b * N + n] = alt;
         }
         J->out[b * N + n] = x;
         ++j;
@@ -756,7 +845,8 @@ static void* tree_draft_worker(void* arg) {
 }
 
 int orc_tree_draft(const void* q, int dtype, int64_t B, int N, int V, const int32_t* parent, double temperature,
-                   int top_k, double top_p, uint64_t seed, uint32_t step, int32_t* out, int nthreads) {
+                   int top_k, double top_p, uint64_t seed, uint32_t step, int32_t* out, double* out_margin,
+                   int32_t* out_alt, double* out_margin_filter, int nthreads) {
   if (!q || !parent || !out || B <= 0 || V <= 0 || !(temperature >= 0.0)) return -1;
   if (orc_tree_depth(parent, N) < 0) return -1;
   nthreads = clamp_threads(nthreads, B);
@@ -774,6 +864,9 @@ int orc_tree_draft(const void* q, int dtype, int64_t B, int N, int V, const int3
     J->pr.seed = seed;
     J->pr.step = step;
     J->out = out;
+    J->out_margin = out_margin;
+    J->out_alt = out_alt;
+    J->out_margin_filter = out_margin_filter;
     J->b0 = B * t / nthreads;
     J->b1 = B * (t + 1) / nthreads;
   }
@@ -786,8 +879,7 @@ int orc_tree_draft(const void* q, int dtype, int64_t B, int N, int V, const int3
 int orc_verify_tree(const void* p, const void* q, int dtype, int64_t B, int N, int V, const int32_t* parent,
                     const int32_t* node_tokens, double temperature, int top_k, double top_p, uint64_t seed,
                     uint32_t step, int32_t* out_tokens, int32_t* out_path, int32_t* out_len,
-                    double* out_margin_acc, double* out_margin_cdf, const double* u_override, int maxC,
-                    int nthreads) {
+                    const orc_tree_margins* margins, const double* u_override, int maxC, int nthreads) {
   if (!p || !q || !parent || !node_tokens || !out_tokens || !out_path || !out_len) return -1;
   if (B <= 0 || V <= 0 || !(temperature >= 0.0)) return -1;
   int D = orc_tree_depth(parent, N);
@@ -820,8 +912,7 @@ int orc_verify_tree(const void* p, const void* q, int dtype, int64_t B, int N, i
     J->out_tokens = out_tokens;
     J->out_path = out_path;
     J->out_len = out_len;
-    J->out_margin_acc = out_margin_acc;
-    J->out_margin_cdf = out_margin_cdf;
+    if (margins) J->mg = *margins;
     J->ovr = u_override;
     J->D = D;
     J->b0 = B * t / nthreads;
@@ -852,10 +943,12 @@ int orc_verify_tree(const void* p, const void* q, int dtype, int64_t B, int N, i
  * token, so parent[n] < n. Enumerated best first: at each step every kept
  * prefix (and the empty one) offers its best child not yet kept, and the best
  * offer in the order is kept; a prefix of probability zero is never kept
- * (nodes past the last prefix of positive probability get -1). *margin = the
- * smallest log-score gap between the kept offer and any other offer of the
- * same step (0 for exact ties across parents). A request with an invalid
- * draft row gets -1 in every parent and token. */
+ * (nodes past the last prefix of positive probability get -1).
+ * out_margin [B][nodes] (may be NULL): for the step that keeps node n, the
+ * smallest log-score gap between the kept offer and any other offer of that
+ * step (0 for exact ties across parents; +inf when no other offer has positive
+ * probability, or for nodes never kept). A request with an invalid draft row
+ * gets -1 in every parent and token. */
 typedef struct {
   const void* q;
   int dtype, K, V, cands, nodes;
@@ -894,16 +987,16 @@ static void* cand_worker(void* arg) {
         clq[i * C + r] = buf[r].key - L;
       }
     }
+    if (J->out_margin)
+      for (int n = 0; n < NN; ++n) J->out_margin[b * NN + n] = INFINITY;
     if (bad) {
       for (int n = 0; n < NN; ++n) par[n] = tok[n] = -1;
-      if (J->out_margin) J->out_margin[b] = 1.0;
       continue;
     }
     /* slot 0 is the empty prefix; slot n + 1 is node n */
     ls[0] = 0.0;
     depth[0] = 0;
     next[0] = 0;
-    double margin = INFINITY;
     for (int n = 0; n < NN; ++n) {
       int best = -1;
       double bls = 0.0;
@@ -925,11 +1018,13 @@ static void* cand_worker(void* arg) {
         for (int m = n; m < NN; ++m) par[m] = tok[m] = -1;
         break;
       }
+      double margin = INFINITY;
       for (int s = 0; s <= n; ++s) {
         if (s == best || depth[s] >= K || next[s] >= C) continue;
         const double gap = bls - (ls[s] + clq[depth[s] * C + next[s]]);
         if (gap < margin) margin = gap; /* an offer of zero probability gives +inf */
       }
+      if (J->out_margin) J->out_margin[b * NN + n] = margin;
       par[n] = best - 1;
       tok[n] = ctok[depth[best] * C + next[best]];
       ls[n + 1] = bls;
@@ -937,7 +1032,6 @@ static void* cand_worker(void* arg) {
       next[n + 1] = 0;
       ++next[best];
     }
-    if (J->out_margin) J->out_margin[b] = isinf(margin) ? 1.0 : margin;
   }
   free(z);
   free(buf);
@@ -991,15 +1085,19 @@ int orc_tree_candidates(const void* q, int dtype, int64_t B, int K, int V, doubl
  * Temperature 0: accept iff tok is the target argmax (lowest id on ties);
  * final token = the argmax. Any malformed parent, token out of range or
  * invalid target row makes the request an error. Outputs [N + 1] tokens and
- * [N] path entries per request, -1 past the end. */
+ * [N] path entries per request, -1 past the end. Margins (orc_tree_margins,
+ * any pointer may be NULL): acc [B][N] |u - r(tok)| of each test taken, r(tok)
+ * = P(tok) / (1 - E) the running target's mass at tok (+inf for nodes never
+ * tested, removed tokens and greedy); fin / fin_alt the final draw; filter is
+ * +inf (no filters here). */
 typedef struct {
   const void* p;
   int dtype, N, V;
   const int32_t *parent, *tokens;
   orc_params pr;
   int32_t *out_tokens, *out_path, *out_len;
-  double *out_margin_acc, *out_margin_cdf;
-  const double* ovr; /* [B][N+1][1+maxC]: slot 0 = d=0, slot 1+j = d=1+j */
+  orc_tree_margins mg; /* acc: |u - r(tok)| with r the running target */
+  const double* ovr;   /* [B][N+1][1+maxC]: slot 0 = d=0, slot 1+j = d=1+j */
   int maxC;
   int64_t b0, b1;
 } dtree_job;
@@ -1011,10 +1109,14 @@ static void dtree_one(dtree_job* J, int64_t b, double* z, double* P, double* w, 
   const int32_t* ntk = J->tokens + b * N;
   int32_t* toks = J->out_tokens + b * R;
   int32_t* path = J->out_path + b * N;
+  const orc_tree_margins* M = &J->mg;
   for (int i = 0; i < R; ++i) toks[i] = -1;
   for (int i = 0; i < N; ++i) path[i] = -1;
-  if (J->out_margin_acc) J->out_margin_acc[b] = 1.0;
-  if (J->out_margin_cdf) J->out_margin_cdf[b] = 1.0;
+  if (M->acc)
+    for (int n = 0; n < N; ++n) M->acc[b * N + n] = INFINITY;
+  if (M->fin) M->fin[b] = INFINITY;
+  if (M->fin_alt) M->fin_alt[b] = -1;
+  if (M->filter) M->filter[b] = INFINITY;
   int bad = 0;
   for (int n = 0; n < N; ++n) {
     if (par[n] < -1 || par[n] >= n) bad = 1;
@@ -1025,7 +1127,6 @@ static void dtree_one(dtree_job* J, int64_t b, double* z, double* P, double* w, 
     J->out_len[b] = -1;
     return;
   }
-  double margin_acc = 1.0, margin_cdf = 1.0;
   const int greedy = pr->temperature == 0.0;
   int row = 0, len = 0, y = -1;
   for (;;) {
@@ -1054,10 +1155,7 @@ static void dtree_one(dtree_job* J, int64_t b, double* z, double* P, double* w, 
         const double u = uni(pr, b, row, 1u + (uint32_t)j, J->ovr,
                              J->ovr ? (size_t)((b * R + row) * (1 + J->maxC) + 1 + j) : 0);
         const double pt = removed[tk] ? 0.0 : P[tk];
-        if (1.0 - E > 0.0) {
-          const double mg = fabs(u - pt / (1.0 - E));
-          if (mg < margin_acc) margin_acc = mg;
-        }
+        if (M->acc && 1.0 - E > 0.0 && pt > 0.0) M->acc[b * N + c] = fabs(u - pt / (1.0 - E));
         if (u * (1.0 - E) < pt) {
           accepted = c;
           break;
@@ -1076,8 +1174,10 @@ static void dtree_one(dtree_job* J, int64_t b, double* z, double* P, double* w, 
         }
         const double u = uni(pr, b, row, 0u, J->ovr, J->ovr ? (size_t)((b * R + row) * (1 + J->maxC)) : 0);
         double mg;
-        y = orc_sample(S > 0.0 ? w : P, V, u, &mg);
-        if (mg < margin_cdf) margin_cdf = mg;
+        int alt;
+        y = orc_sample(S > 0.0 ? w : P, V, u, &mg, &alt);
+        if (M->fin) M->fin[b] = mg;
+        if (M->fin_alt) M->fin_alt[b] = alt;
         break;
       }
     }
@@ -1088,8 +1188,6 @@ static void dtree_one(dtree_job* J, int64_t b, double* z, double* P, double* w, 
   }
   toks[len] = y;
   J->out_len[b] = len;
-  if (J->out_margin_acc) J->out_margin_acc[b] = margin_acc;
-  if (J->out_margin_cdf) J->out_margin_cdf[b] = margin_cdf;
 }
 
 static void* dtree_worker(void* arg) {
@@ -1109,8 +1207,8 @@ static void* dtree_worker(void* arg) {
 
 int orc_verify_tree_det(const void* p, int dtype, int64_t B, int N, int V, const int32_t* parent,
                         const int32_t* node_tokens, double temperature, uint64_t seed, uint32_t step,
-                        int32_t* out_tokens, int32_t* out_path, int32_t* out_len, double* out_margin_acc,
-                        double* out_margin_cdf, const double* u_override, int maxC, int nthreads) {
+                        int32_t* out_tokens, int32_t* out_path, int32_t* out_len,
+                        const orc_tree_margins* margins, const double* u_override, int maxC, int nthreads) {
   if (!p || !parent || !node_tokens || !out_tokens || !out_path || !out_len) return -1;
   if (B <= 0 || N <= 0 || V <= 0 || !(temperature >= 0.0)) return -1;
   if (u_override) {
@@ -1138,8 +1236,7 @@ int orc_verify_tree_det(const void* p, int dtype, int64_t B, int N, int V, const
     J->out_tokens = out_tokens;
     J->out_path = out_path;
     J->out_len = out_len;
-    J->out_margin_acc = out_margin_acc;
-    J->out_margin_cdf = out_margin_cdf;
+    if (margins) J->mg = *margins;
     J->ovr = u_override;
     J->maxC = maxC;
     J->b0 = B * t / nthreads;

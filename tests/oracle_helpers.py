@@ -53,7 +53,7 @@ class FastLinear:
         rc = oracle.lib().orc_verify_linear(
             self.p.ctypes.data_as(P), self.q.ctypes.data_as(P), self.dtype, self.B, self.K, self.V,
             self.draft.ctypes.data_as(P), self.T, self.top_k, self.top_p, 0, 0, 0,
-            self.toks.ctypes.data_as(P), self.len.ctypes.data_as(P), None, None, None, None,
+            self.toks.ctypes.data_as(P), self.len.ctypes.data_as(P), None, None, None,
             self.ovr.ctypes.data_as(P), 1)
         assert rc == 0
         n = int(self.len[0])
@@ -158,7 +158,7 @@ class FastTree:
         rc = oracle.lib().orc_verify_tree(
             self.p.ctypes.data_as(P), self.q.ctypes.data_as(P), self.dtype, self.B, self.N, self.V,
             self.parent.ctypes.data_as(P), self.tokens.ctypes.data_as(P), self.T, 0, 1.0, 0, 0,
-            self.otok.ctypes.data_as(P), self.opath.ctypes.data_as(P), self.olen.ctypes.data_as(P), None, None,
+            self.otok.ctypes.data_as(P), self.opath.ctypes.data_as(P), self.olen.ctypes.data_as(P), None,
             self.ovr.ctypes.data_as(P), self.maxC, 1)
         assert rc == 0
         n = int(self.olen[0])
@@ -190,7 +190,7 @@ class FastDetTree:
         rc = oracle.lib().orc_verify_tree_det(
             self.p.ctypes.data_as(P), self.dtype, 1, self.N, self.V, self.parent.ctypes.data_as(P),
             self.tokens.ctypes.data_as(P), self.T, 0, 0, self.otok.ctypes.data_as(P), self.opath.ctypes.data_as(P),
-            self.olen.ctypes.data_as(P), None, None, self.ovr.ctypes.data_as(P), self.maxC, 1)
+            self.olen.ctypes.data_as(P), None, self.ovr.ctypes.data_as(P), self.maxC, 1)
         assert rc == 0
         n = int(self.olen[0])
         return n, tuple(int(t) for t in self.otok[0, :n + 1]), tuple(int(x) for x in self.opath[0, :n])

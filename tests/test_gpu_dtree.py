@@ -12,14 +12,14 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import THREADS, compare_tree, f32, to_dev
+from gpu_helpers import THREADS, Tally, compare_tree, f32, to_dev
 from oracle_helpers import chi2_pvalue
 
 pytestmark = pytest.mark.gpu
 
-# A candidate choice is a near tie when the oracle's smallest log-score gap of
-# the request is below this: the GPU's log-normalisers of the draft rows are
-# good to ~1e-7, so two offers closer than this may be kept in either order.
+# A candidate choice is a near tie when the oracle's log-score gap of that
+# step is below this: the GPU's log-normalisers of the draft rows are good to
+# ~1e-7, so two offers closer than this may be kept in either order.
 CAND_GAP = 1e-5
 
 
@@ -48,28 +48,34 @@ def _node_scores(q: np.ndarray, T: float, par: np.ndarray, tok: np.ndarray) -> n
 
 
 def check_candidates(q: np.ndarray, cands: int, nodes: int, T: float):
-    """GPU candidates against the oracle's, request by request. A request may
-    differ only when its oracle gap is below CAND_GAP; then the GPU's tree must
-    still be a valid tree whose kept scores match the oracle's. Returns the
-    oracle's (parent, tokens) and the number of excused requests."""
+    """GPU candidates against the oracle's, request by request. Where they
+    differ, the first differing node must have been kept at a step whose
+    oracle gap is below CAND_GAP; the GPU's tree must then still be a valid
+    tree whose kept scores match the oracle's. Returns the oracle's (parent,
+    tokens) and the tally (one decision per step with a rival offer)."""
     psi = _psi()
     g = psi.tree_candidates(to_dev(q), cands, nodes, temperature=T)
     torch.cuda.synchronize()
     gp, gt = g["parent"].cpu().numpy(), g["tokens"].cpu().numpy()
     op, ot, gap = oracle.tree_candidates(q, cands, nodes, T, nthreads=THREADS)
-    excused = 0
+    t = Tally(f"candidates B={q.shape[0]} K={q.shape[1]} V={q.shape[2]} c={cands} n={nodes}")
+    t.requests = q.shape[0]
+    t.decisions = int(np.isfinite(gap).sum())
+    t.near = int((gap < CAND_GAP).sum())
     for b in range(q.shape[0]):
         if np.array_equal(gp[b], op[b]) and np.array_equal(gt[b], ot[b]):
             continue
-        assert gap[b] < CAND_GAP, (f"request {b}: gpu parent {gp[b].tolist()} tokens {gt[b].tolist()} vs oracle "
-                                   f"parent {op[b].tolist()} tokens {ot[b].tolist()} (gap {gap[b]:.3g})")
+        n0 = int(np.nonzero((gp[b] != op[b]) | (gt[b] != ot[b]))[0][0])
+        assert gap[b, n0] < CAND_GAP, (f"request {b}: first difference at node {n0} (gap {gap[b, n0]:.3g}): gpu "
+                                       f"parent {gp[b].tolist()} tokens {gt[b].tolist()} vs oracle parent "
+                                       f"{op[b].tolist()} tokens {ot[b].tolist()}")
         n = np.arange(nodes)
         assert np.all((gp[b] >= -1) & (gp[b] < n)), gp[b]
         gs = np.sort(_node_scores(q[b], T, gp[b], gt[b]))
         os_ = np.sort(_node_scores(q[b], T, op[b], ot[b]))
         assert np.allclose(gs, os_, rtol=0, atol=CAND_GAP), (gs, os_)
-        excused += 1
-    return op, ot, excused
+        t.excused += 1
+    return op, ot, t
 
 
 @pytest.mark.parametrize("B,K,V,dtype,T,cands,nodes,seed", [
@@ -86,9 +92,16 @@ def check_candidates(q: np.ndarray, cands: int, nodes: int, T: float):
 def test_candidates_parity(B, K, V, dtype, T, cands, nodes, seed):
     T = f32(T)
     _, q = synth.pair(B, K, K, V, dtype, seed=seed, sd_a=2.0, mode=0, sd_noise=1.0)
-    op, ot, excused = check_candidates(q, cands, nodes, T)
+    op, ot, t = check_candidates(q, cands, nodes, T)
     if dtype == "f32":
-        assert excused <= 1
+        t.check()
+    else:
+        # bfloat16 rows of this size hold many exact ties of the logits: equal
+        # operands give equal scores on both sides (tested without excuse
+        # below), so what differs here are genuine near ties; each excused
+        # request was checked to keep a valid tree with the oracle's scores
+        print(t.report(), flush=True)
+        assert t.excused <= t.near and t.excused <= max(1, q.shape[0] // 2)
     if K * cands < nodes:
         assert np.all(op[:, K * cands:] == -1)
 
@@ -97,12 +110,12 @@ def test_candidates_full_size():
     """Tree Sampler workload: q [4, 16, 151936] bf16, 32 candidates per
     position, 32 kept prefixes; three input seeds."""
     w = synth.WORKLOADS["treesampler"]
-    excused = 0
+    tot = Tally("candidates full size x3")
     for seed in range(3):
         _, q = synth.treesampler_inputs(seed=seed)
-        _, _, e = check_candidates(q, w["cands"], w["nodes"], f32(w["temperature"]))
-        excused += e
-    assert excused <= 1
+        _, _, t = check_candidates(q, w["cands"], w["nodes"], f32(w["temperature"]))
+        tot += t
+    tot.check()
 
 
 def test_candidates_ties_and_masks():
@@ -114,9 +127,9 @@ def test_candidates_ties_and_masks():
     q[1, 2, :] = -np.inf
     q[1, 2, [3, 77, 401]] = [0.5, 0.5, -1.0]   # three finite logits, two tied
     q[2, :, 10:] = -np.inf                       # ten finite logits per position
-    check_candidates(q, 16, 64, 1.0)
+    check_candidates(q, 16, 64, 1.0)[2].check()
     qb = synth.f32_to_bf16(q)
-    check_candidates(qb, 16, 64, 1.0)
+    check_candidates(qb, 16, 64, 1.0)[2].check()
 
 
 def test_candidates_structural_ties():
@@ -146,7 +159,8 @@ def test_candidates_invalid_rows():
     q[1, 3, 17] = np.nan
     q[2, 0, :] = -np.inf
     q[3, 4, 5] = np.inf
-    op, ot, _ = check_candidates(q, 8, 20, 1.0)
+    op, ot, t = check_candidates(q, 8, 20, 1.0)
+    t.check()
     assert np.all(op[1:] == -1) and np.all(ot[1:] == -1) and np.all(ot[0] >= 0)
 
 
@@ -201,11 +215,13 @@ def test_verify_det_parity(B, N, V, dtype, T, seed):
     par = random_trees(B, N, seed)
     tok = likely_tokens(p, par, seed, top=4, frac=0.85)
     accepted = rejected_all = 0
+    tot = Tally(f"det verify B={B} N={N} V={V}")
     for step in range(4):
         g, o = det_case(p, par, tok, T, seed=seed, step=step)
-        compare_tree(g, o)
+        tot += compare_tree(g, o)
         accepted += int(np.sum(o["len"]))
         rejected_all += int(np.sum(o["len"] == 0))
+    tot.check()
     assert accepted > 0 and rejected_all > 0
 
 
@@ -223,10 +239,12 @@ def test_verify_det_duplicate_siblings():
         tok[b, :6] = [r0[0], r0[1], r0[0], r0[2], r0[1], r0[0]]
         tok[b, 6:] = [top[b, 1, 0], top[b, 1, 0], top[b, 1, 3], top[b, 2, 0], top[b, 2, 1], top[b, 3, 0]]
     finals = set()
+    tot = Tally("det verify duplicate siblings")
     for step in range(24):
         g, o = det_case(p, par, tok, 1.0, seed=5, step=step)
-        compare_tree(g, o)
+        tot += compare_tree(g, o)
         finals |= {int(x) for x, n in zip(o["tokens"][:, 0], o["len"]) if n == 0}
+    tot.check()
     assert finals  # some requests rejected every root child
 
 
@@ -237,14 +255,17 @@ def test_verify_det_full_size():
     w = synth.WORKLOADS["treesampler"]
     T = f32(w["temperature"])
     p, q = synth.treesampler_inputs(seed=1)
-    op, ot, _ = check_candidates(q, w["cands"], w["nodes"], T)
+    op, ot, tc = check_candidates(q, w["cands"], w["nodes"], T)
+    tc.check()
     pd = to_dev(p)
+    tot = Tally("det verify full size x6")
     for step in range(6):
         g = psi.verify_tree_det(pd, torch.from_numpy(op).cuda(), torch.from_numpy(ot).cuda(), temperature=T,
                                 seed=3, step=step)
         torch.cuda.synchronize()
         o = oracle.verify_tree_det(p, op, ot, T, seed=3, step=step, nthreads=THREADS)
-        compare_tree(g, o)
+        tot += compare_tree(g, o)
+    tot.check()
 
 
 def test_verify_det_chained_on_device():
@@ -253,14 +274,14 @@ def test_verify_det_chained_on_device():
     B, K, V, C, NN = 4, 6, 3000, 8, 40
     T = f32(0.8)
     p, q = synth.pair(B, NN + 1, K, V, "bf16", seed=31, sd_a=2.0, mode=0, sd_noise=1.0)
-    op, ot, excused = check_candidates(q, C, NN, T)
-    assert excused == 0
+    op, ot, t = check_candidates(q, C, NN, T)
+    assert t.excused == 0
     qd, pd = to_dev(q), to_dev(p)
     cand = psi.tree_candidates(qd, C, NN, temperature=T)
     g = psi.verify_tree_det(pd, cand["parent"], cand["tokens"], temperature=T, seed=1, step=2)
     torch.cuda.synchronize()
     o = oracle.verify_tree_det(p, op, ot, T, seed=1, step=2, nthreads=THREADS)
-    compare_tree(g, o)
+    compare_tree(g, o).check()
 
 
 def test_verify_det_greedy():
@@ -269,7 +290,7 @@ def test_verify_det_greedy():
     par = random_trees(B, N, 41)
     tok = likely_tokens(p, par, 41, top=2, frac=0.9)
     g, o = det_case(p, par, tok, 0.0)
-    compare_tree(g, o)
+    assert compare_tree(g, o).excused == 0
     assert np.sum(o["len"]) > 0
 
 
@@ -287,7 +308,7 @@ def test_verify_det_errors():
         gl = g["len"].cpu().numpy()
         assert list(gl[1:5]) == [-1] * 4 and gl[0] >= 0 and gl[5] >= 0
         assert np.all(g["tokens"].cpu().numpy()[1:5] == -1)
-        compare_tree(g, o)
+        compare_tree(g, o).check()
 
 
 def test_verify_det_first_token_law():

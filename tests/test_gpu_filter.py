@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import THREADS, compare_linear, f32, to_dev
+from gpu_helpers import THREADS, Tally, compare_drafts, compare_linear, f32, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -34,10 +34,11 @@ def _run(p, q, draft, T, top_k, top_p, seed, step, fused):
 def test_filtered_full_size():
     """Filtered workload at full size: B=128, K=16, V=128256, fp32, T=1, top_k=50, top_p=0.95, fused drafts."""
     p, q = synth.linear_inputs("filtered", seed=0)
-    g, o = _run(p, q, None, 1.0, 50, 0.95, 0, 0, True)
-    assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
-    ex, dec, _ = compare_linear(g, o)
-    assert ex <= max(1, 1e-4 * dec)
+    tot = Tally("filtered full size x2")
+    for step in range(2):
+        g, o = _run(p, q, None, 1.0, 50, 0.95, 0, step, True)
+        tot += compare_linear(g, o, fused=True)
+    tot.check()
 
 
 @pytest.mark.parametrize("dtype,V,T,top_k,top_p", [
@@ -46,11 +47,11 @@ def test_filtered_full_size():
 def test_filtered_small(dtype, V, T, top_k, top_p):
     B, K = 24, 4
     p, q = synth.pair(B, K + 1, K, V, dtype, seed=V, sd_a=2.0, mode=0, sd_noise=0.6)
+    tot = Tally(f"filtered {dtype} V={V} k={top_k} p={top_p}")
     for step in range(3):
         g, o = _run(p, q, None, T, top_k, top_p, 11, step, True)
-        assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
-        ex, dec, _ = compare_linear(g, o)
-        assert ex == 0
+        tot += compare_linear(g, o, fused=True)
+    tot.check()
 
 
 def test_filtered_ties():
@@ -62,7 +63,7 @@ def test_filtered_ties():
     for step in range(4):
         g, o = _run(p.astype(np.float32), q.astype(np.float32), None, 1.0, 30, 0.8, 2, step, True)
         assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
-        compare_linear(g, o)
+        compare_linear(g, o, fused=True).check()
         assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
 
 
@@ -84,7 +85,7 @@ def test_filtered_candidate_overflow():
     for step in range(3):
         g, o = _run(p, q, None, 1.0, 20, 0.53, 5, step, True)
         assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
-        compare_linear(g, o)
+        compare_linear(g, o, fused=True).check()
         assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
         assert int(g["len"][0]) == K  # identical constant rows always accept
 
@@ -106,7 +107,7 @@ def test_filtered_chunk_bound_raised():
     for step in range(3):
         g, o = _run(p, q, None, 1.0, 50, 0.9, 8, step, True)
         assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
-        compare_linear(g, o)
+        compare_linear(g, o, fused=True).check()
         assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
 
 
@@ -124,10 +125,12 @@ def test_top_k_one_matches_greedy():
 def test_filtered_draft_sample():
     psi = _psi()
     p, q = synth.linear_inputs("filtered", seed=1, B=8)
+    tot = Tally("filtered draft sample")
     for step in range(3):
         g = psi.draft_sample(to_dev(q), temperature=1.0, top_k=50, top_p=f32(0.95), seed=3, step=step)
-        o, _ = oracle.draft_sample(q, 1.0, top_k=50, top_p=f32(0.95), seed=3, step=step, nthreads=THREADS)
-        assert np.array_equal(g.cpu().numpy(), o)
+        o, om = oracle.draft_sample(q, 1.0, top_k=50, top_p=f32(0.95), seed=3, step=step, nthreads=THREADS)
+        tot += compare_drafts(g, o, om)
+    tot.check()
 
 
 def test_filtered_errors():
@@ -139,4 +142,4 @@ def test_filtered_errors():
     g, o = _run(p, q, None, 1.0, 20, 0.9, 0, 0, True)
     gl = g["len"].cpu().numpy()
     assert list(gl[[1, 2, 3]]) == [-1, -1, -1]
-    compare_linear(g, o)
+    compare_linear(g, o, fused=True).check()

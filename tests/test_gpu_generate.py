@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import NEAR_TIE_ACCEPT, NEAR_TIE_CDF, THREADS, f32
+from gpu_helpers import NEAR_TIE_ACCEPT, NEAR_TIE_CDF, THREADS, Tally, f32
 
 pytestmark = pytest.mark.gpu
 
@@ -44,29 +44,50 @@ def test_toy_logits_bit_exact(V, kind, dtype):
     assert np.array_equal(_bits(g), ref)
 
 
-def compare_generation(g: dict, o: dict):
-    """Round by round per request: identical until the oracle's round holds a
-    near tie (accept band or inverse-CDF band), after which the request is not
-    compared. Returns the number of requests cut short."""
+def compare_generation(g: dict, o: dict, name: str = "") -> Tally:
+    """Round by round per request: identical until the first round where the
+    two part, and there the first differing token must come from an oracle
+    near tie. Position 0 of a round is the first token's draw; position j >= 1
+    is draft j - 1 if accepted, else the final token. So a difference at j = 0
+    needs the first draw to be a near tie with the GPU on the token across its
+    near edge; at j >= 1 the draw of draft j - 1 or its accept test must be a
+    near tie, or, where the oracle drew its final token there, that draw (the
+    GPU on the token across its edge). The request is not compared after that
+    round."""
     gs, gl, grt = g["seq"].cpu().numpy(), g["len"].cpu().numpy(), g["round_tokens"].cpu().numpy()
     os_, ol, ort = o["seq"], o["len"], o["round_tokens"]
-    near = (o["margin_acc"] < NEAR_TIE_ACCEPT) | (o["margin_cdf"] < NEAR_TIE_CDF)
-    cut = 0
-    for b in range(len(ol)):
+    B, R = ort.shape
+    t = Tally(name)
+    t.requests = B
+    for b in range(B):
         off = 0
-        for r in range(ort.shape[1]):
+        for r in range(R):
+            n_o = int(o["n"][b, r])
+            ma, md = o["m_acc"][b, r], o["m_draft"][b, r]
+            t.decisions += 2 + int(np.isfinite(ma).sum()) + int(np.isfinite(md).sum())
+            t.near += (int(o["m_first"][b, r] < NEAR_TIE_CDF) + int((ma < NEAR_TIE_ACCEPT).sum())
+                       + int((md < NEAR_TIE_CDF).sum()) + int(o["m_final"][b, r] < NEAR_TIE_CDF))
             n = ort[b, r]
             same = grt[b, r] == n and np.array_equal(gs[b, off:off + n], os_[b, off:off + n])
             if not same:
-                assert near[b, r], (f"request {b} round {r}: gpu {gs[b, off:off + grt[b, r]].tolist()} vs oracle "
-                                    f"{os_[b, off:off + n].tolist()} (margins {o['margin_acc'][b, r]:.3g}, "
-                                    f"{o['margin_cdf'][b, r]:.3g})")
-                cut += 1
+                gr_, or_ = gs[b, off:off + grt[b, r]], os_[b, off:off + n]
+                j = next(i for i in range(max(len(gr_), len(or_)))
+                         if i >= len(gr_) or i >= len(or_) or gr_[i] != or_[i])
+                msg = f"request {b} round {r}: gpu {gr_.tolist()} vs oracle {or_.tolist()}, first difference at {j}"
+                if j == 0:
+                    ok = o["m_first"][b, r] < NEAR_TIE_CDF and gr_[0] == o["alt_first"][b, r]
+                else:
+                    i = j - 1
+                    ok = md[i] < NEAR_TIE_CDF or ma[i] < NEAR_TIE_ACCEPT
+                    if i == n_o and j < len(gr_):
+                        ok = ok or (o["m_final"][b, r] < NEAR_TIE_CDF and gr_[j] == o["alt_final"][b, r])
+                assert ok, msg
+                t.excused += 1
                 break
             off += n
         else:
             assert gl[b] == ol[b] and np.array_equal(gs[b], os_[b])
-    return cut
+    return t
 
 
 def _run(B, block, V, T, rounds, dtype="bf16", seed=1, prompt_seed=0):
@@ -85,12 +106,11 @@ def _run(B, block, V, T, rounds, dtype="bf16", seed=1, prompt_seed=0):
     (4, 2, 500, 1.3, 10, "f32"), (64, 8, 32768, 1.0, 3, "bf16")])
 def test_generate_parity(B, block, V, T, rounds, dtype):
     g, o = _run(B, block, V, f32(T), rounds, dtype)
-    cut = compare_generation(g, o)
-    assert cut <= max(1, B // 16)
+    compare_generation(g, o, name=f"generate B={B} block={block} V={V} T={T}").check()
     rt = g["round_tokens"].cpu().numpy()
     assert rt.min() >= 2 and rt.max() <= block + 1
 
 
 def test_generate_greedy():
     g, o = _run(16, 6, 4096, 0.0, 5, "bf16")
-    assert compare_generation(g, o) == 0
+    assert compare_generation(g, o).excused == 0

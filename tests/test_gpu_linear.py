@@ -1,7 +1,8 @@
 """GPU parity of psispec_verify_linear / psispec_draft_sample against the CPU
 oracle, element by element on the same seeded inputs: accepted lengths and
-tokens bit-exact except counted near ties, probabilities within 1e-5
-relative, residual masses within 1e-9 relative."""
+tokens bit-exact except requests whose first differing decision is an oracle
+near tie (gpu_helpers), counted; probabilities within 1e-5 relative, residual
+masses within 1e-9 relative."""
 from __future__ import annotations
 
 import numpy as np
@@ -10,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import THREADS, compare_linear, f32, to_dev
+from gpu_helpers import THREADS, Tally, compare_drafts, compare_linear, f32, to_dev
 from oracle_helpers import alpha, chi2_pvalue, probs
 
 pytestmark = pytest.mark.gpu
@@ -37,14 +38,11 @@ def _run_pair(p, q, draft, T, seed, step, fused, top_k=0, top_p=1.0):
 def test_tiny_trials_fused():
     """Tiny workload (B=1, K=4, V=1024, fp32, T=1), fused drafts, 300 trials with step = trial."""
     p, q = synth.linear_inputs("tiny", seed=0)
-    ex_total = dec_total = 0
+    tot = Tally("tiny x300")
     for t in range(300):
         g, o = _run_pair(p, q, None, 1.0, 0, t, True)
-        assert np.array_equal(g["draft"].cpu().numpy(), o["draft"]) or o["margin_cdf"][0] < 1e-11
-        ex, dec, _ = compare_linear(g, o)
-        ex_total += ex
-        dec_total += dec
-    assert ex_total <= max(1, 1e-4 * dec_total)
+        tot += compare_linear(g, o, fused=True)
+    tot.check()
 
 
 def test_tiny_replicas_one_call():
@@ -55,45 +53,58 @@ def test_tiny_replicas_one_call():
     p = np.ascontiguousarray(np.repeat(p, B, axis=0))
     q = np.ascontiguousarray(np.repeat(q, B, axis=0))
     g, o = _run_pair(p, q, None, 1.0, 0, 0, True)
-    ex, dec, _ = compare_linear(g, o)
-    assert ex <= max(1, 1e-4 * dec)
+    compare_linear(g, o, fused=True, name="tiny 2000 replicas").check()
 
 
 @pytest.mark.parametrize("rho", [0.5, 0.8, 0.95])
 def test_highconc_full_size(rho):
     """High-concurrency workload at full size (B=256, K=8, V=151936, bf16, T=1)
-    in the benchmark's launch configuration, drafts drawn by the oracle."""
+    in the benchmark's launch configuration, over steps 0..19: the drafts of
+    each step drawn on the GPU (psispec_draft_sample, 2048 draws) and checked
+    against the oracle's, then verified on both sides from the GPU's drafts.
+    Near ties must make up less than 1e-4 of the decisions."""
+    psi = _psi()
     p, q = synth.linear_inputs("highconc", seed=0, rho=rho)
-    ex_total = dec_total = 0
-    for step in range(2):
-        d, _ = oracle.draft_sample(q, 1.0, seed=0, step=step, nthreads=THREADS)
-        g, o = _run_pair(p, q, d, 1.0, 0, step, False)
-        ex, dec, _ = compare_linear(g, o)
-        ex_total += ex
-        dec_total += dec
-    assert ex_total <= max(1, 1e-4 * dec_total)
+    pd, qd = to_dev(p), to_dev(q)
+    td, tv = Tally(f"highconc rho {rho} drafts"), Tally(f"highconc rho {rho} verify")
+    for step in range(20):
+        gd = psi.draft_sample(qd, temperature=1.0, seed=0, step=step)
+        g = psi.verify_linear(pd, qd, gd, temperature=1.0, seed=0, step=step)
+        torch.cuda.synchronize()
+        od, om = oracle.draft_sample(q, 1.0, seed=0, step=step, nthreads=THREADS)
+        td += compare_drafts(gd, od, om)
+        d = gd.cpu().numpy()
+        o = oracle.verify_linear(p, q, d, 1.0, seed=0, step=step, nthreads=THREADS)
+        tv += compare_linear(g, o)
+    td.check(near_fraction=True)
+    tv.check(near_fraction=True)
+    both = Tally(f"highconc rho {rho}")
+    both += td
+    both += tv
+    both.check(near_fraction=True)
+    assert both.decisions >= 40960
 
 
 def test_qwen_fused_full_size():
-    """Qwen3-8B-shaped workload (B=64, K=8, V=151936, bf16, T=0.7) with fused drafts."""
+    """Qwen3-8B-shaped workload (B=64, K=8, V=151936, bf16, T=0.7) with fused drafts, 4 steps."""
     p, q = synth.linear_inputs("qwen", seed=0)
-    g, o = _run_pair(p, q, None, 0.7, 0, 3, True)
-    gd = g["draft"].cpu().numpy()
-    mism = np.nonzero(gd != o["draft"])[0]
-    assert all(o["margin_cdf"][b] < 1e-11 for b in mism)
-    ex, dec, _ = compare_linear(g, o)
-    assert ex <= max(1, 1e-4 * dec)
+    tot = Tally("qwen fused x4")
+    for step in range(4):
+        g, o = _run_pair(p, q, None, 0.7, 0, 3 + step, True)
+        tot += compare_linear(g, o, fused=True)
+    tot.check()
 
 
 def test_draft_sample_parity():
     psi = _psi()
+    tot = Tally("draft sample")
     for (wl, T, B) in [("tiny", 1.0, 64), ("qwen", 0.7, 8)]:
         p, q = synth.linear_inputs(wl, seed=1, B=B)
         for step in range(3):
-            g = psi.draft_sample(to_dev(q), temperature=T, seed=7, step=step).cpu().numpy()
-            o, mg = oracle.draft_sample(q, f32(T), seed=7, step=step, nthreads=THREADS)
-            bad = g != o
-            assert np.all(mg[bad] < 1e-11), (np.argwhere(bad), mg[bad])
+            g = psi.draft_sample(to_dev(q), temperature=T, seed=7, step=step)
+            o, om = oracle.draft_sample(q, f32(T), seed=7, step=step, nthreads=THREADS)
+            tot += compare_drafts(g, o, om)
+    tot.check()
 
 
 def test_fused_equals_draft_then_verify():
@@ -131,10 +142,11 @@ def test_ragged_and_unaligned_vocab(dtype, V):
     chunk (unaligned path, ragged tails, V = 1)."""
     B, K = 24, 3
     p, q = synth.pair(B, K + 1, K, V, dtype, seed=9, sd_a=2.0, mode=0, sd_noise=0.7)
+    tot = Tally(f"ragged {dtype} V={V}")
     for step in range(2):
         g, o = _run_pair(p, q, None, 1.0, 3, step, True)
-        ex, dec, _ = compare_linear(g, o)
-        assert ex <= 1
+        tot += compare_linear(g, o, fused=True)
+    tot.check()
 
 
 @pytest.mark.parametrize("K", [1, 64])
@@ -142,8 +154,7 @@ def test_k_extremes(K):
     B, V = 8, 2048
     p, q = synth.pair(B, K + 1, K, V, "bf16", seed=K, sd_a=1.0, mode=1, rho=0.98, sd_noise=1.0)
     g, o = _run_pair(p, q, None, 1.0, 0, 0, True)
-    ex, dec, _ = compare_linear(g, o)
-    assert ex <= 1
+    compare_linear(g, o, fused=True, name=f"K={K}").check()
 
 
 def test_request_errors_and_special_rows():
@@ -164,7 +175,7 @@ def test_request_errors_and_special_rows():
     assert list(gl[[1, 2, 3, 4, 7]]) == [-1] * 5
     assert np.all(g["tokens"].cpu().numpy()[[1, 2, 3, 4, 7]] == -1)
     assert gl[6] == K
-    compare_linear(g, o)
+    compare_linear(g, o, name="request errors").check()
 
 
 def _bf16_bits(f: np.ndarray) -> np.ndarray:
@@ -205,18 +216,23 @@ def test_bf16_weight_window_edges(T):
             fp[b] *= np.float32(0.25)
             fq[b] *= np.float32(0.25)
     p, q = _bf16_bits(fp), _bf16_bits(fq)
+    tot = Tally(f"bf16 window edges T={T}")
     for step in range(3):
         g, o = _run_pair(p, q, None, T, 4, step, True)
-        ex, dec, _ = compare_linear(g, o)
-        assert ex <= 1
+        tot += compare_linear(g, o, fused=True)
         assert int((o["len"] < K).sum()) > 0  # residual draws happen
+    tot.check()
 
 
 def test_greedy_parity():
-    """Greedy mode (temperature 0) on the filtered/greedy workload shape, fused
-    drafts (argmax of q) and given drafts."""
-    p, q = synth.linear_inputs("greedy", seed=0, B=32)
+    """Greedy mode (temperature 0) on the filtered/greedy workload at full size
+    (B=128, K=16, V=128256, fp32): fused drafts (argmax of q), then given
+    drafts with a fifth of them replaced. Argmaxes compare exact values, so
+    everything must match exactly."""
+    p, q = synth.linear_inputs("greedy", seed=0)
+    assert p.shape == (128, 17, 128256)
     g, o = _run_pair(p, q, None, 0.0, 0, 0, True)
+    assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
     assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
     assert np.array_equal(g["len"].cpu().numpy(), o["len"])
     rng = np.random.default_rng(0)
@@ -227,6 +243,7 @@ def test_greedy_parity():
     assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
     assert np.array_equal(g["len"].cpu().numpy(), o["len"])
     assert np.array_equal(g["probs"].cpu().numpy(), o["probs"].astype(np.float32))
+    assert 0 < int((o["len"] < 16).sum()) < 128
 
 
 def test_gpu_law_many_replicas():

@@ -8,20 +8,25 @@ from __future__ import annotations
 import numpy as np
 import pytest
 import torch
+from scipy.special import softmax
 
 import oracle
 import synth
-from gpu_helpers import THREADS, f32
+from gpu_helpers import THREADS, Tally, f32
 
 pytestmark = pytest.mark.gpu
 
 # The GPU's logits carry the fp32 accumulation error of an H-term dot product
-# of bf16 values (~sqrt(H) 2^-24 times the partial sums, about 1e-5 absolute
-# at H = 4096 for these inputs), so a ratio P/Q moves by about 2e-5 relative
-# and a cumulative position by about 1e-5 of the mass: decisions whose oracle
-# margin is inside these bands may differ.
-BAND_ACC = 1e-4
-BAND_CDF = 1e-4
+# of bf16 values, bounded in tests/test_lmhead_error.py by emulating fp32
+# accumulation on the CPU: at most 5e-5 absolute at H = 4096 for these inputs,
+# summing one product at a time). A probability moves by at most twice that,
+# relative, and a ratio P/Q or a CDF edge by at most four times that, so an
+# accept test may differ only where |u - min(1, P/Q)| < BAND_ACC, and a final
+# draw may land on any token whose interval of the oracle's CDF comes within
+# BAND_CDF of the mass of u*W (the draw is then checked for validity, not
+# identity).
+BAND_ACC = 2.5e-4
+BAND_CDF = 2.5e-4
 
 
 def _psi():
@@ -49,42 +54,66 @@ def inputs(B, K, H, V, seed, sd_w=0.05, noise=0.3):
     return _bf16(ht), _bf16(hd), _bf16(w)
 
 
-def check(B, K, H, V, T, seed, steps=3):
+def _final_weights(zp, zq, b, n, K, T):
+    """The oracle's final-draw weights of request b (fp64, from its logits)."""
+    P = softmax(zp[b, n].astype(np.float64) / T)
+    if n == K:
+        return P
+    w = np.maximum(P - softmax(zq[b, n].astype(np.float64) / T), 0.0)
+    return w if w.sum() > 0 else P
+
+
+def check(B, K, H, V, T, seed, steps=3) -> Tally:
+    """Per request: the GPU's accepted length equals the oracle's unless the
+    first accept test where they part is within BAND_ACC; with equal lengths,
+    the GPU's final token is the oracle's, or one whose CDF interval lies
+    within BAND_CDF of the oracle's target mass u*W."""
     psi = _psi()
     ht, hd, w = inputs(B, K, H, V, seed)
     zp = oracle.lmhead_logits(ht, w)
     zq = oracle.lmhead_logits(hd, w)
     dt, dd, dw = _dev(ht), _dev(hd), _dev(w)
-    excused = decisions = 0
+    t = Tally(f"lmhead B={B} K={K} H={H} V={V} T={T}")
     for step in range(steps):
         x, _ = oracle.draft_sample(zq, T, seed=seed, step=step, nthreads=THREADS)
         g = psi.verify_lmhead(dt, dd, dw, torch.from_numpy(x).cuda(), temperature=T, seed=seed, step=step)
         torch.cuda.synchronize()
         o = oracle.verify_linear(zp, zq, x, T, seed=seed, step=step, nthreads=THREADS)
         gl, gt = g["len"].cpu().numpy(), g["tokens"].cpu().numpy()
+        t.requests += B
         for b in range(B):
-            decisions += 1
+            ma, mf = o["m_acc"][b], o["m_final"][b]
+            t.decisions += int(np.isfinite(ma).sum()) + 1
+            t.near += int((ma < BAND_ACC).sum()) + int(mf < BAND_CDF)
             if gl[b] == o["len"][b] and np.array_equal(gt[b], o["tokens"][b]):
                 continue
-            assert o["margin_acc"][b] < BAND_ACC or o["margin_cdf"][b] < BAND_CDF, (
-                f"request {b} step {step}: gpu {gl[b]} {gt[b].tolist()} vs oracle {o['len'][b]} "
-                f"{o['tokens'][b].tolist()} (margins {o['margin_acc'][b]:.3g} {o['margin_cdf'][b]:.3g})")
-            excused += 1
-    return excused, decisions
+            msg = (f"request {b} step {step}: gpu {gl[b]} {gt[b].tolist()} vs oracle {o['len'][b]} "
+                   f"{o['tokens'][b].tolist()} (accept margins {ma.tolist()})")
+            if gl[b] != o["len"][b]:
+                i = min(int(gl[b]), int(o["len"][b]))
+                assert ma[i] < BAND_ACC, msg
+                t.excused += 1
+                continue
+            n = int(gl[b])
+            wts = _final_weights(zp, zq, b, n, K, T)
+            C = np.cumsum(wts) / wts.sum()
+            u = oracle.uniform(seed, step, b, n, 0)
+            j = int(gt[b, n])
+            lo, hi = (C[j - 1] if j else 0.0), C[j]
+            assert wts[j] > 0 and lo - BAND_CDF <= u < hi + BAND_CDF, msg + f"; final token {j} at [{lo}, {hi}), u {u}"
+    return t
 
 
 @pytest.mark.parametrize("B,K,H,V,T,seed", [
     (3, 4, 128, 3000, 1.0, 0), (5, 8, 256, 4096, 0.7, 1), (2, 1, 64, 700, 1.0, 2), (7, 3, 192, 257, 1.3, 3),
     (20, 8, 512, 32768, 1.0, 4)])
 def test_lmhead_parity(B, K, H, V, T, seed):
-    excused, decisions = check(B, K, H, V, f32(T), seed)
-    assert excused <= max(1, decisions // 50)
+    check(B, K, H, V, f32(T), seed).check()
 
 
 def test_lmhead_qwen_shape():
-    """Qwen3-8B head: H = 4096, V = 151,936, four requests of K = 8."""
-    excused, decisions = check(4, 8, 4096, 151936, 1.0, 5, steps=2)
-    assert excused <= 1
+    """Qwen3-8B head: H = 4096, V = 151,936, 64 requests of K = 8, two steps."""
+    check(64, 8, 4096, 151936, 1.0, 5, steps=2).check()
 
 
 def test_lmhead_rejects_bad_shapes():
