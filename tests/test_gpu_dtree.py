@@ -281,7 +281,7 @@ def test_verify_det_chained_on_device():
     g = psi.verify_tree_det(pd, cand["parent"], cand["tokens"], temperature=T, seed=1, step=2)
     torch.cuda.synchronize()
     o = oracle.verify_tree_det(p, op, ot, T, seed=1, step=2, nthreads=THREADS)
-    compare_tree(g, o).check()
+    compare_tree(g, o, name="det verify").check()
 
 
 def test_verify_det_greedy():
@@ -308,7 +308,7 @@ def test_verify_det_errors():
         gl = g["len"].cpu().numpy()
         assert list(gl[1:5]) == [-1] * 4 and gl[0] >= 0 and gl[5] >= 0
         assert np.all(g["tokens"].cpu().numpy()[1:5] == -1)
-        compare_tree(g, o).check()
+        compare_tree(g, o, name="det verify").check()
 
 
 def test_verify_det_first_token_law():

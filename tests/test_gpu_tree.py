@@ -93,7 +93,7 @@ def test_tree_topologies(topo, dtype, V, T, noise):
     rejected = 0
     for step in range(4):
         g, o = _case(p, q, parent, T=T, seed=3, step=step)
-        compare_tree(g, o).check()
+        compare_tree(g, o, name="tree").check()
         rejected += int(np.sum(o["len"] < oracle.tree_depth(parent)))
     assert rejected > 0
 
@@ -107,7 +107,7 @@ def test_tree_given_nodes():
     for step in range(3):
         nodes = synth.randint(40 + step, 0, B * N, V).reshape(B, N)
         g, o = _case(p, q, parent, seed=8, step=step, nodes=nodes)
-        compare_tree(g, o).check()
+        compare_tree(g, o, name="tree").check()
 
 
 def test_chain_tree_matches_linear_gpu():
@@ -148,7 +148,7 @@ def test_tree_filtered(top_k, top_p):
     p, q = synth.pair(B, N + 1, N + 1, V, "f32", seed=top_k, sd_a=2.0, mode=0, sd_noise=0.8)
     for step in range(3):
         g, o = _case(p, q, parent, T=1.0, top_k=top_k, top_p=top_p, seed=2, step=step)
-        compare_tree(g, o).check()
+        compare_tree(g, o, name="tree").check()
 
 
 def test_tree_errors():
@@ -163,10 +163,10 @@ def test_tree_errors():
     g, o = _case(p, q, parent, nodes=nodes)
     gl = g["len"].cpu().numpy()
     assert list(gl[[1, 2, 3, 4]]) == [-1] * 4 and gl[0] >= 0 and gl[5] >= 0
-    compare_tree(g, o).check()
+    compare_tree(g, o, name="tree").check()
     g, o = _case(p, q, parent)  # fused: request 2 has no valid drafts
     assert np.all(g["nodes"].cpu().numpy()[2] == -1)
-    compare_tree(g, o).check()
+    compare_tree(g, o, name="tree").check()
 
 
 def test_tree_first_token_law():
