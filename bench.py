@@ -84,23 +84,78 @@ def pmc_traffic():
         return None
 
 
-def cpu_baseline(p, q, drafts, seed, budget_s=10.0, threads=16):
+def host_cpu():
+    """Host cores this process may use, and the CPU model."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def cpu_baseline(p, q, drafts, seed, budget_s=10.0):
     """Times the CPU oracle (test infrastructure, never tuned) on whole verify
-    calls of the same workload until about budget_s seconds have passed."""
+    calls of the same workload, threads across requests on every host core,
+    until about budget_s seconds have passed; then one thread on a slice of 16
+    requests for a single-core figure."""
     import oracle
 
+    cores, model = host_cpu()
     steps = 0
     t0 = time.perf_counter()
     while True:
-        s = steps % len(drafts)
-        oracle.verify_linear(p, q, drafts[s], T, seed=seed, step=s, nthreads=threads)
+        s_ = steps % len(drafts)
+        oracle.verify_linear(p, q, drafts[s_], T, seed=seed, step=s_, nthreads=cores)
         steps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     wall = time.perf_counter() - t0
-    return {"value": B * K * steps / wall, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} full verify calls (B={B}, K={K}, V={V}, bf16, rho=0.8), {threads} threads, "
-                      f"{wall:.1f} s wall"}
+    Bs = 16
+    t1 = time.perf_counter()
+    oracle.verify_linear(p[:Bs], q[:Bs], drafts[0][:Bs], T, seed=seed, step=0, nthreads=1)
+    one = time.perf_counter() - t1
+    return {"value": B * K * steps / wall, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} full verify calls (B={B}, K={K}, V={V}, bf16, rho=0.8) on {cores} threads, "
+                      f"{wall:.1f} s wall",
+            "cpu_model": model, "nproc": os.cpu_count(),
+            "single_thread_rows_per_s": Bs * K / one,
+            "single_thread_sample": f"one verify call of {Bs} requests on 1 thread, {one:.2f} s"}
+
+
+def decision_sample(p, q, drafts, seed, steps, gpu_len, gpu_tokens, cores):
+    """The oracle on `steps` decode steps of one rho: mean acceptance
+    probability alpha = sum_j min(P_j, Q_j) over the drafted positions, and
+    the GPU's decisions against the oracle's (decisions taken, oracle near
+    ties among them, requests whose outputs differ)."""
+    import oracle
+    from scipy.special import softmax
+
+    dec = near = differ = 0
+    for t in range(steps):
+        o = oracle.verify_linear(p, q, drafts[t], T, seed=seed, step=t, nthreads=cores)
+        ma, mf = o["m_acc"], o["m_final"]
+        dec += int(np.isfinite(ma).sum() + np.isfinite(mf).sum())
+        near += int((ma < 1e-6).sum() + (mf < 1e-11).sum())
+        differ += int(np.sum((o["len"] != gpu_len[t]) | np.any(o["tokens"] != gpu_tokens[t], axis=1)))
+    # alpha over a sample of 128 positions (fp64 softmaxes of the bfloat16 logits)
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(B * K, size=128, replace=False)
+    f32 = lambda h: (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    al = []
+    for r in idx:
+        b_, i_ = divmod(int(r), K)
+        al.append(np.minimum(softmax(f32(p[b_, i_]) / T), softmax(f32(q[b_, i_]) / T)).sum())
+    return {"mean_alpha": float(np.mean(al)), "alpha_sample_positions": 128, "oracle_steps": steps,
+            "decisions": dec, "near_ties": near, "requests_differing": differ}
 
 
 def to_dev(a, torch, dev):
@@ -366,40 +421,56 @@ def main():
     steps, warm = args.steps, args.warmup
     ws = torch.empty(psi.workspace_bytes(B, 2 * K + 1, V, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(psi.workspace_bytes(B, K, V, psi.DTYPE_BF16), dtype=torch.uint8, device=dev)
-    out_tokens = torch.empty((steps + warm, B, K + 1), dtype=torch.int32, device=dev)
-    out_len = torch.empty((steps + warm, B), dtype=torch.int32, device=dev)
     out_probs = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
     out_resid = torch.empty((B,), dtype=torch.float64, device=dev)
-    drafts = torch.empty((steps + warm, B, K), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
-    nb = max(1, min(args.breakdown_steps, steps))
+    nb = max(1, args.breakdown_steps)
     timer = psi.KernelTimer(nb * len(RHOS), len(LINEAR_KERNELS) + 1)
+
+    # Every input is staged before any timing: the three rho workloads in HBM
+    # (3 x 1.32 GB) and their pre-drawn draft sets (set t is used at step t).
+    # The GPU then runs each rho's per-kernel breakdown, warm-up and timed
+    # calls back to back with no host work between them: after even 0.1 s of
+    # idle the first ~100 calls run 10-30% slow while the clocks ramp up, which
+    # a serving loop that never idles does not see.
+    host, dev_in = {}, {}
+    for rho in RHOS:
+        p_np = np.empty((B, K + 1, V), dtype=np.uint16)
+        q_np = np.empty((B, K, V), dtype=np.uint16)
+        synth.pair(B, K + 1, K, V, "bf16", seed=args.seed, out_p=p_np, out_q=q_np,
+                   **{**synth.RECIPES["highconc"], "rho": rho})
+        host[rho] = (p_np, q_np)
+        dev_in[rho] = (to_dev(p_np, torch, dev), to_dev(q_np, torch, dev))
+    n_calls = steps + warm
+    drafts = {rho: torch.empty((n_calls, B, K), dtype=torch.int32, device=dev) for rho in RHOS}
+    out_tokens = {rho: torch.empty((n_calls, B, K + 1), dtype=torch.int32, device=dev) for rho in RHOS}
+    out_len = {rho: torch.empty((n_calls, B), dtype=torch.int32, device=dev) for rho in RHOS}
+    for rho in RHOS:
+        _, q = dev_in[rho]
+        for t in range(n_calls):
+            psi.draft_sample(q, temperature=T, seed=args.seed, step=t, out=drafts[rho][t], workspace=ws_d)
+    torch.cuda.synchronize()
 
     per_rho = []
     total_rows = 0
     total_time = 0.0
     total_emitted = 0
     call_ms = []
-    host_inputs = None
-    p_np = np.empty((B, K + 1, V), dtype=np.uint16)
-    q_np = np.empty((B, K, V), dtype=np.uint16)
     for ri, rho in enumerate(RHOS):
-        synth.pair(B, K + 1, K, V, "bf16", seed=args.seed, out_p=p_np, out_q=q_np,
-                   **{**synth.RECIPES["highconc"], "rho": rho})
-        p = to_dev(p_np, torch, dev)
-        q = to_dev(q_np, torch, dev)
-        # pre-drawn draft sets (untimed): set t is used at step t
-        for t in range(steps + warm):
-            psi.draft_sample(q, temperature=T, seed=args.seed, step=t, out=drafts[t], workspace=ws_d)
-        torch.cuda.synchronize()
-        if rho == 0.8 and not args.no_cpu_baseline:
-            host_inputs = (p_np.copy(), q_np.copy(), drafts[:64].cpu().numpy())
+        p, q = dev_in[rho]
+        dr, ot, ol = drafts[rho], out_tokens[rho], out_len[rho]
 
         def call(t):
-            psi.verify_linear(p, q, drafts[t], temperature=T, seed=args.seed, step=t,
-                              out=dict(tokens=out_tokens[t], len=out_len[t], probs=out_probs, resid=out_resid),
+            psi.verify_linear(p, q, dr[t], temperature=T, seed=args.seed, step=t,
+                              out=dict(tokens=ot[t], len=ol[t], probs=out_probs, resid=out_resid),
                               workspace=ws, stream=stream)
 
+        # per-kernel breakdown (untimed): the library records an event around each launch
+        for i in range(nb):
+            timer.arm(ri * nb + i)
+            call(i % n_calls)
+            timer.note()
+        timer.disarm()
         for t in range(warm):
             call(t)
         torch.cuda.synchronize()
@@ -413,16 +484,9 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ev_ms = ev0.elapsed_time(ev1)
-        lens = out_len[warm:warm + steps].cpu().numpy()
+        lens = ol[warm:warm + steps].cpu().numpy()
         assert (lens >= 0).all()
         emitted = int((lens + 1).sum())
-        # per-kernel breakdown: the library records an event around each launch
-        for i in range(nb):
-            timer.arm(ri * nb + i)
-            call(warm + i)
-            timer.note()
-        timer.disarm()
-        torch.cuda.synchronize()
         per_rho.append({"rho": rho, "ms_per_step": 1e3 * wall / steps, "event_ms_per_step": ev_ms / steps,
                         "rows_per_s": B * K * steps / wall, "emitted_tok_per_s": emitted / wall,
                         "mean_accepted": float(lens.mean()), "mean_emitted": float((lens + 1).mean())})
@@ -432,9 +496,8 @@ def main():
         total_rows += B * K * steps
         total_time += wall
         total_emitted += emitted
-        del p, q
-        torch.cuda.empty_cache()
 
+    drafts_host_08 = drafts[0.8][:64].cpu().numpy() if not args.no_cpu_baseline else None
     dur = timer.durations()  # [calls, kernels] ms
     kmean = np.nanmean(dur, axis=0)
     kernels = {name: {"us_mean": 1e3 * float(kmean[j]), "us_median": 1e3 * float(np.nanmedian(dur[:, j]))}
@@ -472,10 +535,37 @@ def main():
         "kernels": kernels,
         "per_rho": per_rho,
     }
+    # Which rho reaches the pages' Linear B=8 operating point, TPF 2.2, i.e.
+    # about 4.4 emitted tokens per verification at K = 8 ("Uno" explainer,
+    # sampler ablation): mean emitted over 16 calls of 64 requests per rho.
+    sweep = []
+    for rho in (0.95, 0.97, 0.98, 0.99, 0.995):
+        Bs = 64
+        ps, qs = synth.pair(Bs, K + 1, K, V, "bf16", seed=args.seed, **{**synth.RECIPES["highconc"], "rho": rho})
+        pd, qd = to_dev(ps, torch, dev), to_dev(qs, torch, dev)
+        em = []
+        for t in range(16):
+            g = psi.verify_linear(pd, qd, None, temperature=T, seed=args.seed, step=t, fused=True)
+            em.append(float((g["len"].float() + 1).mean().item()))
+        sweep.append({"rho": rho, "mean_emitted": float(np.mean(em))})
+        del pd, qd
+    best = min(sweep, key=lambda r: abs(r["mean_emitted"] - 4.4))
+    result["tpf_sweep"] = {"target_mean_emitted": 4.4, "rho_closest": best["rho"], "points": sweep,
+                           "note": "fused drafts, 64 requests x 16 calls per rho"}
+
+    if not args.no_cpu_baseline:
+        cores, _ = host_cpu()
+        for e, rho in zip(per_rho, RHOS):
+            p_np, q_np = host[rho]
+            e.update(decision_sample(p_np, q_np, drafts[rho][:2].cpu().numpy(), args.seed, 2,
+                                     out_len[rho][:2].cpu().numpy(), out_tokens[rho][:2].cpu().numpy(), cores))
     if not args.no_workloads:
+        del dev_in, drafts, out_tokens, out_len
+        torch.cuda.empty_cache()
         result["workloads"] = other_workloads(torch, psi, synth, dev, stream, args.workload_steps, args.seed)
-    if host_inputs is not None:
-        result["cpu_baseline"] = cpu_baseline(host_inputs[0], host_inputs[1], host_inputs[2], args.seed,
+    if not args.no_cpu_baseline:
+        p_np, q_np = host[0.8]
+        result["cpu_baseline"] = cpu_baseline(p_np, q_np, list(drafts_host_08), args.seed,
                                               budget_s=args.cpu_budget)
     print(json.dumps(result), flush=True)
 

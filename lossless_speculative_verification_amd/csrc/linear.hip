@@ -84,11 +84,14 @@ __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool 
 // keeps the next two sub-blocks in flight, fp32 the next one. TAB: weights
 // are read from the pre-scaled LDS tables tp / tq (bfloat16 only), whose
 // values estimate the probabilities, so the target part is above the draft
-// part where ep > eq; otherwise where a_p - a_q > dx.
-template <int DT, bool AL, bool TAB, bool RESID, bool PICK, int NW = kRWaves>
+// part where ep > eq; otherwise where a_p - a_q > dx. pre() runs once on
+// every thread of the workgroup after each wave has issued the loads of its
+// first sub-blocks and before any weight is read, so that work it does (the
+// tables' scaling, and the barrier after it) hides under their latency.
+template <int DT, bool AL, bool TAB, bool RESID, bool PICK, int NW = kRWaves, class PRE>
 __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
                                              int sb0, int sb1, const double* tp, const double* tq, const WRow& wp,
-                                             const WRow& wq, float dx, ResRec* s_rec) {
+                                             const WRow& wq, float dx, ResRec* s_rec, PRE pre) {
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec;
   constexpr int VPL = kSB / (kWave * EPV);
@@ -191,10 +194,13 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
   constexpr int W = NW;
   Buf x0, x1, x2;
   int s = sb0 + wave;
+  if (s < sb1) {
+    load(s, x0);
+    if constexpr (NBUF == 3) load(s + W, x1);
+  }
+  pre();
   if (s >= sb1) return;
-  load(s, x0);
   if constexpr (NBUF == 3) {
-    load(s + W, x1);
     for (; s < sb1; s += 3 * W) {
       load(s + 2 * W, x2);
       reduce(s, x0);
@@ -216,11 +222,81 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
   }
 }
 
+// The 16 consecutive logits j0 .. j0+15 of one row as raw 16-byte vectors
+// (the aligned path; elements past V read as -inf), so that their loads can be
+// issued before their weights are needed.
+template <int DT>
+struct Raw16 {
+  uint4 v[16 / Elem<DT>::kPerVec];
+};
+template <int DT, bool AL>
+__device__ __forceinline__ void raw16(const LinCfg& c, const char* row, int64_t j0, Raw16<DT>& r) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  constexpr int NV = 16 / EPV;
+  if constexpr (AL) {
+    // unconditional loads (indices clamped into the row; weights16 zeroes
+    // elements past V), so that no branch makes the compiler wait for them
+    const uint4* rp = (const uint4*)row;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) r.v[v] = rp[min(j0 / EPV + v, (int64_t)c.nvec - 1)];
+  } else {
+    load_raw<DT, false, NV, 1>(row, c.V, c.nvec, j0 / EPV, r.v);
+  }
+}
+// Weights of the 16 logits held in r (0 past V), under the rule of fweight;
+// bfloat16 rows with the pre-scaled table read it without branches, and the
+// rare logits below its window are redone out of line.
+template <int DT>
+__device__ __forceinline__ void weights16(const LinCfg& c, const Raw16<DT>& r, int64_t j0, const WRow& w,
+                                          const double* tab_scaled, double (&out)[16]) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  if constexpr (DT == kBF16) {
+    if (w.tab && tab_scaled) {
+      uint32_t low = 0;
+      const char* const tb = (const char*)tab_scaled;
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t o = tab_offsets2(word_of(r.v[v], i), low);
+          out[v * 8 + 2 * i] = *(const double*)(tb + (o & 0xffffu));
+          out[v * 8 + 2 * i + 1] = *(const double*)(tb + (o >> 16));
+        }
+      if (__ballot((low & 0x80008000u) != 0u)) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          float x[EPV];
+          E::unpack(r.v[v], x);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e)
+            if (tab_tiny(__float_as_uint(x[e]) >> 16)) out[v * EPV + e] = tiny_weight(x[e], c.c64, w.scale);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (j0 + k >= c.V) out[k] = 0.0;
+      return;
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 16 / EPV; ++v) {
+    float x[EPV];
+    E::unpack(r.v[v], x);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const int k = v * EPV + e;
+      out[k] = j0 + k < c.V ? fweight<DT>(x[e], w, c.c64, tab_scaled) : 0.0;
+    }
+  }
+}
+
 // Weights of the 16 consecutive logits j0 .. j0+15 of one row (0 past V), for
 // the rescan of the final pick: one or two 16-byte loads when aligned.
 template <int DT, bool AL>
 __device__ __forceinline__ void row16(const LinCfg& c, const char* row, int64_t j0, const WRow& w,
-                                      const double* tab_scaled, double (&out)[16]) {
+                                      const double* tab, double (&out)[16]) {
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec;
   if (AL && j0 + 16 <= c.V) {
@@ -230,11 +306,11 @@ __device__ __forceinline__ void row16(const LinCfg& c, const char* row, int64_t 
       float x[EPV];
       E::unpack(rp[v], x);
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) out[v * EPV + e] = fweight<DT>(x[e], w, c.c64, tab_scaled);
+      for (int e = 0; e < EPV; ++e) out[v * EPV + e] = fweight<DT>(x[e], w, c.c64, tab);
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) out[k] = j0 + k < c.V ? fweight<DT>(E::load1(row, j0 + k), w, c.c64, tab_scaled) : 0.0;
+    for (int k = 0; k < 16; ++k) out[k] = j0 + k < c.V ? fweight<DT>(E::load1(row, j0 + k), w, c.c64, tab) : 0.0;
   }
 }
 
@@ -255,8 +331,8 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   __shared__ float s_m[2 * kMaxK + 1];
   __shared__ double s_S[2 * kMaxK + 1];
   __shared__ int s_bad, s_n;
-  // the 2^(a c) table, then the same multiplied by 2^(-m_p c) (first half)
-  // and by 2^(-m_q c) (second half) once the final rows are known
+  // the 2^(a c) table, then the same multiplied by the scale of the final
+  // target row (first half) and of the final draft row (second half)
   __shared__ double s_tab[2 * kTabSize];
   const bool tab = DT == kBF16 && c.tab;
 
@@ -341,7 +417,8 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   wpair(tab, mp, mq, resid, c64, wp, wq);
   norm_pair(wp, wq, resid, sph, sqh);
   // target part above draft part (ep / sph > eq / sqh) <=> a_p - a_q > dx
-  const float dx = (float)((::log2(sph) - ::log2(sqh) + wp.mc - wq.mc) / c64);
+  // (the rule of rows without the table)
+  const float dx = wp.tab ? 0.0f : (float)((::log2(sph) - ::log2(sqh) + wp.mc - wq.mc) / c64);
   const double u_final = c.rng.u((uint32_t)b, (uint32_t)n, kDrawFinal);
   if (!PICK && part == 0 && t == 0) {
     ReqState st = {};
@@ -354,30 +431,39 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
     st.u_final = u_final;
     c.rs[b] = st;
   }
+
+  // ---- fp64 pass over this part's sub-blocks; the tables are scaled while
+  // the first loads of the pass are in flight
   double* const tabp = s_tab;
   double* const tabq = s_tab + kTabSize;
-  if (DT == kBF16 && wp.tab) {
-    for (int i = t; i < kTabSize; i += kRT) {
-      const double e = s_tab[i];
-      if (resid) tabq[i] = e * wq.scale;
-      tabp[i] = e * wp.scale;
+  auto scale_tables = [&]() {
+    if (DT == kBF16 && wp.tab) {
+      for (int i = t; i < kTabSize; i += kRT) {
+        const double e = s_tab[i];
+        if (resid) tabq[i] = e * wq.scale;
+        tabp[i] = e * wp.scale;
+      }
     }
     __syncthreads();
-  }
-
-  // ---- fp64 pass over this part's sub-blocks
+  };
   const char* prow = prow_of(c, b, n);
   const char* qrow = resid ? qrow_of(c, b, n) : prow;
   const int nsb = c.nsb;
   const int sb0 = (int)((int64_t)part * nsb / parts), sb1 = (int)((int64_t)(part + 1) * nsb / parts);
   if (resid) {
     if (DT == kBF16 && wp.tab)
-      resolve_pass<DT, AL, DT == kBF16, true, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec);
-    else resolve_pass<DT, AL, false, true, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec);
+      resolve_pass<DT, AL, DT == kBF16, true, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec,
+                                                    scale_tables);
+    else
+      resolve_pass<DT, AL, false, true, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec,
+                                              scale_tables);
   } else {
     if (DT == kBF16 && wp.tab)
-      resolve_pass<DT, AL, DT == kBF16, false, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec);
-    else resolve_pass<DT, AL, false, false, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec);
+      resolve_pass<DT, AL, DT == kBF16, false, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec,
+                                                     scale_tables);
+    else
+      resolve_pass<DT, AL, false, false, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec,
+                                               scale_tables);
   }
   if constexpr (PICK) {
     __syncthreads();
@@ -385,37 +471,63 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
     if (wave != 0) return;
     const double* const tps = wp.tab ? tabp : nullptr;
     const double* const tqs = wq.tab ? tabq : nullptr;
-    double resid_mass = 0.0;
-    int y;
-    if (resid) {
-      double sa = 0.0, sb_ = 0.0;
-      for (int i = lane; i < nsb; i += kWave) {
-        sa += s_rec[i].sp;
-        sb_ += s_rec[i].sq;
-      }
-      const double iSp = 1.0 / wave_sum(sa), iSq = 1.0 / wave_sum(sb_);
-      double mine = 0.0;
-      for (int i = lane; i < nsb; i += kWave) mine += fmax(0.0, s_rec[i].a * iSp - s_rec[i].bq * iSq);
-      resid_mass = wave_sum(mine);
-      if (resid_mass > 0.0) {
-        y = wave_pick(
-            nsb, c.V, u_final * resid_mass, [&](int i) { return fmax(0.0, s_rec[i].a * iSp - s_rec[i].bq * iSq); },
-            [&](int64_t j0, double(&w)[16]) {
-              double wq16[16];
-              row16<DT, AL>(c, prow, j0, wp, tps, w);
-              row16<DT, AL>(c, qrow, j0, wq, tqs, wq16);
-#pragma unroll
-              for (int k = 0; k < 16; ++k) w[k] = fmax(0.0, w[k] * iSp - wq16[k] * iSq);
-            });
-      }
+    // Lane l owns a run of consecutive sub-blocks. The scaled sums estimate
+    // probabilities, so the sub-block of the draw is known (except within
+    // ~1e-7 of a sub-block edge) before the exact totals: its logits are
+    // loaded while those are reduced, and loaded again in the rare case that
+    // the exact selection differs.
+    const int per = (nsb + kWave - 1) / kWave;
+    const int s0 = min(nsb, lane * per), s1 = min(nsb, s0 + per);
+    const double kpe = wp.tab ? 1.0 : 1.0 / sph, kqe = wq.tab ? 1.0 : 1.0 / sqh;
+    auto west = [&](int i) {
+      return resid ? fmax(0.0, s_rec[i].a * kpe - s_rec[i].bq * kqe) : s_rec[i].sp;
+    };
+    double me = 0.0, msp = 0.0, msq = 0.0;
+    for (int i = s0; i < s1; ++i) {
+      me += west(i);
+      msp += s_rec[i].sp;
+      msq += s_rec[i].sq;
     }
-    if (!resid || !(resid_mass > 0.0)) {  // bonus row, or a residual that vanished: the target row
+    double pref;
+    const int sel_e = wave_select(nsb, u_final * wave_sum(me), west, pref);
+    Raw16<DT> rp, rq;
+    constexpr int EPL = kSB / kWave;
+    if (sel_e >= 0) {
+      const int64_t j0 = (int64_t)sel_e * kSB + (int64_t)lane * EPL;
+      raw16<DT, AL>(c, prow, j0, rp);
+      if (resid) raw16<DT, AL>(c, qrow, j0, rq);
+    }
+    // exact totals and masses
+    const double Sp = wave_sum(msp), Sq = resid ? wave_sum(msq) : 1.0;
+    const double iSp = 1.0 / Sp, iSq = 1.0 / Sq;
+    double resid_mass = 0.0;
+    if (resid) {
       double mine = 0.0;
-      for (int i = lane; i < nsb; i += kWave) mine += s_rec[i].sp;
-      const double W = wave_sum(mine);
-      y = wave_pick(
-          nsb, c.V, u_final * W, [&](int i) { return s_rec[i].sp; },
-          [&](int64_t j0, double(&w)[16]) { row16<DT, AL>(c, prow, j0, wp, tps, w); });
+      for (int i = s0; i < s1; ++i) mine += fmax(0.0, s_rec[i].a * iSp - s_rec[i].bq * iSq);
+      resid_mass = wave_sum(mine);
+    }
+    // residual weights, or (bonus row, or a residual that vanished) the target row's
+    const bool rmode = resid && resid_mass > 0.0;
+    const double target = u_final * (rmode ? resid_mass : Sp);
+    const int sel = rmode ? wave_select(nsb, target, [&](int i) { return fmax(0.0, s_rec[i].a * iSp - s_rec[i].bq * iSq); },
+                                        pref)
+                          : wave_select(nsb, target, [&](int i) { return s_rec[i].sp; }, pref);
+    int y = -1;
+    if (sel >= 0) {
+      const int64_t j0 = (int64_t)sel * kSB + (int64_t)lane * EPL;
+      if (sel != sel_e) {
+        raw16<DT, AL>(c, prow, j0, rp);
+        if (rmode) raw16<DT, AL>(c, qrow, j0, rq);
+      }
+      double w[EPL];
+      weights16<DT>(c, rp, j0, wp, tps, w);
+      if (rmode) {
+        double wq16[EPL];
+        weights16<DT>(c, rq, j0, wq, tqs, wq16);
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) w[k] = fmax(0.0, w[k] * iSp - wq16[k] * iSq);
+      }
+      y = wave_rescan(sel, target - pref, w);
     }
     for (int i = lane; i <= K; i += kWave) {
       int v = -1;
@@ -545,14 +657,18 @@ __global__ __launch_bounds__(kDT) void k_draftrow(LinCfg c) {
     return;
   }
   const WRow w = wrow(tab, s_m, c.c64);
-  if (DT == kBF16 && w.tab) {
-    for (int j = t; j < kTabSize; j += kDT) s_tab[j] *= w.scale;
+  // the table is scaled while the first loads of the pass are in flight
+  auto scale_table = [&]() {
+    if (DT == kBF16 && w.tab)
+      for (int j = t; j < kTabSize; j += kDT) s_tab[j] *= w.scale;
     __syncthreads();
+  };
+  if (DT == kBF16 && w.tab)
     resolve_pass<DT, AL, DT == kBF16, false, true, kDWaves>(c, b, row, row, 0, c.nsb, s_tab, s_tab, w, w, 0.0f,
-                                                            s_rec);
-  } else {
-    resolve_pass<DT, AL, false, false, true, kDWaves>(c, b, row, row, 0, c.nsb, s_tab, s_tab, w, w, 0.0f, s_rec);
-  }
+                                                            s_rec, scale_table);
+  else
+    resolve_pass<DT, AL, false, false, true, kDWaves>(c, b, row, row, 0, c.nsb, s_tab, s_tab, w, w, 0.0f, s_rec,
+                                                      scale_table);
   __syncthreads();
   if (wave != 0) return;
   const double* const tps = w.tab ? s_tab : nullptr;

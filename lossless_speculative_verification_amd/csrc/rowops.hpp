@@ -66,8 +66,8 @@ __device__ __forceinline__ void wpair(bool bf16_tab, float mp, float mq, bool re
 }
 
 // The final draw of a linear block divides the pre-scale of a table row pair
-// by the rows' normaliser estimates, so that the scaled table values are
-// estimates of the probabilities themselves and compare directly.
+// by the rows' normaliser estimates, so that the scaled weights are estimates
+// of the probabilities themselves and compare directly.
 __device__ __forceinline__ void norm_pair(WRow& wp, WRow& wq, bool resid, double sph, double sqh) {
   if (wp.tab) {
     wp.scale = wp.scale / sph;
@@ -93,8 +93,9 @@ __device__ __forceinline__ void fill_tab(double* tab, double c64) {
   }
 }
 
-// fweight with an optional table already multiplied by w.scale (nullptr:
-// recompute the entry).
+// fp64 weight of one logit under the row rule above, reading a table already
+// multiplied by w.scale when given (nullptr: recompute the entry); the two
+// agree bit for bit.
 template <int DT>
 __device__ __forceinline__ double fweight(float a, const WRow& w, double c64, const double* tab_scaled) {
   if constexpr (DT == kBF16) {
@@ -201,15 +202,14 @@ __device__ int pick_index(int nsb, int V, double target, WSB wsb, WEL wel, doubl
   return j;
 }
 
-// The pick of pick_index done by one whole wave (all 64 lanes active), with
-// no workgroup barrier: lane l owns a run of consecutive sub-blocks, then 16
-// consecutive elements of the chosen sub-block, whose weights welb(j0, w)
-// writes (w[k] = weight of element j0 + k, 0 past the end of the row). Same
-// contract: the smallest j whose running weight exceeds target, the last
-// positive weight if rounding leaves none, -1 if every weight is zero.
-// Returns j on every lane.
-template <class WSB, class WELB>
-__device__ int wave_pick(int nsb, int V, double target, WSB wsb, WELB welb) {
+// Sub-block selection of an inverse-CDF pick by one whole wave (all 64 lanes
+// active), with no workgroup barrier: lane l owns a run of consecutive
+// sub-blocks, whose weights wsb(sb) it reads. Returns, on every lane, the
+// smallest sub-block whose running weight exceeds target, or the last one with
+// positive weight if rounding leaves none (-1 if every weight is zero), and in
+// pref the running weight before it.
+template <class WSB>
+__device__ int wave_select(int nsb, double target, WSB wsb, double& pref) {
   const int lane = threadIdx.x & (kWave - 1);
   const int per = (nsb + kWave - 1) / kWave;
   const int s0 = min(nsb, lane * per), s1 = min(nsb, s0 + per);
@@ -217,7 +217,7 @@ __device__ int wave_pick(int nsb, int V, double target, WSB wsb, WELB welb) {
   for (int sb = s0; sb < s1; ++sb) mine += wsb(sb);
   const double excl = wave_incl_scan(mine) - mine;
   int sel = -1, last = -1;
-  double pref = 0.0, lpref = 0.0;
+  double p0 = 0.0, lp = 0.0;
   {
     double acc = excl;
     for (int sb = s0; sb < s1; ++sb) {
@@ -225,10 +225,10 @@ __device__ int wave_pick(int nsb, int V, double target, WSB wsb, WELB welb) {
       if (w > 0.0) {
         if (sel < 0 && acc + w > target) {
           sel = sb;
-          pref = acc;
+          p0 = acc;
         }
         last = sb;
-        lpref = acc;
+        lp = acc;
       }
       acc += w;
     }
@@ -239,17 +239,27 @@ __device__ int wave_pick(int nsb, int V, double target, WSB wsb, WELB welb) {
     src = __ffsll((long long)m) - 1;
   } else {  // rounding left no crossing: the last sub-block with positive weight
     m = __ballot(last >= 0);
-    if (!m) return -1;
+    if (!m) {
+      pref = 0.0;
+      return -1;
+    }
     src = 63 - __clzll((long long)m);
     sel = last;
-    pref = lpref;
+    p0 = lp;
   }
-  const int sbsel = __shfl(sel, src);
-  const double tin = target - __shfl(pref, src);
+  pref = __shfl(p0, src);
+  return __shfl(sel, src);
+}
+
+// The element pick inside sub-block sbsel by one whole wave: lane l owns the 16
+// consecutive elements from sbsel * kSB + 16 l, whose weights w[16] it holds
+// (0 past the end of the row). Returns, on every lane, the smallest element
+// whose running weight (from the sub-block's start) exceeds tin, or the last
+// positive one if rounding leaves none (-1 if none is positive).
+__device__ __forceinline__ int wave_rescan(int sbsel, double tin, const double (&w)[kSB / kWave]) {
   constexpr int EPL = kSB / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
   const int64_t j0 = (int64_t)sbsel * kSB + (int64_t)lane * EPL;
-  double w[EPL];
-  welb(j0, w);
   double loc = 0.0;
 #pragma unroll
   for (int k = 0; k < EPL; ++k) loc += w[k];
@@ -263,10 +273,26 @@ __device__ int wave_pick(int nsb, int V, double target, WSB wsb, WELB welb) {
     }
     acc += w[k];
   }
-  m = __ballot(jj >= 0);
+  unsigned long long m = __ballot(jj >= 0);
   if (m) return __shfl(jj, __ffsll((long long)m) - 1);
   m = __ballot(jl >= 0);
   return m ? __shfl(jl, 63 - __clzll((long long)m)) : -1;
+}
+
+// The pick of pick_index done by one whole wave: wave_select, then
+// wave_rescan over the weights welb(j0, w) writes (w[k] = weight of element
+// j0 + k, 0 past the end of the row). Same contract as pick_index; returns j
+// on every lane.
+template <class WSB, class WELB>
+__device__ int wave_pick(int nsb, int V, double target, WSB wsb, WELB welb) {
+  double pref;
+  const int sbsel = wave_select(nsb, target, wsb, pref);
+  if (sbsel < 0) return -1;
+  constexpr int EPL = kSB / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  double w[EPL];
+  welb((int64_t)sbsel * kSB + (int64_t)lane * EPL, w);
+  return wave_rescan(sbsel, target - pref, w);
 }
 
 // ------------------------------------------------------- draft pick --
