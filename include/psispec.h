@@ -66,6 +66,8 @@ extern "C" {
                                    top_k is not in [1, min(V-1, PSISPEC_MAX_TOPK)] */
 #define PSISPEC_EWORKSPACE   -3 /* ws_bytes smaller than psispec_workspace_bytes(...) */
 #define PSISPEC_EHIP         -4 /* a HIP launch failed */
+#define PSISPEC_ESCRATCH     -5 /* psispec_verify_linear_noalloc: the call needs more than
+                                   PSISPEC_NOALLOC_SCRATCH_BYTES of scratch */
 
 /* ---- dtypes --------------------------------------------------------------- */
 #define PSISPEC_DTYPE_F32  0
@@ -82,6 +84,7 @@ extern "C" {
 #define PSISPEC_MAX_K         64   /* draft positions per request (one wave64 ballot) */
 #define PSISPEC_MAX_TREE_NODES 256 /* tree nodes per request */
 #define PSISPEC_MAX_TOPK      256  /* largest top_k of filtered sampling */
+#define PSISPEC_NOALLOC_SCRATCH_BYTES (32u << 20) /* device scratch of psispec_verify_linear_noalloc */
 
 /*
  * Sampling parameters (Uno README, inference controls: temperature, top-p,
@@ -178,6 +181,34 @@ int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype,
                           int32_t V, int32_t* draft_tokens, const psispec_params* params,
                           int32_t* out_tokens, int32_t* out_len, float* out_probs, double* out_resid_mass,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Linear verification that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. Arguments, outputs,
+ * rules and errors are those of psispec_verify_linear (same kernels, same
+ * bits). The workspace is a fixed device array of
+ * PSISPEC_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library. Each GPU the
+ * library runs on holds its own copy from the first call on that GPU (the GPU
+ * of `stream`, or the current one for NULL) until the process ends.
+ *   Limit   the call needs, of psispec_workspace_bytes' layout for
+ *           rows_per_req = 2K + 1, the statistics and request records (about
+ *           16 B per logit chunk of 32768 (bf16) or 16384 (fp32) logits per
+ *           row, plus 32 B per 1024 logits of each request and 16 B per 1024
+ *           logits of each row); filtered sampling also needs the kept-set
+ *           sections. B = 256, K = 8, V = 151936 bf16 takes about 12 MB;
+ *           beyond 32 MiB the call returns PSISPEC_ESCRATCH and enqueues
+ *           nothing.
+ *   Races   every call on one GPU shares that GPU's array: calls that may
+ *           overlap on one GPU (different streams, or different threads'
+ *           streams) race and give undefined outputs; order them on one
+ *           stream. The kernels initialise everything they read from the
+ *           array, so it needs no clearing between calls.
+ */
+int psispec_verify_linear_noalloc(const void* p_logits, const void* q_logits, int dtype, int64_t B, int32_t K,
+                                  int32_t V, int32_t* draft_tokens, const psispec_params* params,
+                                  int32_t* out_tokens, int32_t* out_len, float* out_probs, double* out_resid_mass,
+                                  hipStream_t stream);
 
 /*
  * Depth of a candidate tree given its HOST parent array (parent[n] in

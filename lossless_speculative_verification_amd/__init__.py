@@ -26,7 +26,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpsispec.so")
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FUSED_DRAFT = 1
 MAX_K = 64
@@ -69,6 +69,9 @@ def _load():
     L.psispec_verify_linear.argtypes = [P, P, ctypes.c_int, i64, i32, i32, P, ctypes.POINTER(Params), P, P, P, P,
                                         P, sz, P]
     L.psispec_verify_linear.restype = ctypes.c_int
+    L.psispec_verify_linear_noalloc.argtypes = [P, P, ctypes.c_int, i64, i32, i32, P, ctypes.POINTER(Params), P, P,
+                                                P, P, P]
+    L.psispec_verify_linear_noalloc.restype = ctypes.c_int
     L.psispec_tree_depth.argtypes = [P, i32]
     L.psispec_tree_depth.restype = i32
     L.psispec_verify_tree.argtypes = [P, P, ctypes.c_int, i64, i32, i32, P, P, ctypes.POINTER(Params), P, P, P, P,
@@ -257,6 +260,37 @@ def verify_linear(p: torch.Tensor, q: torch.Tensor, draft_tokens: torch.Tensor |
                                    _ptr(out["tokens"]), _ptr(out["len"]), _ptr(out.get("probs")),
                                    _ptr(out.get("resid")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("psispec_verify_linear", rc)
+    out["draft"] = draft_tokens
+    return out
+
+
+def verify_linear_noalloc(p: torch.Tensor, q: torch.Tensor, draft_tokens: torch.Tensor | None, temperature=1.0,
+                          top_k=0, top_p=1.0, seed=0, step=0, fused=False, out=None, want_probs=True,
+                          want_resid=True, stream=None) -> dict:
+    """psispec_verify_linear_noalloc: psispec_verify_linear with the library's
+    fixed device scratch as its workspace. Same arguments and outputs as
+    verify_linear (outputs are allocated here only when `out` is None)."""
+    assert p.is_cuda and q.is_cuda and p.is_contiguous() and q.is_contiguous()
+    B, K1, V = p.shape
+    K = K1 - 1
+    assert q.shape == (B, K, V) and p.dtype == q.dtype
+    dt = dtype_code(p)
+    dev = p.device
+    if draft_tokens is None:
+        if not fused:
+            raise ValueError("draft_tokens required unless fused=True")
+        draft_tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    assert draft_tokens.dtype == torch.int32 and draft_tokens.is_contiguous()
+    if out is None:
+        out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                   len=torch.empty((B,), dtype=torch.int32, device=dev),
+                   probs=torch.empty((B, K, 2), dtype=torch.float32, device=dev) if want_probs else None,
+                   resid=torch.empty((B,), dtype=torch.float64, device=dev) if want_resid else None)
+    prm = make_params(temperature, top_k, top_p, seed, step, fused)
+    rc = lib.psispec_verify_linear_noalloc(_ptr(p), _ptr(q), dt, B, K, V, _ptr(draft_tokens), ctypes.byref(prm),
+                                           _ptr(out["tokens"]), _ptr(out["len"]), _ptr(out.get("probs")),
+                                           _ptr(out.get("resid")), _stream(stream))
+    _check("psispec_verify_linear_noalloc", rc)
     out["draft"] = draft_tokens
     return out
 

@@ -3,8 +3,17 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "psispec.h"
 #include "kernels.hpp"
+
+// Scratch of psispec_verify_linear_noalloc: the workspace of that call lives
+// in this file-scope array instead of a caller buffer. Each GPU the library
+// runs on holds its own copy until the process ends. In host code the name is
+// only a stand-in for the device array: its device address comes from
+// hipGetSymbolAddress (scratch_of below), and only that address is used.
+static __device__ __align__(256) unsigned char scratch[PSISPEC_NOALLOC_SCRATCH_BYTES];
 
 namespace psi {
 
@@ -186,6 +195,32 @@ inline int build_topo(const int32_t* parent, int32_t N, int32_t D, TreeTopo& tp)
   return rounds;
 }
 
+// Device address of the scratch array on device `dev`, looked up once per
+// device with that device current. Returns the lookup's status.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+hipError_t scratch_of(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
 }  // namespace
 }  // namespace psi
 
@@ -250,6 +285,34 @@ int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype,
     e = launch_linear_sampled(c, dtype, stream);  // draws the drafts itself when fused
   }
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
+}
+
+int psispec_verify_linear_noalloc(const void* p_logits, const void* q_logits, int dtype, int64_t B, int32_t K,
+                                  int32_t V, int32_t* draft_tokens, const psispec_params* params,
+                                  int32_t* out_tokens, int32_t* out_len, float* out_probs, double* out_resid_mass,
+                                  hipStream_t stream) {
+  if (!p_logits || !q_logits || !draft_tokens || !out_tokens || !out_len) return PSISPEC_EINVAL;
+  if (B <= 0 || K <= 0 || V <= 0) return PSISPEC_EINVAL;
+  if (int rc = check_params(params, V)) return rc;
+  if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
+  if (K > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
+  if (int rc = check_filter(params, V)) return rc;
+  // Sections of the workspace layout this call uses: statistics, request and
+  // sub-block records, then the kept sets when filtering (the tree sections
+  // after them are never touched by linear verification).
+  const Layout L = layout(B, 2 * K + 1, V, dtype);
+  const size_t need = (params->temperature > 0.0f && filtered(params, V)) ? L.rst : L.fh;
+  if (need > (size_t)PSISPEC_NOALLOC_SCRATCH_BYTES) return PSISPEC_ESCRATCH;
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return PSISPEC_EHIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return PSISPEC_EHIP;
+  }
+  void* ws = nullptr;
+  if (scratch_of(dev, &ws) != hipSuccess || !ws) return PSISPEC_EHIP;
+  return psispec_verify_linear(p_logits, q_logits, dtype, B, K, V, draft_tokens, params, out_tokens, out_len,
+                               out_probs, out_resid_mass, ws, L.total, stream);
 }
 
 int32_t psispec_tree_depth(const int32_t* parent, int32_t N) {
@@ -568,6 +631,8 @@ const char* psispec_strerror(int status) {
       return "workspace too small";
     case PSISPEC_EHIP:
       return "HIP launch failed";
+    case PSISPEC_ESCRATCH:
+      return "the call needs more than the no-alloc entry point's fixed scratch";
     default:
       return "unknown status";
   }

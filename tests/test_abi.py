@@ -92,6 +92,32 @@ def test_linear_argument_errors(psi):
     assert _call_linear(psi, ws_addr=(1 << 20) + 8) == psi.EINVAL
 
 
+def test_noalloc_argument_errors(psi):
+    """The entry point without a workspace validates like psispec_verify_linear
+    and refuses, before touching the GPU, a call whose scratch need exceeds
+    the library's fixed array (the filtered workload at full size)."""
+    f = ctypes.c_void_p(1 << 20)
+    L = psi.lib
+
+    def call(B=4, K=3, V=512, dtype=1, prm=None, null=None):
+        prm = prm or psi.make_params()
+        args = dict(p=f, q=f, d=f, tok=f, len=f)
+        if null:
+            args[null] = None
+        return L.psispec_verify_linear_noalloc(args["p"], args["q"], dtype, B, K, V, args["d"], ctypes.byref(prm),
+                                               args["tok"], args["len"], None, None, None)
+
+    for k in ("p", "q", "d", "tok", "len"):
+        assert call(null=k) == psi.EINVAL
+    assert call(B=0) == psi.EINVAL
+    assert call(K=65) == psi.EUNSUPPORTED
+    assert call(dtype=5) == psi.EUNSUPPORTED
+    assert call(prm=psi.make_params(top_p=0.0)) == psi.EINVAL
+    big = psi.make_params(temperature=1.0, top_k=50, top_p=0.95)
+    assert call(B=128, K=16, V=128256, dtype=0, prm=big) == psi.ESCRATCH
+    assert psi.strerror(psi.ESCRATCH) != psi.strerror(-99)
+
+
 def test_draft_argument_errors(psi):
     prm = psi.make_params()
     f = ctypes.c_void_p(0x20000000)
