@@ -232,35 +232,6 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* sh, dou
   return before + (incl - v);
 }
 
-// fp64-grade exponential (device math library, < 1 ulp).
-__device__ __forceinline__ double exp64(double x) { return ::exp(x); }
-
-// 2^y in fp64 without tables (relative error < 3e-16 for y <= ~1000; -inf and
-// anything below -1100 give 0): y = k + f with k = rint(y), |f| <= 1/2, and
-// 2^f = exp(f ln 2) from its degree-12 Taylor polynomial (remainder < 2e-16).
-__device__ __forceinline__ double exp2_poly(double y) {
-  y = fmax(y, -1100.0);
-  const double k = __builtin_rint(y);
-  const double f = y - k;  // exact
-  constexpr double c[13] = {1.0,
-                            0.69314718055994530942,
-                            0.24022650695910071233,
-                            0.055504108664821579953,
-                            0.0096181291076284771620,
-                            0.0013333558146428443423,
-                            1.5403530393381609954e-4,
-                            1.5252733804059840280e-5,
-                            1.3215486790144309488e-6,
-                            1.0178086009239699727e-7,
-                            7.0549116208011233298e-9,
-                            4.4455382718708114975e-10,
-                            2.5678435993488202539e-11};
-  double p = c[12];
-#pragma unroll
-  for (int i = 11; i >= 0; --i) p = __builtin_fma(p, f, c[i]);
-  return ::ldexp(p, (int)k);
-}
-
 // 2^y in fp64 for y <= 1023 (relative error < 5e-16; 0 for y below -1022,
 // -inf and NaN included). k = the integer nearest y is
 // read from the low word of y + 1.5 * 2^52, f = y - k lies in [-1/2, 1/2],
