@@ -247,21 +247,50 @@ def test_greedy_parity():
 
 
 def test_gpu_law_many_replicas():
-    """10^5 replicas of a V=8, K=2 case in one call: accept-length histogram
-    matches the closed form and the first token follows P_0 (chi-square)."""
+    """10^6 replicas of a V=8, K=2 case in one call: the accept-length
+    histogram matches the closed form (1 - a_0, a_0 (1 - a_1), a_0 a_1), the
+    first emitted token follows P_0 and, on the replicas that reach position 1,
+    the second emitted token follows P_1 (chi-square)."""
     psi = _psi()
     rng = np.random.default_rng(21)
     a = rng.normal(0, 1.5, (1, 3, 8)).astype(np.float32)
     d = (a[:, :2] + rng.normal(0, 1.0, (1, 2, 8))).astype(np.float32)
-    B = 100_000
+    B = 1_000_000
     pd = to_dev(np.repeat(a, B, axis=0))
     qd = to_dev(np.repeat(d, B, axis=0))
     g = psi.verify_linear(pd, qd, None, temperature=1.0, seed=123, step=0, fused=True)
     n = g["len"].cpu().numpy()
-    first = g["tokens"][:, 0].cpu().numpy()
+    tok = g["tokens"].cpu().numpy()
     P = [probs(a[0, i]) for i in range(3)]
     Q = [probs(d[0, i]) for i in range(2)]
     al = [alpha(P[i], Q[i]) for i in range(2)]
     law = np.array([1 - al[0], al[0] * (1 - al[1]), al[0] * al[1]])
     assert chi2_pvalue(np.bincount(n, minlength=3), law * B) > 1e-3
-    assert chi2_pvalue(np.bincount(first, minlength=8), P[0] * B) > 1e-3
+    assert chi2_pvalue(np.bincount(tok[:, 0], minlength=8), P[0] * B) > 1e-3
+    reach = n >= 1
+    assert chi2_pvalue(np.bincount(tok[reach, 1], minlength=8), P[1] * int(reach.sum())) > 1e-3
+
+
+def test_philox_sweep_against_oracle():
+    """The GPU's Philox4x32-10 uniforms equal the oracle's on 1,048,576
+    counters. With equal logits over V = 65536 tokens an inverse-CDF draw lands
+    on floor(u * 65536), so each draft draw shows the top 16 bits of
+    U(seed, step, b, i, 0x40000000); identical target rows accept every draft,
+    so the bonus draw shows those of U(seed, step, b, K, 0)."""
+    psi = _psi()
+    B, K, V = 256, 15, 65536
+    seed = 0x0123456789ABCDEF
+    p = torch.zeros((B, K + 1, V), dtype=torch.float32, device="cuda")
+    q = torch.zeros((B, K, V), dtype=torch.float32, device="cuda")
+    bad = 0
+    for step in range(256):
+        g = psi.verify_linear(p, q, None, temperature=1.0, seed=seed, step=step, fused=True)
+        torch.cuda.synchronize()
+        drafts = g["draft"].cpu().numpy()
+        assert np.all(g["len"].cpu().numpy() == K)
+        bonus = g["tokens"].cpu().numpy()[:, K]
+        want_d = np.array([[int(oracle.uniform(seed, step, b, i, oracle.DRAFT_DRAW) * V) for i in range(K)]
+                           for b in range(B)])
+        want_b = np.array([int(oracle.uniform(seed, step, b, K, 0) * V) for b in range(B)])
+        bad += int((drafts != want_d).sum() + (bonus != want_b).sum())
+    assert bad == 0
