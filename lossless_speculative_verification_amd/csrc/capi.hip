@@ -51,7 +51,7 @@ inline int filt_stride(int32_t V) { return V < kMaxTopK ? V : kMaxTopK; }
 
 // Workspace sections, each 256-byte aligned.
 struct Layout {
-  size_t st, rs, res, dr, fh, fe, fk, fc, ff, rst, ts, tres, total;
+  size_t st, rs, res, dr, fh, fe, fk, fc, ff, wc, rst, ts, tres, total;
 };
 
 inline int nchf_of(int32_t V) { return (V + kFiltChunk - 1) / kFiltChunk; }
@@ -78,6 +78,8 @@ inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
   off = align_up(off + (size_t)B * rows_per_req * nchf_of(V) * kFiltChunkCap * sizeof(FiltCand), 256);
   L.ff = off;
   off = align_up(off + ((size_t)B * rows_per_req + 1) * sizeof(int32_t), 256);
+  L.wc = off;
+  off = align_up(off + (size_t)B * rows_per_req * sizeof(CutRec), 256);
   L.rst = off;
   off = align_up(off + (size_t)B * rows_per_req * sizeof(RowStat), 256);
   L.ts = off;
@@ -104,12 +106,19 @@ inline bool filtered(const psispec_params* prm, int32_t V) {
   return prm->temperature > 0.0f && ((prm->top_k > 0 && prm->top_k < V) || prm->top_p < 1.0f);
 }
 
-// Filtered sampling needs a top-k in [1, kMaxTopK] to bound the kept set.
-inline int check_filter(const psispec_params* prm, int32_t V) {
-  if (!filtered(prm, V)) return PSISPEC_OK;
-  if (prm->top_k <= 0 || prm->top_k >= V) return PSISPEC_EUNSUPPORTED;  // top-p alone over the full vocabulary
-  if (prm->top_k > kMaxTopK) return PSISPEC_EUNSUPPORTED;
-  return PSISPEC_OK;
+// Filtered sampling whose kept set is not bounded by a top_k in
+// [1, kMaxTopK]: top-p alone (top_k 0 or >= V), or a larger top_k. Such rows
+// go to the cut search of wide.hip instead of the kept-set lists of filter.hip.
+inline bool wide_filter(const psispec_params* prm, int32_t V) {
+  return filtered(prm, V) && (prm->top_k <= 0 || prm->top_k >= V || prm->top_k > kMaxTopK);
+}
+
+inline WideCfg wide_cfg(const psispec_params* prm, void* ws, int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
+  WideCfg w;
+  w.cut = (CutRec*)((char*)ws + layout(B, rows_per_req, V, dtype).wc);
+  w.top_k = (prm->top_k > 0 && prm->top_k < V) ? prm->top_k : 0;
+  w.top_p = (double)prm->top_p;
+  return w;
 }
 
 inline FiltCfg filt_cfg(const psispec_params* prm, void* ws, int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
@@ -243,7 +252,6 @@ int psispec_draft_sample(const void* q_logits, int dtype, int64_t B, int32_t K, 
   if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
   if (K > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
   if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
-  if (int rc = check_filter(params, V)) return rc;
   if (ws_bytes < psispec_workspace_bytes(B, K, V, dtype)) return PSISPEC_EWORKSPACE;
   LinCfg c;
   fill_common(c, nullptr, q_logits, dtype, B, K, V, params, workspace, 0);
@@ -251,6 +259,7 @@ int psispec_draft_sample(const void* q_logits, int dtype, int64_t B, int32_t K, 
   timing_begin(stream);
   hipError_t e;
   if (params->temperature == 0.0f) e = launch_draft_greedy(c, dtype, stream);
+  else if (wide_filter(params, V)) e = launch_wide(c, wide_cfg(params, workspace, B, K, V, dtype), dtype, true, stream);
   else if (filtered(params, V)) e = launch_filtered(c, filt_cfg(params, workspace, B, K, V, dtype), dtype, true, stream);
   else e = launch_draft_sampled(c, dtype, stream);
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
@@ -266,7 +275,6 @@ int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype,
   if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
   if (K > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
   if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
-  if (int rc = check_filter(params, V)) return rc;
   if (ws_bytes < psispec_workspace_bytes(B, 2 * K + 1, V, dtype)) return PSISPEC_EWORKSPACE;
   LinCfg c;
   fill_common(c, p_logits, q_logits, dtype, B, K, V, params, workspace, K + 1);
@@ -279,6 +287,8 @@ int psispec_verify_linear(const void* p_logits, const void* q_logits, int dtype,
   hipError_t e;
   if (params->temperature == 0.0f) {
     e = launch_linear_greedy(c, dtype, stream);
+  } else if (wide_filter(params, V)) {
+    e = launch_wide(c, wide_cfg(params, workspace, B, 2 * K + 1, V, dtype), dtype, false, stream);
   } else if (filtered(params, V)) {
     e = launch_filtered(c, filt_cfg(params, workspace, B, 2 * K + 1, V, dtype), dtype, false, stream);
   } else {
@@ -296,7 +306,6 @@ int psispec_verify_linear_noalloc(const void* p_logits, const void* q_logits, in
   if (int rc = check_params(params, V)) return rc;
   if (dtype != PSISPEC_DTYPE_F32 && dtype != PSISPEC_DTYPE_BF16) return PSISPEC_EUNSUPPORTED;
   if (K > PSISPEC_MAX_K) return PSISPEC_EUNSUPPORTED;
-  if (int rc = check_filter(params, V)) return rc;
   // Sections of the workspace layout this call uses: statistics, request and
   // sub-block records, then the kept sets when filtering (the tree sections
   // after them are never touched by linear verification).
@@ -341,7 +350,7 @@ int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, i
   const int32_t D = psispec_tree_depth(parent, N);
   if (D < 0) return D;
   if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
-  if (int rc = check_filter(params, V)) return rc;
+  if (wide_filter(params, V)) return PSISPEC_EUNSUPPORTED;
   const int32_t rows = 2 * (N + 1);
   if (ws_bytes < psispec_workspace_bytes(B, rows, V, dtype)) return PSISPEC_EWORKSPACE;
   TreeTopo tp;

@@ -133,6 +133,25 @@ struct FiltCfg {
   double top_p;     // binary32 value
 };
 
+// Filters with no small bound on the kept set (top-p alone, or top_k above
+// kMaxTopK), wide.hip. The kept set of a row is a prefix of the order (logit
+// descending, id ascending), described by its last token: token j is kept iff
+// key(a_j) > key, or key(a_j) == key and j <= id, with key the order key of
+// the binary32 logit (-0 as +0).
+struct CutRec {
+  float m;       // maximum logit of the row
+  uint32_t key;  // order key of the last kept token
+  int32_t id;    // its token id
+  int32_t bad;   // NaN / +inf / all -inf
+  double S;      // sum over the kept set of 2^((a - m) c), c = log2(e) / T
+  double cnt;    // kept tokens sharing the last key (diagnostic)
+};
+struct WideCfg {
+  CutRec* cut;   // [rows]
+  int top_k;     // 0: no top-k stage
+  double top_p;  // binary32 value; 1: no top-p stage
+};
+
 // Candidate tree topology, passed by value in the kernel arguments. Row 0 is
 // the root context and row n+1 the context after node n; the children of row
 // r are the nodes kids[off[r] .. off[r+1]) in ascending node id.
@@ -249,6 +268,9 @@ hipError_t launch_linear_greedy(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_draft_sampled(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_draft_greedy(const LinCfg& c, int dtype, hipStream_t s);
 hipError_t launch_filtered(const LinCfg& c, const FiltCfg& f, int dtype, bool draft_only, hipStream_t s);
+hipError_t launch_wide(const LinCfg& c, const WideCfg& wc, int dtype, bool draft_only, hipStream_t s);
+// Draft sampling alone: -1 for all drafts of a request with an invalid row.
+__global__ void k_draft_fix(LinCfg c);
 // Tree verification (tree.hip); c.rows holds N + 1 target and N + 1 draft rows
 // per request; `rounds` bounds the rejections that need a new G(c) before the
 // final one along any walk.

@@ -136,10 +136,11 @@ def test_binding_has_no_fallback(psi):
 
 
 def test_filter_limits(psi):
-    # top-p without a top-k bound, and top-k above the supported maximum
-    assert _call_linear(psi, prm=psi.make_params(top_p=0.9)) == psi.EUNSUPPORTED
-    assert _call_linear(psi, V=4096, prm=psi.make_params(top_k=257)) == psi.EUNSUPPORTED
-    assert _call_linear(psi, V=4096, prm=psi.make_params(top_k=256, top_p=0.9), ws_bytes=16) == psi.EWORKSPACE
+    # every admissible filter is accepted (the workspace check is the first to
+    # fail here, before any launch): top-p without a top-k, top-k above 256,
+    # top_k >= V with a top-p, and the bounded kept-set path
+    for V, k, p in ((1000, 0, 0.9), (4096, 257, 1.0), (4096, 5000, 0.5), (4096, 256, 0.9), (4096, 4096, 0.3)):
+        assert _call_linear(psi, V=V, prm=psi.make_params(top_k=k, top_p=p), ws_bytes=16) == psi.EWORKSPACE
 
 
 def _call_cands(psi, B=2, K=15, V=1000, dtype=1, prm=None, cands=32, nodes=32, ws_bytes=1 << 30, ws_addr=1 << 20,
