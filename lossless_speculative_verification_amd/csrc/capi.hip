@@ -350,7 +350,6 @@ int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, i
   const int32_t D = psispec_tree_depth(parent, N);
   if (D < 0) return D;
   if (((uintptr_t)workspace & 255u) != 0) return PSISPEC_EINVAL;
-  if (wide_filter(params, V)) return PSISPEC_EUNSUPPORTED;
   const int32_t rows = 2 * (N + 1);
   if (ws_bytes < psispec_workspace_bytes(B, rows, V, dtype)) return PSISPEC_EWORKSPACE;
   TreeTopo tp;
@@ -372,6 +371,7 @@ int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, i
   timing_begin(stream);
   hipError_t e;
   if (params->temperature == 0.0f) e = launch_tree_greedy(c, tp, tc, dtype, stream);
+  else if (wide_filter(params, V)) e = launch_tree_wide(c, wide_cfg(params, workspace, B, rows, V, dtype), tp, tc, dtype, stream);
   else if (filtered(params, V)) e = launch_tree_filtered(c, filt_cfg(params, workspace, B, rows, V, dtype), tp, tc, dtype, stream);
   else e = launch_tree_sampled(c, tp, tc, rounds, dtype, stream);
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;

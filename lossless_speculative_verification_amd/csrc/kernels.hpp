@@ -279,6 +279,8 @@ __global__ void k_draft_fix(LinCfg c);
 hipError_t launch_tree_sampled(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int rounds, int dtype,
                                hipStream_t s);
 hipError_t launch_tree_greedy(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int dtype, hipStream_t s);
+hipError_t launch_tree_wide(const LinCfg& c, const WideCfg& wc, const TreeTopo& tp, const TreeCfg& tc, int dtype,
+                            hipStream_t s);
 hipError_t launch_tree_filtered(const LinCfg& c, const FiltCfg& f, const TreeTopo& tp, const TreeCfg& tc, int dtype,
                                 hipStream_t s);
 // Row passes over the first `rows` rows of c.rows, reused by the tree:

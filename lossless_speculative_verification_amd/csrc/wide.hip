@@ -28,6 +28,10 @@
 //               tests, first rejection, then fp64 sub-block sums of the final
 //               row's kept weights (target alone, or max(0, p - q)) and the
 //               final draw.
+//   k_wtdraft   tree node drafts, one workgroup per node, as k_wdraft.
+//   k_wtree     tree walk, one workgroup per request: child tests with the
+//               recursive residual kept as one coefficient, one fp64 pass over
+//               the row pair per rejection, and the final draw.
 #include "rowops.hpp"
 
 namespace psi {
@@ -37,6 +41,8 @@ namespace {
 constexpr int kWT = 1024;          // threads of a cut or resolve workgroup
 constexpr int kWTW = kWT / kWave;  // waves of one
 constexpr int kDWT = 512;          // threads of a draft-row workgroup
+constexpr int kTT = 512;           // threads of a tree-walk workgroup (registers for the fp64 passes)
+constexpr int kTTW = kTT / kWave;
 constexpr int kHist = 4096;        // bins of the widest radix level (12 bits)
 constexpr uint32_t kKeyNegInf = 0x007fffffu;  // order key of -inf
 
@@ -430,29 +436,16 @@ __global__ __launch_bounds__(kWT) void k_wcut(LinCfg c, WideCfg wc) {
 }
 
 // ------------------------------------------------------------ draft row --
-// One workgroup per draft row: x ~ softmax(filter(q / T)) by inverse CDF in
-// token-id order with U(seed, step, b, i, 0x40000000) ("Uno" research
-// explainer, §3.3: drafts are drawn from the draft distributions); -1 for an
-// invalid row.
-template <int DT, bool AL>
-__global__ __launch_bounds__(kDWT) void k_wdraft(LinCfg c, WideCfg wc) {
-  using E = Elem<DT>;
-  constexpr int EPV = E::kPerVec;
+// Inverse-CDF draw in token-id order from softmax of the kept set of one row
+// (cut cr), with uniform u, by a workgroup of NT threads: fp64 sub-block sums
+// of the kept weights into s_sb[nsb], then wave 0 picks. Returns the token on
+// the lanes of wave 0 (other waves return -2 and must do nothing more).
+template <int DT, bool AL, int NT>
+__device__ int wide_draw(const LinCfg& c, const CutRec& cr, const char* row, double u, double* s_sb) {
+  constexpr int EPV = Elem<DT>::kPerVec;
   constexpr int EPL = kSB / kWave;
-  extern __shared__ double s_sb[];  // one fp64 sum per sub-block
-  const int64_t qr = blockIdx.x;    // draft row in [0, B * K)
-  const int K = c.K, t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
-  const int64_t b = qr / K;
-  const int i = (int)(qr - b * K);
-  const int64_t sr = b * (c.rows.np + c.rows.nq) + c.rows.np + i;
-  const CutRec cr = wc.cut[sr];
-  if (cr.bad) {
-    if (t == 0) c.draft[qr] = -1;
-    return;
-  }
-  const char* row = c.rows.row(sr);
+  const int t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
   const double c64 = c.c64, mc = (double)cr.m * c64;
-  auto wt = [&](float a, int64_t j) { return kept_by(wkey(a), j, cr.key, cr.id) ? wweight(a, c64, mc) : 0.0; };
   auto weights = [&](int64_t j0, double (&w)[EPL]) {
 #pragma unroll
     for (int v = 0; v < EPL / EPV; ++v) {
@@ -461,12 +454,12 @@ __global__ __launch_bounds__(kDWT) void k_wdraft(LinCfg c, WideCfg wc) {
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
         const int64_t j = j0 + v * EPV + e;
-        w[v * EPV + e] = j < c.V ? wt(x[e], j) : 0.0;
+        w[v * EPV + e] = (j < c.V && kept_by(wkey(x[e]), j, cr.key, cr.id)) ? wweight(x[e], c64, mc) : 0.0;
       }
     }
   };
   const int nsb = c.nsb;
-  for (int sb = wave; sb < nsb; sb += kDWT / kWave) {
+  for (int sb = wave; sb < nsb; sb += NT / kWave) {
     double w[EPL];
     weights((int64_t)sb * kSB + (int64_t)lane * EPL, w);
     double s = 0.0;
@@ -476,14 +469,55 @@ __global__ __launch_bounds__(kDWT) void k_wdraft(LinCfg c, WideCfg wc) {
     if (lane == 0) s_sb[sb] = s;
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (wave != 0) return -2;
   double mine = 0.0;
   for (int sb = lane; sb < nsb; sb += kWave) mine += s_sb[sb];
   const double W = wave_sum(mine);
-  const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
-  const int x = wave_pick(nsb, c.V, u * W, [&](int sb) { return s_sb[sb]; },
-                          [&](int64_t j0, double(&w)[EPL]) { weights(j0, w); });
-  if (lane == 0) c.draft[qr] = x;
+  return wave_pick(nsb, c.V, u * W, [&](int sb) { return s_sb[sb]; },
+                   [&](int64_t j0, double(&w)[EPL]) { weights(j0, w); });
+}
+
+// One workgroup per draft row: x ~ softmax(filter(q / T)) by inverse CDF in
+// token-id order with U(seed, step, b, i, 0x40000000) ("Uno" research
+// explainer, §3.3: drafts are drawn from the draft distributions); -1 for an
+// invalid row.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kDWT) void k_wdraft(LinCfg c, WideCfg wc) {
+  extern __shared__ double s_sb[];  // one fp64 sum per sub-block
+  const int64_t qr = blockIdx.x;    // draft row in [0, B * K)
+  const int K = c.K;
+  const int64_t b = qr / K;
+  const int i = (int)(qr - b * K);
+  const int64_t sr = b * (c.rows.np + c.rows.nq) + c.rows.np + i;
+  const CutRec cr = wc.cut[sr];
+  if (cr.bad) {
+    if (threadIdx.x == 0) c.draft[qr] = -1;
+    return;
+  }
+  const int x = wide_draw<DT, AL, kDWT>(c, cr, c.rows.row(sr), c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft), s_sb);
+  if (threadIdx.x == 0) c.draft[qr] = x;
+}
+
+// Tree node drafts: node n is the sib[n]-th child of row r = prow[n] and is
+// drawn from draft row r with U(seed, step, b, r, 0x40000000 + sib[n]) ("Uno"
+// research explainer, §3.4: the Tree Sampler's candidates come from the draft
+// distributions); -1 for an invalid row.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kDWT) void k_wtdraft(LinCfg c, WideCfg wc, TreeTopo tp, TreeCfg tc) {
+  extern __shared__ double s_sb[];
+  const int N = tc.N;
+  const int64_t b = blockIdx.x / N;
+  const int n = (int)(blockIdx.x - b * N);
+  const int r = tp.prow[n];
+  const int64_t sr = b * 2 * (N + 1) + (N + 1) + r;
+  const CutRec cr = wc.cut[sr];
+  if (cr.bad) {
+    if (threadIdx.x == 0) tc.tokens[b * N + n] = -1;
+    return;
+  }
+  const double u = c.rng.u((uint32_t)b, (uint32_t)r, kDrawDraft + (uint32_t)tp.sib[n]);
+  const int x = wide_draw<DT, AL, kDWT>(c, cr, c.rows.row(sr), u, s_sb);
+  if (threadIdx.x == 0) tc.tokens[b * N + n] = x;
 }
 
 // --------------------------------------------------------------- resolve --
@@ -611,6 +645,148 @@ __global__ __launch_bounds__(kWT) void k_wresolve(LinCfg c, WideCfg wc) {
   }
 }
 
+// ------------------------------------------------------------------ tree --
+// Tree verification on filtered rows ("Uno" research explainer, §3.4;
+// recursive rejection over the children of a node, in ascending node id), one
+// workgroup per request. At a row with children the running target after j
+// rejections is (P - c_j Q)+ / G_j with c_0 = 0, G_0 = 1, c_{j+1} = c_j + G_j
+// and G_j = sum_t max(0, P(t) - c_j Q(t)), which equals the normalised
+// max(0, r_j - Q) of the recursive update; one fp64 pass over the row pair
+// gives each new G. A vanished residual (G = 0) leaves the target as it was.
+// The final draw (all children rejected, or a row without children) is an
+// fp64 inverse-CDF draw from the running target with U(..., row, 0).
+template <int DT, bool AL>
+__global__ __launch_bounds__(kTT) void k_wtree(LinCfg c, WideCfg wc, TreeTopo tp, TreeCfg tc) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  constexpr int EPL = kSB / kWave;
+  extern __shared__ double s_sb[];  // per sub-block sums of the final draw's weights
+  const int64_t b = blockIdx.x;
+  const int N = tc.N, D = tc.D, R = N + 1, t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
+  const CutRec* cut = wc.cut + b * 2 * R;
+  __shared__ int s_bad;
+  __shared__ int s_tok[kMaxNodes];
+  __shared__ double shd[kTTW];
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  for (int i = t; i < 2 * R; i += kTT)
+    if (cut[i].bad) atomicOr(&s_bad, 1);
+  for (int n = t; n < N; n += kTT) {
+    const int x = tc.tokens[b * N + n];
+    s_tok[n] = x;
+    if (x < 0 || x >= c.V) atomicOr(&s_bad, 1);
+  }
+  for (int i = t; i <= D; i += kTT) c.out_tokens[b * (D + 1) + i] = -1;
+  for (int i = t; i < D; i += kTT) tc.out_path[b * D + i] = -1;
+  __syncthreads();
+  if (s_bad) {
+    if (t == 0) c.out_len[b] = -1;
+    return;
+  }
+  const double c64 = c.c64;
+  int row = 0, len = 0;  // uniform across the workgroup
+  for (;;) {
+    const CutRec cp = cut[row], cq = cut[R + row];
+    const char* prow = c.rows.row(b * 2 * R + row);
+    const char* qrow = c.rows.row(b * 2 * R + R + row);
+    const double mcp = (double)cp.m * c64, mcq = (double)cq.m * c64;
+    const double isp = 1.0 / cp.S, isq = 1.0 / cq.S;
+    auto probs = [&](int x, double& P, double& Q) {
+      const float ap = E::load1(prow, x), aq = E::load1(qrow, x);
+      P = kept_by(wkey(ap), x, cp.key, cp.id) ? wweight(ap, c64, mcp) * isp : 0.0;
+      Q = kept_by(wkey(aq), x, cq.key, cq.id) ? wweight(aq, c64, mcq) * isq : 0.0;
+    };
+    // max(0, P - cc Q) of the 16 tokens from j0 (0 past V)
+    auto resid16 = [&](int64_t j0, double cc, double (&w)[EPL]) {
+#pragma unroll
+      for (int v = 0; v < EPL / EPV; ++v) {
+        float xp[EPV], xq[EPV];
+        wvec<DT, AL>(prow, c.V, c.nvec, j0 / EPV + v, xp);
+        if (cc != 0.0) wvec<DT, AL>(qrow, c.V, c.nvec, j0 / EPV + v, xq);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const int64_t j = j0 + v * EPV + e;
+          double pp = 0.0, qq = 0.0;
+          if (j < c.V) {
+            if (kept_by(wkey(xp[e]), j, cp.key, cp.id)) pp = wweight(xp[e], c64, mcp) * isp;
+            if (cc != 0.0 && kept_by(wkey(xq[e]), j, cq.key, cq.id)) qq = wweight(xq[e], c64, mcq) * isq;
+          }
+          w[v * EPV + e] = cc != 0.0 ? fmax(0.0, pp - cc * qq) : pp;
+        }
+      }
+    };
+    // sum of max(0, P - cc Q) over the 16 tokens from j0, one vector at a time
+    auto rsum16 = [&](int64_t j0, double cc) {
+      double acc = 0.0;
+      for (int v = 0; v < EPL / EPV; ++v) {
+        float xp[EPV], xq[EPV];
+        wvec<DT, AL>(prow, c.V, c.nvec, j0 / EPV + v, xp);
+        wvec<DT, AL>(qrow, c.V, c.nvec, j0 / EPV + v, xq);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const int64_t j = j0 + v * EPV + e;
+          double pp = 0.0, qq = 0.0;
+          if (j < c.V) {
+            if (kept_by(wkey(xp[e]), j, cp.key, cp.id)) pp = wweight(xp[e], c64, mcp) * isp;
+            if (kept_by(wkey(xq[e]), j, cq.key, cq.id)) qq = wweight(xq[e], c64, mcq) * isq;
+          }
+          acc += fmax(0.0, pp - cc * qq);
+        }
+      }
+      return acc;
+    };
+    const int k0 = tp.off[row], nk = tp.off[row + 1] - k0;
+    double cc = 0.0, G = 1.0;
+    int next = -1;
+    for (int j = 0; j < nk; ++j) {
+      const int child = tp.kids[k0 + j];
+      double P, Q;
+      probs(s_tok[child], P, Q);
+      const double rt = fmax(0.0, P - cc * Q) / G;
+      if (c.rng.u((uint32_t)b, (uint32_t)row, kDrawAccept + (uint32_t)j) * Q < rt) {
+        next = child;
+        break;
+      }
+      // rejected: G(c + G) over the row pair
+      const double cn = cc + G;
+      double part = 0.0;
+      for (int sb = wave; sb < c.nsb; sb += kTTW) part += rsum16((int64_t)sb * kSB + (int64_t)lane * EPL, cn);
+      const double Gn = block_sum<kTT>(part, shd);
+      if (Gn > 0.0) {
+        cc = cn;
+        G = Gn;
+      }
+    }
+    if (next >= 0) {
+      if (t == 0) {
+        tc.out_path[b * D + len] = next;
+        c.out_tokens[b * (D + 1) + len] = s_tok[next];
+      }
+      ++len;
+      row = next + 1;
+      continue;
+    }
+    // final draw from the running target
+    for (int sb = wave; sb < c.nsb; sb += kTTW) {
+      const double s = wave_sum(rsum16((int64_t)sb * kSB + (int64_t)lane * EPL, cc));
+      if (lane == 0) s_sb[sb] = s;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    double mine = 0.0;
+    for (int sb = lane; sb < c.nsb; sb += kWave) mine += s_sb[sb];
+    const double W = wave_sum(mine);
+    const double u = c.rng.u((uint32_t)b, (uint32_t)row, kDrawFinal);
+    const int y = wave_pick(c.nsb, c.V, u * W, [&](int sb) { return s_sb[sb]; },
+                            [&](int64_t j0, double(&w)[EPL]) { resid16(j0, cc, w); });
+    if (lane == 0) {
+      c.out_tokens[b * (D + 1) + len] = y;
+      c.out_len[b] = len;
+    }
+    return;
+  }
+}
+
 // ------------------------------------------------------------ launchers --
 template <int DT, bool AL>
 static hipError_t wide_t(const LinCfg& c, const WideCfg& wc, bool draft_only, hipStream_t s) {
@@ -626,6 +802,22 @@ static hipError_t wide_t(const LinCfg& c, const WideCfg& wc, bool draft_only, hi
 
 hipError_t launch_wide(const LinCfg& c, const WideCfg& wc, int dtype, bool draft_only, hipStream_t s) {
   return PSI_DISPATCH(wide_t, dtype, c.aligned, c, wc, draft_only, s);
+}
+
+template <int DT, bool AL>
+static hipError_t wide_tree_t(const LinCfg& c, const WideCfg& wc, const TreeTopo& tp, const TreeCfg& tc,
+                              hipStream_t s) {
+  const int64_t rows = c.B * 2 * (int64_t)(tc.N + 1);
+  const size_t lds = (size_t)c.nsb * sizeof(double);
+  PSI_LAUNCH(s, (k_wcut<DT, AL>), dim3((unsigned)rows), dim3(kWT), c, wc);
+  if (c.fused) PSI_LAUNCH_LDS(s, (k_wtdraft<DT, AL>), dim3((unsigned)(c.B * tc.N)), dim3(kDWT), lds, c, wc, tp, tc);
+  PSI_LAUNCH_LDS(s, (k_wtree<DT, AL>), dim3((unsigned)c.B), dim3(kTT), lds, c, wc, tp, tc);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_wide(const LinCfg& c, const WideCfg& wc, const TreeTopo& tp, const TreeCfg& tc, int dtype,
+                            hipStream_t s) {
+  return PSI_DISPATCH(wide_tree_t, dtype, c.aligned, c, wc, tp, tc, s);
 }
 
 }  // namespace psi

@@ -151,6 +151,38 @@ def test_tree_filtered(top_k, top_p):
         compare_tree(g, o, name="tree").check()
 
 
+@pytest.mark.parametrize("topo,dtype,V,top_k,top_p,noise", [
+    ("wide", "f32", 4000, 0, 0.9, 0.8), ("wide", "bf16", 3001, 300, 1.0, 2.0), ("wide", "f32", 5000, 500, 0.7, 2.5),
+    ("branch", "bf16", 6000, 0, 0.5, 1.5), ("random", "f32", 2048, 2048, 0.95, 1.0)])
+def test_tree_filtered_wide(topo, dtype, V, top_k, top_p, noise):
+    """Filters without a small bound on the kept set (top-p alone, top_k above
+    256, top_k >= V with a top-p); high draft noise makes several rejections
+    at a node, each a residual pass over the filtered row pair."""
+    parent = {"wide": wide_parent(12, 2), "branch": synth.branch_chain_parent(4, 8),
+              "random": random_parent(40, 7)}[topo]
+    N, B = len(parent), 6
+    p, q = synth.pair(B, N + 1, N + 1, V, dtype, seed=V + top_k, sd_a=2.0, mode=0, sd_noise=noise)
+    tally = Tally(f"tree wide {topo} k={top_k} p={top_p}")
+    for step in range(3):
+        print(f"[tree wide] {topo} {dtype} V={V} k={top_k} p={top_p} step {step}", flush=True)
+        g, o = _case(p, q, parent, T=1.0, top_k=top_k, top_p=top_p, seed=4, step=step, tally=tally)
+        tally += compare_tree(g, o)
+    tally.check()
+
+
+def test_tree_workload_top_p_alone():
+    """The tree workload at full size ([4, 33, 151936] bf16) with top_k = 0 and
+    top_p = 0.95, node drafts fused, 16 random-number seeds."""
+    parent = synth.branch_chain_parent(4, 8)
+    p, q = synth.tree_inputs("tree", seed=0)
+    tally = Tally("tree workload top-p alone x16")
+    for seed in range(16):
+        print(f"[tree wide] full size seed {seed}", flush=True)
+        g, o = _case(p, q, parent, top_k=0, top_p=0.95, seed=seed, step=seed, tally=tally)
+        tally += compare_tree(g, o)
+    tally.check()
+
+
 def test_tree_errors():
     parent = synth.branch_chain_parent(2, 3)
     N, V, B = len(parent), 1000, 6
@@ -167,6 +199,10 @@ def test_tree_errors():
     g, o = _case(p, q, parent)  # fused: request 2 has no valid drafts
     assert np.all(g["nodes"].cpu().numpy()[2] == -1)
     compare_tree(g, o, name="tree").check()
+    for top_k, top_p in ((0, 0.9), (400, 1.0)):  # the same through the cut search
+        g, o = _case(p, q, parent, nodes=nodes, top_k=top_k, top_p=top_p)
+        assert list(g["len"].cpu().numpy()[[1, 2, 3, 4]]) == [-1] * 4
+        compare_tree(g, o, name="tree wide errors").check()
 
 
 def test_tree_first_token_law():
