@@ -61,9 +61,8 @@ extern "C" {
                                    top_p outside (0, 1], top_k < 0, workspace not 256-byte
                                    aligned, malformed tree topology */
 #define PSISPEC_EUNSUPPORTED -2 /* dtype other than F32/BF16, K or tree depth > 64,
-                                   tree with more than 256 nodes, filtered sampling
-                                   (temperature > 0 with top-k or top-p active) whose
-                                   top_k is not in [1, min(V-1, PSISPEC_MAX_TOPK)] */
+                                   tree with more than 256 nodes; the Tree Sampler
+                                   calls' own limits (see there) */
 #define PSISPEC_EWORKSPACE   -3 /* ws_bytes smaller than psispec_workspace_bytes(...) */
 #define PSISPEC_EHIP         -4 /* a HIP launch failed */
 #define PSISPEC_ESCRATCH     -5 /* psispec_verify_linear_noalloc: the call needs more than
@@ -83,7 +82,8 @@ extern "C" {
 /* ---- limits ----------------------------------------------------------------- */
 #define PSISPEC_MAX_K         64   /* draft positions per request (one wave64 ballot) */
 #define PSISPEC_MAX_TREE_NODES 256 /* tree nodes per request */
-#define PSISPEC_MAX_TOPK      256  /* largest top_k of filtered sampling */
+#define PSISPEC_MAX_TOPK      256  /* largest top_k of the kept-set-list filter path, and
+                                      of the Tree Sampler's candidates per position */
 #define PSISPEC_NOALLOC_SCRATCH_BYTES (32u << 20) /* device scratch of psispec_verify_linear_noalloc */
 
 /*
@@ -93,7 +93,10 @@ extern "C" {
  *                lowest index on ties; draft accepted iff it equals the target
  *                argmax; no random numbers are drawn; top_k/top_p ignored).
  *   top_k        0 or >= V disables; otherwise keep the top_k largest z per
- *                row (ties: the lower token id wins).
+ *                row (ties: the lower token id wins). Every top_k is accepted:
+ *                up to PSISPEC_MAX_TOPK the kept set is gathered as a list in
+ *                one pass over the row; above it, and for top-p without a
+ *                top-k, a cut search reads each row several times (slower).
  *   top_p        1 disables; otherwise, among the tokens kept by top-k, keep the
  *                shortest prefix of the probability-sorted list (ties: lower id
  *                first) whose cumulative probability reaches top_p (at least
