@@ -234,6 +234,11 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed, only=None):
                                                              seed=seed, step=i, fused=True, out=outs, workspace=ws,
                                                              stream=stream), steps, 3, stream)
         line("filtered_topk50_topp0.95_B128_K16_V128256_f32", ms, bytes_alg(Bf, Kf, Vf, 4), Bf * Kf, {})
+        # top-p without a top-k: the cut search reads each row several times
+        ms = time_calls(torch, lambda i: psi.verify_linear(pd, qd, dr, temperature=1.0, top_k=0, top_p=top_p,
+                                                             seed=seed, step=i, fused=True, out=outs, workspace=ws,
+                                                             stream=stream), min(steps, 10), 2, stream)
+        line("filtered_topp0.95_alone_B128_K16_V128256_f32", ms, bytes_alg(Bf, Kf, Vf, 4), Bf * Kf, {})
         ms = time_calls(torch, lambda i: psi.verify_linear(pd, qd, dr, temperature=0.0, fused=True, out=outs,
                                                              workspace=ws, stream=stream), steps, 3, stream)
         line("greedy_B128_K16_V128256_f32", ms, bytes_alg(Bf, Kf, Vf, 4), Bf * Kf, {})
@@ -261,6 +266,11 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed, only=None):
                         steps, 5, stream)
         line("tree_4x8_B4_N32_V151936_bf16", ms, Bt * 2 * (Nt + 1) * Vt * 2 + 4 * Bt * Nt + 4 * Bt * (2 * D + 2),
              Bt * (Nt + 1), {"note": "latency-bound: 10 kernel launches per call"})
+        ms = time_calls(torch, lambda i: psi.verify_tree(*copies[i % 4], parent, nodes, temperature=1.0, top_k=0,
+                                                           top_p=float(np.float32(0.95)), seed=seed, step=i, fused=True,
+                                                           out=outs, workspace=ws, stream=stream),
+                        min(steps, 20), 3, stream)
+        line("tree_topp0.95_alone_B4_N32_V151936_bf16", ms, Bt * 2 * (Nt + 1) * Vt * 2, Bt * (Nt + 1), {})
         del copies, ws
         torch.cuda.empty_cache()
 

@@ -38,7 +38,7 @@ namespace psi {
 
 namespace {
 
-constexpr int kWT = 1024;          // threads of a cut or resolve workgroup
+constexpr int kWT = 1024;          // threads of a resolve workgroup
 constexpr int kWTW = kWT / kWave;  // waves of one
 constexpr int kDWT = 512;          // threads of a draft-row workgroup
 constexpr int kTT = 512;           // threads of a tree-walk workgroup (registers for the fp64 passes)
@@ -126,18 +126,19 @@ __device__ __forceinline__ long long block_scan_ll(long long v, long long* sh, l
 // From the top bin down, the first bin d at which above + (sum of bins >= d)
 // reaches need; returns d and sets *above to the sum of the bins above d
 // added to it. If no bin reaches need, the lowest non-empty bin. `val` holds
-// nb bins (nb a multiple of kWT / 4 ... up to kHist); every thread reads
-// nb / kWT of them.
-template <class T>
+// nb <= kHist bins; of NT threads, thread t owns the ceil(nb / NT) bins of
+// descending rank from t * ceil(nb / NT). `shl` needs NT / kWave + 1 slots.
+template <int NT, class T>
 __device__ int select_bin(const T* val, int nb, unsigned long long need, unsigned long long* above, long long* shl,
                           int* shi) {
+  constexpr int NW = NT / kWave;
   const int t = threadIdx.x;
-  const int per = (nb + kWT - 1) / kWT;
+  const int per = (nb + NT - 1) / NT;
   // thread t owns bins of descending rank [t * per, t * per + per)
   long long mine = 0;
   for (int r = t * per; r < t * per + per && r < nb; ++r) mine += (long long)val[nb - 1 - r];
   long long tot;
-  const long long excl = block_scan_ll<kWT>(mine, shl, &tot);
+  const long long excl = block_scan_ll<NT>(mine, shl, &tot);
   if (t == 0) {
     shi[0] = -1;
     shi[1] = -1;
@@ -165,10 +166,10 @@ __device__ int select_bin(const T* val, int nb, unsigned long long need, unsigne
   if (rsel >= 0 && rsel >= t * per && rsel < t * per + per) {
     unsigned long long acc = base + (unsigned long long)excl;
     for (int r = t * per; r < rsel; ++r) acc += (unsigned long long)val[nb - 1 - r];
-    shl[kWTW] = (long long)acc;
+    shl[NW] = (long long)acc;
   }
   __syncthreads();
-  if (rsel >= 0) *above = (unsigned long long)shl[kWTW];
+  if (rsel >= 0) *above = (unsigned long long)shl[NW];
   __syncthreads();
   return rsel < 0 ? -1 : nb - 1 - rsel;
 }
@@ -176,81 +177,122 @@ __device__ int select_bin(const T* val, int nb, unsigned long long need, unsigne
 }  // namespace
 
 // ------------------------------------------------------------------ cut --
+constexpr int kCT = 512;             // threads of a cut workgroup
+constexpr int kCTW = kCT / kWave;
+constexpr int kCutNV = 4;            // 16-byte vectors in flight per thread in the cut passes
+
+// Calls f(j, a_j) for every logit of a row: thread t takes vectors t, t + NT,
+// ... in groups of NV whose loads are all issued before any is used.
+template <int DT, bool AL, int NT, int NV, class F>
+__device__ __forceinline__ void row_each(const char* row, int V, int nvec, F&& f) {
+  constexpr int EPV = Elem<DT>::kPerVec;
+  const int nv = (V + EPV - 1) / EPV;
+  for (int v0 = threadIdx.x; v0 < nv; v0 += NT * NV) {
+    float x[NV][EPV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) wvec<DT, AL>(row, V, nvec, (int64_t)v0 + k * NT, x[k]);
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const int64_t j = ((int64_t)v0 + k * NT) * EPV + e;
+        if (j < V) f(j, x[k][e]);
+      }
+  }
+}
+
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWT) void k_wcut(LinCfg c, WideCfg wc) {
+__global__ __launch_bounds__(kCT) void k_wcut(LinCfg c, WideCfg wc) {
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec;
+  constexpr int NV = kCutNV;
   const int64_t sr = blockIdx.x;
   const char* row = c.rows.row(sr);
   const int V = c.V, t = threadIdx.x;
   const int nv = (V + EPV - 1) / EPV;
   __shared__ uint32_t s_cnt[kHist];
   __shared__ unsigned long long s_mass[kHist];
-  __shared__ long long shl[kWTW + 1];
-  __shared__ float shf[kWTW];
-  __shared__ double shd[kWTW];
+  __shared__ long long shl[kCTW + 1];
+  __shared__ float shf[kCTW];
+  __shared__ double shd[kCTW];
   __shared__ int shi[4];
+  // radix levels: key bits [20, 32), [8, 20), [0, 8)
+  auto kShift = [](int L) { return L == 0 ? 20 : (L == 1 ? 8 : 0); };
+  auto kBits = [](int L) { return L == 2 ? 8 : 12; };
+  for (int i = t; i < kHist; i += kCT) {
+    s_cnt[i] = 0;
+    s_mass[i] = 0;
+  }
+  __syncthreads();
 
-  // ---- pass 0: maximum, validity, finite count
+  // ---- pass 0: maximum, validity, finite count, and the first count level
+  // of the top-k selection (it needs no maximum)
+  const bool kwant = wc.top_k > 0;
   float m = -INFINITY;
   long long nf = 0, bad = 0;
-  for (int v = t; v < nv; v += kWT) {
-    float x[EPV];
-    wvec<DT, AL>(row, V, c.nvec, v, x);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      if ((int64_t)v * EPV + e >= V) continue;
-      m = fmaxnan(m, x[e]);
-      if (isnan(x[e]) || (isinf(x[e]) && x[e] > 0.0f)) bad = 1;
-      if (!is_neg_inf(x[e])) ++nf;
+  row_each<DT, AL, kCT, NV>(row, V, c.nvec, [&](int64_t, float a) {
+    m = fmaxnan(m, a);
+    if (isnan(a) || (isinf(a) && a > 0.0f)) bad = 1;
+    if (!is_neg_inf(a)) {
+      ++nf;
+      if (kwant) atomicAdd(&s_cnt[wkey(a) >> kShift(0)], 1u);
     }
-  }
-  m = block_max<kWT>(m, shf);
-  bad = block_sum_ll<kWT>(bad, shl);
-  nf = block_sum_ll<kWT>(nf, shl);
+  });
+  m = block_max<kCT>(m, shf);
+  bad = block_sum_ll<kCT>(bad, shl);
+  nf = block_sum_ll<kCT>(nf, shl);
   CutRec* out = wc.cut + sr;
   if (bad || nf == 0 || isnan(m) || isinf(m)) {
     if (t == 0) *out = CutRec{m, kKeyNegInf, -1, 1, 0.0, 0.0};
     return;
   }
   const double c64 = c.c64, mc = (double)m * c64;
-  // scale of the fixed-point masses: every weight is <= 1 and V of them sum
-  // below 2^62
+  // Fixed-point masses of the top-p guess: 2^((a - m) c) in binary32 (at
+  // most 1 + 2^-23) scaled so that V of them stay below 2^63. The guess only
+  // picks the first key to try; exact fp64 sums decide.
+  const float c32 = c.c32, mc32 = m * c.c32;
   const int lg = 64 - __clzll((unsigned long long)V);
   const double fx_scale = ldexp(1.0, 62 - lg);
+  auto fxw = [&](float a) {
+    return (unsigned long long)((double)__builtin_amdgcn_exp2f(__builtin_fmaf(a, c32, -mc32)) * fx_scale);
+  };
 
   // tokens kept by the top-k stage: kept_by(key, j, kkey, kid) (every finite
   // token until a top-k cut is set)
   uint32_t kkey = kKeyNegInf;
   int32_t kid = -1;
 
-  // id of the r-th smallest kept token (1-based) whose key is `key`: rounds of kWT
-  // vectors in id order, each counted and scanned in thread order
+  // id of the r-th smallest kept token (1-based) whose key is `key`: rounds of
+  // kCT * NV vectors in id order (thread t takes NV consecutive vectors), each
+  // counted and scanned in thread order
   auto id_select = [&](uint32_t key, long long r) -> int32_t {
     long long base = 0;
     if (t == 0) shi[2] = -1;
     __syncthreads();
-    for (int v0 = 0; v0 < nv; v0 += kWT) {
-      const int v = v0 + t;
-      float x[EPV];
+    for (int v0 = 0; v0 < nv; v0 += kCT * NV) {
+      const int vt = v0 + t * NV;
+      float x[NV][EPV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) wvec<DT, AL>(row, V, c.nvec, (int64_t)vt + k, x[k]);
       int cnt = 0;
-      if (v < nv) {
-        wvec<DT, AL>(row, V, c.nvec, v, x);
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const int64_t j = (int64_t)v * EPV + e;
-          cnt += (j < V && wkey(x[e]) == key && kept_by(key, j, kkey, kid)) ? 1 : 0;
+          const int64_t j = ((int64_t)vt + k) * EPV + e;
+          cnt += (j < V && wkey(x[k][e]) == key && kept_by(key, j, kkey, kid)) ? 1 : 0;
         }
-      }
       long long tot;
-      const long long excl = block_scan_ll<kWT>(cnt, shl, &tot);
-      if (v < nv && base + excl < r && r <= base + excl + cnt) {
-        long long k = base + excl;
+      const long long excl = block_scan_ll<kCT>(cnt, shl, &tot);
+      if (base + excl < r && r <= base + excl + cnt) {
+        long long n = base + excl;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const int64_t j = (int64_t)v * EPV + e;
-          if (j < V && wkey(x[e]) == key && kept_by(key, j, kkey, kid) && ++k == r) shi[2] = (int)j;
-        }
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const int64_t j = ((int64_t)vt + k) * EPV + e;
+            if (j < V && wkey(x[k][e]) == key && kept_by(key, j, kkey, kid) && ++n == r) shi[2] = (int)j;
+          }
       }
       __syncthreads();
       const int found = shi[2];
@@ -261,43 +303,36 @@ __global__ __launch_bounds__(kWT) void k_wcut(LinCfg c, WideCfg wc) {
     return -1;
   };
 
-  // one radix level over the keys matching (key & pmask) == prefix among the
-  // kept-by-top-k tokens: counts (and fixed-point masses when MASS) of the
-  // `bits` key bits below `shift`
-  auto level = [&](uint32_t prefix, uint32_t pmask, int shift, int bits, bool mass) {
-    const int nb = 1 << bits;
-    for (int i = t; i < nb; i += kWT) {
+  // radix level L > 0 over the kept tokens whose key matches (key & pmask) ==
+  // prefix: counts, or fixed-point masses when `mass`, per value of the
+  // kBits(L) key bits below kShift(L)
+  auto level = [&](int L, uint32_t prefix, uint32_t pmask, bool mass) {
+    const int nb = 1 << kBits(L);
+    for (int i = t; i < nb; i += kCT) {
       s_cnt[i] = 0;
       s_mass[i] = 0;
     }
     __syncthreads();
-    for (int v = t; v < nv; v += kWT) {
-      float x[EPV];
-      wvec<DT, AL>(row, V, c.nvec, v, x);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const int64_t j = (int64_t)v * EPV + e;
-        const uint32_t key = wkey(x[e]);
-        if (j >= V || !kept_by(key, j, kkey, kid) || (key & pmask) != prefix) continue;
-        const int d = (int)((key >> shift) & (uint32_t)(nb - 1));
-        atomicAdd(&s_cnt[d], 1u);
-        if (mass) atomicAdd(&s_mass[d], (unsigned long long)(wweight(x[e], c64, mc) * fx_scale));
-      }
-    }
+    row_each<DT, AL, kCT, NV>(row, V, c.nvec, [&](int64_t j, float a) {
+      const uint32_t key = wkey(a);
+      if (!kept_by(key, j, kkey, kid) || (key & pmask) != prefix) return;
+      const int d = (int)((key >> kShift(L)) & (uint32_t)(nb - 1));
+      if (mass) atomicAdd(&s_mass[d], fxw(a));
+      else atomicAdd(&s_cnt[d], 1u);
+    });
     __syncthreads();
   };
-  constexpr int kShift[3] = {20, 8, 0}, kBits[3] = {12, 12, 8};
 
   // ---- top-k: the top_k-th token of the order
-  const bool kact = wc.top_k > 0 && (long long)wc.top_k < nf;
+  const bool kact = kwant && (long long)wc.top_k < nf;
   if (kact) {
     uint32_t prefix = 0, pmask = 0;
     unsigned long long above = 0;
     for (int L = 0; L < 3; ++L) {
-      level(prefix, pmask, kShift[L], kBits[L], false);
-      const int d = select_bin(s_cnt, 1 << kBits[L], (unsigned long long)wc.top_k, &above, shl, shi);
-      prefix |= (uint32_t)d << kShift[L];
-      pmask |= (uint32_t)((1u << kBits[L]) - 1u) << kShift[L];
+      if (L > 0) level(L, prefix, pmask, false);
+      const int d = select_bin<kCT>(s_cnt, 1 << kBits(L), (unsigned long long)wc.top_k, &above, shl, shi);
+      prefix |= (uint32_t)d << kShift(L);
+      pmask |= (uint32_t)((1u << kBits(L)) - 1u) << kShift(L);
     }
     const long long r = (long long)wc.top_k - (long long)above;  // ties of that key taken, in id order
     const int32_t id = id_select(prefix, r);
@@ -305,34 +340,44 @@ __global__ __launch_bounds__(kWT) void k_wcut(LinCfg c, WideCfg wc) {
     kid = id;
   }
 
-  // ---- mass of the kept-by-top-k tokens (fp64, fixed order)
+  // ---- mass of the kept-by-top-k tokens (fp64, fixed order), and with a
+  // top-p the first mass level of the guess and the total fixed-point mass
   const bool pact = wc.top_p < 1.0;
-  double S = 0.0;
-  for (int v = t; v < nv; v += kWT) {
-    float x[EPV];
-    wvec<DT, AL>(row, V, c.nvec, v, x);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      const int64_t j = (int64_t)v * EPV + e;
-      if (j < V && kept_by(wkey(x[e]), j, kkey, kid)) S += wweight(x[e], c64, mc);
-    }
+  if (pact) {
+    for (int i = t; i < kHist; i += kCT) s_mass[i] = 0;
+    __syncthreads();
   }
-  S = block_sum<kWT>(S, shd);
+  double S = 0.0;
+  long long M = 0;
+  row_each<DT, AL, kCT, NV>(row, V, c.nvec, [&](int64_t j, float a) {
+    const uint32_t key = wkey(a);
+    if (!kept_by(key, j, kkey, kid)) return;
+    S += wweight(a, c64, mc);
+    if (pact) {
+      const unsigned long long f = fxw(a);
+      M += (long long)f;
+      atomicAdd(&s_mass[key >> kShift(0)], f);
+    }
+  });
+  S = block_sum<kCT>(S, shd);
   if (!pact) {
     if (t == 0) *out = CutRec{m, kkey, kid, 0, S, 0.0};
     return;
   }
+  M = block_sum_ll<kCT>(M, shl);
 
-  // ---- top-p: locate the crossing key on fixed-point masses
+  // ---- top-p: the crossing key of the fixed-point masses
   const double target = wc.top_p * S;
   uint32_t prefix = 0, pmask = 0;
-  unsigned long long above = 0;
-  for (int L = 0; L < 3; ++L) {
-    level(prefix, pmask, kShift[L], kBits[L], true);
-    const unsigned long long need = (unsigned long long)(target * fx_scale);
-    const int d = select_bin(s_mass, 1 << kBits[L], need > 0 ? need : 1ull, &above, shl, shi);
-    prefix |= (uint32_t)d << kShift[L];
-    pmask |= (uint32_t)((1u << kBits[L]) - 1u) << kShift[L];
+  {
+    unsigned long long above = 0;
+    const unsigned long long need = (unsigned long long)(wc.top_p * (double)M);
+    for (int L = 0; L < 3; ++L) {
+      if (L > 0) level(L, prefix, pmask, true);
+      const int d = select_bin<kCT>(s_mass, 1 << kBits(L), need > 0 ? need : 1ull, &above, shl, shi);
+      prefix |= (uint32_t)d << kShift(L);
+      pmask |= (uint32_t)((1u << kBits(L)) - 1u) << kShift(L);
+    }
   }
   // ---- confirm on exact fp64 sums. For a probe key k: ma = the mass of the
   // kept tokens above k, cn = the kept tokens at k (all of weight wk). The
@@ -352,26 +397,20 @@ __global__ __launch_bounds__(kWT) void k_wcut(LinCfg c, WideCfg wc) {
     double ma = 0.0;
     long long cn = 0;
     uint32_t up = 0xffffffffu, down = 0u;  // nearest kept keys above and below key_p
-    for (int v = t; v < nv; v += kWT) {
-      float x[EPV];
-      wvec<DT, AL>(row, V, c.nvec, v, x);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const int64_t j = (int64_t)v * EPV + e;
-        const uint32_t key = wkey(x[e]);
-        if (j >= V || !kept_by(key, j, kkey, kid)) continue;
-        if (key > key_p) {
-          ma += wweight(x[e], c64, mc);
-          up = min(up, key);
-        } else if (key == key_p) {
-          ++cn;
-        } else {
-          down = max(down, key);
-        }
+    row_each<DT, AL, kCT, NV>(row, V, c.nvec, [&](int64_t j, float a) {
+      const uint32_t key = wkey(a);
+      if (!kept_by(key, j, kkey, kid)) return;
+      if (key > key_p) {
+        ma += wweight(a, c64, mc);
+        up = min(up, key);
+      } else if (key == key_p) {
+        ++cn;
+      } else {
+        down = max(down, key);
       }
-    }
-    ma = block_sum<kWT>(ma, shd);
-    cn = block_sum_ll<kWT>(cn, shl);
+    });
+    ma = block_sum<kCT>(ma, shd);
+    cn = block_sum_ll<kCT>(cn, shl);
     // nearest keys: wave minimum and maximum, then across the waves
     up = ~wave_max_u32(~up);
     down = wave_max_u32(down);
@@ -791,7 +830,7 @@ __global__ __launch_bounds__(kTT) void k_wtree(LinCfg c, WideCfg wc, TreeTopo tp
 template <int DT, bool AL>
 static hipError_t wide_t(const LinCfg& c, const WideCfg& wc, bool draft_only, hipStream_t s) {
   const int64_t rows = c.B * (c.rows.np + c.rows.nq);
-  PSI_LAUNCH(s, (k_wcut<DT, AL>), dim3((unsigned)rows), dim3(kWT), c, wc);
+  PSI_LAUNCH(s, (k_wcut<DT, AL>), dim3((unsigned)rows), dim3(kCT), c, wc);
   if (c.fused || draft_only)
     PSI_LAUNCH_LDS(s, (k_wdraft<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kDWT), (size_t)c.nsb * sizeof(double), c,
                    wc);
@@ -809,7 +848,7 @@ static hipError_t wide_tree_t(const LinCfg& c, const WideCfg& wc, const TreeTopo
                               hipStream_t s) {
   const int64_t rows = c.B * 2 * (int64_t)(tc.N + 1);
   const size_t lds = (size_t)c.nsb * sizeof(double);
-  PSI_LAUNCH(s, (k_wcut<DT, AL>), dim3((unsigned)rows), dim3(kWT), c, wc);
+  PSI_LAUNCH(s, (k_wcut<DT, AL>), dim3((unsigned)rows), dim3(kCT), c, wc);
   if (c.fused) PSI_LAUNCH_LDS(s, (k_wtdraft<DT, AL>), dim3((unsigned)(c.B * tc.N)), dim3(kDWT), lds, c, wc, tp, tc);
   PSI_LAUNCH_LDS(s, (k_wtree<DT, AL>), dim3((unsigned)c.B), dim3(kTT), lds, c, wc, tp, tc);
   return hipGetLastError();
