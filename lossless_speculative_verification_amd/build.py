@@ -72,7 +72,9 @@ def build(verbose: bool = False) -> str:
 
 def function_hashes(asm: str, pattern: str) -> dict:
     """sha256 (16 hex digits) of the instructions of every function whose
-    mangled name matches `pattern`, comments and blank lines dropped."""
+    mangled name matches `pattern`, comments and blank lines dropped, and the
+    function number in local branch labels (.LBB<function>_<block>) removed,
+    so that adding a function to the file does not change the hash."""
     out = {}
     lines = asm.splitlines()
     for i, line in enumerate(lines):
@@ -85,7 +87,7 @@ def function_hashes(asm: str, pattern: str) -> dict:
                 break
             l = l.split(";", 1)[0].strip()
             if l:
-                body.append(l)
+                body.append(re.sub(r"\.LBB\d+_", ".LBB_", l))
         out[m.group(1)] = hashlib.sha256("\n".join(body).encode()).hexdigest()[:16]
     return out
 

@@ -88,10 +88,15 @@ __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool 
 // every thread of the workgroup after each wave has issued the loads of its
 // first sub-blocks and before any weight is read, so that work it does (the
 // tables' scaling, and the barrier after it) hides under their latency.
-template <int DT, bool AL, bool TAB, bool RESID, bool PICK, int NW = kRWaves, class PRE>
+//
+// CHK (target row alone, bfloat16 table): also sets *chk when the row holds a
+// code above the table window that is positive or NaN, i.e. when the row may
+// not qualify for the table rule; other codes above the window (a < -63.25,
+// -inf) read the zero slot as the rule says.
+template <int DT, bool AL, bool TAB, bool RESID, bool PICK, int NW = kRWaves, class PRE, bool CHK = false>
 __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
                                              int sb0, int sb1, const double* tp, const double* tq, const WRow& wp,
-                                             const WRow& wq, float dx, ResRec* s_rec, PRE pre) {
+                                             const WRow& wq, float dx, ResRec* s_rec, PRE pre, int* chk = nullptr) {
   using E = Elem<DT>;
   constexpr int EPV = E::kPerVec;
   constexpr int VPL = kSB / (kWave * EPV);
@@ -132,13 +137,13 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
       if constexpr (TAB) {
         // two bfloat16 codes per word; logits below the window read a zero
         // slot and get their exact weight in the rare call below
-        uint32_t low = 0;
+        uint32_t low = 0, high = 0;
         const char* const tpb = (const char*)tp;
         const char* const tqb = (const char*)tq;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t wpw = word_of(x.p[v], i), wqw = RESID ? word_of(x.q[v], i) : 0u;
-          const uint32_t op = tab_offsets2(wpw, low);
+          const uint32_t op = CHK ? tab_offsets2_chk(wpw, low, high) : tab_offsets2(wpw, low);
           const uint32_t oq = RESID ? tab_offsets2(wqw, low) : 0u;
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
@@ -151,6 +156,22 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
               a = __builtin_fma(in, ep, a);
               bq = __builtin_fma(in, eq, bq);
             }
+          }
+        }
+        if constexpr (CHK) {
+          if (__ballot((high & 0x80008000u) != 0u)) {
+            // exact test of the flagged codes (codes below the window may set
+            // the flag too)
+            bool hit = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int hf = 0; hf < 2; ++hf) {
+                const uint32_t h = (word_of(x.p[v], i) >> (16 * hf)) & 0xffffu;
+                const bool above = !tab_tiny(h) && tab_idx(h) == (uint32_t)kTabW;
+                hit |= above && (!(h & 0x8000u) || (h & 0x7fffu) > 0x7f80u);
+              }
+            if (hit) atomicOr(chk, 1);
           }
         }
         const bool tiny = (low & 0x80008000u) != 0u;
@@ -682,6 +703,110 @@ __global__ __launch_bounds__(kDT) void k_draftrow(LinCfg c) {
   if (lane == 0) c.draft[qr] = x;
 }
 
+// One pass per bfloat16 draft row, with no statistics pass before it (the
+// table temperatures, c.tab): the fp64 weights of the row are summed per
+// sub-block from the unscaled 2^(a c) table (the rule of fweight with scale
+// 1), tracking whether the row holds a code that may break the table rule
+// (positive or NaN above the window). The largest sub-block sum s bounds the
+// row maximum from below, m >= m_lo = (log2 s - 10) / c (a sub-block holds
+// 1,024 weights), so the row qualifies for the rule when (m_lo + 63.25) c >=
+// 100 and nothing was flagged; otherwise it is read again: its exact maximum,
+// then exp2 weights relative to it. The workgroup then writes the row's chunk
+// records for the verification that follows (reference m_lo, or the exact
+// maximum; the draft rows need no statistics pass of their own) and draws
+// x ~ q from its sub-block sums ("Uno" research explainer, §3.3: the drafts of
+// a block are drawn from the draft distributions). -1 for an invalid row.
+template <bool AL>
+__global__ __launch_bounds__(kDT) void k_qrow(LinCfg c) {
+  using E = Elem<kBF16>;
+  extern __shared__ ResRec s_rec[];  // one record per sub-block (.sp)
+  __shared__ double s_tab[kTabSize];
+  __shared__ float shf[kDWaves];
+  __shared__ int s_chk;
+  __shared__ double s_smax;
+  const int64_t qr = blockIdx.x;  // draft row in [0, B*K)
+  const int K = c.K, t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
+  const int64_t b = qr / K;
+  const int i = (int)(qr - b * K);
+  const char* row = qrow_of(c, b, i);
+  const int nsb = c.nsb;
+  const double c64 = c.c64;
+  const WRow w1 = {0.0, 1.0, true};
+  // the table is filled while the first loads of the pass are in flight
+  auto fill = [&]() {
+    fill_tab<kDT>(s_tab, c64);
+    if (t == 0) s_chk = 0;
+    __syncthreads();
+  };
+  resolve_pass<kBF16, AL, true, false, true, kDWaves, decltype(fill), true>(c, b, row, row, 0, nsb, s_tab, s_tab, w1,
+                                                                           w1, 0.0f, s_rec, fill, &s_chk);
+  __syncthreads();
+  if (wave == 0) {
+    double mx = 0.0;
+    for (int sb = lane; sb < nsb; sb += kWave) mx = fmax(mx, s_rec[sb].sp);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    if (lane == 0) s_smax = mx;
+  }
+  __syncthreads();
+  const double smax = s_smax;
+  const bool fast = !s_chk && smax > 0.0 && (::log2(smax) - 10.0) + kTabMaxAbs * c64 >= 100.0;
+  float m;
+  WRow w = w1;
+  if (fast) {
+    m = __double2float_rd((::log2(smax) - 10.0) / c64);
+  } else {
+    // exact maximum and validity, then the weights relative to it
+    constexpr int EPV = E::kPerVec;
+    float mx = -INFINITY;
+    for (int64_t v0 = t; v0 < c.nvec || (!AL && v0 * EPV < c.V); v0 += kDT * 4) {
+      float x[4][EPV];
+      load_vecs<kBF16, AL, 4, kDT>(row, c.V, c.nvec, v0, x);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) mx = fmaxnan(mx, x[k][e]);
+    }
+    m = block_max<kDT>(mx, shf);
+    if (!isnan(m) && !isinf(m)) {
+      w = wrow(false, m, c64);
+      resolve_pass<kBF16, AL, false, false, true, kDWaves>(c, b, row, row, 0, nsb, s_tab, s_tab, w, w, 0.0f, s_rec,
+                                                           [] {});
+    }
+    __syncthreads();
+  }
+  const bool bad = isnan(m) || isinf(m);  // NaN, +inf, or an all -inf row
+  // chunk records of this row: sums of 2^((a - m) c) over each chunk's sub-blocks
+  {
+    constexpr int kSbPerChunk = kWG * kStatNV * E::kPerVec / kSB;
+    StatRec* rec = c.st + (b * (c.rows.np + c.rows.nq) + c.rows.np + i) * (int64_t)c.nch32;
+    const double scale = fast ? exp2_fast(-(double)m * c64) : 1.0;
+    for (int ch = t; ch < c.nch32; ch += kDT) {
+      double sc = 0.0;
+      for (int sb = ch * kSbPerChunk; sb < min(nsb, (ch + 1) * kSbPerChunk); ++sb) sc += s_rec[sb].sp;
+      StatRec r;
+      r.m = m;
+      r.pad = 0;
+      r.s = bad && !is_neg_inf(m) ? NAN : sc * scale;
+      rec[ch] = r;
+    }
+  }
+  if (wave != 0) return;
+  if (bad) {
+    if (lane == 0) c.draft[qr] = -1;
+    return;
+  }
+  const double* const tps = w.tab ? s_tab : nullptr;
+  double mine = 0.0;
+  for (int sb = lane; sb < nsb; sb += kWave) mine += s_rec[sb].sp;
+  const double W = wave_sum(mine);
+  const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
+  const int x = wave_pick(
+      nsb, c.V, u * W, [&](int sb) { return s_rec[sb].sp; },
+      [&](int64_t j0, double(&wt)[16]) { row16<kBF16, AL>(c, row, j0, w, tps, wt); });
+  if (lane == 0) c.draft[qr] = x;
+}
+
 // Draft sampling alone: a request with an invalid draft row gets -1 for all
 // its drafts.
 __global__ __launch_bounds__(kWave) void k_draft_fix(LinCfg c) {
@@ -870,11 +995,20 @@ __global__ __launch_bounds__(kWG) void k_greedy_draft(LinCfg c) {
 template <int DT, bool AL>
 static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
   const int64_t rows = c.B * (2 * c.K + 1);
-  const hipError_t e = launch_stats32(c, rows, DT, s);
-  if (e != hipSuccess) return e;
-  // drafts drawn inside the call, from the statistics of their rows
-  if (c.fused)
-    PSI_LAUNCH_LDS(s, (k_draftrow<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c);
+  if (c.fused && DT == kBF16 && c.tab) {
+    // drafts drawn in one pass over their rows, which also writes those rows'
+    // chunk records; the statistics pass then reads the target rows only
+    PSI_LAUNCH_LDS(s, (k_qrow<AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c);
+    const hipError_t e = launch_stats32_targets(c, DT, s);
+    if (e != hipSuccess) return e;
+  } else {
+    const hipError_t e = launch_stats32(c, rows, DT, s);
+    if (e != hipSuccess) return e;
+    // drafts drawn inside the call, from the statistics of their rows
+    if (c.fused)
+      PSI_LAUNCH_LDS(s, (k_draftrow<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec),
+                     c);
+  }
   // One resolve workgroup per request when there are enough requests to fill
   // the chip (and its sub-block records fit in LDS); otherwise several per
   // request and a separate final step.
@@ -900,9 +1034,14 @@ static hipError_t linear_greedy_t(const LinCfg& c, hipStream_t s) {
 
 template <int DT, bool AL>
 static hipError_t draft_sampled_t(const LinCfg& c, hipStream_t s) {
-  const hipError_t e = launch_stats32(c, c.B * c.K, DT, s);
-  if (e != hipSuccess) return e;
-  PSI_LAUNCH_LDS(s, (k_draftrow<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c);
+  if (DT == kBF16 && c.tab) {
+    PSI_LAUNCH_LDS(s, (k_qrow<AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c);
+  } else {
+    const hipError_t e = launch_stats32(c, c.B * c.K, DT, s);
+    if (e != hipSuccess) return e;
+    PSI_LAUNCH_LDS(s, (k_draftrow<DT, AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec),
+                   c);
+  }
   PSI_LAUNCH(s, k_draft_fix, dim3((unsigned)c.B), dim3(kWave), c);
   return hipGetLastError();
 }

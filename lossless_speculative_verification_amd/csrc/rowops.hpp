@@ -39,6 +39,15 @@ __device__ __forceinline__ uint32_t tab_offsets2(uint32_t w, uint32_t& low) {
   return (w & 0x80008000u) | __builtin_bit_cast(uint32_t, idx << (u16x2_t)3);
 }
 
+// tab_offsets2, and also ORs into `high` a value whose bit 15 in a half is
+// set when that code lies above the window (or, for codes below it, may be).
+__device__ __forceinline__ uint32_t tab_offsets2_chk(uint32_t w, uint32_t& low, uint32_t& high) {
+  const u16x2_t code = __builtin_bit_cast(u16x2_t, w);
+  const u16x2_t d = (code & (u16x2_t)0x7fff) - (u16x2_t)kTabLo;
+  high |= __builtin_bit_cast(uint32_t, d + (u16x2_t)(0x8000 - kTabW));
+  return tab_offsets2(w, low);
+}
+
 struct WRow {
   double mc, scale;
   bool tab;

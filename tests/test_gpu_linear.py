@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import THREADS, Tally, compare_drafts, compare_linear, f32, to_dev
+from gpu_helpers import PROB_RTOL, RESID_RTOL, THREADS, Tally, compare_drafts, compare_linear, f32, to_dev
 from oracle_helpers import alpha, chi2_pvalue, probs
 
 pytestmark = pytest.mark.gpu
@@ -107,20 +107,27 @@ def test_draft_sample_parity():
     tot.check()
 
 
-def test_fused_equals_draft_then_verify():
-    """Fusing the draft draw into verification gives the same bits as
-    psispec_draft_sample followed by a non-fused verify."""
+@pytest.mark.parametrize("wl,T", [("qwen", 0.7), ("tiny", 1.0)])
+def test_fused_equals_draft_then_verify(wl, T):
+    """Fusing the draft draw into verification draws the same drafts, bit for
+    bit, as psispec_draft_sample, and verifies them to the same lengths and
+    tokens as a non-fused verify. The draft rows' normalisers differ in their
+    last bits (bfloat16 fused drafting sums exact fp64 weights in its one pass
+    over each draft row; the non-fused call uses the binary32-grade
+    statistics), so probabilities agree to 1e-5 and residual masses to 1e-9."""
     psi = _psi()
-    p, q = synth.linear_inputs("qwen", seed=2, B=16)
+    p, q = synth.linear_inputs(wl, seed=2, B=16)
     pd, qd = to_dev(p), to_dev(q)
-    for step in range(2):
-        f = psi.verify_linear(pd, qd, None, temperature=0.7, seed=5, step=step, fused=True)
-        d = psi.draft_sample(qd, temperature=0.7, seed=5, step=step)
-        n = psi.verify_linear(pd, qd, d, temperature=0.7, seed=5, step=step)
+    for step in range(3):
+        f = psi.verify_linear(pd, qd, None, temperature=T, seed=5, step=step, fused=True)
+        d = psi.draft_sample(qd, temperature=T, seed=5, step=step)
+        n = psi.verify_linear(pd, qd, d, temperature=T, seed=5, step=step)
         torch.cuda.synchronize()
         assert torch.equal(f["draft"], d)
-        for k in ("tokens", "len", "probs", "resid"):
+        for k in ("tokens", "len"):
             assert torch.equal(f[k], n[k])
+        np.testing.assert_allclose(f["probs"].cpu().numpy(), n["probs"].cpu().numpy(), rtol=PROB_RTOL, atol=0)
+        np.testing.assert_allclose(f["resid"].cpu().numpy(), n["resid"].cpu().numpy(), rtol=RESID_RTOL, atol=0)
 
 
 def test_deterministic_repeat():
@@ -176,6 +183,31 @@ def test_request_errors_and_special_rows():
     assert np.all(g["tokens"].cpu().numpy()[[1, 2, 3, 4, 7]] == -1)
     assert gl[6] == K
     compare_linear(g, o, name="request errors").check()
+
+
+def test_bf16_draft_row_errors():
+    """bfloat16 draft rows holding a positive or a negative NaN, +inf, or only
+    -inf make their request invalid, both in draft sampling alone and with the
+    drafts fused into verification (one pass over each draft row); a partly
+    -inf draft row is valid."""
+    psi = _psi()
+    B, K, V = 8, 3, 5000
+    p, q = synth.pair(B, K + 1, K, V, "bf16", seed=12, sd_a=2.0, mode=0, sd_noise=0.7)
+    q[1, 0, 17] = 0x7FC0   # NaN
+    q[2, 2, 4000] = 0xFFC1  # NaN with the sign bit set
+    q[3, 1, 9] = 0x7F80    # +inf
+    q[4, 0, :] = 0xFF80    # all -inf
+    q[5, 2, :2500] = 0xFF80  # partly -inf: valid
+    bad = [1, 2, 3, 4]
+    for step in range(2):
+        d = psi.draft_sample(to_dev(q), temperature=1.0, seed=3, step=step).cpu().numpy()
+        o, om = oracle.draft_sample(q, 1.0, seed=3, step=step, nthreads=THREADS)
+        assert np.all(d[bad] == -1) and np.all(o[bad] == -1)
+        compare_drafts(d, o, om, name="bf16 draft row errors").check()
+        g, og = _run_pair(p, q, None, 1.0, 3, step, True)
+        assert list(g["len"].cpu().numpy()[bad]) == [-1] * 4
+        assert np.all(g["len"].cpu().numpy()[[0, 5, 6, 7]] >= 0)
+        compare_linear(g, og, fused=True, name="bf16 fused draft row errors").check()
 
 
 def _bf16_bits(f: np.ndarray) -> np.ndarray:
