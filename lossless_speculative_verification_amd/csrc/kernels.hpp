@@ -292,8 +292,6 @@ hipError_t launch_filter_rows(const LinCfg& c, const FiltCfg& f, int64_t rows, i
 hipError_t launch_tree_candidates(const LinCfg& c, const FiltCfg& f, const CandCfg& cc, int dtype, hipStream_t s);
 hipError_t launch_verify_tree_det(const LinCfg& c, const DTreeCfg& d, int dtype, hipStream_t s);
 hipError_t launch_stats32(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
-// The statistics pass over the c.rows.np target rows of each request only.
-hipError_t launch_stats32_targets(const LinCfg& c, int dtype, hipStream_t s);
 // Total-variation distillation loss (tv.hip): c.rows holds one teacher (p) and
 // one student (q) row per loss row (c.B rows); sgn: ceil(V / per-vector) 16-bit
 // sign words per row (written by the first pass when a gradient is asked for).

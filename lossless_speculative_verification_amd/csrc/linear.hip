@@ -93,7 +93,11 @@ __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool 
 // code above the table window that is positive or NaN, i.e. when the row may
 // not qualify for the table rule; other codes above the window (a < -63.25,
 // -inf) read the zero slot as the rule says.
-template <int DT, bool AL, bool TAB, bool RESID, bool PICK, int NW = kRWaves, class PRE, bool CHK = false>
+//
+// RING > 0 keeps RING sub-blocks in flight per wave in a ring of register
+// buffers (RING - 1 ahead of the one being reduced) instead of the default.
+template <int DT, bool AL, bool TAB, bool RESID, bool PICK, int NW = kRWaves, class PRE, bool CHK = false,
+          int RING = 0>
 __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
                                              int sb0, int sb1, const double* tp, const double* tq, const WRow& wp,
                                              const WRow& wq, float dx, ResRec* s_rec, PRE pre, int* chk = nullptr) {
@@ -213,6 +217,25 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
     }
   };
   constexpr int W = NW;
+  if constexpr (RING > 0) {
+    Buf x[RING];
+    int s = sb0 + wave;
+    if (s < sb1) {
+#pragma unroll
+      for (int k = 0; k < RING - 1; ++k) load(s + k * W, x[k]);
+    }
+    pre();
+    if (s >= sb1) return;
+    for (; s < sb1; s += RING * W) {
+#pragma unroll
+      for (int k = 0; k < RING; ++k) {
+        load(s + (k + RING - 1) * W, x[(k + RING - 1) % RING]);
+        reduce(s + k * W, x[k]);
+        if (s + (k + 1) * W >= sb1) return;
+      }
+    }
+    return;
+  }
   Buf x0, x1, x2;
   int s = sb0 + wave;
   if (s < sb1) {
@@ -565,67 +588,94 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
 
 // ----------------------------------------------------------- final step --
 // Final draw when a request's sub-blocks were summed by several workgroups.
+// Sub-blocks per lane whose records the one-wave picks keep in registers
+// (V <= 64 * kPickPer * 1024); larger rows read them from memory.
+constexpr int kPickPer = 4;
+
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_final(LinCfg c) {
-  using E = Elem<DT>;
+__global__ __launch_bounds__(kWave) void k_final(LinCfg c) {
+  // one wave per request: the request's sub-block records from the resolve
+  // parts (one round of loads into registers), the sub-block selection, and a
+  // rescan of one sub-block
   const int64_t b = blockIdx.x;
-  const int t = threadIdx.x, K = c.K;
+  const int lane = threadIdx.x, K = c.K;
+  const int nsb = c.nsb;
+  const ResRec* rr = c.res + b * nsb;
+  const bool inreg = nsb <= kWave * kPickPer;
+  ResRec mr[kPickPer];
+  if (inreg) {
+#pragma unroll
+    for (int k = 0; k < kPickPer; ++k) {
+      const int sb = lane * kPickPer + k;
+      mr[k] = sb < nsb ? rr[sb] : ResRec{0.0, 0.0, 0.0, 0.0};
+    }
+  }
   const ReqState st = c.rs[b];
   if (st.err) return;
   const int n = st.n;
   const bool bonus = n == K;
-  const int nsb = c.nsb;
-  const ResRec* rr = c.res + b * nsb;
-  __shared__ double sh[kWaves];
-  double Sp = 1.0, Sq = 1.0;
-  if (!bonus) {
-    double a = 0.0, q = 0.0;
-    for (int i = t; i < nsb; i += kWG) {
-      a += rr[i].sp;
-      q += rr[i].sq;
-    }
-    Sp = block_sum(a, sh);
-    Sq = block_sum(q, sh);
-  }
   const char* prow = prow_of(c, b, n);
   const char* qrow = bonus ? prow : qrow_of(c, b, n);
+  // sum over this lane's records of f(record)
+  auto lane_sum = [&](auto f) {
+    double acc = 0.0;
+    if (inreg) {
+#pragma unroll
+      for (int k = 0; k < kPickPer; ++k) acc += f(mr[k]);
+    } else {
+      for (int i = lane; i < nsb; i += kWave) acc += f(rr[i]);
+    }
+    return acc;
+  };
+  double Sp = 1.0, Sq = 1.0;
+  if (!bonus) {
+    Sp = wave_sum(lane_sum([](const ResRec& r) { return r.sp; }));
+    Sq = wave_sum(lane_sum([](const ResRec& r) { return r.sq; }));
+  }
+  const double iSp = 1.0 / Sp, iSq = 1.0 / Sq;
   const double c64 = c.c64;
   WRow wp, wq;
   wpair(DT == kBF16 && c.tab, st.mp, st.mq, !bonus, c64, wp, wq);
   norm_pair(wp, wq, !bonus, st.sp_hat, st.sq_hat);
-  double resid = 0.0;
-  int mode = 0;  // 0: target weights of the final row; 1: residual; 2: residual vanished -> target
-  if (!bonus) {
-    double mine = 0.0;
-    for (int i = t; i < nsb; i += kWG) mine += fmax(0.0, rr[i].a * (1.0 / Sp) - rr[i].bq * (1.0 / Sq));
-    resid = block_sum(mine, sh);
-    mode = resid > 0.0 ? 1 : 2;
-  }
-  int y;
-  if (mode == 1) {
-    y = pick_index(
-        nsb, c.V, st.u_final * resid, [&](int i) { return fmax(0.0, rr[i].a * (1.0 / Sp) - rr[i].bq * (1.0 / Sq)); },
-        [&](int64_t j) {
-          const double ep = fweight<DT>(E::load1(prow, j), wp, c64, nullptr);
-          const double eq = fweight<DT>(E::load1(qrow, j), wq, c64, nullptr);
-          return fmax(0.0, ep * (1.0 / Sp) - eq * (1.0 / Sq));
-        },
-        sh);
+  auto wres = [&](const ResRec& r) { return fmax(0.0, r.a * iSp - r.bq * iSq); };
+  const double resid = bonus ? 0.0 : wave_sum(lane_sum(wres));
+  const bool rmode = !bonus && resid > 0.0;  // else the target row (bonus, or a vanished residual)
+  const double W = rmode ? resid : wave_sum(lane_sum([](const ResRec& r) { return r.sp; }));
+  const double target = st.u_final * W;
+  double pref;
+  int sel;
+  if (inreg) {
+    double v[kPickPer];
+#pragma unroll
+    for (int k = 0; k < kPickPer; ++k) v[k] = rmode ? wres(mr[k]) : mr[k].sp;
+    sel = wave_select_reg(nsb, target, v, pref);
   } else {
-    double mine = 0.0;
-    for (int i = t; i < nsb; i += kWG) mine += rr[i].sp;
-    const double W = block_sum(mine, sh);
-    y = pick_index(
-        nsb, c.V, st.u_final * W, [&](int i) { return rr[i].sp; },
-        [&](int64_t j) { return fweight<DT>(E::load1(prow, j), wp, c64, nullptr); }, sh);
+    sel = rmode ? wave_select(nsb, target, [&](int i) { return wres(rr[i]); }, pref)
+                : wave_select(nsb, target, [&](int i) { return rr[i].sp; }, pref);
   }
-  for (int i = t; i <= K; i += kWG) {
+  int y = -1;
+  if (sel >= 0) {
+    const int64_t j0 = (int64_t)sel * kSB + (int64_t)lane * 16;
+    Raw16<DT> rp, rq;
+    raw16<DT, AL>(c, prow, j0, rp);
+    if (rmode) raw16<DT, AL>(c, qrow, j0, rq);
+    double w[16];
+    weights16<DT>(c, rp, j0, wp, nullptr, w);
+    if (rmode) {
+      double wq16[16];
+      weights16<DT>(c, rq, j0, wq, nullptr, wq16);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) w[k] = fmax(0.0, w[k] * iSp - wq16[k] * iSq);
+    }
+    y = wave_rescan(sel, target - pref, w);
+  }
+  for (int i = lane; i <= K; i += kWave) {
     int v = -1;
     if (i < n) v = c.draft[b * K + i];
     else if (i == n) v = y;
     c.out_tokens[b * (K + 1) + i] = v;
   }
-  if (t == 0) {
+  if (lane == 0) {
     c.out_len[b] = n;
     if (c.out_resid) c.out_resid[b] = resid;
   }
@@ -703,6 +753,89 @@ __global__ __launch_bounds__(kDT) void k_draftrow(LinCfg c) {
   if (lane == 0) c.draft[qr] = x;
 }
 
+// The unscaled 2^(a c) table of the draft-row pass, filled by kDT threads
+// with one exp2 pair per 16 slots: thread t takes the 16 codes that share
+// sign, exponent and the top 3 mantissa bits, A = 2^(a_0 c) for the first of
+// them and r = 2^(u c) for the code step u, and slot k gets A * r^k with r^k
+// a running product (relative error below 2e-15, far inside what the draws
+// need). The pass and the draw of k_qrow both read this table.
+__device__ __forceinline__ void fill_tab_steps(double* tab, double c64) {
+  const int t = threadIdx.x;  // kDT = 2 halves x 256 groups of 16 slots
+  static_assert(kDT == 512 && kTabW <= 4096 && kTabNeg == 4096, "one group of 16 slots per thread");
+  const int half = t >> 8, j0 = (t & 255) * 16;
+  const uint32_t code0 = ((uint32_t)half << 15) | (kTabLo + (uint32_t)j0);
+  const float a0 = __uint_as_float(code0 << 16);
+  const float a1 = __uint_as_float((code0 + 1u) << 16);  // same exponent: j0 + 1 < next multiple of 128
+  const double A = exp2_fast((double)a0 * c64);
+  const double r = exp2_fast(((double)a1 - (double)a0) * c64);
+  double rk = 1.0;
+  double* const out = tab + half * kTabNeg + j0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if (j0 + k < kTabW) out[k] = A * rk;
+    else if (j0 + k == kTabW) out[k] = 0.0;  // the zero slot of this half
+    rk *= r;
+  }
+}
+
+// Statistics record of one (target row, chunk) by one wave, with no
+// workgroup barrier: batches of 8 vectors per lane, a running maximum m of
+// the wave, and the running sum of 2^((a - m) c) (binary32 exp2 of
+// a c - round(m c), corrected by 2^(-(m c)_lo) in fp64 per batch; rescaled in
+// fp64 when m rises). Same record as the statistics pass.
+template <bool AL>
+__device__ __forceinline__ void wave_stats_unit(const LinCfg& c, int64_t u) {
+  using E = Elem<kBF16>;
+  constexpr int EPV = E::kPerVec;
+  constexpr int NVB = 8;
+  constexpr int kVecs = kWG * kStatNV;  // 16-byte vectors per chunk
+  const int lane = threadIdx.x & (kWave - 1);
+  const int chunk = (int)(u % c.nch32);
+  const int64_t pr = u / c.nch32;  // target row in [0, B * np)
+  const int64_t b = pr / c.rows.np;
+  const int64_t sr = b * (c.rows.np + c.rows.nq) + (pr - b * c.rows.np);
+  const char* row = c.rows.row(sr);
+  float m = -INFINITY;
+  double s = 0.0;
+  const float c32 = c.c32;
+  for (int k0 = 0; k0 < kVecs / kWave; k0 += NVB) {
+    float x[NVB][EPV];
+    load_vecs<kBF16, AL, NVB, kWave>(row, c.V, c.nvec, (int64_t)chunk * kVecs + (int64_t)k0 * kWave + lane, x);
+    float bm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NVB; ++k)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) bm = fmaxnan(bm, x[k][e]);
+    const float mn = fmaxnan(m, wave_max(bm));
+    if (isnan(mn) || isinf(mn)) {  // NaN or +inf (the record is invalid), or all -inf so far
+      m = mn;
+      if (!is_neg_inf(mn)) break;
+      continue;
+    }
+    if (mn > m && !is_neg_inf(m)) s *= exp2_fast(((double)m - (double)mn) * (double)c32);
+    m = mn;
+    const float mc_hi = m * c32;
+    const float mc_lo = fmaf(m, c32, -mc_hi);
+    double bs = 0.0;
+#pragma unroll
+    for (int k = 0; k < NVB; ++k) {
+      float e[EPV];
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(x[k][j], c32, -mc_hi));
+      bs += (double)pairwise_sum(e);
+    }
+    s += bs * exp2_fast(-(double)mc_lo);
+  }
+  s = wave_sum(s);
+  if (lane == 0) {
+    StatRec r;
+    r.m = m;
+    r.pad = 0;
+    r.s = (isnan(m) || (isinf(m) && m > 0.0f)) ? NAN : s;
+    c.st[sr * c.nch32 + chunk] = r;
+  }
+}
+
 // One pass per bfloat16 draft row, with no statistics pass before it (the
 // table temperatures, c.tab): the fp64 weights of the row are summed per
 // sub-block from the unscaled 2^(a c) table (the rule of fweight with scale
@@ -711,13 +844,15 @@ __global__ __launch_bounds__(kDT) void k_draftrow(LinCfg c) {
 // row maximum from below, m >= m_lo = (log2 s - 10) / c (a sub-block holds
 // 1,024 weights), so the row qualifies for the rule when (m_lo + 63.25) c >=
 // 100 and nothing was flagged; otherwise it is read again: its exact maximum,
-// then exp2 weights relative to it. The workgroup then writes the row's chunk
+// then exp2 weights relative to it. The workgroup writes the row's chunk
 // records for the verification that follows (reference m_lo, or the exact
-// maximum; the draft rows need no statistics pass of their own) and draws
-// x ~ q from its sub-block sums ("Uno" research explainer, §3.3: the drafts of
-// a block are drawn from the draft distributions). -1 for an invalid row.
+// maximum), and wave 0 draws x ~ q from the sub-block sums and a rescan of
+// one sub-block under the same rule ("Uno" research explainer, §3.3: the
+// drafts of a block are drawn from the draft distributions; -1 for an
+// invalid row), while the other waves compute chunk records of the target
+// rows (wave_stats_unit), `nunits` of them over the whole grid.
 template <bool AL>
-__global__ __launch_bounds__(kDT) void k_qrow(LinCfg c) {
+__global__ __launch_bounds__(kDT) void k_qrow(LinCfg c, int64_t nunits) {
   using E = Elem<kBF16>;
   extern __shared__ ResRec s_rec[];  // one record per sub-block (.sp)
   __shared__ double s_tab[kTabSize];
@@ -734,7 +869,7 @@ __global__ __launch_bounds__(kDT) void k_qrow(LinCfg c) {
   const WRow w1 = {0.0, 1.0, true};
   // the table is filled while the first loads of the pass are in flight
   auto fill = [&]() {
-    fill_tab<kDT>(s_tab, c64);
+    fill_tab_steps(s_tab, c64);
     if (t == 0) s_chk = 0;
     __syncthreads();
   };
@@ -777,34 +912,36 @@ __global__ __launch_bounds__(kDT) void k_qrow(LinCfg c) {
   }
   const bool bad = isnan(m) || isinf(m);  // NaN, +inf, or an all -inf row
   // chunk records of this row: sums of 2^((a - m) c) over each chunk's sub-blocks
-  {
-    constexpr int kSbPerChunk = kWG * kStatNV * E::kPerVec / kSB;
-    StatRec* rec = c.st + (b * (c.rows.np + c.rows.nq) + c.rows.np + i) * (int64_t)c.nch32;
-    const double scale = fast ? exp2_fast(-(double)m * c64) : 1.0;
-    for (int ch = t; ch < c.nch32; ch += kDT) {
-      double sc = 0.0;
-      for (int sb = ch * kSbPerChunk; sb < min(nsb, (ch + 1) * kSbPerChunk); ++sb) sc += s_rec[sb].sp;
-      StatRec r;
-      r.m = m;
-      r.pad = 0;
-      r.s = bad && !is_neg_inf(m) ? NAN : sc * scale;
-      rec[ch] = r;
+  constexpr int kSbPerChunk = kWG * kStatNV * E::kPerVec / kSB;
+  StatRec* rec = c.st + (b * (c.rows.np + c.rows.nq) + c.rows.np + i) * (int64_t)c.nch32;
+  const double scale = fast ? exp2_fast(-(double)m * c64) : 1.0;
+  for (int ch = t; ch < c.nch32; ch += kDT) {
+    double sc = 0.0;
+    for (int sb = ch * kSbPerChunk; sb < min(nsb, (ch + 1) * kSbPerChunk); ++sb) sc += s_rec[sb].sp;
+    StatRec r;
+    r.m = m;
+    r.pad = 0;
+    r.s = bad && !is_neg_inf(m) ? NAN : sc * scale;
+    rec[ch] = r;
+  }
+  if (wave == 0) {
+    int x = -1;
+    if (!bad) {
+      const double* const tps = w.tab ? s_tab : nullptr;
+      double mine = 0.0;
+      for (int sb = lane; sb < nsb; sb += kWave) mine += s_rec[sb].sp;
+      const double W = wave_sum(mine);
+      const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
+      x = wave_pick(nsb, c.V, u * W, [&](int sb) { return s_rec[sb].sp; },
+                    [&](int64_t j0, double(&wt)[16]) { row16<kBF16, AL>(c, row, j0, w, tps, wt); });
     }
+    if (lane == 0) c.draft[qr] = x;
   }
-  if (wave != 0) return;
-  if (bad) {
-    if (lane == 0) c.draft[qr] = -1;
-    return;
-  }
-  const double* const tps = w.tab ? s_tab : nullptr;
-  double mine = 0.0;
-  for (int sb = lane; sb < nsb; sb += kWave) mine += s_rec[sb].sp;
-  const double W = wave_sum(mine);
-  const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
-  const int x = wave_pick(
-      nsb, c.V, u * W, [&](int sb) { return s_rec[sb].sp; },
-      [&](int64_t j0, double(&wt)[16]) { row16<kBF16, AL>(c, row, j0, w, tps, wt); });
-  if (lane == 0) c.draft[qr] = x;
+  // target-row chunk records: wave 0 (busy drawing) takes the last slot of
+  // its workgroup, which the grid reaches last
+  const int slot = wave == 0 ? kDWaves - 1 : wave - 1;
+  for (int64_t un = (int64_t)blockIdx.x * kDWaves + slot; un < nunits; un += (int64_t)gridDim.x * kDWaves)
+    wave_stats_unit<AL>(c, un);
 }
 
 // Draft sampling alone: a request with an invalid draft row gets -1 for all
@@ -996,11 +1133,10 @@ template <int DT, bool AL>
 static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
   const int64_t rows = c.B * (2 * c.K + 1);
   if (c.fused && DT == kBF16 && c.tab) {
-    // drafts drawn in one pass over their rows, which also writes those rows'
-    // chunk records; the statistics pass then reads the target rows only
-    PSI_LAUNCH_LDS(s, (k_qrow<AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c);
-    const hipError_t e = launch_stats32_targets(c, DT, s);
-    if (e != hipSuccess) return e;
+    // drafts drawn in one pass over their rows, whose workgroups also write
+    // those rows' chunk records and, wave by wave, the target rows' ones
+    PSI_LAUNCH_LDS(s, (k_qrow<AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c,
+                   c.B * c.rows.np * (int64_t)c.nch32);
   } else {
     const hipError_t e = launch_stats32(c, rows, DT, s);
     if (e != hipSuccess) return e;
@@ -1019,7 +1155,7 @@ static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
     const int parts = (int)std::min<int64_t>(std::max<int64_t>(1, (kResolveTargetWgs + c.B - 1) / c.B),
                                              std::max(1, c.nsb / kRWaves));
     PSI_LAUNCH(s, (k_resolve<DT, AL, false>), dim3((unsigned)(c.B * parts)), dim3(kRT), c, parts);
-    PSI_LAUNCH(s, (k_final<DT, AL>), dim3((unsigned)c.B), dim3(kWG), c);
+    PSI_LAUNCH(s, (k_final<DT, AL>), dim3((unsigned)c.B), dim3(kWave), c);
   }
   return hipGetLastError();
 }
@@ -1035,7 +1171,8 @@ static hipError_t linear_greedy_t(const LinCfg& c, hipStream_t s) {
 template <int DT, bool AL>
 static hipError_t draft_sampled_t(const LinCfg& c, hipStream_t s) {
   if (DT == kBF16 && c.tab) {
-    PSI_LAUNCH_LDS(s, (k_qrow<AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c);
+    PSI_LAUNCH_LDS(s, (k_qrow<AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c,
+                   (int64_t)0);
   } else {
     const hipError_t e = launch_stats32(c, c.B * c.K, DT, s);
     if (e != hipSuccess) return e;

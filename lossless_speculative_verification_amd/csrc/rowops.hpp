@@ -260,6 +260,49 @@ __device__ int wave_select(int nsb, double target, WSB wsb, double& pref) {
   return __shfl(sel, src);
 }
 
+// wave_select over weights held in registers: lane l owns sub-blocks
+// [l * PER, l * PER + PER) (nsb <= 64 * PER) and v[k] is the weight of its
+// k-th (0 past nsb). Same result as wave_select on the same weights.
+template <int PER>
+__device__ int wave_select_reg(int nsb, double target, const double (&v)[PER], double& pref) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s0 = lane * PER;
+  double mine = 0.0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) mine += v[k];
+  const double excl = wave_incl_scan(mine) - mine;
+  int sel = -1, last = -1;
+  double p0 = 0.0, lp = 0.0, acc = excl;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (s0 + k < nsb && v[k] > 0.0) {
+      if (sel < 0 && acc + v[k] > target) {
+        sel = s0 + k;
+        p0 = acc;
+      }
+      last = s0 + k;
+      lp = acc;
+    }
+    acc += v[k];
+  }
+  unsigned long long m = __ballot(sel >= 0);
+  int src;
+  if (m) {
+    src = __ffsll((long long)m) - 1;
+  } else {  // rounding left no crossing: the last sub-block with positive weight
+    m = __ballot(last >= 0);
+    if (!m) {
+      pref = 0.0;
+      return -1;
+    }
+    src = 63 - __clzll((long long)m);
+    sel = last;
+    p0 = lp;
+  }
+  pref = __shfl(p0, src);
+  return __shfl(sel, src);
+}
+
 // The element pick inside sub-block sbsel by one whole wave: lane l owns the 16
 // consecutive elements from sbsel * kSB + 16 l, whose weights w[16] it holds
 // (0 past the end of the row). Returns, on every lane, the smallest element

@@ -10,10 +10,12 @@
 namespace psi {
 
 // ------------------------------------------------------ statistics pass --
-// Record `item` = sr * nch32 + chunk of row sr.
 template <int DT, bool AL>
-__device__ __forceinline__ void stats_chunk(const LinCfg& c, int64_t sr, int chunk, int64_t item) {
+__global__ __launch_bounds__(kWG) void k_stats32(LinCfg c) {
   constexpr int EPV = Elem<DT>::kPerVec;
+  const int64_t item = blockIdx.x;
+  const int chunk = (int)(item % c.nch32);
+  const int64_t sr = item / c.nch32;
   const char* row = c.rows.row(sr);
   __shared__ float shf[kWaves];
   __shared__ double shd[kWaves];
@@ -51,24 +53,6 @@ __device__ __forceinline__ void stats_chunk(const LinCfg& c, int64_t sr, int chu
 }
 
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_stats32(LinCfg c) {
-  const int64_t item = blockIdx.x;
-  stats_chunk<DT, AL>(c, item / c.nch32, (int)(item % c.nch32), item);
-}
-
-// The target rows of each request only (their draft rows' records are
-// written by the one-pass draft kernel).
-template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_stats32p(LinCfg c) {
-  const int64_t u = blockIdx.x;
-  const int chunk = (int)(u % c.nch32);
-  const int64_t pr = u / c.nch32;  // target row in [0, B * np)
-  const int64_t b = pr / c.rows.np;
-  const int64_t sr = b * (c.rows.np + c.rows.nq) + (pr - b * c.rows.np);
-  stats_chunk<DT, AL>(c, sr, chunk, sr * c.nch32 + chunk);
-}
-
-template <int DT, bool AL>
 static hipError_t stats32_t(const LinCfg& c, int64_t rows, hipStream_t s) {
   PSI_LAUNCH(s, (k_stats32<DT, AL>), dim3((unsigned)(rows * c.nch32)), dim3(kWG), c);
   return hipGetLastError();
@@ -76,16 +60,6 @@ static hipError_t stats32_t(const LinCfg& c, int64_t rows, hipStream_t s) {
 
 hipError_t launch_stats32(const LinCfg& c, int64_t rows, int dtype, hipStream_t s) {
   return PSI_DISPATCH(stats32_t, dtype, c.aligned, c, rows, s);
-}
-
-template <int DT, bool AL>
-static hipError_t stats32p_t(const LinCfg& c, hipStream_t s) {
-  PSI_LAUNCH(s, (k_stats32p<DT, AL>), dim3((unsigned)(c.B * c.rows.np * c.nch32)), dim3(kWG), c);
-  return hipGetLastError();
-}
-
-hipError_t launch_stats32_targets(const LinCfg& c, int dtype, hipStream_t s) {
-  return PSI_DISPATCH(stats32p_t, dtype, c.aligned, c, s);
 }
 
 }  // namespace psi
