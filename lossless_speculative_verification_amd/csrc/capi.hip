@@ -82,10 +82,10 @@ inline Layout layout(int64_t B, int32_t rows_per_req, int32_t V, int dtype) {
   off = align_up(off + (size_t)B * rows_per_req * sizeof(CutRec), 256);
   L.rst = off;
   off = align_up(off + (size_t)B * rows_per_req * sizeof(RowStat), 256);
-  L.ts = off;
-  off = align_up(off + (size_t)B * sizeof(TreeState), 256);
-  L.tres = off;
-  off = align_up(off + (size_t)B * nsb * sizeof(TreeRes), 256);
+  L.ts = off;  // two state buffers (the fused walk rounds alternate between them)
+  off = align_up(off + 2 * (size_t)B * sizeof(TreeState), 256);
+  L.tres = off;  // two sum buffers
+  off = align_up(off + 2 * (size_t)B * nsb * sizeof(TreeRes), 256);
   L.total = off;
   return L;
 }
@@ -366,6 +366,8 @@ int psispec_verify_tree(const void* p_logits, const void* q_logits, int dtype, i
   tc.rst = (RowStat*)(w + L.rst);
   tc.ts = (TreeState*)(w + L.ts);
   tc.tres = (TreeRes*)(w + L.tres);
+  tc.ts2 = tc.ts + B;
+  tc.tres2 = tc.tres + B * (int64_t)nsb_of(V);
   tc.N = N;
   tc.D = D;
   timing_begin(stream);
@@ -611,6 +613,8 @@ int psispec_verify_lmhead(const void* h_target, const void* h_draft, const void*
   memset(&tc, 0, sizeof(tc));
   tc.ts = (TreeState*)(w + L.ts);
   tc.tres = (TreeRes*)(w + L.tres);
+  tc.ts2 = nullptr;  // one walk state per request: no fused walk rounds here
+  tc.tres2 = nullptr;
   tc.N = K;
   tc.D = K;
   timing_begin(stream);

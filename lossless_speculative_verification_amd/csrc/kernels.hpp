@@ -179,6 +179,7 @@ enum TreePhase : int32_t { kTreeTest = 0, kTreeWaitG = 1, kTreeFinal = 2, kTreeD
 struct TreeState {
   int32_t row, j, len, phase, has_exact;
   int32_t urow1;          // row of the final draw's uniform + 1 when it differs from row (0: row)
+  int32_t buf;            // which of the two TreeRes buffers holds the sums of this state's pass
   float mp, mq;      // exact row maxima of the current row pair
   double sp_hat, sq_hat;  // fp32-grade normalisers of the current row pair
   double Sp, Sq;          // fp64-grade normalisers (valid when has_exact)
@@ -199,6 +200,8 @@ struct TreeCfg {
   RowStat* rst;           // [B, 2 (N + 1)]
   TreeState* ts;          // [B]
   TreeRes* tres;          // [B, nsb]
+  TreeState* ts2;         // [B] second state buffer of the fused walk rounds (k_tree_wp)
+  TreeRes* tres2;         // [B, nsb] second sum buffer of the fused walk rounds
   int N, D;
 };
 
@@ -347,6 +350,10 @@ hipError_t launch_lmh_logits(const LmhCfg& g, hipStream_t s);
 // The final draw of a tree-state row pair (tree.hip): the fp64 pass over the
 // rows in c.rows and the pick, for every request whose state is kTreeFinal.
 hipError_t launch_tree_final(const LinCfg& c, const TreeCfg& tc, int dtype, hipStream_t s);
+// Fused bfloat16 node drafts of tree verification at a table temperature
+// (linear.hip): one pass per draft row, which draws the row's children and
+// writes its chunk records, and the target rows' chunk records.
+hipError_t launch_tree_qrows(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, hipStream_t s);
 // fp64 draft-row sub-block records of the first `rows` rows of c.rows.q (linear.hip).
 hipError_t launch_draftpass(const LinCfg& c, int64_t rows, int dtype, hipStream_t s);
 

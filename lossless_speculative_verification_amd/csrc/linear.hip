@@ -43,9 +43,6 @@ constexpr size_t kResolveMaxLds = 64 * 1024;
 constexpr int kRT = 1024;
 constexpr int kRWaves = kRT / kWave;
 
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
 
 // Corrections for one 16-byte bfloat16 vector pair holding logits whose
 // magnitude is below the table window: the pass read a zero slot for them and
@@ -262,76 +259,6 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
       if (s + W >= sb1) break;
       load(s + 2 * W, x0);
       reduce(s + W, x1);
-    }
-  }
-}
-
-// The 16 consecutive logits j0 .. j0+15 of one row as raw 16-byte vectors
-// (the aligned path; elements past V read as -inf), so that their loads can be
-// issued before their weights are needed.
-template <int DT>
-struct Raw16 {
-  uint4 v[16 / Elem<DT>::kPerVec];
-};
-template <int DT, bool AL>
-__device__ __forceinline__ void raw16(const LinCfg& c, const char* row, int64_t j0, Raw16<DT>& r) {
-  using E = Elem<DT>;
-  constexpr int EPV = E::kPerVec;
-  constexpr int NV = 16 / EPV;
-  if constexpr (AL) {
-    // unconditional loads (indices clamped into the row; weights16 zeroes
-    // elements past V), so that no branch makes the compiler wait for them
-    const uint4* rp = (const uint4*)row;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) r.v[v] = rp[min(j0 / EPV + v, (int64_t)c.nvec - 1)];
-  } else {
-    load_raw<DT, false, NV, 1>(row, c.V, c.nvec, j0 / EPV, r.v);
-  }
-}
-// Weights of the 16 logits held in r (0 past V), under the rule of fweight;
-// bfloat16 rows with the pre-scaled table read it without branches, and the
-// rare logits below its window are redone out of line.
-template <int DT>
-__device__ __forceinline__ void weights16(const LinCfg& c, const Raw16<DT>& r, int64_t j0, const WRow& w,
-                                          const double* tab_scaled, double (&out)[16]) {
-  using E = Elem<DT>;
-  constexpr int EPV = E::kPerVec;
-  if constexpr (DT == kBF16) {
-    if (w.tab && tab_scaled) {
-      uint32_t low = 0;
-      const char* const tb = (const char*)tab_scaled;
-#pragma unroll
-      for (int v = 0; v < 2; ++v)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t o = tab_offsets2(word_of(r.v[v], i), low);
-          out[v * 8 + 2 * i] = *(const double*)(tb + (o & 0xffffu));
-          out[v * 8 + 2 * i + 1] = *(const double*)(tb + (o >> 16));
-        }
-      if (__ballot((low & 0x80008000u) != 0u)) {
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          float x[EPV];
-          E::unpack(r.v[v], x);
-#pragma unroll
-          for (int e = 0; e < EPV; ++e)
-            if (tab_tiny(__float_as_uint(x[e]) >> 16)) out[v * EPV + e] = tiny_weight(x[e], c.c64, w.scale);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (j0 + k >= c.V) out[k] = 0.0;
-      return;
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < 16 / EPV; ++v) {
-    float x[EPV];
-    E::unpack(r.v[v], x);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      const int k = v * EPV + e;
-      out[k] = j0 + k < c.V ? fweight<DT>(x[e], w, c.c64, tab_scaled) : 0.0;
     }
   }
 }
@@ -836,60 +763,83 @@ __device__ __forceinline__ void wave_stats_unit(const LinCfg& c, int64_t u) {
   }
 }
 
-// One pass per bfloat16 draft row, with no statistics pass before it (the
-// table temperatures, c.tab): the fp64 weights of the row are summed per
-// sub-block from the unscaled 2^(a c) table (the rule of fweight with scale
-// 1), tracking whether the row holds a code that may break the table rule
-// (positive or NaN above the window). The largest sub-block sum s bounds the
-// row maximum from below, m >= m_lo = (log2 s - 10) / c (a sub-block holds
-// 1,024 weights), so the row qualifies for the rule when (m_lo + 63.25) c >=
-// 100 and nothing was flagged; otherwise it is read again: its exact maximum,
-// then exp2 weights relative to it. The workgroup writes the row's chunk
-// records for the verification that follows (reference m_lo, or the exact
-// maximum), and wave 0 draws x ~ q from the sub-block sums and a rescan of
-// one sub-block under the same rule ("Uno" research explainer, §3.3: the
-// drafts of a block are drawn from the draft distributions; -1 for an
-// invalid row), while the other waves compute chunk records of the target
-// rows (wave_stats_unit), `nunits` of them over the whole grid.
-template <bool AL>
-__global__ __launch_bounds__(kDT) void k_qrow(LinCfg c, int64_t nunits) {
+// One pass over the bfloat16 draft row `row` (row i of request b), with no
+// statistics pass before it (the table temperatures, c.tab): the fp64
+// weights of the row are summed per sub-block into s_rec from the unscaled
+// 2^(a c) table (the rule of fweight with scale 1), tracking whether the row
+// holds a code that may break the table rule (positive or NaN above the
+// window). The largest logit m_lo of the sub-block with the largest sum
+// (read again, 2 KB) bounds the row maximum from below, so the row qualifies
+// for the rule when (m_lo + 63.25) c >= 100 and nothing was flagged;
+// otherwise it is read again: its exact maximum, then exp2 weights relative
+// to it. Writes the row's chunk records for the verification that follows
+// (reference m_lo, or the exact maximum) and returns the row's rule in w
+// (with the LDS table, or exact exponentials) and its validity. Called by
+// every thread of a kDT-thread workgroup.
+// RING > 0: sub-blocks in flight per wave in the pass (more loads in flight
+// for a workgroup that has its CU to itself).
+template <bool AL, int RING = 0>
+__device__ bool qrow_pass(const LinCfg& c, int64_t b, int i, const char* row, ResRec* s_rec, double* s_tab,
+                          float* shf, int* s_chk, double* s_smax, WRow& w) {
   using E = Elem<kBF16>;
-  extern __shared__ ResRec s_rec[];  // one record per sub-block (.sp)
-  __shared__ double s_tab[kTabSize];
-  __shared__ float shf[kDWaves];
-  __shared__ int s_chk;
-  __shared__ double s_smax;
-  const int64_t qr = blockIdx.x;  // draft row in [0, B*K)
-  const int K = c.K, t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
-  const int64_t b = qr / K;
-  const int i = (int)(qr - b * K);
-  const char* row = qrow_of(c, b, i);
+  const int t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
   const int nsb = c.nsb;
   const double c64 = c.c64;
   const WRow w1 = {0.0, 1.0, true};
   // the table is filled while the first loads of the pass are in flight
   auto fill = [&]() {
     fill_tab_steps(s_tab, c64);
-    if (t == 0) s_chk = 0;
+    if (t == 0) *s_chk = 0;
     __syncthreads();
   };
-  resolve_pass<kBF16, AL, true, false, true, kDWaves, decltype(fill), true>(c, b, row, row, 0, nsb, s_tab, s_tab, w1,
-                                                                           w1, 0.0f, s_rec, fill, &s_chk);
+  resolve_pass<kBF16, AL, true, false, true, kDWaves, decltype(fill), true, RING>(c, b, row, row, 0, nsb, s_tab,
+                                                                                 s_tab, w1, w1, 0.0f, s_rec, fill,
+                                                                                 s_chk);
   __syncthreads();
   if (wave == 0) {
+    // the sub-block with the largest sum (lowest index on ties), then its largest logit
     double mx = 0.0;
-    for (int sb = lane; sb < nsb; sb += kWave) mx = fmax(mx, s_rec[sb].sp);
+    int at = 0;
+    for (int sb = lane; sb < nsb; sb += kWave) {
+      const double v = s_rec[sb].sp;
+      if (v > mx) {
+        mx = v;
+        at = sb;
+      }
+    }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
-    if (lane == 0) s_smax = mx;
+    for (int o = 32; o >= 1; o >>= 1) {
+      const double ov = __shfl_xor(mx, o);
+      const int oa = __shfl_xor(at, o);
+      if (ov > mx || (ov == mx && oa < at)) {
+        mx = ov;
+        at = oa;
+      }
+    }
+    float xm = -INFINITY;
+    if (mx > 0.0) {
+      float x[2][E::kPerVec];
+      load_vecs<kBF16, AL, 2, 1>(row, c.V, c.nvec, ((int64_t)at * kSB + (int64_t)lane * 16) / E::kPerVec, x);
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int e = 0; e < E::kPerVec; ++e) xm = fmaxnan(xm, x[k][e]);
+      xm = wave_max(xm);
+    }
+    if (lane == 0) {
+      *s_smax = mx;
+      shf[0] = xm;
+    }
   }
   __syncthreads();
-  const double smax = s_smax;
-  const bool fast = !s_chk && smax > 0.0 && (::log2(smax) - 10.0) + kTabMaxAbs * c64 >= 100.0;
+  const double smax = *s_smax;
+  const float m_lo = shf[0];
+  __syncthreads();  // shf is reused below
+  const bool fast = !*s_chk && smax > 0.0 && !isnan(m_lo) && ((double)m_lo + kTabMaxAbs) * c64 >= 100.0;
   float m;
-  WRow w = w1;
+  w = w1;
   if (fast) {
-    m = __double2float_rd((::log2(smax) - 10.0) / c64);
+    m = m_lo;
   } else {
     // exact maximum and validity, then the weights relative to it
     constexpr int EPV = E::kPerVec;
@@ -924,24 +874,94 @@ __global__ __launch_bounds__(kDT) void k_qrow(LinCfg c, int64_t nunits) {
     r.s = bad && !is_neg_inf(m) ? NAN : sc * scale;
     rec[ch] = r;
   }
-  if (wave == 0) {
-    int x = -1;
-    if (!bad) {
-      const double* const tps = w.tab ? s_tab : nullptr;
-      double mine = 0.0;
-      for (int sb = lane; sb < nsb; sb += kWave) mine += s_rec[sb].sp;
-      const double W = wave_sum(mine);
-      const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
-      x = wave_pick(nsb, c.V, u * W, [&](int sb) { return s_rec[sb].sp; },
-                    [&](int64_t j0, double(&wt)[16]) { row16<kBF16, AL>(c, row, j0, w, tps, wt); });
-    }
-    if (lane == 0) c.draft[qr] = x;
-  }
-  // target-row chunk records: wave 0 (busy drawing) takes the last slot of
-  // its workgroup, which the grid reaches last
-  const int slot = wave == 0 ? kDWaves - 1 : wave - 1;
+  return !bad;
+}
+
+// One inverse-CDF draw from the sub-block sums of qrow_pass (uniform u) by
+// one whole wave, the chosen sub-block rescanned under the row's rule.
+template <bool AL>
+__device__ __forceinline__ int qrow_draw(const LinCfg& c, const char* row, const ResRec* s_rec,
+                                         const double* s_tab, const WRow& w, double u) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const double* const tps = w.tab ? s_tab : nullptr;
+  double mine = 0.0;
+  for (int sb = lane; sb < c.nsb; sb += kWave) mine += s_rec[sb].sp;
+  const double W = wave_sum(mine);
+  return wave_pick(c.nsb, c.V, u * W, [&](int sb) { return s_rec[sb].sp; },
+                   [&](int64_t j0, double(&wt)[16]) { row16<kBF16, AL>(c, row, j0, w, tps, wt); });
+}
+
+// The target-row chunk records of a launch: wave `slot` of workgroup g takes
+// the units g * kDWaves + slot + k * (kDWaves * grid), `nunits` in all.
+template <bool AL>
+__device__ __forceinline__ void stats_units(const LinCfg& c, int64_t nunits, int slot) {
   for (int64_t un = (int64_t)blockIdx.x * kDWaves + slot; un < nunits; un += (int64_t)gridDim.x * kDWaves)
     wave_stats_unit<AL>(c, un);
+}
+
+// One workgroup per draft row of linear verification: qrow_pass, then wave 0
+// draws x ~ q with U(seed, step, b, i, 0x40000000) ("Uno" research explainer,
+// §3.3: the drafts of a block are drawn from the draft distributions; -1 for
+// an invalid row) while the other waves compute the target rows' chunk
+// records (wave_stats_unit), `nunits` of them over the whole grid.
+template <bool AL>
+__global__ __launch_bounds__(kDT) void k_qrow(LinCfg c, int64_t nunits) {
+  extern __shared__ ResRec s_rec[];  // one record per sub-block (.sp)
+  __shared__ double s_tab[kTabSize];
+  __shared__ float shf[kDWaves];
+  __shared__ int s_chk;
+  __shared__ double s_smax;
+  const int64_t qr = blockIdx.x;  // draft row in [0, B*K)
+  const int K = c.K, wave = threadIdx.x / kWave;
+  const int64_t b = qr / K;
+  const int i = (int)(qr - b * K);
+  const char* row = qrow_of(c, b, i);
+  WRow w;
+  const bool ok = qrow_pass<AL>(c, b, i, row, s_rec, s_tab, shf, &s_chk, &s_smax, w);
+  if (wave == 0) {
+    const int x = ok ? qrow_draw<AL>(c, row, s_rec, s_tab, w, c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft)) : -1;
+    if ((threadIdx.x & (kWave - 1)) == 0) c.draft[qr] = x;
+  }
+  // wave 0 (busy drawing) takes the last slot of its workgroup, which the grid reaches last
+  stats_units<AL>(c, nunits, wave == 0 ? kDWaves - 1 : wave - 1);
+}
+
+// Tree node drafts: workgroups [0, nextra) compute target-row chunk records
+// only; workgroup nextra + (b (N + 1) + r) runs qrow_pass on draft row r of
+// request b and draws each child of row r, the j-th (ascending node id) with
+// U(seed, step, b, r, 0x40000000 + j) ("Uno" research explainer, §3.4: the
+// candidates of a row are drawn i.i.d. from its draft distribution), one wave
+// per child; -1 for an invalid row (the walk then marks every node of the
+// request).
+constexpr int64_t kTreeQrowFill = 256;  // workgroups of a tree draft-row launch, at least
+
+template <bool AL>
+__global__ __launch_bounds__(kDT) void k_tqrow(LinCfg c, TreeTopo tp, TreeCfg tc, int64_t nunits, int nextra) {
+  extern __shared__ ResRec s_rec[];
+  __shared__ double s_tab[kTabSize];
+  __shared__ float shf[kDWaves];
+  __shared__ int s_chk;
+  __shared__ double s_smax;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  if ((int)blockIdx.x < nextra) {
+    stats_units<AL>(c, nunits, wave);
+    return;
+  }
+  const int R = tc.N + 1;
+  const int64_t qr = blockIdx.x - nextra;  // draft row in [0, B (N + 1))
+  const int64_t b = qr / R;
+  const int r = (int)(qr - b * R);
+  const char* row = c.rows.q + (qr * (int64_t)c.V) * c.rows.esz;
+  WRow w;
+  const bool ok = qrow_pass<AL>(c, b, r, row, s_rec, s_tab, shf, &s_chk, &s_smax, w);
+  const int k0 = tp.off[r], nk = tp.off[r + 1] - k0;
+  for (int j = wave; j < nk; j += kDWaves) {
+    const int x = ok ? qrow_draw<AL>(c, row, s_rec, s_tab, w,
+                                     c.rng.u((uint32_t)b, (uint32_t)r, kDrawDraft + (uint32_t)j))
+                     : -1;
+    if (lane == 0) tc.tokens[b * tc.N + tp.kids[k0 + j]] = x;
+  }
+  stats_units<AL>(c, nunits, wave);
 }
 
 // Draft sampling alone: a request with an invalid draft row gets -1 for all
@@ -1215,6 +1235,23 @@ hipError_t launch_draft_sampled(const LinCfg& c, int dtype, hipStream_t s) {
 hipError_t launch_draft_greedy(const LinCfg& c, int dtype, hipStream_t s) {
   return PSI_DISPATCH(draft_greedy_t, dtype, c.aligned, c, s);
 }
+template <bool AL>
+static hipError_t tree_qrows_t(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, hipStream_t s) {
+  const int64_t nq = c.B * (int64_t)(tc.N + 1);
+  const int64_t nunits = c.B * c.rows.np * (int64_t)c.nch32;
+  // statistics-only workgroups on the CUs the draft rows leave idle, at most
+  // one per kDWaves target chunks
+  const int64_t spare = std::max<int64_t>(0, kTreeQrowFill - nq);
+  const int nextra = (int)std::min<int64_t>(spare, (nunits + kDWaves - 1) / kDWaves);
+  PSI_LAUNCH_LDS(s, (k_tqrow<AL>), dim3((unsigned)(nextra + nq)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c, tp,
+                 tc, nunits, nextra);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_qrows(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, hipStream_t s) {
+  return c.aligned ? tree_qrows_t<true>(c, tp, tc, s) : tree_qrows_t<false>(c, tp, tc, s);
+}
+
 hipError_t launch_draftpass(const LinCfg& c, int64_t rows, int dtype, hipStream_t s) {
   return PSI_DISPATCH(draftpass_t, dtype, c.aligned, c, rows, s);
 }

@@ -118,6 +118,81 @@ __device__ __forceinline__ double fweight(float a, const WRow& w, double c64, co
   return exp2_fast(__builtin_fma((double)a, c64, -w.mc));
 }
 
+// 32-bit word i of a 16-byte vector.
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// The 16 consecutive logits j0 .. j0+15 of one row as raw 16-byte vectors
+// (the aligned path; elements past V read as -inf), so that their loads can be
+// issued before their weights are needed.
+template <int DT>
+struct Raw16 {
+  uint4 v[16 / Elem<DT>::kPerVec];
+};
+template <int DT, bool AL>
+__device__ __forceinline__ void raw16(const LinCfg& c, const char* row, int64_t j0, Raw16<DT>& r) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  constexpr int NV = 16 / EPV;
+  if constexpr (AL) {
+    // unconditional loads (indices clamped into the row; weights16 zeroes
+    // elements past V), so that no branch makes the compiler wait for them
+    const uint4* rp = (const uint4*)row;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) r.v[v] = rp[min(j0 / EPV + v, (int64_t)c.nvec - 1)];
+  } else {
+    load_raw<DT, false, NV, 1>(row, c.V, c.nvec, j0 / EPV, r.v);
+  }
+}
+// Weights of the 16 logits held in r (0 past V), under the rule of fweight;
+// bfloat16 rows with the pre-scaled table read it without branches, and the
+// rare logits below its window are redone out of line.
+template <int DT>
+__device__ __forceinline__ void weights16(const LinCfg& c, const Raw16<DT>& r, int64_t j0, const WRow& w,
+                                          const double* tab_scaled, double (&out)[16]) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::kPerVec;
+  if constexpr (DT == kBF16) {
+    if (w.tab && tab_scaled) {
+      uint32_t low = 0;
+      const char* const tb = (const char*)tab_scaled;
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t o = tab_offsets2(word_of(r.v[v], i), low);
+          out[v * 8 + 2 * i] = *(const double*)(tb + (o & 0xffffu));
+          out[v * 8 + 2 * i + 1] = *(const double*)(tb + (o >> 16));
+        }
+      if (__ballot((low & 0x80008000u) != 0u)) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          float x[EPV];
+          E::unpack(r.v[v], x);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e)
+            if (tab_tiny(__float_as_uint(x[e]) >> 16)) out[v * EPV + e] = tiny_weight(x[e], c.c64, w.scale);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (j0 + k >= c.V) out[k] = 0.0;
+      return;
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 16 / EPV; ++v) {
+    float x[EPV];
+    E::unpack(r.v[v], x);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const int k = v * EPV + e;
+      out[k] = j0 + k < c.V ? fweight<DT>(x[e], w, c.c64, tab_scaled) : 0.0;
+    }
+  }
+}
+
 // --------------------------------------------- inverse-CDF pick helper --
 // Picks the smallest index j with (sum of weights up to and including j) >
 // target, given per-sub-block weights wsb(sb) and per-element weights w(j)

@@ -16,16 +16,20 @@
 // test needs only P(tok), Q(tok) and (c_j, G(c_j)).
 //
 // Pipeline on the caller's stream:
-//   k_stats32          (linear.hip) fp32-grade maxima and sums of every row.
-//   k_tree_walk        one workgroup per request, launched rounds + 1 times:
-//                      the first launch reduces the row statistics and checks
-//                      the request; each launch then walks the tree (accept
-//                      tests) until the next rejection and asks for G(c).
-//   k_tree_pass        (sub-block, request): fp64 sums of the row pair of every
-//                      request waiting for a G(c); run between walks, and once
-//                      more for the final row.
+//   k_tqrow            (linear.hip; fused bfloat16 node drafts) one pass per
+//                      draft row, which draws the row's children and writes its
+//                      chunk records, and the target rows' chunk records; or
+//                      k_draftpass + k_tree_draft (node drafts) and k_stats32.
+//   k_tree_wp          (sub-block group, request), launched rounds + 1 times:
+//                      every workgroup of a request takes the walk step (row
+//                      statistics and checks first; then G(c) from the previous
+//                      round's sums, and the accept tests until the next
+//                      rejection), then sums its sub-blocks of the row pair
+//                      the new state needs (the next G(c), or the final row).
 //   k_tree_pick        one workgroup per request: inverse-CDF draw of the final
 //                      token from r at the stopping row, outputs.
+// The LM-head path (lmhead.hip) draws its final token with k_tree_pass and
+// k_tree_pick (launch_tree_final).
 // Greedy (temperature 0): k_argmax then k_tree_greedy. Filtered sampling:
 // k_filter_row (filter.hip) then k_tree_filt, which runs the recursive update
 // directly on the at most 2 * top_k entry union of the two kept sets.
@@ -100,17 +104,111 @@ __global__ __launch_bounds__(kWG) void k_tree_draft(LinCfg c, TreeTopo tp, TreeC
 }
 
 // ------------------------------------------------------------------ walk --
+// Thread 0's accept tests down the tree from state s until the next
+// rejection (phase kTreeWaitG: a G(c_new) is needed) or the final row (phase
+// kTreeFinal). rs holds the request's row statistics; the accepted path is
+// written to the outputs when `write` is set.
+// Per node of a request, gathered by the workgroup before the walk: its
+// token, the logits of that token in its parent's target and draft rows, and
+// the uniform of its accept test.
+struct NodeIn {
+  int32_t tok;
+  float ap, aq;
+  double u;
+};
+
 template <int DT>
-__global__ __launch_bounds__(kWG) void k_tree_walk(LinCfg c, TreeTopo tp, TreeCfg tc, int first) {
+__device__ __forceinline__ void gather_nodes(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int64_t b,
+                                             NodeIn* nodes) {
   using E = Elem<DT>;
-  const int64_t b = blockIdx.x;
+  for (int n = threadIdx.x; n < tc.N; n += blockDim.x) {
+    const int r = tp.prow[n];
+    NodeIn o;
+    o.tok = tc.tokens[b * tc.N + n];
+    const bool ok = o.tok >= 0 && o.tok < c.V;
+    o.ap = ok ? E::load1(tree_prow(c, b, r), o.tok) : 0.0f;
+    o.aq = ok ? E::load1(tree_qrow(c, b, r), o.tok) : 0.0f;
+    o.u = c.rng.u((uint32_t)b, (uint32_t)r, (uint32_t)(kDrawAccept + tp.sib[n]));
+    nodes[n] = o;
+  }
+}
+
+template <int DT>
+__device__ void tree_walk_steps(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int64_t b, TreeState& s,
+                                const RowStat* rs, const NodeIn* nodes, bool write) {
+  const int N = tc.N, D = tc.D;
+  for (;;) {
+    const int row = s.row;
+    const int k0 = tp.off[row], nk = tp.off[row + 1] - k0;
+    if (nk == 0) {  // leaf: draw from P
+      s.phase = kTreeFinal;
+      s.c_new = 0.0;
+      s.c_old = 0.0;
+      return;
+    }
+    const int child = tp.kids[k0 + s.j];
+    const NodeIn nd = nodes[child];
+    const int tok = nd.tok;
+    double P, Q;
+    if (s.has_exact) {
+      WRow wp, wq;  // exact sums come from a residual-type pass over this row pair
+      wpair(DT == kBF16 && c.tab, s.mp, s.mq, true, c.c64, wp, wq);
+      P = fweight<DT>(nd.ap, wp, c.c64, nullptr) / s.Sp;
+      Q = fweight<DT>(nd.aq, wq, c.c64, nullptr) / s.Sq;
+    } else {
+      P = ::exp(((double)nd.ap - (double)s.mp) * c.invT - ::log(s.sp_hat));
+      Q = ::exp(((double)nd.aq - (double)s.mq) * c.invT - ::log(s.sq_hat));
+    }
+    const double r = s.cj == 0.0 ? P : fmax(0.0, P - s.cj * Q) / s.Gj;
+    const double u = nd.u;  // U(seed, step, b, row, 1 + j) of the j-th child of this row
+    if (u * Q < r) {
+      if (write) {
+        tc.out_path[b * D + s.len] = child;
+        c.out_tokens[b * (D + 1) + s.len] = tok;
+      }
+      ++s.len;
+      s.row = child + 1;
+      load_row_stats(s, rs, N, s.row);
+      continue;
+    }
+    ++s.j;
+    s.c_old = s.cj;
+    s.c_new = s.cj + s.Gj;
+    s.phase = s.j < nk ? kTreeWaitG : kTreeFinal;
+    return;
+  }
+}
+
+// One round of the walk with the row pass it asks for, grid (sub-block
+// group, request), launched rounds + 1 times. Every workgroup of a request
+// takes the same walk step: in round 0 it reduces the row statistics and
+// checks the request, in later rounds it turns the previous round's sums into
+// the fp64-grade normalisers of the row pair and G(c_new); then the accept
+// tests until the next rejection or the final row. Workgroup 0 writes the
+// state and the outputs; every workgroup then sums its sub-blocks of the row
+// pair the new state needs. States and sums alternate between two buffers,
+// so that a round reads only what the previous round wrote.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_tree_wp(LinCfg c, TreeTopo tp, TreeCfg tc, int round) {
+  const int64_t b = blockIdx.y;
+  const bool lead = blockIdx.x == 0;
   const int t = threadIdx.x, N = tc.N, R2 = 2 * (N + 1);
-  RowStat* rs = tc.rst + b * R2;
-  __shared__ int s_bad;
+  TreeState* const ts_out = (round & 1) ? tc.ts2 : tc.ts;
+  const TreeState* const ts_in = (round & 1) ? tc.ts : tc.ts2;
+  TreeRes* const tres_out = (round & 1) ? tc.tres2 : tc.tres;
+  const TreeRes* const tres_in = (round & 1) ? tc.tres : tc.tres2;
+  __shared__ int s_bad, s_badq;
   __shared__ double sh[kWaves];
-  TreeState s;
-  if (first) {
-    if (t == 0) s_bad = 0;
+  __shared__ RowStat s_rs[2 * (kMaxNodes + 1)];
+  __shared__ NodeIn s_nodes[kMaxNodes];
+  __shared__ TreeState s_st;
+  const RowStat* rs = tc.rst + b * R2;
+  TreeState s = {};
+  if (round == 0) {
+    if (t == 0) {
+      s_bad = 0;
+      s_badq = 0;
+    }
     __syncthreads();
     for (int i = t; i < R2; i += kWG) {
       // same reduction as the linear decide step, so that a chain-shaped tree
@@ -131,35 +229,46 @@ __global__ __launch_bounds__(kWG) void k_tree_walk(LinCfg c, TreeTopo tp, TreeCf
       o.m = m;
       o.bad = bad;
       o.s = S;
-      rs[i] = o;
+      s_rs[i] = o;
+      if (lead) tc.rst[b * R2 + i] = o;
       if (bad) atomicOr(&s_bad, 1);
+      if (bad && i > N) atomicOr(&s_badq, 1);
     }
+    __syncthreads();
     for (int n = t; n < N; n += kWG) {
-      const int x = tc.tokens[b * N + n];
+      int x = tc.tokens[b * N + n];
+      if (c.fused && s_badq) {  // drafts drawn in the call: every node of the request is -1
+        x = -1;
+        if (lead) tc.tokens[b * N + n] = -1;
+      }
       if (x < 0 || x >= c.V) atomicOr(&s_bad, 1);
     }
-    tree_clear_outputs(c, tc, b);
+    if (lead) tree_clear_outputs(c, tc, b);
     __syncthreads();
     if (s_bad) {
-      if (t == 0) {
+      if (lead && t == 0) {
         c.out_len[b] = -1;
         TreeState d = {};
         d.phase = kTreeDone;
-        tc.ts[b] = d;
+        ts_out[b] = d;
       }
       return;
     }
-    if (t != 0) return;
-    s = {};
-    s.row = 0;
-    s.len = 0;
-    s.phase = kTreeTest;
-    load_row_stats(s, rs, N, 0);
+    rs = s_rs;
+    if (t == 0) {
+      s.row = 0;
+      s.len = 0;
+      s.phase = kTreeTest;
+      load_row_stats(s, rs, N, 0);
+    }
   } else {
-    s = tc.ts[b];
-    if (s.phase != kTreeWaitG) return;
-    // fp64-grade normalisers of the row pair and G(c_new) from the row pass
-    const TreeRes* rr = tc.tres + b * c.nsb;
+    s = ts_in[b];
+    if (s.phase != kTreeWaitG) {  // final or done: carried over
+      if (lead && t == 0) ts_out[b] = s;
+      return;
+    }
+    // fp64-grade normalisers of the row pair and G(c_new) from the previous pass
+    const TreeRes* rr = tres_in + b * c.nsb;
     double sp = 0.0, sq = 0.0;
     for (int sb = t; sb < c.nsb; sb += kWG) {
       sp += rr[sb].sp;
@@ -170,7 +279,6 @@ __global__ __launch_bounds__(kWG) void k_tree_walk(LinCfg c, TreeTopo tp, TreeCf
     double g = 0.0;
     for (int sb = t; sb < c.nsb; sb += kWG) g += fmax(0.0, rr[sb].a / Sp - s.c_new * rr[sb].bq / Sq);
     const double G = block_sum(g, sh);
-    if (t != 0) return;
     s.Sp = Sp;
     s.Sq = Sq;
     s.has_exact = 1;
@@ -180,61 +288,27 @@ __global__ __launch_bounds__(kWG) void k_tree_walk(LinCfg c, TreeTopo tp, TreeCf
     }
     s.phase = kTreeTest;
   }
-  // thread 0: accept tests down the tree until the next rejection
-  const int D = tc.D;
-  for (;;) {
-    const int row = s.row;
-    const int k0 = tp.off[row], nk = tp.off[row + 1] - k0;
-    if (nk == 0) {  // leaf: draw from P
-      s.phase = kTreeFinal;
-      s.c_new = 0.0;
-      s.c_old = 0.0;
-      break;
-    }
-    const int child = tp.kids[k0 + s.j];
-    const int tok = tc.tokens[b * N + child];
-    const float ap = E::load1(tree_prow(c, b, row), tok);
-    const float aq = E::load1(tree_qrow(c, b, row), tok);
-    double P, Q;
-    if (s.has_exact) {
-      WRow wp, wq;  // exact sums come from a residual-type pass over this row pair
-      wpair(DT == kBF16 && c.tab, s.mp, s.mq, true, c.c64, wp, wq);
-      P = fweight<DT>(ap, wp, c.c64, nullptr) / s.Sp;
-      Q = fweight<DT>(aq, wq, c.c64, nullptr) / s.Sq;
-    } else {
-      P = ::exp(((double)ap - (double)s.mp) * c.invT - ::log(s.sp_hat));
-      Q = ::exp(((double)aq - (double)s.mq) * c.invT - ::log(s.sq_hat));
-    }
-    const double r = s.cj == 0.0 ? P : fmax(0.0, P - s.cj * Q) / s.Gj;
-    const double u = c.rng.u((uint32_t)b, (uint32_t)row, (uint32_t)(kDrawAccept + s.j));
-    if (u * Q < r) {
-      tc.out_path[b * D + s.len] = child;
-      c.out_tokens[b * (D + 1) + s.len] = tok;
-      ++s.len;
-      s.row = child + 1;
-      load_row_stats(s, rs, N, s.row);
-      continue;
-    }
-    ++s.j;
-    s.c_old = s.cj;
-    s.c_new = s.cj + s.Gj;
-    s.phase = s.j < nk ? kTreeWaitG : kTreeFinal;
-    break;
+  gather_nodes<DT>(c, tp, tc, b, s_nodes);
+  __syncthreads();
+  if (t == 0) {
+    tree_walk_steps<DT>(c, tp, tc, b, s, rs, s_nodes, lead);
+    s.buf = round & 1;
+    s_st = s;
+    if (lead) ts_out[b] = s;
   }
-  tc.ts[b] = s;
+  __syncthreads();
+  const int sb = blockIdx.x * kWaves + t / kWave;
+  if (sb < c.nsb) tree_pass_sb<DT, AL>(c, s_st, b, sb, tres_out);
 }
 
 // -------------------------------------------------------------- row pass --
+// fp64 sums of sub-block sb of the row pair of state s (request b), one wave:
+// the target row alone at a leaf, else the residual parts for c_new and c_old.
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_tree_pass(LinCfg c, TreeCfg tc, int final_pass) {
+__device__ __forceinline__ void tree_pass_sb(const LinCfg& c, const TreeState& s, int64_t b, int sb, TreeRes* dst) {
   constexpr int EPV = Elem<DT>::kPerVec;
   constexpr int VPL = kSB / (kWave * EPV);
-  const int64_t b = blockIdx.y;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int sb = blockIdx.x * kWaves + wave;
-  if (sb >= c.nsb) return;
-  const TreeState s = tc.ts[b];
-  if (s.phase != (final_pass ? kTreeFinal : kTreeWaitG)) return;
+  const int lane = threadIdx.x & (kWave - 1);
   const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
   TreeRes out = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   const double c64 = c.c64;
@@ -285,81 +359,110 @@ __global__ __launch_bounds__(kWG) void k_tree_pass(LinCfg c, TreeCfg tc, int fin
     out.a0 = wave_sum(a0);
     out.bq0 = wave_sum(bq0);
   }
-  if (lane == 0) tc.tres[b * c.nsb + sb] = out;
+  if (lane == 0) dst[b * c.nsb + sb] = out;
+}
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(kWG) void k_tree_pass(LinCfg c, TreeCfg tc, int final_pass) {
+  const int64_t b = blockIdx.y;
+  const int sb = blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (sb >= c.nsb) return;
+  const TreeState s = tc.ts[b];
+  if (s.phase != (final_pass ? kTreeFinal : kTreeWaitG)) return;
+  tree_pass_sb<DT, AL>(c, s, b, sb, tc.tres);
 }
 
 // ------------------------------------------------------------ final pick --
+// One wave per request: the final token from the running target at the
+// stopping row, with the state's sub-block sums loaded once into registers
+// (V <= 64 * kTreePickPer * 1024; larger rows read them from memory), the
+// sub-block selection, and a rescan of one sub-block with 16-byte loads.
+constexpr int kTreePickPer = 4;
+
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_tree_pick(LinCfg c, TreeCfg tc) {
-  using E = Elem<DT>;
+__global__ __launch_bounds__(kWave) void k_tree_pick(LinCfg c, TreeCfg tc) {
   const int64_t b = blockIdx.x;
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x;
   const TreeState s = tc.ts[b];
   if (s.phase != kTreeFinal) return;
   const int nsb = c.nsb, D = tc.D;
-  const TreeRes* rr = tc.tres + b * nsb;
-  __shared__ double sh[kWG + kWaves];
+  const TreeRes* rr = (s.buf ? tc.tres2 : tc.tres) + b * nsb;
+  const bool inreg = nsb <= kWave * kTreePickPer;
+  TreeRes mr[kTreePickPer];
+  if (inreg) {
+#pragma unroll
+    for (int k = 0; k < kTreePickPer; ++k) {
+      const int sb = lane * kTreePickPer + k;
+      mr[k] = sb < nsb ? rr[sb] : TreeRes{0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    }
+  }
+  auto lane_sum = [&](auto f) {
+    double acc = 0.0;
+    if (inreg) {
+#pragma unroll
+      for (int k = 0; k < kTreePickPer; ++k) acc += f(mr[k]);
+    } else {
+      for (int i = lane; i < nsb; i += kWave) acc += f(rr[i]);
+    }
+    return acc;
+  };
   const char* prow = tree_prow(c, b, s.row);
   const char* qrow = tree_qrow(c, b, s.row);
   const double c64 = c.c64;
   WRow rwp, rwq;
   wpair(DT == kBF16 && c.tab, s.mp, s.mq, s.c_new != 0.0, c64, rwp, rwq);
-  auto wp = [&](int64_t j) { return fweight<DT>(E::load1(prow, j), rwp, c64, nullptr); };
-  auto wq = [&](int64_t j) { return fweight<DT>(E::load1(qrow, j), rwq, c64, nullptr); };
   const double u = c.rng.u((uint32_t)b, (uint32_t)(s.urow1 > 0 ? s.urow1 - 1 : s.row), kDrawFinal);
-  int y;
-  if (s.c_new == 0.0) {
-    // leaf: unnormalised target weights, as for the bonus draw of the linear path
-    double mine = 0.0;
-    for (int sb = t; sb < nsb; sb += kWG) mine += rr[sb].sp;
-    const double W = block_sum(mine, sh);
-    y = pick_index(
-        nsb, c.V, u * W, [&](int sb) { return rr[sb].sp; },
-        wp, sh);
-  } else {
-    double a = 0.0, q = 0.0;
-    for (int sb = t; sb < nsb; sb += kWG) {
-      a += rr[sb].sp;
-      q += rr[sb].sq;
-    }
-    const double Sp = block_sum(a, sh);
-    const double Sq = block_sum(q, sh);
+  // 0: target weights (a leaf, or a residual (P - Q)+ that vanished); 1: (P - c_new Q)+;
+  // 2: (r - Q)+ vanished, so r stays (P - c_old Q)+
+  int mode = 0;
+  double Sp = 1.0, Sq = 1.0, cm = 0.0, W = 0.0;
+  if (s.c_new != 0.0) {
+    Sp = wave_sum(lane_sum([](const TreeRes& r) { return r.sp; }));
+    Sq = wave_sum(lane_sum([](const TreeRes& r) { return r.sq; }));
     const double c1 = s.c_new;
-    double mine = 0.0;
-    for (int sb = t; sb < nsb; sb += kWG) mine += fmax(0.0, rr[sb].a / Sp - c1 * rr[sb].bq / Sq);
-    const double G1 = block_sum(mine, sh);
-    if (G1 > 0.0) {
-      y = pick_index(
-          nsb, c.V, u * G1, [&](int sb) { return fmax(0.0, rr[sb].a / Sp - c1 * rr[sb].bq / Sq); },
-          [&](int64_t j) {
-            const double ep = wp(j), eq = wq(j);
-            return fmax(0.0, ep / Sp - c1 * eq / Sq);
-          },
-          sh);
+    W = wave_sum(lane_sum([&](const TreeRes& r) { return fmax(0.0, r.a / Sp - c1 * r.bq / Sq); }));
+    if (W > 0.0) {
+      mode = 1;
+      cm = c1;
     } else if (s.c_old > 0.0) {
-      // (r - Q)+ vanished: r stays (P - c_old Q)+ / G(c_old)
       const double c0 = s.c_old;
-      double m0 = 0.0;
-      for (int sb = t; sb < nsb; sb += kWG) m0 += fmax(0.0, rr[sb].a0 / Sp - c0 * rr[sb].bq0 / Sq);
-      const double G0 = block_sum(m0, sh);
-      y = pick_index(
-          nsb, c.V, u * G0, [&](int sb) { return fmax(0.0, rr[sb].a0 / Sp - c0 * rr[sb].bq0 / Sq); },
-          [&](int64_t j) {
-            const double ep = wp(j), eq = wq(j);
-            return fmax(0.0, ep / Sp - c0 * eq / Sq);
-          },
-          sh);
-    } else {
-      // (P - Q)+ vanished: r stays P
-      double m0 = 0.0;
-      for (int sb = t; sb < nsb; sb += kWG) m0 += rr[sb].sp;
-      const double W = block_sum(m0, sh);
-      y = pick_index(
-          nsb, c.V, u * W, [&](int sb) { return rr[sb].sp; },
-          wp, sh);
+      W = wave_sum(lane_sum([&](const TreeRes& r) { return fmax(0.0, r.a0 / Sp - c0 * r.bq0 / Sq); }));
+      mode = 2;
+      cm = c0;
     }
   }
-  if (t == 0) {
+  auto wsb = [&](const TreeRes& r) {
+    return mode == 1 ? fmax(0.0, r.a / Sp - cm * r.bq / Sq) : (mode == 2 ? fmax(0.0, r.a0 / Sp - cm * r.bq0 / Sq) : r.sp);
+  };
+  if (mode == 0) W = wave_sum(lane_sum([](const TreeRes& r) { return r.sp; }));
+  const double target = u * W;
+  double pref;
+  int sel;
+  if (inreg) {
+    double v[kTreePickPer];
+#pragma unroll
+    for (int k = 0; k < kTreePickPer; ++k) v[k] = wsb(mr[k]);
+    sel = wave_select_reg(nsb, target, v, pref);
+  } else {
+    sel = wave_select(nsb, target, [&](int i) { return wsb(rr[i]); }, pref);
+  }
+  int y = -1;
+  if (sel >= 0) {
+    const int64_t j0 = (int64_t)sel * kSB + (int64_t)lane * 16;
+    Raw16<DT> rp, rq;
+    raw16<DT, AL>(c, prow, j0, rp);
+    if (mode != 0) raw16<DT, AL>(c, qrow, j0, rq);
+    double w[16];
+    weights16<DT>(c, rp, j0, rwp, nullptr, w);
+    if (mode != 0) {
+      double wq16[16];
+      weights16<DT>(c, rq, j0, rwq, nullptr, wq16);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) w[k] = fmax(0.0, w[k] / Sp - cm * wq16[k] / Sq);
+    }
+    y = wave_rescan(sel, target - pref, w);
+  }
+  if (lane == 0) {
     c.out_tokens[b * (D + 1) + s.len] = y;
     c.out_len[b] = s.len;
     TreeState d = s;
@@ -572,20 +675,25 @@ __global__ __launch_bounds__(kWG) void k_tree_filt(LinCfg c, FiltCfg f, TreeTopo
 // ------------------------------------------------------------- launchers --
 template <int DT, bool AL>
 static hipError_t tree_sampled_t(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int rounds, hipStream_t s) {
-  const dim3 pass_grid((c.nsb + kWaves - 1) / kWaves, (unsigned)c.B);
-  PSI_LAUNCH(s, (k_tree_walk<DT>), dim3((unsigned)c.B), dim3(kWG), c, tp, tc, 1);
-  for (int r = 0; r < rounds; ++r) {
-    PSI_LAUNCH(s, (k_tree_pass<DT, AL>), pass_grid, dim3(kWG), c, tc, 0);
-    PSI_LAUNCH(s, (k_tree_walk<DT>), dim3((unsigned)c.B), dim3(kWG), c, tp, tc, 0);
-  }
-  PSI_LAUNCH(s, (k_tree_pass<DT, AL>), pass_grid, dim3(kWG), c, tc, 1);
-  PSI_LAUNCH(s, (k_tree_pick<DT, AL>), dim3((unsigned)c.B), dim3(kWG), c, tc);
+  const dim3 grid((c.nsb + kWaves - 1) / kWaves, (unsigned)c.B);
+  for (int r = 0; r <= rounds; ++r) PSI_LAUNCH(s, (k_tree_wp<DT, AL>), grid, dim3(kWG), c, tp, tc, r);
+  TreeCfg tf = tc;  // the last round's states
+  tf.ts = (rounds & 1) ? tc.ts2 : tc.ts;
+  PSI_LAUNCH(s, (k_tree_pick<DT, AL>), dim3((unsigned)c.B), dim3(kWave), c, tf);
   return hipGetLastError();
 }
 
 hipError_t launch_tree_sampled(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int rounds, int dtype,
                                hipStream_t s) {
   hipError_t e = hipSuccess;
+  if (c.fused && dtype == kBF16 && c.tab) {
+    // node drafts in one pass per draft row (which writes that row's chunk
+    // records); the target rows' records by waves of the same launch
+    e = launch_tree_qrows(c, tp, tc, s);
+    if (e != hipSuccess) return e;
+    return c.aligned ? tree_sampled_t<kBF16, true>(c, tp, tc, rounds, s)
+                     : tree_sampled_t<kBF16, false>(c, tp, tc, rounds, s);
+  }
   if (c.fused) {
     // node drafts: fp64 sub-block records of every draft row, then one pick per node
     e = launch_draftpass(c, c.B * (int64_t)(tc.N + 1), dtype, s);
@@ -607,7 +715,7 @@ template <int DT, bool AL>
 static hipError_t tree_final_t(const LinCfg& c, const TreeCfg& tc, hipStream_t s) {
   PSI_LAUNCH(s, (k_tree_pass<DT, AL>), dim3((unsigned)((c.nsb + kWaves - 1) / kWaves), (unsigned)c.B), dim3(kWG), c,
              tc, 1);
-  PSI_LAUNCH(s, (k_tree_pick<DT, AL>), dim3((unsigned)c.B), dim3(kWG), c, tc);
+  PSI_LAUNCH(s, (k_tree_pick<DT, AL>), dim3((unsigned)c.B), dim3(kWave), c, tc);
   return hipGetLastError();
 }
 
