@@ -550,7 +550,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": "k_stats32",
                      "bytes_per_launch": stats_bytes(B, K, V), "avg_launch_us": 1e3 * stats_ms,
-                     "launches_timed": int(dur.shape[0])},
+                     "launches_timed": int(dur.shape[0]),
+                     # the whole verification call against the same peak (algorithmic bytes of the call
+                     # over its HIP-event time), beside the dominant kernel's figure above
+                     "whole_call_GB_per_s": call_gbs, "whole_call_frac": call_gbs / HBM_PEAK_GBS},
         "kernels": kernels,
         "per_rho": per_rho,
     }
