@@ -348,9 +348,10 @@ int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64
  * verification rule of psispec_verify_linear). The logits are products of
  * hidden states with the vocabulary matrix, p_logits = h_target W^T and
  * q_logits = h_draft W^T, computed on bf16 matrix cores (fp32 accumulation)
- * tile by tile and reduced as they are produced: the K + 1 target and K draft
- * rows are never written out; only the final residual or bonus rows are
- * formed again for the draw.
+ * tile by tile and reduced as they are produced (per row and 512-token tile,
+ * the maximum and the sum of exponentials); the same pass stores the fp32
+ * logits in the workspace, from which the final draw reads the residual or
+ * bonus rows, so the product is made once.
  *   h_target      [B, K+1, H] bf16 target hidden states (row K: the bonus row).
  *   h_draft       [B, K, H] bf16 draft hidden states.
  *   w_vocab       [V, H] bf16 vocabulary matrix (row v gives token v's logit).
@@ -359,9 +360,10 @@ int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64
  *                 psispec_verify_linear, whose decision rules apply unchanged
  *                 to these logits.
  *   out_tokens    [B, K+1], out_len [B]: as psispec_verify_linear.
- * H must be a multiple of 64 and the three inputs 16-byte aligned. The logits
+ * H must be a multiple of 128 and the three inputs 16-byte aligned. The logits
  * carry the fp32 accumulation error of an H-term dot product.
- * Workspace: psispec_lmhead_workspace_bytes(B, K, V).
+ * Workspace: psispec_lmhead_workspace_bytes(B, K, V), about 4 B (2K + 1) V
+ * bytes (the logits of every row), 256-byte aligned.
  */
 size_t psispec_lmhead_workspace_bytes(int64_t B, int32_t K, int32_t V);
 int psispec_verify_lmhead(const void* h_target, const void* h_draft, const void* w_vocab, int64_t B, int32_t K,

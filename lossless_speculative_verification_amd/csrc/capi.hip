@@ -536,7 +536,7 @@ int psispec_generate_toy(int64_t B, int32_t block, int32_t V, int dtype, const p
 namespace psi {
 namespace {
 struct LmhLayout {
-  size_t st, fin, ts, tres, out, total;
+  size_t st, ts, tres, out, total;
 };
 inline LmhLayout lmh_layout(int64_t B, int32_t K, int32_t V) {
   LmhLayout L;
@@ -545,14 +545,12 @@ inline LmhLayout lmh_layout(int64_t B, int32_t K, int32_t V) {
   size_t off = 0;
   L.st = off;
   off = align_up(off + (size_t)(rows * ntn) * sizeof(StatRec), 256);
-  L.fin = off;
-  off = align_up(off + (size_t)(2 * B) * sizeof(int32_t), 256);
   L.ts = off;
   off = align_up(off + (size_t)B * sizeof(TreeState), 256);
   L.tres = off;
   off = align_up(off + (size_t)B * nsb_of(V) * sizeof(TreeRes), 256);
-  L.out = off;
-  off = align_up(off + (size_t)(2 * B) * V * sizeof(float), 256);
+  L.out = off;  // the logits of every row, kept by the product for the final draw
+  off = align_up(off + (size_t)rows * V * sizeof(float), 256);
   L.total = off;
   return L;
 }
@@ -594,13 +592,13 @@ int psispec_verify_lmhead(const void* h_target, const void* h_draft, const void*
   g.draft = draft_tokens;
   g.c32 = (float)(1.4426950408889634074 / (double)params->temperature);
   g.st = (StatRec*)(w + L.st);
-  g.fin = (int32_t*)(w + L.fin);
-  g.out = (float*)(w + L.out);
-  // the draw over the final rows: target rows [B, V] then draft rows [B, V] (fp32)
+  g.all = (float*)(w + L.out);
+  // the draw over the final rows, read from the kept logits: target rows [B, K + 1, V], then
+  // draft rows [B, K, V] (fp32)
   psispec_params prm = *params;
   prm.flags = 0;
   LinCfg c;
-  fill_common(c, g.out, g.out + (size_t)B * V, PSISPEC_DTYPE_F32, B, 1, V, &prm, workspace, 1);
+  fill_common(c, g.all, g.all + (size_t)g.Mp * V, PSISPEC_DTYPE_F32, B, K, V, &prm, workspace, K + 1);
   c.st = nullptr;  // the draw uses only the tree-state sections below
   c.ar = nullptr;
   c.rs = nullptr;
@@ -623,11 +621,6 @@ int psispec_verify_lmhead(const void* h_target, const void* h_draft, const void*
   gs.ntm = (int)((gs.M + kLmhTileM - 1) / kLmhTileM);
   hipError_t e = launch_lmh_stats(gs, stream);
   if (e == hipSuccess) e = launch_lmh_decide(gs, c, tc, stream);
-  LmhCfg gl = g;
-  gl.M = 2 * B;
-  gl.ntm = (int)((gl.M + kLmhTileM - 1) / kLmhTileM);
-  gl.rows = g.fin;
-  if (e == hipSuccess) e = launch_lmh_logits(gl, stream);
   if (e == hipSuccess) e = launch_tree_final(c, tc, PSISPEC_DTYPE_F32, stream);
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }

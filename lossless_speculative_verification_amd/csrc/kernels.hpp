@@ -324,10 +324,9 @@ hipError_t launch_commit(int64_t B, int K, int r, int rounds, int max_len, const
 hipError_t launch_toy_logits(int64_t rows, int V, const int32_t* ctx, const int32_t* pos, int kind,
                              const psispec_toy_model& m, int dtype, void* out, hipStream_t s);
 // Linear verification fused with the LM head (lmhead.hip).
-enum LmhMode { kLmhStats = 0, kLmhLogits = 1 };
-constexpr int kLmhTileM = 128;  // rows of a product tile
-constexpr int kLmhTileN = 512;  // vocabulary entries of a product tile
-constexpr int kLmhStepK = 64;   // the hidden size must be a multiple of this
+constexpr int kLmhTileM = 256;  // rows of a product tile
+constexpr int kLmhTileN = 256;  // vocabulary entries of a product tile
+constexpr int kLmhStepK = 128;  // the hidden size must be a multiple of this
 struct LmhCfg {
   const uint16_t* hp;     // [Mp, H] target hidden states (bf16 bits)
   const uint16_t* hq;     // [Mq, H] draft hidden states
@@ -337,16 +336,14 @@ struct LmhCfg {
   int64_t B;
   int K, H, V;
   int ntm, ntn;           // row tiles, vocabulary tiles
-  const int32_t* rows;    // combined row index of each row of this product (nullptr: the identity)
   const int32_t* draft;   // [B, K]
   float c32;
   StatRec* st;            // [Mp + Mq][ntn] per (row, vocabulary tile)
-  int32_t* fin;           // [2 B] final rows: target row n of each request, then draft row n
-  float* out;             // [M][V] logits (final-row product)
+  float* all;             // [Mp + Mq][V] fp32 logits of every row, kept for the final draw
+                          // (nullptr: not kept)
 };
 hipError_t launch_lmh_stats(const LmhCfg& g, hipStream_t s);
 hipError_t launch_lmh_decide(const LmhCfg& g, const LinCfg& c, const TreeCfg& tc, hipStream_t s);
-hipError_t launch_lmh_logits(const LmhCfg& g, hipStream_t s);
 // The final draw of a tree-state row pair (tree.hip): the fp64 pass over the
 // rows in c.rows and the pick, for every request whose state is kTreeFinal.
 hipError_t launch_tree_final(const LinCfg& c, const TreeCfg& tc, int dtype, hipStream_t s);

@@ -3,38 +3,45 @@
 // ("Uno" research explainer, §3.1: the AR path and the diffusion path share
 // the base model and its output head; §3.3: the verifier needs p and q of the
 // drafted tokens, then one residual or bonus row), computed tile by tile with
-// bf16 matrix cores and reduced in the tile's epilogue, so that the logits of
-// the K + 1 target and K draft rows never reach HBM.
+// bf16 matrix cores and reduced in the tile's epilogue. The product is made
+// once: its epilogue also stores the fp32 logits, of which the final draw
+// reads only target row n and draft row n of each request.
 //
 // Pipeline on the caller's stream:
-//   k_lmh_gemm<kLmhStats>   every target and draft row against every 512-token
+//   k_lmh_gemm              every target and draft row against every 512-token
 //                           vocabulary tile: per (row, tile) the maximum and a
-//                           binary32-grade sum of 2^((z - m) c);
+//                           binary32-grade sum of 2^((z - m) c), and the logits;
 //   k_lmh_decide            per request: row normalisers, the drafted tokens'
 //                           logits (dot products), accept tests
 //                           u * Q(x) < P(x), first rejection n; the draw state;
-//   k_lmh_gemm<kLmhLogits>  the final rows only (target row n and draft row n,
-//                           or the bonus row): fp32 logits;
-//   k_tree_pass, k_tree_pick (tree.hip) the fp64 residual / bonus draw over them.
+//   k_tree_pass, k_tree_pick (tree.hip) the fp64 residual / bonus draw over the
+//                           kept logits of the final rows.
 //
 // GEMM: C[M, V] = A[M, H] * W[V, H]^T, A rows from the target and draft hidden
-// states. A workgroup computes a 128-row x 512-token tile with four waves, each
-// owning 128 tokens of the tile (all 128 rows): 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16, 256 accumulator registers, one wave per SIMD.
-// Operand tiles of 32 hidden elements per step go from global memory straight
-// into LDS (16-byte direct loads, no register staging) through a four-stage
-// ring: the loads of step s + 3 are issued during step s, one between each
-// pair of its products, into the slot step s - 1 has left. A tile row is 64 bytes in
-// LDS: its four 16-byte slots are permuted by an XOR of row bits 2..3, so that
-// the 16-byte fragment reads of a wave do not conflict in the LDS banks. The
-// tile epilogue reduces each row over the wave's 128 columns with a butterfly
-// across the half-wave (every stage halves the rows a lane carries), then
-// over the four waves through LDS.
-// Block operand layout of the instruction (checked on the device): lane l
-// holds A[l % 32][8 (l / 32) .. +7] and W[col l % 32][8 (l / 32) .. +7]; result
-// element i of lane l is C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
-// Tiles are ordered so that the row tiles of one vocabulary tile run one after
-// another on the same XCD and share its L2 copy of the W tile.
+// states, in 256-row x 256-token tiles. The grid is persistent, one workgroup
+// per compute unit: workgroup b runs on XCD b % 8 and walks its share of the
+// tiles, which are ordered so that the row tiles of one vocabulary tile run at
+// the same time on one XCD and share its L2 copy of the W tile. Four waves,
+// one per SIMD, each own a 128 x 128 quarter of the tile as 8 x 8 blocks of
+// v_mfma_f32_16x16x32_bf16 (256 accumulator registers); on gfx950 this block
+// shape issues at a higher rate than 32 x 32 x 16 (measured: 2.4 against 2.1
+// PFLOP/s from registers). Operand tiles of 32 hidden elements per step go
+// from global memory straight into LDS (16-byte direct loads, no register
+// staging) through a four-stage ring that runs on across tile boundaries: the
+// loads of the next tile's first steps are in flight while a tile's epilogue
+// runs. The loads of step s + 3 are issued during step s, one after each
+// group of 8 products, into the slot step s - 1 has left; the fragments of
+// step s + 1 are read from LDS during the second half of step s (double
+// buffered by step parity). A tile row is 64 bytes in LDS: its four 16-byte
+// slots are permuted by an XOR of row bits 2..3, so that the fragment reads
+// of each 16-lane group fall in distinct banks. The tile epilogue stores the
+// logits and reduces each row over the wave's 128 columns with a butterfly
+// across the 16 lanes of a column group (every stage halves the rows a lane
+// carries), then over the two waves of the row through LDS.
+// Block operand layout of the instruction (checked on the device against the
+// 32 x 32 x 16 form): lane l holds A[l % 16][8 (l / 16) .. +7] and
+// W[col l % 16][8 (l / 16) .. +7]; result element i of lane l is
+// C[4 (l / 16) + i][l % 16].
 #include <type_traits>
 
 #include "rowops.hpp"
@@ -44,12 +51,13 @@ namespace psi {
 namespace {
 
 constexpr int kLmhBM = kLmhTileM, kLmhBN = kLmhTileN, kLmhBK = 32;
-static_assert(kLmhBM == 128 && kLmhBN == 512, "four 128 x 128 wave tiles side by side");
-static_assert(kLmhStepK % kLmhBK == 0, "the hidden size is a multiple of the step");
-constexpr int kStages = 4;                        // ring depth (160 KB): loads of step s + 3 spread over step s
+static_assert(kLmhBM == 256 && kLmhBN == 256, "2 x 2 wave quarters of 128 x 128");
+static_assert(kLmhStepK == 4 * kLmhBK, "at least 4 steps, an even number (fragment buffers alternate)");
+constexpr int kWN = 2;                            // waves side by side along the vocabulary
+constexpr int kStages = 4;                        // ring depth (128 KB): loads of step s + 3 spread over step s
 constexpr int kRowB = kLmhBK * 2;                 // bytes of a tile row per step
-constexpr int kAStage = kLmhBM * kRowB;           // 8 KB
-constexpr int kBStage = kLmhBN * kRowB;           // 32 KB
+constexpr int kAStage = kLmhBM * kRowB;           // 16 KB
+constexpr int kBStage = kLmhBN * kRowB;           // 16 KB
 constexpr int kStage = kAStage + kBStage;
 constexpr int kLoadB = kWave * 16;                // bytes of one wave-wide direct load
 constexpr int kRowsPerLoad = kLoadB / kRowB;      // 16 rows of 4 slots
@@ -57,12 +65,12 @@ constexpr int kIA = kAStage / kLoadB / kWaves;    // direct loads per wave per s
 constexpr int kIB = kBStage / kLoadB / kWaves;    //                               W
 constexpr int kLoads = kIA + kIB;
 static_assert(kIA * kLoadB * kWaves == kAStage && kIB * kLoadB * kWaves == kBStage, "whole loads");
-static_assert(kRowsPerLoad == 16 && kLoads == 10, "a load covers 16 rows of 4 slots; 5 loads per half step");
+static_assert(kRowsPerLoad == 16 && kLoads == 8, "a load covers 16 rows of 4 slots; 4 loads per half step");
 constexpr int kHalfLoads = kLoads / 2;
 constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Slot permutation of tile row r (its 4 16-byte slots, by bits 2..3 of r: a
@@ -97,6 +105,14 @@ __device__ __forceinline__ void wait_vm() {
 // Workgroup barrier with no memory fence: the direct loads are waited for
 // explicitly; the asm statements keep the compiler from moving LDS accesses
 // across it.
+// The lane index, computed where it is used: an asm statement is neither
+// merged with another nor moved, so the value is not kept live (or spilled)
+// across the main loop.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 __device__ __forceinline__ void lmh_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -105,198 +121,268 @@ __device__ __forceinline__ void lmh_barrier() {
 
 }  // namespace
 
-template <int MODE>
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k_lmh_gemm(LmhCfg g) {
-  // ring of operand tiles; after the main loop its start holds the
-  // epilogue's per-wave row maxima and sums
-  __shared__ __attribute__((aligned(1024))) unsigned char s_mem[kStages * kStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char s_mem[kStages * kStage];  // operand ring
+  __shared__ float s_wm[kWN][kLmhBM], s_ws[kWN][kLmhBM];  // epilogue: per-wave row maxima and sums
   const int t = threadIdx.x, lane = t & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
-  // tile order: row tiles of one vocabulary tile consecutive on one XCD
-  // (workgroup g runs on XCD g % 8; the grid is a multiple of 8)
-  const int64_t per = (int64_t)gridDim.x / kXcds;
-  const int64_t lt = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  if (lt >= (int64_t)g.ntm * g.ntn) return;  // the whole workgroup
-  const int64_t tn = lt / g.ntm, tm = lt - tn * g.ntm;
-  const int64_t m0 = tm * kLmhBM, n0 = tn * kLmhBN;
-  auto combined_row = [&](int row) -> int64_t {  // combined row index of tile row `row` (-1 past the end)
-    const int64_t i = m0 + row;
-    if (i >= g.M) return -1;
-    return g.rows ? (int64_t)g.rows[i] : i;
+  const int wm = wave / kWN, wn = wave % kWN;
+  // tiles of this workgroup: XCD x (workgroups x, x + 8, ...) takes the
+  // consecutive tiles [x per, (x + 1) per); its workgroup j the tiles
+  // x per + j + i slots (the grid is a multiple of 8)
+  const int G = g.ntm * g.ntn;
+  const int per = (G + kXcds - 1) / kXcds;
+  const int slots = (int)(gridDim.x / kXcds);
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int lt_lo = xcd * per, lt_hi = (xcd + 1) * per < G ? (xcd + 1) * per : G;
+  const int mine = lt_lo + slot < lt_hi ? (lt_hi - lt_lo - slot + slots - 1) / slots : 0;
+  if (mine == 0) return;  // the whole workgroup
+  const int steps = g.H / kLmhBK;
+  // Tile coordinates (row tile tm, vocabulary tile tn = lt / ntm) of this
+  // workgroup's tiles, stepped by `slots` tiles without a division.
+  struct TilePos {
+    int tm, tn;
   };
+  const int ntm = g.ntm;
+  const int dn = __builtin_amdgcn_readfirstlane(slots / ntm), dm = slots - dn * ntm;
+  auto next_tile = [&](TilePos p) {
+    p.tm += dm;
+    p.tn += dn;
+    if (p.tm >= ntm) {
+      p.tm -= ntm;
+      ++p.tn;
+    }
+    p.tm = __builtin_amdgcn_readfirstlane(p.tm);
+    p.tn = __builtin_amdgcn_readfirstlane(p.tn);
+    return p;
+  };
+  TilePos first;
+  first.tn = __builtin_amdgcn_readfirstlane((lt_lo + slot) / ntm);
+  first.tm = __builtin_amdgcn_readfirstlane(lt_lo + slot - first.tn * ntm);
 
   // direct loads: load j of this wave fills 16 tile rows; lane l writes LDS
   // slot l % 4 of row l / 4 of them, i.e. logical slot (l % 4) ^ swz(row),
   // swz(row) = swz(l / 4). Rows past the end read a valid row (their results
-  // are never used).
-  const int lr = lane >> 2;
-  const int kvo = ((lane & 3) ^ lmh_swz(lr)) * 8;  // element offset of this lane's slot
-  const uint16_t* src[kLoads];                     // loads 0 .. kIA - 1: A rows; then W rows
+  // are never used). src[j]: the next load of j, advanced by a step per load.
+  const uint16_t* src[kLoads];  // loads 0 .. kIA - 1: A rows; then W rows
+  auto set_src = [&](TilePos p) {
+    // the lane terms are taken again here (once per tile), not kept live
+    const int lid = lane_here();
+    const int lr = lid >> 2;
+    const int kvo = ((lid & 3) ^ lmh_swz(lr)) * 8;  // element offset of this lane's slot
+    const int64_t m0 = (int64_t)p.tm * kLmhBM, n0 = (int64_t)p.tn * kLmhBN;
 #pragma unroll
-  for (int j = 0; j < kIA; ++j) {
-    const int64_t r = combined_row((wave * kIA + j) * kRowsPerLoad + lr);
-    src[j] = lmh_arow(g, r >= 0 ? r : 0) + kvo;
-  }
+    for (int j = 0; j < kIA; ++j) {
+      const int64_t r = m0 + (wave * kIA + j) * kRowsPerLoad + lr;
+      src[j] = lmh_arow(g, r < g.M ? r : 0) + kvo;
+    }
 #pragma unroll
-  for (int j = 0; j < kIB; ++j) {
-    const int64_t n = n0 + (int64_t)(wave * kIB + j) * kRowsPerLoad + lr;
-    src[kIA + j] = g.w + (n < g.V ? n : (int64_t)g.V - 1) * g.H + kvo;
-  }
+    for (int j = 0; j < kIB; ++j) {
+      const int64_t n = n0 + (int64_t)(wave * kIB + j) * kRowsPerLoad + lr;
+      src[kIA + j] = g.w + (n < g.V ? n : (int64_t)g.V - 1) * g.H + kvo;
+    }
+  };
   auto dst = [&](unsigned char* st, int j) {
     return j < kIA ? st + (wave * kIA + j) * kLoadB : st + kAStage + (wave * kIB + (j - kIA)) * kLoadB;
   };
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.0f;
-
-  // fragment reads: lane l reads row (block + l % 32), logical slot
-  // 2 q + l / 32 of slice q; swz(row) = swz(l % 16)
-  const int fr = lane & 31, half = lane >> 5;
-  const int frow = fr * kRowB;
-  const int fsw = lmh_swz(fr);
-  const int bw = kAStage + wave * 128 * kRowB;  // this wave's W rows in a stage
-  bf16x8_t fa[2][4], fb[2][4];
-  auto read_frag = [&](const unsigned char* st, int q, int slot) {
-    const int fo = frow + (((2 * q + half) ^ fsw) * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[slot][i] = *(const bf16x8_t*)(st + i * 32 * kRowB + fo);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fb[slot][i] = *(const bf16x8_t*)(st + bw + i * 32 * kRowB + fo);
-  };
-  // row blocks of 32 that hold rows of the product (a last row tile may be
-  // partial: its empty blocks are not multiplied)
-  const int mblocks = (int)((g.M - m0 + 31) / 32 < 4 ? (g.M - m0 + 31) / 32 : 4);
-  auto mfma1 = [&](int slot, int i) {
-    if ((i >> 2) < mblocks)
-      acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i >> 2], fb[slot][i & 3],
-                                                                   acc[i >> 2][i & 3], 0, 0, 0);
-  };
-
-  const int steps = g.H / kLmhBK;
   auto ring = [&](int i) { return s_mem + i * kStage; };
-  // Waits until at most n direct loads of this wave are outstanding.
-  auto wait_loads = [&](int n) {
-    if (n >= 3 * kHalfLoads) wait_vm<3 * kHalfLoads>();
-    else if (n >= 2 * kHalfLoads) wait_vm<2 * kHalfLoads>();
-    else if (n >= kHalfLoads) wait_vm<kHalfLoads>();
-    else wait_vm<0>();
+  // load cursor: step ls of tile lk (at lpos) is loaded next
+  int lk = 0, ls = 0;
+  TilePos lpos = first;
+  auto issue = [&](unsigned char* st, int j) {
+    lmh_dma16(src[j], dst(st, j));
+    src[j] += kLmhBK;
   };
-  // prologue: steps 0 .. kStages - 2 in flight, wait for step 0
+  auto advance = [&]() {
+    if (++ls == steps) {
+      ls = 0;
+      ++lk;
+      if (lk < mine) {
+        lpos = next_tile(lpos);
+        set_src(lpos);
+      }
+    }
+  };
+
+  // fragment reads: lane l reads row 16 i + l % 16, logical slot l / 16;
+  // swz(row) = swz(l % 16)
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int fo = r16 * kRowB + ((q4 ^ lmh_swz(r16)) * 16);
+  const int ba = wm * 128 * kRowB + fo, bw = kAStage + wn * 128 * kRowB + fo;
+  // fragments: A single-buffered (rows 4..7 of a step are read during its
+  // first half, rows 0..3 of the next step during its second half), W by
+  // step parity
+  bf16x8_t fa[8], fb[2][8];
+
+  // prologue: the first kStages - 1 steps in flight, wait for the first
+  set_src(lpos);
 #pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < steps)
+  for (int p = 0; p < kStages - 1; ++p) {
 #pragma unroll
-      for (int j = 0; j < kLoads; ++j) lmh_dma16(src[j] + p * kLmhBK, dst(ring(p), j));
-  wait_loads(((steps > 1) + (steps > 2)) * kLoads);
+    for (int j = 0; j < kLoads; ++j) issue(ring(p), j);
+    advance();
+  }
+  wait_vm<(kStages - 2) * kLoads>();  // steps 1 and 2 may stay in flight
   lmh_barrier();
-  read_frag(ring(0), 0, 0);
-  int cur = 0;  // ring slot of step s
-  // One step; REFILL: the loads of step s + 3 are issued (every step but the
-  // last three, which run a copy of the body without them).
-  auto step = [&](int s, auto refill_tag) {
-    constexpr bool kRefill = decltype(refill_tag)::value;
-    unsigned char* st = ring(cur);
-    const int nxt = cur == kStages - 1 ? 0 : cur + 1;
-    // The loads of step s + 3 go to the slot of step s - 1, free since the
-    // middle of step s - 1; they are spread over the products of step s, one
-    // between each pair (the load unit takes them as fast as they come).
-    unsigned char* fill = ring(cur == 0 ? kStages - 1 : cur - 1);
-    const int k0 = (s + 3) * kLmhBK;
-    // slice 0 of step s is in fa[0] / fb[0]; slice 1 is read after the first
-    // product (so that the wait for slice 0 does not include its reads)
+  int cur = 0;  // ring slot of the current step
+  TilePos pos = first;
+  for (int k = 0; k < mine; ++k, pos = next_tile(pos)) {
+    const int tn = pos.tn;
+    const int64_t m0 = (int64_t)pos.tm * kLmhBM, n0 = (int64_t)tn * kLmhBN;
+    // row blocks of 16 of this wave that hold rows of the product (a last
+    // row tile may be partial: its empty blocks are not multiplied)
+    const int64_t mrem = g.M - m0 - wm * 128;
+    const int mb = mrem <= 0 ? 0 : (int)((mrem + 15) / 16 < 8 ? (mrem + 15) / 16 : 8);
+    f32x4_t acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      mfma1(0, i);
-      if (i == 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        read_frag(st, 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (kRefill && (i & 1) && i / 2 < kHalfLoads) lmh_dma16(src[i / 2] + k0, dst(fill, i / 2));
+    for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 8; ++bj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[bi][bj][e] = 0.0f;
+    {
+      const unsigned char* st = ring(cur);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(st + ba + i * 16 * kRowB);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fb[0][i] = *(const bf16x8_t*)(st + bw + i * 16 * kRowB);
     }
-    // step s + 1 is in; the loads of step s + 2 and the first half of step
-    // s + 3 may stay in flight
-    if (kRefill) wait_vm<kLoads + kHalfLoads>();
-    else wait_loads(s + 2 < steps ? kLoads : 0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of this stage are done
-    lmh_barrier();
-    if (s + 1 < steps) read_frag(ring(nxt), 0, 0);
+    // One step of the tile with its fragments in buffer P. REFILL: the loads
+    // of stream step q + 3 are issued; otherwise (the last three steps of the
+    // stream) LEFT steps beyond q + 1 are still loading.
+    auto step = [&](auto refill_tag, auto par_tag, auto left_tag) {
+      constexpr bool kRefill = decltype(refill_tag)::value;
+      constexpr int P = decltype(par_tag)::value;
+      constexpr int kLeft = decltype(left_tag)::value;
+      const unsigned char* st = ring(cur);
+      const int nxt = cur == kStages - 1 ? 0 : cur + 1;
+      unsigned char* fill = ring(cur == 0 ? kStages - 1 : cur - 1);
+      // first half: row blocks 0..3, a load after each group of 8 products;
+      // the A fragments of row blocks 4..7 are read meanwhile
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      mfma1(1, i);
-      if (kRefill && (i & 1) && i / 2 < kHalfLoads)
-        lmh_dma16(src[kHalfLoads + i / 2] + k0, dst(fill, kHalfLoads + i / 2));
-    }
-    cur = nxt;
-  };
-  int s = 0;
-  for (; s + 3 < steps; ++s) step(s, std::true_type{});
-  for (; s < steps; ++s) step(s, std::false_type{});
-
-  // epilogue tables at the start of the ring (no longer read: every wave
-  // passed the last step's barrier after its last read)
-  float(*s_wm)[kLmhBM] = (float(*)[kLmhBM])s_mem;
-  float(*s_ws)[kLmhBM] = (float(*)[kLmhBM])(s_mem + kWaves * kLmhBM * sizeof(float));
-
-  // ---- epilogue. Element e of block (bi, bj) on this lane: tile row
-  // bi 32 + 8 (e / 4) + 4 (lane / 32) + e % 4, tile column
-  // wave 128 + bj 32 + lane % 32.
-  if constexpr (MODE == kLmhLogits) {
+      for (int bi = 0; bi < 4; ++bi) {
+        fa[4 + bi] = *(const bf16x8_t*)(st + ba + (4 + bi) * 16 * kRowB);
+        if (bi < mb) {
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = bi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const int64_t i = m0 + row;
-        if (i >= g.M) continue;
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const int64_t n = n0 + wave * 128 + bj * 32 + fr;
-          if (n < g.V) g.out[i * (int64_t)g.V + n] = acc[bi][bj][e];
+          for (int bj = 0; bj < 8; ++bj)
+            acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi], fb[P][bj], acc[bi][bj], 0, 0, 0);
         }
+        if (kRefill) issue(fill, bi);
       }
-  } else {
+      // step q + 1 is in (and visible after the barrier); the later steps'
+      // loads may stay in flight: steps q + 2 and half of q + 3 while
+      // refilling, else what the stream has left
+      if (kRefill) wait_vm<kLoads + kHalfLoads>();
+      else wait_vm<kLeft * kLoads>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of this slot are done
+      lmh_barrier();
+      // second half: row blocks 4..7; the next step's A fragments of row
+      // blocks 0..3 and its W fragments (buffer 1 - P) are read meanwhile
+      // (after a tile's last step they are read and not used)
+      const unsigned char* sn = ring(nxt);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        fa[gq] = *(const bf16x8_t*)(sn + ba + gq * 16 * kRowB);
+        fb[1 - P][2 * gq] = *(const bf16x8_t*)(sn + bw + (2 * gq) * 16 * kRowB);
+        fb[1 - P][2 * gq + 1] = *(const bf16x8_t*)(sn + bw + (2 * gq + 1) * 16 * kRowB);
+        const int bi = 4 + gq;
+        if (bi < mb) {
+#pragma unroll
+          for (int bj = 0; bj < 8; ++bj)
+            acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi], fb[P][bj], acc[bi][bj], 0, 0, 0);
+        }
+        if (kRefill) issue(fill, kHalfLoads + gq);
+      }
+      if (kRefill) advance();
+      cur = nxt;
+    };
+    using R = std::true_type;
+    using N = std::false_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using L0 = std::integral_constant<int, 0>;
+    using L1 = std::integral_constant<int, 1>;
+    if (k + 1 < mine) {
+      // the stream goes on into the next tile: every step loads (steps >= 4)
+      for (int s = 0; s < steps; s += 2) {
+        step(R{}, P0{}, L0{});
+        step(R{}, P1{}, L0{});
+      }
+    } else {
+      // the stream's last tile: its last three steps load nothing
+      int s = 0;
+      for (; s + 4 < steps; s += 2) {
+        step(R{}, P0{}, L0{});
+        step(R{}, P1{}, L0{});
+      }
+      step(R{}, P0{}, L0{});
+      step(N{}, P1{}, L1{});
+      step(N{}, P0{}, L0{});
+      step(N{}, P1{}, L0{});
+    }
+
+    // ---- epilogue of the tile (the next tile's first steps are loading).
+    // Element e of block (bi, bj) on this lane: tile row wm 128 + bi 16 +
+    // 4 (lane / 16) + e, tile column wn 128 + bj 16 + lane % 16. The lane
+    // index is taken again here so that the epilogue's address arithmetic is
+    // not kept live across the main loop.
+    const int lid = lane_here();
+    const int er = lid & 15, eq = lid >> 4;
+    if (g.all) {
+      // every logit of the tile, kept for the final draw
+#pragma unroll
+      for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t i = m0 + wm * 128 + bi * 16 + 4 * eq + e;
+          if (i >= g.M) continue;
+#pragma unroll
+          for (int bj = 0; bj < 8; ++bj) {
+            const int64_t n = n0 + wn * 128 + bj * 16 + er;
+            if (n < g.V) g.all[i * (int64_t)g.V + n] = acc[bi][bj][e];
+          }
+        }
+    }
     const float c32 = g.c32;
-    // Per row of the tile (item it = 16 bi + e of this lane: row
-    // 32 bi + 8 (e / 4) + 4 (lane / 32) + e % 4): the maximum and the sum of
-    // 2^((z - m) c) over this lane's 4 columns, then over the 32 lanes of the
-    // half-wave by a butterfly that halves the items at every stage (at offset
-    // o a lane keeps the items whose index bit matches its lane bit and sends
-    // the others), so that lane l ends with items 2 (l % 32) and 2 (l % 32) + 1.
-    bool vcol[4];  // this lane's column of block bj is inside the vocabulary
+    // Per row of the tile (item it = 4 bi + e of this lane: row
+    // 16 bi + 4 (lane / 16) + e of the wave's quarter): the maximum and the
+    // sum of 2^((z - m) c) over this lane's 8 columns, then over the 16 lanes
+    // of the column group by a butterfly that halves the items at every stage
+    // (at offset o a lane keeps the items whose index bit matches its lane bit
+    // and sends the others), so that lane l ends with items 2 (l % 16) and
+    // 2 (l % 16) + 1.
+    bool vcol[8];  // this lane's column of block bj is inside the vocabulary
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) vcol[bj] = n0 + wave * 128 + bj * 32 + fr < g.V;
-    float im[64], is[64];
+    for (int bj = 0; bj < 8; ++bj) vcol[bj] = n0 + wn * 128 + bj * 16 + er < g.V;
+    float im[32], is[32];
 #pragma unroll
-    for (int it = 0; it < 64; ++it) {
-      const int bi = it >> 4, e = it & 15;
+    for (int it = 0; it < 32; ++it) {
+      const int bi = it >> 2, e = it & 3;
       float m = -INFINITY;
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) m = vcol[bj] ? fmaxnan(m, acc[bi][bj][e]) : m;
+      for (int bj = 0; bj < 8; ++bj) m = vcol[bj] ? fmaxnan(m, acc[bi][bj][e]) : m;
       const float mo = is_neg_inf(m) ? 0.0f : m;  // an empty part sums to 0
       float sl = 0.0f;
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) sl += vcol[bj] ? __builtin_amdgcn_exp2f((acc[bi][bj][e] - mo) * c32) : 0.0f;
+      for (int bj = 0; bj < 8; ++bj) sl += vcol[bj] ? __builtin_amdgcn_exp2f((acc[bi][bj][e] - mo) * c32) : 0.0f;
       im[it] = m;
       is[it] = sl;
     }
+    auto xor_lane = [&](float v, int off) {  // v of lane lid ^ off (addresses from the epilogue's lane index)
+      return __int_as_float(__builtin_amdgcn_ds_bpermute((lid ^ off) << 2, __float_as_int(v)));
+    };
     auto part = [&](float mx, float sx, float m) {  // sx 2^((mx - m) c), 0 for an empty part
       return is_neg_inf(mx) ? 0.0f : sx * __builtin_amdgcn_exp2f((mx - m) * c32);
     };
 #pragma unroll
-    for (int stg = 0; stg < 5; ++stg) {
-      const int off = 16 >> stg, n = 32 >> stg;
-      const bool up = (fr & off) != 0;
+    for (int stg = 0; stg < 4; ++stg) {
+      const int off = 8 >> stg, n = 16 >> stg;
+      const bool up = (er & off) != 0;
 #pragma unroll
       for (int i = 0; i < n; ++i) {
         const float mk = up ? im[i + n] : im[i], sk = up ? is[i + n] : is[i];
         const float mo = up ? im[i] : im[i + n], so = up ? is[i] : is[i + n];
-        const float mr = __shfl_xor(mo, off), sr = __shfl_xor(so, off);
+        const float mr = xor_lane(mo, off), sr = xor_lane(so, off);
         const float m = fmaxnan(mk, mr);
         im[i] = m;
         is[i] = is_neg_inf(m) ? 0.0f : part(mk, sk, m) + part(mr, sr, m);
@@ -304,28 +390,28 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int it = 2 * fr + i, bi = it >> 4, e = it & 15;
-      const int row = bi * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-      s_wm[wave][row] = im[i];
-      s_ws[wave][row] = is[i];
+      const int it = 2 * er + i, bi = it >> 2, e = it & 3;
+      const int row = wm * 128 + bi * 16 + 4 * eq + e;
+      s_wm[wn][row] = im[i];
+      s_ws[wn][row] = is[i];
     }
     __syncthreads();
-    if (t < kLmhBM) {
-      const int64_t r = combined_row(t);
-      if (r >= 0) {
+    if (t < kLmhBM) {  // a thread per tile row (the tables are next written after the next tile's barriers)
+      const int64_t r = m0 + t;
+      if (r < g.M) {
         float m = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) m = fmaxnan(m, s_wm[w][t]);
-        double s = 0.0;
+        for (int w = 0; w < kWN; ++w) m = fmaxnan(m, s_wm[w][t]);
+        double sum = 0.0;
         if (!is_neg_inf(m)) {
 #pragma unroll
-          for (int w = 0; w < kWaves; ++w) {
+          for (int w = 0; w < kWN; ++w) {
             const float mw = s_wm[w][t];
-            if (!is_neg_inf(mw)) s += (double)s_ws[w][t] * ::exp2(((double)mw - (double)m) * (double)c32);
+            if (!is_neg_inf(mw)) sum += (double)s_ws[w][t] * ::exp2(((double)mw - (double)m) * (double)c32);
           }
         }
-        if (isnan(m) || isinf(m)) s = NAN;
-        g.st[r * (int64_t)g.ntn + tn] = StatRec{m, 0u, s};
+        if (isnan(m) || isinf(m)) sum = NAN;
+        g.st[r * (int64_t)g.ntn + tn] = StatRec{m, 0u, sum};
       }
     }
   }
@@ -417,8 +503,8 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
     st.phase = kTreeDone;
   } else {
     st.phase = kTreeFinal;
-    st.row = 0;  // the final rows are row b of the target and draft final-row buffers
-    st.urow1 = n + 1;  // the final draw's uniform is that of position n
+    st.row = n;  // target row n and draft row n of the request, in the kept logits
+    st.urow1 = 0;  // the final draw's uniform is that of position n
     st.len = n;
     st.mp = s_m[n];
     st.sp_hat = s_S[n];
@@ -430,30 +516,36 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
     st.c_old = 0.0;
   }
   tc.ts[b] = st;
-  // final rows: target row n, then draft row n (the target row again for a bonus)
-  g.fin[b] = (int32_t)(b * (K + 1) + n);
-  g.fin[g.B + b] = (int32_t)(n < K ? g.Mp + b * K + n : b * (K + 1) + n);
 }
 
 namespace {
-// Workgroups of a product: the tile count rounded up to a multiple of the XCD
-// count, so that the XCD-major tile order covers every tile once.
-inline unsigned lmh_grid(const LmhCfg& g) {
-  const int64_t G = (int64_t)g.ntm * g.ntn;
-  return (unsigned)((G + kXcds - 1) / kXcds * kXcds);
+// Workgroups of the persistent product: one per compute unit, a multiple of
+// the XCD count (the device's compute units, read once per device).
+hipError_t lmh_grid(unsigned* grid) {
+  static int cus[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cus[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cus[dev] = n / kXcds * kXcds > 0 ? n / kXcds * kXcds : kXcds;
+  }
+  *grid = (unsigned)cus[dev];
+  return hipSuccess;
 }
 }  // namespace
 
 hipError_t launch_lmh_stats(const LmhCfg& g, hipStream_t s) {
-  PSI_LAUNCH(s, k_lmh_gemm<kLmhStats>, dim3(lmh_grid(g)), dim3(kWG), g);
+  unsigned grid = 0;
+  if (hipError_t e = lmh_grid(&grid)) return e;
+  PSI_LAUNCH(s, k_lmh_gemm, dim3(grid), dim3(kWG), g);
   return hipGetLastError();
 }
 hipError_t launch_lmh_decide(const LmhCfg& g, const LinCfg& c, const TreeCfg& tc, hipStream_t s) {
   PSI_LAUNCH(s, k_lmh_decide, dim3((unsigned)g.B), dim3(kDecideWG), g, c, tc);
-  return hipGetLastError();
-}
-hipError_t launch_lmh_logits(const LmhCfg& g, hipStream_t s) {
-  PSI_LAUNCH(s, k_lmh_gemm<kLmhLogits>, dim3(lmh_grid(g)), dim3(kWG), g);
   return hipGetLastError();
 }
 

@@ -260,7 +260,8 @@ def test_lmhead_argument_errors(psi):
     assert call(ht=None) == psi.EINVAL
     assert call(B=0) == psi.EINVAL
     assert call(H=0) == psi.EINVAL
-    assert call(H=96) == psi.EUNSUPPORTED          # not a multiple of 64
+    assert call(H=96) == psi.EUNSUPPORTED          # not a multiple of 128
+    assert call(H=192) == psi.EUNSUPPORTED
     assert call(K=65) == psi.EUNSUPPORTED
     assert call(prm_=psi.make_params(temperature=0.0)) == psi.EUNSUPPORTED
     assert call(prm_=psi.make_params(top_k=10)) == psi.EUNSUPPORTED

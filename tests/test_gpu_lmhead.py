@@ -105,8 +105,11 @@ def check(B, K, H, V, T, seed, steps=3) -> Tally:
 
 
 @pytest.mark.parametrize("B,K,H,V,T,seed", [
-    (3, 4, 128, 3000, 1.0, 0), (5, 8, 256, 4096, 0.7, 1), (2, 1, 64, 700, 1.0, 2), (7, 3, 192, 257, 1.3, 3),
-    (20, 8, 512, 32768, 1.0, 4)])
+    (3, 4, 128, 3000, 1.0, 0), (5, 8, 256, 4096, 0.7, 1), (2, 1, 128, 700, 1.0, 2), (7, 3, 384, 257, 1.3, 3),
+    (20, 8, 512, 32768, 1.0, 4),
+    # 680 rows (the last row tile partial, down to part of a 16-row block),
+    # 588 tiles: workgroups walk two or three tiles each
+    (40, 8, 256, 50000, 1.0, 7)])
 def test_lmhead_parity(B, K, H, V, T, seed):
     check(B, K, H, V, f32(T), seed).check()
 
@@ -118,7 +121,8 @@ def test_lmhead_qwen_shape():
 
 def test_lmhead_rejects_bad_shapes():
     psi = _psi()
-    ht, hd, w = inputs(2, 2, 96, 100, 6)  # H not a multiple of 64
     x = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
-    with pytest.raises(psi.PsiSpecError):
-        psi.verify_lmhead(_dev(ht), _dev(hd), _dev(w), x)
+    for H in (96, 192):  # not multiples of 128
+        ht, hd, w = inputs(2, 2, H, 100, 6)
+        with pytest.raises(psi.PsiSpecError):
+            psi.verify_lmhead(_dev(ht), _dev(hd), _dev(w), x)
