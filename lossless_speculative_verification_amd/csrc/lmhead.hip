@@ -209,10 +209,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
   const int r16 = lane & 15, q4 = lane >> 4;
   const int fo = r16 * kRowB + ((q4 ^ lmh_swz(r16)) * 16);
   const int ba = wm * 128 * kRowB + fo, bw = kAStage + wn * 128 * kRowB + fo;
-  // fragments: A single-buffered (rows 4..7 of a step are read during its
-  // first half, rows 0..3 of the next step during its second half), W by
-  // step parity
-  bf16x8_t fa[8], fb[2][8];
+  bf16x8_t fa[2][8], fb[2][8];  // by step parity
 
   // prologue: the first kStages - 1 steps in flight, wait for the first
   set_src(lpos);
@@ -243,7 +240,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     {
       const unsigned char* st = ring(cur);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(st + ba + i * 16 * kRowB);
+      for (int i = 0; i < 8; ++i) fa[0][i] = *(const bf16x8_t*)(st + ba + i * 16 * kRowB);
 #pragma unroll
       for (int i = 0; i < 8; ++i) fb[0][i] = *(const bf16x8_t*)(st + bw + i * 16 * kRowB);
     }
@@ -254,18 +251,15 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
       constexpr bool kRefill = decltype(refill_tag)::value;
       constexpr int P = decltype(par_tag)::value;
       constexpr int kLeft = decltype(left_tag)::value;
-      const unsigned char* st = ring(cur);
       const int nxt = cur == kStages - 1 ? 0 : cur + 1;
       unsigned char* fill = ring(cur == 0 ? kStages - 1 : cur - 1);
-      // first half: row blocks 0..3, a load after each group of 8 products;
-      // the A fragments of row blocks 4..7 are read meanwhile
+      // first half: row blocks 0..3, a load after each group of 8 products
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
-        fa[4 + bi] = *(const bf16x8_t*)(st + ba + (4 + bi) * 16 * kRowB);
         if (bi < mb) {
 #pragma unroll
           for (int bj = 0; bj < 8; ++bj)
-            acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi], fb[P][bj], acc[bi][bj], 0, 0, 0);
+            acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[P][bi], fb[P][bj], acc[bi][bj], 0, 0, 0);
         }
         if (kRefill) issue(fill, bi);
       }
@@ -276,20 +270,20 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
       else wait_vm<kLeft * kLoads>();
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of this slot are done
       lmh_barrier();
-      // second half: row blocks 4..7; the next step's A fragments of row
-      // blocks 0..3 and its W fragments (buffer 1 - P) are read meanwhile
-      // (after a tile's last step they are read and not used)
+      // second half: row blocks 4..7, the next step's fragments read into
+      // buffer 1 - P (after a tile's last step they are read and not used)
       const unsigned char* sn = ring(nxt);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        fa[gq] = *(const bf16x8_t*)(sn + ba + gq * 16 * kRowB);
+        fa[1 - P][2 * gq] = *(const bf16x8_t*)(sn + ba + (2 * gq) * 16 * kRowB);
+        fa[1 - P][2 * gq + 1] = *(const bf16x8_t*)(sn + ba + (2 * gq + 1) * 16 * kRowB);
         fb[1 - P][2 * gq] = *(const bf16x8_t*)(sn + bw + (2 * gq) * 16 * kRowB);
         fb[1 - P][2 * gq + 1] = *(const bf16x8_t*)(sn + bw + (2 * gq + 1) * 16 * kRowB);
         const int bi = 4 + gq;
         if (bi < mb) {
 #pragma unroll
           for (int bj = 0; bj < 8; ++bj)
-            acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[bi], fb[P][bj], acc[bi][bj], 0, 0, 0);
+            acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[P][bi], fb[P][bj], acc[bi][bj], 0, 0, 0);
         }
         if (kRefill) issue(fill, kHalfLoads + gq);
       }
@@ -418,15 +412,17 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
 }
 
 // Per request (one workgroup): the row normalisers of the K + 1 target and K
-// draft rows from the tile records (a wave per row), the logits of the drafted
-// tokens as dot products of the hidden states with the tokens' rows of W (fp32
-// products, summed per lane in order and across lanes in fp64), the accept
-// tests, the first rejection n, the accepted tokens, and the state of the
-// final draw.
-constexpr int kDecideWG = 1024;  // 16 waves: about one row of the request per wave
+// draft rows from the tile records (a half-wave per row: 2K + 1 <= 32 rows
+// for K <= 15, else a second pass), the logits of the drafted tokens as dot
+// products of the hidden states with the tokens' rows of W (fp32 products,
+// summed per lane in order and across lanes in fp64), the accept tests (a lane
+// per position, the first rejection n by a ballot), the accepted tokens, and
+// the state of the final draw.
+constexpr int kDecideWG = 1024;
 __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, TreeCfg tc) {
   const int64_t b = blockIdx.x;
-  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  const int hl = t & 31, hw = t >> 5;  // lane in the half-wave, half-wave
   const int K = g.K;
   __shared__ float s_m[2 * kMaxK + 1];
   __shared__ double s_S[2 * kMaxK + 1];
@@ -434,46 +430,91 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
   __shared__ int s_bad;
   if (t == 0) s_bad = 0;
   __syncthreads();
-  for (int j = wave; j < 2 * K + 1; j += kDecideWG / kWave) {
+  // half-wave sums and maxima (xor distances below 32 stay in the half-wave)
+  auto hsum = [](double v) {
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+  };
+  auto hmax = [](float v) {
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) v = fmaxnan(v, __shfl_xor(v, o));
+    return v;
+  };
+  for (int j = hw; j < 2 * K + 1; j += kDecideWG / 32) {
     const int64_t r = j <= K ? b * (K + 1) + j : g.Mp + b * K + (j - K - 1);
+    const StatRec* rec = g.st + r * (int64_t)g.ntn;
+    // loads are issued in batches of kDecB before their values are used, so
+    // that a row costs a few memory latencies rather than one per iteration
+    constexpr int kDecB = 8;
+    float m = -INFINITY;
+    int bad = 0;
+    for (int i0 = hl; i0 < g.ntn; i0 += 32 * kDecB) {
+      float mm[kDecB];
+      double ss[kDecB];
+#pragma unroll
+      for (int u = 0; u < kDecB; ++u) {
+        const int i = i0 + 32 * u;
+        mm[u] = i < g.ntn ? rec[i].m : -INFINITY;
+        ss[u] = i < g.ntn ? rec[i].s : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kDecB; ++u) {
+        m = fmaxnan(m, mm[u]);
+        bad |= isnan(ss[u]) ? 1 : 0;
+      }
+    }
+    float z = NAN;
     if (j != K) {  // row K is the bonus row: no drafted token
       const int x = g.draft[b * K + (j < K ? j : j - K - 1)];
-      float z = NAN;
       if (x >= 0 && x < g.V) {
         const uint4* hv = (const uint4*)lmh_arow(g, r);
         const uint4* wv = (const uint4*)(g.w + (int64_t)x * g.H);
         float a = 0.0f;
-        for (int v = lane; v < g.H / 8; v += kWave) {
-          float h8[8], w8[8];
-          Elem<kBF16>::unpack(hv[v], h8);
-          Elem<kBF16>::unpack(wv[v], w8);
+        const int nv = g.H / 8;
+        for (int v0 = hl; v0 < nv; v0 += 32 * kDecB) {
+          uint4 hh[kDecB], ww[kDecB];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a = __builtin_fmaf(h8[e], w8[e], a);
+          for (int u = 0; u < kDecB; ++u) {
+            const int v = v0 + 32 * u;
+            hh[u] = v < nv ? hv[v] : make_uint4(0, 0, 0, 0);
+            ww[u] = v < nv ? wv[v] : make_uint4(0, 0, 0, 0);
+          }
+#pragma unroll
+          for (int u = 0; u < kDecB; ++u) {
+            if (v0 + 32 * u >= nv) break;
+            float h8[8], w8[8];
+            Elem<kBF16>::unpack(hh[u], h8);
+            Elem<kBF16>::unpack(ww[u], w8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = __builtin_fmaf(h8[e], w8[e], a);
+          }
         }
-        z = (float)wave_sum((double)a);
+        z = (float)hsum((double)a);
       }
-      if (lane == 0) s_z[j] = z;
     }
-    const StatRec* rec = g.st + r * (int64_t)g.ntn;
-    float m = -INFINITY;
-    int bad = 0;
-    for (int i = lane; i < g.ntn; i += kWave) {
-      const StatRec x = rec[i];
-      m = fmaxnan(m, x.m);
-      bad |= isnan(x.s) ? 1 : 0;
-    }
-    m = wave_max(m);
+    m = hmax(m);
     double S = 0.0;
     if (!isnan(m) && !isinf(m))
-      for (int i = lane; i < g.ntn; i += kWave) {
-        const StatRec x = rec[i];
-        if (!is_neg_inf(x.m)) S += x.s * ::exp2(((double)x.m - (double)m) * (double)g.c32);
+      for (int i0 = hl; i0 < g.ntn; i0 += 32 * kDecB) {
+        float mm[kDecB];
+        double ss[kDecB];
+#pragma unroll
+        for (int u = 0; u < kDecB; ++u) {
+          const int i = i0 + 32 * u;
+          mm[u] = i < g.ntn ? rec[i].m : -INFINITY;
+          ss[u] = i < g.ntn ? rec[i].s : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kDecB; ++u)
+          if (!is_neg_inf(mm[u])) S += ss[u] * ::exp2(((double)mm[u] - (double)m) * (double)g.c32);
       }
-    S = wave_sum(S);
-    bad = wave_or(bad);
-    if (lane == 0) {
+    S = hsum(S);
+    bad = (int)hsum((double)bad);
+    if (hl == 0) {
       s_m[j] = m;
       s_S[j] = S;
+      s_z[j] = z;
       if (bad || isnan(m) || isinf(m) || !(S > 0.0)) atomicOr(&s_bad, 1);
     }
   }
@@ -482,23 +523,34 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
     if (x < 0 || x >= g.V) atomicOr(&s_bad, 1);
   }
   __syncthreads();
-  if (t != 0) return;
+  if (t >= kWave) return;
+  // accept tests u Q(x) < P(x), a lane per position (positions K .. are
+  // never rejected); n = the first rejection
+  const int nbad = s_bad;
   int n = K;
-  if (!s_bad) {
-    for (int i = 0; i < K; ++i) {
-      const double P = ::exp(((double)s_z[i] - (double)s_m[i]) * c.invT - ::log(s_S[i]));
-      const double Q = ::exp(((double)s_z[K + 1 + i] - (double)s_m[K + 1 + i]) * c.invT -
-                             ::log(s_S[K + 1 + i]));
-      const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawAccept);
-      if (!(u * Q < P)) {
-        n = i;
+  if (!nbad) {
+    for (int i0 = 0; i0 < K; i0 += kWave) {
+      const int i = i0 + lane;
+      bool rej = false;
+      if (i < K) {
+        const double P = ::exp(((double)s_z[i] - (double)s_m[i]) * c.invT - ::log(s_S[i]));
+        const double Q = ::exp(((double)s_z[K + 1 + i] - (double)s_m[K + 1 + i]) * c.invT -
+                               ::log(s_S[K + 1 + i]));
+        const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawAccept);
+        rej = !(u * Q < P);
+      }
+      const unsigned long long mask = __ballot(rej);
+      if (mask) {
+        n = i0 + __builtin_ctzll(mask);
         break;
       }
     }
   }
-  for (int i = 0; i <= K; ++i) c.out_tokens[b * (K + 1) + i] = (!s_bad && i < n) ? g.draft[b * K + i] : -1;
+  for (int i = lane; i <= K; i += kWave)
+    c.out_tokens[b * (K + 1) + i] = (!nbad && i < n) ? g.draft[b * K + i] : -1;
+  if (lane != 0) return;
   TreeState st = {};
-  if (s_bad) {
+  if (nbad) {
     c.out_len[b] = -1;
     st.phase = kTreeDone;
   } else {
