@@ -50,24 +50,6 @@ __device__ __forceinline__ double rd_lane(double v, int l) {
   return __hiloint2double(hi, lo);
 }
 
-// Row normaliser of one row from its statistics records: exact maximum m and
-// S ~ sum_t 2^((a_t - m) c). Returns false for an invalid row.
-__device__ __forceinline__ bool row_norm(const StatRec* rec, int nch, float c32, float* m_out, double* S_out) {
-  float m = -INFINITY;
-  for (int ch = 0; ch < nch; ++ch) m = fmaxnan(m, rec[ch].m);
-  double S = 0.0;
-  bool bad = isnan(m) || isinf(m);
-  if (!bad)
-    for (int ch = 0; ch < nch; ++ch) {
-      const StatRec r = rec[ch];
-      if (isnan(r.s)) bad = true;
-      else if (!is_neg_inf(r.m)) S += r.s * ::exp2(((double)r.m - (double)m) * (double)c32);
-    }
-  if (!(S > 0.0)) bad = true;
-  *m_out = m;
-  *S_out = S;
-  return !bad;
-}
 
 }  // namespace
 

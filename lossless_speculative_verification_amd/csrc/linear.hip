@@ -325,18 +325,10 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   }
   const int r = t - 2 * kWave;
   if (r >= 0 && r < R) {
-    const StatRec* rec = c.st + (b * R + r) * (int64_t)c.nch32;
-    float m = -INFINITY;
-    for (int ch = 0; ch < c.nch32; ++ch) m = fmaxnan(m, rec[ch].m);
-    double S = 0.0;
-    int bad = isnan(m) || isinf(m);  // NaN, +inf, or an all -inf row
-    if (!bad)
-      for (int ch = 0; ch < c.nch32; ++ch) {
-        const StatRec rc = rec[ch];
-        if (isnan(rc.s)) bad = 1;
-        else if (!is_neg_inf(rc.m)) S += rc.s * ::exp2(((double)rc.m - (double)m) * (double)c.c32);
-      }
-    if (!(S > 0.0)) bad = 1;
+    float m;
+    double S;
+    // NaN, +inf, or an all -inf row
+    const int bad = row_norm(c.st + (b * R + r) * (int64_t)c.nch32, c.nch32, c.c32, &m, &S) ? 0 : 1;
     s_m[r] = m;
     s_S[r] = S;
     if (bad) atomicOr(&s_bad, 1);

@@ -504,4 +504,46 @@ __device__ inline int draw_list(int cnt, double u, W w, const FiltEnt* e) {
   return last >= 0 ? e[last].i : -1;
 }
 
+// Row normaliser of one row from its statistics records, by one thread: the
+// exact maximum m and S = sum over the chunks, in chunk order, of
+// s 2^((m_chunk - m) c) in fp64. Returns false for an invalid row (a NaN or
+// +inf, or nothing finite). The records are loaded in batches before their
+// values are used, so that a row costs a few memory latencies rather than one
+// per chunk; the order of the sum is still the chunks' (results are the same
+// bit for bit as a plain loop's).
+__device__ __forceinline__ bool row_norm(const StatRec* rec, int nch, float c32, float* m_out, double* S_out) {
+  constexpr int kB = 8;
+  float m = -INFINITY;
+  for (int c0 = 0; c0 < nch; c0 += kB) {
+    float mm[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) mm[u] = c0 + u < nch ? rec[c0 + u].m : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) m = fmaxnan(m, mm[u]);
+  }
+  double S = 0.0;
+  bool bad = isnan(m) || isinf(m);
+  if (!bad)
+    for (int c0 = 0; c0 < nch; c0 += kB) {
+      float mm[kB];
+      double ss[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const bool in = c0 + u < nch;
+        mm[u] = in ? rec[c0 + u].m : -INFINITY;
+        ss[u] = in ? rec[c0 + u].s : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (c0 + u >= nch) break;
+        if (isnan(ss[u])) bad = true;
+        else if (!is_neg_inf(mm[u])) S += ss[u] * ::exp2(((double)mm[u] - (double)m) * (double)c32);
+      }
+    }
+  if (!(S > 0.0)) bad = true;
+  *m_out = m;
+  *S_out = S;
+  return !bad;
+}
+
 }  // namespace psi

@@ -213,18 +213,9 @@ __global__ __launch_bounds__(kWG) void k_tree_wp(LinCfg c, TreeTopo tp, TreeCfg 
     for (int i = t; i < R2; i += kWG) {
       // same reduction as the linear decide step, so that a chain-shaped tree
       // reproduces the linear result bit for bit
-      const StatRec* rec = c.st + (b * R2 + i) * (int64_t)c.nch32;
-      float m = -INFINITY;
-      for (int ch = 0; ch < c.nch32; ++ch) m = fmaxnan(m, rec[ch].m);
-      double S = 0.0;
-      int bad = isnan(m) || isinf(m);
-      if (!bad)
-        for (int ch = 0; ch < c.nch32; ++ch) {
-          const StatRec r = rec[ch];
-          if (isnan(r.s)) bad = 1;
-          else if (!is_neg_inf(r.m)) S += r.s * ::exp2(((double)r.m - (double)m) * (double)c.c32);
-        }
-      if (!(S > 0.0)) bad = 1;
+      float m;
+      double S;
+      const int bad = row_norm(c.st + (b * R2 + i) * (int64_t)c.nch32, c.nch32, c.c32, &m, &S) ? 0 : 1;
       RowStat o;
       o.m = m;
       o.bad = bad;
