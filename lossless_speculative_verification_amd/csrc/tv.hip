@@ -83,7 +83,11 @@ __device__ __forceinline__ void tv_probs(const TvRow& t, float c32, float a, flo
 }
 
 
-constexpr int kTvSpw = 4;  // sub-blocks per wave (the row normalisers are read once per wave)
+// sub-blocks per wave (the row normalisers are read once per wave): the
+// first pass holds two rows' vectors per sub-block, the second one row's and
+// keeps the next sub-block's loads in flight
+constexpr int kTvSpwPass = 4;
+constexpr int kTvSpwGrad = 8;
 
 }  // namespace
 
@@ -98,13 +102,13 @@ __global__ __launch_bounds__(kWG) void k_tv_pass(LinCfg c, uint16_t* sgn) {
   constexpr int VPL = kSB / (kWave * EPV);
   const int64_t r = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int sb0 = (blockIdx.x * kWaves + wave) * kTvSpw;
+  const int sb0 = (blockIdx.x * kWaves + wave) * kTvSpwPass;
   if (sb0 >= c.nsb) return;
   const int64_t nv = ((int64_t)c.V + EPV - 1) / EPV;  // sign words per row
   const TvRow t = tv_row(c, r);
   const char* prow = c.rows.p + (r * (int64_t)c.V) * c.rows.esz;
   const char* qrow = c.rows.q + (r * (int64_t)c.V) * c.rows.esz;
-  for (int sb = sb0; sb < sb0 + kTvSpw && sb < c.nsb; ++sb) {
+  for (int sb = sb0; sb < sb0 + kTvSpwPass && sb < c.nsb; ++sb) {
     const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
     float xa[VPL][EPV], xd[VPL][EPV];
     load_vecs<DT, AL, VPL, kWave>(prow, c.V, c.nvec, vfirst, xa);
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const uint16_t* sgn, 
   constexpr int VPL = kSB / (kWave * EPV);
   const int64_t r = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int sb0 = (blockIdx.x * kWaves + wave) * kTvSpw;
+  const int sb0 = (blockIdx.x * kWaves + wave) * kTvSpwGrad;
   if (sb0 >= c.nsb) return;
   const int64_t nv = ((int64_t)c.V + EPV - 1) / EPV;
   const TvRow t = tv_row(c, r);
@@ -196,16 +200,33 @@ __global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const uint16_t* sgn, 
   const float gbar = (float)GQ;
   const float scale = t.ok ? (float)((w_row ? (double)w_row[r] : 1.0) / T) : NAN;
   const char* qrow = c.rows.q + (r * (int64_t)c.V) * c.rows.esz;
-  for (int sb = sb0; sb < sb0 + kTvSpw && sb < c.nsb; ++sb) {
-    const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
-    float xd[VPL][EPV];
-    uint32_t codes[VPL];
+  // the loads of sub-block sb + 1 are issued before sub-block sb is written
+  const int sbe = min(sb0 + kTvSpwGrad, c.nsb);
+  auto load_codes = [&](int64_t vfirst, uint32_t (&codes)[VPL]) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int64_t vec = vfirst + (int64_t)v * kWave;
       codes[v] = vec < nv ? (uint32_t)sgn[r * nv + vec] : 0u;
     }
-    load_vecs<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, vfirst, xd);
+  };
+  float yd[VPL][EPV];
+  uint32_t ycodes[VPL];
+  load_codes((int64_t)sb0 * (kSB / EPV) + lane, ycodes);
+  load_vecs<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, (int64_t)sb0 * (kSB / EPV) + lane, yd);
+  for (int sb = sb0; sb < sbe; ++sb) {
+    const int64_t vfirst = (int64_t)sb * (kSB / EPV) + lane;
+    float xd[VPL][EPV];
+    uint32_t codes[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      codes[v] = ycodes[v];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) xd[v][e] = yd[v][e];
+    }
+    if (sb + 1 < sbe) {
+      load_codes(vfirst + kSB / EPV, ycodes);
+      load_vecs<DT, AL, VPL, kWave>(qrow, c.V, c.nvec, vfirst + kSB / EPV, yd);
+    }
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       float gout[EPV];
@@ -231,11 +252,12 @@ __global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const uint16_t* sgn, 
 template <int DT, bool AL>
 static hipError_t tv_t(const LinCfg& c, uint16_t* sgn, const float* w_row, double* loss, void* grad, double T,
                        hipStream_t s) {
-  const unsigned gx = (unsigned)((c.nsb + kWaves * kTvSpw - 1) / (kWaves * kTvSpw));
+  const unsigned gxp = (unsigned)((c.nsb + kWaves * kTvSpwPass - 1) / (kWaves * kTvSpwPass));
+  const unsigned gxg = (unsigned)((c.nsb + kWaves * kTvSpwGrad - 1) / (kWaves * kTvSpwGrad));
   hipError_t e = launch_stats32(c, 2 * c.B, DT, s);
   if (e != hipSuccess) return e;
-  PSI_LAUNCH(s, (k_tv_pass<DT, AL>), dim3(gx, (unsigned)c.B), dim3(kWG), c, grad ? sgn : nullptr);
-  PSI_LAUNCH(s, (k_tv_grad<DT, AL>), dim3(grad ? gx : 1u, (unsigned)c.B), dim3(kWG), c, (const uint16_t*)sgn, w_row,
+  PSI_LAUNCH(s, (k_tv_pass<DT, AL>), dim3(gxp, (unsigned)c.B), dim3(kWG), c, grad ? sgn : nullptr);
+  PSI_LAUNCH(s, (k_tv_grad<DT, AL>), dim3(grad ? gxg : 1u, (unsigned)c.B), dim3(kWG), c, (const uint16_t*)sgn, w_row,
              loss, grad, T);
   return hipGetLastError();
 }
