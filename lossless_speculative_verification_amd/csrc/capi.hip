@@ -467,9 +467,12 @@ int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64
   LinCfg c;
   fill_common(c, p_logits, q_logits, dtype, R, 1, V, &prm, workspace, 1);
   c.aligned = c.aligned && (out_grad == nullptr || aligned16(out_grad));
-  uint16_t* sgn = (uint16_t*)((char*)workspace + layout(R, 2, V, dtype).total);
+  const Layout L = layout(R, 2, V, dtype);
+  uint16_t* sgn = (uint16_t*)((char*)workspace + L.total);
+  RowStat* rn = (RowStat*)((char*)workspace + L.rst);  // [R, 2] teacher and student row normalisers
   timing_begin(stream);
-  const hipError_t e = launch_tv_loss(c, sgn, row_weights, out_loss, out_grad, (double)temperature, dtype, stream);
+  const hipError_t e =
+      launch_tv_loss(c, rn, sgn, row_weights, out_loss, out_grad, (double)temperature, dtype, stream);
   return e == hipSuccess ? PSISPEC_OK : PSISPEC_EHIP;
 }
 

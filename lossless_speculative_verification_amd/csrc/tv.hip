@@ -11,6 +11,8 @@
 // Pipeline on the caller's stream (streaming the rows in chunks that fit the
 // last-level cache between the passes measured slower than whole passes):
 //   k_stats32   maxima and binary32-grade sums of every teacher and student row;
+//   k_tv_rows   a wave per teacher or student row: its maximum and normaliser
+//               from the chunk records, once;
 //   k_tv_pass   (sub-block, row): sum |p - q| and sum g q per 1,024 logits,
 //               and (with a gradient) the sign of q - p of every logit, two
 //               bits each, 16 bits per 16-byte vector;
@@ -62,12 +64,13 @@ struct TvRow {
   bool ok;
 };
 
-__device__ __forceinline__ TvRow tv_row(const LinCfg& c, int64_t r) {
+__device__ __forceinline__ TvRow tv_row(const LinCfg& c, const RowStat* rn, int64_t r) {
   TvRow t;
-  double Sp, Sq;
-  const bool okp = wave_row_norm(c.st + (2 * r) * (int64_t)c.nch32, c.nch32, c.c32, &t.mp, &Sp);
-  const bool okq = wave_row_norm(c.st + (2 * r + 1) * (int64_t)c.nch32, c.nch32, c.c32, &t.mq, &Sq);
-  t.ok = okp && okq;
+  const RowStat a = rn[2 * r], d = rn[2 * r + 1];
+  t.mp = a.m;
+  t.mq = d.m;
+  const double Sp = a.s, Sq = d.s;
+  t.ok = !a.bad && !d.bad;
   t.mcp = t.mp * c.c32;
   t.mcq = t.mq * c.c32;
   t.ip = (float)(1.0 / Sp);
@@ -91,13 +94,24 @@ constexpr int kTvSpwGrad = 8;
 
 }  // namespace
 
+// Maximum and normaliser of every teacher and student row (rn[2 r], rn[2 r + 1]),
+// a wave per row.
+__global__ __launch_bounds__(kWG) void k_tv_rows(LinCfg c, RowStat* rn, int64_t rows) {
+  const int64_t sr = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (sr >= rows) return;
+  float m;
+  double S;
+  const bool ok = wave_row_norm(c.st + sr * (int64_t)c.nch32, c.nch32, c.c32, &m, &S);
+  if ((threadIdx.x & (kWave - 1)) == 0) rn[sr] = RowStat{m, ok ? 0 : 1, S};
+}
+
 // c.rows: np = 1 teacher row and nq = 1 student row per "request" (= row of
 // the loss); row blockIdx.y.
 // Sign code of q - p: 0 tie, 1 positive (g = +1/2), 2 negative (g = -1/2).
 __device__ __forceinline__ float tv_code_g(uint32_t code) { return code == 1u ? 0.5f : (code == 2u ? -0.5f : 0.0f); }
 
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_tv_pass(LinCfg c, uint16_t* sgn) {
+__global__ __launch_bounds__(kWG) void k_tv_pass(LinCfg c, const RowStat* rn, uint16_t* sgn) {
   constexpr int EPV = Elem<DT>::kPerVec;
   constexpr int VPL = kSB / (kWave * EPV);
   const int64_t r = blockIdx.y;
@@ -105,7 +119,7 @@ __global__ __launch_bounds__(kWG) void k_tv_pass(LinCfg c, uint16_t* sgn) {
   const int sb0 = (blockIdx.x * kWaves + wave) * kTvSpwPass;
   if (sb0 >= c.nsb) return;
   const int64_t nv = ((int64_t)c.V + EPV - 1) / EPV;  // sign words per row
-  const TvRow t = tv_row(c, r);
+  const TvRow t = tv_row(c, rn, r);
   const char* prow = c.rows.p + (r * (int64_t)c.V) * c.rows.esz;
   const char* qrow = c.rows.q + (r * (int64_t)c.V) * c.rows.esz;
   for (int sb = sb0; sb < sb0 + kTvSpwPass && sb < c.nsb; ++sb) {
@@ -177,8 +191,8 @@ __device__ __forceinline__ uint4 pack_grad<kBF16>(const float (&x)[8]) {
 // sign codes of the first pass. With grad == nullptr only the loss is written
 // (grid x = 1).
 template <int DT, bool AL>
-__global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const uint16_t* sgn, const float* w_row, double* loss,
-                                                 void* grad, double T) {
+__global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const RowStat* rn, const uint16_t* sgn, const float* w_row,
+                                                 double* loss, void* grad, double T) {
   constexpr int EPV = Elem<DT>::kPerVec;
   constexpr int VPL = kSB / (kWave * EPV);
   const int64_t r = blockIdx.y;
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const uint16_t* sgn, 
   const int sb0 = (blockIdx.x * kWaves + wave) * kTvSpwGrad;
   if (sb0 >= c.nsb) return;
   const int64_t nv = ((int64_t)c.V + EPV - 1) / EPV;
-  const TvRow t = tv_row(c, r);
+  const TvRow t = tv_row(c, rn, r);
   double L1 = 0.0, GQ = 0.0;
   for (int i = lane; i < c.nsb; i += kWave) {
     const ResRec x = c.res[r * c.nsb + i];
@@ -250,21 +264,23 @@ __global__ __launch_bounds__(kWG) void k_tv_grad(LinCfg c, const uint16_t* sgn, 
 }
 
 template <int DT, bool AL>
-static hipError_t tv_t(const LinCfg& c, uint16_t* sgn, const float* w_row, double* loss, void* grad, double T,
-                       hipStream_t s) {
+static hipError_t tv_t(const LinCfg& c, RowStat* rn, uint16_t* sgn, const float* w_row, double* loss, void* grad,
+                       double T, hipStream_t s) {
   const unsigned gxp = (unsigned)((c.nsb + kWaves * kTvSpwPass - 1) / (kWaves * kTvSpwPass));
   const unsigned gxg = (unsigned)((c.nsb + kWaves * kTvSpwGrad - 1) / (kWaves * kTvSpwGrad));
   hipError_t e = launch_stats32(c, 2 * c.B, DT, s);
   if (e != hipSuccess) return e;
-  PSI_LAUNCH(s, (k_tv_pass<DT, AL>), dim3(gxp, (unsigned)c.B), dim3(kWG), c, grad ? sgn : nullptr);
-  PSI_LAUNCH(s, (k_tv_grad<DT, AL>), dim3(grad ? gxg : 1u, (unsigned)c.B), dim3(kWG), c, (const uint16_t*)sgn, w_row,
+  PSI_LAUNCH(s, k_tv_rows, dim3((unsigned)((2 * c.B + kWaves - 1) / kWaves)), dim3(kWG), c, rn, 2 * c.B);
+  PSI_LAUNCH(s, (k_tv_pass<DT, AL>), dim3(gxp, (unsigned)c.B), dim3(kWG), c, (const RowStat*)rn, grad ? sgn : nullptr);
+  PSI_LAUNCH(s, (k_tv_grad<DT, AL>), dim3(grad ? gxg : 1u, (unsigned)c.B), dim3(kWG), c, (const RowStat*)rn,
+             (const uint16_t*)sgn, w_row,
              loss, grad, T);
   return hipGetLastError();
 }
 
-hipError_t launch_tv_loss(const LinCfg& c, uint16_t* sgn, const float* w_row, double* loss, void* grad, double T,
-                          int dtype, hipStream_t s) {
-  return PSI_DISPATCH(tv_t, dtype, c.aligned, c, sgn, w_row, loss, grad, T, s);
+hipError_t launch_tv_loss(const LinCfg& c, RowStat* rn, uint16_t* sgn, const float* w_row, double* loss, void* grad,
+                          double T, int dtype, hipStream_t s) {
+  return PSI_DISPATCH(tv_t, dtype, c.aligned, c, rn, sgn, w_row, loss, grad, T, s);
 }
 
 }  // namespace psi
