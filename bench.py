@@ -370,26 +370,33 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed, only=None):
         # [1088, 4096] times a contiguous copy of W^T [4096, 151936]
         hall = torch.cat([ht.reshape(-1, Hl), hd.reshape(-1, Hl)]).contiguous()
         wt = wv.t().contiguous()
-        # The two are timed call by call, alternating, so that both see the
-        # same clock and power state (both slow by up to a third within a run
-        # as the chip reaches its power limit).
+        # The two are timed call by call, back to back and alternating which
+        # goes first, so that both see the same clock and power state (both
+        # slow by up to a third within a run as the chip reaches its power
+        # limit, and a call right after an idle gap runs a few percent slow).
         call = lambda i: psi.verify_lmhead(ht, hd, wv, xl, temperature=1.0, seed=seed, step=i, out=outs,
                                            workspace=wsl, stream=stream)
         for i in range(3):
             call(i)
             torch.mm(hall, wt)
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        n_pairs = max(steps // 5, 6)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_pairs)]
+        for i in range(n_pairs):
+            first, second = (lambda: call(3 + i), lambda: torch.mm(hall, wt))
+            if i & 1:
+                first, second = second, first
+            ev[i][0].record(stream)
+            first()
+            ev[i][1].record(stream)
+            second()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
         ours, lib = [], []
-        for i in range(max(steps // 5, 5)):
-            ev[0].record(stream)
-            call(3 + i)
-            ev[1].record(stream)
-            torch.mm(hall, wt)
-            ev[2].record(stream)
-            torch.cuda.synchronize()
-            ours.append(ev[0].elapsed_time(ev[1]))
-            lib.append(ev[1].elapsed_time(ev[2]))
+        for i in range(n_pairs):
+            a, b = ev[i][0].elapsed_time(ev[i][1]), ev[i][1].elapsed_time(ev[i][2])
+            ours.append(b if i & 1 else a)
+            lib.append(a if i & 1 else b)
         ms, gms = sum(ours) / len(ours), sum(lib) / len(lib)
         # the method's product: every one of the 17 rows per request through the head once
         flops = 2.0 * (Bl * (2 * Kl + 1)) * Hl * Vl
@@ -400,7 +407,8 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed, only=None):
             "library_gemm_TFLOP_per_s": flops / (gms * 1e-3) / 1e12,
             "note": "flops of the method's product (all 17 rows per request through the head once, its "
                     "epilogue also storing the fp32 logits for the final draw); library_gemm_us: the bare "
-                    "product alone, bf16 logits written, no verification; the two timed call by call, alternating"}
+                    "product alone, bf16 logits written, no verification; the two timed call by call, back to back, "
+                    "alternating which goes first"}
         print(f"# lmhead_verify: {1e3 * ms:.0f} us/call, {tfs:.0f} TFLOP/s; library GEMM of the same product "
               f"{1e3 * gms:.0f} us", file=sys.stderr, flush=True)
         del ht, hd, wv, wsl, hall, wt

@@ -128,6 +128,17 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
   return v;
 }
 
+// Sum over the wave, the same on every lane, by the DPP scan (lane 63 of the
+// inclusive sum, read back): VALU lane moves instead of LDS permutes, for
+// latency-bound paths with few waves per SIMD. The order of the additions is
+// the scan's.
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v = wave_incl_scan(v);
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), kWave - 1);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), kWave - 1);
+  return __hiloint2double(hi, lo);
+}
+
 // Sum over the wave, the same on every lane (butterfly).
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll

@@ -121,7 +121,10 @@ template <int DT>
 __device__ __forceinline__ void gather_nodes(const LinCfg& c, const TreeTopo& tp, const TreeCfg& tc, int64_t b,
                                              NodeIn* nodes) {
   using E = Elem<DT>;
-  for (int n = threadIdx.x; n < tc.N; n += blockDim.x) {
+  // threads from wave 1 on first, so that wave 0 is free for other work when N
+  // is below the workgroup size less a wave
+  const int first = (int)((threadIdx.x + blockDim.x - kWave) % blockDim.x);
+  for (int n = first; n < tc.N; n += blockDim.x) {
     const int r = tp.prow[n];
     NodeIn o;
     o.tok = tc.tokens[b * tc.N + n];
@@ -198,7 +201,6 @@ __global__ __launch_bounds__(kWG) void k_tree_wp(LinCfg c, TreeTopo tp, TreeCfg 
   TreeRes* const tres_out = (round & 1) ? tc.tres2 : tc.tres;
   const TreeRes* const tres_in = (round & 1) ? tc.tres : tc.tres2;
   __shared__ int s_bad, s_badq;
-  __shared__ double sh[kWaves];
   __shared__ RowStat s_rs[2 * (kMaxNodes + 1)];
   __shared__ NodeIn s_nodes[kMaxNodes];
   __shared__ TreeState s_st;
@@ -258,26 +260,30 @@ __global__ __launch_bounds__(kWG) void k_tree_wp(LinCfg c, TreeTopo tp, TreeCfg 
       if (lead && t == 0) ts_out[b] = s;
       return;
     }
-    // fp64-grade normalisers of the row pair and G(c_new) from the previous pass
-    const TreeRes* rr = tres_in + b * c.nsb;
-    double sp = 0.0, sq = 0.0;
-    for (int sb = t; sb < c.nsb; sb += kWG) {
-      sp += rr[sb].sp;
-      sq += rr[sb].sq;
+    // fp64-grade normalisers of the row pair and G(c_new) from the previous
+    // pass, by wave 0 (thread 0 takes the walk), while the other waves gather
+    // the node inputs
+    if (t < kWave) {
+      const TreeRes* rr = tres_in + b * c.nsb;
+      double sp = 0.0, sq = 0.0;
+      for (int sb = t; sb < c.nsb; sb += kWave) {
+        sp += rr[sb].sp;
+        sq += rr[sb].sq;
+      }
+      const double Sp = wave_sum_dpp(sp);
+      const double Sq = wave_sum_dpp(sq);
+      double g = 0.0;
+      for (int sb = t; sb < c.nsb; sb += kWave) g += fmax(0.0, rr[sb].a / Sp - s.c_new * rr[sb].bq / Sq);
+      const double G = wave_sum_dpp(g);
+      s.Sp = Sp;
+      s.Sq = Sq;
+      s.has_exact = 1;
+      if (G > 0.0) {
+        s.cj = s.c_new;
+        s.Gj = G;
+      }
+      s.phase = kTreeTest;
     }
-    const double Sp = block_sum(sp, sh);
-    const double Sq = block_sum(sq, sh);
-    double g = 0.0;
-    for (int sb = t; sb < c.nsb; sb += kWG) g += fmax(0.0, rr[sb].a / Sp - s.c_new * rr[sb].bq / Sq);
-    const double G = block_sum(g, sh);
-    s.Sp = Sp;
-    s.Sq = Sq;
-    s.has_exact = 1;
-    if (G > 0.0) {
-      s.cj = s.c_new;
-      s.Gj = G;
-    }
-    s.phase = kTreeTest;
   }
   gather_nodes<DT>(c, tp, tc, b, s_nodes);
   __syncthreads();
@@ -314,7 +320,7 @@ __device__ __forceinline__ void tree_pass_sb(const LinCfg& c, const TreeState& s
     for (int v = 0; v < VPL; ++v)
 #pragma unroll
       for (int e = 0; e < EPV; ++e) sp += fweight<DT>(x[v][e], wp, c64, nullptr);
-    out.sp = wave_sum(sp);
+    out.sp = wave_sum_dpp(sp);
     out.a = out.sp;
     out.a0 = out.sp;
   } else {
@@ -343,12 +349,12 @@ __device__ __forceinline__ void tree_pass_sb(const LinCfg& c, const TreeState& s
         a0 = __builtin_fma(in0, ep, a0);
         bq0 = __builtin_fma(in0, eq, bq0);
       }
-    out.sp = wave_sum(sp);
-    out.sq = wave_sum(sq);
-    out.a = wave_sum(a);
-    out.bq = wave_sum(bq);
-    out.a0 = wave_sum(a0);
-    out.bq0 = wave_sum(bq0);
+    out.sp = wave_sum_dpp(sp);
+    out.sq = wave_sum_dpp(sq);
+    out.a = wave_sum_dpp(a);
+    out.bq = wave_sum_dpp(bq);
+    out.a0 = wave_sum_dpp(a0);
+    out.bq0 = wave_sum_dpp(bq0);
   }
   if (lane == 0) dst[b * c.nsb + sb] = out;
 }
@@ -408,16 +414,16 @@ __global__ __launch_bounds__(kWave) void k_tree_pick(LinCfg c, TreeCfg tc) {
   int mode = 0;
   double Sp = 1.0, Sq = 1.0, cm = 0.0, W = 0.0;
   if (s.c_new != 0.0) {
-    Sp = wave_sum(lane_sum([](const TreeRes& r) { return r.sp; }));
-    Sq = wave_sum(lane_sum([](const TreeRes& r) { return r.sq; }));
+    Sp = wave_sum_dpp(lane_sum([](const TreeRes& r) { return r.sp; }));
+    Sq = wave_sum_dpp(lane_sum([](const TreeRes& r) { return r.sq; }));
     const double c1 = s.c_new;
-    W = wave_sum(lane_sum([&](const TreeRes& r) { return fmax(0.0, r.a / Sp - c1 * r.bq / Sq); }));
+    W = wave_sum_dpp(lane_sum([&](const TreeRes& r) { return fmax(0.0, r.a / Sp - c1 * r.bq / Sq); }));
     if (W > 0.0) {
       mode = 1;
       cm = c1;
     } else if (s.c_old > 0.0) {
       const double c0 = s.c_old;
-      W = wave_sum(lane_sum([&](const TreeRes& r) { return fmax(0.0, r.a0 / Sp - c0 * r.bq0 / Sq); }));
+      W = wave_sum_dpp(lane_sum([&](const TreeRes& r) { return fmax(0.0, r.a0 / Sp - c0 * r.bq0 / Sq); }));
       mode = 2;
       cm = c0;
     }
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(kWave) void k_tree_pick(LinCfg c, TreeCfg tc) {
   auto wsb = [&](const TreeRes& r) {
     return mode == 1 ? fmax(0.0, r.a / Sp - cm * r.bq / Sq) : (mode == 2 ? fmax(0.0, r.a0 / Sp - cm * r.bq0 / Sq) : r.sp);
   };
-  if (mode == 0) W = wave_sum(lane_sum([](const TreeRes& r) { return r.sp; }));
+  if (mode == 0) W = wave_sum_dpp(lane_sum([](const TreeRes& r) { return r.sp; }));
   const double target = u * W;
   double pref;
   int sel;
