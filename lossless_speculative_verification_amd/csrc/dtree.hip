@@ -380,8 +380,8 @@ __global__ __launch_bounds__(kWG) void k_dtree_walkpass(LinCfg c, DTreeCfg d) {
       all += w;
       kept += (gone >> (v * EPV + e)) & 1u ? 0.0 : w;
     }
-  all = wave_sum(all);
-  kept = wave_sum(kept);
+  all = wave_sum_dpp(all);
+  kept = wave_sum_dpp(kept);
   if (lane == 0) c.res[b * c.nsb + sb] = ResRec{kept, all, 0.0, 0.0};
 }
 
@@ -406,8 +406,8 @@ __global__ __launch_bounds__(kWave) void k_dtree_pick(LinCfg c, DTreeCfg d) {
     W += r.sp;
     W0 += r.sq;
   }
-  W = wave_sum(W);
-  W0 = wave_sum(W0);
+  W = wave_sum_dpp(W);
+  W0 = wave_sum_dpp(W0);
   const char* row = det_row(c, b, s.row);
   const WRow wr = wrow(DT == kBF16 && c.tab, s.m, c.c64);
   const double u = c.rng.u((uint32_t)b, (uint32_t)s.row, kDrawFinal);

@@ -209,7 +209,7 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
       const double tot = wave_sum4(sp, sq, a, bq);
       if ((lane & 15) == 0) reinterpret_cast<double*>(rec)[lane >> 4] = tot;  // ResRec is four doubles
     } else {
-      const double tot = wave_sum(sp);
+      const double tot = wave_sum_dpp(sp);
       if (lane == 0) *rec = ResRec{tot, 0.0, 0.0, 0.0};
     }
   };
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
       msq += s_rec[i].sq;
     }
     double pref;
-    const int sel_e = wave_select(nsb, u_final * wave_sum(me), west, pref);
+    const int sel_e = wave_select(nsb, u_final * wave_sum_dpp(me), west, pref);
     Raw16<DT> rp, rq;
     constexpr int EPL = kSB / kWave;
     if (sel_e >= 0) {
@@ -461,13 +461,13 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
       if (resid) raw16<DT, AL>(c, qrow, j0, rq);
     }
     // exact totals and masses
-    const double Sp = wave_sum(msp), Sq = resid ? wave_sum(msq) : 1.0;
+    const double Sp = wave_sum_dpp(msp), Sq = resid ? wave_sum_dpp(msq) : 1.0;
     const double iSp = 1.0 / Sp, iSq = 1.0 / Sq;
     double resid_mass = 0.0;
     if (resid) {
       double mine = 0.0;
       for (int i = s0; i < s1; ++i) mine += fmax(0.0, s_rec[i].a * iSp - s_rec[i].bq * iSq);
-      resid_mass = wave_sum(mine);
+      resid_mass = wave_sum_dpp(mine);
     }
     // residual weights, or (bonus row, or a residual that vanished) the target row's
     const bool rmode = resid && resid_mass > 0.0;
@@ -548,8 +548,8 @@ __global__ __launch_bounds__(kWave) void k_final(LinCfg c) {
   };
   double Sp = 1.0, Sq = 1.0;
   if (!bonus) {
-    Sp = wave_sum(lane_sum([](const ResRec& r) { return r.sp; }));
-    Sq = wave_sum(lane_sum([](const ResRec& r) { return r.sq; }));
+    Sp = wave_sum_dpp(lane_sum([](const ResRec& r) { return r.sp; }));
+    Sq = wave_sum_dpp(lane_sum([](const ResRec& r) { return r.sq; }));
   }
   const double iSp = 1.0 / Sp, iSq = 1.0 / Sq;
   const double c64 = c.c64;
@@ -557,9 +557,9 @@ __global__ __launch_bounds__(kWave) void k_final(LinCfg c) {
   wpair(DT == kBF16 && c.tab, st.mp, st.mq, !bonus, c64, wp, wq);
   norm_pair(wp, wq, !bonus, st.sp_hat, st.sq_hat);
   auto wres = [&](const ResRec& r) { return fmax(0.0, r.a * iSp - r.bq * iSq); };
-  const double resid = bonus ? 0.0 : wave_sum(lane_sum(wres));
+  const double resid = bonus ? 0.0 : wave_sum_dpp(lane_sum(wres));
   const bool rmode = !bonus && resid > 0.0;  // else the target row (bonus, or a vanished residual)
-  const double W = rmode ? resid : wave_sum(lane_sum([](const ResRec& r) { return r.sp; }));
+  const double W = rmode ? resid : wave_sum_dpp(lane_sum([](const ResRec& r) { return r.sp; }));
   const double target = st.u_final * W;
   double pref;
   int sel;
@@ -664,7 +664,7 @@ __global__ __launch_bounds__(kDT) void k_draftrow(LinCfg c) {
   const double* const tps = w.tab ? s_tab : nullptr;
   double mine = 0.0;
   for (int sb = lane; sb < c.nsb; sb += kWave) mine += s_rec[sb].sp;
-  const double W = wave_sum(mine);
+  const double W = wave_sum_dpp(mine);
   const double u = c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft);
   const int x = wave_pick(
       c.nsb, c.V, u * W, [&](int sb) { return s_rec[sb].sp; },
@@ -745,7 +745,7 @@ __device__ __forceinline__ void wave_stats_unit(const LinCfg& c, int64_t u) {
     }
     s += bs * exp2_fast(-(double)mc_lo);
   }
-  s = wave_sum(s);
+  s = wave_sum_dpp(s);
   if (lane == 0) {
     StatRec r;
     r.m = m;
@@ -878,7 +878,7 @@ __device__ __forceinline__ int qrow_draw(const LinCfg& c, const char* row, const
   const double* const tps = w.tab ? s_tab : nullptr;
   double mine = 0.0;
   for (int sb = lane; sb < c.nsb; sb += kWave) mine += s_rec[sb].sp;
-  const double W = wave_sum(mine);
+  const double W = wave_sum_dpp(mine);
   return wave_pick(c.nsb, c.V, u * W, [&](int sb) { return s_rec[sb].sp; },
                    [&](int64_t j0, double(&wt)[16]) { row16<kBF16, AL>(c, row, j0, w, tps, wt); });
 }
@@ -994,7 +994,7 @@ __global__ __launch_bounds__(kWG) void k_draftpass(LinCfg c) {
     for (int v = 0; v < VPL; ++v)
 #pragma unroll
       for (int e = 0; e < EPV; ++e) s += exp2_fast(((double)x[v][e] - md) * c.c64);
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
   }
   if (lane == 0) {
     DraftRec r;
