@@ -37,6 +37,36 @@ constexpr int64_t kResolveOneWgMinB = 192;
 constexpr int64_t kResolveTargetWgs = 256;
 constexpr size_t kResolveMaxLds = 64 * 1024;
 
+// Threads of a draft-row workgroup (k_draftrow, k_qrow, k_tqrow).
+constexpr int kDT = 512;
+constexpr int kDWaves = kDT / kWave;
+
+// The unscaled 2^(a c) table, filled by kDT threads
+// with one exp2 pair per 16 slots: thread t takes the 16 codes that share
+// sign, exponent and the top 3 mantissa bits, A = 2^(a_0 c) for the first of
+// them and r = 2^(u c) for the code step u, and slot k gets A * r^k with r^k
+// a running product (relative error below 2e-15, far inside what the draws
+// need). The draft-row pass and its draw (k_qrow), and the resolve step
+// (scaled copies) read this table.
+__device__ __forceinline__ void fill_tab_steps(double* tab, double c64) {
+  const int t = threadIdx.x;  // kDT = 2 halves x 256 groups of 16 slots
+  static_assert(kDT == 512 && kTabW <= 4096 && kTabNeg == 4096, "one group of 16 slots per thread");
+  const int half = t >> 8, j0 = (t & 255) * 16;
+  const uint32_t code0 = ((uint32_t)half << 15) | (kTabLo + (uint32_t)j0);
+  const float a0 = __uint_as_float(code0 << 16);
+  const float a1 = __uint_as_float((code0 + 1u) << 16);  // same exponent: j0 + 1 < next multiple of 128
+  const double A = exp2_fast((double)a0 * c64);
+  const double r = exp2_fast(((double)a1 - (double)a0) * c64);
+  double rk = 1.0;
+  double* const out = tab + half * kTabNeg + j0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if (j0 + k < kTabW) out[k] = A * rk;
+    else if (j0 + k == kTabW) out[k] = 0.0;  // the zero slot of this half
+    rk *= r;
+  }
+}
+
 // ------------------------------------------------------------ resolve --
 // Threads of a resolve workgroup: 16 waves, so that one workgroup per request
 // keeps every SIMD of a CU busy through the fp64 final-row pass.
@@ -333,7 +363,9 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
     s_S[r] = S;
     if (bad) atomicOr(&s_bad, 1);
   }
-  if (tab) fill_tab<kRT>(s_tab, c.c64);
+  // the table by the running-product fill (one exp2 pair per 16 slots, by the
+  // first kDT threads)
+  if (tab && t < kDT) fill_tab_steps(s_tab, c.c64);
   __syncthreads();
   int acc = 1;
   double P = 0.0, Q = 0.0;
@@ -608,9 +640,6 @@ __global__ __launch_bounds__(kWave) void k_final(LinCfg c) {
 // then wave 0 draws x ~ q by inverse CDF over the sub-block sums and a rescan
 // of the chosen sub-block ("Uno" research explainer, §3.3: the drafts of a
 // block are drawn from the draft distributions). -1 for an invalid row.
-constexpr int kDT = 512;
-constexpr int kDWaves = kDT / kWave;
-
 template <int DT, bool AL>
 __global__ __launch_bounds__(kDT) void k_draftrow(LinCfg c) {
   extern __shared__ ResRec s_rec[];  // one record per sub-block
@@ -670,31 +699,6 @@ __global__ __launch_bounds__(kDT) void k_draftrow(LinCfg c) {
       c.nsb, c.V, u * W, [&](int sb) { return s_rec[sb].sp; },
       [&](int64_t j0, double(&wt)[16]) { row16<DT, AL>(c, row, j0, w, tps, wt); });
   if (lane == 0) c.draft[qr] = x;
-}
-
-// The unscaled 2^(a c) table of the draft-row pass, filled by kDT threads
-// with one exp2 pair per 16 slots: thread t takes the 16 codes that share
-// sign, exponent and the top 3 mantissa bits, A = 2^(a_0 c) for the first of
-// them and r = 2^(u c) for the code step u, and slot k gets A * r^k with r^k
-// a running product (relative error below 2e-15, far inside what the draws
-// need). The pass and the draw of k_qrow both read this table.
-__device__ __forceinline__ void fill_tab_steps(double* tab, double c64) {
-  const int t = threadIdx.x;  // kDT = 2 halves x 256 groups of 16 slots
-  static_assert(kDT == 512 && kTabW <= 4096 && kTabNeg == 4096, "one group of 16 slots per thread");
-  const int half = t >> 8, j0 = (t & 255) * 16;
-  const uint32_t code0 = ((uint32_t)half << 15) | (kTabLo + (uint32_t)j0);
-  const float a0 = __uint_as_float(code0 << 16);
-  const float a1 = __uint_as_float((code0 + 1u) << 16);  // same exponent: j0 + 1 < next multiple of 128
-  const double A = exp2_fast((double)a0 * c64);
-  const double r = exp2_fast(((double)a1 - (double)a0) * c64);
-  double rk = 1.0;
-  double* const out = tab + half * kTabNeg + j0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    if (j0 + k < kTabW) out[k] = A * rk;
-    else if (j0 + k == kTabW) out[k] = 0.0;  // the zero slot of this half
-    rk *= r;
-  }
 }
 
 // Statistics record of one (target row, chunk) by one wave, with no
