@@ -8,7 +8,7 @@
 // reads only target row n and draft row n of each request.
 //
 // Pipeline on the caller's stream:
-//   k_lmh_gemm              every target and draft row against every 512-token
+//   k_lmh_gemm              every target and draft row against every 256-token
 //                           vocabulary tile: per (row, tile) the maximum and a
 //                           binary32-grade sum of 2^((z - m) c), and the logits;
 //   k_lmh_decide            per request: row normalisers, the drafted tokens'
