@@ -348,7 +348,7 @@ int psispec_tv_loss(const void* p_logits, const void* q_logits, int dtype, int64
  * verification rule of psispec_verify_linear). The logits are products of
  * hidden states with the vocabulary matrix, p_logits = h_target W^T and
  * q_logits = h_draft W^T, computed on bf16 matrix cores (fp32 accumulation)
- * tile by tile and reduced as they are produced (per row and 256-token tile,
+ * tile by tile and reduced as they are produced (per row and 128-token chunk,
  * the maximum and the sum of exponentials); the same pass stores the fp32
  * logits in the workspace, from which the final draw reads the residual or
  * bonus rows, so the product is made once.

@@ -547,7 +547,7 @@ inline LmhLayout lmh_layout(int64_t B, int32_t K, int32_t V) {
   const int64_t ntn = (V + kLmhTileN - 1) / kLmhTileN;
   size_t off = 0;
   L.st = off;
-  off = align_up(off + (size_t)(rows * ntn) * sizeof(StatRec), 256);
+  off = align_up(off + (size_t)(rows * ntn * (kLmhTileN / kLmhChunk)) * sizeof(StatRec), 256);
   L.ts = off;
   off = align_up(off + (size_t)B * sizeof(TreeState), 256);
   L.tres = off;

@@ -327,6 +327,7 @@ hipError_t launch_toy_logits(int64_t rows, int V, const int32_t* ctx, const int3
 // Linear verification fused with the LM head (lmhead.hip).
 constexpr int kLmhTileM = 256;  // rows of a product tile
 constexpr int kLmhTileN = 256;  // vocabulary entries of a product tile
+constexpr int kLmhChunk = 128;  // vocabulary entries of a statistics record (a wave's share of a tile)
 constexpr int kLmhStepK = 128;  // the hidden size must be a multiple of this
 struct LmhCfg {
   const uint16_t* hp;     // [Mp, H] target hidden states (bf16 bits)
@@ -339,7 +340,7 @@ struct LmhCfg {
   int ntm, ntn;           // row tiles, vocabulary tiles
   const int32_t* draft;   // [B, K]
   float c32;
-  StatRec* st;            // [Mp + Mq][ntn] per (row, vocabulary tile)
+  StatRec* st;            // [Mp + Mq][ntn V-tiles x 2 chunks] per (row, 128-token chunk)
   float* all;             // [Mp + Mq][V] fp32 logits of every row, kept for the final draw
                           // (nullptr: not kept)
 };

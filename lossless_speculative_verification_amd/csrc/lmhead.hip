@@ -9,8 +9,9 @@
 //
 // Pipeline on the caller's stream:
 //   k_lmh_gemm              every target and draft row against every 256-token
-//                           vocabulary tile: per (row, tile) the maximum and a
-//                           binary32-grade sum of 2^((z - m) c), and the logits;
+//                           vocabulary tile: per row and 128-token chunk the
+//                           maximum and a binary32-grade sum of 2^((z - m) c),
+//                           and the logits;
 //   k_lmh_decide            per request: row normalisers, the drafted tokens'
 //                           logits (dot products), accept tests
 //                           u * Q(x) < P(x), first rejection n; the draw state;
@@ -36,8 +37,10 @@
 // slots are permuted by an XOR of row bits 2..3, so that the fragment reads
 // of each 16-lane group fall in distinct banks. The tile epilogue stores the
 // logits and reduces each row over the wave's 128 columns with a butterfly
-// across the 16 lanes of a column group (every stage halves the rows a lane
-// carries), then over the two waves of the row through LDS.
+// across the 16 lanes of a column group (DPP moves within the row of 16
+// lanes; every stage halves the rows a lane carries): a record per row and
+// wave, so the epilogue has no barrier and the waves of a tile do not wait
+// for one another.
 // Block operand layout of the instruction (checked on the device against the
 // 32 x 32 x 16 form): lane l holds A[l % 16][8 (l / 16) .. +7] and
 // W[col l % 16][8 (l / 16) .. +7]; result element i of lane l is
@@ -52,6 +55,7 @@ namespace {
 
 constexpr int kLmhBM = kLmhTileM, kLmhBN = kLmhTileN, kLmhBK = 32;
 static_assert(kLmhBM == 256 && kLmhBN == 256, "2 x 2 wave quarters of 128 x 128");
+static_assert(kLmhChunk * 2 == kLmhBN, "a statistics record per wave column");
 static_assert(kLmhStepK == 4 * kLmhBK, "at least 4 steps, an even number (fragment buffers alternate)");
 constexpr int kWN = 2;                            // waves side by side along the vocabulary
 constexpr int kStages = 4;                        // ring depth (128 KB): loads of step s + 3 spread over step s
@@ -118,12 +122,19 @@ __device__ __forceinline__ void lmh_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+// A value from another lane of the same row of 16 lanes, by DPP: lane
+// l ^ 15 (row mirror), l ^ 7 (half-row mirror), l ^ 3 and l ^ 1 (quad
+// permutations 3 2 1 0 and 1 0 3 2).
+constexpr int kDppRowMirror = 0x140, kDppHalfMirror = 0x141, kDppXor3 = 0x1B, kDppXor1 = 0xB1;
+template <int kCtrl>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
 
 }  // namespace
 
 __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k_lmh_gemm(LmhCfg g) {
   __shared__ __attribute__((aligned(1024))) unsigned char s_mem[kStages * kStage];  // operand ring
-  __shared__ float s_wm[kWN][kLmhBM], s_ws[kWN][kLmhBM];  // epilogue: per-wave row maxima and sums
   const int t = threadIdx.x, lane = t & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
   const int wm = wave / kWN, wn = wave % kWN;
@@ -319,100 +330,125 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     // Element e of block (bi, bj) on this lane: tile row wm 128 + bi 16 +
     // 4 (lane / 16) + e, tile column wn 128 + bj 16 + lane % 16. The lane
     // index is taken again here so that the epilogue's address arithmetic is
-    // not kept live across the main loop.
+    // not kept live across the main loop. No barrier: each wave writes the
+    // records of its own 128 columns.
     const int lid = lane_here();
     const int er = lid & 15, eq = lid >> 4;
-    if (g.all) {
-      // every logit of the tile, kept for the final draw
-#pragma unroll
-      for (int bi = 0; bi < 8; ++bi)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t i = m0 + wm * 128 + bi * 16 + 4 * eq + e;
-          if (i >= g.M) continue;
-#pragma unroll
-          for (int bj = 0; bj < 8; ++bj) {
-            const int64_t n = n0 + wn * 128 + bj * 16 + er;
-            if (n < g.V) g.all[i * (int64_t)g.V + n] = acc[bi][bj][e];
-          }
-        }
-    }
+    const int64_t c0 = n0 + wn * 128;  // first column of the wave's chunk
+    const bool fullc = c0 + 128 <= g.V;
     const float c32 = g.c32;
-    // Per row of the tile (item it = 4 bi + e of this lane: row
-    // 16 bi + 4 (lane / 16) + e of the wave's quarter): the maximum and the
-    // sum of 2^((z - m) c) over this lane's 8 columns, then over the 16 lanes
-    // of the column group by a butterfly that halves the items at every stage
-    // (at offset o a lane keeps the items whose index bit matches its lane bit
-    // and sends the others), so that lane l ends with items 2 (l % 16) and
+    // Row block by row block: the block's logits are stored (kept for the
+    // final draw; a block whose 16 rows and 128 columns are all in the product
+    // without per-element tests, the columns of block bj at immediate
+    // offsets), then, from the same values, per row of the wave's chunk (item
+    // it = 4 bi + e of this lane: row 16 bi + 4 (lane / 16) + e of the wave's
+    // quarter) the maximum and the sum of 2^((z - m) c) over this lane's 8
+    // columns; columns past the vocabulary (a last tile) are left out. Then
+    // the items are reduced over the 16 lanes of the column group by a
+    // butterfly that halves them at every stage (with the partner lane ^ 15,
+    // ^ 7, ^ 3, ^ 1, moved by DPP within the row of 16 lanes: a lane keeps the
+    // items whose index bit 3, 2, 1, 0 matches that bit of its lane and sends
+    // the others), so that lane l ends with items 2 (l % 16) and
     // 2 (l % 16) + 1.
-    bool vcol[8];  // this lane's column of block bj is inside the vocabulary
-#pragma unroll
-    for (int bj = 0; bj < 8; ++bj) vcol[bj] = n0 + wn * 128 + bj * 16 + er < g.V;
     float im[32], is[32];
 #pragma unroll
-    for (int it = 0; it < 32; ++it) {
-      const int bi = it >> 2, e = it & 3;
-      float m = -INFINITY;
+    for (int bi = 0; bi < 8; ++bi) {
+      const int64_t rb = m0 + wm * 128 + bi * 16;
+      if (rb >= g.M) {  // rows past the product: no logits, an empty part
 #pragma unroll
-      for (int bj = 0; bj < 8; ++bj) m = vcol[bj] ? fmaxnan(m, acc[bi][bj][e]) : m;
-      const float mo = is_neg_inf(m) ? 0.0f : m;  // an empty part sums to 0
-      float sl = 0.0f;
+        for (int e = 0; e < 4; ++e) {
+          im[4 * bi + e] = -INFINITY;
+          is[4 * bi + e] = 0.0f;
+        }
+        continue;
+      }
+      if (g.all) {
+        if (fullc && rb + 16 <= g.M) {
 #pragma unroll
-      for (int bj = 0; bj < 8; ++bj) sl += vcol[bj] ? __builtin_amdgcn_exp2f((acc[bi][bj][e] - mo) * c32) : 0.0f;
-      im[it] = m;
-      is[it] = sl;
+          for (int e = 0; e < 4; ++e) {
+            float* const p = g.all + (rb + 4 * eq + e) * (int64_t)g.V + c0 + er;
+#pragma unroll
+            for (int bj = 0; bj < 8; ++bj) p[bj * 16] = acc[bi][bj][e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t i = rb + 4 * eq + e;
+            if (i >= g.M) continue;
+#pragma unroll
+            for (int bj = 0; bj < 8; ++bj) {
+              const int64_t n = c0 + bj * 16 + er;
+              if (n < g.V) g.all[i * (int64_t)g.V + n] = acc[bi][bj][e];
+            }
+          }
+        }
+      }
+      auto item = [&](auto full_tag, int e) {
+        constexpr bool kFull = decltype(full_tag)::value;
+        float x[8];
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj)
+          x[bj] = kFull || c0 + bj * 16 + er < g.V ? acc[bi][bj][e] : -INFINITY;
+        float m = x[0];
+#pragma unroll
+        for (int bj = 1; bj < 8; ++bj) m = fmaxnan(m, x[bj]);
+        const float mo = is_neg_inf(m) ? 0.0f : m;  // an empty part sums to 0
+        float sl = 0.0f;
+#pragma unroll
+        for (int bj = 0; bj < 8; ++bj) sl += __builtin_amdgcn_exp2f((x[bj] - mo) * c32);
+        im[4 * bi + e] = m;
+        is[4 * bi + e] = sl;
+      };
+      if (fullc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) item(std::true_type{}, e);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) item(std::false_type{}, e);
+      }
     }
-    auto xor_lane = [&](float v, int off) {  // v of lane lid ^ off (addresses from the epilogue's lane index)
-      return __int_as_float(__builtin_amdgcn_ds_bpermute((lid ^ off) << 2, __float_as_int(v)));
+    // two parts (ma, sa), (mb, sb) as one: the part with the smaller maximum
+    // is scaled by 2^((min - max) c), the other is exact
+    auto merge = [&](float ma, float sa, float mb, float sb, float& m, float& sm) {
+      m = fmaxnan(ma, mb);
+      const bool ab = ma >= mb;
+      const float big = ab ? sa : sb, small = ab ? sb : sa;
+      const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(ma - mb) * c32);
+      sm = is_neg_inf(m) ? 0.0f : big + small * e;
     };
-    auto part = [&](float mx, float sx, float m) {  // sx 2^((mx - m) c), 0 for an empty part
-      return is_neg_inf(mx) ? 0.0f : sx * __builtin_amdgcn_exp2f((mx - m) * c32);
-    };
-#pragma unroll
-    for (int stg = 0; stg < 4; ++stg) {
-      const int off = 8 >> stg, n = 16 >> stg;
-      const bool up = (er & off) != 0;
+    auto stage = [&](auto ctrl_tag, int bit, int n) {
+      constexpr int kCtrl = decltype(ctrl_tag)::value;
+      const bool up = (er & bit) != 0;
 #pragma unroll
       for (int i = 0; i < n; ++i) {
         const float mk = up ? im[i + n] : im[i], sk = up ? is[i + n] : is[i];
         const float mo = up ? im[i] : im[i + n], so = up ? is[i] : is[i + n];
-        const float mr = xor_lane(mo, off), sr = xor_lane(so, off);
-        const float m = fmaxnan(mk, mr);
-        im[i] = m;
-        is[i] = is_neg_inf(m) ? 0.0f : part(mk, sk, m) + part(mr, sr, m);
+        merge(mk, sk, dpp_row<kCtrl>(mo), dpp_row<kCtrl>(so), im[i], is[i]);
       }
-    }
+    };
+    stage(std::integral_constant<int, kDppRowMirror>{}, 8, 16);
+    stage(std::integral_constant<int, kDppHalfMirror>{}, 4, 8);
+    stage(std::integral_constant<int, kDppXor3>{}, 2, 4);
+    stage(std::integral_constant<int, kDppXor1>{}, 1, 2);
+    // the records of the wave's chunk: an overflowed or NaN maximum marks the
+    // record invalid; an empty chunk (past the vocabulary) has maximum -inf
+    // and sum 0
+    const int nch = g.ntn * (kLmhBN / kLmhChunk);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int it = 2 * er + i, bi = it >> 2, e = it & 3;
-      const int row = wm * 128 + bi * 16 + 4 * eq + e;
-      s_wm[wn][row] = im[i];
-      s_ws[wn][row] = is[i];
-    }
-    __syncthreads();
-    if (t < kLmhBM) {  // a thread per tile row (the tables are next written after the next tile's barriers)
-      const int64_t r = m0 + t;
+      const int64_t r = m0 + wm * 128 + bi * 16 + 4 * eq + e;
       if (r < g.M) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWN; ++w) m = fmaxnan(m, s_wm[w][t]);
-        double sum = 0.0;
-        if (!is_neg_inf(m)) {
-#pragma unroll
-          for (int w = 0; w < kWN; ++w) {
-            const float mw = s_wm[w][t];
-            if (!is_neg_inf(mw)) sum += (double)s_ws[w][t] * ::exp2(((double)mw - (double)m) * (double)c32);
-          }
-        }
-        if (isnan(m) || isinf(m)) sum = NAN;
-        g.st[r * (int64_t)g.ntn + tn] = StatRec{m, 0u, sum};
+        const float m = im[i];
+        const double s = (isnan(m) || m == INFINITY) ? (double)NAN : (double)is[i];
+        g.st[r * nch + 2 * tn + wn] = StatRec{m, 0u, s};
       }
     }
   }
 }
 
 // Per request (one workgroup): the row normalisers of the K + 1 target and K
-// draft rows from the tile records (a half-wave per row: 2K + 1 <= 32 rows
+// draft rows from the chunk records (a half-wave per row: 2K + 1 <= 32 rows
 // for K <= 15, else a second pass), the logits of the drafted tokens as dot
 // products of the hidden states with the tokens' rows of W (fp32 products,
 // summed per lane in order and across lanes in fp64), the accept tests (a lane
@@ -424,6 +460,7 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
   const int t = threadIdx.x, lane = t & (kWave - 1);
   const int hl = t & 31, hw = t >> 5;  // lane in the half-wave, half-wave
   const int K = g.K;
+  const int nch = g.ntn * (kLmhTileN / kLmhChunk);  // records per row
   __shared__ float s_m[2 * kMaxK + 1];
   __shared__ double s_S[2 * kMaxK + 1];
   __shared__ float s_z[2 * kMaxK + 1];  // logit of the row's drafted token
@@ -443,20 +480,20 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
   };
   for (int j = hw; j < 2 * K + 1; j += kDecideWG / 32) {
     const int64_t r = j <= K ? b * (K + 1) + j : g.Mp + b * K + (j - K - 1);
-    const StatRec* rec = g.st + r * (int64_t)g.ntn;
+    const StatRec* rec = g.st + r * (int64_t)nch;
     // loads are issued in batches of kDecB before their values are used, so
     // that a row costs a few memory latencies rather than one per iteration
     constexpr int kDecB = 8;
     float m = -INFINITY;
     int bad = 0;
-    for (int i0 = hl; i0 < g.ntn; i0 += 32 * kDecB) {
+    for (int i0 = hl; i0 < nch; i0 += 32 * kDecB) {
       float mm[kDecB];
       double ss[kDecB];
 #pragma unroll
       for (int u = 0; u < kDecB; ++u) {
         const int i = i0 + 32 * u;
-        mm[u] = i < g.ntn ? rec[i].m : -INFINITY;
-        ss[u] = i < g.ntn ? rec[i].s : 0.0;
+        mm[u] = i < nch ? rec[i].m : -INFINITY;
+        ss[u] = i < nch ? rec[i].s : 0.0;
       }
 #pragma unroll
       for (int u = 0; u < kDecB; ++u) {
@@ -496,14 +533,14 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
     m = hmax(m);
     double S = 0.0;
     if (!isnan(m) && !isinf(m))
-      for (int i0 = hl; i0 < g.ntn; i0 += 32 * kDecB) {
+      for (int i0 = hl; i0 < nch; i0 += 32 * kDecB) {
         float mm[kDecB];
         double ss[kDecB];
 #pragma unroll
         for (int u = 0; u < kDecB; ++u) {
           const int i = i0 + 32 * u;
-          mm[u] = i < g.ntn ? rec[i].m : -INFINITY;
-          ss[u] = i < g.ntn ? rec[i].s : 0.0;
+          mm[u] = i < nch ? rec[i].m : -INFINITY;
+          ss[u] = i < nch ? rec[i].s : 0.0;
         }
 #pragma unroll
         for (int u = 0; u < kDecB; ++u)
