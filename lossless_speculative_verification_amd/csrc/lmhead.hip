@@ -26,11 +26,12 @@
 // one per SIMD, each own a 128 x 128 quarter of the tile as 8 x 8 blocks of
 // v_mfma_f32_16x16x32_bf16 (256 accumulator registers); on gfx950 this block
 // shape issues at a higher rate than 32 x 32 x 16 (measured: 2.4 against 2.1
-// PFLOP/s from registers). Operand tiles of 32 hidden elements per step go
-// from global memory straight into LDS (16-byte direct loads, no register
-// staging) through a four-stage ring that runs on across tile boundaries: the
-// loads of the next tile's first steps are in flight while a tile's epilogue
-// runs. The loads of step s + 3 are issued during step s, one after each
+// PFLOP/s from registers); a last row tile with fewer rows is split evenly
+// between the two wave rows, whose empty blocks are skipped. Operand tiles of
+// 32 hidden elements per step go from global memory straight into LDS
+// (16-byte direct loads, no register staging) through a four-stage ring that
+// runs on across tile boundaries: the loads of the next tile's first steps
+// are in flight while a tile's epilogue runs. The loads of step s + 3 are issued during step s, one after each
 // group of 8 products, into the slot step s - 1 has left; the fragments of
 // step s + 1 are read from LDS during the second half of step s (double
 // buffered by step parity). A tile row is 64 bytes in LDS: its four 16-byte
@@ -237,10 +238,18 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
   for (int k = 0; k < mine; ++k, pos = next_tile(pos)) {
     const int tn = pos.tn;
     const int64_t m0 = (int64_t)pos.tm * kLmhBM, n0 = (int64_t)tn * kLmhBN;
-    // row blocks of 16 of this wave that hold rows of the product (a last
-    // row tile may be partial: its empty blocks are not multiplied)
-    const int64_t mrem = g.M - m0 - wm * 128;
-    const int mb = mrem <= 0 ? 0 : (int)((mrem + 15) / 16 < 8 ? (mrem + 15) / 16 : 8);
+    // Rows of the tile per wave row: 128, or in a last row tile with fewer
+    // than 256 rows of the product an even split of its 16-row blocks
+    // between the two wave rows (wave row wm takes tile rows [wm rpw,
+    // (wm + 1) rpw)); mb of the wave's row blocks hold rows of the product,
+    // the others are not multiplied, stored or recorded.
+    const int64_t rrem = g.M - m0;
+    const int rpw = rrem >= kLmhBM ? 128 : 16 * (int)((rrem + 31) / 32);
+    const int64_t mrem = rrem - wm * rpw;
+    const int mb = __builtin_amdgcn_readfirstlane(
+        mrem <= 0 ? 0 : (int)((mrem + 15) / 16 < rpw / 16 ? (mrem + 15) / 16 : rpw / 16));
+    const int64_t mw = m0 + wm * rpw;      // first row of the wave's share
+    const int bat = ba - wm * (128 - rpw) * kRowB;  // its fragment reads
     f32x4_t acc[8][8];
 #pragma unroll
     for (int bi = 0; bi < 8; ++bi)
@@ -251,7 +260,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     {
       const unsigned char* st = ring(cur);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) fa[0][i] = *(const bf16x8_t*)(st + ba + i * 16 * kRowB);
+      for (int i = 0; i < 8; ++i) fa[0][i] = *(const bf16x8_t*)(st + bat + i * 16 * kRowB);
 #pragma unroll
       for (int i = 0; i < 8; ++i) fb[0][i] = *(const bf16x8_t*)(st + bw + i * 16 * kRowB);
     }
@@ -286,8 +295,8 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
       const unsigned char* sn = ring(nxt);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        fa[1 - P][2 * gq] = *(const bf16x8_t*)(sn + ba + (2 * gq) * 16 * kRowB);
-        fa[1 - P][2 * gq + 1] = *(const bf16x8_t*)(sn + ba + (2 * gq + 1) * 16 * kRowB);
+        fa[1 - P][2 * gq] = *(const bf16x8_t*)(sn + bat + (2 * gq) * 16 * kRowB);
+        fa[1 - P][2 * gq + 1] = *(const bf16x8_t*)(sn + bat + (2 * gq + 1) * 16 * kRowB);
         fb[1 - P][2 * gq] = *(const bf16x8_t*)(sn + bw + (2 * gq) * 16 * kRowB);
         fb[1 - P][2 * gq + 1] = *(const bf16x8_t*)(sn + bw + (2 * gq + 1) * 16 * kRowB);
         const int bi = 4 + gq;
@@ -327,7 +336,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     }
 
     // ---- epilogue of the tile (the next tile's first steps are loading).
-    // Element e of block (bi, bj) on this lane: tile row wm 128 + bi 16 +
+    // Element e of block (bi, bj) on this lane: tile row wm rpw + bi 16 +
     // 4 (lane / 16) + e, tile column wn 128 + bj 16 + lane % 16. The lane
     // index is taken again here so that the epilogue's address arithmetic is
     // not kept live across the main loop. No barrier: each wave writes the
@@ -342,7 +351,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     // without per-element tests, the columns of block bj at immediate
     // offsets), then, from the same values, per row of the wave's chunk (item
     // it = 4 bi + e of this lane: row 16 bi + 4 (lane / 16) + e of the wave's
-    // quarter) the maximum and the sum of 2^((z - m) c) over this lane's 8
+    // share) the maximum and the sum of 2^((z - m) c) over this lane's 8
     // columns; columns past the vocabulary (a last tile) are left out. Then
     // the items are reduced over the 16 lanes of the column group by a
     // butterfly that halves them at every stage (with the partner lane ^ 15,
@@ -353,8 +362,8 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
     float im[32], is[32];
 #pragma unroll
     for (int bi = 0; bi < 8; ++bi) {
-      const int64_t rb = m0 + wm * 128 + bi * 16;
-      if (rb >= g.M) {  // rows past the product: no logits, an empty part
+      const int64_t rb = mw + bi * 16;
+      if (bi >= mb) {  // not the wave's rows of the product: an empty part
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           im[4 * bi + e] = -INFINITY;
@@ -437,8 +446,8 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(1))) void k
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int it = 2 * er + i, bi = it >> 2, e = it & 3;
-      const int64_t r = m0 + wm * 128 + bi * 16 + 4 * eq + e;
-      if (r < g.M) {
+      const int64_t r = mw + bi * 16 + 4 * eq + e;
+      if (bi < mb && r < g.M) {
         const float m = im[i];
         const double s = (isnan(m) || m == INFINITY) ? (double)NAN : (double)is[i];
         g.st[r * nch + 2 * tn + wn] = StatRec{m, 0u, s};
