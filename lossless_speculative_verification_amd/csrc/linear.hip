@@ -887,12 +887,17 @@ __device__ __forceinline__ int qrow_draw(const LinCfg& c, const char* row, const
                    [&](int64_t j0, double(&wt)[16]) { row16<kBF16, AL>(c, row, j0, w, tps, wt); });
 }
 
-// The target-row chunk records of a launch: wave `slot` of workgroup g takes
-// the units g * kDWaves + slot + k * (kDWaves * grid), `nunits` in all.
-template <bool AL>
+// The target-row chunk records of a launch, `nunits` in all. Workgroup-major
+// (WG_MAJOR): wave `slot` of workgroup g takes the units g * kDWaves + slot +
+// k * (kDWaves * grid), so the first workgroups take them all. Otherwise
+// slot-major: it takes slot * grid + g + k * (kDWaves * grid), so every
+// workgroup gets the same number of units to within one and no CU streams
+// more target rows than another.
+template <bool AL, bool WG_MAJOR = true>
 __device__ __forceinline__ void stats_units(const LinCfg& c, int64_t nunits, int slot) {
-  for (int64_t un = (int64_t)blockIdx.x * kDWaves + slot; un < nunits; un += (int64_t)gridDim.x * kDWaves)
-    wave_stats_unit<AL>(c, un);
+  const int64_t g = blockIdx.x, G = gridDim.x;
+  const int64_t first = WG_MAJOR ? g * kDWaves + slot : (int64_t)slot * G + g;
+  for (int64_t un = first; un < nunits; un += G * kDWaves) wave_stats_unit<AL>(c, un);
 }
 
 // One workgroup per draft row of linear verification: qrow_pass, then wave 0
@@ -918,8 +923,8 @@ __global__ __launch_bounds__(kDT) void k_qrow(LinCfg c, int64_t nunits) {
     const int x = ok ? qrow_draw<AL>(c, row, s_rec, s_tab, w, c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft)) : -1;
     if ((threadIdx.x & (kWave - 1)) == 0) c.draft[qr] = x;
   }
-  // wave 0 (busy drawing) takes the last slot of its workgroup, which the grid reaches last
-  stats_units<AL>(c, nunits, wave == 0 ? kDWaves - 1 : wave - 1);
+  // wave 0 (busy drawing) takes the last slot, which the grid reaches last
+  stats_units<AL, false>(c, nunits, wave == 0 ? kDWaves - 1 : wave - 1);
 }
 
 // Tree node drafts: workgroups [0, nextra) compute target-row chunk records
