@@ -265,7 +265,8 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed, only=None):
                                                            step=i, fused=True, out=outs, workspace=ws, stream=stream),
                         steps, 5, stream)
         line("tree_4x8_B4_N32_V151936_bf16", ms, Bt * 2 * (Nt + 1) * Vt * 2 + 4 * Bt * Nt + 4 * Bt * (2 * D + 2),
-             Bt * (Nt + 1), {"note": "latency-bound: 10 kernel launches per call"})
+             Bt * (Nt + 1), {"note": "latency-bound: 6 kernel launches per call (draft rows with the target-row "
+                             "statistics, one walk round per root child, the final pick)"})
         ms = time_calls(torch, lambda i: psi.verify_tree(*copies[i % 4], parent, nodes, temperature=1.0, top_k=0,
                                                            top_p=float(np.float32(0.95)), seed=seed, step=i, fused=True,
                                                            out=outs, workspace=ws, stream=stream),
@@ -301,7 +302,7 @@ def other_workloads(torch, psi, synth, dev, stream, steps, seed, only=None):
 
         ms = time_calls(torch, sampler_step, steps, 5, stream)
         line("treesampler_16_32_32_B4_V151936_bf16", ms, (Bs * Ks + Bs * (Ns + 1)) * Vs * 2, Bs * (Ks + Ns + 1),
-             {"note": "candidates (4 launches) + verification of deterministic candidates (4 launches)"})
+             {"note": "candidates (4 launches) + verification of deterministic candidates (3 launches)"})
         del copies, wsc, wsv
         torch.cuda.empty_cache()
 
