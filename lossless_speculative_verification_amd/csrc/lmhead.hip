@@ -490,26 +490,9 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
   for (int j = hw; j < 2 * K + 1; j += kDecideWG / 32) {
     const int64_t r = j <= K ? b * (K + 1) + j : g.Mp + b * K + (j - K - 1);
     const StatRec* rec = g.st + r * (int64_t)nch;
-    // loads are issued in batches of kDecB before their values are used, so
-    // that a row costs a few memory latencies rather than one per iteration
+    // loads are issued in batches before their values are used, so that a
+    // row costs a few memory latencies rather than one per iteration
     constexpr int kDecB = 8;
-    float m = -INFINITY;
-    int bad = 0;
-    for (int i0 = hl; i0 < nch; i0 += 32 * kDecB) {
-      float mm[kDecB];
-      double ss[kDecB];
-#pragma unroll
-      for (int u = 0; u < kDecB; ++u) {
-        const int i = i0 + 32 * u;
-        mm[u] = i < nch ? rec[i].m : -INFINITY;
-        ss[u] = i < nch ? rec[i].s : 0.0;
-      }
-#pragma unroll
-      for (int u = 0; u < kDecB; ++u) {
-        m = fmaxnan(m, mm[u]);
-        bad |= isnan(ss[u]) ? 1 : 0;
-      }
-    }
     float z = NAN;
     if (j != K) {  // row K is the bonus row: no drafted token
       const int x = g.draft[b * K + (j < K ? j : j - K - 1)];
@@ -539,22 +522,40 @@ __global__ __launch_bounds__(kDecideWG) void k_lmh_decide(LmhCfg g, LinCfg c, Tr
         z = (float)hsum((double)a);
       }
     }
-    m = hmax(m);
-    double S = 0.0;
-    if (!isnan(m) && !isinf(m))
-      for (int i0 = hl; i0 < nch; i0 += 32 * kDecB) {
-        float mm[kDecB];
-        double ss[kDecB];
+    // one pass over the row's records: a running maximum ml per lane and the
+    // sum Sl of 2^((z - ml) c), rescaled in fp64 when ml rises
+    constexpr int kRecB = 16;
+    const double c32 = (double)g.c32;
+    float ml = -INFINITY;
+    double Sl = 0.0;
+    int bad = 0;
+    for (int i0 = hl; i0 < nch; i0 += 32 * kRecB) {
+      float mm[kRecB];
+      double ss[kRecB];
 #pragma unroll
-        for (int u = 0; u < kDecB; ++u) {
-          const int i = i0 + 32 * u;
-          mm[u] = i < nch ? rec[i].m : -INFINITY;
-          ss[u] = i < nch ? rec[i].s : 0.0;
-        }
-#pragma unroll
-        for (int u = 0; u < kDecB; ++u)
-          if (!is_neg_inf(mm[u])) S += ss[u] * ::exp2(((double)mm[u] - (double)m) * (double)g.c32);
+      for (int u = 0; u < kRecB; ++u) {
+        const int i = i0 + 32 * u;
+        mm[u] = i < nch ? rec[i].m : -INFINITY;
+        ss[u] = i < nch ? rec[i].s : 0.0;
       }
+#pragma unroll
+      for (int u = 0; u < kRecB; ++u) {
+        bad |= (isnan(ss[u]) || isnan(mm[u])) ? 1 : 0;
+        if (is_neg_inf(mm[u]) || isnan(mm[u])) continue;
+        if (is_neg_inf(ml)) {
+          ml = mm[u];
+          Sl = ss[u];
+        } else if (mm[u] > ml) {
+          Sl = Sl * exp2_fast(((double)ml - (double)mm[u]) * c32) + ss[u];
+          ml = mm[u];
+        } else {
+          Sl += ss[u] * exp2_fast(((double)mm[u] - (double)ml) * c32);
+        }
+      }
+    }
+    const float m = hmax(ml);
+    double S = 0.0;
+    if (!isnan(m) && !isinf(m) && !is_neg_inf(ml)) S = Sl * exp2_fast(((double)ml - (double)m) * c32);
     S = hsum(S);
     bad = (int)hsum((double)bad);
     if (hl == 0) {
