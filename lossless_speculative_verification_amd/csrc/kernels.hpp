@@ -41,6 +41,12 @@ constexpr uint32_t kTabLo = 101u << 7;
 constexpr int kTabW = 4094;
 constexpr int kTabNeg = 4096;
 constexpr int kTabSize = kTabNeg + kTabW + 1;
+// Slots of a table filled by the running-product fill: both halves whole
+// (4096 slots each, slots kTabW .. kTabNeg - 1 of a half zero), 64 KB, so
+// that a code whose magnitude lies in [kTabLo, kTabLo + kTabNeg) finds its
+// slot without the clamp to the zero slot, and a second such table placed
+// right after the first starts at byte 2^16.
+constexpr int kTabAlloc = 2 * kTabNeg;
 constexpr double kTabMaxAbs = 63.25;  // the largest magnitude in the window
 
 // Per (row, chunk) record of the fp32-grade statistics pass: chunk maximum of

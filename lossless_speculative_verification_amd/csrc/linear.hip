@@ -35,13 +35,15 @@ namespace psi {
 // (256 CUs), else about this many workgroups in total.
 constexpr int64_t kResolveOneWgMinB = 192;
 constexpr int64_t kResolveTargetWgs = 256;
-constexpr size_t kResolveMaxLds = 64 * 1024;
+// Sub-block records a one-workgroup resolve keeps in LDS at most: the
+// workgroup also holds the two 64 KB weight tables, within 160 KB.
+constexpr size_t kResolveMaxLds = 24 * 1024;
 
 // Threads of a draft-row workgroup (k_draftrow, k_qrow, k_tqrow).
 constexpr int kDT = 512;
 constexpr int kDWaves = kDT / kWave;
 
-// The unscaled 2^(a c) table, filled by kDT threads
+// The unscaled 2^(a c) table (kTabAlloc slots), filled by kDT threads
 // with one exp2 pair per 16 slots: thread t takes the 16 codes that share
 // sign, exponent and the top 3 mantissa bits, A = 2^(a_0 c) for the first of
 // them and r = 2^(u c) for the code step u, and slot k gets A * r^k with r^k
@@ -61,8 +63,7 @@ __device__ __forceinline__ void fill_tab_steps(double* tab, double c64) {
   double* const out = tab + half * kTabNeg + j0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    if (j0 + k < kTabW) out[k] = A * rk;
-    else if (j0 + k == kTabW) out[k] = 0.0;  // the zero slot of this half
+    out[k] = j0 + k < kTabW ? A * rk : 0.0;  // the zero slots of this half
     rk *= r;
   }
 }
@@ -123,8 +124,15 @@ __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool 
 //
 // RING > 0 keeps RING sub-blocks in flight per wave in a ring of register
 // buffers (RING - 1 ahead of the one being reduced) instead of the default.
+//
+// FAST (TAB, not CHK): the tables hold kTabAlloc slots each (the
+// running-product fill) and tq = tp + kTabAlloc. A vector pair whose codes
+// all lie inside the window then takes its slots from tab_fast_off2, with
+// the second table reached at byte 2^16; any other vector pair takes the
+// general code below. Both read the same slots.
+
 template <int DT, bool AL, bool TAB, bool RESID, bool PICK, int NW = kRWaves, class PRE, bool CHK = false,
-          int RING = 0>
+          int RING = 0, bool FAST = false>
 __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
                                              int sb0, int sb1, const double* tp, const double* tq, const WRow& wp,
                                              const WRow& wq, float dx, ResRec* s_rec, PRE pre, int* chk = nullptr) {
@@ -165,7 +173,41 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
     double sp = 0.0, sq = 0.0, a = 0.0, bq = 0.0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
+      bool general = TAB;
+      if constexpr (TAB && FAST && !CHK) {
+        uint32_t tw[2][4], out = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          tw[0][i] = tab_t2(word_of(x.p[v], i));
+          tw[1][i] = RESID ? tab_t2(word_of(x.q[v], i)) : 0u;
+          out |= tw[0][i] | tw[1][i];
+        }
+        general = __ballot((out & kTabOutside) != 0u) != 0ull;
+        if (!general) {
+          const char* const tb = (const char*)tp;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t op = tab_fast_off2(tw[0][i]);
+            const uint32_t oq = RESID ? tab_fast_off2(tw[1][i]) : 0u;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const double ep = *(const double*)(tb + (hf ? op >> 16 : op & 0xffffu));
+              sp += ep;
+              if constexpr (RESID) {
+                // the draft table starts at byte 2^16: bit 16 set on its offsets
+                const uint32_t aq = hf ? __builtin_amdgcn_alignbit(1u, oq, 16u) : ((oq & 0xffffu) | 0x10000u);
+                const double eq = *(const double*)(tb + aq);
+                sq += eq;
+                const double in = ep > eq ? 1.0 : 0.0;  // target part above draft part
+                a = __builtin_fma(in, ep, a);
+                bq = __builtin_fma(in, eq, bq);
+              }
+            }
+          }
+        }
+      }
       if constexpr (TAB) {
+       if (general) {
         // two bfloat16 codes per word; logits below the window read a zero
         // slot and get their exact weight in the rare call below
         uint32_t low = 0, high = 0;
@@ -215,6 +257,7 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
           a += f.a;
           bq += f.bq;
         }
+       }
       } else {
         float xp[EPV], xq[EPV];
         E::unpack(x.p[v], xp);
@@ -334,7 +377,7 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   __shared__ int s_bad, s_n;
   // the 2^(a c) table, then the same multiplied by the scale of the final
   // target row (first half) and of the final draft row (second half)
-  __shared__ double s_tab[2 * kTabSize];
+  __shared__ double s_tab[2 * kTabAlloc];
   const bool tab = DT == kBF16 && c.tab;
 
   // ---- decision: row normalisers, accept tests, first rejection. Wave 0
@@ -430,10 +473,10 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   // ---- fp64 pass over this part's sub-blocks; the tables are scaled while
   // the first loads of the pass are in flight
   double* const tabp = s_tab;
-  double* const tabq = s_tab + kTabSize;
+  double* const tabq = s_tab + kTabAlloc;
   auto scale_tables = [&]() {
     if (DT == kBF16 && wp.tab) {
-      for (int i = t; i < kTabSize; i += kRT) {
+      for (int i = t; i < kTabAlloc; i += kRT) {
         const double e = s_tab[i];
         if (resid) tabq[i] = e * wq.scale;
         tabp[i] = e * wp.scale;
@@ -447,15 +490,15 @@ __global__ __launch_bounds__(kRT) void k_resolve(LinCfg c, int parts) {
   const int sb0 = (int)((int64_t)part * nsb / parts), sb1 = (int)((int64_t)(part + 1) * nsb / parts);
   if (resid) {
     if (DT == kBF16 && wp.tab)
-      resolve_pass<DT, AL, DT == kBF16, true, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec,
-                                                    scale_tables);
+      resolve_pass<DT, AL, DT == kBF16, true, PICK, kRWaves, decltype(scale_tables), false, 0, true>(
+          c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec, scale_tables);
     else
       resolve_pass<DT, AL, false, true, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec,
                                               scale_tables);
   } else {
     if (DT == kBF16 && wp.tab)
-      resolve_pass<DT, AL, DT == kBF16, false, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec,
-                                                     scale_tables);
+      resolve_pass<DT, AL, DT == kBF16, false, PICK, kRWaves, decltype(scale_tables), false, 0, true>(
+          c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec, scale_tables);
     else
       resolve_pass<DT, AL, false, false, PICK>(c, b, prow, qrow, sb0, sb1, tabp, tabq, wp, wq, dx, s_rec,
                                                scale_tables);
@@ -908,7 +951,7 @@ __device__ __forceinline__ void stats_units(const LinCfg& c, int64_t nunits, int
 template <bool AL>
 __global__ __launch_bounds__(kDT) void k_qrow(LinCfg c, int64_t nunits) {
   extern __shared__ ResRec s_rec[];  // one record per sub-block (.sp)
-  __shared__ double s_tab[kTabSize];
+  __shared__ double s_tab[kTabAlloc];  // the running-product fill
   __shared__ float shf[kDWaves];
   __shared__ int s_chk;
   __shared__ double s_smax;
@@ -939,7 +982,7 @@ constexpr int64_t kTreeQrowFill = 256;  // workgroups of a tree draft-row launch
 template <bool AL>
 __global__ __launch_bounds__(kDT) void k_tqrow(LinCfg c, TreeTopo tp, TreeCfg tc, int64_t nunits, int nextra) {
   extern __shared__ ResRec s_rec[];
-  __shared__ double s_tab[kTabSize];
+  __shared__ double s_tab[kTabAlloc];  // the running-product fill
   __shared__ float shf[kDWaves];
   __shared__ int s_chk;
   __shared__ double s_smax;

@@ -39,6 +39,25 @@ __device__ __forceinline__ uint32_t tab_offsets2(uint32_t w, uint32_t& low) {
   return (w & 0x80008000u) | __builtin_bit_cast(uint32_t, idx << (u16x2_t)3);
 }
 
+// Packed differences t = code - kTabLo of the two codes of w (16-bit halves,
+// wrapping). For a code whose magnitude lies in [kTabLo, kTabLo + kTabNeg) a
+// half of t holds the sign in bit 15 and the slot within its half in bits
+// 0..11; for every other code (below the window: the difference wraps; above
+// it; NaN and infinities) bits 12..14 of the half are not all zero. Callers
+// test that on all the codes of a vector before tab_fast_off2.
+__device__ __forceinline__ uint32_t tab_t2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, w) - (u16x2_t)kTabLo);
+}
+constexpr uint32_t kTabOutside = 0x70007000u;  // bits of t that flag a code outside the window
+// Byte offsets (8 * slot) of the two codes from t = tab_t2(w), for codes
+// inside the window, in a table of kTabAlloc slots: slot kTabW and kTabW + 1
+// of a half are zero slots, so codes just above the window (magnitude codes
+// kTabLo + kTabW, + 1) read zero as tab_offsets2 gives them.
+__device__ __forceinline__ uint32_t tab_fast_off2(uint32_t t) {
+  static_assert(kTabNeg == 4096 && kTabW + 2 == kTabNeg, "sign in bit 15, slot in bits 3..14");
+  return (t & 0x80008000u) | __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, t) << (u16x2_t)3);
+}
+
 // tab_offsets2, and also ORs into `high` a value whose bit 15 in a half is
 // set when that code lies above the window (or, for codes below it, may be).
 __device__ __forceinline__ uint32_t tab_offsets2_chk(uint32_t w, uint32_t& low, uint32_t& high) {

@@ -232,7 +232,7 @@ def test_bf16_weight_window_edges(T):
     fp, fq = _bf16_float(p).copy(), _bf16_float(q).copy()
     rng = np.random.default_rng(77)
     tiny = np.array([0.0, -0.0, 2.0 ** -30, -(2.0 ** -30), 2.0 ** -27, -(2.0 ** -40)], np.float32)
-    edge = np.array([-63.25, -63.5, -64.0, -70.0, -1.0e4], np.float32)
+    edge = np.array([-63.25, -63.5, -63.75, -64.0, -70.0, -1.0e4], np.float32)
     for f in (fp, fq):
         m = rng.random(f.shape) < 0.08
         f[m] = rng.choice(tiny, size=int(m.sum()))
@@ -252,6 +252,33 @@ def test_bf16_weight_window_edges(T):
     for step in range(3):
         g, o = _run_pair(p, q, None, T, 4, step, True)
         tot += compare_linear(g, o, fused=True)
+        assert int((o["len"] < K).sum()) > 0  # residual draws happen
+    tot.check()
+
+
+def test_bf16_window_top_one_workgroup_resolve():
+    """Requests enough for one resolve workgroup each (B=192), bfloat16 rows
+    inside the table window except for a few logits just above it in
+    magnitude (-63.5 and -63.75, the last two codes before -64, which weigh
+    zero under the table rule) and fewer still beyond it (-64, -1e4): most
+    16-byte vector pairs have every code inside the window, some carry the
+    codes just above it, a few take the general slot computation. Given
+    drafts, three steps: lengths, tokens and residual masses match."""
+    B, K, V = 192, 4, 4096
+    p, q = synth.pair(B, K + 1, K, V, "bf16", seed=23, sd_a=3.0, mode=0, sd_noise=1.0)
+    fp, fq = _bf16_float(p).copy(), _bf16_float(q).copy()
+    rng = np.random.default_rng(78)
+    for f in (fp, fq):
+        m = rng.random(f.shape) < 0.004
+        f[m] = rng.choice(np.array([-63.5, -63.75], np.float32), size=int(m.sum()))
+        m = rng.random(f.shape) < 0.0005
+        f[m] = rng.choice(np.array([-64.0, -1.0e4], np.float32), size=int(m.sum()))
+    p, q = _bf16_bits(fp), _bf16_bits(fq)
+    drafts, _ = oracle.draft_sample(q, 1.0, seed=5, step=0, nthreads=THREADS)
+    tot = Tally("bf16 window top, one workgroup per request")
+    for step in range(3):
+        g, o = _run_pair(p, q, drafts, 1.0, 5, step, False)
+        tot += compare_linear(g, o, fused=False)
         assert int((o["len"] < K).sum()) > 0  # residual draws happen
     tot.check()
 
