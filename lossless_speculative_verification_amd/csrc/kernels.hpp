@@ -35,8 +35,7 @@ constexpr int kStatNV = 16;  // 16-byte vectors per thread in the fp32-grade sta
 // [kTabLo, kTabLo + kTabW) = |a| in [2^-26, 63.25], both signs. Positive codes
 // take slots [0, kTabW), negative ones [kTabNeg, kTabNeg + kTabW); slot kTabW
 // of each half is a zero slot. 8 * kTabSize < 2^16, so the byte offset of a
-// slot fits a 16-bit lane (the sign is its bit 15) and a second table placed
-// right after the first is reached through the LDS immediate offset.
+// slot fits a 16-bit lane (the sign is its bit 15).
 constexpr uint32_t kTabLo = 101u << 7;
 constexpr int kTabW = 4094;
 constexpr int kTabNeg = 4096;
