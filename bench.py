@@ -11,7 +11,7 @@ Prints ONE JSON line:
   value          verified (request, position) rows/s over the whole rho sweep;
   roofline       the dominant kernel (the statistics pass that streams every
                  logit once), its duration measured live with HIP events that
-                 the library records around each of its launches;
+                 each of the library's launches records at its start and end;
   kernels        mean duration of every kernel of the verify call;
   workloads      the other workloads of the method (fused-draft linear,
                  filtered, greedy, tree), each timed with HIP events;
@@ -471,7 +471,7 @@ def main():
     out_resid = torch.empty((B,), dtype=torch.float64, device=dev)
     stream = torch.cuda.current_stream()
     nb = max(1, args.breakdown_steps)
-    timer = psi.KernelTimer(nb * len(RHOS), len(LINEAR_KERNELS) + 1)
+    timer = psi.KernelTimer(nb * len(RHOS), len(LINEAR_KERNELS))
 
     # Every input is staged before any timing: the three rho workloads in HBM
     # (3 x 1.32 GB) and their pre-drawn draft sets (set t is used at step t).
@@ -511,7 +511,7 @@ def main():
                               out=dict(tokens=ot[t], len=ol[t], probs=out_probs, resid=out_resid),
                               workspace=ws, stream=stream)
 
-        # per-kernel breakdown (untimed): the library records an event around each launch
+        # per-kernel breakdown (untimed): each launch records its start and end events
         for i in range(nb):
             timer.arm(ri * nb + i)
             call(i % n_calls)

@@ -436,15 +436,18 @@ int psispec_generate_toy(int64_t B, int32_t block, int32_t V, int dtype, const p
 /*
  * Benchmark timing hook (not part of the method; for measuring each kernel of
  * a call live on the caller's stream). While armed with n > 0 caller-created
- * HIP events, every compute entry point records events[0] on its stream before
- * its first kernel and events[i] right after its i-th kernel launch (i < n),
- * so hipEventElapsedTime(events[i-1], events[i]) brackets kernel i. The events
+ * HIP events (timing enabled), every compute entry point launches its i-th
+ * kernel (0-based, while 2i + 1 < n) with events[2i] and events[2i + 1] as
+ * its start and stop events (hipExtLaunchKernelGGL: the timestamps of the
+ * kernel's own dispatch), so hipEventElapsedTime(events[2i], events[2i + 1])
+ * is kernel i's execution time, without the gaps between kernels. The events
  * stay owned by the caller and must outlive every armed call. The setting is
  * process-wide and not thread-safe; events == NULL or n <= 0 disarms it.
  */
 int psispec_set_timing_events(hipEvent_t* events, int n);
 
-/* Number of events recorded by the most recent compute call while armed. */
+/* Number of events the most recent compute call used while armed (two per
+   kernel launch). */
 int psispec_timing_count(void);
 
 /* Static message for a status code. */

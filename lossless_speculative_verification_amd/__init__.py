@@ -111,15 +111,17 @@ lib = _load()
 
 
 class KernelTimer:
-    """Per-kernel durations of library calls, measured with HIP events recorded
-    by the library itself on the call's stream (psispec_set_timing_events).
+    """Per-kernel durations of library calls, measured with HIP events that the
+    library's kernel launches record at their start and end
+    (psispec_set_timing_events).
 
-    Holds `calls` rows of `slots` events; `arm(i)` points the library at row i,
-    `disarm()` stops recording, `durations()` returns [calls, slots - 1] ms
-    (kernel j of call i is column j) after the stream has been synchronised.
+    Holds `calls` rows of 2 * `kernels` events; `arm(i)` points the library at
+    row i, `disarm()` stops recording, `durations()` returns [calls, kernels]
+    ms (kernel j of call i is column j) after the stream has been synchronised.
     """
 
-    def __init__(self, calls: int, slots: int):
+    def __init__(self, calls: int, kernels: int):
+        slots = 2 * kernels
         self._hip = ctypes.CDLL("libamdhip64.so")
         self._hip.hipEventCreate.argtypes = [ctypes.c_void_p]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
@@ -148,13 +150,13 @@ class KernelTimer:
     def durations(self):
         import numpy as np
 
-        out = np.full((self.calls, self.slots - 1), np.nan)
+        out = np.full((self.calls, self.slots // 2), np.nan)
         ms = ctypes.c_float()
         for i in range(self.calls):
-            for j in range(1, self.recorded[i]):
-                a, b = self._ev[i * self.slots + j - 1], self._ev[i * self.slots + j]
+            for j in range(self.recorded[i] // 2):
+                a, b = self._ev[i * self.slots + 2 * j], self._ev[i * self.slots + 2 * j + 1]
                 if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0:
-                    out[i, j - 1] = ms.value
+                    out[i, j] = ms.value
         return out
 
     def __del__(self):

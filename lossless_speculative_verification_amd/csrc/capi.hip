@@ -17,18 +17,19 @@ static __device__ __align__(256) unsigned char scratch[PSISPEC_NOALLOC_SCRATCH_B
 
 namespace psi {
 
-// Benchmark timing hook: caller-owned events, recorded in order.
+// Benchmark timing hook: caller-owned events, two per kernel launch in order.
 static hipEvent_t* g_timing_events = nullptr;
 static int g_timing_n = 0;
 static int g_timing_next = 0;
 
-void timing_begin(hipStream_t s) {
-  g_timing_next = 0;
-  if (g_timing_events && g_timing_n > 0) hipEventRecord(g_timing_events[g_timing_next++], s);
-}
+void timing_begin(hipStream_t) { g_timing_next = 0; }
 
-void timing_mark(hipStream_t s) {
-  if (g_timing_events && g_timing_next < g_timing_n) hipEventRecord(g_timing_events[g_timing_next++], s);
+bool timing_pair(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_timing_events || g_timing_next + 1 >= g_timing_n) return false;
+  *start = g_timing_events[g_timing_next];
+  *stop = g_timing_events[g_timing_next + 1];
+  g_timing_next += 2;
+  return true;
 }
 
 namespace {

@@ -1,6 +1,7 @@
 // Internal interface between the C ABI (capi.hip) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -9,18 +10,22 @@
 
 namespace psi {
 
-// Benchmark timing hook (psispec_set_timing_events, capi.hip): when armed,
-// timing_begin records the first event before an entry point's first kernel
-// and timing_mark the next one after every kernel launch.
+// Benchmark timing hook (psispec_set_timing_events, capi.hip): timing_begin
+// starts an entry point's sequence; while armed, timing_pair hands out the
+// next two events, which the launch of the next kernel records as that
+// kernel's start and end (its dispatch's own timestamps).
 void timing_begin(hipStream_t s);
-void timing_mark(hipStream_t s);
+bool timing_pair(hipEvent_t* start, hipEvent_t* stop);
 
 // Every kernel launch of the library goes through PSI_LAUNCH (or
 // PSI_LAUNCH_LDS with dynamic LDS bytes).
-#define PSI_LAUNCH_LDS(s, kernel, grid, block, lds, ...)           \
-  do {                                                              \
-    hipLaunchKernelGGL(kernel, grid, block, lds, s, __VA_ARGS__);   \
-    ::psi::timing_mark(s);                                          \
+#define PSI_LAUNCH_LDS(s, kernel, grid, block, lds, ...)                                  \
+  do {                                                                                     \
+    hipEvent_t psi_ev0_, psi_ev1_;                                                         \
+    if (::psi::timing_pair(&psi_ev0_, &psi_ev1_))                                          \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, s, psi_ev0_, psi_ev1_, 0u, __VA_ARGS__); \
+    else                                                                                   \
+      hipLaunchKernelGGL(kernel, grid, block, lds, s, __VA_ARGS__);                        \
   } while (0)
 #define PSI_LAUNCH(s, kernel, grid, block, ...) PSI_LAUNCH_LDS(s, kernel, grid, block, 0, __VA_ARGS__)
 // Calls the instance fn<dtype, aligned> of a launcher template.
