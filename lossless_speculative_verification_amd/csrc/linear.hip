@@ -130,7 +130,6 @@ __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool 
 // all lie inside the window then takes its slots from tab_fast_off2, with
 // the second table reached at byte 2^16; any other vector pair takes the
 // general code below. Both read the same slots.
-
 template <int DT, bool AL, bool TAB, bool RESID, bool PICK, int NW = kRWaves, class PRE, bool CHK = false,
           int RING = 0, bool FAST = false>
 __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const char* prow, const char* qrow,
@@ -207,57 +206,57 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
         }
       }
       if constexpr (TAB) {
-       if (general) {
-        // two bfloat16 codes per word; logits below the window read a zero
-        // slot and get their exact weight in the rare call below
-        uint32_t low = 0, high = 0;
-        const char* const tpb = (const char*)tp;
-        const char* const tqb = (const char*)tq;
+        if (general) {
+          // two bfloat16 codes per word; logits below the window read a zero
+          // slot and get their exact weight in the rare call below
+          uint32_t low = 0, high = 0;
+          const char* const tpb = (const char*)tp;
+          const char* const tqb = (const char*)tq;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t wpw = word_of(x.p[v], i), wqw = RESID ? word_of(x.q[v], i) : 0u;
-          const uint32_t op = CHK ? tab_offsets2_chk(wpw, low, high) : tab_offsets2(wpw, low);
-          const uint32_t oq = RESID ? tab_offsets2(wqw, low) : 0u;
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t wpw = word_of(x.p[v], i), wqw = RESID ? word_of(x.q[v], i) : 0u;
+            const uint32_t op = CHK ? tab_offsets2_chk(wpw, low, high) : tab_offsets2(wpw, low);
+            const uint32_t oq = RESID ? tab_offsets2(wqw, low) : 0u;
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const double ep = *(const double*)(tpb + (hf ? op >> 16 : op & 0xffffu));
-            sp += ep;
-            if constexpr (RESID) {
-              const double eq = *(const double*)(tqb + (hf ? oq >> 16 : oq & 0xffffu));
-              sq += eq;
-              const double in = ep > eq ? 1.0 : 0.0;  // target part above draft part
-              a = __builtin_fma(in, ep, a);
-              bq = __builtin_fma(in, eq, bq);
+            for (int hf = 0; hf < 2; ++hf) {
+              const double ep = *(const double*)(tpb + (hf ? op >> 16 : op & 0xffffu));
+              sp += ep;
+              if constexpr (RESID) {
+                const double eq = *(const double*)(tqb + (hf ? oq >> 16 : oq & 0xffffu));
+                sq += eq;
+                const double in = ep > eq ? 1.0 : 0.0;  // target part above draft part
+                a = __builtin_fma(in, ep, a);
+                bq = __builtin_fma(in, eq, bq);
+              }
             }
           }
-        }
-        if constexpr (CHK) {
-          if (__ballot((high & 0x80008000u) != 0u)) {
-            // exact test of the flagged codes (codes below the window may set
-            // the flag too)
-            bool hit = false;
+          if constexpr (CHK) {
+            if (__ballot((high & 0x80008000u) != 0u)) {
+              // exact test of the flagged codes (codes below the window may set
+              // the flag too)
+              bool hit = false;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+              for (int i = 0; i < 4; ++i)
 #pragma unroll
-              for (int hf = 0; hf < 2; ++hf) {
-                const uint32_t h = (word_of(x.p[v], i) >> (16 * hf)) & 0xffffu;
-                const bool above = !tab_tiny(h) && tab_idx(h) == (uint32_t)kTabW;
-                hit |= above && (!(h & 0x8000u) || (h & 0x7fffu) > 0x7f80u);
-              }
-            if (hit) atomicOr(chk, 1);
+                for (int hf = 0; hf < 2; ++hf) {
+                  const uint32_t h = (word_of(x.p[v], i) >> (16 * hf)) & 0xffffu;
+                  const bool above = !tab_tiny(h) && tab_idx(h) == (uint32_t)kTabW;
+                  hit |= above && (!(h & 0x8000u) || (h & 0x7fffu) > 0x7f80u);
+                }
+              if (hit) atomicOr(chk, 1);
+            }
+          }
+          const bool tiny = (low & 0x80008000u) != 0u;
+          if (__ballot(tiny)) {
+            // a call, so that this rare work stays out of the common path
+            const ResRec f = tiny_fixup(x.p[v], RESID ? x.q[v] : make_uint4(0, 0, 0, 0), RESID, c64, wp.scale,
+                                        wq.scale, tp, tq);
+            sp += f.sp;
+            sq += f.sq;
+            a += f.a;
+            bq += f.bq;
           }
         }
-        const bool tiny = (low & 0x80008000u) != 0u;
-        if (__ballot(tiny)) {
-          // a call, so that this rare work stays out of the common path
-          const ResRec f = tiny_fixup(x.p[v], RESID ? x.q[v] : make_uint4(0, 0, 0, 0), RESID, c64, wp.scale,
-                                      wq.scale, tp, tq);
-          sp += f.sp;
-          sq += f.sq;
-          a += f.a;
-          bq += f.bq;
-        }
-       }
       } else {
         float xp[EPV], xq[EPV];
         E::unpack(x.p[v], xp);
