@@ -107,7 +107,7 @@ __device__ __attribute__((noinline)) ResRec tiny_fixup(uint4 rp, uint4 rq, bool 
 
 // fp64 sums of this workgroup's sub-blocks [sb0, sb1) of the final row pair
 // (RESID) or the target row alone, one wave per sub-block (sb0 + wave, then
-// every NW-th, NW the workgroup's waves). Software-pipelined over NBUF register buffers that change
+// every NW-th, by the first NW waves of the workgroup; every wave runs pre()). Software-pipelined over NBUF register buffers that change
 // roles each step (no copies, so loads stay in flight across steps): bfloat16
 // keeps the next two sub-blocks in flight, fp32 the next one. TAB: weights
 // are read from the pre-scaled LDS tables tp / tq (bfloat16 only), whose
@@ -286,15 +286,17 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
     }
   };
   constexpr int W = NW;
+  // waves from NW on take no part in the pass (they only run pre())
+  const bool member = wave < W;
   if constexpr (RING > 0) {
     Buf x[RING];
     int s = sb0 + wave;
-    if (s < sb1) {
+    if (member && s < sb1) {
 #pragma unroll
       for (int k = 0; k < RING - 1; ++k) load(s + k * W, x[k]);
     }
     pre();
-    if (s >= sb1) return;
+    if (!member || s >= sb1) return;
     for (; s < sb1; s += RING * W) {
 #pragma unroll
       for (int k = 0; k < RING; ++k) {
@@ -307,12 +309,12 @@ __device__ __forceinline__ void resolve_pass(const LinCfg& c, int64_t b, const c
   }
   Buf x0, x1, x2;
   int s = sb0 + wave;
-  if (s < sb1) {
+  if (member && s < sb1) {
     load(s, x0);
     if constexpr (NBUF == 3) load(s + W, x1);
   }
   pre();
-  if (s >= sb1) return;
+  if (!member || s >= sb1) return;
   if constexpr (NBUF == 3) {
     for (; s < sb1; s += 3 * W) {
       load(s + 2 * W, x2);
@@ -815,10 +817,14 @@ __device__ __forceinline__ void wave_stats_unit(const LinCfg& c, int64_t u) {
 // (with the LDS table, or exact exponentials) and its validity. Called by
 // every thread of a kDT-thread workgroup.
 // RING > 0: sub-blocks in flight per wave in the pass (more loads in flight
-// for a workgroup that has its CU to itself).
-template <bool AL, int RING = 0>
+// for a workgroup that has its CU to itself). NP < kDWaves: only the first NP
+// waves run the pass, and the others call during() meanwhile.
+struct NoWork {
+  __device__ void operator()() const {}
+};
+template <bool AL, int RING = 0, int NP = kDWaves, class DURING = NoWork>
 __device__ bool qrow_pass(const LinCfg& c, int64_t b, int i, const char* row, ResRec* s_rec, double* s_tab,
-                          float* shf, int* s_chk, double* s_smax, WRow& w) {
+                          float* shf, int* s_chk, double* s_smax, WRow& w, DURING during = DURING{}) {
   using E = Elem<kBF16>;
   const int t = threadIdx.x, wave = t / kWave, lane = t & (kWave - 1);
   const int nsb = c.nsb;
@@ -830,9 +836,11 @@ __device__ bool qrow_pass(const LinCfg& c, int64_t b, int i, const char* row, Re
     if (t == 0) *s_chk = 0;
     __syncthreads();
   };
-  resolve_pass<kBF16, AL, true, false, true, kDWaves, decltype(fill), true, RING>(c, b, row, row, 0, nsb, s_tab,
-                                                                                 s_tab, w1, w1, 0.0f, s_rec, fill,
-                                                                                 s_chk);
+  resolve_pass<kBF16, AL, true, false, true, NP, decltype(fill), true, RING>(c, b, row, row, 0, nsb, s_tab, s_tab,
+                                                                            w1, w1, 0.0f, s_rec, fill, s_chk);
+  if constexpr (NP < kDWaves) {
+    if (wave >= NP) during();  // waves outside the pass do other work meanwhile
+  }
   __syncthreads();
   if (wave == 0) {
     // the sub-block with the largest sum (lowest index on ties), then its largest logit
@@ -929,26 +937,32 @@ __device__ __forceinline__ int qrow_draw(const LinCfg& c, const char* row, const
                    [&](int64_t j0, double(&wt)[16]) { row16<kBF16, AL>(c, row, j0, w, tps, wt); });
 }
 
-// The target-row chunk records of a launch, `nunits` in all. Workgroup-major
-// (WG_MAJOR): wave `slot` of workgroup g takes the units g * kDWaves + slot +
-// k * (kDWaves * grid), so the first workgroups take them all. Otherwise
-// slot-major: it takes slot * grid + g + k * (kDWaves * grid), so every
-// workgroup gets the same number of units to within one and no CU streams
-// more target rows than another.
-template <bool AL, bool WG_MAJOR = true>
+// The target-row chunk records of a launch: wave `slot` of workgroup g takes
+// the units g * kDWaves + slot + k * (kDWaves * grid), `nunits` in all.
+template <bool AL>
 __device__ __forceinline__ void stats_units(const LinCfg& c, int64_t nunits, int slot) {
-  const int64_t g = blockIdx.x, G = gridDim.x;
-  const int64_t first = WG_MAJOR ? g * kDWaves + slot : (int64_t)slot * G + g;
-  for (int64_t un = first; un < nunits; un += G * kDWaves) wave_stats_unit<AL>(c, un);
+  for (int64_t un = (int64_t)blockIdx.x * kDWaves + slot; un < nunits; un += (int64_t)gridDim.x * kDWaves)
+    wave_stats_unit<AL>(c, un);
 }
+
+// Waves of a fused draft-row workgroup that stream target rows while the
+// others run the pass over its draft row, and the statistics units each of
+// them takes meanwhile.
+constexpr int kQrowEarlyWaves = 2;
+constexpr int kQrowEarlyUnits = 1;
 
 // One workgroup per draft row of linear verification: qrow_pass, then wave 0
 // draws x ~ q with U(seed, step, b, i, 0x40000000) ("Uno" research explainer,
 // §3.3: the drafts of a block are drawn from the draft distributions; -1 for
-// an invalid row) while the other waves compute the target rows' chunk
-// records (wave_stats_unit), `nunits` of them over the whole grid.
-template <bool AL>
-__global__ __launch_bounds__(kDT) void k_qrow(LinCfg c, int64_t nunits) {
+// an invalid row). The target rows' chunk records (wave_stats_unit, `nunits`
+// of them over the whole grid) come in two parts. SPLIT: the last
+// kQrowEarlyWaves waves compute kQrowEarlyUnits each while the others run
+// the pass over the draft row (the table-bound pass and the streaming of
+// target rows share the CU); then every wave takes the rest slot-major, wave 0
+// (busy drawing) taking the last slot, which the grid reaches last. Held to
+// 128 registers (four waves per SIMD), so that two workgroups share a CU.
+template <bool AL, bool SPLIT>
+__global__ __launch_bounds__(kDT) __attribute__((amdgpu_waves_per_eu(4))) void k_qrow(LinCfg c, int64_t nunits) {
   extern __shared__ ResRec s_rec[];  // one record per sub-block (.sp)
   __shared__ double s_tab[kTabAlloc];  // the running-product fill
   __shared__ float shf[kDWaves];
@@ -959,14 +973,23 @@ __global__ __launch_bounds__(kDT) void k_qrow(LinCfg c, int64_t nunits) {
   const int64_t b = qr / K;
   const int i = (int)(qr - b * K);
   const char* row = qrow_of(c, b, i);
+  const int64_t g = blockIdx.x, G = gridDim.x;
+  constexpr int NP = SPLIT ? kDWaves - kQrowEarlyWaves : kDWaves;
+  const int64_t early = SPLIT ? (int64_t)kQrowEarlyWaves * kQrowEarlyUnits * G : 0;
+  auto during = [&]() {
+    for (int r = 0; r < kQrowEarlyUnits; ++r) {
+      const int64_t un = ((int64_t)r * kQrowEarlyWaves + (wave - NP)) * G + g;
+      if (un < nunits) wave_stats_unit<AL>(c, un);
+    }
+  };
   WRow w;
-  const bool ok = qrow_pass<AL>(c, b, i, row, s_rec, s_tab, shf, &s_chk, &s_smax, w);
+  const bool ok = qrow_pass<AL, 0, NP>(c, b, i, row, s_rec, s_tab, shf, &s_chk, &s_smax, w, during);
   if (wave == 0) {
     const int x = ok ? qrow_draw<AL>(c, row, s_rec, s_tab, w, c.rng.u((uint32_t)b, (uint32_t)i, kDrawDraft)) : -1;
     if ((threadIdx.x & (kWave - 1)) == 0) c.draft[qr] = x;
   }
-  // wave 0 (busy drawing) takes the last slot, which the grid reaches last
-  stats_units<AL, false>(c, nunits, wave == 0 ? kDWaves - 1 : wave - 1);
+  const int slot = wave == 0 ? kDWaves - 1 : wave - 1;
+  for (int64_t un = early + slot * G + g; un < nunits; un += G * kDWaves) wave_stats_unit<AL>(c, un);
 }
 
 // Tree node drafts: workgroups [0, nextra) compute target-row chunk records
@@ -1198,8 +1221,8 @@ static hipError_t linear_sampled_t(const LinCfg& c, hipStream_t s) {
   if (c.fused && DT == kBF16 && c.tab) {
     // drafts drawn in one pass over their rows, whose workgroups also write
     // those rows' chunk records and, wave by wave, the target rows' ones
-    PSI_LAUNCH_LDS(s, (k_qrow<AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c,
-                   c.B * c.rows.np * (int64_t)c.nch32);
+    PSI_LAUNCH_LDS(s, (k_qrow<AL, true>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec),
+                   c, c.B * c.rows.np * (int64_t)c.nch32);
   } else {
     const hipError_t e = launch_stats32(c, rows, DT, s);
     if (e != hipSuccess) return e;
@@ -1234,8 +1257,8 @@ static hipError_t linear_greedy_t(const LinCfg& c, hipStream_t s) {
 template <int DT, bool AL>
 static hipError_t draft_sampled_t(const LinCfg& c, hipStream_t s) {
   if (DT == kBF16 && c.tab) {
-    PSI_LAUNCH_LDS(s, (k_qrow<AL>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec), c,
-                   (int64_t)0);
+    PSI_LAUNCH_LDS(s, (k_qrow<AL, false>), dim3((unsigned)(c.B * c.K)), dim3(kDT), (size_t)c.nsb * sizeof(ResRec),
+                   c, (int64_t)0);
   } else {
     const hipError_t e = launch_stats32(c, c.B * c.K, DT, s);
     if (e != hipSuccess) return e;
