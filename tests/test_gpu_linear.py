@@ -353,3 +353,29 @@ def test_philox_sweep_against_oracle():
         want_b = np.array([int(oracle.uniform(seed, step, b, K, 0) * V) for b in range(B)])
         bad += int((drafts != want_d).sum() + (bonus != want_b).sum())
     assert bad == 0
+
+
+def test_timing_hook_two_events_per_kernel():
+    """The benchmark timing hook: an armed verification call launches each of
+    its kernels with a start and a stop event, two per kernel (statistics pass
+    and resolve at one workgroup per request: four); the durations are
+    positive, and the outputs equal those of the same call unarmed."""
+    psi = _psi()
+    B, K, V = 192, 4, 4096
+    p, q = synth.pair(B, K + 1, K, V, "bf16", seed=31, sd_a=3.0, mode=0, sd_noise=1.0)
+    pd, qd = to_dev(p), to_dev(q)
+    drafts, _ = oracle.draft_sample(q, 1.0, seed=2, step=0, nthreads=THREADS)
+    dd = torch.from_numpy(drafts.astype(np.int32)).cuda()
+    plain = psi.verify_linear(pd, qd, dd, temperature=1.0, seed=2, step=0)
+    timer = psi.KernelTimer(3, 4)
+    for i in range(3):
+        timer.arm(i)
+        g = psi.verify_linear(pd, qd, dd, temperature=1.0, seed=2, step=0)
+        timer.note()
+    timer.disarm()
+    torch.cuda.synchronize()
+    assert timer.recorded == [4, 4, 4]
+    dur = timer.durations()
+    assert dur.shape == (3, 4) and np.isfinite(dur[:, :2]).all() and (dur[:, :2] > 0).all()
+    assert np.isnan(dur[:, 2:]).all()  # two kernels: the last two slots stay unused
+    assert torch.equal(g["tokens"], plain["tokens"]) and torch.equal(g["len"], plain["len"])
